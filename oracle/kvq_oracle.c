@@ -1,0 +1,408 @@
+/*
+ * kvq_oracle.c -- reference CPU oracle for the FP8 paged KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow definition that the
+ * GPU library is checked against.  Only the test-suite, the smoke check and
+ * the benchmark's CPU-baseline leg may load it.  It shares no source, header,
+ * table or helper with the HIP library, and the library never calls it.
+ *
+ * Everything is written from the definitions on the pages:
+ *   [T]  "10.4 KV Cache 量化: INT8 基础、KIVI 2-bit、FP8 KV" (KV-cache quantization
+ *        textbook chapter), sections 10.4.1 - 10.4.5.
+ *   [G]  "vLLM FP8 量化 KV Cache 完整指南" (vLLM FP8 KV-cache guide), sections on
+ *        kv_cache_dtype formats, the two scale granularities and scale sources.
+ * plus the OCP 8-bit floating point specification for the bit layouts of
+ * E4M3 ("fn": no infinities, one NaN mantissa) and E5M2 (IEEE-like).
+ *
+ * Floating point is fp64 unless a step is defined in fp32 (the quantize
+ * quotient and the scale, which the cache stores as fp32).
+ *
+ * Readings of points the pages leave open (numbered as in the design notes):
+ *   R1 quantize divides by the scale (not multiply by a reciprocal);
+ *   R2 rounding is round-to-nearest, ties to even;
+ *   R3 out-of-range and +-Inf saturate to +-max, NaN stays NaN, -0 keeps its
+ *      sign, subnormal codes are produced (no flush to zero);
+ *   R4 scale = amax/fmax in fp32, 1.0 if amax is 0 or not finite;
+ *   R5 query head hq reads KV head hq / (Hq/Hkv);
+ *   R7 decode has no mask; prefill is causal at absolute positions;
+ *   zero-length context gives an all-zero output row.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_FMT_E4M3 0
+#define ORC_FMT_E5M2 1
+#define ORC_GRAN_TENSOR 0
+#define ORC_GRAN_HEAD 1
+
+/* ---- format parameters (OCP FP8): mantissa bits, exponent bias, max ---- */
+
+static int fmt_mbits(int fmt) { return fmt == ORC_FMT_E4M3 ? 3 : 2; }
+static int fmt_bias(int fmt) { return fmt == ORC_FMT_E4M3 ? 7 : 15; }
+
+double orc_fp8_max(int fmt) {
+  /* E4M3fn: exponent field 15, mantissa 110b -> 1.75 * 2^8.
+   * E5M2:   exponent field 30, mantissa 11b  -> 1.75 * 2^15. */
+  return fmt == ORC_FMT_E4M3 ? 1.75 * 256.0 : 1.75 * 32768.0;
+}
+
+/* ---- decode: code -> exact value (textbook 10.4.5: cast_float(Kfp8)) ---- */
+
+double orc_fp8_decode(int fmt, uint8_t code) {
+  int s = code >> 7;
+  int mb = fmt_mbits(fmt);
+  int bias = fmt_bias(fmt);
+  int e = (code & 0x7f) >> mb;
+  int m = code & ((1 << mb) - 1);
+  double v;
+  if (fmt == ORC_FMT_E4M3) {
+    if (e == 15 && m == 7) return NAN; /* the only NaN mantissa; no Inf */
+  } else {
+    if (e == 31) return m == 0 ? (s ? -INFINITY : INFINITY) : NAN;
+  }
+  if (e == 0)
+    v = ldexp((double)m, 1 - bias - mb); /* subnormal: m * 2^(1-bias-mb) */
+  else
+    v = ldexp(1.0 + (double)m / (double)(1 << mb), e - bias);
+  return s ? -v : v;
+}
+
+/* ---- encode: fp32 -> code, saturating round-to-nearest-even (R2, R3) ----
+ * |x| is rounded onto the target grid as if the exponent were unbounded
+ * above (quantum 2^(e-mb) in binade e, 2^(emin-mb) below the normal range),
+ * then anything above max saturates.  All arithmetic is exact in fp64. */
+
+uint8_t orc_fp8_encode(int fmt, float x) {
+  int mb = fmt_mbits(fmt);
+  int bias = fmt_bias(fmt);
+  int emin = 1 - bias;
+  double fmax = orc_fp8_max(fmt);
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  double a = fabs((double)x);
+  if (isnan(x)) return (uint8_t)(sign | 0x7f); /* 0x7f is NaN in both formats */
+  if (isinf(x) || a > fmax) {
+    /* saturate: encode max */
+  } else {
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2); /* a = f * 2^e2, f in [0.5,1) -> binade e2-1 */
+    int binade = e2 - 1;
+    if (binade < emin) binade = emin;
+    double quantum = ldexp(1.0, binade - mb);
+    double n = rint(a / quantum); /* exact quotient; rint = ties-to-even */
+    double r = n * quantum;
+    if (r <= fmax) {
+      if (r == 0.0) return sign;
+      int er;
+      frexp(r, &er);
+      int be = er - 1;
+      if (be < emin) { /* subnormal code: value = mant * 2^(emin-mb) */
+        int mant = (int)(r / ldexp(1.0, emin - mb));
+        return (uint8_t)(sign | mant);
+      }
+      int mant = (int)((r / ldexp(1.0, be) - 1.0) * (double)(1 << mb));
+      int efield = be + bias;
+      return (uint8_t)(sign | (efield << mb) | mant);
+    }
+  }
+  /* +-max */
+  {
+    int efield = fmt == ORC_FMT_E4M3 ? 15 : 30;
+    int mant = fmt == ORC_FMT_E4M3 ? 6 : 3;
+    return (uint8_t)(sign | (efield << mb) | mant);
+  }
+}
+
+void orc_fp8_encode_many(int fmt, const float* x, uint8_t* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_fp8_encode(fmt, x[i]);
+}
+
+void orc_fp8_decode_all(int fmt, double* out256) {
+  for (int c = 0; c < 256; ++c) out256[c] = orc_fp8_decode(fmt, (uint8_t)c);
+}
+
+/* ---- bf16 and the quantize step (textbook 10.4.5: cast_fp8(K / sK)) ---- */
+
+float orc_bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16; /* bf16 is the top half of an fp32 */
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* fl32(x / s): the fp64 quotient of two fp32 values, rounded once more to
+ * fp32, equals the correctly rounded fp32 quotient (53 >= 2*24 + 2). */
+float orc_quotient(float x, float s) { return (float)((double)x / (double)s); }
+
+uint8_t orc_quantize(int fmt, uint16_t x_bf16, float s) {
+  return orc_fp8_encode(fmt, orc_quotient(orc_bf16_to_f32(x_bf16), s));
+}
+
+void orc_quantize_many(int fmt, const uint16_t* x, int64_t n, float s, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_quantize(fmt, x[i], s);
+}
+
+/* ---- scale calibration (textbook 10.4.3 granularity table; guide's scale
+ * shapes [1] / [num_heads] / [num_kv_heads]) ----
+ * amax = max |x| over the granularity set (NaN anywhere in the set gives NaN);
+ * scale = fl32(amax / fmax) when amax is finite and > 0, else 1.0 (R4, the
+ * guide's default scale when no calibration is done). */
+
+float orc_scale_from_amax(int fmt, float amax) {
+  if (!(amax > 0.0f) || isinf(amax)) return 1.0f;
+  return (float)((double)amax / orc_fp8_max(fmt));
+}
+
+void orc_calibrate(const uint16_t* x, int64_t T, int H, int dh, int fmt, int gran,
+                   float* amax_out, float* scale_out) {
+  int nset = gran == ORC_GRAN_HEAD ? H : 1;
+  for (int g = 0; g < nset; ++g) {
+    double amax = 0.0;
+    int saw_nan = 0;
+    for (int64_t t = 0; t < T; ++t)
+      for (int h = 0; h < H; ++h) {
+        if (gran == ORC_GRAN_HEAD && h != g) continue;
+        for (int d = 0; d < dh; ++d) {
+          double v = fabs((double)orc_bf16_to_f32(x[(t * H + h) * dh + d]));
+          if (isnan(v)) saw_nan = 1;
+          else if (v > amax) amax = v;
+        }
+      }
+    amax_out[g] = saw_nan ? NAN : (float)amax; /* |bf16| is exact in fp32 */
+    scale_out[g] = orc_scale_from_amax(fmt, amax_out[g]);
+  }
+}
+
+/* ---- paged quantize-write ----
+ * For every token t with slot_mapping[t] >= 0, every KV head h and channel d:
+ *   cache[slot / bs][h][slot % bs][d] = quantize(x[t][h][d], s[h or 0]).
+ * Cache layout: uint8 [num_blocks][Hkv][bs][dh]. */
+
+void orc_cache_write(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv, int dh,
+                     const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                     int64_t num_blocks, int bs, const float* k_scale, const float* v_scale,
+                     int fmt, int gran) {
+  (void)num_blocks;
+  for (int64_t t = 0; t < T; ++t) {
+    int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    int64_t blk = slot / bs, off = slot % bs;
+    for (int h = 0; h < Hkv; ++h) {
+      float sk = k_scale[gran == ORC_GRAN_HEAD ? h : 0];
+      float sv = v_scale[gran == ORC_GRAN_HEAD ? h : 0];
+      for (int d = 0; d < dh; ++d) {
+        int64_t src = (t * Hkv + h) * dh + d;
+        int64_t dst = ((blk * Hkv + h) * bs + off) * dh + d;
+        k_cache[dst] = orc_quantize(fmt, k[src], sk);
+        v_cache[dst] = orc_quantize(fmt, v[src], sv);
+      }
+    }
+  }
+}
+
+/* ---- dequantized read: x_hat = s * cast_float(code) (textbook 10.4.2/10.4.5) ---- */
+
+static double deq(const uint8_t* cache, int64_t blk, int h, int off, int d, int Hkv, int bs,
+                  int dh, double s, int fmt) {
+  return s * orc_fp8_decode(fmt, cache[(((int64_t)blk * Hkv + h) * bs + off) * dh + d]);
+}
+
+/* Attention of one query vector q[dh] (fp64) over keys 0..nkeys-1 of one
+ * sequence's paged cache (textbook 10.4.2: P = softmax(Q K^T / sqrt(dh) + mask),
+ * O = P V), all in fp64; writes o[dh]. */
+static void attend_one(double* o, const double* q, int nkeys, const uint8_t* k_cache,
+                       const uint8_t* v_cache, const int32_t* btab, int h, int Hkv, int bs,
+                       int dh, double sk, double sv, int fmt, double sm_scale) {
+  for (int d = 0; d < dh; ++d) o[d] = 0.0;
+  if (nkeys <= 0) return;
+  double* z = (double*)malloc(sizeof(double) * (size_t)nkeys);
+  double zmax = -INFINITY;
+  for (int j = 0; j < nkeys; ++j) {
+    int64_t blk = btab[j / bs];
+    int off = j % bs;
+    double acc = 0.0;
+    for (int d = 0; d < dh; ++d) acc += q[d] * deq(k_cache, blk, h, off, d, Hkv, bs, dh, sk, fmt);
+    z[j] = acc * sm_scale;
+    if (z[j] > zmax) zmax = z[j];
+  }
+  double l = 0.0;
+  for (int j = 0; j < nkeys; ++j) {
+    z[j] = exp(z[j] - zmax);
+    l += z[j];
+  }
+  for (int j = 0; j < nkeys; ++j) {
+    int64_t blk = btab[j / bs];
+    int off = j % bs;
+    double p = z[j] / l;
+    for (int d = 0; d < dh; ++d) o[d] += p * deq(v_cache, blk, h, off, d, Hkv, bs, dh, sv, fmt);
+  }
+  free(z);
+}
+
+static double default_scale(float softmax_scale, int dh) {
+  return softmax_scale > 0.0f ? (double)softmax_scale : 1.0 / sqrt((double)dh);
+}
+
+/* Decode: one query token per sequence, the last position, already written;
+ * it attends to every cached key 0..context_lens[b]-1 (no mask, R7).
+ * q: bf16 [B][Hq][dh]; out: fp64 [B][Hq][dh]. */
+void orc_decode_attn(double* out, const uint16_t* q, const uint8_t* k_cache,
+                     const uint8_t* v_cache, const int32_t* block_tables, int max_blocks,
+                     const int32_t* context_lens, int B, int Hq, int Hkv, int dh, int bs,
+                     const float* k_scale, const float* v_scale, int fmt, int gran,
+                     float softmax_scale) {
+  int G = Hq / Hkv;
+  double sm = default_scale(softmax_scale, dh);
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int b = 0; b < B; ++b)
+    for (int hq = 0; hq < Hq; ++hq) {
+      int h = hq / G;
+      double qd[512];
+      for (int d = 0; d < dh; ++d) qd[d] = (double)orc_bf16_to_f32(q[((int64_t)b * Hq + hq) * dh + d]);
+      double sk = k_scale[gran == ORC_GRAN_HEAD ? h : 0];
+      double sv = v_scale[gran == ORC_GRAN_HEAD ? h : 0];
+      attend_one(out + ((int64_t)b * Hq + hq) * dh, qd, context_lens[b], k_cache, v_cache,
+                 block_tables + (int64_t)b * max_blocks, h, Hkv, bs, dh, sk, sv, fmt, sm);
+    }
+}
+
+/* Decode for an explicit list of (b, hq) rows only (bounded CPU baseline and
+ * sampled checks at full size).  rows: int32 pairs [n][2]; out: fp64 [n][dh]. */
+void orc_decode_rows(double* out, const int32_t* rows, int n, const uint16_t* q,
+                     const uint8_t* k_cache, const uint8_t* v_cache, const int32_t* block_tables,
+                     int max_blocks, const int32_t* context_lens, int B, int Hq, int Hkv, int dh,
+                     int bs, const float* k_scale, const float* v_scale, int fmt, int gran,
+                     float softmax_scale) {
+  (void)B;
+  int G = Hq / Hkv;
+  double sm = default_scale(softmax_scale, dh);
+#pragma omp parallel for schedule(dynamic)
+  for (int i = 0; i < n; ++i) {
+    int b = rows[2 * i], hq = rows[2 * i + 1];
+    int h = hq / G;
+    double qd[512];
+    for (int d = 0; d < dh; ++d) qd[d] = (double)orc_bf16_to_f32(q[((int64_t)b * Hq + hq) * dh + d]);
+    double sk = k_scale[gran == ORC_GRAN_HEAD ? h : 0];
+    double sv = v_scale[gran == ORC_GRAN_HEAD ? h : 0];
+    attend_one(out + (int64_t)i * dh, qd, context_lens[b], k_cache, v_cache,
+               block_tables + (int64_t)b * max_blocks, h, Hkv, bs, dh, sk, sv, fmt, sm);
+  }
+}
+
+/* Prefill of a chunk on top of a cached prefix, with Q quantized to E4M3 as
+ * in the FP8-domain attention path the pages describe (the guide's FA3 note;
+ * textbook 10.4.5): q_hat = s_q * cast_float(cast_fp8(q / s_q)).
+ * Sequence b owns query rows cu_seqlens[b] .. cu_seqlens[b+1]-1; its row i
+ * sits at absolute position context_lens[b] - qlen_b + i and attends keys
+ * 0..position (causal mask, R7).  The chunk's own K/V must already be in the
+ * cache.  P is kept exact (fp64).  out: fp64 [total_q][Hq][dh]. */
+static void prefill_row(double* o, const uint16_t* q, const int32_t* cu_seqlens,
+                        const float* q_scale, int q_gran, const uint8_t* k_cache,
+                        const uint8_t* v_cache, const int32_t* block_tables, int max_blocks,
+                        const int32_t* context_lens, int b, int64_t row, int hq, int Hq, int Hkv,
+                        int dh, int bs, const float* k_scale, const float* v_scale, int fmt,
+                        int kv_gran, double sm) {
+  int G = Hq / Hkv;
+  int h = hq / G;
+  int qlen = cu_seqlens[b + 1] - cu_seqlens[b];
+  int64_t i = row - cu_seqlens[b];
+  int64_t pos = (int64_t)context_lens[b] - qlen + i;
+  float sq = q_scale[q_gran == ORC_GRAN_HEAD ? hq : 0];
+  double qd[512];
+  for (int d = 0; d < dh; ++d) {
+    uint8_t c = orc_quantize(ORC_FMT_E4M3, q[(row * Hq + hq) * dh + d], sq);
+    qd[d] = (double)sq * orc_fp8_decode(ORC_FMT_E4M3, c);
+  }
+  double sk = k_scale[kv_gran == ORC_GRAN_HEAD ? h : 0];
+  double sv = v_scale[kv_gran == ORC_GRAN_HEAD ? h : 0];
+  attend_one(o, qd, (int)(pos + 1), k_cache, v_cache, block_tables + (int64_t)b * max_blocks, h,
+             Hkv, bs, dh, sk, sv, fmt, sm);
+}
+
+static int seq_of_row(const int32_t* cu_seqlens, int B, int64_t row) {
+  int b = 0;
+  while (b + 1 < B && cu_seqlens[b + 1] <= row) ++b;
+  return b;
+}
+
+void orc_prefill_attn(double* out, const uint16_t* q, const int32_t* cu_seqlens,
+                      const float* q_scale, int q_gran, const uint8_t* k_cache,
+                      const uint8_t* v_cache, const int32_t* block_tables, int max_blocks,
+                      const int32_t* context_lens, int B, int Hq, int Hkv, int dh, int bs,
+                      const float* k_scale, const float* v_scale, int fmt, int kv_gran,
+                      float softmax_scale) {
+  int64_t total = cu_seqlens[B];
+  double sm = default_scale(softmax_scale, dh);
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t row = 0; row < total; ++row)
+    for (int hq = 0; hq < Hq; ++hq) {
+      int b = seq_of_row(cu_seqlens, B, row);
+      prefill_row(out + (row * Hq + hq) * dh, q, cu_seqlens, q_scale, q_gran, k_cache, v_cache,
+                  block_tables, max_blocks, context_lens, b, row, hq, Hq, Hkv, dh, bs, k_scale,
+                  v_scale, fmt, kv_gran, sm);
+    }
+}
+
+/* Prefill for an explicit list of (row, hq) pairs only.  out: fp64 [n][dh]. */
+void orc_prefill_rows(double* out, const int64_t* rows, int n, const uint16_t* q,
+                      const int32_t* cu_seqlens, const float* q_scale, int q_gran,
+                      const uint8_t* k_cache, const uint8_t* v_cache, const int32_t* block_tables,
+                      int max_blocks, const int32_t* context_lens, int B, int Hq, int Hkv, int dh,
+                      int bs, const float* k_scale, const float* v_scale, int fmt, int kv_gran,
+                      float softmax_scale) {
+  double sm = default_scale(softmax_scale, dh);
+#pragma omp parallel for schedule(dynamic)
+  for (int i = 0; i < n; ++i) {
+    int64_t row = rows[2 * i];
+    int hq = (int)rows[2 * i + 1];
+    int b = seq_of_row(cu_seqlens, B, row);
+    prefill_row(out + (int64_t)i * dh, q, cu_seqlens, q_scale, q_gran, k_cache, v_cache,
+                block_tables, max_blocks, context_lens, b, row, hq, Hq, Hkv, dh, bs, k_scale,
+                v_scale, fmt, kv_gran, sm);
+  }
+}
+
+/* Attention of explicit fp64 queries over an explicit fp64 K/V (no cache):
+ * the plain softmax(q K^T * sm) V used to cross-check the paged paths.
+ * q [nq][dh], k/v [nk][dh], out [nq][dh]; query i attends keys 0..nk-1, or
+ * 0..(nk-nq+i) when causal. */
+void orc_dense_attn(double* out, const double* q, const double* k, const double* v, int nq,
+                    int nk, int dh, int causal, double sm) {
+  for (int i = 0; i < nq; ++i) {
+    int lim = causal ? nk - nq + i + 1 : nk;
+    double zmax = -INFINITY, l = 0.0;
+    double* z = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+    for (int j = 0; j < lim; ++j) {
+      double acc = 0.0;
+      for (int d = 0; d < dh; ++d) acc += q[(int64_t)i * dh + d] * k[(int64_t)j * dh + d];
+      z[j] = acc * sm;
+      if (z[j] > zmax) zmax = z[j];
+    }
+    for (int d = 0; d < dh; ++d) out[(int64_t)i * dh + d] = 0.0;
+    for (int j = 0; j < lim; ++j) {
+      z[j] = exp(z[j] - zmax);
+      l += z[j];
+    }
+    for (int j = 0; j < lim; ++j)
+      for (int d = 0; d < dh; ++d) out[(int64_t)i * dh + d] += z[j] / l * v[(int64_t)j * dh + d];
+    free(z);
+  }
+}
+
+/* ---- memory arithmetic ----
+ * textbook 10.4.1: M_KV = 2 * L * B * Hkv * S * dh * bytes_per_element, the
+ * leading 2 counting K and V.  bits_per_elem may be below 8 (2-bit payload). */
+uint64_t orc_kv_cache_bytes(int L, int B, int Hkv, int64_t S, int dh, int bits_per_elem) {
+  uint64_t elems = 2ull * (uint64_t)L * (uint64_t)B * (uint64_t)Hkv * (uint64_t)S * (uint64_t)dh;
+  return elems * (uint64_t)bits_per_elem / 8ull;
+}
+
+/* textbook 10.4.3: bytes one (token, head) costs for K and V together when each
+ * of K and V carries its own per-token scale of scale_bytes. */
+uint64_t orc_token_head_bytes(int dh, int bits_per_elem, int scale_bytes) {
+  return 2ull * (uint64_t)dh * (uint64_t)bits_per_elem / 8ull + 2ull * (uint64_t)scale_bytes;
+}
