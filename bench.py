@@ -1,0 +1,273 @@
+"""Benchmark of the FP8 paged KV-cache path on one MI355X.
+
+Headline workload: one decode step of a Llama-3-8B-shaped attention layer
+(B=32 sequences, Hq=32, Hkv=8, dh=128, context lengths ~ U{512..8192}, cache
+blocks of 16 tokens, per-tensor E4M3 scales = amax/448).  A step is what the
+library does for that layer per generated token: quantize-write the new
+token's K/V into the paged cache (kvq_cache_write) and run split-K paged
+decode attention over the whole cached history (kvq_decode_attn).  The scales
+are calibrated once over the prompt's K/V (kvq_calibrate_scales) before the
+timed region, as a serving engine would.
+
+Inputs are synthetic (seeded, see workloads.py) and already resident in HBM
+when timing starts.  Each timed step reads a different one of several
+identical cache copies, so the working set (> 1 GB) exceeds the 256 MB
+Infinity Cache and the HBM figure is honest.
+
+Printed: one JSON line with the headline metric, a roofline object for the
+decode kernel (algorithmic KV bytes / average kernel time from HIP events on
+the launch stream), the CPU oracle's throughput on a bounded sample, and the
+other hot-path rows (calibration, full-context write, FP8 prefill) measured
+on their own workloads after the timed loop.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 matrix peak
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--copies", type=int, default=4, help="cache copies rotated per step")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-rows", action="store_true", help="skip the extra per-row measurements")
+    p.add_argument("--cpu-sample-rows", type=int, default=0,
+                   help="(b, hq) rows in the CPU oracle sample (0 = all rows)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import quantized_kv_cache_fp8_amd as K
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def dt(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ------------------------------------------------------------ setup (untimed)
+    wl = W.llama_layer_decode()
+    B, Hq, Hkv, dh, bs = wl.B, wl.Hq, wl.Hkv, wl.dh, wl.bs
+    cl = wl.paging.context_lens
+    sum_ctx = int(cl.sum())
+    max_ctx = int(cl.max())
+    k_all, v_all = dt(wl.kv.k), dt(wl.kv.v)
+    slots_all = dt(wl.kv.slot_mapping)
+    q = dt(wl.q)
+    bt = dt(wl.paging.block_tables)
+    ctx = dt(cl)
+    ks = torch.empty(1, device=dev)
+    vs = torch.empty(1, device=dev)
+    amax = torch.empty(1, device=dev)
+    K.kvq_calibrate_scales(k_all, "fp8_e4m3", "tensor", amax, ks)
+    K.kvq_calibrate_scales(v_all, "fp8_e4m3", "tensor", amax, vs)
+    shape = (wl.paging.num_blocks, Hkv, bs, dh)
+    caches = []
+    for _ in range(args.copies):
+        kc = torch.empty(shape, dtype=torch.uint8, device=dev)
+        vc = torch.empty(shape, dtype=torch.uint8, device=dev)
+        K.kvq_cache_write(k_all, v_all, slots_all, kc, vc, ks, vs, "fp8_e4m3", "tensor")
+        caches.append((kc, vc))
+    # the step's new token of every sequence: its last position
+    last = wl.kv.seq_offsets[1:] - 1
+    k_new, v_new = k_all[torch.from_numpy(last).to(dev)], v_all[torch.from_numpy(last).to(dev)]
+    slot_new = slots_all[torch.from_numpy(last).to(dev)]
+    out = torch.empty((B, Hq, dh), dtype=torch.float32, device=dev)
+    ws_bytes = K.kvq_decode_workspace_size(B, Hq, dh, max_ctx, bs)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        kc, vc = caches[i % len(caches)]
+        K.kvq_cache_write(k_new, v_new, slot_new, kc, vc, ks, vs, "fp8_e4m3", "tensor")
+        K.kvq_decode_attn(out, q, kc, vc, bt, ctx, max_ctx, ks, vs, "fp8_e4m3", "tensor",
+                          workspace=ws)
+
+    kv_bytes = sum_ctx * Hkv * dh * 2  # FP8 K + V history read by one decode step
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # decode kernel time from HIP events on the launch stream, over the timed region
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        kc, vc = caches[i % len(caches)]
+        K.kvq_cache_write(k_new, v_new, slot_new, kc, vc, ks, vs, "fp8_e4m3", "tensor")
+        ev[i][0].record(stream)
+        K.kvq_decode_attn(out, q, kc, vc, bt, ctx, max_ctx, ks, vs, "fp8_e4m3", "tensor",
+                          workspace=ws)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (dec_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "decode-attn KV GB/s & % of HBM peak (Llama-3-8B-shaped layer); prefill TFLOP/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 cache, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "Hq": Hq, "Hkv": Hkv, "dh": dh,
+                   "block_size": bs, "sum_context": sum_ctx, "max_context": max_ctx,
+                   "kv_format": "e4m3", "scale": "per-tensor amax/448",
+                   "step": "cache_write(new token) + decode_attn", "cache_copies": args.copies,
+                   "kv_bytes_per_step": kv_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "kvq_decode_attn (split + combine)",
+                     "avg_ms": round(dec_ms, 5)},
+    }
+
+    # ------------------------------------------------------------ other rows (untimed loop)
+    if not args.no_rows:
+        result["rows"] = measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches,
+                                      ks, vs, wl)
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows)
+
+    print(json.dumps(result), flush=True)
+
+
+def time_call(torch, stream, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, vs, wl):
+    rows = {}
+    T = k_all.shape[0]
+    amax = torch.empty(1, device=dev)
+    sc = torch.empty(1, device=dev)
+
+    def calib():
+        K.kvq_calibrate_scales(k_all, "fp8_e4m3", "tensor", amax, sc)
+        K.kvq_calibrate_scales(v_all, "fp8_e4m3", "tensor", amax, sc)
+    ms = time_call(torch, stream, calib, 10)
+    nbytes = 2 * T * wl.Hkv * wl.dh * 2
+    rows["calibrate"] = {"workload": wl.name + " K+V per-tensor", "ms": round(ms, 4),
+                         "GB/s": round(nbytes / ms / 1e6, 1)}
+    kc, vc = caches[0]
+
+    def write():
+        K.kvq_cache_write(k_all, v_all, slots_all, kc, vc, ks, vs, "fp8_e4m3", "tensor")
+    ms = time_call(torch, stream, write, 10)
+    nbytes = T * (wl.Hkv * wl.dh * 2 * 2 + wl.Hkv * wl.dh * 2 + 8)
+    rows["cache_write"] = {"workload": wl.name + " full context", "ms": round(ms, 4),
+                           "GB/s": round(nbytes / ms / 1e6, 1)}
+    del kc, vc
+    # FP8-domain causal chunked prefill: 8 x (4096 cached + 4096 new), per-head scales
+    pw = W.fp8_chunked_prefill()
+
+    def dt(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q = dt(pw.q)
+    pk, pv = dt(pw.kv.k), dt(pw.kv.v)
+    qs = torch.empty(pw.Hq, device=dev)
+    pks = torch.empty(pw.Hkv, device=dev)
+    pvs = torch.empty(pw.Hkv, device=dev)
+    am = torch.empty(pw.Hq, device=dev)
+    K.kvq_calibrate_scales(q, "fp8_e4m3", "head", am, qs)
+    K.kvq_calibrate_scales(pk, "fp8_e4m3", "head", am[:pw.Hkv], pks)
+    K.kvq_calibrate_scales(pv, "fp8_e4m3", "head", am[:pw.Hkv], pvs)
+    shape = (pw.paging.num_blocks, pw.Hkv, pw.bs, pw.dh)
+    pkc = torch.empty(shape, dtype=torch.uint8, device=dev)
+    pvc = torch.empty(shape, dtype=torch.uint8, device=dev)
+    K.kvq_cache_write(pk, pv, dt(pw.kv.slot_mapping), pkc, pvc, pks, pvs, "fp8_e4m3", "head")
+    out = torch.empty((q.shape[0], pw.Hq, pw.dh), dtype=torch.float32, device=dev)
+    cu, bt, cl = dt(pw.cu_seqlens), dt(pw.paging.block_tables), dt(pw.paging.context_lens)
+    max_q = int(np.diff(pw.cu_seqlens).max())
+
+    def prefill():
+        K.kvq_prefill_attn(out, q, cu, max_q, qs, "head", pkc, pvc, bt, cl, pks, pvs,
+                           "fp8_e4m3", "head")
+    ms = time_call(torch, stream, prefill, 5)
+    flops = 0
+    for b in range(len(pw.prefix_lens)):
+        P, C = int(pw.prefix_lens[b]), int(pw.cu_seqlens[b + 1] - pw.cu_seqlens[b])
+        flops += 4 * pw.dh * pw.Hq * (C * P + C * (C + 1) // 2)
+    tf = flops / (ms * 1e-3) / 1e12
+    rows["prefill"] = {"workload": pw.name, "ms": round(ms, 4),
+                       "algorithmic_TFLOP": round(flops / 1e12, 4), "TFLOP/s": round(tf, 1),
+                       "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
+    return rows
+
+
+def cpu_baseline(wl, sample_rows):
+    """The fp64 oracle on the host: the same decode step (new-token write plus
+    decode attention) over a bounded sample of (sequence, head) rows."""
+    import oracle
+    import os as _os
+    fmt, gran = oracle.FMT_E4M3, oracle.GRAN_TENSOR
+    ks = oracle.calibrate(wl.kv.k, fmt, gran)[1]
+    vs = oracle.calibrate(wl.kv.v, fmt, gran)[1]
+    shape = (wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh)
+    kc = np.zeros(shape, np.uint8)
+    vc = np.zeros(shape, np.uint8)
+    oracle.cache_write(wl.kv.k, wl.kv.v, wl.kv.slot_mapping, kc, vc, ks, vs, fmt, gran)
+    rows = np.array([(b, h) for b in range(wl.B) for h in range(wl.Hq)], np.int32)
+    if sample_rows:
+        rows = rows[np.random.Generator(np.random.PCG64(5)).permutation(len(rows))[:sample_rows]]
+    cl = wl.paging.context_lens
+    t0 = time.perf_counter()
+    oracle.decode_rows(rows, wl.q, kc, vc, wl.paging.block_tables, cl, ks, vs, fmt, gran)
+    t = time.perf_counter() - t0
+    # bytes of the FP8 history the sampled rows read (each row reads its sequence's K and V)
+    G = wl.Hq // wl.Hkv
+    kv_bytes = float(sum(int(cl[b]) for b, _ in rows)) * wl.dh * 2 / G
+    threads = int(_os.environ.get("OMP_NUM_THREADS", _os.cpu_count() or 1))
+    return {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds": round(t, 3),
+            "sample": f"decode attention of {len(rows)} of {wl.B * wl.Hq} (sequence, head) rows "
+                      f"of the same layer, fp64, OpenMP over rows; bytes counted as the FP8 K+V "
+                      f"history those rows read (shared by the {G} heads of a group)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+/*
+ * kvq.h -- C ABI of the FP8 paged KV-cache library for AMD Instinct MI355X (gfx950).
+ *
+ * Keys and values are quantized as they are written into a paged cache of OCP
+ * FP8 codes (E4M3fn or E5M2), with one fp32 scale per tensor or per KV head,
+ * and attention reads that cache with the dequantization fused into the
+ * kernel: no bf16/fp32 copy of the cache is ever written.
+ *
+ * What each call computes is defined on these pages:
+ *   [T] "10.4 KV Cache 量化: INT8 基础、KIVI 2-bit、FP8 KV" (KV-cache
+ *       quantization textbook chapter): 10.4.1 memory formula, 10.4.2 write /
+ *       read / attention equations and the fused-dequant path, 10.4.3 scale
+ *       granularity, 10.4.5 FP8 storage and compute types.
+ *   [G] "vLLM FP8 量化 KV Cache 完整指南" (vLLM FP8 KV-cache guide): the
+ *       kv_cache_dtype formats, per-tensor / per-attention-head scale shapes,
+ *       scale sources (default 1.0), FP8 caches held as uint8 tensors, and the
+ *       FP8-domain attention path that also quantizes Q.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Memory: every pointer argument is DEVICE memory on the current HIP device,
+ *   allocated and owned by the caller.  The library allocates nothing and keeps
+ *   no state except a cached copy of the device's compute-unit count.
+ * - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *   stream).  Every call only enqueues work on that stream and returns; a
+ *   status of KVQ_OK means the arguments were valid and the launches were
+ *   accepted.  Faults inside a kernel surface at the caller's synchronize.
+ * - Validation happens on the host before any HIP call, so a call with
+ *   invalid arguments returns an error and touches no device memory.
+ * - bf16 tensors are passed as void* holding IEEE bfloat16 bit patterns.
+ * - Cache layout (this library's design; the pages fix only that FP8 caches
+ *   are raw bytes): k_cache and v_cache are uint8 [num_blocks][Hkv][bs][dh].
+ *   Token position j of sequence b lives in physical block
+ *   block_tables[b][j / bs] at offset j % bs.  Each (block, head) tile is one
+ *   contiguous bs*dh-byte run.
+ * - GQA: query head hq reads KV head hq / (Hq / Hkv).
+ * - Supported now: dh in {64, 128}; bs == 16; Hq % Hkv == 0; Hq/Hkv <= 16.
+ * - Calls are reentrant; calls on the same stream run in order.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = -1,        /* a required pointer is NULL */
+  KVQ_ERR_SHAPE = -2,       /* a size is negative, zero where it may not be, or inconsistent */
+  KVQ_ERR_UNSUPPORTED = -3, /* a valid but unimplemented value (dh, bs, group size, enum) */
+  KVQ_ERR_WORKSPACE = -4,   /* the decode workspace is smaller than kvq_decode_workspace_size */
+  KVQ_ERR_LAUNCH = -5,      /* the HIP runtime refused a launch (hipGetLastError) */
+  KVQ_ERR_DEVICE = -6       /* no usable HIP device, or it is not gfx950 */
+} kvq_status;
+
+/* Storage format of the cache codes ([G] kv_cache_dtype table: fp8 == fp8_e4m3,
+ * fp8_e5m2).  OCP E4M3fn: bias 7, max 448, no Inf, NaN = S.1111.111.
+ * OCP E5M2: bias 15, max 57344, IEEE-style Inf/NaN. */
+typedef enum { KVQ_FMT_E4M3 = 0, KVQ_FMT_E5M2 = 1 } kvq_fmt;
+
+/* Scale granularity ([T] 10.4.3 table; [G] shapes [1] vs [num_heads] /
+ * [num_kv_heads]): one fp32 scale for the whole tensor, or one per head. */
+typedef enum { KVQ_SCALE_TENSOR = 0, KVQ_SCALE_HEAD = 1 } kvq_gran;
+
+/* Element type of attention outputs. */
+typedef enum { KVQ_OUT_F32 = 0, KVQ_OUT_BF16 = 1 } kvq_out;
+
+typedef void* kvq_stream; /* hipStream_t */
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* kvq_strerror(kvq_status status);
+
+/* Bytes of a KV cache payload, [T] 10.4.1:
+ *   M_KV = 2 * L * B * Hkv * S * dh * bits_per_elem / 8
+ * (the 2 counts K and V; metadata, padding and scales are not included).
+ * Pure host arithmetic; returns 0 if any argument is negative. */
+uint64_t kvq_kv_cache_bytes(int L, int B, int Hkv, int64_t S, int dh, int bits_per_elem);
+
+/* ---------------------------------------------------------------- codec
+ * The element codec every kernel uses ([T] 10.4.5: cast_fp8 on write,
+ * cast_float on read), exposed for callers and tests.
+ *   kvq_fp8_encode: out[i] = saturating round-to-nearest-even code of x[i]
+ *     (|x| beyond max and +-Inf give +-max; NaN gives a NaN code; -0 gives
+ *     0x80; subnormal codes are produced).  x: fp32 [n], out: uint8 [n].
+ *   kvq_fp8_decode: out[i] = exact fp32 value of code[i] (NaN codes give NaN,
+ *     E5M2 Inf codes give +-Inf).  codes: uint8 [n], out: fp32 [n].
+ * n == 0 is a no-op.  Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE (n < 0),
+ * KVQ_ERR_UNSUPPORTED (fmt). */
+kvq_status kvq_fp8_encode(kvq_fmt fmt, const float* x, int64_t n, uint8_t* out,
+                          kvq_stream stream);
+kvq_status kvq_fp8_decode(kvq_fmt fmt, const uint8_t* codes, int64_t n, float* out,
+                          kvq_stream stream);
+
+/* ---------------------------------------------------------------- calibration
+ * Scale calibration ([T] 10.4.3 per-tensor / per-head; [G] scale shapes and
+ * scale sources: scales fitted to the activation range, 1.0 without one).
+ *   x: bf16 [T][H][dh].
+ *   amax = max |x| over the whole tensor (gran == KVQ_SCALE_TENSOR, arrays of
+ *     length 1) or over x[:, h, :] for each h (KVQ_SCALE_HEAD, length H).
+ *     A NaN anywhere in a set makes that amax NaN.
+ *   accumulate == 0: amax_io <- amax.  accumulate != 0: amax_io <- max(amax_io,
+ *     amax), so calibration can continue over further batches.
+ *   scale_out <- amax_io / fmax(fmt) correctly rounded in fp32 if that amax is
+ *     finite and > 0, else 1.0.
+ * T == 0 is allowed (amax of an empty set is 0).  amax_io and scale_out are
+ * fp32 device arrays.  Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE (T < 0, H < 1,
+ * dh < 1 or dh % 8), KVQ_ERR_UNSUPPORTED (fmt, gran). */
+kvq_status kvq_calibrate_scales(const void* x_bf16, int64_t T, int H, int dh, kvq_fmt fmt,
+                                kvq_gran gran, float* amax_io, float* scale_out, int accumulate,
+                                kvq_stream stream);
+
+/* ---------------------------------------------------------------- quantize-write
+ * Quantize-on-write into the paged cache ([T] 10.4.2 write rule, 10.4.5
+ * cast_fp8(K / sK)):
+ *   for every token t with 0 <= slot_mapping[t] < num_blocks * bs, every KV
+ *   head h and channel d:
+ *     cache[slot / bs][h][slot % bs][d] = fp8(fl32(x[t][h][d] / s))
+ *   with s = scale[h] (KVQ_SCALE_HEAD) or scale[0] (KVQ_SCALE_TENSOR), the
+ *   quotient correctly rounded to fp32 and fp8() the encoder above.  Tokens
+ *   whose slot is negative (padding) or out of range are skipped; no other
+ *   cache byte is touched.  Scales must lie in [2^-126, 2^126) (positive
+ *   fp32 values whose reciprocal is a normal number, as every calibrated
+ *   scale of a tensor with amax >= 2^-117 is); other values give unspecified
+ *   codes.
+ *   k, v: bf16 [T][Hkv][dh]; slot_mapping: int64 [T].
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED. */
+kvq_status kvq_cache_write(const void* k_bf16, const void* v_bf16, int64_t T, int Hkv, int dh,
+                           const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                           int64_t num_blocks, int bs, const float* k_scale,
+                           const float* v_scale, kvq_fmt fmt, kvq_gran gran, kvq_stream stream);
+
+/* ---------------------------------------------------------------- decode
+ * Bytes of device workspace kvq_decode_attn needs for these sizes (split-K
+ * partial results).  Returns 0 for invalid sizes. */
+size_t kvq_decode_workspace_size(int B, int Hq, int dh, int max_context_len, int bs);
+
+/* Paged decode attention over the FP8 cache with the dequantization fused in
+ * ([T] 10.4.2: P = softmax(Q K_hat^T / sqrt(dh)), O = P V_hat with
+ * K_hat = sK * K8, V_hat = sV * V8; the fused path of the same section).
+ *   q: bf16 [B][Hq][dh], one query per sequence: the newest token, whose own
+ *     K/V must already be in the cache.  It attends to every cached position
+ *     0 .. context_lens[b]-1 (no mask).
+ *   block_tables: int32 [B][max_blocks]; context_lens: int32 [B], read on the
+ *     device only.  max_context_len: host-side bound, >= every context_lens[b]
+ *     (larger values are clamped to it) and <= max_blocks * bs.
+ *   num_blocks: pool size; block ids outside [0, num_blocks) are clamped into
+ *     it, so a corrupt table gives wrong numbers but never an out-of-bounds read.
+ *   softmax_scale <= 0 means 1/sqrt(dh).
+ *   out: [B][Hq][dh] fp32 or bf16 (round-to-nearest-even); a sequence with
+ *     context length 0 gets an all-zero row.
+ *   workspace: device buffer of >= kvq_decode_workspace_size(...) bytes; its
+ *     contents need no initialisation and are overwritten.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE. */
+kvq_status kvq_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
+                           const uint8_t* k_cache, const uint8_t* v_cache, int64_t num_blocks,
+                           const int32_t* block_tables, int max_blocks,
+                           const int32_t* context_lens, int B, int Hq, int Hkv, int dh, int bs,
+                           int max_context_len, const float* k_scale, const float* v_scale,
+                           kvq_fmt fmt, kvq_gran gran, float softmax_scale, void* workspace,
+                           size_t ws_bytes, kvq_stream stream);
+
+/* ---------------------------------------------------------------- prefill
+ * Causal chunked prefill in the FP8 domain ([G] the FlashAttention-3 note:
+ * attention computed on FP8 operands with Q quantized too; [T] 10.4.5 storage
+ * vs compute type; [T] 10.4.2 attention with a mask):
+ *   q: bf16 [total_q][Hq][dh], variable length: sequence b owns rows
+ *     cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (int32 [B+1], cu_seqlens_q[0] = 0),
+ *     read on the device only; max_q_len bounds every chunk length on the host.
+ *   Row i of sequence b is the token at absolute position
+ *     context_lens[b] - qlen_b + i and attends keys 0..position (causal).  The
+ *     chunk's own K/V must already be in the cache (kvq_cache_write).
+ *   Q is quantized in-kernel to E4M3 with q_scale (q_gran: [1] or [Hq]):
+ *     q_hat = s_q * fp8(fl32(q / s_q)); Q K^T runs on FP8 matrix cores with
+ *     fp32 accumulation; P is fed to the P V product as two E4M3 terms
+ *     (P = (P_hi + P_lo / 16) / 256) so the FP8 product keeps about 8
+ *     significant bits of P.
+ *   out: [total_q][Hq][dh] fp32 or bf16.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED. */
+kvq_status kvq_prefill_attn(void* out, kvq_out out_dtype, const void* q_bf16,
+                            const int32_t* cu_seqlens_q, int max_q_len, const float* q_scale,
+                            kvq_gran q_gran, const uint8_t* k_cache, const uint8_t* v_cache,
+                            int64_t num_blocks, const int32_t* block_tables, int max_blocks,
+                            const int32_t* context_lens, int B, int Hq, int Hkv, int dh, int bs,
+                            const float* k_scale, const float* v_scale, kvq_fmt fmt,
+                            kvq_gran kv_gran, float softmax_scale, kvq_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -160,21 +160,23 @@ float orc_scale_from_amax(int fmt, float amax) {
 void orc_calibrate(const uint16_t* x, int64_t T, int H, int dh, int fmt, int gran,
                    float* amax_out, float* scale_out) {
   int nset = gran == ORC_GRAN_HEAD ? H : 1;
-  for (int g = 0; g < nset; ++g) {
-    double amax = 0.0;
-    int saw_nan = 0;
-    for (int64_t t = 0; t < T; ++t)
-      for (int h = 0; h < H; ++h) {
-        if (gran == ORC_GRAN_HEAD && h != g) continue;
-        for (int d = 0; d < dh; ++d) {
-          double v = fabs((double)orc_bf16_to_f32(x[(t * H + h) * dh + d]));
-          if (isnan(v)) saw_nan = 1;
-          else if (v > amax) amax = v;
-        }
+  double* amax = (double*)calloc((size_t)nset, sizeof(double));
+  int* saw_nan = (int*)calloc((size_t)nset, sizeof(int));
+  for (int64_t t = 0; t < T; ++t)
+    for (int h = 0; h < H; ++h) {
+      int g = gran == ORC_GRAN_HEAD ? h : 0; /* the set this row belongs to */
+      for (int d = 0; d < dh; ++d) {
+        double v = fabs((double)orc_bf16_to_f32(x[(t * H + h) * dh + d]));
+        if (isnan(v)) saw_nan[g] = 1;
+        else if (v > amax[g]) amax[g] = v;
       }
-    amax_out[g] = saw_nan ? NAN : (float)amax; /* |bf16| is exact in fp32 */
+    }
+  for (int g = 0; g < nset; ++g) {
+    amax_out[g] = saw_nan[g] ? NAN : (float)amax[g]; /* |bf16| is exact in fp32 */
     scale_out[g] = orc_scale_from_amax(fmt, amax_out[g]);
   }
+  free(amax);
+  free(saw_nan);
 }
 
 /* ---- paged quantize-write ----
@@ -186,10 +188,11 @@ void orc_cache_write(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv, i
                      const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
                      int64_t num_blocks, int bs, const float* k_scale, const float* v_scale,
                      int fmt, int gran) {
-  (void)num_blocks;
+  /* tokens are independent (distinct slots), so they may be written in parallel */
+#pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t) {
     int64_t slot = slot_mapping[t];
-    if (slot < 0) continue;
+    if (slot < 0 || slot >= num_blocks * bs) continue; /* padding or out-of-range: skipped */
     int64_t blk = slot / bs, off = slot % bs;
     for (int h = 0; h < Hkv; ++h) {
       float sk = k_scale[gran == ORC_GRAN_HEAD ? h : 0];

@@ -1,0 +1,175 @@
+"""FP8 paged KV cache with fused-dequant attention for AMD Instinct MI355X (gfx950).
+
+Python binding of the C-ABI library ``libkvq.so`` (declared in
+``include/kvq.h``).  The functions here carry the C names and only marshal
+arguments: they read sizes off torch tensors, pass device pointers and the
+current HIP stream, and raise :class:`KvqError` on a non-zero status.  Every
+step of the path runs in the library's HIP kernels; if the library is missing
+the import of :func:`lib` fails loudly (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvq.so")
+
+# enums of include/kvq.h
+KVQ_OK = 0
+KVQ_FMT_E4M3, KVQ_FMT_E5M2 = 0, 1
+KVQ_SCALE_TENSOR, KVQ_SCALE_HEAD = 0, 1
+KVQ_OUT_F32, KVQ_OUT_BF16 = 0, 1
+
+# kv_cache_dtype strings of the vLLM FP8 KV-cache guide ("fp8" is an alias of "fp8_e4m3")
+FMT_NAMES = {"fp8": KVQ_FMT_E4M3, "fp8_e4m3": KVQ_FMT_E4M3, "e4m3": KVQ_FMT_E4M3,
+             "fp8_e5m2": KVQ_FMT_E5M2, "e5m2": KVQ_FMT_E5M2}
+GRAN_NAMES = {"tensor": KVQ_SCALE_TENSOR, "head": KVQ_SCALE_HEAD,
+              "attn_head": KVQ_SCALE_HEAD}
+
+EXPORTS = ["kvq_strerror", "kvq_kv_cache_bytes", "kvq_fp8_encode", "kvq_fp8_decode",
+           "kvq_calibrate_scales", "kvq_cache_write", "kvq_decode_workspace_size",
+           "kvq_decode_attn", "kvq_prefill_attn"]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({kvq_strerror(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvq.so (build it first with ``python -m quantized_kv_cache_fp8_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run "
+                              "`python -m quantized_kv_cache_fp8_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        sz = ctypes.c_size_t
+        L.kvq_strerror.argtypes = [i32]
+        L.kvq_strerror.restype = ctypes.c_char_p
+        L.kvq_kv_cache_bytes.argtypes = [i32, i32, i32, i64, i32, i32]
+        L.kvq_kv_cache_bytes.restype = ctypes.c_uint64
+        L.kvq_fp8_encode.argtypes = [i32, P, i64, P, P]
+        L.kvq_fp8_decode.argtypes = [i32, P, i64, P, P]
+        L.kvq_calibrate_scales.argtypes = [P, i64, i32, i32, i32, i32, P, P, i32, P]
+        L.kvq_cache_write.argtypes = [P, P, i64, i32, i32, P, P, P, i64, i32, P, P, i32, i32, P]
+        L.kvq_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.kvq_decode_workspace_size.restype = sz
+        L.kvq_decode_attn.argtypes = [P, i32, P, P, P, i64, P, i32, P, i32, i32, i32, i32, i32,
+                                      i32, P, P, i32, i32, f32, P, sz, P]
+        L.kvq_prefill_attn.argtypes = [P, i32, P, P, i32, P, i32, P, P, i64, P, i32, P, i32, i32,
+                                       i32, i32, i32, P, P, i32, i32, f32, P]
+        _lib = L
+    return _lib
+
+
+def _fmt(f) -> int:
+    return FMT_NAMES[f] if isinstance(f, str) else int(f)
+
+
+def _gran(g) -> int:
+    return GRAN_NAMES[g] if isinstance(g, str) else int(g)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return int(stream)
+    import torch
+    if torch.cuda.is_available():
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+def _check(fn: str, st: int) -> None:
+    if st != KVQ_OK:
+        raise KvqError(fn, st)
+
+
+def kvq_strerror(status: int) -> str:
+    return lib().kvq_strerror(int(status)).decode()
+
+
+def kvq_kv_cache_bytes(L: int, B: int, Hkv: int, S: int, dh: int, bits_per_elem: int) -> int:
+    return int(lib().kvq_kv_cache_bytes(L, B, Hkv, S, dh, bits_per_elem))
+
+
+def kvq_fp8_encode(x, fmt, out, stream=None) -> None:
+    """out (uint8, same numel) <- saturating RNE codes of fp32 x."""
+    _check("kvq_fp8_encode", lib().kvq_fp8_encode(_fmt(fmt), _ptr(x), x.numel(), _ptr(out),
+                                                  _stream(stream)))
+
+
+def kvq_fp8_decode(codes, fmt, out, stream=None) -> None:
+    """out (fp32, same numel) <- exact values of uint8 codes."""
+    _check("kvq_fp8_decode", lib().kvq_fp8_decode(_fmt(fmt), _ptr(codes), codes.numel(),
+                                                  _ptr(out), _stream(stream)))
+
+
+def kvq_calibrate_scales(x, fmt, gran, amax_io, scale_out, accumulate=False, stream=None) -> None:
+    """x: bf16 [T, H, dh]; amax_io / scale_out: fp32 [1] or [H]."""
+    T, H, dh = x.shape
+    _check("kvq_calibrate_scales",
+           lib().kvq_calibrate_scales(_ptr(x), T, H, dh, _fmt(fmt), _gran(gran), _ptr(amax_io),
+                                      _ptr(scale_out), int(bool(accumulate)), _stream(stream)))
+
+
+def kvq_cache_write(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, fmt, gran,
+                    stream=None) -> None:
+    """k, v: bf16 [T, Hkv, dh]; slot_mapping int64 [T]; caches uint8 [nb, Hkv, bs, dh]."""
+    T, Hkv, dh = k.shape
+    nb, _, bs, _ = k_cache.shape
+    _check("kvq_cache_write",
+           lib().kvq_cache_write(_ptr(k), _ptr(v), T, Hkv, dh, _ptr(slot_mapping), _ptr(k_cache),
+                                 _ptr(v_cache), nb, bs, _ptr(k_scale), _ptr(v_scale), _fmt(fmt),
+                                 _gran(gran), _stream(stream)))
+
+
+def kvq_decode_workspace_size(B: int, Hq: int, dh: int, max_context_len: int, bs: int) -> int:
+    return int(lib().kvq_decode_workspace_size(B, Hq, dh, max_context_len, bs))
+
+
+def kvq_decode_attn(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                    k_scale, v_scale, fmt, gran, softmax_scale=0.0, workspace=None,
+                    stream=None) -> None:
+    """out: fp32 or bf16 [B, Hq, dh]; q bf16 [B, Hq, dh]; block_tables int32 [B, max_blocks]."""
+    import torch
+    B, Hq, dh = q.shape
+    nb, Hkv, bs, _ = k_cache.shape
+    ws_bytes = kvq_decode_workspace_size(B, Hq, dh, max_context_len, bs)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
+    _check("kvq_decode_attn",
+           lib().kvq_decode_attn(_ptr(out), out_dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), nb,
+                                 _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B,
+                                 Hq, Hkv, dh, bs, int(max_context_len), _ptr(k_scale),
+                                 _ptr(v_scale), _fmt(fmt), _gran(gran), float(softmax_scale),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)))
+
+
+def kvq_prefill_attn(out, q, cu_seqlens_q, max_q_len, q_scale, q_gran, k_cache, v_cache,
+                     block_tables, context_lens, k_scale, v_scale, fmt, kv_gran,
+                     softmax_scale=0.0, stream=None) -> None:
+    """out: fp32 or bf16 [total_q, Hq, dh]; q bf16 [total_q, Hq, dh]; cu_seqlens_q int32 [B+1]."""
+    import torch
+    _, Hq, dh = q.shape
+    nb, Hkv, bs, _ = k_cache.shape
+    B = cu_seqlens_q.shape[0] - 1
+    out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
+    _check("kvq_prefill_attn",
+           lib().kvq_prefill_attn(_ptr(out), out_dt, _ptr(q), _ptr(cu_seqlens_q), int(max_q_len),
+                                  _ptr(q_scale), _gran(q_gran), _ptr(k_cache), _ptr(v_cache), nb,
+                                  _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                  B, Hq, Hkv, dh, bs, _ptr(k_scale), _ptr(v_scale), _fmt(fmt),
+                                  _gran(kv_gran), float(softmax_scale), _stream(stream)))

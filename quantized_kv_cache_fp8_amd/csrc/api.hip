@@ -1,0 +1,194 @@
+// api.hip -- the extern "C" entry points declared in include/kvq.h.
+//
+// Every entry point validates its arguments on the host before any HIP call
+// (so invalid calls are cheap, deterministic and touch no device state), then
+// hands a launch to the kernel translation units.  Status mapping:
+// hipErrorNoDevice / wrong architecture -> KVQ_ERR_DEVICE, any other launch
+// error -> KVQ_ERR_LAUNCH.
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/kvq.h"
+#include "launch.hpp"
+
+namespace kvq {
+
+namespace {
+constexpr int kMaxDevices = 64;
+int g_cu[kMaxDevices];
+std::once_flag g_once[kMaxDevices];
+}  // namespace
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  std::call_once(g_once[dev], [dev] {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    g_cu[dev] = n;
+  });
+  return g_cu[dev];
+}
+
+static kvq_status map_err(hipError_t e) {
+  if (e == hipSuccess) return KVQ_OK;
+  if (e == hipErrorNoDevice || e == hipErrorInvalidDevice || e == hipErrorNoBinaryForGpu ||
+      e == hipErrorInvalidDeviceFunction)
+    return KVQ_ERR_DEVICE;
+  return KVQ_ERR_LAUNCH;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+static bool fmt_ok(int f) { return f == KVQ_FMT_E4M3 || f == KVQ_FMT_E5M2; }
+static bool gran_ok(int g) { return g == KVQ_SCALE_TENSOR || g == KVQ_SCALE_HEAD; }
+static bool out_ok(int o) { return o == KVQ_OUT_F32 || o == KVQ_OUT_BF16; }
+static bool dh_ok(int dh) { return dh == 64 || dh == 128; }
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+const char* kvq_strerror(kvq_status st) {
+  switch (st) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "a required pointer is NULL";
+    case KVQ_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported value (dh, block size, group size, format, "
+                                     "granularity, output type or alignment)";
+    case KVQ_ERR_WORKSPACE: return "decode workspace too small";
+    case KVQ_ERR_LAUNCH: return "HIP kernel launch failed";
+    case KVQ_ERR_DEVICE: return "no usable gfx950 HIP device";
+  }
+  return "unknown status";
+}
+
+uint64_t kvq_kv_cache_bytes(int L, int B, int Hkv, int64_t S, int dh, int bits_per_elem) {
+  if (L < 0 || B < 0 || Hkv < 0 || S < 0 || dh < 0 || bits_per_elem < 0) return 0;
+  return 2ull * (uint64_t)L * (uint64_t)B * (uint64_t)Hkv * (uint64_t)S * (uint64_t)dh *
+         (uint64_t)bits_per_elem / 8ull;
+}
+
+kvq_status kvq_fp8_encode(kvq_fmt fmt, const float* x, int64_t n, uint8_t* out,
+                          kvq_stream stream) {
+  if (!fmt_ok(fmt)) return KVQ_ERR_UNSUPPORTED;
+  if (n < 0) return KVQ_ERR_SHAPE;
+  if (n == 0) return KVQ_OK;
+  if (!x || !out) return KVQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(out, 4)) return KVQ_ERR_UNSUPPORTED;
+  return map_err(launch_fp8_encode(fmt, x, n, out, (hipStream_t)stream));
+}
+
+kvq_status kvq_fp8_decode(kvq_fmt fmt, const uint8_t* codes, int64_t n, float* out,
+                          kvq_stream stream) {
+  if (!fmt_ok(fmt)) return KVQ_ERR_UNSUPPORTED;
+  if (n < 0) return KVQ_ERR_SHAPE;
+  if (n == 0) return KVQ_OK;
+  if (!codes || !out) return KVQ_ERR_NULL;
+  if (!aligned(codes, 4) || !aligned(out, 16)) return KVQ_ERR_UNSUPPORTED;
+  return map_err(launch_fp8_decode(fmt, codes, n, out, (hipStream_t)stream));
+}
+
+kvq_status kvq_calibrate_scales(const void* x_bf16, int64_t T, int H, int dh, kvq_fmt fmt,
+                                kvq_gran gran, float* amax_io, float* scale_out, int accumulate,
+                                kvq_stream stream) {
+  if (!fmt_ok(fmt) || !gran_ok(gran)) return KVQ_ERR_UNSUPPORTED;
+  if (T < 0 || H < 1 || H > 65535 || dh < 8 || dh % 8 || dh > 2048) return KVQ_ERR_SHAPE;
+  if (!amax_io || !scale_out || (T > 0 && !x_bf16)) return KVQ_ERR_NULL;
+  if (T > 0 && !aligned(x_bf16, 16)) return KVQ_ERR_UNSUPPORTED;
+  return map_err(launch_calibrate((const uint16_t*)x_bf16, T, H, dh, fmt,
+                                  gran == KVQ_SCALE_HEAD, amax_io, scale_out, accumulate,
+                                  (hipStream_t)stream));
+}
+
+kvq_status kvq_cache_write(const void* k_bf16, const void* v_bf16, int64_t T, int Hkv, int dh,
+                           const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                           int64_t num_blocks, int bs, const float* k_scale,
+                           const float* v_scale, kvq_fmt fmt, kvq_gran gran,
+                           kvq_stream stream) {
+  if (!fmt_ok(fmt) || !gran_ok(gran)) return KVQ_ERR_UNSUPPORTED;
+  if (T < 0 || Hkv < 1 || num_blocks < 1) return KVQ_ERR_SHAPE;
+  if (!dh_ok(dh) || bs != 16 || Hkv > 256) return KVQ_ERR_UNSUPPORTED;
+  if ((uint64_t)T * (uint64_t)Hkv * (uint64_t)(dh / 8) >= (1ull << 32)) return KVQ_ERR_SHAPE;
+  if (!k_cache || !v_cache || !k_scale || !v_scale) return KVQ_ERR_NULL;
+  if (T == 0) return KVQ_OK;
+  if (!k_bf16 || !v_bf16 || !slot_mapping) return KVQ_ERR_NULL;
+  if (!aligned(k_bf16, 16) || !aligned(v_bf16, 16) || !aligned(k_cache, 8) ||
+      !aligned(v_cache, 8) || !aligned(slot_mapping, 8))
+    return KVQ_ERR_UNSUPPORTED;
+  return map_err(launch_cache_write((const uint16_t*)k_bf16, (const uint16_t*)v_bf16, T, Hkv, dh,
+                                    slot_mapping, k_cache, v_cache, num_blocks, k_scale, v_scale,
+                                    fmt, gran == KVQ_SCALE_HEAD, (hipStream_t)stream));
+}
+
+size_t kvq_decode_workspace_size(int B, int Hq, int dh, int max_context_len, int bs) {
+  return decode_plan(B, Hq, dh, max_context_len, bs).ws_bytes;
+}
+
+static kvq_status check_attn_common(const void* out, int out_dtype, const void* q,
+                                    const uint8_t* kc, const uint8_t* vc, int64_t num_blocks,
+                                    const int32_t* bt, int max_blocks, const int32_t* ctx, int B,
+                                    int Hq, int Hkv, int dh, int bs, const float* ks,
+                                    const float* vs, int fmt, int gran) {
+  if (!fmt_ok(fmt) || !gran_ok(gran) || !out_ok(out_dtype)) return KVQ_ERR_UNSUPPORTED;
+  if (B < 1 || Hq < 1 || Hkv < 1 || num_blocks < 1 || max_blocks < 1) return KVQ_ERR_SHAPE;
+  if (Hq % Hkv) return KVQ_ERR_SHAPE;
+  if (!dh_ok(dh) || bs != 16 || Hq / Hkv > 16 || B > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (!out || !q || !kc || !vc || !bt || !ctx || !ks || !vs) return KVQ_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(out, 16))
+    return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
+                           const uint8_t* k_cache, const uint8_t* v_cache, int64_t num_blocks,
+                           const int32_t* block_tables, int max_blocks,
+                           const int32_t* context_lens, int B, int Hq, int Hkv, int dh, int bs,
+                           int max_context_len, const float* k_scale, const float* v_scale,
+                           kvq_fmt fmt, kvq_gran gran, float softmax_scale, void* workspace,
+                           size_t ws_bytes, kvq_stream stream) {
+  kvq_status st = check_attn_common(out, out_dtype, q_bf16, k_cache, v_cache, num_blocks,
+                                    block_tables, max_blocks, context_lens, B, Hq, Hkv, dh, bs,
+                                    k_scale, v_scale, fmt, gran);
+  if (st != KVQ_OK) return st;
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks * bs)
+    return KVQ_ERR_SHAPE;
+  DecodePlan plan = decode_plan(B, Hq, dh, max_context_len, bs);
+  if (plan.nsplit > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (!workspace) return KVQ_ERR_NULL;
+  if (ws_bytes < plan.ws_bytes) return KVQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return KVQ_ERR_UNSUPPORTED;
+  return map_err(launch_decode(out, out_dtype == KVQ_OUT_BF16, (const uint16_t*)q_bf16, k_cache,
+                               v_cache, num_blocks, block_tables, max_blocks, context_lens, B, Hq,
+                               Hkv, dh, max_context_len, k_scale, v_scale, fmt,
+                               gran == KVQ_SCALE_HEAD, softmax_scale, plan, workspace,
+                               (hipStream_t)stream));
+}
+
+kvq_status kvq_prefill_attn(void* out, kvq_out out_dtype, const void* q_bf16,
+                            const int32_t* cu_seqlens_q, int max_q_len, const float* q_scale,
+                            kvq_gran q_gran, const uint8_t* k_cache, const uint8_t* v_cache,
+                            int64_t num_blocks, const int32_t* block_tables, int max_blocks,
+                            const int32_t* context_lens, int B, int Hq, int Hkv, int dh, int bs,
+                            const float* k_scale, const float* v_scale, kvq_fmt fmt,
+                            kvq_gran kv_gran, float softmax_scale, kvq_stream stream) {
+  kvq_status st = check_attn_common(out, out_dtype, q_bf16, k_cache, v_cache, num_blocks,
+                                    block_tables, max_blocks, context_lens, B, Hq, Hkv, dh, bs,
+                                    k_scale, v_scale, fmt, kv_gran);
+  if (st != KVQ_OK) return st;
+  if (!gran_ok(q_gran)) return KVQ_ERR_UNSUPPORTED;
+  if (max_q_len < 0) return KVQ_ERR_SHAPE;
+  if (!cu_seqlens_q || !q_scale) return KVQ_ERR_NULL;
+  if (max_q_len == 0) return KVQ_OK;
+  return map_err(launch_prefill(out, out_dtype == KVQ_OUT_BF16, (const uint16_t*)q_bf16,
+                                cu_seqlens_q, max_q_len, q_scale, q_gran == KVQ_SCALE_HEAD,
+                                k_cache, v_cache, num_blocks, block_tables, max_blocks,
+                                context_lens, B, Hq, Hkv, dh, k_scale, v_scale, fmt,
+                                kv_gran == KVQ_SCALE_HEAD, softmax_scale, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,138 @@
+// codec.hpp -- device-side FP8 element codec for gfx950 (CDNA4).
+//
+// The operation is the FP8 cache path of the KV-cache quantization textbook
+// (section 10.4.5): write cast_fp8(x / s), read cast_float(code) * s, with the
+// OCP E4M3fn / E5M2 formats named in the vLLM FP8 KV-cache guide's
+// kv_cache_dtype table.  Encoding saturates (|q| beyond max and +-Inf give
+// +-max), rounds to nearest even, keeps NaN as NaN, keeps the sign of zero and
+// produces subnormal codes.
+//
+// gfx950 converts natively between fp32 and OCP fp8/bf8 (v_cvt_pk_fp8_f32,
+// v_cvt_pk_bf8_f32, round-to-nearest-even) and from fp8/bf8 to f32, f16 and
+// bf16 (v_cvt_pk_f32_fp8, v_cvt_scalef32_pk_{f16,bf16}_{fp8,bf8}).  The only
+// extra work the encoder needs is the saturating clamp, which must let NaN
+// through: v_med3 alone would turn NaN into a finite value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+enum Fmt : int { E4M3 = 0, E5M2 = 1 };
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int FMT>
+struct FmtTraits;
+template <>
+struct FmtTraits<E4M3> {
+  static constexpr float kMax = 448.0f;
+};
+template <>
+struct FmtTraits<E5M2> {
+  static constexpr float kMax = 57344.0f;
+};
+
+// Saturating clamp that keeps NaN: med3 clamps finite values and +-Inf.
+__device__ __forceinline__ float clamp_keep_nan(float x, float m) {
+  float y = __builtin_amdgcn_fmed3f(x, -m, m);
+  return (x != x) ? x : y;
+}
+
+// Two fp32 values -> two codes in the low 16 bits (a in byte 0, b in byte 1).
+template <int FMT>
+__device__ __forceinline__ uint32_t enc2(float a, float b) {
+  const float m = FmtTraits<FMT>::kMax;
+  a = clamp_keep_nan(a, m);
+  b = clamp_keep_nan(b, m);
+  if constexpr (FMT == E4M3)
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  else
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+}
+
+// Four fp32 values -> four codes packed little-endian in one dword.
+template <int FMT>
+__device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
+  const float m = FmtTraits<FMT>::kMax;
+  a = clamp_keep_nan(a, m);
+  b = clamp_keep_nan(b, m);
+  c = clamp_keep_nan(c, m);
+  d = clamp_keep_nan(d, m);
+  int w;
+  if constexpr (FMT == E4M3) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+  }
+  return (uint32_t)w;
+}
+
+// Two codes (bytes 2*hi, 2*hi+1 of w) -> exact fp32 values.
+template <int FMT, bool HI>
+__device__ __forceinline__ f32x2 dec2_f32(uint32_t w) {
+  if constexpr (FMT == E4M3)
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  else
+    return __builtin_amdgcn_cvt_pk_f32_bf8((int)w, HI);
+}
+
+// Two codes -> two exact bf16 values (every E4M3 and E5M2 value is a bf16 value).
+template <int FMT, bool HI>
+__device__ __forceinline__ bf16x2 dec2_bf16(uint32_t w) {
+  if constexpr (FMT == E4M3)
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI);
+  else
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w, 1.0f, HI);
+}
+
+// Two codes -> two exact f16 values (every E4M3 and E5M2 value is an f16 value).
+template <int FMT, bool HI>
+__device__ __forceinline__ f16x2 dec2_f16(uint32_t w) {
+  if constexpr (FMT == E4M3)
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HI);
+  else
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_bf8((int)w, 1.0f, HI);
+}
+
+// ---------------------------------------------------------------- quotient
+// fl32(x / s) for a positive, finite, normal scale s, given rs = fl32(1 / s).
+//
+// q0 = fl32(x * rs) is within an ulp of x / s; its remainder
+// e = x - s * q0 is exact in one FMA, and q0 + e * rs rounded once is the
+// correctly rounded quotient (Markstein's correction step, IBM J. Res. Dev.
+// 34(1), 1990).  Three cases fall outside the theorem and are routed around
+// it: |q0| >= 2^16 (including Inf and overflow), where every later step
+// saturates to the format's max anyway and q0 is kept; NaN input, kept by the
+// same select; and the sign of zero, restored from x.  Quotients below 2^-126
+// may be off by an ulp there, but every such value encodes to a signed zero in
+// both formats.  The library's tests compare this against an fp64 division
+// over every bf16 input for each scale they use.
+__device__ __forceinline__ float quotient(float x, float s, float rs) {
+  float q0 = x * rs;
+  float e = __builtin_fmaf(-q0, s, x);
+  float q1 = __builtin_fmaf(e, rs, q0);
+  q1 = (__builtin_fabsf(q0) < 65536.0f) ? q1 : q0;
+  return __builtin_copysignf(q1, x);
+}
+
+// Correctly rounded reciprocal of the scale (computed once per thread).
+__device__ __forceinline__ float recip_rn(float s) { return __fdiv_rn(1.0f, s); }
+
+// bf16 bit patterns packed two per dword -> fp32 (exact).
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept as a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+}  // namespace kvq

@@ -1,0 +1,47 @@
+// launch.hpp -- host-side launchers shared between the C ABI layer (api.hip)
+// and the kernel translation units.  Arguments have been validated by the
+// caller; each launcher only sizes the grid and enqueues kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq {
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+hipError_t launch_fp8_encode(int fmt, const float* x, int64_t n, uint8_t* out, hipStream_t s);
+hipError_t launch_fp8_decode(int fmt, const uint8_t* c, int64_t n, float* out, hipStream_t s);
+
+hipError_t launch_calibrate(const uint16_t* x, int64_t T, int H, int dh, int fmt, int per_head,
+                            float* amax_io, float* scale_out, int accumulate, hipStream_t s);
+
+hipError_t launch_cache_write(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv, int dh,
+                              const int64_t* slot, uint8_t* kc, uint8_t* vc, int64_t num_blocks,
+                              const float* ks, const float* vs, int fmt, int per_head,
+                              hipStream_t s);
+
+// Split-K decode geometry, shared by the workspace query and the launch.
+struct DecodePlan {
+  int part_blocks;  // cache blocks per split
+  int nsplit;       // splits per sequence
+  size_t ws_bytes;  // workspace bytes
+};
+DecodePlan decode_plan(int B, int Hq, int dh, int max_context_len, int bs);
+
+hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8_t* kc,
+                         const uint8_t* vc, int64_t num_blocks, const int32_t* bt,
+                         int max_blocks, const int32_t* ctx, int B, int Hq, int Hkv, int dh,
+                         int max_ctx, const float* ks, const float* vs, int fmt, int per_head,
+                         float softmax_scale, const DecodePlan& plan, void* ws, hipStream_t s);
+
+hipError_t launch_prefill(void* out, int out_bf16, const uint16_t* q, const int32_t* cu,
+                          int max_q_len, const float* qs, int q_per_head, const uint8_t* kc,
+                          const uint8_t* vc, int64_t num_blocks, const int32_t* bt,
+                          int max_blocks, const int32_t* ctx, int B, int Hq, int Hkv, int dh,
+                          const float* ks, const float* vs, int fmt, int kv_per_head,
+                          float softmax_scale, hipStream_t s);
+
+}  // namespace kvq

@@ -1,0 +1,326 @@
+// prefill.hip -- causal chunked prefill attention in the FP8 domain.
+//
+// The FP8-domain attention path the vLLM FP8 KV-cache guide describes for its
+// FlashAttention-3 backend (Q quantized to FP8 like K and V, attention computed
+// on FP8 operands) and the storage-vs-compute note of the KV-cache
+// quantization textbook (section 10.4.5), applied to the attention equation
+// with a causal mask (section 10.4.2).  Both contractions run on gfx950 FP8
+// matrix cores (v_mfma_f32_32x32x64_f8f6f4, fp32 accumulation):
+//
+//   S^T = K8 . Q8^T        (A = key rows from LDS, B = quantized query rows)
+//   O^T = V8^T . P8^T      (A = value columns from LDS, B = probabilities)
+//
+// Probabilities are carried as two E4M3 terms, P_hi = e4m3(F p) and
+// P_lo = e4m3(16 (F p - P_hi)), accumulated into separate fp32 tiles and
+// recombined as (acc_hi + acc_lo / 16) / F: one E4M3 term alone keeps 4
+// significant bits of p, the pair about 8.
+//
+// Work decomposition: grid (query tiles of 32 rows, Hq / GT, sequences); a
+// workgroup has GT waves, one per query head of a GQA group, so every K/V tile
+// staged in LDS serves all GT heads.  Query tiles are issued longest-first
+// (the causal triangle makes late tiles the most expensive).  Per 64-key tile:
+// the workgroup copies K (4 cache blocks) into LDS row-major and V transposed
+// (channel-major, keys permuted into the order the B operand holds P in, so
+// each lane's A operand is one 32-byte run), then each wave runs 2*DH/64
+// MFMAs for S^T, the online softmax in registers (one query per lane pair,
+// the running max only raised when a score exceeds it by more than 2^2), and
+// 2*DH/32 MFMAs for O^T.
+#include "codec.hpp"
+#include "launch.hpp"
+
+namespace kvq {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace {
+constexpr int kQT = 32;          // query rows per wave
+constexpr int kKT = 64;          // keys per tile
+constexpr float kTau = 2.0f;     // lazy-max headroom (log2)
+constexpr float kPF = 64.0f;     // F = 2^(8 - tau): F * p <= 256
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;
+
+// position of key k (0..63) inside a transposed V row: keys are stored in the
+// order lane group g = (k>>2)&1 reads them, byte j = 16*(k>>5) + 4*((k>>3)&3) + (k&3)
+__device__ __forceinline__ int vt_pos(int k) {
+  return 32 * ((k >> 2) & 1) + 16 * (k >> 5) + 4 * ((k >> 3) & 3) + (k & 3);
+}
+
+template <int FMT>
+constexpr int mfma_fmt() { return FMT == E4M3 ? 0 : 1; }  // cbsz/blgp: 0 = fp8, 1 = bf8
+}  // namespace
+
+template <int FMT, int DH, int GT>
+__global__ __launch_bounds__(64 * GT) void prefill_kernel(
+    void* __restrict__ out, int out_bf16, const uint16_t* __restrict__ q,
+    const int32_t* __restrict__ cu, int n_qtiles, const float* __restrict__ qs, int q_per_head,
+    const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc, int64_t num_blocks,
+    const int32_t* __restrict__ bt, int max_blocks, const int32_t* __restrict__ ctx_lens, int Hq,
+    int Hkv, const float* __restrict__ ks, const float* __restrict__ vs, int kv_per_head,
+    float sm_scale) {
+  constexpr int NT = 64 * GT;          // threads
+  constexpr int KROW = DH + 16;        // padded K row in LDS (bytes)
+  constexpr int VROW = kKT + 16;       // padded transposed-V row in LDS (bytes)
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kKT * KROW];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[DH * VROW];
+
+  const int qt = n_qtiles - 1 - (int)blockIdx.x;  // longest tiles first
+  const int grp = blockIdx.y, b = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int gpk = G / GT;
+  const int h = grp / gpk;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hq = h * G + (grp - h * gpk) * GT + wave;
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 31, g = lane >> 5;
+
+  const int q0 = cu[b];
+  const int qlen = cu[b + 1] - q0;
+  if (qt * kQT >= qlen) return;
+  int ctx = ctx_lens[b];
+  const int ctx_cap = max_blocks * 16;
+  ctx = ctx < 0 ? 0 : (ctx > ctx_cap ? ctx_cap : ctx);
+  const int nblk_ctx = (ctx + 15) / 16;
+  const int qi = qt * kQT + c;                       // this lane's query (chunk index)
+  const bool qvalid = qi < qlen;
+  const int pos = qvalid ? ctx - qlen + qi : -1;      // absolute position; keys 0..pos
+  const int last_q = (qt * kQT + kQT - 1 < qlen - 1) ? qt * kQT + kQT - 1 : qlen - 1;
+  const int pos_max = ctx - qlen + last_q;
+  const int pos_min = ctx - qlen + qt * kQT;
+  const int nkt = pos_max < 0 ? 0 : (pos_max + kKT) / kKT;
+
+  // ---- quantize this wave's query rows to E4M3 (B operand of S^T)
+  const float sq = qs[q_per_head ? hq : 0];
+  const float rsq = recip_rn(sq);
+  i32x8 qb[DH / 64];
+  {
+    const uint16_t* qp = q + ((size_t)(q0 + qi) * Hq + hq) * DH;
+#pragma unroll
+    for (int m = 0; m < DH / 64; ++m) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // 4 x 8 channels = bytes [64m + 32g, +32)
+        uint4 w = qvalid ? *reinterpret_cast<const uint4*>(qp + 64 * m + 32 * g + 8 * j)
+                         : make_uint4(0, 0, 0, 0);
+        qb[m][2 * j] = (int)enc4<E4M3>(quotient(bf16lo(w.x), sq, rsq), quotient(bf16hi(w.x), sq, rsq),
+                                       quotient(bf16lo(w.y), sq, rsq), quotient(bf16hi(w.y), sq, rsq));
+        qb[m][2 * j + 1] = (int)enc4<E4M3>(quotient(bf16lo(w.z), sq, rsq), quotient(bf16hi(w.z), sq, rsq),
+                                           quotient(bf16lo(w.w), sq, rsq), quotient(bf16hi(w.w), sq, rsq));
+      }
+    }
+  }
+  // log2-domain score = raw * sq * sk / sqrt(dh) * log2(e)
+  const float zc = sm_scale * sq * ks[kv_per_head ? h : 0] * kLog2e;
+
+  f32x16 acc_hi[DH / 32], acc_lo[DH / 32];
+#pragma unroll
+  for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { acc_hi[dt][v] = 0.0f; acc_lo[dt][v] = 0.0f; }
+  float m_run = kNegBig, l_run = 0.0f;
+
+  const int32_t* btab = bt + (size_t)b * max_blocks;
+  const size_t tile_stride = (size_t)16 * DH;
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    __syncthreads();  // previous tile fully consumed
+    // ---- K tile -> LDS, row-major: thread covers 32 bytes of one key
+    for (int u = threadIdx.x; u < kKT * (DH / 32); u += NT) {
+      const int key = u / (DH / 32), ch = u % (DH / 32);
+      const int bi = kt * 4 + (key >> 4);
+      uint4 a = make_uint4(0, 0, 0, 0), bq = make_uint4(0, 0, 0, 0);
+      if (bi < nblk_ctx) {
+        int64_t blk = btab[bi];
+        blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
+        const uint8_t* src = kc + ((size_t)blk * Hkv + h) * tile_stride + (key & 15) * DH + ch * 32;
+        a = *reinterpret_cast<const uint4*>(src);
+        bq = *reinterpret_cast<const uint4*>(src + 16);
+      }
+      *reinterpret_cast<uint4*>(k_lds + key * KROW + ch * 32) = a;
+      *reinterpret_cast<uint4*>(k_lds + key * KROW + ch * 32 + 16) = bq;
+    }
+    // ---- V tile -> LDS transposed: thread takes 4 keys x 4 channels, 4x4 byte transpose
+    for (int u = threadIdx.x; u < (kKT / 4) * (DH / 4); u += NT) {
+      const int kq = u / (DH / 4), dc = u % (DH / 4);
+      const int k0 = kq * 4;
+      const int bi = kt * 4 + (k0 >> 4);
+      uint32_t r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+      if (bi < nblk_ctx) {
+        int64_t blk = btab[bi];
+        blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
+        const uint8_t* src = vc + ((size_t)blk * Hkv + h) * tile_stride + (k0 & 15) * DH + dc * 4;
+        r0 = *reinterpret_cast<const uint32_t*>(src);
+        r1 = *reinterpret_cast<const uint32_t*>(src + DH);
+        r2 = *reinterpret_cast<const uint32_t*>(src + 2 * DH);
+        r3 = *reinterpret_cast<const uint32_t*>(src + 3 * DH);
+      }
+      // rows r0..r3 = keys k0..k0+3, bytes = channels 4dc..4dc+3
+      const uint32_t t0 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);  // a0 b0 a1 b1
+      const uint32_t t1 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);  // a2 b2 a3 b3
+      const uint32_t t2 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);  // c0 d0 c1 d1
+      const uint32_t t3 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);  // c2 d2 c3 d3
+      const int p = vt_pos(k0);
+      uint8_t* dst = v_lds + (dc * 4) * VROW + p;
+      *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+      *reinterpret_cast<uint32_t*>(dst + VROW) = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+      *reinterpret_cast<uint32_t*>(dst + 2 * VROW) = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+      *reinterpret_cast<uint32_t*>(dst + 3 * VROW) = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for keys [64kt, 64kt + 64)
+    f32x16 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[t][v] = 0.0f;
+#pragma unroll
+      for (int m = 0; m < DH / 64; ++m) {
+        const uint8_t* ap = k_lds + (32 * t + c) * KROW + 64 * m + 32 * g;
+        const uint4 a0 = *reinterpret_cast<const uint4*>(ap);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16);
+        i32x8 A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                   (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        s[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, qb[m], s[t], mfma_fmt<FMT>(), 0,
+                                                               0, 0, 0, 0);
+      }
+    }
+
+    // ---- online softmax for this lane's query (column c); lane holds keys
+    //      64kt + 32t + 8(v/4) + 4g + (v%4)
+    const bool need_mask = kt * kKT + kKT - 1 > pos_min;
+    float tmax = kNegBig;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float z = s[t][v] * zc;
+        if (need_mask) {
+          const int key = kt * kKT + 32 * t + 8 * (v >> 2) + 4 * g + (v & 3);
+          z = key <= pos ? z : -__builtin_inff();
+        }
+        s[t][v] = z;
+        tmax = __builtin_fmaxf(tmax, z);
+      }
+    tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+    if (tmax > m_run + kTau) {
+      const float f = __builtin_amdgcn_exp2f(m_run - tmax);
+      l_run *= f;
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { acc_hi[dt][v] *= f; acc_lo[dt][v] *= f; }
+      m_run = tmax;
+    }
+    i32x8 ph, pl;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        float fp[4], lo[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(s[t][4 * v4 + r] - m_run);
+          l_run += p;
+          fp[r] = p * kPF;
+        }
+        const uint32_t hi = enc4<E4M3>(fp[0], fp[1], fp[2], fp[3]);
+        const f32x2 h01 = dec2_f32<E4M3, false>(hi), h23 = dec2_f32<E4M3, true>(hi);
+        lo[0] = (fp[0] - h01.x) * 16.0f;
+        lo[1] = (fp[1] - h01.y) * 16.0f;
+        lo[2] = (fp[2] - h23.x) * 16.0f;
+        lo[3] = (fp[3] - h23.y) * 16.0f;
+        ph[4 * t + v4] = (int)hi;
+        pl[4 * t + v4] = (int)enc4<E4M3>(lo[0], lo[1], lo[2], lo[3]);
+      }
+
+    // ---- O^T += V^T P^T for channel tiles of 32
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt) {
+      const uint8_t* ap = v_lds + (32 * dt + c) * VROW + 32 * g;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(ap);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16);
+      i32x8 A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                 (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      acc_hi[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, ph, acc_hi[dt],
+                                                                   mfma_fmt<FMT>(), 0, 0, 0, 0, 0);
+      acc_lo[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, pl, acc_lo[dt],
+                                                                   mfma_fmt<FMT>(), 0, 0, 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue: O = (acc_hi + acc_lo/16) / (F * l) * sV; lane holds
+  //      channels 32dt + 8i + 4g + r of query c
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!qvalid) return;
+  const float sv = vs[kv_per_head ? h : 0];
+  const float scale = l_tot > 0.0f ? sv / (l_tot * kPF) : 0.0f;
+  const size_t orow = ((size_t)(q0 + qi) * Hq + hq) * DH;
+#pragma unroll
+  for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        o[r] = (acc_hi[dt][4 * i + r] + acc_lo[dt][4 * i + r] * 0.0625f) * scale;
+      const int d = 32 * dt + 8 * i + 4 * g;
+      if (out_bf16) {
+        uint2 w;
+        w.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
+        w.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + orow + d) = w;
+      } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + orow + d) =
+            make_float4(o[0], o[1], o[2], o[3]);
+      }
+    }
+}
+
+template <int FMT, int DH>
+static void launch_prefill_gt(int GT, dim3 grid, hipStream_t s, void* out, int out_bf16,
+                              const uint16_t* q, const int32_t* cu, int nqt, const float* qs,
+                              int qph, const uint8_t* kc, const uint8_t* vc, int64_t nb,
+                              const int32_t* bt, int mb, const int32_t* ctx, int Hq, int Hkv,
+                              const float* ks, const float* vs, int kvph, float sm) {
+  if (GT == 4)
+    prefill_kernel<FMT, DH, 4><<<grid, 256, 0, s>>>(out, out_bf16, q, cu, nqt, qs, qph, kc, vc, nb,
+                                                    bt, mb, ctx, Hq, Hkv, ks, vs, kvph, sm);
+  else if (GT == 2)
+    prefill_kernel<FMT, DH, 2><<<grid, 128, 0, s>>>(out, out_bf16, q, cu, nqt, qs, qph, kc, vc, nb,
+                                                    bt, mb, ctx, Hq, Hkv, ks, vs, kvph, sm);
+  else
+    prefill_kernel<FMT, DH, 1><<<grid, 64, 0, s>>>(out, out_bf16, q, cu, nqt, qs, qph, kc, vc, nb,
+                                                   bt, mb, ctx, Hq, Hkv, ks, vs, kvph, sm);
+}
+
+hipError_t launch_prefill(void* out, int out_bf16, const uint16_t* q, const int32_t* cu,
+                          int max_q_len, const float* qs, int q_per_head, const uint8_t* kc,
+                          const uint8_t* vc, int64_t num_blocks, const int32_t* bt,
+                          int max_blocks, const int32_t* ctx, int B, int Hq, int Hkv, int dh,
+                          const float* ks, const float* vs, int fmt, int kv_per_head,
+                          float softmax_scale, hipStream_t s) {
+  const int G = Hq / Hkv;
+  const int GT = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
+  const int nqt = (max_q_len + kQT - 1) / kQT;
+  const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / __builtin_sqrtf((float)dh);
+  dim3 grid(nqt, Hq / GT, B);
+  if (fmt == E4M3) {
+    if (dh == 128)
+      launch_prefill_gt<E4M3, 128>(GT, grid, s, out, out_bf16, q, cu, nqt, qs, q_per_head, kc, vc,
+                                   num_blocks, bt, max_blocks, ctx, Hq, Hkv, ks, vs, kv_per_head, sm);
+    else
+      launch_prefill_gt<E4M3, 64>(GT, grid, s, out, out_bf16, q, cu, nqt, qs, q_per_head, kc, vc,
+                                  num_blocks, bt, max_blocks, ctx, Hq, Hkv, ks, vs, kv_per_head, sm);
+  } else {
+    if (dh == 128)
+      launch_prefill_gt<E5M2, 128>(GT, grid, s, out, out_bf16, q, cu, nqt, qs, q_per_head, kc, vc,
+                                   num_blocks, bt, max_blocks, ctx, Hq, Hkv, ks, vs, kv_per_head, sm);
+    else
+      launch_prefill_gt<E5M2, 64>(GT, grid, s, out, out_bf16, q, cu, nqt, qs, q_per_head, kc, vc,
+                                  num_blocks, bt, max_blocks, ctx, Hq, Hkv, ks, vs, kv_per_head, sm);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq

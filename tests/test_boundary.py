@@ -1,0 +1,120 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function include/kvq.h declares, and rejects invalid arguments with the
+documented status before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_kv_cache_fp8_amd as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+FAKE = 0x10000  # a non-NULL pointer value; only ever passed to calls that must fail validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["kvq_calibrate_scales", "kvq_cache_write", "kvq_decode_attn", "kvq_prefill_attn",
+              "kvq_decode_workspace_size", "kvq_kv_cache_bytes", "kvq_strerror"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = K.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(declared_functions()) == set(K.EXPORTS)
+
+
+def test_strerror_covers_every_status():
+    for st in range(-6, 1):
+        assert K.kvq_strerror(st) and K.kvq_strerror(st) != "unknown status"
+    assert K.kvq_strerror(-99) == "unknown status"
+
+
+def test_kv_cache_bytes_worked_example():
+    # KV-cache quantization textbook 10.4.1: 4 GiB bf16, 2 GiB FP8 for this shape
+    assert K.kvq_kv_cache_bytes(32, 1, 8, 32768, 128, 16) == 4 << 30
+    assert K.kvq_kv_cache_bytes(32, 1, 8, 32768, 128, 8) == 2 << 30
+    assert K.kvq_kv_cache_bytes(32, 1, 8, 32768, 128, 2) == 1 << 29
+    assert K.kvq_kv_cache_bytes(-1, 1, 8, 32768, 128, 8) == 0
+
+
+def test_workspace_size_is_positive_and_monotone():
+    a = K.kvq_decode_workspace_size(32, 32, 128, 8192, 16)
+    b = K.kvq_decode_workspace_size(32, 32, 128, 16384, 16)
+    assert 0 < a <= b
+    assert K.kvq_decode_workspace_size(0, 32, 128, 8192, 16) == 0
+    # (m, l) pair plus dh partial sums per (b, hq, split)
+    assert a % (32 * 32 * (128 + 2) * 4) == 0
+
+
+def status_of_decode(**over):
+    L = K.lib()
+    args = dict(out=FAKE, odt=0, q=FAKE, kc=FAKE, vc=FAKE, nb=10, bt=FAKE, mb=4, cl=FAKE, B=2,
+                Hq=8, Hkv=2, dh=128, bs=16, maxctx=64, ks=FAKE, vs=FAKE, fmt=0, gran=0, sm=0.0,
+                ws=FAKE, wsb=0, stream=None)
+    args.update(over)
+    return L.kvq_decode_attn(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), -1), (dict(ks=None), -1), (dict(bt=None), -1), (dict(ws=None, wsb=1 << 20), -1),
+    (dict(Hq=6, Hkv=4), -2), (dict(B=0), -2), (dict(maxctx=65), -2), (dict(maxctx=-1), -2),
+    (dict(nb=0), -2), (dict(dh=96), -3), (dict(bs=32), -3), (dict(fmt=2), -3), (dict(gran=5), -3),
+    (dict(odt=3), -3), (dict(Hq=64, Hkv=2), -3), (dict(wsb=16), -4),
+])
+def test_decode_validation(over, status):
+    assert status_of_decode(**over) == status
+
+
+def test_write_validation():
+    L = K.lib()
+    base = [FAKE, FAKE, 4, 2, 128, FAKE, FAKE, FAKE, 8, 16, FAKE, FAKE, 0, 0, None]
+    def st(**kw):
+        a = list(base)
+        idx = dict(k=0, v=1, T=2, Hkv=3, dh=4, slots=5, kc=6, vc=7, nb=8, bs=9, ks=10, vs=11,
+                   fmt=12, gran=13)
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return L.kvq_cache_write(*a)
+    assert st(kc=None) == -1 and st(slots=None) == -1 and st(ks=None) == -1
+    assert st(T=-1) == -2 and st(nb=0) == -2 and st(Hkv=0) == -2
+    assert st(dh=80) == -3 and st(bs=8) == -3 and st(fmt=7) == -3
+    assert st(k=FAKE + 2) == -3  # misaligned
+    assert st(T=0) == 0  # empty batch: nothing to launch
+
+
+def test_calibrate_and_codec_validation():
+    L = K.lib()
+    assert L.kvq_calibrate_scales(FAKE, 4, 2, 128, 0, 0, None, FAKE, 0, None) == -1
+    assert L.kvq_calibrate_scales(FAKE, -4, 2, 128, 0, 0, FAKE, FAKE, 0, None) == -2
+    assert L.kvq_calibrate_scales(FAKE, 4, 2, 12, 0, 0, FAKE, FAKE, 0, None) == -2
+    assert L.kvq_calibrate_scales(FAKE, 4, 2, 128, 3, 0, FAKE, FAKE, 0, None) == -3
+    assert L.kvq_fp8_encode(0, None, 8, FAKE, None) == -1
+    assert L.kvq_fp8_encode(0, FAKE, -8, FAKE, None) == -2
+    assert L.kvq_fp8_encode(0, FAKE, 0, FAKE, None) == 0
+    assert L.kvq_fp8_decode(9, FAKE, 8, FAKE, None) == -3
+
+
+def test_prefill_validation():
+    L = K.lib()
+    base = dict(out=FAKE, odt=0, q=FAKE, cu=FAKE, maxq=8, qs=FAKE, qg=0, kc=FAKE, vc=FAKE, nb=4,
+                bt=FAKE, mb=4, cl=FAKE, B=1, Hq=8, Hkv=2, dh=128, bs=16, ks=FAKE, vs=FAKE, fmt=0,
+                kvg=0, sm=0.0, stream=None)
+    def st(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.kvq_prefill_attn(*a.values())
+    assert st(cu=None) == -1 and st(qs=None) == -1
+    assert st(maxq=-1) == -2 and st(Hq=7) == -2
+    assert st(qg=4) == -3 and st(dh=256) == -3
+    assert st(maxq=0) == 0

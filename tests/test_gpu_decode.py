@@ -1,0 +1,110 @@
+"""GPU parity of split-K paged decode attention against the oracle.
+
+Bar: max |o - r| / max |r| <= 2e-3 over the whole output and over every
+(sequence, head) row, with fp32 output; the bf16 output must be exactly the
+fp32 output rounded to nearest even.  Every case first checks the cache bytes
+bit-exactly.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from helpers import ATTN_TOL, DecodeRun, rel_err, row_rel_err, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(wl, check_cache=True):
+    run = DecodeRun(wl)
+    run.gpu_scales()
+    run.gpu_write()
+    kc, vc = run.oracle_caches()
+    if check_cache:
+        assert np.array_equal(to_np(run.kc), kc) and np.array_equal(to_np(run.vc), vc)
+    out = run.gpu_decode()
+    ref = oracle.decode_attn(wl.q, kc, vc, wl.paging.block_tables, wl.paging.context_lens,
+                             run.ks_ref, run.vs_ref, run.fmt, run.gran)
+    return run, out, ref
+
+
+def check(out, ref):
+    e, er = rel_err(out, ref), row_rel_err(out, ref)
+    print(f"global rel err {e:.3e}  worst row {er:.3e}", flush=True)
+    assert e <= ATTN_TOL and er <= ATTN_TOL
+
+
+def test_tiny_decode():
+    """B=1, Hq=4, Hkv=2, dh=64, context 256 in 16 shuffled blocks, scale 1.0, E4M3."""
+    wl = W.tiny_decode()
+    _, out, ref = run_case(wl)
+    check(out, ref)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("gran", ["tensor", "head"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_ragged_batch(fmt, gran, out_dtype):
+    """Ragged contexts (1 .. 1500 tokens: partial blocks, partial splits, a
+    single-token context) for a Llama-shaped GQA group of 4."""
+    cl = [1, 15, 16, 17, 255, 513, 1031, 1500]
+    wl = W.decode_workload("ragged", 101, len(cl), 32, 8, 128, cl, 16, fmt, gran,
+                           k_outliers=(4, 10.0), v_outliers=(4, 10.0), head_range=(0.5, 20.0))
+    run, out, ref = run_case(wl)
+    check(out, ref)
+    if out_dtype == "bf16":
+        # the bf16 output is the fp32 result rounded to nearest even, element by element
+        import torch
+        run.out = torch.empty(run.out.shape, dtype=torch.bfloat16, device=run.out.device)
+        assert np.array_equal(run.gpu_decode(), W.f32_to_bf16_bits(out))
+
+
+@pytest.mark.parametrize("Hq,Hkv,dh", [(8, 8, 128), (16, 8, 64), (12, 4, 128), (64, 8, 128),
+                                       (6, 2, 64), (5, 5, 64)])
+def test_group_sizes_and_head_dims(Hq, Hkv, dh):
+    cl = [700, 33, 129]
+    wl = W.decode_workload("groups", 102 + Hq, len(cl), Hq, Hkv, dh, cl, 16, "e4m3", "head",
+                           head_range=(0.5, 20.0))
+    _, out, ref = run_case(wl)
+    check(out, ref)
+
+
+def test_zero_length_context_gives_zero_row():
+    wl = W.decode_workload("zero", 103, 3, 8, 2, 128, [40, 0, 5], 16, "e4m3", "tensor")
+    _, out, ref = run_case(wl)
+    assert np.all(out[1] == 0) and np.all(ref[1] == 0)
+    check(out, ref)
+
+
+def test_result_does_not_depend_on_the_split_plan():
+    """A larger host bound changes the number of splits; the output stays within rounding."""
+    wl = W.decode_workload("plan", 104, 2, 32, 8, 128, [3000, 2000], 16, "e4m3", "tensor")
+    run = DecodeRun(wl)
+    run.gpu_scales()
+    run.gpu_write()
+    a = run.gpu_decode()
+    b = run.gpu_decode(max_ctx=int(wl.paging.block_tables.shape[1]) * 16)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-5 * np.abs(a).max())
+
+
+@pytest.mark.parametrize("which", ["llama", "long-e4m3", "long-e5m2"])
+def test_full_size_sampled_rows(which):
+    """Full-size workloads; the oracle computes a seeded sample of rows
+    (every sequence's first and last head plus random pairs)."""
+    wl = {"llama": W.llama_layer_decode, "long-e4m3": lambda: W.long_context_decode("e4m3"),
+          "long-e5m2": lambda: W.long_context_decode("e5m2")}[which]()
+    print(f"[{which}] B={wl.B} tokens={wl.kv.k.shape[0]}", flush=True)
+    run = DecodeRun(wl)
+    run.gpu_scales()
+    run.gpu_write()
+    out = run.gpu_decode()
+    kc, vc = run.oracle_caches()
+    g = W.rng(55)
+    rows = [(b, 0) for b in range(wl.B)] + [(b, wl.Hq - 1) for b in range(wl.B)]
+    rows += [(int(g.integers(wl.B)), int(g.integers(wl.Hq))) for _ in range(32)]
+    rows = np.array(rows, np.int32)
+    ref = oracle.decode_rows(rows, wl.q, kc, vc, wl.paging.block_tables, wl.paging.context_lens,
+                             run.ks_ref, run.vs_ref, run.fmt, run.gran)
+    got = out[rows[:, 0], rows[:, 1]]
+    check(got, ref)
+    assert np.all(np.isfinite(out))

@@ -1,0 +1,144 @@
+"""GPU parity of the FP8-domain causal chunked prefill against the oracle.
+
+The oracle quantizes Q to E4M3 exactly as the kernel does and keeps P exact;
+the kernel carries P as two E4M3 terms on FP8 matrix cores.  Bar:
+max |o - r| / max |r| <= 2e-3 over the output (per-row error is printed).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from helpers import ATTN_TOL, FMT_ID, SENTINEL, rel_err, row_rel_err, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+class PrefillRun:
+    def __init__(self, wl, q_gran="head", kv_gran="head", out_dtype="f32"):
+        import torch
+        import quantized_kv_cache_fp8_amd as K
+        self.wl, self.K = wl, K
+        self.fmt = FMT_ID[wl.fmt]
+        self.qg = oracle.GRAN_HEAD if q_gran == "head" else oracle.GRAN_TENSOR
+        self.kg = oracle.GRAN_HEAD if kv_gran == "head" else oracle.GRAN_TENSOR
+        # scales: Q always E4M3; K/V in the cache format, calibrated over prefix + chunk
+        self.qs_ref = oracle.calibrate(wl.q, oracle.FMT_E4M3, self.qg)[1]
+        self.ks_ref = oracle.calibrate(wl.kv.k, self.fmt, self.kg)[1]
+        self.vs_ref = oracle.calibrate(wl.kv.v, self.fmt, self.kg)[1]
+        dev = torch.device("cuda:0")
+        self.q = to_dev(wl.q)
+        shape = (wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh)
+        self.kc = torch.full(shape, SENTINEL, dtype=torch.uint8, device=dev)
+        self.vc = torch.full(shape, SENTINEL, dtype=torch.uint8, device=dev)
+        nq = wl.Hq if self.qg == oracle.GRAN_HEAD else 1
+        nk = wl.Hkv if self.kg == oracle.GRAN_HEAD else 1
+        self.qs = torch.empty(nq, device=dev)
+        self.ks = torch.empty(nk, device=dev)
+        self.vs = torch.empty(nk, device=dev)
+        amax = torch.empty(max(nq, nk), device=dev)
+        k, v = to_dev(wl.kv.k), to_dev(wl.kv.v)
+        K.kvq_calibrate_scales(self.q, oracle.FMT_E4M3, self.qg, amax[:nq], self.qs)
+        K.kvq_calibrate_scales(k, self.fmt, self.kg, amax[:nk], self.ks)
+        K.kvq_calibrate_scales(v, self.fmt, self.kg, amax[:nk], self.vs)
+        K.kvq_cache_write(k, v, to_dev(wl.kv.slot_mapping), self.kc, self.vc, self.ks, self.vs,
+                          self.fmt, self.kg)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(self.qs), self.qs_ref)
+        assert np.array_equal(to_np(self.ks), self.ks_ref)
+        self.bt = to_dev(wl.paging.block_tables)
+        self.cl = to_dev(wl.paging.context_lens)
+        self.cu = to_dev(wl.cu_seqlens)
+        odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+        self.out = torch.empty((wl.q.shape[0], wl.Hq, wl.dh), dtype=odt, device=dev)
+        self.max_q = int(np.diff(wl.cu_seqlens).max())
+
+    def gpu(self):
+        import torch
+        self.K.kvq_prefill_attn(self.out, self.q, self.cu, self.max_q, self.qs, self.qg, self.kc,
+                                self.vc, self.bt, self.cl, self.ks, self.vs, self.fmt, self.kg)
+        torch.cuda.synchronize()
+        return to_np(self.out)
+
+    def oracle_caches(self):
+        wl = self.wl
+        shape = (wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh)
+        kc = np.full(shape, SENTINEL, np.uint8)
+        vc = np.full(shape, SENTINEL, np.uint8)
+        oracle.cache_write(wl.kv.k, wl.kv.v, wl.kv.slot_mapping, kc, vc, self.ks_ref, self.vs_ref,
+                           self.fmt, self.kg)
+        return kc, vc
+
+    def oracle_full(self):
+        kc, vc = self.oracle_caches()
+        wl = self.wl
+        return oracle.prefill_attn(wl.q, wl.cu_seqlens, self.qs_ref, self.qg, kc, vc,
+                                   wl.paging.block_tables, wl.paging.context_lens, self.ks_ref,
+                                   self.vs_ref, self.fmt, self.kg)
+
+
+def check(out, ref):
+    e, er = rel_err(out, ref), row_rel_err(out, ref)
+    print(f"global rel err {e:.3e}  worst row {er:.3e}", flush=True)
+    assert e <= ATTN_TOL
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("dh", [128, 64])
+def test_small_ragged_chunks(fmt, dh):
+    """Chunks shorter than a query tile, an empty prefix, a one-token chunk."""
+    wl = W.prefill_workload("small", 201, [20, 0, 16, 100], [13, 9, 1, 40], 8, 2, dh, 16, fmt)
+    run = PrefillRun(wl)
+    check(run.gpu(), run.oracle_full())
+
+
+@pytest.mark.parametrize("q_gran,kv_gran", [("tensor", "tensor"), ("head", "tensor"),
+                                            ("tensor", "head")])
+def test_scale_granularities(q_gran, kv_gran):
+    wl = W.prefill_workload("gran", 202, [300, 77], [200, 130], 32, 8, 128, 16, "e4m3")
+    run = PrefillRun(wl, q_gran, kv_gran)
+    check(run.gpu(), run.oracle_full())
+
+
+def test_bf16_output():
+    """The bf16 output is the fp32 result rounded to nearest even, element by element."""
+    wl = W.prefill_workload("bf16", 203, [64, 31], [96, 50], 16, 4, 128, 16, "e4m3")
+    f32 = PrefillRun(wl).gpu()
+    check(f32, PrefillRun(wl).oracle_full())
+    b16 = PrefillRun(wl, out_dtype="bf16").gpu()
+    assert np.array_equal(b16, W.f32_to_bf16_bits(f32))
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_group_sizes(G):
+    wl = W.prefill_workload("g", 204 + G, [50, 130], [70, 33], 8 * G if G < 8 else 16, 8 if G < 8 else 2,
+                            128, 16, "e4m3")
+    run = PrefillRun(wl)
+    check(run.gpu(), run.oracle_full())
+
+
+def test_reduced_chunked_prefill():
+    """Two sequences of 512 cached + 512 new tokens at the full head shape."""
+    wl = W.fp8_chunked_prefill(B=2, prefix=512, chunk=512)
+    run = PrefillRun(wl)
+    check(run.gpu(), run.oracle_full())
+
+
+def test_full_size_sampled_rows():
+    """8 x (4096 cached + 4096 new) tokens, Hq=32, Hkv=8, dh=128; a seeded
+    sample of (row, head) pairs including every sequence's first and last row."""
+    wl = W.fp8_chunked_prefill()
+    run = PrefillRun(wl)
+    out = run.gpu()
+    kc, vc = run.oracle_caches()
+    g = W.rng(66)
+    cu = wl.cu_seqlens
+    rows = [(int(cu[b]), 0) for b in range(8)] + [(int(cu[b + 1]) - 1, 31) for b in range(8)]
+    rows += [(int(g.integers(cu[-1])), int(g.integers(32))) for _ in range(48)]
+    rows = np.array(rows, np.int64)
+    ref = oracle.prefill_rows(rows, wl.q, wl.cu_seqlens, run.qs_ref, run.qg, kc, vc,
+                              wl.paging.block_tables, wl.paging.context_lens, run.ks_ref,
+                              run.vs_ref, run.fmt, run.kg)
+    got = out[rows[:, 0], rows[:, 1]]
+    check(got, ref)
+    assert np.all(np.isfinite(out))

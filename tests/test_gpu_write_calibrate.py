@@ -1,0 +1,162 @@
+"""GPU parity of scale calibration and quantize-on-write (bit-exact against the oracle)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from helpers import SENTINEL, DecodeRun, same_codes, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+FMTS = [oracle.FMT_E4M3, oracle.FMT_E5M2]
+ALL_BF16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+
+# scales in the supported range [2^-126, 2^126): powers of two, amax/fmax-like values,
+# the extremes (quotients overflow / underflow) and a seeded log-uniform spread
+SCALES = ([1.0, 0.5, 2.0 ** -9, 1.0 / 448, 10.0 / 448, 3.0, 0.0123, 123.456, 1e-30, 3.3e20,
+           1.1754944e-38, 6.0e37]
+          + list(np.exp(W.rng(77).uniform(np.log(1e-6), np.log(1e6), 48)).astype(np.float32)))
+
+
+def gpu_write(k_bits, v_bits, slots, nb, Hkv, dh, ks, vs, fmt, gran):
+    import torch
+    import quantized_kv_cache_fp8_amd as K
+    kc = torch.full((nb, Hkv, 16, dh), SENTINEL, dtype=torch.uint8, device="cuda:0")
+    vc = torch.full_like(kc, SENTINEL)
+    K.kvq_cache_write(to_dev(k_bits), to_dev(v_bits), to_dev(slots), kc, vc,
+                      to_dev(np.asarray(ks, np.float32)), to_dev(np.asarray(vs, np.float32)),
+                      fmt, gran)
+    torch.cuda.synchronize()
+    return to_np(kc), to_np(vc)
+
+
+def oracle_write(k_bits, v_bits, slots, nb, Hkv, dh, ks, vs, fmt, gran):
+    kc = np.full((nb, Hkv, 16, dh), SENTINEL, np.uint8)
+    vc = kc.copy()
+    oracle.cache_write(k_bits, v_bits, slots, kc, vc, np.asarray(ks, np.float32),
+                       np.asarray(vs, np.float32), fmt, gran)
+    return kc, vc
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_write_every_bf16_input_for_every_scale(fmt):
+    """All 65536 bf16 patterns (as K, and reversed as V) for each scale: the
+    cache bytes equal the oracle's, i.e. fp8(fl32(x / s)) exactly."""
+    k = ALL_BF16.reshape(512, 1, 128)
+    v = ALL_BF16[::-1].copy().reshape(512, 1, 128)
+    slots = np.arange(512, dtype=np.int64)
+    for s in SCALES:
+        s = np.float32(s)
+        gk, gv = gpu_write(k, v, slots, 32, 1, 128, [s], [s], fmt, oracle.GRAN_TENSOR)
+        rk, rv = oracle_write(k, v, slots, 32, 1, 128, [s], [s], fmt, oracle.GRAN_TENSOR)
+        assert same_codes(fmt, gk, rk), f"K differs at scale {s!r}"
+        assert same_codes(fmt, gv, rv), f"V differs at scale {s!r}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_write_per_head_scales(fmt):
+    g = W.rng(5)
+    Hkv, dh = 4, 64
+    k = g.permutation(ALL_BF16).reshape(256, Hkv, dh)
+    v = g.permutation(ALL_BF16).reshape(256, Hkv, dh)
+    ks = np.array([0.25, 1.0 / 448, 7.0, 3.1e-3], np.float32)
+    vs = np.array([1.5e-2, 2.0, 1.0, 9.9e3], np.float32)
+    slots = g.permutation(256 + 48)[:256].astype(np.int64)  # scattered over a larger pool
+    gk, gv = gpu_write(k, v, slots, 19, Hkv, dh, ks, vs, fmt, oracle.GRAN_HEAD)
+    rk, rv = oracle_write(k, v, slots, 19, Hkv, dh, ks, vs, fmt, oracle.GRAN_HEAD)
+    assert same_codes(fmt, gk, rk) and same_codes(fmt, gv, rv)
+
+
+def test_write_skips_padding_and_out_of_range_slots():
+    g = W.rng(6)
+    Hkv, dh = 2, 128
+    k = W.normal_bf16(g, (40, Hkv, dh))
+    v = W.normal_bf16(g, (40, Hkv, dh))
+    slots = g.permutation(64)[:40].astype(np.int64)
+    slots[[3, 17]] = -1  # padding
+    slots[[5, 30]] = [64, 1 << 40]  # beyond the pool of 4 blocks: skipped, never written
+    gk, gv = gpu_write(k, v, slots, 4, Hkv, dh, [0.01], [0.02], 0, 0)
+    rk, rv = oracle_write(k, v, slots, 4, Hkv, dh, [0.01], [0.02], 0, 0)
+    assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
+    assert (gk == SENTINEL).sum() == (rk == SENTINEL).sum() > 0
+
+
+def test_write_empty_batch_is_a_no_op():
+    gk, gv = gpu_write(np.zeros((0, 2, 64), np.uint16), np.zeros((0, 2, 64), np.uint16),
+                       np.zeros(0, np.int64), 2, 2, 64, [1.0], [1.0], 0, 0)
+    assert np.all(gk == SENTINEL) and np.all(gv == SENTINEL)
+
+
+# ------------------------------------------------------------------ calibration
+
+def gpu_calibrate(x_bits, fmt, gran, amax_in=None):
+    import torch
+    import quantized_kv_cache_fp8_amd as K
+    n = x_bits.shape[1] if gran == oracle.GRAN_HEAD else 1
+    amax = to_dev(np.asarray(amax_in, np.float32)) if amax_in is not None else \
+        torch.full((n,), 12345.0, device="cuda:0")
+    sc = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    K.kvq_calibrate_scales(to_dev(x_bits), fmt, gran, amax, sc, accumulate=amax_in is not None)
+    torch.cuda.synchronize()
+    return to_np(amax), to_np(sc)
+
+
+def same_f32(a, b):
+    a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
+    return np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(
+        a[~np.isnan(a)].view(np.uint32), b[~np.isnan(b)].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("gran", [oracle.GRAN_TENSOR, oracle.GRAN_HEAD])
+@pytest.mark.parametrize("shape", [(1, 1, 64), (333, 6, 64), (4099, 8, 128), (50, 32, 128)])
+def test_calibrate_matches_oracle(fmt, gran, shape):
+    g = W.rng(sum(shape) + fmt)
+    x = W.normal_bf16(g, shape, 1, W.log_uniform(g, shape[1], 0.5, 20.0), g.choice(shape[2], 2),
+                      10.0)
+    ga, gs = gpu_calibrate(x, fmt, gran)
+    ra, rs = oracle.calibrate(x, fmt, gran)
+    assert same_f32(ga, ra) and same_f32(gs, rs)
+
+
+def test_calibrate_accumulates_across_batches():
+    g = W.rng(8)
+    a = W.normal_bf16(g, (100, 4, 64), 1, np.array([1, 2, 3, 4.0]))
+    b = W.normal_bf16(g, (70, 4, 64), 1, np.array([4, 3, 2, 1.0]))
+    ga, _ = gpu_calibrate(a, 0, oracle.GRAN_HEAD)
+    ga2, gs2 = gpu_calibrate(b, 0, oracle.GRAN_HEAD, amax_in=ga)
+    ra, rs = oracle.calibrate(np.concatenate([a, b]), 0, oracle.GRAN_HEAD)
+    assert same_f32(ga2, ra) and same_f32(gs2, rs)
+
+
+def test_calibrate_degenerate_sets():
+    z = np.zeros((64, 3, 64), np.uint16)
+    z[:, 2, :] = 0x8000  # -0 only
+    z[7, 1, 9] = 0x7FC0  # NaN in head 1
+    ga, gs = gpu_calibrate(z, 0, oracle.GRAN_HEAD)
+    ra, rs = oracle.calibrate(z, 0, oracle.GRAN_HEAD)
+    assert same_f32(ga, ra) and same_f32(gs, rs)
+    assert gs[0] == 1.0 and np.isnan(ga[1]) and gs[1] == 1.0 and gs[2] == 1.0
+    z[7, 1, 9] = 0xFF80  # -Inf
+    ga, gs = gpu_calibrate(z, 1, oracle.GRAN_TENSOR)
+    assert np.isinf(ga[0]) and gs[0] == 1.0
+    ga, gs = gpu_calibrate(np.zeros((0, 3, 64), np.uint16), 1, oracle.GRAN_HEAD)
+    assert np.all(ga == 0) and np.all(gs == 1.0)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+@pytest.mark.parametrize("which", ["llama", "long-e4m3", "long-e5m2"])
+def test_full_size_calibrate_and_write(which):
+    """The Llama-3-8B-shaped layer (B=32, ctx ~ U[512, 8192], per-tensor) and
+    the long-context batch (B=4, S=32768, per-head): GPU scales and every cache
+    byte equal the oracle's."""
+    wl = {"llama": W.llama_layer_decode, "long-e4m3": lambda: W.long_context_decode("e4m3"),
+          "long-e5m2": lambda: W.long_context_decode("e5m2")}[which]()
+    print(f"[{which}] tokens={wl.kv.k.shape[0]}", flush=True)
+    run = DecodeRun(wl)
+    run.gpu_scales()
+    assert same_f32(to_np(run.ks), run.ks_ref) and same_f32(to_np(run.vs), run.vs_ref)
+    run.gpu_write()
+    rk, rv = run.oracle_caches()
+    assert np.array_equal(to_np(run.kc), rk)
+    assert np.array_equal(to_np(run.vc), rv)
