@@ -83,11 +83,10 @@ def main():
     amax = torch.empty(1, device=dev)
     K.kvq_calibrate_scales(k_all, "fp8_e4m3", "tensor", amax, ks)
     K.kvq_calibrate_scales(v_all, "fp8_e4m3", "tensor", amax, vs)
-    shape = (wl.paging.num_blocks, Hkv, bs, dh)
     caches = []
     for _ in range(args.copies):
-        kc = torch.empty(shape, dtype=torch.uint8, device=dev)
-        vc = torch.empty(shape, dtype=torch.uint8, device=dev)
+        kc = torch.empty((wl.paging.num_blocks, Hkv, bs, dh), dtype=torch.uint8, device=dev)
+        vc = torch.empty((wl.paging.num_blocks, Hkv, dh, bs), dtype=torch.uint8, device=dev)
         K.kvq_cache_write(k_all, v_all, slots_all, kc, vc, ks, vs, "fp8_e4m3", "tensor")
         caches.append((kc, vc))
     # the step's new token of every sequence: its last position
@@ -216,9 +215,8 @@ def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, 
     K.kvq_calibrate_scales(q, "fp8_e4m3", "head", am, qs)
     K.kvq_calibrate_scales(pk, "fp8_e4m3", "head", am[:pw.Hkv], pks)
     K.kvq_calibrate_scales(pv, "fp8_e4m3", "head", am[:pw.Hkv], pvs)
-    shape = (pw.paging.num_blocks, pw.Hkv, pw.bs, pw.dh)
-    pkc = torch.empty(shape, dtype=torch.uint8, device=dev)
-    pvc = torch.empty(shape, dtype=torch.uint8, device=dev)
+    pkc = torch.empty((pw.paging.num_blocks, pw.Hkv, pw.bs, pw.dh), dtype=torch.uint8, device=dev)
+    pvc = torch.empty((pw.paging.num_blocks, pw.Hkv, pw.dh, pw.bs), dtype=torch.uint8, device=dev)
     K.kvq_cache_write(pk, pv, dt(pw.kv.slot_mapping), pkc, pvc, pks, pvs, "fp8_e4m3", "head")
     out = torch.empty((q.shape[0], pw.Hq, pw.dh), dtype=torch.float32, device=dev)
     cu, bt, cl = dt(pw.cu_seqlens), dt(pw.paging.block_tables), dt(pw.paging.context_lens)
@@ -247,9 +245,8 @@ def cpu_baseline(wl, sample_rows):
     fmt, gran = oracle.FMT_E4M3, oracle.GRAN_TENSOR
     ks = oracle.calibrate(wl.kv.k, fmt, gran)[1]
     vs = oracle.calibrate(wl.kv.v, fmt, gran)[1]
-    shape = (wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh)
-    kc = np.zeros(shape, np.uint8)
-    vc = np.zeros(shape, np.uint8)
+    kc = np.zeros((wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh), np.uint8)
+    vc = np.zeros((wl.paging.num_blocks, wl.Hkv, wl.dh, wl.bs), np.uint8)
     oracle.cache_write(wl.kv.k, wl.kv.v, wl.kv.slot_mapping, kc, vc, ks, vs, fmt, gran)
     rows = np.array([(b, h) for b in range(wl.B) for h in range(wl.Hq)], np.int32)
     if sample_rows:

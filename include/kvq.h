@@ -29,10 +29,12 @@
  *   invalid arguments returns an error and touches no device memory.
  * - bf16 tensors are passed as void* holding IEEE bfloat16 bit patterns.
  * - Cache layout (this library's design; the pages fix only that FP8 caches
- *   are raw bytes): k_cache and v_cache are uint8 [num_blocks][Hkv][bs][dh].
- *   Token position j of sequence b lives in physical block
+ *   are raw bytes): k_cache is uint8 [num_blocks][Hkv][bs][dh] (token-major
+ *   tiles) and v_cache is uint8 [num_blocks][Hkv][dh][bs] (channel-major
+ *   tiles).  Token position j of sequence b lives in physical block
  *   block_tables[b][j / bs] at offset j % bs.  Each (block, head) tile is one
- *   contiguous bs*dh-byte run.
+ *   contiguous bs*dh-byte run.  Attention contracts K over channels and V over
+ *   tokens, so these orders give both contractions contiguous operands.
  * - GQA: query head hq reads KV head hq / (Hq / Hkv).
  * - Supported now: dh in {64, 128}; bs == 16; Hq % Hkv == 0; Hq/Hkv <= 16.
  * - Calls are reentrant; calls on the same stream run in order.
@@ -118,11 +120,13 @@ kvq_status kvq_calibrate_scales(const void* x_bf16, int64_t T, int H, int dh, kv
  * cast_fp8(K / sK)):
  *   for every token t with 0 <= slot_mapping[t] < num_blocks * bs, every KV
  *   head h and channel d:
- *     cache[slot / bs][h][slot % bs][d] = fp8(fl32(x[t][h][d] / s))
+ *     k_cache[slot / bs][h][slot % bs][d] = fp8(fl32(k[t][h][d] / sK))
+ *     v_cache[slot / bs][h][d][slot % bs] = fp8(fl32(v[t][h][d] / sV))
  *   with s = scale[h] (KVQ_SCALE_HEAD) or scale[0] (KVQ_SCALE_TENSOR), the
  *   quotient correctly rounded to fp32 and fp8() the encoder above.  Tokens
  *   whose slot is negative (padding) or out of range are skipped; no other
- *   cache byte is touched.  Scales must lie in [2^-126, 2^126) (positive
+ *   cache byte is touched; if two tokens name the same slot, which one lands
+ *   is unspecified.  Scales must lie in [2^-126, 2^126) (positive
  *   fp32 values whose reciprocal is a normal number, as every calibrated
  *   scale of a tensor with amax >= 2^-117 is); other values give unspecified
  *   codes.

@@ -165,11 +165,12 @@ def calibrate(x_bf16, fmt: int, gran: int):
 
 def cache_write(k_bf16, v_bf16, slot_mapping: np.ndarray, k_cache: np.ndarray,
                 v_cache: np.ndarray, k_scale, v_scale, fmt: int, gran: int) -> None:
-    """Quantize-write into uint8 caches [num_blocks][Hkv][bs][dh] (in place)."""
+    """Quantize-write (in place) into uint8 caches: K [num_blocks][Hkv][bs][dh]
+    (token-major tiles), V [num_blocks][Hkv][dh][bs] (channel-major tiles)."""
     k, v = _u16(k_bf16), _u16(v_bf16)
     T, Hkv, dh = k.shape
     nb, hk, bs, dh2 = k_cache.shape
-    assert hk == Hkv and dh2 == dh and v_cache.shape == k_cache.shape
+    assert hk == Hkv and dh2 == dh and v_cache.shape == (nb, Hkv, dh, bs)
     sm = np.ascontiguousarray(slot_mapping, np.int64)
     ks = np.ascontiguousarray(k_scale, np.float32)
     vs = np.ascontiguousarray(v_scale, np.float32)

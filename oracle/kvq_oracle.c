@@ -180,9 +180,19 @@ void orc_calibrate(const uint16_t* x, int64_t T, int H, int dh, int fmt, int gra
 }
 
 /* ---- paged quantize-write ----
- * For every token t with slot_mapping[t] >= 0, every KV head h and channel d:
- *   cache[slot / bs][h][slot % bs][d] = quantize(x[t][h][d], s[h or 0]).
- * Cache layout: uint8 [num_blocks][Hkv][bs][dh]. */
+ * For every token t with 0 <= slot_mapping[t] < num_blocks * bs, every KV head
+ * h and channel d, with blk = slot / bs and off = slot % bs:
+ *   K code -> k_cache[blk][h][off][d]   (token-major tile [bs][dh])
+ *   V code -> v_cache[blk][h][d][off]   (channel-major tile [dh][bs])
+ * each code = quantize(x[t][h][d], s[h or 0]).  The two tile orders are this
+ * library's layout (the pages fix only that FP8 caches are raw bytes). */
+
+static int64_t k_index(int64_t blk, int h, int off, int d, int Hkv, int bs, int dh) {
+  return ((blk * Hkv + h) * bs + off) * dh + d;
+}
+static int64_t v_index(int64_t blk, int h, int off, int d, int Hkv, int bs, int dh) {
+  return ((blk * Hkv + h) * dh + d) * bs + off;
+}
 
 void orc_cache_write(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv, int dh,
                      const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
@@ -199,9 +209,8 @@ void orc_cache_write(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv, i
       float sv = v_scale[gran == ORC_GRAN_HEAD ? h : 0];
       for (int d = 0; d < dh; ++d) {
         int64_t src = (t * Hkv + h) * dh + d;
-        int64_t dst = ((blk * Hkv + h) * bs + off) * dh + d;
-        k_cache[dst] = orc_quantize(fmt, k[src], sk);
-        v_cache[dst] = orc_quantize(fmt, v[src], sv);
+        k_cache[k_index(blk, h, (int)off, d, Hkv, bs, dh)] = orc_quantize(fmt, k[src], sk);
+        v_cache[v_index(blk, h, (int)off, d, Hkv, bs, dh)] = orc_quantize(fmt, v[src], sv);
       }
     }
   }
@@ -209,9 +218,13 @@ void orc_cache_write(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv, i
 
 /* ---- dequantized read: x_hat = s * cast_float(code) (textbook 10.4.2/10.4.5) ---- */
 
-static double deq(const uint8_t* cache, int64_t blk, int h, int off, int d, int Hkv, int bs,
-                  int dh, double s, int fmt) {
-  return s * orc_fp8_decode(fmt, cache[(((int64_t)blk * Hkv + h) * bs + off) * dh + d]);
+static double deq_k(const uint8_t* cache, int64_t blk, int h, int off, int d, int Hkv, int bs,
+                    int dh, double s, int fmt) {
+  return s * orc_fp8_decode(fmt, cache[k_index(blk, h, off, d, Hkv, bs, dh)]);
+}
+static double deq_v(const uint8_t* cache, int64_t blk, int h, int off, int d, int Hkv, int bs,
+                    int dh, double s, int fmt) {
+  return s * orc_fp8_decode(fmt, cache[v_index(blk, h, off, d, Hkv, bs, dh)]);
 }
 
 /* Attention of one query vector q[dh] (fp64) over keys 0..nkeys-1 of one
@@ -228,7 +241,7 @@ static void attend_one(double* o, const double* q, int nkeys, const uint8_t* k_c
     int64_t blk = btab[j / bs];
     int off = j % bs;
     double acc = 0.0;
-    for (int d = 0; d < dh; ++d) acc += q[d] * deq(k_cache, blk, h, off, d, Hkv, bs, dh, sk, fmt);
+    for (int d = 0; d < dh; ++d) acc += q[d] * deq_k(k_cache, blk, h, off, d, Hkv, bs, dh, sk, fmt);
     z[j] = acc * sm_scale;
     if (z[j] > zmax) zmax = z[j];
   }
@@ -241,7 +254,7 @@ static void attend_one(double* o, const double* q, int nkeys, const uint8_t* k_c
     int64_t blk = btab[j / bs];
     int off = j % bs;
     double p = z[j] / l;
-    for (int d = 0; d < dh; ++d) o[d] += p * deq(v_cache, blk, h, off, d, Hkv, bs, dh, sv, fmt);
+    for (int d = 0; d < dh; ++d) o[d] += p * deq_v(v_cache, blk, h, off, d, Hkv, bs, dh, sv, fmt);
   }
   free(z);
 }

@@ -3,44 +3,52 @@
 //
 // Computes, per sequence b and query head hq (KV head h = hq / G):
 //   z_j = (q . k_hat_j) / sqrt(dh),  P = softmax(z),  o = sum_j P_j v_hat_j
-// with k_hat = sK * cast_float(K8), v_hat = sV * cast_float(V8): the attention
-// equation and the fused dequant + attention path of the KV-cache quantization
-// textbook (section 10.4.2), on the FP8 storage of section 10.4.5.  No
-// dequantized copy of the cache exists anywhere: codes go from HBM into
-// registers and are converted there.
+// with k_hat = sK * cast_float(K8) and v_hat = sV * cast_float(V8): the
+// attention equation and the fused dequant + attention path of the KV-cache
+// quantization textbook (section 10.4.2) on the FP8 storage of section
+// 10.4.5.  No dequantized copy of the cache exists anywhere: codes go from HBM
+// into registers, are converted there (exactly: every E4M3/E5M2 value is a
+// bf16 and an f16 value) and feed the matrix cores.
 //
-// Work decomposition (flash-decoding):
-//   grid = (nsplit, Hq / GT, B); a workgroup of 4 waves owns one split of
-//   part_blocks cache blocks of one sequence and GT query heads that share one
-//   KV head (GT = 4 for the usual GQA group of 4).  Wave w takes blocks
-//   w, w+4, ... of the split.
-// Per cache block (16 tokens, one (block, head) tile = 16*dh contiguous bytes)
-// a wave issues two coalesced loads of K and two of V (lane l holds dh/8
-// bytes of token l/8 and of token 8 + l/8), so every byte is read from HBM
-// exactly once and reused in registers by all GT query heads:
-//   * q.k: codes -> bf16 pairs (exact, v_cvt_scalef32_pk_bf16_*), v_dot2 with
-//     the bf16 query (exact products, fp32 accumulation), then a sum over the
-//     8 lanes of a token by DPP (quad_perm, quad_perm, row_half_mirror);
-//   * online softmax per lane in the log2 domain, with the running max only
-//     raised when a score exceeds it by more than 2^8 (p stays <= 256), so the
-//     accumulator rescale is rare;
-//   * p.v: each lane pairs the codes of its two tokens channel by channel
-//     (v_perm_b32), converts to f16 pairs (exact) and accumulates
-//     p_a*v_a + p_b*v_b with v_dot2_f32_f16 (p rounded to f16, 11 bits).
-// The split's partial (m, l, o) is merged across the 8 token lanes, across the
-// 4 waves through LDS, and written to the workspace; a second kernel merges
-// the splits (log-sum-exp) and applies sV.
+// Work decomposition (flash-decoding): grid = (nsplit, Hq / NH, B).  A
+// workgroup of 4 waves owns one split (part_blocks cache blocks of 16 tokens)
+// of one sequence and the NH <= 16 query heads that share one KV head, so
+// every K/V byte is read from HBM once and serves all NH heads.  Wave w takes
+// block pairs w, w+4, ... of the split.  Two passes over the split:
+//
+//   pass 1  S = Q K^T on v_mfma_f32_16x16x32_bf16: A = the NH query rows
+//           (bf16, rows NH..15 zero), B = 16 keys of one block (fp8 -> bf16
+//           in registers; each lane loads 16 contiguous bytes of one key).
+//           Scores (log2 domain, masked past the context) go to LDS; the
+//           per-head maximum of the split is reduced with DPP and LDS.
+//   middle  p = exp2(z - M) once per (token, head), stored as f16 in LDS,
+//           row sums l accumulated with LDS atomics.
+//   pass 2  O += P V on v_mfma_f32_16x16x32_f16: A = P of 32 tokens (a
+//           block pair), B = V from the channel-major tile (each lane loads
+//           the 8 contiguous token bytes of one channel, fp8 -> f16).
+//
+// The split's partial (M, l, O) goes to the workspace; a second kernel merges
+// the splits (log-sum-exp) and applies sV.  Loads of the next block pair are
+// issued before the current pair is computed.
 #include "codec.hpp"
 #include "launch.hpp"
 
 namespace kvq {
 
-constexpr int kBlockSize = 16;   // tokens per cache block
-constexpr float kLazyTau = 8.0f; // log2 headroom before the running max moves
+// Largest split (cache blocks per workgroup): 8, 16 or 32.  Larger splits mean
+// fewer partial results to merge, smaller ones more workgroups in flight.
+#ifndef KVQ_DECODE_MAX_SPLIT_BLOCKS
+#define KVQ_DECODE_MAX_SPLIT_BLOCKS 16
+#endif
+
+namespace {
+constexpr int kBlockSize = 16;  // tokens per cache block
 constexpr float kLog2e = 1.4426950408889634f;
-// Running maxima start finite, so exp2(-inf - m) = 0 for masked keys and no
-// merge ever forms -inf - (-inf).
-constexpr float kNegBig = -1.0e30f;
+constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -48,218 +56,218 @@ __device__ __forceinline__ float dpp(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 8 lanes of each half-row (lanes 8i .. 8i+7); every lane gets it.
-__device__ __forceinline__ float sum8(float x) {
-  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp<0x141>(x);  // row_half_mirror
+// max over the 16 lanes of a row (lanes 16i .. 16i+15); every lane gets it
+__device__ __forceinline__ float max16(float x) {
+  x = __builtin_fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = __builtin_fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = __builtin_fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+  x = __builtin_fmaxf(x, dpp<0x140>(x));  // row_mirror
   return x;
 }
 
-template <int DPL>
-struct Chunk;  // DPL bytes of one token row held by one lane
-template <>
-struct Chunk<16> {
-  uint32_t w[4];
-  __device__ __forceinline__ void load(const uint8_t* p) {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  }
-};
-template <>
-struct Chunk<8> {
-  uint32_t w[2];
-  __device__ __forceinline__ void load(const uint8_t* p) {
-    uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x; w[1] = v.y;
-  }
-};
+// 8 codes (two dwords) -> 8 exact bf16 / f16 values
+template <int FMT>
+__device__ __forceinline__ bf16x8 codes_to_bf16x8(uint32_t a, uint32_t b) {
+  const bf16x2 p0 = dec2_bf16<FMT, false>(a), p1 = dec2_bf16<FMT, true>(a);
+  const bf16x2 p2 = dec2_bf16<FMT, false>(b), p3 = dec2_bf16<FMT, true>(b);
+  return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+template <int FMT>
+__device__ __forceinline__ f16x8 codes_to_f16x8(uint32_t a, uint32_t b) {
+  const f16x2 p0 = dec2_f16<FMT, false>(a), p1 = dec2_f16<FMT, true>(a);
+  const f16x2 p2 = dec2_f16<FMT, false>(b), p3 = dec2_f16<FMT, true>(b);
+  return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
 
-template <int DPL>
-struct Tile {  // one lane's share of one block: tokens (l/8) and (8 + l/8), K and V
-  Chunk<DPL> k0, k1, v0, v1;
-};
+__device__ __forceinline__ int64_t clamp_block(int64_t blk, int64_t num_blocks) {
+  return blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
+}
+}  // namespace
 
-template <int FMT, int DH, int GT>
-__global__ __launch_bounds__(256) void decode_split_kernel(
+// dynamic LDS bytes for one workgroup of nw waves: per-wave P transpose
+// scratch [nw][16 rows][32 tokens] f16, then the wave-merge buffers.
+static size_t decode_lds_bytes(int nw, int NH, int dh) {
+  return (size_t)nw * 16 * 32 * sizeof(_Float16) + 2 * (size_t)nw * 16 * sizeof(float) +
+         (size_t)nw * NH * dh * sizeof(float);
+}
+
+// Lazy running max: it only moves when a score exceeds it by more than 2^8,
+// so p = exp2(z - m) <= 256 (safe in f16) and accumulator rescales are rare.
+constexpr float kLazyTau = 8.0f;
+
+template <int FMT, int DH, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ vc, int64_t num_blocks, const int32_t* __restrict__ bt,
-    int max_blocks, const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int max_ctx,
-    const float* __restrict__ ks, int per_head, float sm_scale, int part_blocks, int nsplit,
+    int max_blocks, const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int NH, int max_ctx,
+    const float* __restrict__ ks, int per_head, float sm_scale, int nsplit,
     float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
-  constexpr int DPL = DH / 8;  // bytes of a token row per lane
-  constexpr int NW = DPL / 4;  // dwords per lane per token
+  constexpr int NK = DH / 64;   // 16-byte key loads per block per lane
+  constexpr int NQ = DH / 32;   // bf16 MFMAs per block (k = 32 channels each)
+  constexpr int NV = DH / 16;   // f16 MFMAs per block pair (16 channels each)
+  constexpr int PB = 2 * NW;    // blocks per split: one block pair per wave
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
   const int split = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
-  const int gpk = G / GT;  // workgroups per KV head
+  const int gpk = G / NH;
   const int h = grp / gpk;
-  const int hq0 = h * G + (grp - h * gpk) * GT;
+  const int hq0 = h * G + (grp - h * gpk) * NH;
 
   int ctx = ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > max_ctx ? max_ctx : ctx);
-  const int tok0 = split * part_blocks * kBlockSize;
+  const int tok0 = split * PB * kBlockSize;
   if (tok0 >= ctx) return;  // nothing of this sequence lies in this split
   const int nblk_left = (ctx - tok0 + kBlockSize - 1) / kBlockSize;
-  const int nblk = nblk_left < part_blocks ? nblk_left : part_blocks;
+  const int nblk = nblk_left < PB ? nblk_left : PB;
+  const int npair = (nblk + 1) >> 1;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kg = lane >> 3, dl = lane & 7;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const bool head_real = c16 < NH;
+  _Float16* ptr = reinterpret_cast<_Float16*>(smem) + wave * 16 * 32;  // this wave's P scratch
+  float* wm = reinterpret_cast<float*>(smem + NW * 16 * 32 * sizeof(_Float16));
+  float* wl = wm + NW * 16;
+  float* wo = wl + NW * 16;  // [NW][NH][DH]
+  const int32_t* btab = bt + (size_t)b * max_blocks + (size_t)split * PB;
+  const size_t tile = (size_t)kBlockSize * DH;  // bytes per (block, head) tile
+  const int eb = g4 >> 1, tk = 8 * (g4 & 1);   // V: this lane's block in a pair, token half
 
-  // query rows of the GT heads, this lane's DPL channels, as bf16 pairs
-  bf16x2 qv[GT][DPL / 2];
+  // this wave's block pair: blocks 2 wave and 2 wave + 1 of the split
+  const int p = wave;
+  const bool active = p < npair;
+  uint4 kb[2][NK];  // lane: 16 bytes of token c16 of each block, channels 64 m + 16 g4 ..
+  uint2 vb[NV];     // lane: tokens tk .. tk + 7 of block eb, channel 16 n + c16
 #pragma unroll
-  for (int g = 0; g < GT; ++g) {
-    const uint16_t* qp = q + ((size_t)b * Hq + hq0 + g) * DH + dl * DPL;
+  for (int e = 0; e < 2; ++e) {
+    const int bi = 2 * p + e;
+    if (bi < nblk) {
+      const int64_t blk = clamp_block(btab[bi], num_blocks);
+      const uint8_t* src = kc + ((size_t)blk * Hkv + h) * tile + c16 * DH + 16 * g4;
 #pragma unroll
-    for (int j = 0; j < DPL / 8; ++j) {
-      uint4 w = *reinterpret_cast<const uint4*>(qp + j * 8);
-      qv[g][4 * j + 0] = __builtin_bit_cast(bf16x2, w.x);
-      qv[g][4 * j + 1] = __builtin_bit_cast(bf16x2, w.y);
-      qv[g][4 * j + 2] = __builtin_bit_cast(bf16x2, w.z);
-      qv[g][4 * j + 3] = __builtin_bit_cast(bf16x2, w.w);
+      for (int m = 0; m < NK; ++m) kb[e][m] = *reinterpret_cast<const uint4*>(src + 64 * m);
     }
   }
-  // z (log2 domain) = (q . k_code) * sK / sqrt(dh) * log2(e)
+  {
+    const int bi = 2 * p + eb;
+    if (bi < nblk) {
+      const int64_t blk = clamp_block(btab[bi], num_blocks);
+      const uint8_t* src = vc + ((size_t)blk * Hkv + h) * tile + c16 * kBlockSize + tk;
+#pragma unroll
+      for (int n = 0; n < NV; ++n)
+        vb[n] = *reinterpret_cast<const uint2*>(src + 16 * n * kBlockSize);
+    } else {
+#pragma unroll
+      for (int n = 0; n < NV; ++n) vb[n] = make_uint2(0, 0);  // no token: exact zeros
+    }
+  }
+
+  // A operand of S = Q K^T: query row c16, channels 64(j/2) + 16 g4 + 8(j%2) + 0..7
+  bf16x8 qop[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (head_real)
+      w = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + hq0 + c16) * DH + 64 * (j >> 1) +
+                                          16 * g4 + 8 * (j & 1));
+    qop[j] = __builtin_bit_cast(bf16x8, w);
+  }
   const float zc = sm_scale * ks[per_head ? h : 0] * kLog2e;
 
-  float m[GT], l[GT], acc[GT][DPL];
+  // running state of rows 4 g4 + r (identical across the 16 lanes of a group)
+  float m_run[4] = {kNegBig, kNegBig, kNegBig, kNegBig};
+  float l_part[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // this lane's token share of the row sum
+  f32x4 O[NV];
 #pragma unroll
-  for (int g = 0; g < GT; ++g) {
-    m[g] = kNegBig;
-    l[g] = 0.0f;
+  for (int n = 0; n < NV; ++n) O[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  if (active) {
+    // ---- S for both blocks: lane holds rows 4 g4 + r for token c16 of each block
+    float z[2][4];
 #pragma unroll
-    for (int d = 0; d < DPL; ++d) acc[g][d] = 0.0f;
+    for (int e = 0; e < 2; ++e) {
+      f32x4 S = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int m = 0; m < NK; ++m) {
+        const bf16x8 k0 = codes_to_bf16x8<FMT>(kb[e][m].x, kb[e][m].y);
+        const bf16x8 k1 = codes_to_bf16x8<FMT>(kb[e][m].z, kb[e][m].w);
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[2 * m], k0, S, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[2 * m + 1], k1, S, 0, 0, 0);
+      }
+      const bool valid = tok0 + (2 * p + e) * kBlockSize + c16 < ctx;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z[e][r] = valid ? S[r] * zc : -__builtin_inff();
+    }
+    // ---- softmax state per row (one pair per wave: the running max is set once)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mt = max16(__builtin_fmaxf(z[0][r], z[1][r]));
+      if (mt > m_run[r] + kLazyTau) {
+        const float f = __builtin_amdgcn_exp2f(m_run[r] - mt);
+        l_part[r] *= f;
+#pragma unroll
+        for (int n = 0; n < NV; ++n) O[n][r] *= f;
+        m_run[r] = mt;
+      }
+      const float p0 = __builtin_amdgcn_exp2f(z[0][r] - m_run[r]);
+      const float p1 = __builtin_amdgcn_exp2f(z[1][r] - m_run[r]);
+      l_part[r] += p0 + p1;
+      const int row = 4 * g4 + r;
+      ptr[row * 32 + c16] = (_Float16)p0;
+      ptr[row * 32 + 16 + c16] = (_Float16)p1;
+    }
+    // ---- P V: A = P rows (head c16), tokens 8 g4 .. 8 g4 + 7 of the pair
+    f16x8 pop = {};
+    if (head_real) pop = *reinterpret_cast<const f16x8*>(ptr + c16 * 32 + 8 * g4);
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+      O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          pop, codes_to_f16x8<FMT>(vb[n].x, vb[n].y), O[n], 0, 0, 0);
   }
 
-  const int32_t* btab = bt + (size_t)b * max_blocks + (size_t)split * part_blocks;
-  const size_t tile_stride = (size_t)kBlockSize * DH;  // bytes per (block, head) tile
-  auto load_tile = [&](int i, Tile<DPL>& t) {
-    int64_t blk = btab[i];
-    blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
-    const size_t base = ((size_t)blk * Hkv + h) * tile_stride + (size_t)lane * DPL;
-    t.k0.load(kc + base);
-    t.k1.load(kc + base + 8 * DH);
-    t.v0.load(vc + base);
-    t.v1.load(vc + base + 8 * DH);
-  };
-
-  Tile<DPL> cur, nxt;
-  int i = wave;
-  if (i < nblk) load_tile(i, cur);
-  for (; i < nblk; i += 4) {
-    if (i + 4 < nblk) load_tile(i + 4, nxt);
-    const int tokb = tok0 + i * kBlockSize;
-    const bool ok0 = tokb + kg < ctx, ok1 = tokb + 8 + kg < ctx;
-
-    // ---- scores of this lane's two tokens for the GT heads
-    float z0[GT], z1[GT];
+  // ---- merge the NW waves through LDS and write the split's partial
+  float l_row[4];
 #pragma unroll
-    for (int g = 0; g < GT; ++g) { z0[g] = 0.0f; z1[g] = 0.0f; }
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const bf16x2 a_lo = dec2_bf16<FMT, false>(cur.k0.w[w]);
-      const bf16x2 a_hi = dec2_bf16<FMT, true>(cur.k0.w[w]);
-      const bf16x2 b_lo = dec2_bf16<FMT, false>(cur.k1.w[w]);
-      const bf16x2 b_hi = dec2_bf16<FMT, true>(cur.k1.w[w]);
-#pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        z0[g] = __builtin_amdgcn_fdot2_f32_bf16(qv[g][2 * w], a_lo, z0[g], false);
-        z0[g] = __builtin_amdgcn_fdot2_f32_bf16(qv[g][2 * w + 1], a_hi, z0[g], false);
-        z1[g] = __builtin_amdgcn_fdot2_f32_bf16(qv[g][2 * w], b_lo, z1[g], false);
-        z1[g] = __builtin_amdgcn_fdot2_f32_bf16(qv[g][2 * w + 1], b_hi, z1[g], false);
-      }
-    }
-    f16x2 ph[GT];
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      float s0 = ok0 ? sum8(z0[g]) * zc : -__builtin_inff();
-      float s1 = ok1 ? sum8(z1[g]) * zc : -__builtin_inff();
-      const float smax = __builtin_fmaxf(s0, s1);
-      if (smax > m[g] + kLazyTau) {  // raise the running max, rescale (rare)
-        const float f = __builtin_amdgcn_exp2f(m[g] - smax);
-        l[g] *= f;
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) acc[g][d] *= f;
-        m[g] = smax;
-      }
-      const float p0 = __builtin_amdgcn_exp2f(s0 - m[g]);
-      const float p1 = __builtin_amdgcn_exp2f(s1 - m[g]);
-      l[g] += p0 + p1;
-      ph[g] = f16x2{(_Float16)p0, (_Float16)p1};
-    }
-
-    // ---- p . v: channel-wise pairs (token a, token b) against (p_a, p_b)
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const uint32_t x = cur.v0.w[w], y = cur.v1.w[w];
-      const uint32_t lo = __builtin_amdgcn_perm(x, y, 0x01050004u);  // x0 y0 x1 y1
-      const uint32_t hi = __builtin_amdgcn_perm(x, y, 0x03070206u);  // x2 y2 x3 y3
-      const f16x2 c0 = dec2_f16<FMT, false>(lo), c1 = dec2_f16<FMT, true>(lo);
-      const f16x2 c2 = dec2_f16<FMT, false>(hi), c3 = dec2_f16<FMT, true>(hi);
-#pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        acc[g][4 * w + 0] = __builtin_amdgcn_fdot2(ph[g], c0, acc[g][4 * w + 0], false);
-        acc[g][4 * w + 1] = __builtin_amdgcn_fdot2(ph[g], c1, acc[g][4 * w + 1], false);
-        acc[g][4 * w + 2] = __builtin_amdgcn_fdot2(ph[g], c2, acc[g][4 * w + 2], false);
-        acc[g][4 * w + 3] = __builtin_amdgcn_fdot2(ph[g], c3, acc[g][4 * w + 3], false);
-      }
-    }
-    cur = nxt;
+  for (int r = 0; r < 4; ++r) {
+    float x = l_part[r];
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    l_row[r] = x;
   }
-
-  // ---- merge the 8 token lanes that share a channel chunk (xor 8, 16, 32)
 #pragma unroll
-  for (int off = 8; off <= 32; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      const float mo = __shfl_xor(m[g], off);
-      const float lo = __shfl_xor(l[g], off);
-      const float mn = __builtin_fmaxf(m[g], mo);
-      const float fa = __builtin_amdgcn_exp2f(m[g] - mn);
-      const float fb = __builtin_amdgcn_exp2f(mo - mn);
-      l[g] = l[g] * fa + lo * fb;
-#pragma unroll
-      for (int d = 0; d < DPL; ++d) {
-        const float ao = __shfl_xor(acc[g][d], off);
-        acc[g][d] = acc[g][d] * fa + ao * fb;
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * g4 + r;
+    if (row < NH) {
+      if (c16 == 0) {
+        wm[wave * 16 + row] = m_run[r];
+        wl[wave * 16 + row] = l_row[r];
       }
-      m[g] = mn;
-    }
-  }
-
-  // ---- merge the 4 waves through LDS and write the split's partial
-  __shared__ float s_m[4][GT], s_l[4][GT];
-  __shared__ float s_acc[4][GT][DH];
-  if (kg == 0) {
 #pragma unroll
-    for (int g = 0; g < GT; ++g) {
-#pragma unroll
-      for (int d = 0; d < DPL; ++d) s_acc[wave][g][dl * DPL + d] = acc[g][d];
-      if (dl == 0) {
-        s_m[wave][g] = m[g];
-        s_l[wave][g] = l[g];
-      }
+      for (int n = 0; n < NV; ++n) wo[(wave * NH + row) * DH + 16 * n + c16] = O[n][r];
     }
   }
   __syncthreads();
-  for (int o = threadIdx.x; o < GT * DH; o += 256) {
-    const int g = o / DH, d = o - g * DH;
+  for (int o = tid; o < NH * DH; o += 64 * NW) {
+    const int row = o / DH, d = o - row * DH;
     float M = kNegBig;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = __builtin_fmaxf(M, s_m[w][g]);
+    for (int w = 0; w < NW; ++w) M = __builtin_fmaxf(M, wm[w * 16 + row]);
     float a = 0.0f, L = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = __builtin_amdgcn_exp2f(s_m[w][g] - M);
-      a += f * s_acc[w][g][d];
-      L += f * s_l[w][g];
+    for (int w = 0; w < NW; ++w) {
+      const float f = __builtin_amdgcn_exp2f(wm[w * 16 + row] - M);
+      a += f * wo[(w * NH + row) * DH + d];
+      L += f * wl[w * 16 + row];
     }
-    const size_t row = ((size_t)b * Hq + hq0 + g) * nsplit + split;
-    ws_acc[row * DH + d] = a;
+    const size_t ridx = ((size_t)b * Hq + hq0 + row) * nsplit + split;
+    ws_acc[ridx * DH + d] = a;
     if (d == 0) {
-      ws_ml[row * 2 + 0] = M;
-      ws_ml[row * 2 + 1] = L;
+      ws_ml[ridx * 2 + 0] = M;
+      ws_ml[ridx * 2 + 1] = L;
     }
   }
 }
@@ -270,19 +278,53 @@ __global__ __launch_bounds__(DH) void decode_combine_kernel(
     void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
     const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int max_ctx,
     const float* __restrict__ vs, int per_head, int part_blocks, int nsplit) {
+  __shared__ float s_w[DH];
+  __shared__ float s_red[2];
   const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   int ctx = ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > max_ctx ? max_ctx : ctx);
   const int span = part_blocks * kBlockSize;
   const int nvalid = (ctx + span - 1) / span;
   const size_t row0 = ((size_t)b * Hq + hq) * nsplit;
+  float a = 0.0f;
+  float L = 0.0f;
+  // splits are merged in chunks of DH: weights exp2(m_s - M) staged in LDS
   float M = kNegBig;
-  for (int s = 0; s < nvalid; ++s) M = __builtin_fmaxf(M, ws_ml[(row0 + s) * 2]);
-  float L = 0.0f, a = 0.0f;
-  for (int s = 0; s < nvalid; ++s) {
-    const float f = __builtin_amdgcn_exp2f(ws_ml[(row0 + s) * 2] - M);
-    L += f * ws_ml[(row0 + s) * 2 + 1];
-    a += f * ws_acc[(row0 + s) * DH + d];
+  for (int s = d; s < nvalid; s += DH) M = __builtin_fmaxf(M, ws_ml[(row0 + s) * 2]);
+  for (int off = 32; off >= 1; off >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, off));
+  if (DH > 64) {  // two waves: combine their maxima
+    if ((d & 63) == 0) s_red[d >> 6] = M;
+    __syncthreads();
+    M = __builtin_fmaxf(s_red[0], s_red[1]);
+  }
+  for (int s0 = 0; s0 < nvalid; s0 += DH) {
+    __syncthreads();
+    const int s = s0 + d;
+    float w = 0.0f;
+    if (s < nvalid) {
+      w = __builtin_amdgcn_exp2f(ws_ml[(row0 + s) * 2] - M);
+      L += w * ws_ml[(row0 + s) * 2 + 1];
+    }
+    s_w[d] = w;
+    __syncthreads();
+    const int n = nvalid - s0 < DH ? nvalid - s0 : DH;
+    int j = 0;
+    for (; j + 4 <= n; j += 4) {  // four independent loads in flight
+      const float a0 = ws_acc[(row0 + s0 + j) * DH + d];
+      const float a1 = ws_acc[(row0 + s0 + j + 1) * DH + d];
+      const float a2 = ws_acc[(row0 + s0 + j + 2) * DH + d];
+      const float a3 = ws_acc[(row0 + s0 + j + 3) * DH + d];
+      a += s_w[j] * a0 + s_w[j + 1] * a1 + s_w[j + 2] * a2 + s_w[j + 3] * a3;
+    }
+    for (; j < n; ++j) a += s_w[j] * ws_acc[(row0 + s0 + j) * DH + d];
+  }
+  // total l: sum of the per-thread partial sums
+  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+  if (DH > 64) {
+    __syncthreads();
+    if ((d & 63) == 0) s_red[d >> 6] = L;
+    __syncthreads();
+    L = s_red[0] + s_red[1];
   }
   const int h = hq / (Hq / Hkv);
   const float r = L > 0.0f ? a / L * vs[per_head ? h : 0] : 0.0f;
@@ -293,46 +335,25 @@ __global__ __launch_bounds__(DH) void decode_combine_kernel(
     reinterpret_cast<float*>(out)[o] = r;
 }
 
+static int heads_per_group(int G) {
+  // largest divisor of G that fits the 16 rows of one MFMA tile
+  for (int n = G < 16 ? G : 16; n >= 1; --n)
+    if (G % n == 0) return n;
+  return 1;
+}
+
 DecodePlan decode_plan(int B, int Hq, int dh, int max_context_len, int bs) {
   DecodePlan p{0, 0, 0};
   if (B < 1 || Hq < 1 || dh < 1 || bs < 1 || max_context_len < 0) return p;
   const int64_t nb = ((int64_t)max_context_len + bs - 1) / bs;
   const int64_t groups = (int64_t)B * (Hq >= 4 ? Hq / 4 : 1);
-  int P = 32;
+  int P = KVQ_DECODE_MAX_SPLIT_BLOCKS;
   // shrink the split until the grid has enough workgroups to fill the chip
-  while (P > 4 && groups * ((nb + P - 1) / P) < 2048) P >>= 1;
+  while (P > 8 && groups * ((nb + P - 1) / P) < 2048) P >>= 1;
   p.part_blocks = P;
   p.nsplit = (int)(nb > 0 ? (nb + P - 1) / P : 1);
   p.ws_bytes = (size_t)B * Hq * p.nsplit * (2 + dh) * sizeof(float);
   return p;
-}
-
-template <int FMT, int DH, int GT>
-static void launch_split(dim3 grid, hipStream_t s, const uint16_t* q, const uint8_t* kc,
-                         const uint8_t* vc, int64_t num_blocks, const int32_t* bt,
-                         int max_blocks, const int32_t* ctx, int Hq, int Hkv, int max_ctx,
-                         const float* ks, int per_head, float sm, const DecodePlan& plan,
-                         float* ml, float* acc) {
-  decode_split_kernel<FMT, DH, GT><<<grid, 256, 0, s>>>(q, kc, vc, num_blocks, bt, max_blocks, ctx,
-                                                        Hq, Hkv, max_ctx, ks, per_head, sm,
-                                                        plan.part_blocks, plan.nsplit, ml, acc);
-}
-
-template <int FMT, int DH>
-static void launch_split_gt(int GT, dim3 grid, hipStream_t s, const uint16_t* q,
-                            const uint8_t* kc, const uint8_t* vc, int64_t num_blocks,
-                            const int32_t* bt, int max_blocks, const int32_t* ctx, int Hq, int Hkv,
-                            int max_ctx, const float* ks, int per_head, float sm,
-                            const DecodePlan& plan, float* ml, float* acc) {
-  if (GT == 4)
-    launch_split<FMT, DH, 4>(grid, s, q, kc, vc, num_blocks, bt, max_blocks, ctx, Hq, Hkv,
-                             max_ctx, ks, per_head, sm, plan, ml, acc);
-  else if (GT == 2)
-    launch_split<FMT, DH, 2>(grid, s, q, kc, vc, num_blocks, bt, max_blocks, ctx, Hq, Hkv,
-                             max_ctx, ks, per_head, sm, plan, ml, acc);
-  else
-    launch_split<FMT, DH, 1>(grid, s, q, kc, vc, num_blocks, bt, max_blocks, ctx, Hq, Hkv,
-                             max_ctx, ks, per_head, sm, plan, ml, acc);
 }
 
 hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8_t* kc,
@@ -341,45 +362,42 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
                          int max_ctx, const float* ks, const float* vs, int fmt, int per_head,
                          float softmax_scale, const DecodePlan& plan, void* ws, hipStream_t s) {
   const int G = Hq / Hkv;
-  const int GT = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
+  const int NH = heads_per_group(G);
   float* ml = reinterpret_cast<float*>(ws);
   float* acc = ml + (size_t)B * Hq * plan.nsplit * 2;
   const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / __builtin_sqrtf((float)dh);
-  dim3 grid(plan.nsplit, Hq / GT, B);
+  const dim3 grid(plan.nsplit, Hq / NH, B);
+  const int nw = plan.part_blocks / 2;  // waves per workgroup: one block pair each
+  const size_t lds = decode_lds_bytes(nw, NH, dh);
   if (max_ctx > 0) {
+#define KVQ_SPLIT(F, D, N)                                                                      \
+  decode_split_kernel<F, D, N><<<grid, 64 * N, lds, s>>>(q, kc, vc, num_blocks, bt, max_blocks, ctx, \
+                                                      Hq, Hkv, NH, max_ctx, ks, per_head, sm,     \
+                                                      plan.nsplit, ml, acc)
+#define KVQ_SPLIT_NP(F, D)                                        \
+  do {                                                            \
+    if (plan.part_blocks == 32) KVQ_SPLIT(F, D, 16);              \
+    else if (plan.part_blocks == 16) KVQ_SPLIT(F, D, 8);          \
+    else KVQ_SPLIT(F, D, 4);                                      \
+  } while (0)
     if (fmt == E4M3) {
-      if (dh == 128)
-        launch_split_gt<E4M3, 128>(GT, grid, s, q, kc, vc, num_blocks, bt, max_blocks, ctx, Hq,
-                                   Hkv, max_ctx, ks, per_head, sm, plan, ml, acc);
-      else
-        launch_split_gt<E4M3, 64>(GT, grid, s, q, kc, vc, num_blocks, bt, max_blocks, ctx, Hq,
-                                  Hkv, max_ctx, ks, per_head, sm, plan, ml, acc);
+      if (dh == 128) KVQ_SPLIT_NP(E4M3, 128); else KVQ_SPLIT_NP(E4M3, 64);
     } else {
-      if (dh == 128)
-        launch_split_gt<E5M2, 128>(GT, grid, s, q, kc, vc, num_blocks, bt, max_blocks, ctx, Hq,
-                                   Hkv, max_ctx, ks, per_head, sm, plan, ml, acc);
-      else
-        launch_split_gt<E5M2, 64>(GT, grid, s, q, kc, vc, num_blocks, bt, max_blocks, ctx, Hq,
-                                  Hkv, max_ctx, ks, per_head, sm, plan, ml, acc);
+      if (dh == 128) KVQ_SPLIT_NP(E5M2, 128); else KVQ_SPLIT_NP(E5M2, 64);
     }
+#undef KVQ_SPLIT_NP
+#undef KVQ_SPLIT
   }
-  dim3 cgrid(Hq, B);
+  const dim3 cgrid(Hq, B);
+#define KVQ_COMBINE(D, BF)                                                                     \
+  decode_combine_kernel<D, BF><<<cgrid, D, 0, s>>>(out, ml, acc, ctx, Hq, Hkv, max_ctx, vs,    \
+                                                   per_head, plan.part_blocks, plan.nsplit)
   if (dh == 128) {
-    if (out_bf16)
-      decode_combine_kernel<128, true><<<cgrid, 128, 0, s>>>(out, ml, acc, ctx, Hq, Hkv, max_ctx, vs,
-                                                             per_head, plan.part_blocks, plan.nsplit);
-    else
-      decode_combine_kernel<128, false><<<cgrid, 128, 0, s>>>(out, ml, acc, ctx, Hq, Hkv, max_ctx,
-                                                              vs, per_head, plan.part_blocks,
-                                                              plan.nsplit);
+    if (out_bf16) KVQ_COMBINE(128, true); else KVQ_COMBINE(128, false);
   } else {
-    if (out_bf16)
-      decode_combine_kernel<64, true><<<cgrid, 64, 0, s>>>(out, ml, acc, ctx, Hq, Hkv, max_ctx, vs,
-                                                           per_head, plan.part_blocks, plan.nsplit);
-    else
-      decode_combine_kernel<64, false><<<cgrid, 64, 0, s>>>(out, ml, acc, ctx, Hq, Hkv, max_ctx, vs,
-                                                            per_head, plan.part_blocks, plan.nsplit);
+    if (out_bf16) KVQ_COMBINE(64, true); else KVQ_COMBINE(64, false);
   }
+#undef KVQ_COMBINE
   return hipGetLastError();
 }
 

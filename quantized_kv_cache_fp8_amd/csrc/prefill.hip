@@ -19,9 +19,9 @@
 // workgroup has GT waves, one per query head of a GQA group, so every K/V tile
 // staged in LDS serves all GT heads.  Query tiles are issued longest-first
 // (the causal triangle makes late tiles the most expensive).  Per 64-key tile:
-// the workgroup copies K (4 cache blocks) into LDS row-major and V transposed
-// (channel-major, keys permuted into the order the B operand holds P in, so
-// each lane's A operand is one 32-byte run), then each wave runs 2*DH/64
+// the workgroup copies K (4 cache blocks) into LDS row-major and V, whose cache
+// tiles are already channel-major, with its keys permuted into the order the B
+// operand holds P in (so each lane's A operand is one 32-byte run), then each wave runs 2*DH/64
 // MFMAs for S^T, the online softmax in registers (one query per lane pair,
 // the running max only raised when a score exceeds it by more than 2^2), and
 // 2*DH/32 MFMAs for O^T.
@@ -139,32 +139,22 @@ __global__ __launch_bounds__(64 * GT) void prefill_kernel(
       *reinterpret_cast<uint4*>(k_lds + key * KROW + ch * 32) = a;
       *reinterpret_cast<uint4*>(k_lds + key * KROW + ch * 32 + 16) = bq;
     }
-    // ---- V tile -> LDS transposed: thread takes 4 keys x 4 channels, 4x4 byte transpose
-    for (int u = threadIdx.x; u < (kKT / 4) * (DH / 4); u += NT) {
-      const int kq = u / (DH / 4), dc = u % (DH / 4);
-      const int k0 = kq * 4;
-      const int bi = kt * 4 + (k0 >> 4);
-      uint32_t r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+    // ---- V tile -> LDS: the cache tiles are already channel-major ([dh][16]);
+    //      thread copies the 16 token bytes of one channel of one block and
+    //      scatters its four dwords to their key-permuted positions
+    for (int u = threadIdx.x; u < 4 * DH; u += NT) {
+      const int beta = u / DH, d = u - beta * DH;
+      const int bi = kt * 4 + beta;
+      uint4 w = make_uint4(0, 0, 0, 0);
       if (bi < nblk_ctx) {
         int64_t blk = btab[bi];
         blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
-        const uint8_t* src = vc + ((size_t)blk * Hkv + h) * tile_stride + (k0 & 15) * DH + dc * 4;
-        r0 = *reinterpret_cast<const uint32_t*>(src);
-        r1 = *reinterpret_cast<const uint32_t*>(src + DH);
-        r2 = *reinterpret_cast<const uint32_t*>(src + 2 * DH);
-        r3 = *reinterpret_cast<const uint32_t*>(src + 3 * DH);
+        w = *reinterpret_cast<const uint4*>(vc + ((size_t)blk * Hkv + h) * tile_stride + d * 16);
       }
-      // rows r0..r3 = keys k0..k0+3, bytes = channels 4dc..4dc+3
-      const uint32_t t0 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);  // a0 b0 a1 b1
-      const uint32_t t1 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);  // a2 b2 a3 b3
-      const uint32_t t2 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);  // c0 d0 c1 d1
-      const uint32_t t3 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);  // c2 d2 c3 d3
-      const int p = vt_pos(k0);
-      uint8_t* dst = v_lds + (dc * 4) * VROW + p;
-      *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
-      *reinterpret_cast<uint32_t*>(dst + VROW) = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
-      *reinterpret_cast<uint32_t*>(dst + 2 * VROW) = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-      *reinterpret_cast<uint32_t*>(dst + 3 * VROW) = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+      // dword i holds keys 16 beta + 4i .. + 3; vt_pos puts i = 0, 2 and i = 1, 3 side by side
+      uint8_t* row = v_lds + d * VROW + vt_pos(16 * beta);
+      *reinterpret_cast<uint2*>(row) = make_uint2(w.x, w.z);
+      *reinterpret_cast<uint2*>(row + 32) = make_uint2(w.y, w.w);
     }
     __syncthreads();
 

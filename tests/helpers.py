@@ -58,6 +58,16 @@ def row_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
     return worst
 
 
+def k_shape(wl):
+    """K cache: token-major tiles [num_blocks][Hkv][bs][dh]."""
+    return (wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh)
+
+
+def v_shape(wl):
+    """V cache: channel-major tiles [num_blocks][Hkv][dh][bs]."""
+    return (wl.paging.num_blocks, wl.Hkv, wl.dh, wl.bs)
+
+
 def same_codes(fmt: int, a: np.ndarray, b: np.ndarray) -> bool:
     """Bytes equal, except that any two NaN codes count as equal."""
     if np.array_equal(a, b):
@@ -93,9 +103,8 @@ class DecodeRun:
         self.slots = to_dev(wl.kv.slot_mapping)
         self.bt = to_dev(wl.paging.block_tables)
         self.cl = to_dev(wl.paging.context_lens)
-        shape = (wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh)
-        self.kc = torch.full(shape, SENTINEL, dtype=torch.uint8, device=dev)
-        self.vc = torch.full(shape, SENTINEL, dtype=torch.uint8, device=dev)
+        self.kc = torch.full(k_shape(wl), SENTINEL, dtype=torch.uint8, device=dev)
+        self.vc = torch.full(v_shape(wl), SENTINEL, dtype=torch.uint8, device=dev)
         self.ks = torch.empty(nh, dtype=torch.float32, device=dev)
         self.vs = torch.empty(nh, dtype=torch.float32, device=dev)
         self.kamax = torch.empty(nh, dtype=torch.float32, device=dev)
@@ -131,9 +140,8 @@ class DecodeRun:
 
     def oracle_caches(self):
         wl = self.wl
-        shape = (wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh)
-        kc = np.full(shape, SENTINEL, np.uint8)
-        vc = np.full(shape, SENTINEL, np.uint8)
+        kc = np.full(k_shape(wl), SENTINEL, np.uint8)
+        vc = np.full(v_shape(wl), SENTINEL, np.uint8)
         oracle.cache_write(wl.kv.k, wl.kv.v, wl.kv.slot_mapping, kc, vc, self.ks_ref, self.vs_ref,
                            self.fmt, self.gran)
         return kc, vc

@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 import workloads as W
-from helpers import ATTN_TOL, FMT_ID, SENTINEL, rel_err, row_rel_err, to_dev, to_np
+from helpers import (ATTN_TOL, FMT_ID, SENTINEL, k_shape, rel_err, row_rel_err, to_dev, to_np,
+                     v_shape)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,9 +29,8 @@ class PrefillRun:
         self.vs_ref = oracle.calibrate(wl.kv.v, self.fmt, self.kg)[1]
         dev = torch.device("cuda:0")
         self.q = to_dev(wl.q)
-        shape = (wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh)
-        self.kc = torch.full(shape, SENTINEL, dtype=torch.uint8, device=dev)
-        self.vc = torch.full(shape, SENTINEL, dtype=torch.uint8, device=dev)
+        self.kc = torch.full(k_shape(wl), SENTINEL, dtype=torch.uint8, device=dev)
+        self.vc = torch.full(v_shape(wl), SENTINEL, dtype=torch.uint8, device=dev)
         nq = wl.Hq if self.qg == oracle.GRAN_HEAD else 1
         nk = wl.Hkv if self.kg == oracle.GRAN_HEAD else 1
         self.qs = torch.empty(nq, device=dev)
@@ -62,9 +62,8 @@ class PrefillRun:
 
     def oracle_caches(self):
         wl = self.wl
-        shape = (wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh)
-        kc = np.full(shape, SENTINEL, np.uint8)
-        vc = np.full(shape, SENTINEL, np.uint8)
+        kc = np.full(k_shape(wl), SENTINEL, np.uint8)
+        vc = np.full(v_shape(wl), SENTINEL, np.uint8)
         oracle.cache_write(wl.kv.k, wl.kv.v, wl.kv.slot_mapping, kc, vc, self.ks_ref, self.vs_ref,
                            self.fmt, self.kg)
         return kc, vc

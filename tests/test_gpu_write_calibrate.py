@@ -21,7 +21,7 @@ def gpu_write(k_bits, v_bits, slots, nb, Hkv, dh, ks, vs, fmt, gran):
     import torch
     import quantized_kv_cache_fp8_amd as K
     kc = torch.full((nb, Hkv, 16, dh), SENTINEL, dtype=torch.uint8, device="cuda:0")
-    vc = torch.full_like(kc, SENTINEL)
+    vc = torch.full((nb, Hkv, dh, 16), SENTINEL, dtype=torch.uint8, device="cuda:0")
     K.kvq_cache_write(to_dev(k_bits), to_dev(v_bits), to_dev(slots), kc, vc,
                       to_dev(np.asarray(ks, np.float32)), to_dev(np.asarray(vs, np.float32)),
                       fmt, gran)
@@ -31,7 +31,7 @@ def gpu_write(k_bits, v_bits, slots, nb, Hkv, dh, ks, vs, fmt, gran):
 
 def oracle_write(k_bits, v_bits, slots, nb, Hkv, dh, ks, vs, fmt, gran):
     kc = np.full((nb, Hkv, 16, dh), SENTINEL, np.uint8)
-    vc = kc.copy()
+    vc = np.full((nb, Hkv, dh, 16), SENTINEL, np.uint8)
     oracle.cache_write(k_bits, v_bits, slots, kc, vc, np.asarray(ks, np.float32),
                        np.asarray(vs, np.float32), fmt, gran)
     return kc, vc
@@ -78,6 +78,23 @@ def test_write_skips_padding_and_out_of_range_slots():
     rk, rv = oracle_write(k, v, slots, 4, Hkv, dh, [0.01], [0.02], 0, 0)
     assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
     assert (gk == SENTINEL).sum() == (rk == SENTINEL).sum() > 0
+
+
+@pytest.mark.parametrize("start", [0, 2, 5])
+def test_write_partial_and_misaligned_runs(start):
+    """Consecutive slots that start off a 4-token boundary, a ragged token count
+    and a gap in the middle: every mix of the dword and byte store paths."""
+    g = W.rng(9 + start)
+    Hkv, dh, T = 3, 128, 37
+    k = W.normal_bf16(g, (T, Hkv, dh))
+    v = W.normal_bf16(g, (T, Hkv, dh))
+    slots = np.arange(start, start + T, dtype=np.int64)
+    slots[20:] += 7  # a gap: later tokens land in other blocks at other offsets
+    gk, gv = gpu_write(k, v, slots, 5, Hkv, dh, [0.02, 0.03, 0.05], [0.01, 0.04, 0.2], 1,
+                       oracle.GRAN_HEAD)
+    rk, rv = oracle_write(k, v, slots, 5, Hkv, dh, [0.02, 0.03, 0.05], [0.01, 0.04, 0.2], 1,
+                          oracle.GRAN_HEAD)
+    assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
 
 
 def test_write_empty_batch_is_a_no_op():

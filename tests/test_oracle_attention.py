@@ -20,16 +20,20 @@ def build_cache(paging, kv, Hkv, dh, fmt, gran, g):
     ks = (g.uniform(0.005, 0.05, n)).astype(np.float32)
     vs = (g.uniform(0.005, 0.05, n)).astype(np.float32)
     kc = np.zeros((paging.num_blocks, Hkv, paging.bs, dh), np.uint8)
-    vc = np.zeros_like(kc)
+    vc = np.zeros((paging.num_blocks, Hkv, dh, paging.bs), np.uint8)
     oracle.cache_write(kv.k, kv.v, kv.slot_mapping, kc, vc, ks, vs, fmt, gran)
     return kc, vc, ks, vs
 
 
-def gather(cache, paging, b, n, fmt, scales, gran):
-    """Dequantized [Hkv, n, dh] history of sequence b, read through the block table."""
+def gather(cache, paging, b, n, fmt, scales, gran, kind):
+    """Dequantized [Hkv, n, dh] history of sequence b, read through the block
+    table; K tiles are [bs][dh] (token-major), V tiles [dh][bs] (channel-major)."""
     pos = np.arange(n)
     blk = paging.block_tables[b, pos // paging.bs]
-    codes = cache[blk, :, pos % paging.bs, :]  # [n, Hkv, dh]
+    if kind == "k":
+        codes = cache[blk, :, pos % paging.bs, :]  # [n, Hkv, dh]
+    else:
+        codes = cache[blk, :, :, pos % paging.bs]  # [n, Hkv, dh]
     Hkv = cache.shape[1]
     s = np.asarray(scales, np.float64).reshape(-1)
     s = s if gran == oracle.GRAN_HEAD else np.repeat(s, Hkv)
@@ -60,8 +64,8 @@ def test_decode_matches_library_sdpa(fmt, gran):
     qf = W.bf16_bits_to_f32(q).astype(np.float64)
     for b in range(B):
         n = int(paging.context_lens[b])
-        k = gather(kc, paging, b, n, fmt, ks, gran)
-        v = gather(vc, paging, b, n, fmt, vs, gran)
+        k = gather(kc, paging, b, n, fmt, ks, gran, "k")
+        v = gather(vc, paging, b, n, fmt, vs, gran, "v")
         ref = sdpa(qf[b][:, None, :], k, v, Hq // Hkv)[:, 0, :]
         np.testing.assert_allclose(out[b], ref, rtol=1e-12, atol=1e-12)
 
@@ -77,7 +81,7 @@ def test_decode_special_cases():
     q = W.normal_bf16(g, (1, Hq, dh))
     out = oracle.decode_attn(q, kc, vc, paging.block_tables, paging.context_lens, ks, vs, fmt,
                              gran)
-    v0 = gather(vc, paging, 0, 1, fmt, vs, gran)[:, 0, :]
+    v0 = gather(vc, paging, 0, 1, fmt, vs, gran, "v")[:, 0, :]
     assert np.array_equal(out[0], np.repeat(v0, Hq // Hkv, axis=0))
     # q = 0: uniform weights, the output is the mean of the dequantized values
     paging = W.make_paging(g, [45], bs)
@@ -86,14 +90,14 @@ def test_decode_special_cases():
     q0 = np.zeros((1, Hq, dh), np.uint16)
     out = oracle.decode_attn(q0, kc, vc, paging.block_tables, paging.context_lens, ks, vs, fmt,
                              gran)
-    vmean = gather(vc, paging, 0, 45, fmt, vs, gran).mean(axis=1)
+    vmean = gather(vc, paging, 0, 45, fmt, vs, gran, "v").mean(axis=1)
     np.testing.assert_allclose(out[0], np.repeat(vmean, 2, axis=0), rtol=1e-13, atol=1e-15)
     # every key equal: same uniform weights for any q
     kv.k[:] = kv.k[0]
     kc, vc, ks, vs = build_cache(paging, kv, Hkv, dh, fmt, gran, g)
     out = oracle.decode_attn(q, kc, vc, paging.block_tables, paging.context_lens, ks, vs, fmt,
                              gran)
-    vmean = gather(vc, paging, 0, 45, fmt, vs, gran).mean(axis=1)
+    vmean = gather(vc, paging, 0, 45, fmt, vs, gran, "v").mean(axis=1)
     np.testing.assert_allclose(out[0], np.repeat(vmean, 2, axis=0), rtol=1e-13, atol=1e-15)
     # one dominant logit: the output is (almost exactly) that key's value row
     kv = W.make_kv(g, paging, Hkv, dh)
@@ -105,7 +109,7 @@ def test_decode_special_cases():
     one = np.ones(1, np.float32)
     out = oracle.decode_attn(W.f32_to_bf16_bits(qd), kc, vc, paging.block_tables,
                              paging.context_lens, one, one, fmt, gran, softmax_scale=1.0)
-    v30 = gather(vc, paging, 0, 45, fmt, one, gran)[:, 30, :]
+    v30 = gather(vc, paging, 0, 45, fmt, one, gran, "v")[:, 30, :]
     np.testing.assert_allclose(out[0], np.repeat(v30, 2, axis=0), rtol=0, atol=1e-100)
 
 
@@ -126,7 +130,7 @@ def test_decode_invariant_under_key_order_and_block_placement():
     kv2 = W.KVBatch(kv.k[perm].copy(), kv.v[perm].copy(), paging2.slots(0, np.arange(70)),
                     kv.seq_offsets)
     kc2 = np.zeros((paging2.num_blocks, Hkv, 16, dh), np.uint8)
-    vc2 = np.zeros_like(kc2)
+    vc2 = np.zeros((paging2.num_blocks, Hkv, dh, 16), np.uint8)
     oracle.cache_write(kv2.k, kv2.v, kv2.slot_mapping, kc2, vc2, ks, vs, fmt, gran)
     out2 = oracle.decode_attn(q, kc2, vc2, paging2.block_tables, paging2.context_lens, ks, vs,
                               fmt, gran)
@@ -180,8 +184,8 @@ def test_prefill_matches_library_sdpa_with_causal_offset(fmt):
     for b in range(3):
         lo, hi = wl.cu_seqlens[b], wl.cu_seqlens[b + 1]
         n = int(wl.paging.context_lens[b])
-        k = gather(kc, wl.paging, b, n, fmt, ks, oracle.GRAN_HEAD)
-        v = gather(vc, wl.paging, b, n, fmt, vs, oracle.GRAN_HEAD)
+        k = gather(kc, wl.paging, b, n, fmt, ks, oracle.GRAN_HEAD, "k")
+        v = gather(vc, wl.paging, b, n, fmt, vs, oracle.GRAN_HEAD, "v")
         qlen = hi - lo
         pos = n - qlen + np.arange(qlen)
         mask = np.arange(n)[None, :] <= pos[:, None]

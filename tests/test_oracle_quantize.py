@@ -169,7 +169,7 @@ def test_cache_write_places_every_code(fmt, gran):
     sm = kv.slot_mapping.copy()
     sm[5] = -1  # a padding token: skipped
     kc = np.full((paging.num_blocks, Hkv, bs, dh), 0xA5, np.uint8)
-    vc = kc.copy()
+    vc = np.full((paging.num_blocks, Hkv, dh, bs), 0xA5, np.uint8)  # channel-major V tiles
     oracle.cache_write(kv.k, kv.v, sm, kc, vc, ks, vs, fmt, gran)
     touched = np.zeros(kc.shape[:3], bool)
     for t in range(len(sm)):
@@ -182,9 +182,10 @@ def test_cache_write_places_every_code(fmt, gran):
             xk = (W.bf16_bits_to_f32(kv.k[t, h]) / s_k).astype(np.float32)
             xv = (W.bf16_bits_to_f32(kv.v[t, h]) / s_v).astype(np.float32)
             check_against_torch(fmt, kc[blk, h, off], xk)
-            check_against_torch(fmt, vc[blk, h, off], xv)
+            check_against_torch(fmt, vc[blk, h, :, off], xv)
             touched[blk, h, off] = True
-    assert np.all(kc[~touched] == 0xA5) and np.all(vc[~touched] == 0xA5)
+    assert np.all(kc[~touched] == 0xA5)
+    assert np.all(vc.transpose(0, 1, 3, 2)[~touched] == 0xA5)
     # the skipped token's slot was left alone
     blk, off = kv.slot_mapping[5] // bs, kv.slot_mapping[5] % bs
-    assert np.all(kc[blk, :, off] == 0xA5)
+    assert np.all(kc[blk, :, off] == 0xA5) and np.all(vc[blk, :, :, off] == 0xA5)
