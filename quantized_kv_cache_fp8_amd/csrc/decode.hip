@@ -14,22 +14,27 @@
 // workgroup of 4 waves owns one split (part_blocks cache blocks of 16 tokens)
 // of one sequence and the NH <= 16 query heads that share one KV head, so
 // every K/V byte is read from HBM once and serves all NH heads.  Wave w takes
-// block pairs w, w+4, ... of the split.  Two passes over the split:
+// block pairs w, w + 4, ... of the split, one pair (32 tokens) per step:
 //
-//   pass 1  S = Q K^T on v_mfma_f32_16x16x32_bf16: A = the NH query rows
-//           (bf16, rows NH..15 zero), B = 16 keys of one block (fp8 -> bf16
-//           in registers; each lane loads 16 contiguous bytes of one key).
-//           Scores (log2 domain, masked past the context) go to LDS; the
-//           per-head maximum of the split is reduced with DPP and LDS.
-//   middle  p = exp2(z - M) once per (token, head), stored as f16 in LDS,
-//           row sums l accumulated with LDS atomics.
-//   pass 2  O += P V on v_mfma_f32_16x16x32_f16: A = P of 32 tokens (a
-//           block pair), B = V from the channel-major tile (each lane loads
-//           the 8 contiguous token bytes of one channel, fp8 -> f16).
+//   S = Q K^T on v_mfma_f32_16x16x32_bf16: A = the NH query rows (bf16, rows
+//     NH..15 zero), B = the 16 tokens of a block (codes -> bf16 in registers;
+//     each lane holds 32 code bytes of one token).
+//   online softmax per row in the log2 domain, the running max raised lazily;
+//     the S tile and the O tile map rows to lanes the same way, so rescaling
+//     is lane-local.
+//   O += P V on v_mfma_f32_16x16x32_f16: A = P of the pair (transposed
+//     through a 1 KB per-wave LDS scratch), B = V from the channel-major tile
+//     (each lane holds the 8 contiguous token bytes of one channel, -> f16).
 //
-// The split's partial (M, l, O) goes to the workspace; a second kernel merges
-// the splits (log-sum-exp) and applies sV.  Loads of the next block pair are
-// issued before the current pair is computed.
+// The next pair's keys are loaded as soon as the current keys are consumed and
+// its values as soon as the current values are; registers are not doubled.  The
+// 4 waves' (m, l, O) are merged through LDS and the split's partial goes to
+// the workspace; a second kernel merges the splits (log-sum-exp), applies sV.
+//
+// Q K^T stays on bf16 (not FP8) matrix cores on purpose: the FP8 MFMA's
+// internal accumulation keeps only about 16 bits relative to the largest
+// product, which at decode-sized logits (tens in log2 units) is visible in
+// the output, whereas bf16 products accumulate in full fp32.
 #include "codec.hpp"
 #include "launch.hpp"
 
@@ -38,7 +43,13 @@ namespace kvq {
 // Largest split (cache blocks per workgroup): 8, 16 or 32.  Larger splits mean
 // fewer partial results to merge, smaller ones more workgroups in flight.
 #ifndef KVQ_DECODE_MAX_SPLIT_BLOCKS
-#define KVQ_DECODE_MAX_SPLIT_BLOCKS 16
+#define KVQ_DECODE_MAX_SPLIT_BLOCKS 32
+#endif
+// Whether a wave loads its next block pair into a second register set before
+// computing the current one (true), or into the current set as each half of
+// it is consumed: keys after Q K^T, values after P V (false).
+#ifndef KVQ_DECODE_PREFETCH
+#define KVQ_DECODE_PREFETCH false
 #endif
 
 namespace {
@@ -65,18 +76,23 @@ __device__ __forceinline__ float max16(float x) {
   return x;
 }
 
-// 8 codes (two dwords) -> 8 exact bf16 / f16 values
+// 8 codes (two dwords) -> 8 exact bf16 / f16 values, assembled as one 128-bit
+// value so the converts land directly in the MFMA operand registers
 template <int FMT>
 __device__ __forceinline__ bf16x8 codes_to_bf16x8(uint32_t a, uint32_t b) {
-  const bf16x2 p0 = dec2_bf16<FMT, false>(a), p1 = dec2_bf16<FMT, true>(a);
-  const bf16x2 p2 = dec2_bf16<FMT, false>(b), p3 = dec2_bf16<FMT, true>(b);
-  return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+  const uint4 u = make_uint4(__builtin_bit_cast(uint32_t, dec2_bf16<FMT, false>(a)),
+                             __builtin_bit_cast(uint32_t, dec2_bf16<FMT, true>(a)),
+                             __builtin_bit_cast(uint32_t, dec2_bf16<FMT, false>(b)),
+                             __builtin_bit_cast(uint32_t, dec2_bf16<FMT, true>(b)));
+  return __builtin_bit_cast(bf16x8, u);
 }
 template <int FMT>
 __device__ __forceinline__ f16x8 codes_to_f16x8(uint32_t a, uint32_t b) {
-  const f16x2 p0 = dec2_f16<FMT, false>(a), p1 = dec2_f16<FMT, true>(a);
-  const f16x2 p2 = dec2_f16<FMT, false>(b), p3 = dec2_f16<FMT, true>(b);
-  return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+  const uint4 u = make_uint4(__builtin_bit_cast(uint32_t, dec2_f16<FMT, false>(a)),
+                             __builtin_bit_cast(uint32_t, dec2_f16<FMT, true>(a)),
+                             __builtin_bit_cast(uint32_t, dec2_f16<FMT, false>(b)),
+                             __builtin_bit_cast(uint32_t, dec2_f16<FMT, true>(b)));
+  return __builtin_bit_cast(f16x8, u);
 }
 
 __device__ __forceinline__ int64_t clamp_block(int64_t blk, int64_t num_blocks) {
@@ -84,28 +100,34 @@ __device__ __forceinline__ int64_t clamp_block(int64_t blk, int64_t num_blocks) 
 }
 }  // namespace
 
-// dynamic LDS bytes for one workgroup of nw waves: per-wave P transpose
-// scratch [nw][16 rows][32 tokens] f16, then the wave-merge buffers.
-static size_t decode_lds_bytes(int nw, int NH, int dh) {
-  return (size_t)nw * 16 * 32 * sizeof(_Float16) + 2 * (size_t)nw * 16 * sizeof(float) +
-         (size_t)nw * NH * dh * sizeof(float);
+// dynamic LDS bytes for one workgroup: per-wave P transpose scratch
+// [4][16 rows][32 tokens] f16, then the wave-merge buffers.
+static size_t decode_lds_bytes(int NH, int dh) {
+  return 4 * 16 * 32 * sizeof(_Float16) + 2 * 4 * 16 * sizeof(float) +
+         (size_t)4 * NH * dh * sizeof(float);
 }
 
 // Lazy running max: it only moves when a score exceeds it by more than 2^8,
 // so p = exp2(z - m) <= 256 (safe in f16) and accumulator rescales are rare.
 constexpr float kLazyTau = 8.0f;
 
-template <int FMT, int DH, int NW>
-__global__ __launch_bounds__(64 * NW) void decode_split_kernel(
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Channel slot i (0 or 1) of lane group g4: 16 contiguous channels at
+// 16 g4 + i * DH / 2, present when g4 < DH / 32 (dh = 64 uses two groups).
+template <int DH>
+__device__ __forceinline__ bool chan_group_live(int g4) { return g4 < DH / 32; }
+
+template <int FMT, int DH, int NPW, bool PF>
+__global__ __launch_bounds__(256) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ vc, int64_t num_blocks, const int32_t* __restrict__ bt,
     int max_blocks, const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int NH, int max_ctx,
     const float* __restrict__ ks, int per_head, float sm_scale, int nsplit,
     float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
-  constexpr int NK = DH / 64;   // 16-byte key loads per block per lane
-  constexpr int NQ = DH / 32;   // bf16 MFMAs per block (k = 32 channels each)
   constexpr int NV = DH / 16;   // f16 MFMAs per block pair (16 channels each)
-  constexpr int PB = 2 * NW;    // blocks per split: one block pair per wave
+  constexpr int PB = 8 * NPW;   // blocks per split: 4 waves x NPW pairs x 2
+  constexpr int HALF = DH / 2;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int split = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
@@ -127,51 +149,68 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, g4 = lane >> 4;
   const bool head_real = c16 < NH;
+  const bool chan_live = chan_group_live<DH>(g4);
   _Float16* ptr = reinterpret_cast<_Float16*>(smem) + wave * 16 * 32;  // this wave's P scratch
-  float* wm = reinterpret_cast<float*>(smem + NW * 16 * 32 * sizeof(_Float16));
-  float* wl = wm + NW * 16;
-  float* wo = wl + NW * 16;  // [NW][NH][DH]
+  float* wm = reinterpret_cast<float*>(smem + 4 * 16 * 32 * sizeof(_Float16));
+  float* wl = wm + 4 * 16;
+  float* wo = wl + 4 * 16;  // [4][NH][DH]
   const int32_t* btab = bt + (size_t)b * max_blocks + (size_t)split * PB;
   const size_t tile = (size_t)kBlockSize * DH;  // bytes per (block, head) tile
   const int eb = g4 >> 1, tk = 8 * (g4 & 1);   // V: this lane's block in a pair, token half
 
-  // this wave's block pair: blocks 2 wave and 2 wave + 1 of the split
-  const int p = wave;
-  const bool active = p < npair;
-  uint4 kb[2][NK];  // lane: 16 bytes of token c16 of each block, channels 64 m + 16 g4 ..
-  uint2 vb[NV];     // lane: tokens tk .. tk + 7 of block eb, channel 16 n + c16
+  // A block pair (2 blocks of 16 tokens).  K: lane holds the 32 code bytes of
+  // token c16 in channel slots 16 g4 + [0,16) and DH/2 + 16 g4 + [0,16).
+  // V: lane holds tokens tk .. tk + 7 of block eb for channel 16 n + c16.
+  struct Pair {
+    i32x8 k[2];
+    uint2 v[NV];
+  };
+  auto load_k = [&](int p, Pair& P) {
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int bi = 2 * p + e;
-    if (bi < nblk) {
-      const int64_t blk = clamp_block(btab[bi], num_blocks);
-      const uint8_t* src = kc + ((size_t)blk * Hkv + h) * tile + c16 * DH + 16 * g4;
-#pragma unroll
-      for (int m = 0; m < NK; ++m) kb[e][m] = *reinterpret_cast<const uint4*>(src + 64 * m);
+    for (int e = 0; e < 2; ++e) {
+      const int bi = 2 * p + e;
+      P.k[e] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (bi < nblk && chan_live) {
+        const int64_t blk = clamp_block(btab[bi], num_blocks);
+        const uint8_t* src = kc + ((size_t)blk * Hkv + h) * tile + c16 * DH + 16 * g4;
+        const uint4 a0 = *reinterpret_cast<const uint4*>(src);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(src + HALF);
+        P.k[e] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                       (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      }
     }
-  }
-  {
+  };
+  auto load_v = [&](int p, Pair& P) {
     const int bi = 2 * p + eb;
     if (bi < nblk) {
       const int64_t blk = clamp_block(btab[bi], num_blocks);
       const uint8_t* src = vc + ((size_t)blk * Hkv + h) * tile + c16 * kBlockSize + tk;
 #pragma unroll
       for (int n = 0; n < NV; ++n)
-        vb[n] = *reinterpret_cast<const uint2*>(src + 16 * n * kBlockSize);
+        P.v[n] = *reinterpret_cast<const uint2*>(src + 16 * n * kBlockSize);
     } else {
 #pragma unroll
-      for (int n = 0; n < NV; ++n) vb[n] = make_uint2(0, 0);  // no token: exact zeros
+      for (int n = 0; n < NV; ++n) P.v[n] = make_uint2(0, 0);  // no token: exact zeros
     }
-  }
+  };
+  auto load_pair = [&](int p, Pair& P) {
+    load_k(p, P);
+    load_v(p, P);
+  };
 
-  // A operand of S = Q K^T: query row c16, channels 64(j/2) + 16 g4 + 8(j%2) + 0..7
-  bf16x8 qop[NQ];
+  Pair cur, nxt;
+  int p = wave;
+  if (p < npair) load_pair(p, cur);
+
+  // A operand of S = Q K^T (bf16, exact): query row c16 in the channel slots
+  // of the K operand: j = 2 i + c covers channels 16 g4 + i * DH/2 + 8 c + 0..7
+  bf16x8 qop[4];
 #pragma unroll
-  for (int j = 0; j < NQ; ++j) {
+  for (int j = 0; j < 4; ++j) {
     uint4 w = make_uint4(0, 0, 0, 0);
-    if (head_real)
-      w = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + hq0 + c16) * DH + 64 * (j >> 1) +
-                                          16 * g4 + 8 * (j & 1));
+    if (head_real && chan_live)
+      w = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + hq0 + c16) * DH + 16 * g4 +
+                                          (j >> 1) * HALF + 8 * (j & 1));
     qop[j] = __builtin_bit_cast(bf16x8, w);
   }
   const float zc = sm_scale * ks[per_head ? h : 0] * kLog2e;
@@ -183,34 +222,50 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
 #pragma unroll
   for (int n = 0; n < NV; ++n) O[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (active) {
-    // ---- S for both blocks: lane holds rows 4 g4 + r for token c16 of each block
+#pragma unroll 1
+  for (; p < npair; p += 4) {
+    if (PF && p + 4 < npair) load_pair(p + 4, nxt);
+    // ---- S for both blocks on bf16 matrix cores (codes -> bf16 is exact):
+    //      lane holds rows 4 g4 + r for token c16
     float z[2][4];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       f32x4 S = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int m = 0; m < NK; ++m) {
-        const bf16x8 k0 = codes_to_bf16x8<FMT>(kb[e][m].x, kb[e][m].y);
-        const bf16x8 k1 = codes_to_bf16x8<FMT>(kb[e][m].z, kb[e][m].w);
-        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[2 * m], k0, S, 0, 0, 0);
-        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[2 * m + 1], k1, S, 0, 0, 0);
-      }
+      for (int j = 0; j < 4; ++j)
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            qop[j], codes_to_bf16x8<FMT>((uint32_t)cur.k[e][2 * j], (uint32_t)cur.k[e][2 * j + 1]),
+            S, 0, 0, 0);
       const bool valid = tok0 + (2 * p + e) * kBlockSize + c16 < ctx;
 #pragma unroll
       for (int r = 0; r < 4; ++r) z[e][r] = valid ? S[r] * zc : -__builtin_inff();
     }
-    // ---- softmax state per row (one pair per wave: the running max is set once)
+    // this pair's K registers are free: the next pair's keys load during the
+    // softmax and P V below
+    if (!PF && p + 4 < npair) load_k(p + 4, cur);
+    // ---- online softmax per row; the rescale factor is lane-local because
+    //      the O tile uses the same row -> (g4, r) mapping as the S tile.  The
+    //      running max moves rarely, so the rescale is one wave-uniform branch.
+    float mt[4];
+    bool need = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float mt = max16(__builtin_fmaxf(z[0][r], z[1][r]));
-      if (mt > m_run[r] + kLazyTau) {
-        const float f = __builtin_amdgcn_exp2f(m_run[r] - mt);
+      mt[r] = max16(__builtin_fmaxf(z[0][r], z[1][r]));
+      need |= mt[r] > m_run[r] + kLazyTau;
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool up = mt[r] > m_run[r] + kLazyTau;
+        const float f = up ? __builtin_amdgcn_exp2f(m_run[r] - mt[r]) : 1.0f;
+        m_run[r] = up ? mt[r] : m_run[r];
         l_part[r] *= f;
 #pragma unroll
         for (int n = 0; n < NV; ++n) O[n][r] *= f;
-        m_run[r] = mt;
       }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
       const float p0 = __builtin_amdgcn_exp2f(z[0][r] - m_run[r]);
       const float p1 = __builtin_amdgcn_exp2f(z[1][r] - m_run[r]);
       l_part[r] += p0 + p1;
@@ -218,16 +273,21 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
       ptr[row * 32 + c16] = (_Float16)p0;
       ptr[row * 32 + 16 + c16] = (_Float16)p1;
     }
-    // ---- P V: A = P rows (head c16), tokens 8 g4 .. 8 g4 + 7 of the pair
+    // ---- P V on f16 matrix cores: A = P rows (head c16), tokens 8 g4 .. 8 g4 + 7
     f16x8 pop = {};
     if (head_real) pop = *reinterpret_cast<const f16x8*>(ptr + c16 * 32 + 8 * g4);
 #pragma unroll
     for (int n = 0; n < NV; ++n)
       O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-          pop, codes_to_f16x8<FMT>(vb[n].x, vb[n].y), O[n], 0, 0, 0);
+          pop, codes_to_f16x8<FMT>(cur.v[n].x, cur.v[n].y), O[n], 0, 0, 0);
+    if (PF) {
+      cur = nxt;
+    } else if (p + 4 < npair) {
+      load_v(p + 4, cur);  // V registers are free now
+    }
   }
 
-  // ---- merge the NW waves through LDS and write the split's partial
+  // ---- merge the 4 waves through LDS and write the split's partial
   float l_row[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -251,14 +311,14 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
     }
   }
   __syncthreads();
-  for (int o = tid; o < NH * DH; o += 64 * NW) {
+  for (int o = tid; o < NH * DH; o += 256) {
     const int row = o / DH, d = o - row * DH;
     float M = kNegBig;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = __builtin_fmaxf(M, wm[w * 16 + row]);
+    for (int w = 0; w < 4; ++w) M = __builtin_fmaxf(M, wm[w * 16 + row]);
     float a = 0.0f, L = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
+    for (int w = 0; w < 4; ++w) {
       const float f = __builtin_amdgcn_exp2f(wm[w * 16 + row] - M);
       a += f * wo[(w * NH + row) * DH + d];
       L += f * wl[w * 16 + row];
@@ -367,18 +427,17 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
   float* acc = ml + (size_t)B * Hq * plan.nsplit * 2;
   const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / __builtin_sqrtf((float)dh);
   const dim3 grid(plan.nsplit, Hq / NH, B);
-  const int nw = plan.part_blocks / 2;  // waves per workgroup: one block pair each
-  const size_t lds = decode_lds_bytes(nw, NH, dh);
+  const size_t lds = decode_lds_bytes(NH, dh);
   if (max_ctx > 0) {
-#define KVQ_SPLIT(F, D, N)                                                                      \
-  decode_split_kernel<F, D, N><<<grid, 64 * N, lds, s>>>(q, kc, vc, num_blocks, bt, max_blocks, ctx, \
-                                                      Hq, Hkv, NH, max_ctx, ks, per_head, sm,     \
-                                                      plan.nsplit, ml, acc)
-#define KVQ_SPLIT_NP(F, D)                                        \
-  do {                                                            \
-    if (plan.part_blocks == 32) KVQ_SPLIT(F, D, 16);              \
-    else if (plan.part_blocks == 16) KVQ_SPLIT(F, D, 8);          \
-    else KVQ_SPLIT(F, D, 4);                                      \
+#define KVQ_SPLIT(F, D, N, PF)                                                                \
+  decode_split_kernel<F, D, N, PF><<<grid, 256, lds, s>>>(q, kc, vc, num_blocks, bt, max_blocks, \
+                                                          ctx, Hq, Hkv, NH, max_ctx, ks,         \
+                                                          per_head, sm, plan.nsplit, ml, acc)
+#define KVQ_SPLIT_NP(F, D)                                                    \
+  do {                                                                        \
+    if (plan.part_blocks == 32) KVQ_SPLIT(F, D, 4, KVQ_DECODE_PREFETCH);      \
+    else if (plan.part_blocks == 16) KVQ_SPLIT(F, D, 2, KVQ_DECODE_PREFETCH); \
+    else KVQ_SPLIT(F, D, 1, false);                                           \
   } while (0)
     if (fmt == E4M3) {
       if (dh == 128) KVQ_SPLIT_NP(E4M3, 128); else KVQ_SPLIT_NP(E4M3, 64);
