@@ -8,23 +8,30 @@
 //   V tiles are channel-major [num_blocks][Hkv][dh][bs]
 // Both attention kernels contract V over tokens, so a channel-major V tile
 // hands every matrix-core operand a contiguous run of tokens; the transpose
-// is paid here, once per byte, in registers.
+// is paid here, once per byte.
 //
-// Each thread owns four consecutive tokens x four consecutive channels of one
-// KV head, for both K and V (consecutive threads take consecutive channel
-// quads, so the bf16 loads are coalesced rows).  K codes go out as one dword
-// per token.  When the four tokens occupy four consecutive, 4-aligned slots
-// (the normal case: tokens of one sequence written in order) the 4x4 V code
-// block is transposed with v_perm_b32 and goes out as one dword per channel;
-// otherwise each V code is stored as a byte.  Per-head scales and their
-// correctly rounded reciprocals are staged once per workgroup in LDS.
+// A workgroup owns a chunk of 64 consecutive tokens of one KV head.
+//   1. The chunk's slots go to LDS; wave 0 marks the start of every run of
+//      tokens whose slots are consecutive inside one aligned group of four
+//      slots ("quad"), with the run's length (1..4).
+//   2. Every thread quantizes 4 tokens x 4 channels of K and V (bf16 loads of
+//      consecutive threads are one row).  K codes go straight out, one dword
+//      per token; the 4x4 V code block is transposed with v_perm_b32 and
+//      parked in an LDS tile [dh][64 tokens].
+//   3. For each run and channel one thread reads the run's codes from the LDS
+//      tile and stores them: one dword when the run fills its quad (the
+//      normal case for tokens of a sequence written in order, whatever its
+//      starting offset), single bytes otherwise (a decode step's one new
+//      token per sequence, the ends of a chunk or of a sequence).
+// Tokens with a negative slot, or a slot outside the pool, are skipped.
 #include "codec.hpp"
 #include "launch.hpp"
 
 namespace kvq {
 
-constexpr int kMaxHeadsLds = 256;
-constexpr int kBs = 16;  // tokens per cache block
+constexpr int kBs = 16;     // tokens per cache block
+constexpr int kChunk = 64;  // tokens per workgroup (one wave marks the runs)
+constexpr int kRowDw = kChunk / 4 + 1;  // LDS V-tile row: 16 dwords of codes + 1 pad
 
 template <int FMT>
 __device__ __forceinline__ uint32_t quant4(uint2 w, float s, float rs) {
@@ -32,42 +39,55 @@ __device__ __forceinline__ uint32_t quant4(uint2 w, float s, float rs) {
                    quotient(bf16lo(w.y), s, rs), quotient(bf16hi(w.y), s, rs));
 }
 
-template <int FMT>
+template <int FMT, int DH>
 __global__ __launch_bounds__(256) void cache_write_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t T, int Hkv,
-    int dh_shift, uint32_t units, const int64_t* __restrict__ slot_mapping,
-    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, int64_t num_slots,
-    const float* __restrict__ ks, const float* __restrict__ vs, int per_head) {
-  __shared__ float s_k[kMaxHeadsLds], r_k[kMaxHeadsLds], s_v[kMaxHeadsLds], r_v[kMaxHeadsLds];
-  const int nh = per_head ? Hkv : 1;
-  for (int i = threadIdx.x; i < nh; i += blockDim.x) {
-    const float a = ks[i], b = vs[i];
-    s_k[i] = a;
-    r_k[i] = recip_rn(a);
-    s_v[i] = b;
-    r_v[i] = recip_rn(b);
+    const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+    int64_t num_slots, const float* __restrict__ ks, const float* __restrict__ vs, int per_head) {
+  constexpr int kCq = DH / 4;  // channel quads per token row
+  __shared__ int64_t s_slot[kChunk];
+  __shared__ uint32_t s_run[kChunk];  // token index | run length << 8, compacted
+  __shared__ int s_nrun;
+  __shared__ uint32_t s_vt[DH * kRowDw];
+
+  const int h = (int)(blockIdx.x % (uint32_t)Hkv);
+  const int64_t t0 = (int64_t)(blockIdx.x / (uint32_t)Hkv) * kChunk;
+  const int tid = threadIdx.x;
+  if (tid < kChunk) {
+    const int64_t t = t0 + tid;
+    int64_t s = t < T ? slot_mapping[t] : -1;
+    if (s >= num_slots) s = -1;  // out of the pool: skipped like padding
+    s_slot[tid] = s < 0 ? -1 : s;
   }
   __syncthreads();
-  const int dh = 1 << dh_shift;
-  const int cq_shift = dh_shift - 2;  // channel quads per row = dh / 4
-  const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
-    const uint32_t cq = u & ((1u << cq_shift) - 1);
-    const uint32_t rest = u >> cq_shift;  // tq * Hkv + h
-    const uint32_t tq = rest / (uint32_t)Hkv;
-    const int h = (int)(rest - tq * (uint32_t)Hkv);
-    const int hs = per_head ? h : 0;
-    const float sk = s_k[hs], rk = r_k[hs], sv = s_v[hs], rv = r_v[hs];
-    const int64_t t0 = (int64_t)tq * 4;
+
+  if (tid < kChunk) {  // wave 0: runs of consecutive slots inside one quad
+    const int64_t s = s_slot[tid];
+    const int q = (int)(s & 3);
+    const bool cont = tid > 0 && q != 0 && s >= 0 && s_slot[tid - 1] == s - 1;
+    const bool start = s >= 0 && !cont;
+    int n = 1;
+    while (start && n < 4 - q && tid + n < kChunk && s_slot[tid + n] == s + n) ++n;
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(start);
+    if (start) {
+      const int pos = __builtin_popcountll(mask & ((1ull << tid) - 1));
+      s_run[pos] = (uint32_t)tid | ((uint32_t)n << 8);
+    }
+    if (tid == 0) s_nrun = __builtin_popcountll(mask);
+  }
+
+  const float sk = ks[per_head ? h : 0], sv = vs[per_head ? h : 0];
+  const float rk = recip_rn(sk), rv = recip_rn(sv);
+  for (int job = tid; job < (kChunk / 4) * kCq; job += 256) {
+    const int cq = job % kCq, tq = job / kCq;
     int64_t slot[4];
     uint2 wk[4], wv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t t = t0 + j;
-      slot[j] = t < T ? slot_mapping[t] : -1;
-      if (slot[j] >= num_slots) slot[j] = -1;  // out of the pool: skipped like padding
+      slot[j] = s_slot[4 * tq + j];
+      wk[j] = wv[j] = make_uint2(0, 0);
       if (slot[j] >= 0) {
-        const size_t src = ((size_t)t * Hkv + h) * dh + cq * 4;
+        const size_t src = ((size_t)(t0 + 4 * tq + j) * Hkv + h) * DH + cq * 4;
         wk[j] = *reinterpret_cast<const uint2*>(k + src);
         wv[j] = *reinterpret_cast<const uint2*>(v + src);
       }
@@ -75,39 +95,50 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     uint32_t cv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      cv[j] = quant4<FMT>(wv[j], sv, rv);
       if (slot[j] < 0) continue;
       const int64_t blk = slot[j] >> 4, off = slot[j] & (kBs - 1);
-      const size_t kt = ((size_t)(blk * Hkv + h) * kBs + off) * dh + cq * 4;
+      const size_t kt = ((size_t)(blk * Hkv + h) * kBs + off) * DH + cq * 4;
       *reinterpret_cast<uint32_t*>(kc + kt) = quant4<FMT>(wk[j], sk, rk);
-      cv[j] = quant4<FMT>(wv[j], sv, rv);
     }
-    const bool run4 = slot[0] >= 0 && (slot[0] & 3) == 0 && slot[1] == slot[0] + 1 &&
-                      slot[2] == slot[0] + 2 && slot[3] == slot[0] + 3;
-    if (run4) {
-      // rows cv[j] = token j, bytes = channels 4cq..4cq+3 -> one dword per channel
-      const uint32_t t0l = __builtin_amdgcn_perm(cv[1], cv[0], 0x05010400u);  // a0 b0 a1 b1
-      const uint32_t t1l = __builtin_amdgcn_perm(cv[1], cv[0], 0x07030602u);  // a2 b2 a3 b3
-      const uint32_t t2l = __builtin_amdgcn_perm(cv[3], cv[2], 0x05010400u);  // c0 d0 c1 d1
-      const uint32_t t3l = __builtin_amdgcn_perm(cv[3], cv[2], 0x07030602u);  // c2 d2 c3 d3
-      const int64_t blk = slot[0] >> 4, off = slot[0] & (kBs - 1);
-      uint8_t* dst = vc + ((size_t)(blk * Hkv + h) * dh + cq * 4) * kBs + off;
-      *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(t2l, t0l, 0x05040100u);
-      *reinterpret_cast<uint32_t*>(dst + kBs) = __builtin_amdgcn_perm(t2l, t0l, 0x07060302u);
-      *reinterpret_cast<uint32_t*>(dst + 2 * kBs) = __builtin_amdgcn_perm(t3l, t1l, 0x05040100u);
-      *reinterpret_cast<uint32_t*>(dst + 3 * kBs) = __builtin_amdgcn_perm(t3l, t1l, 0x07060302u);
+    // rows cv[j] = token j, bytes = channels 4cq..4cq+3 -> one dword per channel
+    const uint32_t t0l = __builtin_amdgcn_perm(cv[1], cv[0], 0x05010400u);  // a0 b0 a1 b1
+    const uint32_t t1l = __builtin_amdgcn_perm(cv[1], cv[0], 0x07030602u);  // a2 b2 a3 b3
+    const uint32_t t2l = __builtin_amdgcn_perm(cv[3], cv[2], 0x05010400u);  // c0 d0 c1 d1
+    const uint32_t t3l = __builtin_amdgcn_perm(cv[3], cv[2], 0x07030602u);  // c2 d2 c3 d3
+    uint32_t* row = s_vt + (4 * cq) * kRowDw + tq;
+    row[0] = __builtin_amdgcn_perm(t2l, t0l, 0x05040100u);
+    row[kRowDw] = __builtin_amdgcn_perm(t2l, t0l, 0x07060302u);
+    row[2 * kRowDw] = __builtin_amdgcn_perm(t3l, t1l, 0x05040100u);
+    row[3 * kRowDw] = __builtin_amdgcn_perm(t3l, t1l, 0x07060302u);
+  }
+  __syncthreads();
+
+  const int nrun = s_nrun;
+  for (int job = tid; job < nrun * DH; job += 256) {
+    const int c = job % DH;
+    const uint32_t e = s_run[job / DH];
+    const int i = (int)(e & 0xff), n = (int)(e >> 8);
+    const int64_t s = s_slot[i];
+    // codes of tokens i..i+3 of channel c (bytes past the run are ignored)
+    const uint32_t* row = s_vt + c * kRowDw + (i >> 2);
+    const uint32_t w = __builtin_amdgcn_alignbyte(row[1], row[0], (uint32_t)(i & 3));
+    uint8_t* dst = vc + ((size_t)((s >> 4) * Hkv + h) * DH + c) * kBs + (s & (kBs - 1));
+    if (n == 4) {
+      *reinterpret_cast<uint32_t*>(dst) = w;  // a full quad starts 4-aligned
     } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (slot[j] < 0) continue;
-        const int64_t blk = slot[j] >> 4, off = slot[j] & (kBs - 1);
-        uint8_t* dst = vc + ((size_t)(blk * Hkv + h) * dh + cq * 4) * kBs + off;
-        dst[0] = (uint8_t)cv[j];
-        dst[kBs] = (uint8_t)(cv[j] >> 8);
-        dst[2 * kBs] = (uint8_t)(cv[j] >> 16);
-        dst[3 * kBs] = (uint8_t)(cv[j] >> 24);
-      }
+      for (int b = 0; b < n; ++b) dst[b] = (uint8_t)(w >> (8 * b));
     }
   }
+}
+
+template <int FMT, int DH>
+void launch_write(int64_t T, int Hkv, const uint16_t* k, const uint16_t* v, const int64_t* slot,
+                  uint8_t* kc, uint8_t* vc, int64_t num_slots, const float* ks, const float* vs,
+                  int per_head, hipStream_t s) {
+  const uint32_t grid = (uint32_t)(((T + kChunk - 1) / kChunk) * Hkv);
+  cache_write_kernel<FMT, DH><<<grid, 256, 0, s>>>(k, v, T, Hkv, slot, kc, vc, num_slots, ks, vs,
+                                                    per_head);
 }
 
 hipError_t launch_cache_write(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv, int dh,
@@ -115,19 +146,14 @@ hipError_t launch_cache_write(const uint16_t* k, const uint16_t* v, int64_t T, i
                               const float* ks, const float* vs, int fmt, int per_head,
                               hipStream_t s) {
   if (T == 0) return hipSuccess;
-  int dh_shift = 0;
-  while ((1 << dh_shift) < dh) ++dh_shift;
-  const uint32_t units = (uint32_t)(((T + 3) / 4) * Hkv * (dh / 4));
-  int64_t want = ((int64_t)units + 255) / 256;
-  int64_t cap = (int64_t)device_cu_count() * 16;
-  int grid = (int)(want < cap ? want : cap);
   const int64_t num_slots = num_blocks * kBs;
-  if (fmt == E4M3)
-    cache_write_kernel<E4M3><<<grid, 256, 0, s>>>(k, v, T, Hkv, dh_shift, units, slot, kc, vc,
-                                                   num_slots, ks, vs, per_head);
-  else
-    cache_write_kernel<E5M2><<<grid, 256, 0, s>>>(k, v, T, Hkv, dh_shift, units, slot, kc, vc,
-                                                   num_slots, ks, vs, per_head);
+  if (fmt == E4M3) {
+    if (dh == 128) launch_write<E4M3, 128>(T, Hkv, k, v, slot, kc, vc, num_slots, ks, vs, per_head, s);
+    else launch_write<E4M3, 64>(T, Hkv, k, v, slot, kc, vc, num_slots, ks, vs, per_head, s);
+  } else {
+    if (dh == 128) launch_write<E5M2, 128>(T, Hkv, k, v, slot, kc, vc, num_slots, ks, vs, per_head, s);
+    else launch_write<E5M2, 64>(T, Hkv, k, v, slot, kc, vc, num_slots, ks, vs, per_head, s);
+  }
   return hipGetLastError();
 }
 
