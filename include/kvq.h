@@ -179,9 +179,11 @@ kvq_status kvq_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
  *     chunk's own K/V must already be in the cache (kvq_cache_write).
  *   Q is quantized in-kernel to E4M3 with q_scale (q_gran: [1] or [Hq]):
  *     q_hat = s_q * fp8(fl32(q / s_q)); Q K^T runs on FP8 matrix cores with
- *     fp32 accumulation; P is fed to the P V product as two E4M3 terms
- *     (P = (P_hi + P_lo / 16) / 256) so the FP8 product keeps about 8
- *     significant bits of P.
+ *     fp32 accumulation; P is fed to the P V product as two E4M3 terms,
+ *     P_hi = fp8(F p) and P_lo = fp8(16 (F p - P_hi)) with F = 64 and the
+ *     running max kept within 2 (log2) of the true one, recombined as
+ *     (P_hi + P_lo / 16) / F, so the FP8 product keeps about 8 significant
+ *     bits of P.
  *   out: [total_q][Hq][dh] fp32 or bf16.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED. */
 kvq_status kvq_prefill_attn(void* out, kvq_out out_dtype, const void* q_bf16,
