@@ -45,11 +45,11 @@ namespace kvq {
 #ifndef KVQ_DECODE_MAX_SPLIT_BLOCKS
 #define KVQ_DECODE_MAX_SPLIT_BLOCKS 32
 #endif
-// Whether a wave loads its next block pair into a second register set before
-// computing the current one (true), or into the current set as each half of
-// it is consumed: keys after Q K^T, values after P V (false).
-#ifndef KVQ_DECODE_PREFETCH
-#define KVQ_DECODE_PREFETCH false
+// Waves per SIMD the split kernel is compiled for.  At 4 the whole state
+// (Q operand, one block pair of codes, the O tile) fits in 128 registers, so
+// a compute unit keeps 16 waves' loads in flight.
+#ifndef KVQ_DECODE_WAVES_PER_EU
+#define KVQ_DECODE_WAVES_PER_EU 4
 #endif
 
 namespace {
@@ -118,16 +118,29 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 template <int DH>
 __device__ __forceinline__ bool chan_group_live(int g4) { return g4 < DH / 32; }
 
-template <int FMT, int DH, int NPW, bool PF>
-__global__ __launch_bounds__(256) void decode_split_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
-    const uint8_t* __restrict__ vc, int64_t num_blocks, const int32_t* __restrict__ bt,
-    int max_blocks, const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int NH, int max_ctx,
-    const float* __restrict__ ks, int per_head, float sm_scale, int nsplit,
-    float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
+// Rows of the 16-row MFMA tiles are given to query heads in runs of
+// RPH = 16 / NHp rows per head (NHp = NH rounded up to a power of two), so
+// S and O rows come out replicated per head.  A lane holding S rows
+// 4 g4 .. 4 g4 + 3 then holds HPL = max(1, NHp / 4) distinct heads, and the
+// softmax is computed once per (head, token) rather than once per row.
+template <int HPL>
+struct LaneHeads {
+  static constexpr int kStride = 4 / HPL;  // S register of distinct head i: r = i * kStride
+};
+
+template <int FMT, int DH, int NPW, int HPL>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(KVQ_DECODE_WAVES_PER_EU, KVQ_DECODE_WAVES_PER_EU))) void
+decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
+                    const uint8_t* __restrict__ vc, int64_t num_blocks,
+                    const int32_t* __restrict__ bt, int max_blocks,
+                    const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int NH, int rph_shift,
+                    int max_ctx, const float* __restrict__ ks, int per_head, float sm_scale,
+                    int nsplit, float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
   constexpr int NV = DH / 16;   // f16 MFMAs per block pair (16 channels each)
   constexpr int PB = 8 * NPW;   // blocks per split: 4 waves x NPW pairs x 2
   constexpr int HALF = DH / 2;
+  constexpr int RS = LaneHeads<HPL>::kStride;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int split = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
@@ -148,7 +161,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, g4 = lane >> 4;
-  const bool head_real = c16 < NH;
+  const int rph_mask = (1 << rph_shift) - 1;
+  // A operands (Q for S, P for O): row c16 carries head c16 / RPH
+  const int head_a = c16 >> rph_shift;
+  const bool head_a_real = head_a < NH;
   const bool chan_live = chan_group_live<DH>(g4);
   _Float16* ptr = reinterpret_cast<_Float16*>(smem) + wave * 16 * 32;  // this wave's P scratch
   float* wm = reinterpret_cast<float*>(smem + 4 * 16 * 32 * sizeof(_Float16));
@@ -158,156 +174,168 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const size_t tile = (size_t)kBlockSize * DH;  // bytes per (block, head) tile
   const int eb = g4 >> 1, tk = 8 * (g4 & 1);   // V: this lane's block in a pair, token half
 
+  // distinct heads of this lane's S / O rows, and whether this lane group is
+  // the first copy of each (the one that publishes P and the results)
+  int head_l[HPL];
+  bool pub_l[HPL];
+#pragma unroll
+  for (int i = 0; i < HPL; ++i) {
+    const int row = 4 * g4 + i * RS;
+    head_l[i] = row >> rph_shift;
+    pub_l[i] = (row & rph_mask) == 0 && head_l[i] < NH;
+  }
+
   // A block pair (2 blocks of 16 tokens).  K: lane holds the 32 code bytes of
   // token c16 in channel slots 16 g4 + [0,16) and DH/2 + 16 g4 + [0,16).
   // V: lane holds tokens tk .. tk + 7 of block eb for channel 16 n + c16.
-  struct Pair {
-    i32x8 k[2];
-    uint2 v[NV];
+  // Blocks past the split's end re-read its last block; their scores are
+  // masked and their values zeroed, so nothing outside the table is read.
+  i32x8 kr[2];
+  uint2 vr[NV];
+  auto block_src = [&](int bi) {
+    bi = bi < nblk ? bi : nblk - 1;
+    return (size_t)clamp_block(btab[bi], num_blocks) * Hkv + h;
   };
-  auto load_k = [&](int p, Pair& P) {
+  auto load_k = [&](int p) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int bi = 2 * p + e;
-      P.k[e] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (bi < nblk && chan_live) {
-        const int64_t blk = clamp_block(btab[bi], num_blocks);
-        const uint8_t* src = kc + ((size_t)blk * Hkv + h) * tile + c16 * DH + 16 * g4;
+      kr[e] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (chan_live) {
+        const uint8_t* src = kc + block_src(2 * p + e) * tile + c16 * DH + 16 * g4;
         const uint4 a0 = *reinterpret_cast<const uint4*>(src);
         const uint4 a1 = *reinterpret_cast<const uint4*>(src + HALF);
-        P.k[e] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                       (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        kr[e] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
       }
     }
   };
-  auto load_v = [&](int p, Pair& P) {
-    const int bi = 2 * p + eb;
-    if (bi < nblk) {
-      const int64_t blk = clamp_block(btab[bi], num_blocks);
-      const uint8_t* src = vc + ((size_t)blk * Hkv + h) * tile + c16 * kBlockSize + tk;
+  auto load_v = [&](int p) {
+    const uint8_t* src = vc + block_src(2 * p + eb) * tile + c16 * kBlockSize + tk;
 #pragma unroll
-      for (int n = 0; n < NV; ++n)
-        P.v[n] = *reinterpret_cast<const uint2*>(src + 16 * n * kBlockSize);
-    } else {
-#pragma unroll
-      for (int n = 0; n < NV; ++n) P.v[n] = make_uint2(0, 0);  // no token: exact zeros
-    }
-  };
-  auto load_pair = [&](int p, Pair& P) {
-    load_k(p, P);
-    load_v(p, P);
+    for (int n = 0; n < NV; ++n) vr[n] = *reinterpret_cast<const uint2*>(src + 16 * n * kBlockSize);
   };
 
-  Pair cur, nxt;
   int p = wave;
-  if (p < npair) load_pair(p, cur);
+  if (p < npair) {
+    load_k(p);
+    load_v(p);
+  }
 
-  // A operand of S = Q K^T (bf16, exact): query row c16 in the channel slots
+  // A operand of S = Q K^T (bf16, exact): query head_a in the channel slots
   // of the K operand: j = 2 i + c covers channels 16 g4 + i * DH/2 + 8 c + 0..7
   bf16x8 qop[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     uint4 w = make_uint4(0, 0, 0, 0);
-    if (head_real && chan_live)
-      w = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + hq0 + c16) * DH + 16 * g4 +
+    if (head_a_real && chan_live)
+      w = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + hq0 + head_a) * DH + 16 * g4 +
                                           (j >> 1) * HALF + 8 * (j & 1));
     qop[j] = __builtin_bit_cast(bf16x8, w);
   }
   const float zc = sm_scale * ks[per_head ? h : 0] * kLog2e;
 
-  // running state of rows 4 g4 + r (identical across the 16 lanes of a group)
-  float m_run[4] = {kNegBig, kNegBig, kNegBig, kNegBig};
-  float l_part[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // this lane's token share of the row sum
+  // running state per distinct head (identical across the 16 lanes of a group)
+  float m_run[HPL], l_part[HPL];
+#pragma unroll
+  for (int i = 0; i < HPL; ++i) {
+    m_run[i] = kNegBig;
+    l_part[i] = 0.0f;  // this lane's token share of the row sum
+  }
   f32x4 O[NV];
 #pragma unroll
   for (int n = 0; n < NV; ++n) O[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
 #pragma unroll 1
   for (; p < npair; p += 4) {
-    if (PF && p + 4 < npair) load_pair(p + 4, nxt);
     // ---- S for both blocks on bf16 matrix cores (codes -> bf16 is exact):
-    //      lane holds rows 4 g4 + r for token c16
-    float z[2][4];
+    //      lane holds head head_l[i] for token c16 of block e
+    float z[2][HPL];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       f32x4 S = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            qop[j], codes_to_bf16x8<FMT>((uint32_t)cur.k[e][2 * j], (uint32_t)cur.k[e][2 * j + 1]),
-            S, 0, 0, 0);
+            qop[j], codes_to_bf16x8<FMT>((uint32_t)kr[e][2 * j], (uint32_t)kr[e][2 * j + 1]), S,
+            0, 0, 0);
       const bool valid = tok0 + (2 * p + e) * kBlockSize + c16 < ctx;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) z[e][r] = valid ? S[r] * zc : -__builtin_inff();
+      for (int i = 0; i < HPL; ++i) z[e][i] = valid ? S[i * RS] * zc : -__builtin_inff();
     }
     // this pair's K registers are free: the next pair's keys load during the
     // softmax and P V below
-    if (!PF && p + 4 < npair) load_k(p + 4, cur);
-    // ---- online softmax per row; the rescale factor is lane-local because
-    //      the O tile uses the same row -> (g4, r) mapping as the S tile.  The
-    //      running max moves rarely, so the rescale is one wave-uniform branch.
-    float mt[4];
+    if (p + 4 < npair) load_k(p + 4);
+    // ---- online softmax per head.  Each lane tests its own scores against
+    //      the running max; only when one exceeds it by more than tau does the
+    //      wave take the (rare, wave-uniform) branch that finds the exact
+    //      maxima of the 16-lane groups and rescales.  The O tile maps rows to
+    //      lanes as the S tile does, so the rescale is lane-local.
     bool need = false;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      mt[r] = max16(__builtin_fmaxf(z[0][r], z[1][r]));
-      need |= mt[r] > m_run[r] + kLazyTau;
-    }
+    for (int i = 0; i < HPL; ++i)
+      need |= __builtin_fmaxf(z[0][i], z[1][i]) > m_run[i] + kLazyTau;
     if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool up = mt[r] > m_run[r] + kLazyTau;
-        const float f = up ? __builtin_amdgcn_exp2f(m_run[r] - mt[r]) : 1.0f;
-        m_run[r] = up ? mt[r] : m_run[r];
-        l_part[r] *= f;
+      for (int i = 0; i < HPL; ++i) {
+        const float mt = max16(__builtin_fmaxf(z[0][i], z[1][i]));
+        const bool up = mt > m_run[i] + kLazyTau;
+        const float f = up ? __builtin_amdgcn_exp2f(m_run[i] - mt) : 1.0f;
+        m_run[i] = up ? mt : m_run[i];
+        l_part[i] *= f;
 #pragma unroll
-        for (int n = 0; n < NV; ++n) O[n][r] *= f;
+        for (int n = 0; n < NV; ++n)
+#pragma unroll
+          for (int r = i * RS; r < (i + 1) * RS; ++r) O[n][r] *= f;
       }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p0 = __builtin_amdgcn_exp2f(z[0][r] - m_run[r]);
-      const float p1 = __builtin_amdgcn_exp2f(z[1][r] - m_run[r]);
-      l_part[r] += p0 + p1;
-      const int row = 4 * g4 + r;
-      ptr[row * 32 + c16] = (_Float16)p0;
-      ptr[row * 32 + 16 + c16] = (_Float16)p1;
+    for (int i = 0; i < HPL; ++i) {
+      const float p0 = __builtin_amdgcn_exp2f(z[0][i] - m_run[i]);
+      const float p1 = __builtin_amdgcn_exp2f(z[1][i] - m_run[i]);
+      l_part[i] += p0 + p1;
+      if (pub_l[i]) {
+        ptr[head_l[i] * 32 + c16] = (_Float16)p0;
+        ptr[head_l[i] * 32 + 16 + c16] = (_Float16)p1;
+      }
     }
-    // ---- P V on f16 matrix cores: A = P rows (head c16), tokens 8 g4 .. 8 g4 + 7
+    // ---- P V on f16 matrix cores: A = P of head head_a, tokens 8 g4 .. 8 g4 + 7.
+    //      Value codes of tokens past the context (the tail of the last block,
+    //      or a re-read block) may hold anything, NaN included: zero them,
+    //      since their zero weights would not cancel a NaN.
+    if (2 * p + 2 > nblk_left || tok0 + (2 * p + 2) * kBlockSize > ctx) {
+      const int left = ctx - (tok0 + (2 * p + eb) * kBlockSize + tk);
+      const uint64_t keep = left >= 8 ? ~0ull : (left <= 0 ? 0ull : (1ull << (8 * left)) - 1);
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        vr[n].x &= (uint32_t)keep;
+        vr[n].y &= (uint32_t)(keep >> 32);
+      }
+    }
     f16x8 pop = {};
-    if (head_real) pop = *reinterpret_cast<const f16x8*>(ptr + c16 * 32 + 8 * g4);
+    if (head_a_real) pop = *reinterpret_cast<const f16x8*>(ptr + head_a * 32 + 8 * g4);
 #pragma unroll
     for (int n = 0; n < NV; ++n)
-      O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-          pop, codes_to_f16x8<FMT>(cur.v[n].x, cur.v[n].y), O[n], 0, 0, 0);
-    if (PF) {
-      cur = nxt;
-    } else if (p + 4 < npair) {
-      load_v(p + 4, cur);  // V registers are free now
-    }
+      O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, codes_to_f16x8<FMT>(vr[n].x, vr[n].y),
+                                                    O[n], 0, 0, 0);
+    if (p + 4 < npair) load_v(p + 4);  // V registers are free now
   }
 
   // ---- merge the 4 waves through LDS and write the split's partial
-  float l_row[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float x = l_part[r];
+  for (int i = 0; i < HPL; ++i) {
+    float x = l_part[i];
     x += dpp<0xB1>(x);
     x += dpp<0x4E>(x);
     x += dpp<0x141>(x);
     x += dpp<0x140>(x);
-    l_row[r] = x;
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * g4 + r;
-    if (row < NH) {
+    if (pub_l[i]) {
+      const int hh = head_l[i];
       if (c16 == 0) {
-        wm[wave * 16 + row] = m_run[r];
-        wl[wave * 16 + row] = l_row[r];
+        wm[wave * 16 + hh] = m_run[i];
+        wl[wave * 16 + hh] = x;
       }
 #pragma unroll
-      for (int n = 0; n < NV; ++n) wo[(wave * NH + row) * DH + 16 * n + c16] = O[n][r];
+      for (int n = 0; n < NV; ++n) wo[(wave * NH + hh) * DH + 16 * n + c16] = O[n][i * RS];
     }
   }
   __syncthreads();
@@ -428,16 +456,26 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
   const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / __builtin_sqrtf((float)dh);
   const dim3 grid(plan.nsplit, Hq / NH, B);
   const size_t lds = decode_lds_bytes(NH, dh);
+  int nhp_shift = 0;
+  while ((1 << nhp_shift) < NH) ++nhp_shift;  // NHp = 2^nhp_shift >= NH
+  const int rph_shift = 4 - nhp_shift;         // RPH = 16 / NHp rows per head
   if (max_ctx > 0) {
-#define KVQ_SPLIT(F, D, N, PF)                                                                \
-  decode_split_kernel<F, D, N, PF><<<grid, 256, lds, s>>>(q, kc, vc, num_blocks, bt, max_blocks, \
-                                                          ctx, Hq, Hkv, NH, max_ctx, ks,         \
-                                                          per_head, sm, plan.nsplit, ml, acc)
-#define KVQ_SPLIT_NP(F, D)                                                    \
-  do {                                                                        \
-    if (plan.part_blocks == 32) KVQ_SPLIT(F, D, 4, KVQ_DECODE_PREFETCH);      \
-    else if (plan.part_blocks == 16) KVQ_SPLIT(F, D, 2, KVQ_DECODE_PREFETCH); \
-    else KVQ_SPLIT(F, D, 1, false);                                           \
+#define KVQ_SPLIT(F, D, N, HP)                                                               \
+  decode_split_kernel<F, D, N, HP><<<grid, 256, lds, s>>>(q, kc, vc, num_blocks, bt,          \
+                                                          max_blocks, ctx, Hq, Hkv, NH,       \
+                                                          rph_shift, max_ctx, ks, per_head,   \
+                                                          sm, plan.nsplit, ml, acc)
+#define KVQ_SPLIT_HP(F, D, N)                                     \
+  do {                                                            \
+    if (nhp_shift <= 2) KVQ_SPLIT(F, D, N, 1);                    \
+    else if (nhp_shift == 3) KVQ_SPLIT(F, D, N, 2);               \
+    else KVQ_SPLIT(F, D, N, 4);                                   \
+  } while (0)
+#define KVQ_SPLIT_NP(F, D)                                    \
+  do {                                                        \
+    if (plan.part_blocks == 32) KVQ_SPLIT_HP(F, D, 4);        \
+    else if (plan.part_blocks == 16) KVQ_SPLIT_HP(F, D, 2);   \
+    else KVQ_SPLIT_HP(F, D, 1);                               \
   } while (0)
     if (fmt == E4M3) {
       if (dh == 128) KVQ_SPLIT_NP(E4M3, 128); else KVQ_SPLIT_NP(E4M3, 64);
@@ -445,6 +483,7 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
       if (dh == 128) KVQ_SPLIT_NP(E5M2, 128); else KVQ_SPLIT_NP(E5M2, 64);
     }
 #undef KVQ_SPLIT_NP
+#undef KVQ_SPLIT_HP
 #undef KVQ_SPLIT
   }
   const dim3 cgrid(Hq, B);

@@ -150,6 +150,17 @@ __global__ __launch_bounds__(64 * GT) void prefill_kernel(
         int64_t blk = btab[bi];
         blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
         w = *reinterpret_cast<const uint4*>(vc + ((size_t)blk * Hkv + h) * tile_stride + d * 16);
+        // slots past the context may hold any bytes, NaN codes included; their
+        // zero weights would not cancel a NaN, so they are zeroed here
+        const int left = ctx - bi * 16;
+        if (left < 16) {
+          uint32_t* wd = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = left - 4 * i;  // tokens of dword i inside the context
+            wd[i] &= n >= 4 ? 0xffffffffu : (n <= 0 ? 0u : (1u << (8 * n)) - 1);
+          }
+        }
       }
       // dword i holds keys 16 beta + 4i .. + 3; vt_pos puts i = 0, 2 and i = 1, 3 side by side
       uint8_t* row = v_lds + d * VROW + vt_pos(16 * beta);

@@ -81,7 +81,7 @@ class DecodeRun:
     """One decode workload through the GPU path (calibrate -> write -> decode)
     and the same inputs through the oracle."""
 
-    def __init__(self, wl, out_dtype="f32", copies: int = 1):
+    def __init__(self, wl, out_dtype="f32", fill: int = SENTINEL):
         import torch
         import quantized_kv_cache_fp8_amd as K
         self.wl, self.K = wl, K
@@ -103,8 +103,11 @@ class DecodeRun:
         self.slots = to_dev(wl.kv.slot_mapping)
         self.bt = to_dev(wl.paging.block_tables)
         self.cl = to_dev(wl.paging.context_lens)
-        self.kc = torch.full(k_shape(wl), SENTINEL, dtype=torch.uint8, device=dev)
-        self.vc = torch.full(v_shape(wl), SENTINEL, dtype=torch.uint8, device=dev)
+        # cache bytes no token writes keep this value (a NaN code tests that
+        # slots past a context never reach the output)
+        self.fill = fill
+        self.kc = torch.full(k_shape(wl), fill, dtype=torch.uint8, device=dev)
+        self.vc = torch.full(v_shape(wl), fill, dtype=torch.uint8, device=dev)
         self.ks = torch.empty(nh, dtype=torch.float32, device=dev)
         self.vs = torch.empty(nh, dtype=torch.float32, device=dev)
         self.kamax = torch.empty(nh, dtype=torch.float32, device=dev)
@@ -140,8 +143,8 @@ class DecodeRun:
 
     def oracle_caches(self):
         wl = self.wl
-        kc = np.full(k_shape(wl), SENTINEL, np.uint8)
-        vc = np.full(v_shape(wl), SENTINEL, np.uint8)
+        kc = np.full(k_shape(wl), self.fill, np.uint8)
+        vc = np.full(v_shape(wl), self.fill, np.uint8)
         oracle.cache_write(wl.kv.k, wl.kv.v, wl.kv.slot_mapping, kc, vc, self.ks_ref, self.vs_ref,
                            self.fmt, self.gran)
         return kc, vc

@@ -15,8 +15,8 @@ from helpers import ATTN_TOL, DecodeRun, rel_err, row_rel_err, to_np
 pytestmark = pytest.mark.gpu
 
 
-def run_case(wl, check_cache=True):
-    run = DecodeRun(wl)
+def run_case(wl, check_cache=True, fill=None):
+    run = DecodeRun(wl) if fill is None else DecodeRun(wl, fill=fill)
     run.gpu_scales()
     run.gpu_write()
     kc, vc = run.oracle_caches()
@@ -66,6 +66,19 @@ def test_group_sizes_and_head_dims(Hq, Hkv, dh):
     wl = W.decode_workload("groups", 102 + Hq, len(cl), Hq, Hkv, dh, cl, 16, "e4m3", "head",
                            head_range=(0.5, 20.0))
     _, out, ref = run_case(wl)
+    check(out, ref)
+
+
+@pytest.mark.parametrize("fmt,fill", [("e4m3", 0xFF), ("e4m3", 0x7F), ("e5m2", 0xFF),
+                                      ("e5m2", 0x7C)])
+def test_stale_nan_bytes_past_the_context(fmt, fill):
+    """Slots of a block past its sequence's context hold NaN (or Inf) codes, as
+    a reused pool may: they carry zero weight and must not reach the output."""
+    cl = [1, 17, 31, 250, 517, 1029]
+    wl = W.decode_workload("stale", 106, len(cl), 32, 8, 128, cl, 16, fmt, "head",
+                           head_range=(0.5, 20.0))
+    _, out, ref = run_case(wl, fill=fill)
+    assert np.all(np.isfinite(out))
     check(out, ref)
 
 

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 
 class PrefillRun:
-    def __init__(self, wl, q_gran="head", kv_gran="head", out_dtype="f32"):
+    def __init__(self, wl, q_gran="head", kv_gran="head", out_dtype="f32", fill=SENTINEL):
         import torch
         import quantized_kv_cache_fp8_amd as K
         self.wl, self.K = wl, K
@@ -29,8 +29,9 @@ class PrefillRun:
         self.vs_ref = oracle.calibrate(wl.kv.v, self.fmt, self.kg)[1]
         dev = torch.device("cuda:0")
         self.q = to_dev(wl.q)
-        self.kc = torch.full(k_shape(wl), SENTINEL, dtype=torch.uint8, device=dev)
-        self.vc = torch.full(v_shape(wl), SENTINEL, dtype=torch.uint8, device=dev)
+        self.fill = fill
+        self.kc = torch.full(k_shape(wl), fill, dtype=torch.uint8, device=dev)
+        self.vc = torch.full(v_shape(wl), fill, dtype=torch.uint8, device=dev)
         nq = wl.Hq if self.qg == oracle.GRAN_HEAD else 1
         nk = wl.Hkv if self.kg == oracle.GRAN_HEAD else 1
         self.qs = torch.empty(nq, device=dev)
@@ -62,8 +63,8 @@ class PrefillRun:
 
     def oracle_caches(self):
         wl = self.wl
-        kc = np.full(k_shape(wl), SENTINEL, np.uint8)
-        vc = np.full(v_shape(wl), SENTINEL, np.uint8)
+        kc = np.full(k_shape(wl), self.fill, np.uint8)
+        vc = np.full(v_shape(wl), self.fill, np.uint8)
         oracle.cache_write(wl.kv.k, wl.kv.v, wl.kv.slot_mapping, kc, vc, self.ks_ref, self.vs_ref,
                            self.fmt, self.kg)
         return kc, vc
@@ -89,6 +90,17 @@ def test_small_ragged_chunks(fmt, dh):
     wl = W.prefill_workload("small", 201, [20, 0, 16, 100], [13, 9, 1, 40], 8, 2, dh, 16, fmt)
     run = PrefillRun(wl)
     check(run.gpu(), run.oracle_full())
+
+
+@pytest.mark.parametrize("fmt,fill", [("e4m3", 0xFF), ("e5m2", 0xFF), ("e5m2", 0x7C)])
+def test_stale_nan_bytes_past_the_context(fmt, fill):
+    """Slots past each sequence's context hold NaN (or Inf) codes, as a reused
+    pool may; the last blocks are partial, so those slots sit inside staged tiles."""
+    wl = W.prefill_workload("stale", 206, [20, 0, 5, 100], [13, 9, 1, 40], 8, 2, 128, 16, fmt)
+    run = PrefillRun(wl, fill=fill)
+    out = run.gpu()
+    assert np.all(np.isfinite(out))
+    check(out, run.oracle_full())
 
 
 @pytest.mark.parametrize("q_gran,kv_gran", [("tensor", "tensor"), ("head", "tensor"),
