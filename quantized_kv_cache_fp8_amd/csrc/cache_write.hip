@@ -15,7 +15,8 @@
 //      tokens whose slots are consecutive inside one aligned group of four
 //      slots ("quad"), with the run's length (1..4).
 //   2. Every thread quantizes 4 tokens x 4 channels of K and V (bf16 loads of
-//      consecutive threads are one row).  K codes go straight out, one dword
+//      consecutive threads are one row; they are issued before step 1's
+//      barrier, since they do not depend on the slots).  K codes go straight out, one dword
 //      per token; the 4x4 V code block is transposed with v_perm_b32 and
 //      parked in an LDS tile [dh][64 tokens].
 //   3. For each run and channel one thread reads the run's codes from the LDS
@@ -53,6 +54,25 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   const int h = (int)(blockIdx.x % (uint32_t)Hkv);
   const int64_t t0 = (int64_t)(blockIdx.x / (uint32_t)Hkv) * kChunk;
   const int tid = threadIdx.x;
+  // the bf16 loads do not depend on the slots: issue them first so both
+  // latencies overlap (tokens past T read nothing)
+  constexpr int kJobs = (kChunk / 4) * kCq / 256;  // 4x4 jobs per thread
+  uint2 wk[kJobs][4], wv[kJobs][4];
+#pragma unroll
+  for (int jb = 0; jb < kJobs; ++jb) {
+    const int job = tid + 256 * jb;
+    const int cq = job % kCq, tq = job / kCq;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t t = t0 + 4 * tq + j;
+      wk[jb][j] = wv[jb][j] = make_uint2(0, 0);
+      if (t < T) {
+        const size_t src = ((size_t)t * Hkv + h) * DH + cq * 4;
+        wk[jb][j] = *reinterpret_cast<const uint2*>(k + src);
+        wv[jb][j] = *reinterpret_cast<const uint2*>(v + src);
+      }
+    }
+  }
   if (tid < kChunk) {
     const int64_t t = t0 + tid;
     int64_t s = t < T ? slot_mapping[t] : -1;
@@ -78,28 +98,19 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
 
   const float sk = ks[per_head ? h : 0], sv = vs[per_head ? h : 0];
   const float rk = recip_rn(sk), rv = recip_rn(sv);
-  for (int job = tid; job < (kChunk / 4) * kCq; job += 256) {
-    const int cq = job % kCq, tq = job / kCq;
-    int64_t slot[4];
-    uint2 wk[4], wv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      slot[j] = s_slot[4 * tq + j];
-      wk[j] = wv[j] = make_uint2(0, 0);
-      if (slot[j] >= 0) {
-        const size_t src = ((size_t)(t0 + 4 * tq + j) * Hkv + h) * DH + cq * 4;
-        wk[j] = *reinterpret_cast<const uint2*>(k + src);
-        wv[j] = *reinterpret_cast<const uint2*>(v + src);
-      }
-    }
+  for (int jb = 0; jb < kJobs; ++jb) {
+    const int job = tid + 256 * jb;
+    const int cq = job % kCq, tq = job / kCq;
     uint32_t cv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      cv[j] = quant4<FMT>(wv[j], sv, rv);
-      if (slot[j] < 0) continue;
-      const int64_t blk = slot[j] >> 4, off = slot[j] & (kBs - 1);
+      cv[j] = quant4<FMT>(wv[jb][j], sv, rv);
+      const int64_t slot = s_slot[4 * tq + j];
+      if (slot < 0) continue;
+      const int64_t blk = slot >> 4, off = slot & (kBs - 1);
       const size_t kt = ((size_t)(blk * Hkv + h) * kBs + off) * DH + cq * 4;
-      *reinterpret_cast<uint32_t*>(kc + kt) = quant4<FMT>(wk[j], sk, rk);
+      *reinterpret_cast<uint32_t*>(kc + kt) = quant4<FMT>(wk[jb][j], sk, rk);
     }
     // rows cv[j] = token j, bytes = channels 4cq..4cq+3 -> one dword per channel
     const uint32_t t0l = __builtin_amdgcn_perm(cv[1], cv[0], 0x05010400u);  // a0 b0 a1 b1

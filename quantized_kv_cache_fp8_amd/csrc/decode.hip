@@ -40,7 +40,7 @@
 
 namespace kvq {
 
-// Largest split (cache blocks per workgroup): 8, 16 or 32.  Larger splits mean
+// Largest split (cache blocks per workgroup): 8, 16, 32 or 64.  Larger splits mean
 // fewer partial results to merge, smaller ones more workgroups in flight.
 #ifndef KVQ_DECODE_MAX_SPLIT_BLOCKS
 #define KVQ_DECODE_MAX_SPLIT_BLOCKS 32
@@ -473,7 +473,8 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
   } while (0)
 #define KVQ_SPLIT_NP(F, D)                                    \
   do {                                                        \
-    if (plan.part_blocks == 32) KVQ_SPLIT_HP(F, D, 4);        \
+    if (plan.part_blocks == 64) KVQ_SPLIT_HP(F, D, 8);        \
+    else if (plan.part_blocks == 32) KVQ_SPLIT_HP(F, D, 4);   \
     else if (plan.part_blocks == 16) KVQ_SPLIT_HP(F, D, 2);   \
     else KVQ_SPLIT_HP(F, D, 1);                               \
   } while (0)

@@ -100,6 +100,36 @@ def test_result_does_not_depend_on_the_split_plan():
     np.testing.assert_allclose(a, b, rtol=0, atol=1e-5 * np.abs(a).max())
 
 
+def test_workspace_reuse_across_calls():
+    """One workspace, never cleared, serves calls of different shapes and split
+    plans; every output equals the output of a call with a fresh workspace."""
+    import torch
+    import quantized_kv_cache_fp8_amd as K
+    runs = [DecodeRun(W.decode_workload("ws-a", 107, 3, 32, 8, 128, [3000, 40, 1700], 16,
+                                        "e4m3", "tensor")),
+            DecodeRun(W.decode_workload("ws-b", 108, 5, 16, 4, 64, [700, 1, 513, 0, 2222], 16,
+                                        "e5m2", "head", head_range=(0.5, 20.0)))]
+    for r in runs:
+        r.gpu_scales()
+        r.gpu_write()
+    fresh = [r.gpu_decode() for r in runs]
+    big = max(K.kvq_decode_workspace_size(r.wl.B, r.wl.Hq, r.wl.dh,
+                                          int(r.wl.paging.block_tables.shape[1]) * 16, 16)
+              for r in runs)
+    ws = torch.full((big,), 0xFF, dtype=torch.uint8, device="cuda:0")  # NaN-filled
+    for rep in range(3):
+        for r, want in zip(runs, fresh):
+            mc = r.max_ctx if rep != 1 else int(r.wl.paging.block_tables.shape[1]) * 16
+            K.kvq_decode_attn(r.out, r.q, r.kc, r.vc, r.bt, r.cl, mc, r.ks, r.vs, r.fmt, r.gran,
+                              workspace=ws)
+            torch.cuda.synchronize()
+            got = to_np(r.out)
+            if rep != 1:
+                assert np.array_equal(got, want)
+            else:
+                np.testing.assert_allclose(got, want, rtol=0, atol=1e-5 * np.abs(want).max())
+
+
 @pytest.mark.parametrize("which", ["llama", "long-e4m3", "long-e5m2"])
 def test_full_size_sampled_rows(which):
     """Full-size workloads; the oracle computes a seeded sample of rows
