@@ -44,7 +44,48 @@ def parse():
     p.add_argument("--no-rows", action="store_true", help="skip the extra per-row measurements")
     p.add_argument("--cpu-sample-rows", type=int, default=0,
                    help="(b, hq) rows in the CPU oracle sample (0 = all rows)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum CPU time of the oracle baseline (the sample is repeated)")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="after the run, copy this many MiB device-to-device three times (a "
+                        "plain copy kernel of known size, to calibrate HBM byte counters)")
     return p.parse_args()
+
+
+# HBM bytes per decode call from rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by the
+# counters' reading for a plain copy of known size; valid only for the decode
+# source it was measured on.
+TRAFFIC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "decode_llama3_8b_layer_hbm_traffic.md")
+DECODE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantized_kv_cache_fp8_amd",
+                          "csrc", "decode.hip")
+
+
+def decode_source_digest() -> str:
+    import hashlib
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """traffic_bytes_per_call from the committed counter summary, or None when
+    the summary is missing or was taken on a different decode source."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- `") and "`: " in line:
+            k, v = line[3:].split("`: ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("decode_source_sha256") != decode_source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -147,7 +188,8 @@ def main():
                    "step": "cache_write(new token) + decode_attn", "cache_copies": args.copies,
                    "kv_bytes_per_step": kv_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(),
                      "kernel": "kvq_decode_attn (split + combine)",
                      "avg_ms": round(dec_ms, 5)},
     }
@@ -157,9 +199,21 @@ def main():
         result["rows"] = measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches,
                                       ks, vs, wl)
 
+    # ------------------------------------------------------------ copy probe (untimed)
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.full((n,), 7, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = n
+        del src, dst
+
     # ------------------------------------------------------------ CPU oracle baseline
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
 
@@ -237,11 +291,11 @@ def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, 
     return rows
 
 
-def cpu_baseline(wl, sample_rows):
-    """The fp64 oracle on the host: the same decode step (new-token write plus
-    decode attention) over a bounded sample of (sequence, head) rows."""
+def cpu_baseline(wl, sample_rows, min_seconds):
+    """The fp64 oracle on the host: decode attention of the layer over a bounded
+    sample of (sequence, head) rows, repeated until at least min_seconds of
+    work have been timed."""
     import oracle
-    import os as _os
     fmt, gran = oracle.FMT_E4M3, oracle.GRAN_TENSOR
     ks = oracle.calibrate(wl.kv.k, fmt, gran)[1]
     vs = oracle.calibrate(wl.kv.v, fmt, gran)[1]
@@ -252,18 +306,24 @@ def cpu_baseline(wl, sample_rows):
     if sample_rows:
         rows = rows[np.random.Generator(np.random.PCG64(5)).permutation(len(rows))[:sample_rows]]
     cl = wl.paging.context_lens
+    reps = 0
     t0 = time.perf_counter()
-    oracle.decode_rows(rows, wl.q, kc, vc, wl.paging.block_tables, cl, ks, vs, fmt, gran)
-    t = time.perf_counter() - t0
+    while True:
+        oracle.decode_rows(rows, wl.q, kc, vc, wl.paging.block_tables, cl, ks, vs, fmt, gran)
+        reps += 1
+        t = time.perf_counter() - t0
+        if t >= min_seconds:
+            break
     # bytes of the FP8 history the sampled rows read (each row reads its sequence's K and V)
     G = wl.Hq // wl.Hkv
-    kv_bytes = float(sum(int(cl[b]) for b, _ in rows)) * wl.dh * 2 / G
-    threads = int(_os.environ.get("OMP_NUM_THREADS", _os.cpu_count() or 1))
+    kv_bytes = float(sum(int(cl[b]) for b, _ in rows)) * wl.dh * 2 / G * reps
+    threads = oracle.num_threads()
     return {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "seconds": round(t, 3),
+            "kind": "oracle", "seconds": round(t, 3), "repeats": reps,
             "sample": f"decode attention of {len(rows)} of {wl.B * wl.Hq} (sequence, head) rows "
-                      f"of the same layer, fp64, OpenMP over rows; bytes counted as the FP8 K+V "
-                      f"history those rows read (shared by the {G} heads of a group)"}
+                      f"of the same layer, repeated {reps} times; fp64, OpenMP over rows; bytes "
+                      f"counted as the FP8 K+V history those rows read (shared by the {G} heads "
+                      f"of a group)"}
 
 
 if __name__ == "__main__":

@@ -49,6 +49,11 @@ def build(force: bool = True) -> str:
 _lib = None
 
 
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_num_threads())
+
+
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
@@ -58,6 +63,8 @@ def lib() -> ctypes.CDLL:
         P = ctypes.c_void_p
         i32, i64, f32, f64, u8 = (ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_double,
                                   ctypes.c_uint8)
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = i32
         L.orc_fp8_max.argtypes = [i32]
         L.orc_fp8_max.restype = f64
         L.orc_fp8_decode.argtypes = [i32, u8]

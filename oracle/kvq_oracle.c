@@ -31,6 +31,19 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the OpenMP loops below use (1 without OpenMP): reported next to
+ * the oracle's timing. */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 #define ORC_FMT_E4M3 0
 #define ORC_FMT_E5M2 1
