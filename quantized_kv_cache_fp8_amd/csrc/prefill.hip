@@ -11,9 +11,10 @@
 //   O^T = V8^T . P8^T      (A = value columns from LDS, B = probabilities)
 //
 // Probabilities are carried as two E4M3 terms, P_hi = e4m3(F p) and
-// P_lo = e4m3(16 (F p - P_hi)), accumulated into separate fp32 tiles and
-// recombined as (acc_hi + acc_lo / 16) / F: one E4M3 term alone keeps 4
-// significant bits of p, the pair about 8.
+// P_lo = e4m3(16 (F p - P_hi)): one E4M3 term alone keeps 4 significant bits
+// of p, the pair about 8.  Both products accumulate into the same fp32 tiles:
+// P_lo's MFMA applies the block scale 2^-4 (the scaled form of the
+// instruction), so the accumulator holds V^T (P_hi + P_lo / 16) = F V^T P.
 //
 // Work decomposition: grid (query tiles of 32 rows, Hq / GT, sequences); a
 // workgroup has GT waves, one per query head of a GQA group, so every K/V tile
@@ -21,10 +22,11 @@
 // (the causal triangle makes late tiles the most expensive).  Per 64-key tile:
 // the workgroup copies K (4 cache blocks) into LDS row-major and V, whose cache
 // tiles are already channel-major, with its keys permuted into the order the B
-// operand holds P in (so each lane's A operand is one 32-byte run), then each wave runs 2*DH/64
-// MFMAs for S^T, the online softmax in registers (one query per lane pair,
-// the running max only raised when a score exceeds it by more than 2^2), and
-// 2*DH/32 MFMAs for O^T.
+// operand holds P in (so each lane's A operand is one 32-byte run); the next
+// tile's bytes are loaded into registers while the current one is computed.
+// Each wave then runs 2*DH/64 MFMAs for S^T, the online softmax in registers
+// (one query per lane pair, the running max only raised when a score exceeds
+// it by more than 2^2), and 2*DH/32 MFMAs for O^T.
 #include "codec.hpp"
 #include "launch.hpp"
 
@@ -37,7 +39,9 @@ namespace {
 constexpr int kQT = 32;          // query rows per wave
 constexpr int kKT = 64;          // keys per tile
 constexpr float kTau = 2.0f;     // lazy-max headroom (log2)
-constexpr float kPF = 64.0f;     // F = 2^(8 - tau): F * p <= 256
+constexpr float kLog2F = 6.0f;   // F = 2^6 = 2^(8 - tau): F * p <= 256
+constexpr int kScaleOne = 127;   // E8M0 block scale 2^0
+constexpr int kScaleLo = 123;    // E8M0 block scale 2^-4 (P_lo carries 16x its value)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
 
@@ -47,12 +51,20 @@ __device__ __forceinline__ int vt_pos(int k) {
   return 32 * ((k >> 2) & 1) + 16 * (k >> 5) + 4 * ((k >> 3) & 3) + (k & 3);
 }
 
+// MFMA operand format code (cbsz / blgp): 0 = fp8 (E4M3), 1 = bf8 (E5M2)
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+}
+
 template <int FMT>
-constexpr int mfma_fmt() { return FMT == E4M3 ? 0 : 1; }  // cbsz/blgp: 0 = fp8, 1 = bf8
+struct MfmaFmt {
+  static constexpr int value = FMT == E4M3 ? 0 : 1;
+};
 }  // namespace
 
 template <int FMT, int DH, int GT>
-__global__ __launch_bounds__(64 * GT) void prefill_kernel(
+__global__ __launch_bounds__(64 * GT)
+__attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void prefill_kernel(
     void* __restrict__ out, int out_bf16, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ cu, int n_qtiles, const float* __restrict__ qs, int q_per_head,
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc, int64_t num_blocks,
@@ -109,40 +121,45 @@ __global__ __launch_bounds__(64 * GT) void prefill_kernel(
       }
     }
   }
-  // log2-domain score = raw * sq * sk / sqrt(dh) * log2(e)
+  // log2-domain score = raw * sq * sk / sqrt(dh) * log2(e)  (zc > 0)
   const float zc = sm_scale * sq * ks[kv_per_head ? h : 0] * kLog2e;
 
-  f32x16 acc_hi[DH / 32], acc_lo[DH / 32];
+  // O^T accumulator: channels 32 dt + 8 i + 4 g + r of query c (one tile per
+  // 32 channels); P_hi and P_lo / 16 accumulate into the same tiles
+  f32x16 acc[DH / 32];
 #pragma unroll
   for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) { acc_hi[dt][v] = 0.0f; acc_lo[dt][v] = 0.0f; }
-  float m_run = kNegBig, l_run = 0.0f;
+    for (int v = 0; v < 16; ++v) acc[dt][v] = 0.0f;
+  // running max of the raw score (zc applied at use) and running sum of F p
+  float m_raw = kNegBig, l_run = 0.0f;
 
   const int32_t* btab = bt + (size_t)b * max_blocks;
   const size_t tile_stride = (size_t)16 * DH;
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    __syncthreads();  // previous tile fully consumed
-    // ---- K tile -> LDS, row-major: thread covers 32 bytes of one key
-    for (int u = threadIdx.x; u < kKT * (DH / 32); u += NT) {
-      const int key = u / (DH / 32), ch = u % (DH / 32);
+  // ---- staging of one 64-key tile: every thread owns a fixed set of 16-byte
+  //      K pieces and V channel rows; the next tile's pieces are loaded into
+  //      registers while the current tile is computed
+  constexpr int KP = kKT * DH / 16 / NT;  // K pieces (16 B) per thread
+  constexpr int VP = 4 * DH / NT;         // V (block, channel) rows (16 B) per thread
+  uint4 kreg[KP], vreg[VP];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int u = threadIdx.x + i * NT;
+      const int key = u / (DH / 16), piece = u % (DH / 16);
       const int bi = kt * 4 + (key >> 4);
-      uint4 a = make_uint4(0, 0, 0, 0), bq = make_uint4(0, 0, 0, 0);
+      kreg[i] = make_uint4(0, 0, 0, 0);
       if (bi < nblk_ctx) {
         int64_t blk = btab[bi];
         blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
-        const uint8_t* src = kc + ((size_t)blk * Hkv + h) * tile_stride + (key & 15) * DH + ch * 32;
-        a = *reinterpret_cast<const uint4*>(src);
-        bq = *reinterpret_cast<const uint4*>(src + 16);
+        kreg[i] = *reinterpret_cast<const uint4*>(kc + ((size_t)blk * Hkv + h) * tile_stride +
+                                                   (key & 15) * DH + piece * 16);
       }
-      *reinterpret_cast<uint4*>(k_lds + key * KROW + ch * 32) = a;
-      *reinterpret_cast<uint4*>(k_lds + key * KROW + ch * 32 + 16) = bq;
     }
-    // ---- V tile -> LDS: the cache tiles are already channel-major ([dh][16]);
-    //      thread copies the 16 token bytes of one channel of one block and
-    //      scatters its four dwords to their key-permuted positions
-    for (int u = threadIdx.x; u < 4 * DH; u += NT) {
+#pragma unroll
+    for (int i = 0; i < VP; ++i) {
+      const int u = threadIdx.x + i * NT;
       const int beta = u / DH, d = u - beta * DH;
       const int bi = kt * 4 + beta;
       uint4 w = make_uint4(0, 0, 0, 0);
@@ -156,20 +173,41 @@ __global__ __launch_bounds__(64 * GT) void prefill_kernel(
         if (left < 16) {
           uint32_t* wd = reinterpret_cast<uint32_t*>(&w);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int n = left - 4 * i;  // tokens of dword i inside the context
-            wd[i] &= n >= 4 ? 0xffffffffu : (n <= 0 ? 0u : (1u << (8 * n)) - 1);
+          for (int j = 0; j < 4; ++j) {
+            const int n = left - 4 * j;  // tokens of dword j inside the context
+            wd[j] &= n >= 4 ? 0xffffffffu : (n <= 0 ? 0u : (1u << (8 * n)) - 1);
           }
         }
       }
-      // dword i holds keys 16 beta + 4i .. + 3; vt_pos puts i = 0, 2 and i = 1, 3 side by side
-      uint8_t* row = v_lds + d * VROW + vt_pos(16 * beta);
-      *reinterpret_cast<uint2*>(row) = make_uint2(w.x, w.z);
-      *reinterpret_cast<uint2*>(row + 32) = make_uint2(w.y, w.w);
+      vreg[i] = w;
     }
-    __syncthreads();
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int u = threadIdx.x + i * NT;
+      const int key = u / (DH / 16), piece = u % (DH / 16);
+      *reinterpret_cast<uint4*>(k_lds + key * KROW + piece * 16) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VP; ++i) {
+      const int u = threadIdx.x + i * NT;
+      const int beta = u / DH, d = u - beta * DH;
+      // dword j holds keys 16 beta + 4j .. + 3; vt_pos puts j = 0, 2 and j = 1, 3 side by side
+      uint8_t* row = v_lds + d * VROW + vt_pos(16 * beta);
+      *reinterpret_cast<uint2*>(row) = make_uint2(vreg[i].x, vreg[i].z);
+      *reinterpret_cast<uint2*>(row + 32) = make_uint2(vreg[i].y, vreg[i].w);
+    }
+  };
 
-    // ---- S^T = K Q^T for keys [64kt, 64kt + 64)
+  if (nkt > 0) load_tile(0);
+  for (int kt = 0; kt < nkt; ++kt) {
+    __syncthreads();  // previous tile fully consumed
+    store_tile();
+    __syncthreads();
+    if (kt + 1 < nkt) load_tile(kt + 1);  // lands while this tile is computed
+
+    // ---- S^T = K Q^T for keys [64kt, 64kt + 64): raw FP8 dot products
     f32x16 s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -182,60 +220,69 @@ __global__ __launch_bounds__(64 * GT) void prefill_kernel(
         const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16);
         i32x8 A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                    (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        s[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, qb[m], s[t], mfma_fmt<FMT>(), 0,
-                                                               0, 0, 0, 0);
+        s[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, qb[m], s[t], MfmaFmt<FMT>::value,
+                                                               0, 0, 0, 0, 0);
       }
     }
 
     // ---- online softmax for this lane's query (column c); lane holds keys
-    //      64kt + 32t + 8(v/4) + 4g + (v%4)
-    const bool need_mask = kt * kKT + kKT - 1 > pos_min;
+    //      64kt + 32t + 8(v/4) + 4g + (v%4).  Causally masked scores (and
+    //      every key past the context) become -inf.
+    if (kt * kKT + kKT - 1 > pos_min) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kt * kKT + 32 * t + 8 * (v >> 2) + 4 * g + (v & 3);
+          s[t][v] = key <= pos ? s[t][v] : -__builtin_inff();
+        }
+    }
     float tmax = kNegBig;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float z = s[t][v] * zc;
-        if (need_mask) {
-          const int key = kt * kKT + 32 * t + 8 * (v >> 2) + 4 * g + (v & 3);
-          z = key <= pos ? z : -__builtin_inff();
-        }
-        s[t][v] = z;
-        tmax = __builtin_fmaxf(tmax, z);
-      }
+      for (int v = 0; v < 16; v += 2) tmax = fmax3(tmax, s[t][v], s[t][v + 1]);
     tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (tmax > m_run + kTau) {
-      const float f = __builtin_amdgcn_exp2f(m_run - tmax);
+    // the running max only moves when a score exceeds it by more than 2^tau
+    // (in log2 units), so F p stays <= F 2^tau = 256 and rescales are rare
+    if (__builtin_amdgcn_ballot_w64((tmax - m_raw) * zc > kTau)) {
+      const float mnew = __builtin_fmaxf(m_raw, tmax);
+      const float f = __builtin_amdgcn_exp2f((m_raw - mnew) * zc);
       l_run *= f;
 #pragma unroll
       for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) { acc_hi[dt][v] *= f; acc_lo[dt][v] *= f; }
-      m_run = tmax;
+        for (int v = 0; v < 16; ++v) acc[dt][v] *= f;
+      m_raw = mnew;
     }
+    // F p = exp2(raw * zc - (m * zc - log2 F)); P_hi = e4m3(F p),
+    // P_lo = e4m3(16 (F p - P_hi)); both exact-range, no saturation needed
+    const float bias = m_raw * zc - kLog2F;
     i32x8 ph, pl;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
-        float fp[4], lo[4];
+        float fp[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[t][4 * v4 + r] - m_run);
-          l_run += p;
-          fp[r] = p * kPF;
+          fp[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][4 * v4 + r], zc, -bias));
+          l_run += fp[r];
         }
-        const uint32_t hi = enc4<E4M3>(fp[0], fp[1], fp[2], fp[3]);
-        const f32x2 h01 = dec2_f32<E4M3, false>(hi), h23 = dec2_f32<E4M3, true>(hi);
-        lo[0] = (fp[0] - h01.x) * 16.0f;
-        lo[1] = (fp[1] - h01.y) * 16.0f;
-        lo[2] = (fp[2] - h23.x) * 16.0f;
-        lo[3] = (fp[3] - h23.y) * 16.0f;
-        ph[4 * t + v4] = (int)hi;
-        pl[4 * t + v4] = (int)enc4<E4M3>(lo[0], lo[1], lo[2], lo[3]);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[0], fp[1], 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[2], fp[3], hi, true);
+        const f32x2 h01 = dec2_f32<E4M3, false>((uint32_t)hi);
+        const f32x2 h23 = dec2_f32<E4M3, true>((uint32_t)hi);
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32((fp[0] - h01.x) * 16.0f, (fp[1] - h01.y) * 16.0f,
+                                                 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32((fp[2] - h23.x) * 16.0f, (fp[3] - h23.y) * 16.0f, lo,
+                                             true);
+        ph[4 * t + v4] = hi;
+        pl[4 * t + v4] = lo;
       }
 
-    // ---- O^T += V^T P^T for channel tiles of 32
+    // ---- O^T += V^T P^T for channel tiles of 32: P_hi at scale 1, P_lo at
+    //      scale 2^-4 (E8M0 block scales 127 and 123) into one accumulator
 #pragma unroll
     for (int dt = 0; dt < DH / 32; ++dt) {
       const uint8_t* ap = v_lds + (32 * dt + c) * VROW + 32 * g;
@@ -243,19 +290,19 @@ __global__ __launch_bounds__(64 * GT) void prefill_kernel(
       const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16);
       i32x8 A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                  (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      acc_hi[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, ph, acc_hi[dt],
-                                                                   mfma_fmt<FMT>(), 0, 0, 0, 0, 0);
-      acc_lo[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, pl, acc_lo[dt],
-                                                                   mfma_fmt<FMT>(), 0, 0, 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, ph, acc[dt], MfmaFmt<FMT>::value,
+                                                                0, 0, kScaleOne, 0, kScaleOne);
+      acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, pl, acc[dt], MfmaFmt<FMT>::value,
+                                                                0, 0, kScaleOne, 0, kScaleLo);
     }
   }
 
-  // ---- epilogue: O = (acc_hi + acc_lo/16) / (F * l) * sV; lane holds
-  //      channels 32dt + 8i + 4g + r of query c
+  // ---- epilogue: O = acc / (sum of F p) * sV; lane holds channels
+  //      32dt + 8i + 4g + r of query c
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!qvalid) return;
   const float sv = vs[kv_per_head ? h : 0];
-  const float scale = l_tot > 0.0f ? sv / (l_tot * kPF) : 0.0f;
+  const float scale = l_tot > 0.0f ? sv / l_tot : 0.0f;
   const size_t orow = ((size_t)(q0 + qi) * Hq + hq) * DH;
 #pragma unroll
   for (int dt = 0; dt < DH / 32; ++dt)
@@ -263,8 +310,7 @@ __global__ __launch_bounds__(64 * GT) void prefill_kernel(
     for (int i = 0; i < 4; ++i) {
       float o[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        o[r] = (acc_hi[dt][4 * i + r] + acc_lo[dt][4 * i + r] * 0.0625f) * scale;
+      for (int r = 0; r < 4; ++r) o[r] = acc[dt][4 * i + r] * scale;
       const int d = 32 * dt + 8 * i + 4 * g;
       if (out_bf16) {
         uint2 w;
