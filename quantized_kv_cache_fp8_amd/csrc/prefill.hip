@@ -144,42 +144,58 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
   constexpr int VP = 4 * DH / NT;         // V (block, channel) rows (16 B) per thread
   uint4 kreg[KP], vreg[VP];
   auto load_tile = [&](int kt) {
+    // the tile's 4 block ids are the same for the whole workgroup: scalar
+    // loads, so waiting for them never drains the vector loads in flight
+    size_t base[4];
+    bool live[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int bi = kt * 4 + j;
+      live[j] = bi < nblk_ctx;
+      int64_t blk = btab[live[j] ? bi : nblk_ctx - 1];  // nblk_ctx >= 1 inside the loop
+      blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
+      base[j] = ((size_t)blk * Hkv + h) * tile_stride;
+    }
+    auto pick = [&](int j, size_t& off, bool& ok) {
+      off = j == 0 ? base[0] : j == 1 ? base[1] : j == 2 ? base[2] : base[3];
+      ok = j == 0 ? live[0] : j == 1 ? live[1] : j == 2 ? live[2] : live[3];
+    };
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int u = threadIdx.x + i * NT;
       const int key = u / (DH / 16), piece = u % (DH / 16);
-      const int bi = kt * 4 + (key >> 4);
+      size_t off;
+      bool ok;
+      pick(key >> 4, off, ok);
       kreg[i] = make_uint4(0, 0, 0, 0);
-      if (bi < nblk_ctx) {
-        int64_t blk = btab[bi];
-        blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
-        kreg[i] = *reinterpret_cast<const uint4*>(kc + ((size_t)blk * Hkv + h) * tile_stride +
-                                                   (key & 15) * DH + piece * 16);
-      }
+      if (ok)
+        kreg[i] = *reinterpret_cast<const uint4*>(kc + off + (key & 15) * DH + piece * 16);
     }
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
       const int u = threadIdx.x + i * NT;
       const int beta = u / DH, d = u - beta * DH;
-      const int bi = kt * 4 + beta;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (bi < nblk_ctx) {
-        int64_t blk = btab[bi];
-        blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
-        w = *reinterpret_cast<const uint4*>(vc + ((size_t)blk * Hkv + h) * tile_stride + d * 16);
-        // slots past the context may hold any bytes, NaN codes included; their
-        // zero weights would not cancel a NaN, so they are zeroed here
-        const int left = ctx - bi * 16;
-        if (left < 16) {
-          uint32_t* wd = reinterpret_cast<uint32_t*>(&w);
+      size_t off;
+      bool ok;
+      pick(beta, off, ok);
+      vreg[i] = make_uint4(0, 0, 0, 0);
+      if (ok) vreg[i] = *reinterpret_cast<const uint4*>(vc + off + d * 16);
+    }
+    // slots past the context may hold any bytes, NaN codes included; their
+    // zero weights would not cancel a NaN, so they are zeroed (only the tile
+    // holding the context's last block has any)
+    if (kt * kKT + kKT > ctx) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = left - 4 * j;  // tokens of dword j inside the context
-            wd[j] &= n >= 4 ? 0xffffffffu : (n <= 0 ? 0u : (1u << (8 * n)) - 1);
-          }
+      for (int i = 0; i < VP; ++i) {
+        const int beta = (threadIdx.x + i * NT) / DH;
+        const int left = ctx - (kt * 4 + beta) * 16;  // tokens of this block inside the context
+        uint32_t* wd = reinterpret_cast<uint32_t*>(&vreg[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = left - 4 * j;  // tokens of dword j inside the context
+          wd[j] &= n >= 4 ? 0xffffffffu : (n <= 0 ? 0u : (1u << (8 * n)) - 1);
         }
       }
-      vreg[i] = w;
     }
   };
   auto store_tile = [&]() {
