@@ -34,6 +34,7 @@ namespace kvq {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 constexpr int kQT = 32;          // query rows per wave
@@ -143,16 +144,20 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
   constexpr int KP = kKT * DH / 16 / NT;  // K pieces (16 B) per thread
   constexpr int VP = 4 * DH / NT;         // V (block, channel) rows (16 B) per thread
   uint4 kreg[KP], vreg[VP];
-  auto load_tile = [&](int kt) {
-    // the tile's 4 block ids are the same for the whole workgroup: scalar
-    // loads, so waiting for them never drains the vector loads in flight
+  // block ids of tile kt: lanes 0..3 of idv hold btab[4 kt + lane] (clamped
+  // to the context's last block); loaded one tile ahead as a vector load, so
+  // neither a scalar-load chain nor a wait for it sits on the tile's path
+  auto load_ids = [&](int kt) {
+    const int bi = kt * 4 + (lane & 3);
+    return btab[bi < nblk_ctx ? bi : nblk_ctx - 1];
+  };
+  auto load_tile = [&](int kt, int idv) {
     size_t base[4];
     bool live[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int bi = kt * 4 + j;
-      live[j] = bi < nblk_ctx;
-      int64_t blk = btab[live[j] ? bi : nblk_ctx - 1];  // nblk_ctx >= 1 inside the loop
+      live[j] = kt * 4 + j < nblk_ctx;
+      int64_t blk = __builtin_amdgcn_readlane(idv, j);
       blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
       base[j] = ((size_t)blk * Hkv + h) * tile_stride;
     }
@@ -216,21 +221,28 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
     }
   };
 
-  if (nkt > 0) load_tile(0);
+  i32x8 ph = {}, pl = {};  // probability operands (every byte rewritten per tile)
+  int ids_next = 0;
+  if (nkt > 0) {
+    load_tile(0, load_ids(0));
+    if (nkt > 1) ids_next = load_ids(1);
+  }
   for (int kt = 0; kt < nkt; ++kt) {
     __syncthreads();  // previous tile fully consumed
     store_tile();
     __syncthreads();
-    if (kt + 1 < nkt) load_tile(kt + 1);  // lands while this tile is computed
+    if (kt + 1 < nkt) load_tile(kt + 1, ids_next);  // lands while this tile is computed
 
     // ---- S^T = K Q^T for keys [64kt, 64kt + 64): raw FP8 dot products
     f32x16 s[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[t][v] = 0.0f;
 #pragma unroll
-      for (int m = 0; m < DH / 64; ++m) {
+    for (int m = 0; m < DH / 64; ++m)  // the two key halves' chains interleave
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
         const uint8_t* ap = k_lds + (32 * t + c) * KROW + 64 * m + 32 * g;
         const uint4 a0 = *reinterpret_cast<const uint4*>(ap);
         const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16);
@@ -239,7 +251,6 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
         s[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, qb[m], s[t], MfmaFmt<FMT>::value,
                                                                0, 0, 0, 0, 0);
       }
-    }
 
     // ---- online softmax for this lane's query (column c); lane holds keys
     //      64kt + 32t + 8(v/4) + 4g + (v%4).  Causally masked scores (and
@@ -274,7 +285,6 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
     // F p = exp2(raw * zc - (m * zc - log2 F)); P_hi = e4m3(F p),
     // P_lo = e4m3(16 (F p - P_hi)); both exact-range, no saturation needed
     const float bias = m_raw * zc - kLog2F;
-    i32x8 ph, pl;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -285,32 +295,43 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
           fp[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][4 * v4 + r], zc, -bias));
           l_run += fp[r];
         }
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[0], fp[1], 0, false);
+        // both halves of each dword are written, so the merge operand's old
+        // contents do not matter
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[0], fp[1], ph[4 * t + v4], false);
         hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[2], fp[3], hi, true);
         const f32x2 h01 = dec2_f32<E4M3, false>((uint32_t)hi);
         const f32x2 h23 = dec2_f32<E4M3, true>((uint32_t)hi);
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32((fp[0] - h01.x) * 16.0f, (fp[1] - h01.y) * 16.0f,
-                                                 0, false);
-        lo = __builtin_amdgcn_cvt_pk_fp8_f32((fp[2] - h23.x) * 16.0f, (fp[3] - h23.y) * 16.0f, lo,
-                                             true);
+        // the scaled encode divides by its scale: e4m3((F p - P_hi) * 16)
+        s16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+            __builtin_bit_cast(s16x2, pl[4 * t + v4]), fp[0] - h01.x, fp[1] - h01.y, 0.0625f,
+            false);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, fp[2] - h23.x, fp[3] - h23.y, 0.0625f,
+                                                      true);
         ph[4 * t + v4] = hi;
-        pl[4 * t + v4] = lo;
+        pl[4 * t + v4] = __builtin_bit_cast(int, lo);
       }
 
     // ---- O^T += V^T P^T for channel tiles of 32: P_hi at scale 1, P_lo at
     //      scale 2^-4 (E8M0 block scales 127 and 123) into one accumulator
+    i32x8 va[DH / 32];
 #pragma unroll
     for (int dt = 0; dt < DH / 32; ++dt) {
       const uint8_t* ap = v_lds + (32 * dt + c) * VROW + 32 * g;
       const uint4 a0 = *reinterpret_cast<const uint4*>(ap);
       const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16);
-      i32x8 A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                 (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, ph, acc[dt], MfmaFmt<FMT>::value,
-                                                                0, 0, kScaleOne, 0, kScaleOne);
-      acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, pl, acc[dt], MfmaFmt<FMT>::value,
-                                                                0, 0, kScaleOne, 0, kScaleLo);
+      va[dt] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                     (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
     }
+    // the next tile's block ids: their latency overlaps the MFMAs below
+    if (kt + 2 < nkt) ids_next = load_ids(kt + 2);
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt)
+      acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          va[dt], ph, acc[dt], MfmaFmt<FMT>::value, 0, 0, kScaleOne, 0, kScaleOne);
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt)
+      acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          va[dt], pl, acc[dt], MfmaFmt<FMT>::value, 0, 0, kScaleOne, 0, kScaleLo);
   }
 
   // ---- epilogue: O = acc / (sum of F p) * sV; lane holds channels
