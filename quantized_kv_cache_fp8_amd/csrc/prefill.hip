@@ -75,8 +75,10 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
   constexpr int NT = 64 * GT;          // threads
   constexpr int KROW = DH + 16;        // padded K row in LDS (bytes)
   constexpr int VROW = kKT + 16;       // padded transposed-V row in LDS (bytes)
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kKT * KROW];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[DH * VROW];
+  // two K/V tile buffers: tile kt is read from buffer kt & 1 while tile kt + 1
+  // is written into the other one
+  __shared__ __attribute__((aligned(16))) uint8_t k_buf[2][kKT * KROW];
+  __shared__ __attribute__((aligned(16))) uint8_t v_buf[2][DH * VROW];
 
   const int qt = n_qtiles - 1 - (int)blockIdx.x;  // longest tiles first
   const int grp = blockIdx.y, b = blockIdx.z;
@@ -203,7 +205,7 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](uint8_t* k_lds, uint8_t* v_lds) {
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int u = threadIdx.x + i * NT;
@@ -225,13 +227,14 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
   int ids_next = 0;
   if (nkt > 0) {
     load_tile(0, load_ids(0));
-    if (nkt > 1) ids_next = load_ids(1);
+    store_tile(k_buf[0], v_buf[0]);
+    if (nkt > 1) load_tile(1, load_ids(1));
+    __syncthreads();
   }
   for (int kt = 0; kt < nkt; ++kt) {
-    __syncthreads();  // previous tile fully consumed
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < nkt) load_tile(kt + 1, ids_next);  // lands while this tile is computed
+    const uint8_t* k_lds = k_buf[kt & 1];
+    const uint8_t* v_lds = v_buf[kt & 1];
+    if (kt + 2 < nkt) ids_next = load_ids(kt + 2);  // lands during this tile
 
     // ---- S^T = K Q^T for keys [64kt, 64kt + 64): raw FP8 dot products
     f32x16 s[2];
@@ -322,8 +325,6 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
       va[dt] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
     }
-    // the next tile's block ids: their latency overlaps the MFMAs below
-    if (kt + 2 < nkt) ids_next = load_ids(kt + 2);
 #pragma unroll
     for (int dt = 0; dt < DH / 32; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -332,6 +333,15 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
     for (int dt = 0; dt < DH / 32; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
           va[dt], pl, acc[dt], MfmaFmt<FMT>::value, 0, 0, kScaleOne, 0, kScaleLo);
+
+    // ---- tile kt + 1 (loaded during this tile) into the other buffer, whose
+    //      readers all passed the previous barrier; then start loading tile
+    //      kt + 2; one barrier per tile
+    if (kt + 1 < nkt) {
+      store_tile(k_buf[(kt + 1) & 1], v_buf[(kt + 1) & 1]);
+      if (kt + 2 < nkt) load_tile(kt + 2, ids_next);
+    }
+    __syncthreads();
   }
 
   // ---- epilogue: O = acc / (sum of F p) * sV; lane holds channels
