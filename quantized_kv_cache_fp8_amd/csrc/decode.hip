@@ -361,66 +361,58 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 }
 
 // grid (Hq, B), DH threads: merge the valid splits of one (b, hq) row.
+// Splits are taken 16 at a time, every load of a batch issued together (the
+// (m, l) pairs are the same for all threads of the row: broadcast loads), and
+// merged by log-sum-exp with a running maximum, so a typical row costs one
+// round trip to memory and needs no LDS or barrier.
 template <int DH, bool BF16>
 __global__ __launch_bounds__(DH) void decode_combine_kernel(
     void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
     const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int max_ctx,
     const float* __restrict__ vs, int per_head, int part_blocks, int nsplit) {
-  __shared__ float s_w[DH];
-  __shared__ float s_red[2];
+  constexpr int kBatch = 16;
   const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   int ctx = ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > max_ctx ? max_ctx : ctx);
   const int span = part_blocks * kBlockSize;
   const int nvalid = (ctx + span - 1) / span;
   const size_t row0 = ((size_t)b * Hq + hq) * nsplit;
-  float a = 0.0f;
-  float L = 0.0f;
-  // splits are merged in chunks of DH: weights exp2(m_s - M) staged in LDS
-  float M = kNegBig;
-  for (int s = d; s < nvalid; s += DH) M = __builtin_fmaxf(M, ws_ml[(row0 + s) * 2]);
-  for (int off = 32; off >= 1; off >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, off));
-  if (DH > 64) {  // two waves: combine their maxima
-    if ((d & 63) == 0) s_red[d >> 6] = M;
-    __syncthreads();
-    M = __builtin_fmaxf(s_red[0], s_red[1]);
-  }
-  for (int s0 = 0; s0 < nvalid; s0 += DH) {
-    __syncthreads();
-    const int s = s0 + d;
-    float w = 0.0f;
-    if (s < nvalid) {
-      w = __builtin_amdgcn_exp2f(ws_ml[(row0 + s) * 2] - M);
-      L += w * ws_ml[(row0 + s) * 2 + 1];
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml);
+  float M = kNegBig, L = 0.0f, a = 0.0f;
+  for (int s0 = 0; s0 < nvalid; s0 += kBatch) {
+    const int n = nvalid - s0 < kBatch ? nvalid - s0 : kBatch;
+    float2 p[kBatch];
+    float o[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      p[j] = make_float2(kNegBig, 0.0f);
+      o[j] = 0.0f;
+      if (j < n) {
+        p[j] = ml[row0 + s0 + j];
+        o[j] = ws_acc[(row0 + s0 + j) * DH + d];
+      }
     }
-    s_w[d] = w;
-    __syncthreads();
-    const int n = nvalid - s0 < DH ? nvalid - s0 : DH;
-    int j = 0;
-    for (; j + 4 <= n; j += 4) {  // four independent loads in flight
-      const float a0 = ws_acc[(row0 + s0 + j) * DH + d];
-      const float a1 = ws_acc[(row0 + s0 + j + 1) * DH + d];
-      const float a2 = ws_acc[(row0 + s0 + j + 2) * DH + d];
-      const float a3 = ws_acc[(row0 + s0 + j + 3) * DH + d];
-      a += s_w[j] * a0 + s_w[j + 1] * a1 + s_w[j + 2] * a2 + s_w[j + 3] * a3;
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) Mn = __builtin_fmaxf(Mn, p[j].x);
+    const float f = __builtin_amdgcn_exp2f(M - Mn);
+    L *= f;
+    a *= f;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float w = __builtin_amdgcn_exp2f(p[j].x - Mn);  // 0 for the padding entries
+      L += w * p[j].y;
+      a += w * o[j];
     }
-    for (; j < n; ++j) a += s_w[j] * ws_acc[(row0 + s0 + j) * DH + d];
-  }
-  // total l: sum of the per-thread partial sums
-  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
-  if (DH > 64) {
-    __syncthreads();
-    if ((d & 63) == 0) s_red[d >> 6] = L;
-    __syncthreads();
-    L = s_red[0] + s_red[1];
+    M = Mn;
   }
   const int h = hq / (Hq / Hkv);
   const float r = L > 0.0f ? a / L * vs[per_head ? h : 0] : 0.0f;
-  const size_t o = ((size_t)b * Hq + hq) * DH + d;
+  const size_t oi = ((size_t)b * Hq + hq) * DH + d;
   if constexpr (BF16)
-    reinterpret_cast<uint16_t*>(out)[o] = (uint16_t)f32_to_bf16_rne(r);
+    reinterpret_cast<uint16_t*>(out)[oi] = (uint16_t)f32_to_bf16_rne(r);
   else
-    reinterpret_cast<float*>(out)[o] = r;
+    reinterpret_cast<float*>(out)[oi] = r;
 }
 
 static int heads_per_group(int G) {
