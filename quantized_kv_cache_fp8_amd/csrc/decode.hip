@@ -48,6 +48,11 @@ namespace kvq {
 // Waves per SIMD the split kernel is compiled for.  At 4 the whole state
 // (Q operand, one block pair of codes, the O tile) fits in 128 registers, so
 // a compute unit keeps 16 waves' loads in flight.
+// Whether cache loads are marked nontemporal: every cache byte is read once
+// per call, so the loads stream through L2 instead of allocating in it.
+#ifndef KVQ_DECODE_NT_LOADS
+#define KVQ_DECODE_NT_LOADS 1
+#endif
 #ifndef KVQ_DECODE_WAVES_PER_EU
 #define KVQ_DECODE_WAVES_PER_EU 4
 #endif
@@ -93,6 +98,25 @@ __device__ __forceinline__ f16x8 codes_to_f16x8(uint32_t a, uint32_t b) {
                              __builtin_bit_cast(uint32_t, dec2_f16<FMT, false>(b)),
                              __builtin_bit_cast(uint32_t, dec2_f16<FMT, true>(b)));
   return __builtin_bit_cast(f16x8, u);
+}
+
+__device__ __forceinline__ uint4 load16(const uint8_t* p) {
+#if KVQ_DECODE_NT_LOADS
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *reinterpret_cast<const uint4*>(p);
+#endif
+}
+__device__ __forceinline__ uint2 load8(const uint8_t* p) {
+#if KVQ_DECODE_NT_LOADS
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+#else
+  return *reinterpret_cast<const uint2*>(p);
+#endif
 }
 
 __device__ __forceinline__ int64_t clamp_block(int64_t blk, int64_t num_blocks) {
@@ -202,8 +226,8 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
       kr[e] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
       if (chan_live) {
         const uint8_t* src = kc + block_src(2 * p + e) * tile + c16 * DH + 16 * g4;
-        const uint4 a0 = *reinterpret_cast<const uint4*>(src);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(src + HALF);
+        const uint4 a0 = load16(src);
+        const uint4 a1 = load16(src + HALF);
         kr[e] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                       (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
       }
@@ -212,7 +236,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   auto load_v = [&](int p) {
     const uint8_t* src = vc + block_src(2 * p + eb) * tile + c16 * kBlockSize + tk;
 #pragma unroll
-    for (int n = 0; n < NV; ++n) vr[n] = *reinterpret_cast<const uint2*>(src + 16 * n * kBlockSize);
+    for (int n = 0; n < NV; ++n) vr[n] = load8(src + 16 * n * kBlockSize);
   };
 
   int p = wave;
