@@ -126,7 +126,9 @@ def main():
     K.kvq_calibrate_scales(v_all, "fp8_e4m3", "tensor", amax, vs)
     caches = []
     for _ in range(args.copies):
-        kc = torch.empty((wl.paging.num_blocks, Hkv, bs, dh), dtype=torch.uint8, device=dev)
+        # K tiles: 16-channel chunks, token-major inside a chunk
+        kc = torch.empty((wl.paging.num_blocks, Hkv, dh // 16, bs, 16), dtype=torch.uint8,
+                         device=dev)
         vc = torch.empty((wl.paging.num_blocks, Hkv, dh, bs), dtype=torch.uint8, device=dev)
         K.kvq_cache_write(k_all, v_all, slots_all, kc, vc, ks, vs, "fp8_e4m3", "tensor")
         caches.append((kc, vc))
@@ -269,7 +271,8 @@ def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, 
     K.kvq_calibrate_scales(q, "fp8_e4m3", "head", am, qs)
     K.kvq_calibrate_scales(pk, "fp8_e4m3", "head", am[:pw.Hkv], pks)
     K.kvq_calibrate_scales(pv, "fp8_e4m3", "head", am[:pw.Hkv], pvs)
-    pkc = torch.empty((pw.paging.num_blocks, pw.Hkv, pw.bs, pw.dh), dtype=torch.uint8, device=dev)
+    pkc = torch.empty((pw.paging.num_blocks, pw.Hkv, pw.dh // 16, pw.bs, 16), dtype=torch.uint8,
+                      device=dev)
     pvc = torch.empty((pw.paging.num_blocks, pw.Hkv, pw.dh, pw.bs), dtype=torch.uint8, device=dev)
     K.kvq_cache_write(pk, pv, dt(pw.kv.slot_mapping), pkc, pvc, pks, pvs, "fp8_e4m3", "head")
     out = torch.empty((q.shape[0], pw.Hq, pw.dh), dtype=torch.float32, device=dev)
@@ -299,7 +302,7 @@ def cpu_baseline(wl, sample_rows, min_seconds):
     fmt, gran = oracle.FMT_E4M3, oracle.GRAN_TENSOR
     ks = oracle.calibrate(wl.kv.k, fmt, gran)[1]
     vs = oracle.calibrate(wl.kv.v, fmt, gran)[1]
-    kc = np.zeros((wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh), np.uint8)
+    kc = np.zeros(oracle.k_cache_shape(wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh), np.uint8)
     vc = np.zeros((wl.paging.num_blocks, wl.Hkv, wl.dh, wl.bs), np.uint8)
     oracle.cache_write(wl.kv.k, wl.kv.v, wl.kv.slot_mapping, kc, vc, ks, vs, fmt, gran)
     rows = np.array([(b, h) for b in range(wl.B) for h in range(wl.Hq)], np.int32)

@@ -29,12 +29,15 @@
  *   invalid arguments returns an error and touches no device memory.
  * - bf16 tensors are passed as void* holding IEEE bfloat16 bit patterns.
  * - Cache layout (this library's design; the pages fix only that FP8 caches
- *   are raw bytes): k_cache is uint8 [num_blocks][Hkv][bs][dh] (token-major
- *   tiles) and v_cache is uint8 [num_blocks][Hkv][dh][bs] (channel-major
- *   tiles).  Token position j of sequence b lives in physical block
+ *   are raw bytes): k_cache is uint8 [num_blocks][Hkv][dh/16][bs][16] (each
+ *   tile is cut into 16-channel chunks, token-major inside a chunk: channel d
+ *   of the token at offset o sits at byte (d/16)*bs*16 + o*16 + d%16 of its
+ *   tile) and v_cache is uint8 [num_blocks][Hkv][dh][bs] (channel-major tiles).
+ *   Token position j of sequence b lives in physical block
  *   block_tables[b][j / bs] at offset j % bs.  Each (block, head) tile is one
- *   contiguous bs*dh-byte run.  Attention contracts K over channels and V over
- *   tokens, so these orders give both contractions contiguous operands.
+ *   contiguous bs*dh-byte run.  The K order lets one 64-lane load of the
+ *   matrix-core operand (16 tokens x 4 chunks) cover 1 KB of contiguous
+ *   memory; V is channel-major because P V contracts over tokens.
  * - GQA: query head hq reads KV head hq / (Hq / Hkv).
  * - Supported now: dh in {64, 128}; bs == 16; Hq % Hkv == 0; Hq/Hkv <= 16.
  * - Calls are reentrant; calls on the same stream run in order.
@@ -120,7 +123,7 @@ kvq_status kvq_calibrate_scales(const void* x_bf16, int64_t T, int H, int dh, kv
  * cast_fp8(K / sK)):
  *   for every token t with 0 <= slot_mapping[t] < num_blocks * bs, every KV
  *   head h and channel d:
- *     k_cache[slot / bs][h][slot % bs][d] = fp8(fl32(k[t][h][d] / sK))
+ *     k_cache[slot / bs][h][d / 16][slot % bs][d % 16] = fp8(fl32(k[t][h][d] / sK))
  *     v_cache[slot / bs][h][d][slot % bs] = fp8(fl32(v[t][h][d] / sV))
  *   with s = scale[h] (KVQ_SCALE_HEAD) or scale[0] (KVQ_SCALE_TENSOR), the
  *   quotient correctly rounded to fp32 and fp8() the encoder above.  Tokens

@@ -170,13 +170,39 @@ def calibrate(x_bf16, fmt: int, gran: int):
     return amax, scale
 
 
+def k_cache_shape(num_blocks: int, Hkv: int, bs: int, dh: int) -> tuple:
+    """K cache: tiles of 16-channel chunks, token-major inside a chunk:
+    [num_blocks][Hkv][dh/16][bs][16]."""
+    return (num_blocks, Hkv, dh // 16, bs, 16)
+
+
+def v_cache_shape(num_blocks: int, Hkv: int, bs: int, dh: int) -> tuple:
+    """V cache: channel-major tiles [num_blocks][Hkv][dh][bs]."""
+    return (num_blocks, Hkv, dh, bs)
+
+
+def k_token_view(k_cache: np.ndarray) -> np.ndarray:
+    """The K cache as [num_blocks][Hkv][bs][dh]: element [blk, h, off, d] is the
+    code of channel d of the token in slot off (a copy)."""
+    nb, Hkv, nc, bs, w = k_cache.shape
+    return k_cache.transpose(0, 1, 3, 2, 4).reshape(nb, Hkv, bs, nc * w)
+
+
+def _kv_dims(k_cache):
+    """(num_blocks, Hkv, bs, dh); the K layout needs dh to be a multiple of 16."""
+    nb, Hkv, nc, bs, w = k_cache.shape
+    assert w == 16
+    return nb, Hkv, bs, nc * w
+
+
 def cache_write(k_bf16, v_bf16, slot_mapping: np.ndarray, k_cache: np.ndarray,
                 v_cache: np.ndarray, k_scale, v_scale, fmt: int, gran: int) -> None:
-    """Quantize-write (in place) into uint8 caches: K [num_blocks][Hkv][bs][dh]
-    (token-major tiles), V [num_blocks][Hkv][dh][bs] (channel-major tiles)."""
+    """Quantize-write (in place) into uint8 caches: K [num_blocks][Hkv][dh/16][bs][16]
+    (16-channel chunks, token-major inside a chunk), V [num_blocks][Hkv][dh][bs]
+    (channel-major tiles)."""
     k, v = _u16(k_bf16), _u16(v_bf16)
     T, Hkv, dh = k.shape
-    nb, hk, bs, dh2 = k_cache.shape
+    nb, hk, bs, dh2 = _kv_dims(k_cache)
     assert hk == Hkv and dh2 == dh and v_cache.shape == (nb, Hkv, dh, bs)
     sm = np.ascontiguousarray(slot_mapping, np.int64)
     ks = np.ascontiguousarray(k_scale, np.float32)
@@ -189,7 +215,7 @@ def decode_attn(q_bf16, k_cache, v_cache, block_tables, context_lens, k_scale, v
                 gran, softmax_scale: float = 0.0) -> np.ndarray:
     q = _u16(q_bf16)
     B, Hq, dh = q.shape
-    _, Hkv, bs, _ = k_cache.shape
+    _, Hkv, bs, _ = _kv_dims(k_cache)
     bt = np.ascontiguousarray(block_tables, np.int32)
     cl = np.ascontiguousarray(context_lens, np.int32)
     ks = np.ascontiguousarray(k_scale, np.float32)
@@ -205,7 +231,7 @@ def decode_rows(rows: np.ndarray, q_bf16, k_cache, v_cache, block_tables, contex
     """Decode output for the listed (b, hq) pairs only; returns fp64 [n, dh]."""
     q = _u16(q_bf16)
     B, Hq, dh = q.shape
-    _, Hkv, bs, _ = k_cache.shape
+    _, Hkv, bs, _ = _kv_dims(k_cache)
     rows = np.ascontiguousarray(rows, np.int32).reshape(-1, 2)
     bt = np.ascontiguousarray(block_tables, np.int32)
     cl = np.ascontiguousarray(context_lens, np.int32)
@@ -223,7 +249,7 @@ def prefill_attn(q_bf16, cu_seqlens, q_scale, q_gran, k_cache, v_cache, block_ta
                  softmax_scale: float = 0.0) -> np.ndarray:
     q = _u16(q_bf16)
     total, Hq, dh = q.shape
-    _, Hkv, bs, _ = k_cache.shape
+    _, Hkv, bs, _ = _kv_dims(k_cache)
     cu = np.ascontiguousarray(cu_seqlens, np.int32)
     B = cu.shape[0] - 1
     bt = np.ascontiguousarray(block_tables, np.int32)
@@ -244,7 +270,7 @@ def prefill_rows(rows: np.ndarray, q_bf16, cu_seqlens, q_scale, q_gran, k_cache,
     """Prefill output for the listed (query row, hq) pairs only; fp64 [n, dh]."""
     q = _u16(q_bf16)
     total, Hq, dh = q.shape
-    _, Hkv, bs, _ = k_cache.shape
+    _, Hkv, bs, _ = _kv_dims(k_cache)
     rows = np.ascontiguousarray(rows, np.int64).reshape(-1, 2)
     cu = np.ascontiguousarray(cu_seqlens, np.int32)
     B = cu.shape[0] - 1

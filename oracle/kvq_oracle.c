@@ -195,13 +195,15 @@ void orc_calibrate(const uint16_t* x, int64_t T, int H, int dh, int fmt, int gra
 /* ---- paged quantize-write ----
  * For every token t with 0 <= slot_mapping[t] < num_blocks * bs, every KV head
  * h and channel d, with blk = slot / bs and off = slot % bs:
- *   K code -> k_cache[blk][h][off][d]   (token-major tile [bs][dh])
- *   V code -> v_cache[blk][h][d][off]   (channel-major tile [dh][bs])
+ *   K code -> k_cache[blk][h][d / 16][off][d % 16]  (tile [dh/16][bs][16]:
+ *             16-channel chunks, token-major inside a chunk)
+ *   V code -> v_cache[blk][h][d][off]               (channel-major tile [dh][bs])
  * each code = quantize(x[t][h][d], s[h or 0]).  The two tile orders are this
- * library's layout (the pages fix only that FP8 caches are raw bytes). */
+ * library's layout (the pages fix only that FP8 caches are raw bytes); the K
+ * order needs dh to be a multiple of 16. */
 
 static int64_t k_index(int64_t blk, int h, int off, int d, int Hkv, int bs, int dh) {
-  return ((blk * Hkv + h) * bs + off) * dh + d;
+  return (((blk * Hkv + h) * (dh / 16) + d / 16) * bs + off) * 16 + d % 16;
 }
 static int64_t v_index(int64_t blk, int h, int off, int d, int Hkv, int bs, int dh) {
   return ((blk * Hkv + h) * dh + d) * bs + off;

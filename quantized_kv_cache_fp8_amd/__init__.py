@@ -81,6 +81,19 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+def _cache_dims(k_cache, v_cache):
+    """(num_blocks, Hkv, bs, dh) of a cache pair: K uint8 [nb, Hkv, dh/16, bs, 16]
+    (16-channel chunks, token-major inside a chunk), V uint8 [nb, Hkv, dh, bs]."""
+    if k_cache.dim() != 5 or k_cache.shape[4] != 16 or v_cache.dim() != 4:
+        raise ValueError("k_cache must be [nb, Hkv, dh/16, bs, 16] and v_cache [nb, Hkv, dh, bs]")
+    nb, Hkv, nc, bs, _ = k_cache.shape
+    dh = nc * 16
+    if tuple(v_cache.shape) != (nb, Hkv, dh, bs):
+        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} does not match k_cache "
+                         f"{tuple(k_cache.shape)}")
+    return nb, Hkv, bs, dh
+
+
 def _stream(stream) -> int | None:
     if stream is not None:
         return int(stream)
@@ -125,9 +138,10 @@ def kvq_calibrate_scales(x, fmt, gran, amax_io, scale_out, accumulate=False, str
 
 def kvq_cache_write(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, fmt, gran,
                     stream=None) -> None:
-    """k, v: bf16 [T, Hkv, dh]; slot_mapping int64 [T]; caches uint8 [nb, Hkv, bs, dh]."""
+    """k, v: bf16 [T, Hkv, dh]; slot_mapping int64 [T]; caches: K uint8
+    [nb, Hkv, dh/16, bs, 16], V uint8 [nb, Hkv, dh, bs]."""
     T, Hkv, dh = k.shape
-    nb, _, bs, _ = k_cache.shape
+    nb, _, bs, _ = _cache_dims(k_cache, v_cache)
     _check("kvq_cache_write",
            lib().kvq_cache_write(_ptr(k), _ptr(v), T, Hkv, dh, _ptr(slot_mapping), _ptr(k_cache),
                                  _ptr(v_cache), nb, bs, _ptr(k_scale), _ptr(v_scale), _fmt(fmt),
@@ -144,7 +158,7 @@ def kvq_decode_attn(out, q, k_cache, v_cache, block_tables, context_lens, max_co
     """out: fp32 or bf16 [B, Hq, dh]; q bf16 [B, Hq, dh]; block_tables int32 [B, max_blocks]."""
     import torch
     B, Hq, dh = q.shape
-    nb, Hkv, bs, _ = k_cache.shape
+    nb, Hkv, bs, _ = _cache_dims(k_cache, v_cache)
     ws_bytes = kvq_decode_workspace_size(B, Hq, dh, max_context_len, bs)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
@@ -164,7 +178,7 @@ def kvq_prefill_attn(out, q, cu_seqlens_q, max_q_len, q_scale, q_gran, k_cache, 
     """out: fp32 or bf16 [total_q, Hq, dh]; q bf16 [total_q, Hq, dh]; cu_seqlens_q int32 [B+1]."""
     import torch
     _, Hq, dh = q.shape
-    nb, Hkv, bs, _ = k_cache.shape
+    nb, Hkv, bs, _ = _cache_dims(k_cache, v_cache)
     B = cu_seqlens_q.shape[0] - 1
     out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
     _check("kvq_prefill_attn",

@@ -4,7 +4,9 @@
 // Kq = Q(K / sK), stored with sK) in its FP8 form (section 10.4.5,
 // cast_fp8(K / sK)), placed through a slot mapping into the paged layout
 // (slot -> block slot/bs, offset slot%bs):
-//   K tiles are token-major  [num_blocks][Hkv][bs][dh]
+//   K tiles [num_blocks][Hkv][dh/16][bs][16]: 16-channel chunks, token-major
+//     inside a chunk (what the attention kernels' K loads want: 16 tokens x
+//     4 chunks = 1 KB of contiguous bytes per 64-lane load)
 //   V tiles are channel-major [num_blocks][Hkv][dh][bs]
 // Both attention kernels contract V over tokens, so a channel-major V tile
 // hands every matrix-core operand a contiguous run of tokens; the transpose
@@ -16,14 +18,17 @@
 //      slots ("quad"), with the run's length (1..4).
 //   2. Every thread quantizes 4 tokens x 4 channels of K and V (bf16 loads of
 //      consecutive threads are one row; they are issued before step 1's
-//      barrier, since they do not depend on the slots).  K codes go straight out, one dword
-//      per token; the 4x4 V code block is transposed with v_perm_b32 and
-//      parked in an LDS tile [dh][64 tokens].
-//   3. For each run and channel one thread reads the run's codes from the LDS
-//      tile and stores them: one dword when the run fills its quad (the
-//      normal case for tokens of a sequence written in order, whatever its
-//      starting offset), single bytes otherwise (a decode step's one new
-//      token per sequence, the ends of a chunk or of a sequence).
+//      barrier, since they do not depend on the slots).  K codes are parked
+//      in an LDS tile [64 tokens][dh]; the 4x4 V code block is transposed
+//      with v_perm_b32 and parked in an LDS tile [dh][64 tokens].
+//   3. K: for each valid token and 16-channel chunk one thread stores the 16
+//      code bytes (consecutive threads take consecutive tokens, so a block's
+//      chunk row of 16 tokens goes out as 256 contiguous bytes).  V: for each
+//      run and channel one thread stores the run's codes: one dword when the
+//      run fills its quad (the normal case for tokens of a sequence written
+//      in order, whatever its starting offset), single bytes otherwise (a
+//      decode step's one new token per sequence, the ends of a chunk or of a
+//      sequence).
 // Tokens with a negative slot, or a slot outside the pool, are skipped.
 #include "codec.hpp"
 #include "launch.hpp"
@@ -50,6 +55,8 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   __shared__ uint32_t s_run[kChunk];  // token index | run length << 8, compacted
   __shared__ int s_nrun;
   __shared__ uint32_t s_vt[DH * kRowDw];
+  constexpr int kKRow = DH / 4 + 4;  // LDS K-tile row (dwords): DH codes + 16 B pad
+  __shared__ __attribute__((aligned(16))) uint32_t s_kt[kChunk * kKRow];
 
   const int h = (int)(blockIdx.x % (uint32_t)Hkv);
   const int64_t t0 = (int64_t)(blockIdx.x / (uint32_t)Hkv) * kChunk;
@@ -106,11 +113,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       cv[j] = quant4<FMT>(wv[jb][j], sv, rv);
-      const int64_t slot = s_slot[4 * tq + j];
-      if (slot < 0) continue;
-      const int64_t blk = slot >> 4, off = slot & (kBs - 1);
-      const size_t kt = ((size_t)(blk * Hkv + h) * kBs + off) * DH + cq * 4;
-      *reinterpret_cast<uint32_t*>(kc + kt) = quant4<FMT>(wk[jb][j], sk, rk);
+      s_kt[(4 * tq + j) * kKRow + cq] = quant4<FMT>(wk[jb][j], sk, rk);
     }
     // rows cv[j] = token j, bytes = channels 4cq..4cq+3 -> one dword per channel
     const uint32_t t0l = __builtin_amdgcn_perm(cv[1], cv[0], 0x05010400u);  // a0 b0 a1 b1
@@ -124,6 +127,16 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     row[3 * kRowDw] = __builtin_amdgcn_perm(t3l, t1l, 0x07060302u);
   }
   __syncthreads();
+
+  // K: 16 code bytes per (token, chunk); tokens fastest across threads
+  for (int job = tid; job < kChunk * (DH / 16); job += 256) {
+    const int t = job % kChunk, q = job / kChunk;
+    const int64_t s = s_slot[t];
+    if (s < 0) continue;
+    const uint4 w = *reinterpret_cast<const uint4*>(s_kt + t * kKRow + 4 * q);
+    *reinterpret_cast<uint4*>(kc + (size_t)((s >> 4) * Hkv + h) * kBs * DH + q * (kBs * 16) +
+                              (s & (kBs - 1)) * 16) = w;
+  }
 
   const int nrun = s_nrun;
   for (int job = tid; job < nrun * DH; job += 256) {

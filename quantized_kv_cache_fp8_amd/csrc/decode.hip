@@ -53,6 +53,10 @@ namespace kvq {
 #ifndef KVQ_DECODE_NT_LOADS
 #define KVQ_DECODE_NT_LOADS 1
 #endif
+// Whether each wave keeps two block pairs in flight (two register sets).
+#ifndef KVQ_DECODE_DOUBLE_BUFFER
+#define KVQ_DECODE_DOUBLE_BUFFER 0
+#endif
 #ifndef KVQ_DECODE_WAVES_PER_EU
 #define KVQ_DECODE_WAVES_PER_EU 4
 #endif
@@ -210,30 +214,34 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   }
 
   // A block pair (2 blocks of 16 tokens).  K: lane holds the 32 code bytes of
-  // token c16 in channel slots 16 g4 + [0,16) and DH/2 + 16 g4 + [0,16).
+  // token c16 in channel slots 16 g4 + [0,16) and DH/2 + 16 g4 + [0,16) (K
+  // tiles are [DH/16 chunks][16 tokens][16 channels]).
   // V: lane holds tokens tk .. tk + 7 of block eb for channel 16 n + c16.
   // Blocks past the split's end re-read its last block; their scores are
   // masked and their values zeroed, so nothing outside the table is read.
-  i32x8 kr[2];
-  uint2 vr[NV];
+  i32x8 kr[2], kr2[2];
+  uint2 vr[NV], vr2[NV];
   auto block_src = [&](int bi) {
     bi = bi < nblk ? bi : nblk - 1;
     return (size_t)clamp_block(btab[bi], num_blocks) * Hkv + h;
   };
-  auto load_k = [&](int p) {
+  auto load_k = [&](int p, i32x8 (&kr)[2]) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       kr[e] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
       if (chan_live) {
-        const uint8_t* src = kc + block_src(2 * p + e) * tile + c16 * DH + 16 * g4;
+        // chunks g4 and DH/32 + g4 (channels 16 g4 + [0,16) and DH/2 + 16 g4 + [0,16))
+        // of token c16: each of the two loads covers 16 tokens x 4 chunks, i.e.
+        // DH/32 KB of contiguous tile
+        const uint8_t* src = kc + block_src(2 * p + e) * tile + g4 * 256 + c16 * 16;
         const uint4 a0 = load16(src);
-        const uint4 a1 = load16(src + HALF);
+        const uint4 a1 = load16(src + HALF * 16);
         kr[e] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                       (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
       }
     }
   };
-  auto load_v = [&](int p) {
+  auto load_v = [&](int p, uint2 (&vr)[NV]) {
     const uint8_t* src = vc + block_src(2 * p + eb) * tile + c16 * kBlockSize + tk;
 #pragma unroll
     for (int n = 0; n < NV; ++n) vr[n] = load8(src + 16 * n * kBlockSize);
@@ -241,8 +249,12 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 
   int p = wave;
   if (p < npair) {
-    load_k(p);
-    load_v(p);
+    load_k(p, kr);
+    load_v(p, vr);
+  }
+  if (KVQ_DECODE_DOUBLE_BUFFER && p + 4 < npair) {
+    load_k(p + 4, kr2);
+    load_v(p + 4, vr2);
   }
 
   // A operand of S = Q K^T (bf16, exact): query head_a in the channel slots
@@ -269,8 +281,8 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 #pragma unroll
   for (int n = 0; n < NV; ++n) O[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-#pragma unroll 1
-  for (; p < npair; p += 4) {
+  // one block pair: S, online softmax, P V (kr / vr hold the pair's codes)
+  auto pair_step = [&](int p, i32x8 (&kr)[2], uint2 (&vr)[NV]) {
     // ---- S for both blocks on bf16 matrix cores (codes -> bf16 is exact):
     //      lane holds head head_l[i] for token c16 of block e
     float z[2][HPL];
@@ -288,7 +300,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     }
     // this pair's K registers are free: the next pair's keys load during the
     // softmax and P V below
-    if (p + 4 < npair) load_k(p + 4);
+    if (!KVQ_DECODE_DOUBLE_BUFFER && p + 4 < npair) load_k(p + 4, kr);
     // ---- online softmax per head.  Each lane tests its own scores against
     //      the running max; only when one exceeds it by more than tau does the
     //      wave take the (rare, wave-uniform) branch that finds the exact
@@ -341,8 +353,30 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     for (int n = 0; n < NV; ++n)
       O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, codes_to_f16x8<FMT>(vr[n].x, vr[n].y),
                                                     O[n], 0, 0, 0);
-    if (p + 4 < npair) load_v(p + 4);  // V registers are free now
+    if (!KVQ_DECODE_DOUBLE_BUFFER && p + 4 < npair) load_v(p + 4, vr);  // V registers are free now
+    };
+
+#if KVQ_DECODE_DOUBLE_BUFFER
+  // two register sets: while one pair is computed the pair after it lands
+#pragma unroll 1
+  for (; p < npair; p += 8) {
+    pair_step(p, kr, vr);
+    if (p + 8 < npair) {
+      load_k(p + 8, kr);
+      load_v(p + 8, vr);
+    }
+    if (p + 4 < npair) {
+      pair_step(p + 4, kr2, vr2);
+      if (p + 12 < npair) {
+        load_k(p + 12, kr2);
+        load_v(p + 12, vr2);
+      }
+    }
   }
+#else
+#pragma unroll 1
+  for (; p < npair; p += 4) pair_step(p, kr, vr);
+#endif
 
   // ---- merge the 4 waves through LDS and write the split's partial
 #pragma unroll

@@ -169,14 +169,15 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
     };
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
+      // piece u = (block beta, 16-channel chunk, token): consecutive threads
+      // read consecutive 16-byte runs of a K tile ([DH/16][16 tokens][16])
       const int u = threadIdx.x + i * NT;
-      const int key = u / (DH / 16), piece = u % (DH / 16);
+      const int beta = u / DH, piece = (u / 16) % (DH / 16), t = u % 16;
       size_t off;
       bool ok;
-      pick(key >> 4, off, ok);
+      pick(beta, off, ok);
       kreg[i] = make_uint4(0, 0, 0, 0);
-      if (ok)
-        kreg[i] = *reinterpret_cast<const uint4*>(kc + off + (key & 15) * DH + piece * 16);
+      if (ok) kreg[i] = *reinterpret_cast<const uint4*>(kc + off + piece * 256 + t * 16);
     }
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
@@ -209,7 +210,7 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int u = threadIdx.x + i * NT;
-      const int key = u / (DH / 16), piece = u % (DH / 16);
+      const int key = 16 * (u / DH) + u % 16, piece = (u / 16) % (DH / 16);
       *reinterpret_cast<uint4*>(k_lds + key * KROW + piece * 16) = kreg[i];
     }
 #pragma unroll

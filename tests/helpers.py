@@ -59,8 +59,9 @@ def row_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
 
 
 def k_shape(wl):
-    """K cache: token-major tiles [num_blocks][Hkv][bs][dh]."""
-    return (wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh)
+    """K cache: [num_blocks][Hkv][dh/16][bs][16] (16-channel chunks, token-major
+    inside a chunk)."""
+    return oracle.k_cache_shape(wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh)
 
 
 def v_shape(wl):

@@ -20,7 +20,8 @@ SCALES = ([1.0, 0.5, 2.0 ** -9, 1.0 / 448, 10.0 / 448, 3.0, 0.0123, 123.456, 1e-
 def gpu_write(k_bits, v_bits, slots, nb, Hkv, dh, ks, vs, fmt, gran):
     import torch
     import quantized_kv_cache_fp8_amd as K
-    kc = torch.full((nb, Hkv, 16, dh), SENTINEL, dtype=torch.uint8, device="cuda:0")
+    kc = torch.full(oracle.k_cache_shape(nb, Hkv, 16, dh), SENTINEL, dtype=torch.uint8,
+                    device="cuda:0")
     vc = torch.full((nb, Hkv, dh, 16), SENTINEL, dtype=torch.uint8, device="cuda:0")
     K.kvq_cache_write(to_dev(k_bits), to_dev(v_bits), to_dev(slots), kc, vc,
                       to_dev(np.asarray(ks, np.float32)), to_dev(np.asarray(vs, np.float32)),
@@ -30,7 +31,7 @@ def gpu_write(k_bits, v_bits, slots, nb, Hkv, dh, ks, vs, fmt, gran):
 
 
 def oracle_write(k_bits, v_bits, slots, nb, Hkv, dh, ks, vs, fmt, gran):
-    kc = np.full((nb, Hkv, 16, dh), SENTINEL, np.uint8)
+    kc = np.full(oracle.k_cache_shape(nb, Hkv, 16, dh), SENTINEL, np.uint8)
     vc = np.full((nb, Hkv, dh, 16), SENTINEL, np.uint8)
     oracle.cache_write(k_bits, v_bits, slots, kc, vc, np.asarray(ks, np.float32),
                        np.asarray(vs, np.float32), fmt, gran)

@@ -19,7 +19,7 @@ def build_cache(paging, kv, Hkv, dh, fmt, gran, g):
     n = Hkv if gran == oracle.GRAN_HEAD else 1
     ks = (g.uniform(0.005, 0.05, n)).astype(np.float32)
     vs = (g.uniform(0.005, 0.05, n)).astype(np.float32)
-    kc = np.zeros((paging.num_blocks, Hkv, paging.bs, dh), np.uint8)
+    kc = np.zeros(oracle.k_cache_shape(paging.num_blocks, Hkv, paging.bs, dh), np.uint8)
     vc = np.zeros((paging.num_blocks, Hkv, dh, paging.bs), np.uint8)
     oracle.cache_write(kv.k, kv.v, kv.slot_mapping, kc, vc, ks, vs, fmt, gran)
     return kc, vc, ks, vs
@@ -27,11 +27,12 @@ def build_cache(paging, kv, Hkv, dh, fmt, gran, g):
 
 def gather(cache, paging, b, n, fmt, scales, gran, kind):
     """Dequantized [Hkv, n, dh] history of sequence b, read through the block
-    table; K tiles are [bs][dh] (token-major), V tiles [dh][bs] (channel-major)."""
+    table; K tiles are [dh/16][bs][16] (viewed token-major), V tiles [dh][bs]
+    (channel-major)."""
     pos = np.arange(n)
     blk = paging.block_tables[b, pos // paging.bs]
     if kind == "k":
-        codes = cache[blk, :, pos % paging.bs, :]  # [n, Hkv, dh]
+        codes = oracle.k_token_view(cache)[blk, :, pos % paging.bs, :]  # [n, Hkv, dh]
     else:
         codes = cache[blk, :, :, pos % paging.bs]  # [n, Hkv, dh]
     Hkv = cache.shape[1]
@@ -117,7 +118,7 @@ def test_decode_invariant_under_key_order_and_block_placement():
     """Attention without a mask is a function of the set of (k, v) pairs: moving
     tokens to other positions and other physical blocks leaves the output alone."""
     g = W.rng(23)
-    Hq, Hkv, dh = 6, 3, 24
+    Hq, Hkv, dh = 6, 3, 48
     fmt, gran = oracle.FMT_E5M2, oracle.GRAN_HEAD
     paging = W.make_paging(g, [70], 16)
     kv = W.make_kv(g, paging, Hkv, dh, head_range=(0.5, 20.0))
@@ -129,7 +130,7 @@ def test_decode_invariant_under_key_order_and_block_placement():
     paging2 = W.make_paging(W.rng(99), [70], 16)
     kv2 = W.KVBatch(kv.k[perm].copy(), kv.v[perm].copy(), paging2.slots(0, np.arange(70)),
                     kv.seq_offsets)
-    kc2 = np.zeros((paging2.num_blocks, Hkv, 16, dh), np.uint8)
+    kc2 = np.zeros(oracle.k_cache_shape(paging2.num_blocks, Hkv, 16, dh), np.uint8)
     vc2 = np.zeros((paging2.num_blocks, Hkv, dh, 16), np.uint8)
     oracle.cache_write(kv2.k, kv2.v, kv2.slot_mapping, kc2, vc2, ks, vs, fmt, gran)
     out2 = oracle.decode_attn(q, kc2, vc2, paging2.block_tables, paging2.context_lens, ks, vs,
@@ -140,9 +141,9 @@ def test_decode_invariant_under_key_order_and_block_placement():
 def test_decode_zero_context_gives_zero_row():
     g = W.rng(24)
     paging = W.make_paging(g, [0, 5], 16)
-    kv = W.make_kv(g, paging, 1, 8)
-    kc, vc, ks, vs = build_cache(paging, kv, 1, 8, 0, 0, g)
-    out = oracle.decode_attn(W.normal_bf16(g, (2, 2, 8)), kc, vc, paging.block_tables,
+    kv = W.make_kv(g, paging, 1, 16)
+    kc, vc, ks, vs = build_cache(paging, kv, 1, 16, 0, 0, g)
+    out = oracle.decode_attn(W.normal_bf16(g, (2, 2, 16)), kc, vc, paging.block_tables,
                              paging.context_lens, ks, vs, 0, 0)
     assert np.all(out[0] == 0) and np.all(np.isfinite(out[1])) and np.any(out[1] != 0)
 

@@ -168,9 +168,18 @@ def test_cache_write_places_every_code(fmt, gran):
     vs = np.array([0.04, 0.05, 0.06], np.float32)[: (Hkv if gran else 1)]
     sm = kv.slot_mapping.copy()
     sm[5] = -1  # a padding token: skipped
-    kc = np.full((paging.num_blocks, Hkv, bs, dh), 0xA5, np.uint8)
+    kc5 = np.full(oracle.k_cache_shape(paging.num_blocks, Hkv, bs, dh), 0xA5, np.uint8)
     vc = np.full((paging.num_blocks, Hkv, dh, bs), 0xA5, np.uint8)  # channel-major V tiles
-    oracle.cache_write(kv.k, kv.v, sm, kc, vc, ks, vs, fmt, gran)
+    oracle.cache_write(kv.k, kv.v, sm, kc5, vc, ks, vs, fmt, gran)
+    # K tiles hold 16-channel chunks, token-major inside a chunk: byte
+    # (((blk * Hkv + h) * dh/16 + d/16) * bs + off) * 16 + d % 16
+    flat = kc5.reshape(-1)
+    idx = ((((np.arange(paging.num_blocks)[:, None, None, None] * Hkv
+              + np.arange(Hkv)[None, :, None, None]) * (dh // 16)
+             + np.arange(dh)[None, None, None, :] // 16) * bs
+            + np.arange(bs)[None, None, :, None]) * 16 + np.arange(dh)[None, None, None, :] % 16)
+    kc = flat[idx]  # [num_blocks][Hkv][bs][dh], gathered by the layout formula
+    assert np.array_equal(kc, oracle.k_token_view(kc5))
     touched = np.zeros(kc.shape[:3], bool)
     for t in range(len(sm)):
         if sm[t] < 0:
