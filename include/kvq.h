@@ -28,6 +28,9 @@
  * - Validation happens on the host before any HIP call, so a call with
  *   invalid arguments returns an error and touches no device memory.
  * - bf16 tensors are passed as void* holding IEEE bfloat16 bit patterns.
+ * - Alignment: bf16 inputs, caches, attention outputs and the decode
+ *   workspace must be 16-byte aligned, slot mappings 8-byte aligned (every
+ *   torch allocation is); otherwise the call returns KVQ_ERR_UNSUPPORTED.
  * - Cache layout (this library's design; the pages fix only that FP8 caches
  *   are raw bytes): k_cache is uint8 [num_blocks][Hkv][dh/16][bs][16] (each
  *   tile is cut into 16-channel chunks, token-major inside a chunk: channel d

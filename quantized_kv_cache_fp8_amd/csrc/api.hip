@@ -117,7 +117,7 @@ kvq_status kvq_cache_write(const void* k_bf16, const void* v_bf16, int64_t T, in
   if (!k_cache || !v_cache || !k_scale || !v_scale) return KVQ_ERR_NULL;
   if (T == 0) return KVQ_OK;
   if (!k_bf16 || !v_bf16 || !slot_mapping) return KVQ_ERR_NULL;
-  if (!aligned(k_bf16, 16) || !aligned(v_bf16, 16) || !aligned(k_cache, 8) ||
+  if (!aligned(k_bf16, 16) || !aligned(v_bf16, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 8) || !aligned(slot_mapping, 8))
     return KVQ_ERR_UNSUPPORTED;
   return map_err(launch_cache_write((const uint16_t*)k_bf16, (const uint16_t*)v_bf16, T, Hkv, dh,

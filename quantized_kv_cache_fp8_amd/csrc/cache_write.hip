@@ -30,6 +30,7 @@
 //      decode step's one new token per sequence, the ends of a chunk or of a
 //      sequence).
 // Tokens with a negative slot, or a slot outside the pool, are skipped.
+// Writes of at most 512 tokens (a decode step) take a one-pass kernel instead.
 #include "codec.hpp"
 #include "launch.hpp"
 
@@ -156,10 +157,59 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   }
 }
 
+// Short writes (a decode step's new tokens, one per sequence, each in its own
+// block): one thread per (token, head, 16-channel chunk) loads its slot and
+// its 16 K and V values together, quantizes them and stores 16 K bytes and 16
+// single V bytes -- one memory round trip, no LDS, no barrier.
+template <int FMT, int DH>
+__global__ __launch_bounds__(256) void cache_write_short_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint32_t units, int Hkv,
+    const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+    int64_t num_slots, const float* __restrict__ ks, const float* __restrict__ vs, int per_head) {
+  constexpr int kNc = DH / 16;  // chunks per token row
+  const uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= units) return;
+  const uint32_t q = u % kNc, th = u / kNc;  // th = t * Hkv + h
+  const uint32_t t = th / (uint32_t)Hkv;
+  const int h = (int)(th - t * (uint32_t)Hkv);
+  const size_t src = (size_t)th * DH + q * 16;
+  const uint4 k0 = *reinterpret_cast<const uint4*>(k + src);
+  const uint4 k1 = *reinterpret_cast<const uint4*>(k + src + 8);
+  const uint4 v0 = *reinterpret_cast<const uint4*>(v + src);
+  const uint4 v1 = *reinterpret_cast<const uint4*>(v + src + 8);
+  const int64_t s = slot_mapping[t];
+  if (s < 0 || s >= num_slots) return;  // padding or out of the pool: skipped
+  const float sk = ks[per_head ? h : 0], sv = vs[per_head ? h : 0];
+  const float rk = recip_rn(sk), rv = recip_rn(sv);
+  const uint4 kq = make_uint4(quant4<FMT>(make_uint2(k0.x, k0.y), sk, rk),
+                              quant4<FMT>(make_uint2(k0.z, k0.w), sk, rk),
+                              quant4<FMT>(make_uint2(k1.x, k1.y), sk, rk),
+                              quant4<FMT>(make_uint2(k1.z, k1.w), sk, rk));
+  const uint32_t vq[4] = {quant4<FMT>(make_uint2(v0.x, v0.y), sv, rv),
+                          quant4<FMT>(make_uint2(v0.z, v0.w), sv, rv),
+                          quant4<FMT>(make_uint2(v1.x, v1.y), sv, rv),
+                          quant4<FMT>(make_uint2(v1.z, v1.w), sv, rv)};
+  const size_t tile = (size_t)((s >> 4) * Hkv + h) * kBs * DH;
+  const int off = (int)(s & (kBs - 1));
+  *reinterpret_cast<uint4*>(kc + tile + q * (kBs * 16) + off * 16) = kq;
+  uint8_t* vd = vc + tile + (size_t)q * 16 * kBs + off;  // channel 16 q, token off
+#pragma unroll
+  for (int c = 0; c < 16; ++c) vd[c * kBs] = (uint8_t)(vq[c >> 2] >> (8 * (c & 3)));
+}
+
+// Writes of at most this many tokens take the one-pass kernel above.
+constexpr int64_t kShortWrite = 512;
+
 template <int FMT, int DH>
 void launch_write(int64_t T, int Hkv, const uint16_t* k, const uint16_t* v, const int64_t* slot,
                   uint8_t* kc, uint8_t* vc, int64_t num_slots, const float* ks, const float* vs,
                   int per_head, hipStream_t s) {
+  if (T <= kShortWrite) {
+    const uint32_t units = (uint32_t)(T * Hkv * (DH / 16));
+    cache_write_short_kernel<FMT, DH><<<(units + 255) / 256, 256, 0, s>>>(
+        k, v, units, Hkv, slot, kc, vc, num_slots, ks, vs, per_head);
+    return;
+  }
   const uint32_t grid = (uint32_t)(((T + kChunk - 1) / kChunk) * Hkv);
   cache_write_kernel<FMT, DH><<<grid, 256, 0, s>>>(k, v, T, Hkv, slot, kc, vc, num_slots, ks, vs,
                                                     per_head);

@@ -89,7 +89,7 @@ def test_write_validation():
     assert st(kc=None) == -1 and st(slots=None) == -1 and st(ks=None) == -1
     assert st(T=-1) == -2 and st(nb=0) == -2 and st(Hkv=0) == -2
     assert st(dh=80) == -3 and st(bs=8) == -3 and st(fmt=7) == -3
-    assert st(k=FAKE + 2) == -3  # misaligned
+    assert st(k=FAKE + 2) == -3 and st(kc=FAKE + 8) == -3  # misaligned
     assert st(T=0) == 0  # empty batch: nothing to launch
 
 

@@ -17,9 +17,20 @@ SCALES = ([1.0, 0.5, 2.0 ** -9, 1.0 / 448, 10.0 / 448, 3.0, 0.0123, 123.456, 1e-
           + list(np.exp(W.rng(77).uniform(np.log(1e-6), np.log(1e6), 48)).astype(np.float32)))
 
 
-def gpu_write(k_bits, v_bits, slots, nb, Hkv, dh, ks, vs, fmt, gran):
+# Writes of up to 512 tokens take the one-pass kernel, longer ones the
+# LDS-staged kernel; "long" pads a short write with skipped tokens (slot -1) so
+# the same cases also run through the second kernel.
+SHORT_WRITE = 512
+
+
+def gpu_write(k_bits, v_bits, slots, nb, Hkv, dh, ks, vs, fmt, gran, path="short"):
     import torch
     import quantized_kv_cache_fp8_amd as K
+    if path == "long" and k_bits.shape[0] <= SHORT_WRITE:
+        pad = SHORT_WRITE + 1 - k_bits.shape[0]
+        z = np.zeros((pad, Hkv, dh), np.uint16)
+        k_bits, v_bits = np.concatenate([k_bits, z]), np.concatenate([v_bits, z])
+        slots = np.concatenate([slots, np.full(pad, -1, np.int64)])
     kc = torch.full(oracle.k_cache_shape(nb, Hkv, 16, dh), SENTINEL, dtype=torch.uint8,
                     device="cuda:0")
     vc = torch.full((nb, Hkv, dh, 16), SENTINEL, dtype=torch.uint8, device="cuda:0")
@@ -39,7 +50,8 @@ def oracle_write(k_bits, v_bits, slots, nb, Hkv, dh, ks, vs, fmt, gran):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_write_every_bf16_input_for_every_scale(fmt):
+@pytest.mark.parametrize("path", ["short", "long"])
+def test_write_every_bf16_input_for_every_scale(fmt, path):
     """All 65536 bf16 patterns (as K, and reversed as V) for each scale: the
     cache bytes equal the oracle's, i.e. fp8(fl32(x / s)) exactly."""
     k = ALL_BF16.reshape(512, 1, 128)
@@ -47,14 +59,15 @@ def test_write_every_bf16_input_for_every_scale(fmt):
     slots = np.arange(512, dtype=np.int64)
     for s in SCALES:
         s = np.float32(s)
-        gk, gv = gpu_write(k, v, slots, 32, 1, 128, [s], [s], fmt, oracle.GRAN_TENSOR)
+        gk, gv = gpu_write(k, v, slots, 32, 1, 128, [s], [s], fmt, oracle.GRAN_TENSOR, path)
         rk, rv = oracle_write(k, v, slots, 32, 1, 128, [s], [s], fmt, oracle.GRAN_TENSOR)
         assert same_codes(fmt, gk, rk), f"K differs at scale {s!r}"
         assert same_codes(fmt, gv, rv), f"V differs at scale {s!r}"
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_write_per_head_scales(fmt):
+@pytest.mark.parametrize("path", ["short", "long"])
+def test_write_per_head_scales(fmt, path):
     g = W.rng(5)
     Hkv, dh = 4, 64
     k = g.permutation(ALL_BF16).reshape(256, Hkv, dh)
@@ -62,12 +75,13 @@ def test_write_per_head_scales(fmt):
     ks = np.array([0.25, 1.0 / 448, 7.0, 3.1e-3], np.float32)
     vs = np.array([1.5e-2, 2.0, 1.0, 9.9e3], np.float32)
     slots = g.permutation(256 + 48)[:256].astype(np.int64)  # scattered over a larger pool
-    gk, gv = gpu_write(k, v, slots, 19, Hkv, dh, ks, vs, fmt, oracle.GRAN_HEAD)
+    gk, gv = gpu_write(k, v, slots, 19, Hkv, dh, ks, vs, fmt, oracle.GRAN_HEAD, path)
     rk, rv = oracle_write(k, v, slots, 19, Hkv, dh, ks, vs, fmt, oracle.GRAN_HEAD)
     assert same_codes(fmt, gk, rk) and same_codes(fmt, gv, rv)
 
 
-def test_write_skips_padding_and_out_of_range_slots():
+@pytest.mark.parametrize("path", ["short", "long"])
+def test_write_skips_padding_and_out_of_range_slots(path):
     g = W.rng(6)
     Hkv, dh = 2, 128
     k = W.normal_bf16(g, (40, Hkv, dh))
@@ -75,14 +89,15 @@ def test_write_skips_padding_and_out_of_range_slots():
     slots = g.permutation(64)[:40].astype(np.int64)
     slots[[3, 17]] = -1  # padding
     slots[[5, 30]] = [64, 1 << 40]  # beyond the pool of 4 blocks: skipped, never written
-    gk, gv = gpu_write(k, v, slots, 4, Hkv, dh, [0.01], [0.02], 0, 0)
+    gk, gv = gpu_write(k, v, slots, 4, Hkv, dh, [0.01], [0.02], 0, 0, path)
     rk, rv = oracle_write(k, v, slots, 4, Hkv, dh, [0.01], [0.02], 0, 0)
     assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
     assert (gk == SENTINEL).sum() == (rk == SENTINEL).sum() > 0
 
 
 @pytest.mark.parametrize("start", [0, 2, 5])
-def test_write_partial_and_misaligned_runs(start):
+@pytest.mark.parametrize("path", ["short", "long"])
+def test_write_partial_and_misaligned_runs(start, path):
     """Consecutive slots that start off a 4-token boundary, a ragged token count
     and a gap in the middle: every mix of the dword and byte store paths."""
     g = W.rng(9 + start)
@@ -92,7 +107,7 @@ def test_write_partial_and_misaligned_runs(start):
     slots = np.arange(start, start + T, dtype=np.int64)
     slots[20:] += 7  # a gap: later tokens land in other blocks at other offsets
     gk, gv = gpu_write(k, v, slots, 5, Hkv, dh, [0.02, 0.03, 0.05], [0.01, 0.04, 0.2], 1,
-                       oracle.GRAN_HEAD)
+                       oracle.GRAN_HEAD, path)
     rk, rv = oracle_write(k, v, slots, 5, Hkv, dh, [0.02, 0.03, 0.05], [0.01, 0.04, 0.2], 1,
                           oracle.GRAN_HEAD)
     assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
