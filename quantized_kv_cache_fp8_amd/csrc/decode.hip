@@ -57,6 +57,10 @@ namespace kvq {
 #ifndef KVQ_DECODE_DOUBLE_BUFFER
 #define KVQ_DECODE_DOUBLE_BUFFER 0
 #endif
+// Waves per SIMD of the kernel for groups of at most 4 heads.
+#ifndef KVQ_DECODE_G4_WAVES_PER_EU
+#define KVQ_DECODE_G4_WAVES_PER_EU 5
+#endif
 #ifndef KVQ_DECODE_WAVES_PER_EU
 #define KVQ_DECODE_WAVES_PER_EU 4
 #endif
@@ -418,6 +422,237 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Groups of at most 4 query heads (G <= 4: the Llama-3 shape has G = 4).
+// Q K^T and the softmax are as above (one distinct head per lane, rows
+// replicated).  P V runs on v_mfma_f32_4x4x4_16b_f16 instead: 16 independent
+// 4x4x4 products per instruction, where D[r][c] = sum_k A[r][k] B[k][c] with
+// A row r in lane 4 blk + r, B and D column c in lane 4 blk + c and D's rows in
+// that lane's 4 registers.  So lane l owns channel l (and 64 + l) of the
+// output, for all 4 heads at once (8 accumulator registers, not 32):
+//   A = P[head l % 4][4 tokens], B = V[4 tokens][channel l] (4 code bytes of
+//   the channel's row in the channel-major tile),
+// and each lane loads its channel's 16 token bytes per block: one 64-lane load
+// is 1 KB of contiguous tile.
+template <int FMT, int DH, int NPW>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(KVQ_DECODE_G4_WAVES_PER_EU, KVQ_DECODE_G4_WAVES_PER_EU))) void
+decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
+                       const uint8_t* __restrict__ vc, int64_t num_blocks,
+                       const int32_t* __restrict__ bt, int max_blocks,
+                       const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int NH,
+                       int rph_shift, int max_ctx, const float* __restrict__ ks, int per_head,
+                       float sm_scale, int nsplit, float* __restrict__ ws_ml,
+                       float* __restrict__ ws_acc) {
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  constexpr int PB = 8 * NPW;     // blocks per split: 4 waves x NPW pairs x 2
+  constexpr int HALF = DH / 2;
+  constexpr int NC = DH / 64;     // 64-channel halves of the output
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int split = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int gpk = G / NH;
+  const int h = grp / gpk;
+  const int hq0 = h * G + (grp - h * gpk) * NH;
+
+  int ctx = ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > max_ctx ? max_ctx : ctx);
+  const int tok0 = split * PB * kBlockSize;
+  if (tok0 >= ctx) return;  // nothing of this sequence lies in this split
+  const int nblk_left = (ctx - tok0 + kBlockSize - 1) / kBlockSize;
+  const int nblk = nblk_left < PB ? nblk_left : PB;
+  const int npair = (nblk + 1) >> 1;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int rph_mask = (1 << rph_shift) - 1;
+  const int head_a = c16 >> rph_shift;  // Q row of S's A operand
+  const bool head_a_real = head_a < NH;
+  const bool chan_live = chan_group_live<DH>(g4);
+  // this lane's head in the S tile, and whether its lane group publishes P
+  const int head_s = (4 * g4) >> rph_shift;
+  const bool pub = ((4 * g4) & rph_mask) == 0 && head_s < NH;
+  // P V: A row of this lane (head lane % 4), and the lane that holds head r's
+  // running state in the S layout (first lane of its first lane group)
+  const int head_p = lane & 3;
+  _Float16* ptr = reinterpret_cast<_Float16*>(smem) + wave * 16 * 32;  // this wave's P scratch
+  float* wm = reinterpret_cast<float*>(smem + 4 * 16 * 32 * sizeof(_Float16));
+  float* wl = wm + 4 * 16;
+  float* wo = wl + 4 * 16;  // [4][NH][DH]
+  const int32_t* btab = bt + (size_t)b * max_blocks + (size_t)split * PB;
+  const size_t tile = (size_t)kBlockSize * DH;  // bytes per (block, head) tile
+
+  i32x8 kr[2];
+  uint4 vq[2][NC];  // [block of the pair][half]: 16 token codes of channel 64 half + lane
+  auto block_src = [&](int bi) {
+    bi = bi < nblk ? bi : nblk - 1;
+    return (size_t)clamp_block(btab[bi], num_blocks) * Hkv + h;
+  };
+  auto load_k = [&](int p) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      kr[e] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (chan_live) {
+        const uint8_t* src = kc + block_src(2 * p + e) * tile + g4 * 256 + c16 * 16;
+        const uint4 a0 = load16(src);
+        const uint4 a1 = load16(src + HALF * 16);
+        kr[e] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      }
+    }
+  };
+  auto load_v = [&](int p) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint8_t* src = vc + block_src(2 * p + e) * tile + lane * kBlockSize;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) vq[e][c] = load16(src + c * 64 * kBlockSize);
+    }
+  };
+
+  int p = wave;
+  if (p < npair) {
+    load_k(p);
+    load_v(p);
+  }
+  bf16x8 qop[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (head_a_real && chan_live)
+      w = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + hq0 + head_a) * DH + 16 * g4 +
+                                          (j >> 1) * HALF + 8 * (j & 1));
+    qop[j] = __builtin_bit_cast(bf16x8, w);
+  }
+  const float zc = sm_scale * ks[per_head ? h : 0] * kLog2e;
+
+  float m_run = kNegBig, l_part = 0.0f;  // this lane's head (S layout)
+  f32x4 O[NC];                           // O[c][r]: head r, channel 64 c + lane
+#pragma unroll
+  for (int c = 0; c < NC; ++c) O[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll 1
+  for (; p < npair; p += 4) {
+    // ---- S for both blocks (bf16 matrix cores, rows replicated per head)
+    float z[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      f32x4 S = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            qop[j], codes_to_bf16x8<FMT>((uint32_t)kr[e][2 * j], (uint32_t)kr[e][2 * j + 1]), S,
+            0, 0, 0);
+      const bool valid = tok0 + (2 * p + e) * kBlockSize + c16 < ctx;
+      z[e] = valid ? S[0] * zc : -__builtin_inff();
+    }
+    if (p + 4 < npair) load_k(p + 4);  // K registers are free
+    // ---- online softmax (lazy max, wave-uniform rare rescale)
+    const bool need = __builtin_fmaxf(z[0], z[1]) > m_run + kLazyTau;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float mt = max16(__builtin_fmaxf(z[0], z[1]));
+      const bool up = mt > m_run + kLazyTau;
+      const float f = up ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+      m_run = up ? mt : m_run;
+      l_part *= f;
+      // head r's factor sits in lane (4 r) << rph_shift (first lane of its group)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r < NH) {
+          const float fr = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), (4 * r) << rph_shift));
+#pragma unroll
+          for (int c = 0; c < NC; ++c) O[c][r] *= fr;
+        }
+      }
+    }
+    const float p0 = __builtin_amdgcn_exp2f(z[0] - m_run);
+    const float p1 = __builtin_amdgcn_exp2f(z[1] - m_run);
+    l_part += p0 + p1;
+    if (pub) {
+      ptr[head_s * 32 + c16] = (_Float16)p0;
+      ptr[head_s * 32 + 16 + c16] = (_Float16)p1;
+    }
+    // ---- value codes of slots past the context may hold anything (NaN
+    //      included) and their zero weights would not cancel a NaN: zero them
+    if (tok0 + (2 * p + 2) * kBlockSize > ctx) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int left = ctx - (tok0 + (2 * p + e) * kBlockSize);  // tokens inside the context
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int n = left - 4 * w;
+          const uint32_t keep = n >= 4 ? 0xffffffffu : (n <= 0 ? 0u : (1u << (8 * n)) - 1);
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            uint32_t* d = reinterpret_cast<uint32_t*>(&vq[e][c]);
+            d[w] &= keep;
+          }
+        }
+      }
+    }
+    // ---- P V: 8 groups of 4 tokens x NC halves of 64 channels
+    f16x8 pa[4] = {};
+    if (head_p < NH) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pa[i] = *reinterpret_cast<const f16x8*>(ptr + head_p * 32 + 8 * i);
+    }
+#pragma unroll
+    for (int tq = 0; tq < 8; ++tq) {
+      const f16x8 p8 = pa[tq >> 1];
+      const f16x4 a = (tq & 1) ? f16x4{p8[4], p8[5], p8[6], p8[7]}
+                               : f16x4{p8[0], p8[1], p8[2], p8[3]};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint32_t codes = reinterpret_cast<const uint32_t*>(&vq[tq >> 2][c])[tq & 3];
+        const f16x2 lo = dec2_f16<FMT, false>(codes), hi = dec2_f16<FMT, true>(codes);
+        const f16x4 bv = {lo[0], lo[1], hi[0], hi[1]};
+        O[c] = __builtin_amdgcn_mfma_f32_4x4x4f16(a, bv, O[c], 0, 0, 0);
+      }
+    }
+    if (p + 4 < npair) load_v(p + 4);  // V registers are free
+  }
+
+  // ---- merge the 4 waves through LDS and write the split's partial
+  float x = l_part;
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  if (pub && c16 == 0) {
+    wm[wave * 16 + head_s] = m_run;
+    wl[wave * 16 + head_s] = x;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (r < NH)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) wo[(wave * NH + r) * DH + 64 * c + lane] = O[c][r];
+  __syncthreads();
+  for (int o = tid; o < NH * DH; o += 256) {
+    const int row = o / DH, d = o - row * DH;
+    float M = kNegBig;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = __builtin_fmaxf(M, wm[w * 16 + row]);
+    float a = 0.0f, L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = __builtin_amdgcn_exp2f(wm[w * 16 + row] - M);
+      a += f * wo[(w * NH + row) * DH + d];
+      L += f * wl[w * 16 + row];
+    }
+    const size_t ridx = ((size_t)b * Hq + hq0 + row) * nsplit + split;
+    ws_acc[ridx * DH + d] = a;
+    if (d == 0) {
+      ws_ml[ridx * 2 + 0] = M;
+      ws_ml[ridx * 2 + 1] = L;
+    }
+  }
+}
+
 // grid (Hq, B), DH threads: merge the valid splits of one (b, hq) row.
 // Splits are taken 16 at a time, every load of a batch issued together (the
 // (m, l) pairs are the same for all threads of the row: broadcast loads), and
@@ -515,9 +750,13 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
                                                           max_blocks, ctx, Hq, Hkv, NH,       \
                                                           rph_shift, max_ctx, ks, per_head,   \
                                                           sm, plan.nsplit, ml, acc)
+#define KVQ_SPLIT_G4(F, D, N)                                                              \
+  decode_split_g4_kernel<F, D, N><<<grid, 256, lds, s>>>(q, kc, vc, num_blocks, bt, max_blocks,   \
+                                                         ctx, Hq, Hkv, NH, rph_shift, max_ctx,  \
+                                                         ks, per_head, sm, plan.nsplit, ml, acc)
 #define KVQ_SPLIT_HP(F, D, N)                                     \
   do {                                                            \
-    if (nhp_shift <= 2) KVQ_SPLIT(F, D, N, 1);                    \
+    if (nhp_shift <= 2) KVQ_SPLIT_G4(F, D, N);                    \
     else if (nhp_shift == 3) KVQ_SPLIT(F, D, N, 2);               \
     else KVQ_SPLIT(F, D, N, 4);                                   \
   } while (0)
@@ -535,6 +774,7 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
     }
 #undef KVQ_SPLIT_NP
 #undef KVQ_SPLIT_HP
+#undef KVQ_SPLIT_G4
 #undef KVQ_SPLIT
   }
   const dim3 cgrid(Hq, B);
