@@ -31,6 +31,7 @@ LIB = os.path.join(HERE, "liborc.so")
 
 FMT_E4M3 = 0
 FMT_E5M2 = 1
+FMT_INT8 = 2  # symmetric INT8: clip(round(x / s), -127, 127)
 GRAN_TENSOR = 0
 GRAN_HEAD = 1
 

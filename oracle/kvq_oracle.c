@@ -25,7 +25,9 @@
  *   R4 scale = amax/fmax in fp32, 1.0 if amax is 0 or not finite;
  *   R5 query head hq reads KV head hq / (Hq/Hkv);
  *   R7 decode has no mask; prefill is causal at absolute positions;
- *   zero-length context gives an all-zero output row.
+ *   zero-length context gives an all-zero output row;
+ *   symmetric INT8 (format 2): clip(round-half-even(fl32(x / s)), -127, 127),
+ *   NaN -> 0, +-Inf -> +-127, scale = amax / 127.
  */
 #include <math.h>
 #include <stdint.h>
@@ -47,6 +49,7 @@ int orc_num_threads(void) {
 
 #define ORC_FMT_E4M3 0
 #define ORC_FMT_E5M2 1
+#define ORC_FMT_INT8 2 /* symmetric INT8 (textbook 10.4.2 write rule) */
 #define ORC_GRAN_TENSOR 0
 #define ORC_GRAN_HEAD 1
 
@@ -57,13 +60,31 @@ static int fmt_bias(int fmt) { return fmt == ORC_FMT_E4M3 ? 7 : 15; }
 
 double orc_fp8_max(int fmt) {
   /* E4M3fn: exponent field 15, mantissa 110b -> 1.75 * 2^8.
-   * E5M2:   exponent field 30, mantissa 11b  -> 1.75 * 2^15. */
+   * E5M2:   exponent field 30, mantissa 11b  -> 1.75 * 2^15.
+   * INT8:   the clip bound of the symmetric write rule, 127. */
+  if (fmt == ORC_FMT_INT8) return 127.0;
   return fmt == ORC_FMT_E4M3 ? 1.75 * 256.0 : 1.75 * 32768.0;
 }
 
-/* ---- decode: code -> exact value (textbook 10.4.5: cast_float(Kfp8)) ---- */
+/* ---- symmetric INT8 (textbook 10.4.2): Kq = clip(round(K / sK), -127, 127),
+ * read back as K_hat = sK * Kq.  The quotient arrives as fp32 (as for FP8);
+ * round is to nearest with ties to even (R2); a NaN quotient gives code 0 and
+ * +-Inf clip to +-127 (there is no NaN or Inf code).  The code is the two's
+ * complement byte of Kq. ---- */
+
+static uint8_t int8_encode(float x) {
+  if (isnan(x)) return 0;
+  double r = rint((double)x); /* default rounding mode: ties to even */
+  if (r > 127.0) r = 127.0;
+  if (r < -127.0) r = -127.0;
+  return (uint8_t)(int8_t)r;
+}
+
+/* ---- decode: code -> exact value (textbook 10.4.5: cast_float(Kfp8); for
+ * INT8 the signed integer itself) ---- */
 
 double orc_fp8_decode(int fmt, uint8_t code) {
+  if (fmt == ORC_FMT_INT8) return (double)(int8_t)code;
   int s = code >> 7;
   int mb = fmt_mbits(fmt);
   int bias = fmt_bias(fmt);
@@ -88,6 +109,7 @@ double orc_fp8_decode(int fmt, uint8_t code) {
  * then anything above max saturates.  All arithmetic is exact in fp64. */
 
 uint8_t orc_fp8_encode(int fmt, float x) {
+  if (fmt == ORC_FMT_INT8) return int8_encode(x);
   int mb = fmt_mbits(fmt);
   int bias = fmt_bias(fmt);
   int emin = 1 - bias;

@@ -12,7 +12,7 @@ import torch
 import oracle
 import workloads as W
 
-FMTS = [oracle.FMT_E4M3, oracle.FMT_E5M2]
+FMTS = [oracle.FMT_E4M3, oracle.FMT_E5M2, oracle.FMT_INT8]
 
 
 def build_cache(paging, kv, Hkv, dh, fmt, gran, g):
