@@ -199,7 +199,7 @@ def main():
     # ------------------------------------------------------------ other rows (untimed loop)
     if not args.no_rows:
         result["rows"] = measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches,
-                                      ks, vs, wl)
+                                      ks, vs, wl, (q, bt, ctx, max_ctx, ws, out))
 
     # ------------------------------------------------------------ copy probe (untimed)
     if args.copy_probe_mib > 0:
@@ -232,8 +232,39 @@ def time_call(torch, stream, fn, reps):
     return a.elapsed_time(b) / reps
 
 
-def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, vs, wl):
+def decode_row(K, torch, dev, stream, k_all, v_all, slots_all, caches, wl, dec, fmt, reps=50):
+    """Decode attention of the headline layer with the cache in another format
+    (the caches are rewritten); KV bytes per call / mean event time."""
+    q, bt, ctx, max_ctx, ws, out = dec
+    ks = torch.empty(1, device=dev)
+    vs = torch.empty(1, device=dev)
+    amax = torch.empty(1, device=dev)
+    K.kvq_calibrate_scales(k_all, fmt, "tensor", amax, ks)
+    K.kvq_calibrate_scales(v_all, fmt, "tensor", amax, vs)
+    for kc, vc in caches:
+        K.kvq_cache_write(k_all, v_all, slots_all, kc, vc, ks, vs, fmt, "tensor")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i in range(reps + 5):
+        kc, vc = caches[i % len(caches)]
+        if i >= 5:
+            ev[i - 5][0].record(stream)
+        K.kvq_decode_attn(out, q, kc, vc, bt, ctx, max_ctx, ks, vs, fmt, "tensor", workspace=ws)
+        if i >= 5:
+            ev[i - 5][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    kv_bytes = int(wl.paging.context_lens.sum()) * wl.Hkv * wl.dh * 2
+    gbs = kv_bytes / ms / 1e6
+    return {"workload": wl.name + f" ({fmt} cache, per-tensor scale)", "ms": round(ms, 5),
+            "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, vs, wl, dec):
     rows = {}
+    # the same decode with a symmetric INT8 cache (textbook 10.4.2 write rule)
+    rows["decode_int8"] = decode_row(K, torch, dev, stream, k_all, v_all, slots_all, caches, wl,
+                                     dec, "int8")
     T = k_all.shape[0]
     amax = torch.empty(1, device=dev)
     sc = torch.empty(1, device=dev)

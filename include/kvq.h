@@ -67,8 +67,13 @@ typedef enum {
 
 /* Storage format of the cache codes ([G] kv_cache_dtype table: fp8 == fp8_e4m3,
  * fp8_e5m2).  OCP E4M3fn: bias 7, max 448, no Inf, NaN = S.1111.111.
- * OCP E5M2: bias 15, max 57344, IEEE-style Inf/NaN. */
-typedef enum { KVQ_FMT_E4M3 = 0, KVQ_FMT_E5M2 = 1 } kvq_fmt;
+ * OCP E5M2: bias 15, max 57344, IEEE-style Inf/NaN.
+ * INT8: symmetric 8-bit integers, [T] 10.4.2's write rule
+ *   code = clip(round(x / s), -127, 127) (ties to even; a NaN quotient gives 0,
+ *   +-Inf clip to +-127), read back as s * code; "max" (for calibration) is
+ *   127.  Calibration, the codec, quantize-write and decode attention take it;
+ *   the FP8-domain prefill does not (KVQ_ERR_UNSUPPORTED). */
+typedef enum { KVQ_FMT_E4M3 = 0, KVQ_FMT_E5M2 = 1, KVQ_FMT_INT8 = 2 } kvq_fmt;
 
 /* Scale granularity ([T] 10.4.3 table; [G] shapes [1] vs [num_heads] /
  * [num_kv_heads]): one fp32 scale for the whole tensor, or one per head. */

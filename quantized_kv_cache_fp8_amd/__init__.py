@@ -17,13 +17,13 @@ LIB_PATH = os.path.join(HERE, "libkvq.so")
 
 # enums of include/kvq.h
 KVQ_OK = 0
-KVQ_FMT_E4M3, KVQ_FMT_E5M2 = 0, 1
+KVQ_FMT_E4M3, KVQ_FMT_E5M2, KVQ_FMT_INT8 = 0, 1, 2
 KVQ_SCALE_TENSOR, KVQ_SCALE_HEAD = 0, 1
 KVQ_OUT_F32, KVQ_OUT_BF16 = 0, 1
 
 # kv_cache_dtype strings of the vLLM FP8 KV-cache guide ("fp8" is an alias of "fp8_e4m3")
 FMT_NAMES = {"fp8": KVQ_FMT_E4M3, "fp8_e4m3": KVQ_FMT_E4M3, "e4m3": KVQ_FMT_E4M3,
-             "fp8_e5m2": KVQ_FMT_E5M2, "e5m2": KVQ_FMT_E5M2}
+             "fp8_e5m2": KVQ_FMT_E5M2, "e5m2": KVQ_FMT_E5M2, "int8": KVQ_FMT_INT8}
 GRAN_NAMES = {"tensor": KVQ_SCALE_TENSOR, "head": KVQ_SCALE_HEAD,
               "attn_head": KVQ_SCALE_HEAD}
 

@@ -42,7 +42,9 @@ static kvq_status map_err(hipError_t e) {
 }
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
-static bool fmt_ok(int f) { return f == KVQ_FMT_E4M3 || f == KVQ_FMT_E5M2; }
+static bool fmt_ok(int f) {
+  return f == KVQ_FMT_E4M3 || f == KVQ_FMT_E5M2 || f == KVQ_FMT_INT8;
+}
 static bool gran_ok(int g) { return g == KVQ_SCALE_TENSOR || g == KVQ_SCALE_HEAD; }
 static bool out_ok(int o) { return o == KVQ_OUT_F32 || o == KVQ_OUT_BF16; }
 static bool dh_ok(int dh) { return dh == 64 || dh == 128; }
@@ -180,6 +182,7 @@ kvq_status kvq_prefill_attn(void* out, kvq_out out_dtype, const void* q_bf16,
                                     block_tables, max_blocks, context_lens, B, Hq, Hkv, dh, bs,
                                     k_scale, v_scale, fmt, kv_gran);
   if (st != KVQ_OK) return st;
+  if (fmt == KVQ_FMT_INT8) return KVQ_ERR_UNSUPPORTED;  // FP8-domain path: FP8 caches only
   if (!gran_ok(q_gran)) return KVQ_ERR_UNSUPPORTED;
   if (max_q_len < 0) return KVQ_ERR_SHAPE;
   if (!cu_seqlens_q || !q_scale) return KVQ_ERR_NULL;

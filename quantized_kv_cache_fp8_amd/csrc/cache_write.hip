@@ -221,13 +221,11 @@ hipError_t launch_cache_write(const uint16_t* k, const uint16_t* v, int64_t T, i
                               hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int64_t num_slots = num_blocks * kBs;
-  if (fmt == E4M3) {
-    if (dh == 128) launch_write<E4M3, 128>(T, Hkv, k, v, slot, kc, vc, num_slots, ks, vs, per_head, s);
-    else launch_write<E4M3, 64>(T, Hkv, k, v, slot, kc, vc, num_slots, ks, vs, per_head, s);
-  } else {
-    if (dh == 128) launch_write<E5M2, 128>(T, Hkv, k, v, slot, kc, vc, num_slots, ks, vs, per_head, s);
-    else launch_write<E5M2, 64>(T, Hkv, k, v, slot, kc, vc, num_slots, ks, vs, per_head, s);
-  }
+  dispatch_fmt(fmt, [&](auto f) {
+    constexpr int F = decltype(f)::value;
+    if (dh == 128) launch_write<F, 128>(T, Hkv, k, v, slot, kc, vc, num_slots, ks, vs, per_head, s);
+    else launch_write<F, 64>(T, Hkv, k, v, slot, kc, vc, num_slots, ks, vs, per_head, s);
+  });
   return hipGetLastError();
 }
 

@@ -95,10 +95,9 @@ hipError_t launch_calibrate(const uint16_t* x, int64_t T, int H, int dh, int fmt
     int gx = (int)(rows_wg < target ? rows_wg : target);
     amax_kernel<<<dim3(gx, H), 256, 0, s>>>(x, T, H, dh, per_head, amax);
   }
-  if (fmt == E4M3)
-    scale_finalize_kernel<E4M3><<<(n + 255) / 256, 256, 0, s>>>(amax, scale_out, n);
-  else
-    scale_finalize_kernel<E5M2><<<(n + 255) / 256, 256, 0, s>>>(amax, scale_out, n);
+  dispatch_fmt(fmt, [&](auto f) {
+    scale_finalize_kernel<decltype(f)::value><<<(n + 255) / 256, 256, 0, s>>>(amax, scale_out, n);
+  });
   return hipGetLastError();
 }
 

@@ -19,11 +19,25 @@
 
 namespace kvq {
 
-enum Fmt : int { E4M3 = 0, E5M2 = 1 };
+// E4M3 / E5M2: OCP FP8.  INT8: symmetric 8-bit integers, clip(round(x/s),
+// -127, 127) (the KV-cache quantization textbook's write rule, 10.4.2).
+enum Fmt : int { E4M3 = 0, E5M2 = 1, INT8 = 2 };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Calls f(FmtTag<F>{}) for the runtime format (a template argument inside f).
+template <int F>
+struct FmtTag {
+  static constexpr int value = F;
+};
+template <typename Fn>
+__host__ inline void dispatch_fmt(int fmt, Fn&& f) {
+  if (fmt == E4M3) f(FmtTag<E4M3>{});
+  else if (fmt == E5M2) f(FmtTag<E5M2>{});
+  else f(FmtTag<INT8>{});
+}
 
 template <int FMT>
 struct FmtTraits;
@@ -35,6 +49,28 @@ template <>
 struct FmtTraits<E5M2> {
   static constexpr float kMax = 57344.0f;
 };
+template <>
+struct FmtTraits<INT8> {
+  static constexpr float kMax = 127.0f;
+};
+
+// ---------------------------------------------------------------- INT8
+// code = two's complement byte of clip(round-half-even(x), -127, 127); a NaN
+// quotient gives 0 and +-Inf clip to +-127 (there is no NaN or Inf code).
+__device__ __forceinline__ uint32_t i8_code(float x) {
+  float r = __builtin_amdgcn_fmed3f(__builtin_rintf(x), -127.0f, 127.0f);  // v_rndne_f32
+  r = (x != x) ? 0.0f : r;
+  return (uint32_t)(int)r & 0xffu;
+}
+// two signed codes (bytes 2 HI, 2 HI + 1 of w) -> f16x2, exact: the byte
+// with its sign bit flipped is b + 128, placed as the low mantissa bits of
+// the f16 1024.0 (bits 0x64xx) it reads 1152 + b; one packed subtract.
+template <bool HI>
+__device__ __forceinline__ f16x2 i8x2_to_f16(uint32_t w) {
+  const uint32_t x = (HI ? (w >> 16) : w) ^ 0x8080u;
+  const uint32_t bits = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);  // [x0,64,x1,64]
+  return __builtin_bit_cast(f16x2, bits) - f16x2{(_Float16)1152.0f, (_Float16)1152.0f};
+}
 
 // Saturating clamp that keeps NaN: med3 clamps finite values and +-Inf.
 __device__ __forceinline__ float clamp_keep_nan(float x, float m) {
@@ -45,6 +81,7 @@ __device__ __forceinline__ float clamp_keep_nan(float x, float m) {
 // Two fp32 values -> two codes in the low 16 bits (a in byte 0, b in byte 1).
 template <int FMT>
 __device__ __forceinline__ uint32_t enc2(float a, float b) {
+  if constexpr (FMT == INT8) return i8_code(a) | (i8_code(b) << 8);
   const float m = FmtTraits<FMT>::kMax;
   a = clamp_keep_nan(a, m);
   b = clamp_keep_nan(b, m);
@@ -57,6 +94,8 @@ __device__ __forceinline__ uint32_t enc2(float a, float b) {
 // Four fp32 values -> four codes packed little-endian in one dword.
 template <int FMT>
 __device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
+  if constexpr (FMT == INT8)
+    return i8_code(a) | (i8_code(b) << 8) | (i8_code(c) << 16) | (i8_code(d) << 24);
   const float m = FmtTraits<FMT>::kMax;
   a = clamp_keep_nan(a, m);
   b = clamp_keep_nan(b, m);
@@ -76,7 +115,11 @@ __device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
 // Two codes (bytes 2*hi, 2*hi+1 of w) -> exact fp32 values.
 template <int FMT, bool HI>
 __device__ __forceinline__ f32x2 dec2_f32(uint32_t w) {
-  if constexpr (FMT == E4M3)
+  if constexpr (FMT == INT8) {
+    const uint32_t x = w ^ 0x80808080u;  // unsigned byte = code + 128
+    return HI ? f32x2{(float)((x >> 16) & 0xffu) - 128.0f, (float)(x >> 24) - 128.0f}
+              : f32x2{(float)(x & 0xffu) - 128.0f, (float)((x >> 8) & 0xffu) - 128.0f};
+  } else if constexpr (FMT == E4M3)
     return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
   else
     return __builtin_amdgcn_cvt_pk_f32_bf8((int)w, HI);
@@ -85,7 +128,13 @@ __device__ __forceinline__ f32x2 dec2_f32(uint32_t w) {
 // Two codes -> two exact bf16 values (every E4M3 and E5M2 value is a bf16 value).
 template <int FMT, bool HI>
 __device__ __forceinline__ bf16x2 dec2_bf16(uint32_t w) {
-  if constexpr (FMT == E4M3)
+  if constexpr (FMT == INT8) {
+    // |code| <= 128 has at most 8 significant bits: the fp32 value's top half
+    // is the exact bf16
+    const f32x2 f = dec2_f32<INT8, HI>(w);
+    return __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(__float_as_uint(f.y),
+                                                            __float_as_uint(f.x), 0x07060302u));
+  } else if constexpr (FMT == E4M3)
     return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI);
   else
     return __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w, 1.0f, HI);
@@ -94,7 +143,9 @@ __device__ __forceinline__ bf16x2 dec2_bf16(uint32_t w) {
 // Two codes -> two exact f16 values (every E4M3 and E5M2 value is an f16 value).
 template <int FMT, bool HI>
 __device__ __forceinline__ f16x2 dec2_f16(uint32_t w) {
-  if constexpr (FMT == E4M3)
+  if constexpr (FMT == INT8)
+    return i8x2_to_f16<HI>(w);
+  else if constexpr (FMT == E4M3)
     return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HI);
   else
     return __builtin_amdgcn_cvt_scalef32_pk_f16_bf8((int)w, 1.0f, HI);

@@ -44,19 +44,17 @@ static int flat_grid(int64_t n) {
 
 hipError_t launch_fp8_encode(int fmt, const float* x, int64_t n, uint8_t* out, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (fmt == E4M3)
-    encode_kernel<E4M3><<<flat_grid(n), 256, 0, s>>>(x, n, out);
-  else
-    encode_kernel<E5M2><<<flat_grid(n), 256, 0, s>>>(x, n, out);
+  dispatch_fmt(fmt, [&](auto f) {
+    encode_kernel<decltype(f)::value><<<flat_grid(n), 256, 0, s>>>(x, n, out);
+  });
   return hipGetLastError();
 }
 
 hipError_t launch_fp8_decode(int fmt, const uint8_t* c, int64_t n, float* out, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (fmt == E4M3)
-    decode_kernel<E4M3><<<flat_grid(n), 256, 0, s>>>(c, n, out);
-  else
-    decode_kernel<E5M2><<<flat_grid(n), 256, 0, s>>>(c, n, out);
+  dispatch_fmt(fmt, [&](auto f) {
+    decode_kernel<decltype(f)::value><<<flat_grid(n), 256, 0, s>>>(c, n, out);
+  });
   return hipGetLastError();
 }
 

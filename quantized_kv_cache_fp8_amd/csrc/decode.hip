@@ -767,11 +767,10 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
     else if (plan.part_blocks == 16) KVQ_SPLIT_HP(F, D, 2);   \
     else KVQ_SPLIT_HP(F, D, 1);                               \
   } while (0)
-    if (fmt == E4M3) {
-      if (dh == 128) KVQ_SPLIT_NP(E4M3, 128); else KVQ_SPLIT_NP(E4M3, 64);
-    } else {
-      if (dh == 128) KVQ_SPLIT_NP(E5M2, 128); else KVQ_SPLIT_NP(E5M2, 64);
-    }
+    dispatch_fmt(fmt, [&](auto f) {
+      constexpr int F = decltype(f)::value;
+      if (dh == 128) KVQ_SPLIT_NP(F, 128); else KVQ_SPLIT_NP(F, 64);
+    });
 #undef KVQ_SPLIT_NP
 #undef KVQ_SPLIT_HP
 #undef KVQ_SPLIT_G4

@@ -7,7 +7,7 @@ import numpy as np
 
 import oracle
 
-FMT_ID = {"e4m3": oracle.FMT_E4M3, "e5m2": oracle.FMT_E5M2}
+FMT_ID = {"e4m3": oracle.FMT_E4M3, "e5m2": oracle.FMT_E5M2, "int8": oracle.FMT_INT8}
 GRAN_ID = {"tensor": oracle.GRAN_TENSOR, "head": oracle.GRAN_HEAD}
 SENTINEL = 0xA5
 

@@ -69,7 +69,7 @@ def status_of_decode(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(q=None), -1), (dict(ks=None), -1), (dict(bt=None), -1), (dict(ws=None, wsb=1 << 20), -1),
     (dict(Hq=6, Hkv=4), -2), (dict(B=0), -2), (dict(maxctx=65), -2), (dict(maxctx=-1), -2),
-    (dict(nb=0), -2), (dict(dh=96), -3), (dict(bs=32), -3), (dict(fmt=2), -3), (dict(gran=5), -3),
+    (dict(nb=0), -2), (dict(dh=96), -3), (dict(bs=32), -3), (dict(fmt=3), -3), (dict(gran=5), -3),
     (dict(odt=3), -3), (dict(Hq=64, Hkv=2), -3), (dict(wsb=16), -4),
 ])
 def test_decode_validation(over, status):
@@ -117,4 +117,5 @@ def test_prefill_validation():
     assert st(cu=None) == -1 and st(qs=None) == -1
     assert st(maxq=-1) == -2 and st(Hq=7) == -2
     assert st(qg=4) == -3 and st(dh=256) == -3
+    assert st(fmt=2) == -3  # INT8 caches: the FP8-domain prefill does not take them
     assert st(maxq=0) == 0

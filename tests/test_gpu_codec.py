@@ -1,4 +1,4 @@
-"""GPU parity of the device FP8 codec against the oracle (bit-exact).
+"""GPU parity of the device FP8 and INT8 codec against the oracle (bit-exact).
 
 Decode: all 256 codes.  Encode: every one of the 2^32 fp32 bit patterns, in
 chunks, through the library's kvq_fp8_encode (the same device codec the cache
@@ -12,7 +12,7 @@ import oracle
 from helpers import same_codes, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
-FMTS = [oracle.FMT_E4M3, oracle.FMT_E5M2]
+FMTS = [oracle.FMT_E4M3, oracle.FMT_E5M2, oracle.FMT_INT8]
 
 
 @pytest.mark.parametrize("fmt", FMTS)

@@ -41,7 +41,7 @@ def test_tiny_decode():
     check(out, ref)
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "int8"])
 @pytest.mark.parametrize("gran", ["tensor", "head"])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_ragged_batch(fmt, gran, out_dtype):
@@ -59,11 +59,12 @@ def test_ragged_batch(fmt, gran, out_dtype):
         assert np.array_equal(run.gpu_decode(), W.f32_to_bf16_bits(out))
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "int8"])
 @pytest.mark.parametrize("Hq,Hkv,dh", [(8, 8, 128), (16, 8, 64), (12, 4, 128), (64, 8, 128),
                                        (6, 2, 64), (5, 5, 64)])
-def test_group_sizes_and_head_dims(Hq, Hkv, dh):
+def test_group_sizes_and_head_dims(Hq, Hkv, dh, fmt):
     cl = [700, 33, 129]
-    wl = W.decode_workload("groups", 102 + Hq, len(cl), Hq, Hkv, dh, cl, 16, "e4m3", "head",
+    wl = W.decode_workload("groups", 102 + Hq, len(cl), Hq, Hkv, dh, cl, 16, fmt, "head",
                            head_range=(0.5, 20.0))
     _, out, ref = run_case(wl)
     check(out, ref)
@@ -130,12 +131,13 @@ def test_workspace_reuse_across_calls():
                 np.testing.assert_allclose(got, want, rtol=0, atol=1e-5 * np.abs(want).max())
 
 
-@pytest.mark.parametrize("which", ["llama", "long-e4m3", "long-e5m2"])
+@pytest.mark.parametrize("which", ["llama", "long-e4m3", "long-e5m2", "long-int8"])
 def test_full_size_sampled_rows(which):
     """Full-size workloads; the oracle computes a seeded sample of rows
     (every sequence's first and last head plus random pairs)."""
     wl = {"llama": W.llama_layer_decode, "long-e4m3": lambda: W.long_context_decode("e4m3"),
-          "long-e5m2": lambda: W.long_context_decode("e5m2")}[which]()
+          "long-e5m2": lambda: W.long_context_decode("e5m2"),
+          "long-int8": lambda: W.long_context_decode("int8")}[which]()
     print(f"[{which}] B={wl.B} tokens={wl.kv.k.shape[0]}", flush=True)
     run = DecodeRun(wl)
     run.gpu_scales()

@@ -7,7 +7,7 @@ import workloads as W
 from helpers import SENTINEL, DecodeRun, same_codes, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
-FMTS = [oracle.FMT_E4M3, oracle.FMT_E5M2]
+FMTS = [oracle.FMT_E4M3, oracle.FMT_E5M2, oracle.FMT_INT8]
 ALL_BF16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
 
 # scales in the supported range [2^-126, 2^126): powers of two, amax/fmax-like values,

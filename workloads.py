@@ -129,7 +129,7 @@ class DecodeWorkload:
     Hkv: int
     dh: int
     bs: int
-    fmt: str  # "e4m3" | "e5m2"
+    fmt: str  # "e4m3" | "e5m2" | "int8"
     gran: str  # "tensor" | "head"
     paging: Paging
     kv: KVBatch
