@@ -64,6 +64,13 @@ def lib() -> ctypes.CDLL:
         P = ctypes.c_void_p
         i32, i64, f32, f64, u8 = (ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_double,
                                   ctypes.c_uint8)
+        L.orc_f16_to_double.argtypes = [ctypes.c_uint16]
+        L.orc_f16_to_double.restype = f64
+        L.orc_scale16_from_amax.argtypes = [i32, f32]
+        L.orc_scale16_from_amax.restype = ctypes.c_uint16
+        L.orc_cache_write_token.argtypes = [P, P, i64, i32, i32, P, P, P, P, P, i64, i32, i32]
+        L.orc_decode_token_rows.argtypes = [P, P, i32, P, P, P, P, P, P, i32, P, i32, i32, i32,
+                                            i32, i32, f32]
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = i32
         L.orc_fp8_max.argtypes = [i32]
@@ -305,3 +312,49 @@ def kv_cache_bytes(L: int, B: int, Hkv: int, S: int, dh: int, bits_per_elem: int
 
 def token_head_bytes(dh: int, bits_per_elem: int, scale_bytes: int) -> int:
     return int(lib().orc_token_head_bytes(dh, bits_per_elem, scale_bytes))
+
+
+# ---------------------------------------------------------------- per-token-head scales
+
+def scale16_from_amax(fmt: int, amax: float) -> int:
+    """fp16 bits of fl16(clamp(fl32(amax / fmax), 2^-24, 65504)); 1.0 if amax is 0 or not finite."""
+    return int(lib().orc_scale16_from_amax(fmt, amax))
+
+
+def f16_to_double(bits: int) -> float:
+    return lib().orc_f16_to_double(bits)
+
+
+def scale_cache_shape(num_blocks: int, Hkv: int, bs: int) -> tuple:
+    """fp16 per-token-head scales (uint16 bit patterns) [num_blocks][Hkv][bs]."""
+    return (num_blocks, Hkv, bs)
+
+
+def cache_write_token(k_bf16, v_bf16, slot_mapping, k_cache, v_cache, k_scale_cache,
+                      v_scale_cache, fmt: int) -> None:
+    """Quantize-write with one fp16 scale per (token, head), stored beside the codes."""
+    k, v = _u16(k_bf16), _u16(v_bf16)
+    T, Hkv, dh = k.shape
+    nb, hk, bs, dh2 = _kv_dims(k_cache)
+    assert hk == Hkv and dh2 == dh and v_cache.shape == (nb, Hkv, dh, bs)
+    assert k_scale_cache.shape == (nb, Hkv, bs) and k_scale_cache.dtype == np.uint16
+    assert v_scale_cache.shape == (nb, Hkv, bs) and v_scale_cache.dtype == np.uint16
+    sm = np.ascontiguousarray(slot_mapping, np.int64)
+    lib().orc_cache_write_token(_p(k), _p(v), T, Hkv, dh, _p(sm), _p(k_cache), _p(v_cache),
+                                _p(k_scale_cache), _p(v_scale_cache), nb, bs, fmt)
+
+
+def decode_token_rows(rows, q_bf16, k_cache, v_cache, k_scale_cache, v_scale_cache,
+                      block_tables, context_lens, fmt: int, softmax_scale: float = 0.0):
+    """Decode output (fp64 [n, dh]) for the listed (b, hq) rows with per-token-head scales."""
+    q = _u16(q_bf16)
+    B, Hq, dh = q.shape
+    _, Hkv, bs, _ = _kv_dims(k_cache)
+    rows = np.ascontiguousarray(rows, np.int32).reshape(-1, 2)
+    bt = np.ascontiguousarray(block_tables, np.int32)
+    cl = np.ascontiguousarray(context_lens, np.int32)
+    out = np.zeros((rows.shape[0], dh), np.float64)
+    lib().orc_decode_token_rows(_p(out), _p(rows), rows.shape[0], _p(q), _p(k_cache),
+                                _p(v_cache), _p(k_scale_cache), _p(v_scale_cache), _p(bt),
+                                bt.shape[1], _p(cl), Hq, Hkv, dh, bs, fmt, softmax_scale)
+    return out

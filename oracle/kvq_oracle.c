@@ -267,9 +267,39 @@ static double deq_v(const uint8_t* cache, int64_t blk, int h, int off, int d, in
 /* Attention of one query vector q[dh] (fp64) over keys 0..nkeys-1 of one
  * sequence's paged cache (textbook 10.4.2: P = softmax(Q K^T / sqrt(dh) + mask),
  * O = P V), all in fp64; writes o[dh]. */
+/* fp16 bits -> exact value (IEEE binary16: 5 exponent bits, bias 15). */
+double orc_f16_to_double(uint16_t b) {
+  int s = b >> 15, e = (b >> 10) & 31, m = b & 1023;
+  double v;
+  if (e == 31) v = m ? NAN : INFINITY;
+  else if (e == 0) v = ldexp((double)m, -24);
+  else v = ldexp(1.0 + m / 1024.0, e - 15);
+  return s ? -v : v;
+}
+
+/* scale of one (block, head, offset) slot: the uniform scale, or the slot's
+ * fp16 per-token scale when a scale cache is given */
+static double slot_scale(const uint16_t* sc, double s, int64_t blk, int h, int off, int Hkv,
+                         int bs) {
+  return sc ? orc_f16_to_double(sc[(blk * Hkv + h) * bs + off]) : s;
+}
+
+static void attend_one_ts(double* o, const double* q, int nkeys, const uint8_t* k_cache,
+                          const uint8_t* v_cache, const uint16_t* ksc, const uint16_t* vsc,
+                          const int32_t* btab, int h, int Hkv, int bs, int dh, double sk,
+                          double sv, int fmt, double sm_scale);
+
 static void attend_one(double* o, const double* q, int nkeys, const uint8_t* k_cache,
                        const uint8_t* v_cache, const int32_t* btab, int h, int Hkv, int bs,
                        int dh, double sk, double sv, int fmt, double sm_scale) {
+  attend_one_ts(o, q, nkeys, k_cache, v_cache, NULL, NULL, btab, h, Hkv, bs, dh, sk, sv, fmt,
+                sm_scale);
+}
+
+static void attend_one_ts(double* o, const double* q, int nkeys, const uint8_t* k_cache,
+                          const uint8_t* v_cache, const uint16_t* ksc, const uint16_t* vsc,
+                          const int32_t* btab, int h, int Hkv, int bs, int dh, double sk,
+                          double sv, int fmt, double sm_scale) {
   for (int d = 0; d < dh; ++d) o[d] = 0.0;
   if (nkeys <= 0) return;
   double* z = (double*)malloc(sizeof(double) * (size_t)nkeys);
@@ -278,7 +308,8 @@ static void attend_one(double* o, const double* q, int nkeys, const uint8_t* k_c
     int64_t blk = btab[j / bs];
     int off = j % bs;
     double acc = 0.0;
-    for (int d = 0; d < dh; ++d) acc += q[d] * deq_k(k_cache, blk, h, off, d, Hkv, bs, dh, sk, fmt);
+    double skj = slot_scale(ksc, sk, blk, h, off, Hkv, bs);
+    for (int d = 0; d < dh; ++d) acc += q[d] * deq_k(k_cache, blk, h, off, d, Hkv, bs, dh, skj, fmt);
     z[j] = acc * sm_scale;
     if (z[j] > zmax) zmax = z[j];
   }
@@ -291,7 +322,8 @@ static void attend_one(double* o, const double* q, int nkeys, const uint8_t* k_c
     int64_t blk = btab[j / bs];
     int off = j % bs;
     double p = z[j] / l;
-    for (int d = 0; d < dh; ++d) o[d] += p * deq_v(v_cache, blk, h, off, d, Hkv, bs, dh, sv, fmt);
+    double svj = slot_scale(vsc, sv, blk, h, off, Hkv, bs);
+    for (int d = 0; d < dh; ++d) o[d] += p * deq_v(v_cache, blk, h, off, d, Hkv, bs, dh, svj, fmt);
   }
   free(z);
 }
@@ -449,6 +481,93 @@ void orc_dense_attn(double* out, const double* q, const double* k, const double*
 /* ---- memory arithmetic ----
  * textbook 10.4.1: M_KV = 2 * L * B * Hkv * S * dh * bytes_per_element, the
  * leading 2 counting K and V.  bits_per_elem may be below 8 (2-bit payload). */
+/* ---- per-token-head scales (textbook 10.4.3: one scale per token along dh;
+ * its metadata example keeps one FP16 scale per (token, head) for K and for
+ * V).  Reading: s = fl16(clamp(fl32(amax / fmax), 2^-24, 65504)) with
+ * round-to-nearest-even into fp16, 1.0 when amax is 0 or not finite; the
+ * codes are then quantize(x, s) with that fp16 value.  Scale caches are fp16
+ * [num_blocks][Hkv][bs], beside the code caches. ---- */
+
+static uint16_t f16_bits_rne(double x) {
+  /* x positive, in [2^-24, 65504]: round to the binary16 grid, ties to even */
+  int e2;
+  frexp(x, &e2);
+  int be = e2 - 1;               /* x in [2^be, 2^(be+1)) */
+  if (be < -14) be = -14;        /* subnormal range: quantum 2^-24 */
+  double quantum = ldexp(1.0, be - 10);
+  double r = rint(x / quantum) * quantum;
+  /* encode r */
+  if (r < ldexp(1.0, -14)) return (uint16_t)(r / ldexp(1.0, -24));
+  int er;
+  frexp(r, &er);
+  int bexp = er - 1;
+  int mant = (int)((r / ldexp(1.0, bexp) - 1.0) * 1024.0);
+  return (uint16_t)(((bexp + 15) << 10) | mant);
+}
+
+uint16_t orc_scale16_from_amax(int fmt, float amax) {
+  if (!(amax > 0.0f) || isinf(amax)) return 0x3C00; /* 1.0 */
+  double s = (double)(float)((double)amax / orc_fp8_max(fmt)); /* fl32(amax / fmax) */
+  if (s < ldexp(1.0, -24)) s = ldexp(1.0, -24);
+  if (s > 65504.0) s = 65504.0;
+  return f16_bits_rne(s);
+}
+
+void orc_cache_write_token(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv, int dh,
+                           const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                           uint16_t* k_scale_cache, uint16_t* v_scale_cache, int64_t num_blocks,
+                           int bs, int fmt) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= num_blocks * bs) continue; /* padding or out-of-range: skipped */
+    int64_t blk = slot / bs, off = slot % bs;
+    for (int h = 0; h < Hkv; ++h) {
+      const uint16_t* kr = k + (t * Hkv + h) * dh;
+      const uint16_t* vr = v + (t * Hkv + h) * dh;
+      float ak = 0.0f, av = 0.0f;
+      int knan = 0, vnan = 0;
+      for (int d = 0; d < dh; ++d) {
+        float a = fabsf(orc_bf16_to_f32(kr[d])), b = fabsf(orc_bf16_to_f32(vr[d]));
+        knan |= isnan(a);
+        vnan |= isnan(b);
+        if (a > ak) ak = a;
+        if (b > av) av = b;
+      }
+      uint16_t sk16 = orc_scale16_from_amax(fmt, knan ? NAN : ak);
+      uint16_t sv16 = orc_scale16_from_amax(fmt, vnan ? NAN : av);
+      k_scale_cache[(blk * Hkv + h) * bs + off] = sk16;
+      v_scale_cache[(blk * Hkv + h) * bs + off] = sv16;
+      float sk = (float)orc_f16_to_double(sk16), sv = (float)orc_f16_to_double(sv16);
+      for (int d = 0; d < dh; ++d) {
+        k_cache[k_index(blk, h, (int)off, d, Hkv, bs, dh)] = orc_quantize(fmt, kr[d], sk);
+        v_cache[v_index(blk, h, (int)off, d, Hkv, bs, dh)] = orc_quantize(fmt, vr[d], sv);
+      }
+    }
+  }
+}
+
+/* Decode rows (b, hq) with per-token-head scales; as orc_decode_rows. */
+void orc_decode_token_rows(double* out, const int32_t* rows, int n, const uint16_t* q,
+                           const uint8_t* k_cache, const uint8_t* v_cache,
+                           const uint16_t* k_scale_cache, const uint16_t* v_scale_cache,
+                           const int32_t* block_tables, int max_blocks,
+                           const int32_t* context_lens, int Hq, int Hkv, int dh, int bs, int fmt,
+                           float softmax_scale) {
+  int G = Hq / Hkv;
+  double sm = default_scale(softmax_scale, dh);
+#pragma omp parallel for schedule(dynamic)
+  for (int i = 0; i < n; ++i) {
+    int b = rows[2 * i], hq = rows[2 * i + 1];
+    int h = hq / G;
+    double qd[512];
+    for (int d = 0; d < dh; ++d) qd[d] = (double)orc_bf16_to_f32(q[((int64_t)b * Hq + hq) * dh + d]);
+    attend_one_ts(out + (int64_t)i * dh, qd, context_lens[b], k_cache, v_cache, k_scale_cache,
+                  v_scale_cache, block_tables + (int64_t)b * max_blocks, h, Hkv, bs, dh, 1.0,
+                  1.0, fmt, sm);
+  }
+}
+
 uint64_t orc_kv_cache_bytes(int L, int B, int Hkv, int64_t S, int dh, int bits_per_elem) {
   uint64_t elems = 2ull * (uint64_t)L * (uint64_t)B * (uint64_t)Hkv * (uint64_t)S * (uint64_t)dh;
   return elems * (uint64_t)bits_per_elem / 8ull;
