@@ -260,8 +260,51 @@ def decode_row(K, torch, dev, stream, k_all, v_all, slots_all, caches, wl, dec, 
             "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def token_scale_rows(K, torch, dev, stream, k_all, v_all, slots_all, caches, wl, dec, reps=50):
+    """Per-token-head fp16 scales (textbook 10.4.3): the full-context write that
+    derives them, and decode of the headline layer over that cache; bytes count
+    codes plus the 2-byte scales."""
+    q, bt, ctx, max_ctx, ws, out = dec
+    T = k_all.shape[0]
+    nb = caches[0][0].shape[0]
+    scs = [(torch.empty((nb, wl.Hkv, wl.bs), dtype=torch.int16, device=dev),
+            torch.empty((nb, wl.Hkv, wl.bs), dtype=torch.int16, device=dev)) for _ in caches]
+    rows = {}
+    kc, vc = caches[0]
+    ksc, vsc = scs[0]
+
+    def write():
+        K.kvq_cache_write_token_scales(k_all, v_all, slots_all, kc, vc, ksc, vsc, "fp8_e4m3")
+    ms = time_call(torch, stream, write, 10)
+    nbytes = T * (wl.Hkv * wl.dh * 2 * 2 + wl.Hkv * wl.dh * 2 + wl.Hkv * 4 + 8)
+    rows["cache_write_token_scales"] = {"workload": wl.name + " full context, e4m3",
+                                        "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1)}
+    for (kc, vc), (ksc, vsc) in zip(caches, scs):
+        K.kvq_cache_write_token_scales(k_all, v_all, slots_all, kc, vc, ksc, vsc, "fp8_e4m3")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i in range(reps + 5):
+        (kc, vc), (ksc, vsc) = caches[i % len(caches)], scs[i % len(caches)]
+        if i >= 5:
+            ev[i - 5][0].record(stream)
+        K.kvq_decode_attn_token_scales(out, q, kc, vc, ksc, vsc, bt, ctx, max_ctx, "fp8_e4m3",
+                                       workspace=ws)
+        if i >= 5:
+            ev[i - 5][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    kv_bytes = int(wl.paging.context_lens.sum()) * wl.Hkv * (wl.dh * 2 + 4)
+    gbs = kv_bytes / ms / 1e6
+    rows["decode_token_scales"] = {"workload": wl.name + " (e4m3 cache, fp16 per-token-head "
+                                   "scales)", "ms": round(ms, 5), "GB/s": round(gbs, 1),
+                                   "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    return rows
+
+
 def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, vs, wl, dec):
     rows = {}
+    rows.update(token_scale_rows(K, torch, dev, stream, k_all, v_all, slots_all, caches, wl,
+                                 dec))
     # the same decode with a symmetric INT8 cache (textbook 10.4.2 write rule)
     rows["decode_int8"] = decode_row(K, torch, dev, stream, k_all, v_all, slots_all, caches, wl,
                                      dec, "int8")

@@ -178,6 +178,46 @@ kvq_status kvq_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
                            kvq_fmt fmt, kvq_gran gran, float softmax_scale, void* workspace,
                            size_t ws_bytes, kvq_stream stream);
 
+/* ---------------------------------------------------------------- per-token-head scales
+ * Finer scale granularity ([T] 10.4.3: one scale per token row along dh; its
+ * metadata example keeps one FP16 scale for K and one for V per token and
+ * head).  The scales live in caches paged like the codes:
+ *   k_scale_cache, v_scale_cache: fp16 bit patterns, uint16 [num_blocks][Hkv][bs];
+ *   the scale of the token at slot s and head h sits at [s / bs][h][s % bs].
+ *
+ * Quantize-on-write computing each row's own scale: for every token t with
+ * 0 <= slot_mapping[t] < num_blocks * bs and every KV head h, with
+ * amax = max_d |x[t][h][d]| (x = k, then v):
+ *   s = fl16(clamp(fl32(amax / fmax(fmt)), 2^-24, 65504))  (round to nearest
+ *       even; 1.0 if amax is 0 or the row holds an Inf or NaN)
+ *   codes as kvq_cache_write with that s; the scale caches receive s.
+ * Skipped tokens touch neither codes nor scales.  Any fmt; dh in {64, 128};
+ * bs == 16.  The scale caches must be 2-byte aligned.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED. */
+kvq_status kvq_cache_write_token_scales(const void* k_bf16, const void* v_bf16, int64_t T,
+                                        int Hkv, int dh, const int64_t* slot_mapping,
+                                        uint8_t* k_cache, uint8_t* v_cache,
+                                        uint16_t* k_scale_cache, uint16_t* v_scale_cache,
+                                        int64_t num_blocks, int bs, kvq_fmt fmt,
+                                        kvq_stream stream);
+
+/* Paged decode over a cache written by kvq_cache_write_token_scales: as
+ * kvq_decode_attn with K_hat[j] = sK[j] * K8[j] and V_hat[j] = sV[j] * V8[j]
+ * per cached position j ([T] 10.4.2 read rule at 10.4.3's per-token
+ * granularity).  Only groups of at most 4 query heads per KV head
+ * (Hq / Hkv <= 4) are supported; larger groups return KVQ_ERR_UNSUPPORTED.
+ * The workspace is sized by kvq_decode_workspace_size as for kvq_decode_attn.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE. */
+kvq_status kvq_decode_attn_token_scales(void* out, kvq_out out_dtype, const void* q_bf16,
+                                        const uint8_t* k_cache, const uint8_t* v_cache,
+                                        const uint16_t* k_scale_cache,
+                                        const uint16_t* v_scale_cache, int64_t num_blocks,
+                                        const int32_t* block_tables, int max_blocks,
+                                        const int32_t* context_lens, int B, int Hq, int Hkv,
+                                        int dh, int bs, int max_context_len, kvq_fmt fmt,
+                                        float softmax_scale, void* workspace, size_t ws_bytes,
+                                        kvq_stream stream);
+
 /* ---------------------------------------------------------------- prefill
  * Causal chunked prefill in the FP8 domain ([G] the FlashAttention-3 note:
  * attention computed on FP8 operands with Q quantized too; [T] 10.4.5 storage

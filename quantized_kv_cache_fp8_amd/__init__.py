@@ -29,7 +29,8 @@ GRAN_NAMES = {"tensor": KVQ_SCALE_TENSOR, "head": KVQ_SCALE_HEAD,
 
 EXPORTS = ["kvq_strerror", "kvq_kv_cache_bytes", "kvq_fp8_encode", "kvq_fp8_decode",
            "kvq_calibrate_scales", "kvq_cache_write", "kvq_decode_workspace_size",
-           "kvq_decode_attn", "kvq_prefill_attn"]
+           "kvq_decode_attn", "kvq_prefill_attn", "kvq_cache_write_token_scales",
+           "kvq_decode_attn_token_scales"]
 
 
 class KvqError(RuntimeError):
@@ -63,6 +64,10 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_workspace_size.restype = sz
         L.kvq_decode_attn.argtypes = [P, i32, P, P, P, i64, P, i32, P, i32, i32, i32, i32, i32,
                                       i32, P, P, i32, i32, f32, P, sz, P]
+        L.kvq_cache_write_token_scales.argtypes = [P, P, i64, i32, i32, P, P, P, P, P, i64, i32,
+                                                   i32, P]
+        L.kvq_decode_attn_token_scales.argtypes = [P, i32, P, P, P, P, P, i64, P, i32, P, i32, i32,
+                                                   i32, i32, i32, i32, i32, f32, P, sz, P]
         L.kvq_prefill_attn.argtypes = [P, i32, P, P, i32, P, i32, P, P, i64, P, i32, P, i32, i32,
                                        i32, i32, i32, P, P, i32, i32, f32, P]
         _lib = L
@@ -170,6 +175,48 @@ def kvq_decode_attn(out, q, k_cache, v_cache, block_tables, context_lens, max_co
                                  _ptr(v_scale), _fmt(fmt), _gran(gran), float(softmax_scale),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(stream)))
+
+
+def _scale_cache_dims(k_scale_cache, v_scale_cache, nb, Hkv, bs):
+    want = (nb, Hkv, bs)
+    for t in (k_scale_cache, v_scale_cache):
+        if tuple(t.shape) != want or t.element_size() != 2:
+            raise ValueError(f"scale caches must be 16-bit {want}, got {tuple(t.shape)}")
+
+
+def kvq_cache_write_token_scales(k, v, slot_mapping, k_cache, v_cache, k_scale_cache,
+                                 v_scale_cache, fmt, stream=None) -> None:
+    """As kvq_cache_write with one fp16 scale per (token, KV head), computed from
+    the row and stored in k_scale_cache / v_scale_cache (16-bit [nb, Hkv, bs])."""
+    T, Hkv, dh = k.shape
+    nb, _, bs, _ = _cache_dims(k_cache, v_cache)
+    _scale_cache_dims(k_scale_cache, v_scale_cache, nb, Hkv, bs)
+    _check("kvq_cache_write_token_scales",
+           lib().kvq_cache_write_token_scales(_ptr(k), _ptr(v), T, Hkv, dh, _ptr(slot_mapping),
+                                              _ptr(k_cache), _ptr(v_cache), _ptr(k_scale_cache),
+                                              _ptr(v_scale_cache), nb, bs, _fmt(fmt),
+                                              _stream(stream)))
+
+
+def kvq_decode_attn_token_scales(out, q, k_cache, v_cache, k_scale_cache, v_scale_cache,
+                                 block_tables, context_lens, max_context_len, fmt,
+                                 softmax_scale=0.0, workspace=None, stream=None) -> None:
+    """kvq_decode_attn over a cache with per-token-head fp16 scales (Hq / Hkv <= 4)."""
+    import torch
+    B, Hq, dh = q.shape
+    nb, Hkv, bs, _ = _cache_dims(k_cache, v_cache)
+    _scale_cache_dims(k_scale_cache, v_scale_cache, nb, Hkv, bs)
+    ws_bytes = kvq_decode_workspace_size(B, Hq, dh, max_context_len, bs)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
+    _check("kvq_decode_attn_token_scales",
+           lib().kvq_decode_attn_token_scales(
+               _ptr(out), out_dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale_cache),
+               _ptr(v_scale_cache), nb, _ptr(block_tables), block_tables.shape[1],
+               _ptr(context_lens), B, Hq, Hkv, dh, bs, int(max_context_len), _fmt(fmt),
+               float(softmax_scale), _ptr(workspace),
+               workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def kvq_prefill_attn(out, q, cu_seqlens_q, max_q_len, q_scale, q_gran, k_cache, v_cache,

@@ -134,8 +134,8 @@ size_t kvq_decode_workspace_size(int B, int Hq, int dh, int max_context_len, int
 static kvq_status check_attn_common(const void* out, int out_dtype, const void* q,
                                     const uint8_t* kc, const uint8_t* vc, int64_t num_blocks,
                                     const int32_t* bt, int max_blocks, const int32_t* ctx, int B,
-                                    int Hq, int Hkv, int dh, int bs, const float* ks,
-                                    const float* vs, int fmt, int gran) {
+                                    int Hq, int Hkv, int dh, int bs, const void* ks,
+                                    const void* vs, int fmt, int gran) {
   if (!fmt_ok(fmt) || !gran_ok(gran) || !out_ok(out_dtype)) return KVQ_ERR_UNSUPPORTED;
   if (B < 1 || Hq < 1 || Hkv < 1 || num_blocks < 1 || max_blocks < 1) return KVQ_ERR_SHAPE;
   if (Hq % Hkv) return KVQ_ERR_SHAPE;
@@ -143,6 +143,17 @@ static kvq_status check_attn_common(const void* out, int out_dtype, const void* 
   if (!out || !q || !kc || !vc || !bt || !ctx || !ks || !vs) return KVQ_ERR_NULL;
   if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(out, 16))
     return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+static kvq_status check_decode_ws(const DecodePlan& plan, int max_context_len, int max_blocks,
+                                  int bs, const void* workspace, size_t ws_bytes) {
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks * bs)
+    return KVQ_ERR_SHAPE;
+  if (plan.nsplit > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (!workspace) return KVQ_ERR_NULL;
+  if (ws_bytes < plan.ws_bytes) return KVQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 
@@ -157,18 +168,63 @@ kvq_status kvq_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
                                     block_tables, max_blocks, context_lens, B, Hq, Hkv, dh, bs,
                                     k_scale, v_scale, fmt, gran);
   if (st != KVQ_OK) return st;
-  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks * bs)
-    return KVQ_ERR_SHAPE;
-  DecodePlan plan = decode_plan(B, Hq, dh, max_context_len, bs);
-  if (plan.nsplit > 65535) return KVQ_ERR_UNSUPPORTED;
-  if (!workspace) return KVQ_ERR_NULL;
-  if (ws_bytes < plan.ws_bytes) return KVQ_ERR_WORKSPACE;
-  if (!aligned(workspace, 16)) return KVQ_ERR_UNSUPPORTED;
+  const DecodePlan plan = decode_plan(B, Hq, dh, max_context_len, bs);
+  st = check_decode_ws(plan, max_context_len, max_blocks, bs, workspace, ws_bytes);
+  if (st != KVQ_OK) return st;
   return map_err(launch_decode(out, out_dtype == KVQ_OUT_BF16, (const uint16_t*)q_bf16, k_cache,
                                v_cache, num_blocks, block_tables, max_blocks, context_lens, B, Hq,
                                Hkv, dh, max_context_len, k_scale, v_scale, fmt,
                                gran == KVQ_SCALE_HEAD, softmax_scale, plan, workspace,
                                (hipStream_t)stream));
+}
+
+kvq_status kvq_cache_write_token_scales(const void* k_bf16, const void* v_bf16, int64_t T,
+                                        int Hkv, int dh, const int64_t* slot_mapping,
+                                        uint8_t* k_cache, uint8_t* v_cache,
+                                        uint16_t* k_scale_cache, uint16_t* v_scale_cache,
+                                        int64_t num_blocks, int bs, kvq_fmt fmt,
+                                        kvq_stream stream) {
+  if (!fmt_ok(fmt)) return KVQ_ERR_UNSUPPORTED;
+  if (T < 0 || Hkv < 1 || num_blocks < 1) return KVQ_ERR_SHAPE;
+  if (!dh_ok(dh) || bs != 16 || Hkv > 256) return KVQ_ERR_UNSUPPORTED;
+  if ((uint64_t)T * (uint64_t)Hkv * (uint64_t)(dh / 16) + 256 >= (1ull << 32))
+    return KVQ_ERR_SHAPE;
+  if (!k_cache || !v_cache || !k_scale_cache || !v_scale_cache) return KVQ_ERR_NULL;
+  if (T == 0) return KVQ_OK;
+  if (!k_bf16 || !v_bf16 || !slot_mapping) return KVQ_ERR_NULL;
+  if (!aligned(k_bf16, 16) || !aligned(v_bf16, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(k_scale_cache, 2) || !aligned(v_scale_cache, 2) ||
+      !aligned(slot_mapping, 8))
+    return KVQ_ERR_UNSUPPORTED;
+  return map_err(launch_cache_write_token((const uint16_t*)k_bf16, (const uint16_t*)v_bf16, T,
+                                          Hkv, dh, slot_mapping, k_cache, v_cache,
+                                          k_scale_cache, v_scale_cache, num_blocks, fmt,
+                                          (hipStream_t)stream));
+}
+
+kvq_status kvq_decode_attn_token_scales(void* out, kvq_out out_dtype, const void* q_bf16,
+                                        const uint8_t* k_cache, const uint8_t* v_cache,
+                                        const uint16_t* k_scale_cache,
+                                        const uint16_t* v_scale_cache, int64_t num_blocks,
+                                        const int32_t* block_tables, int max_blocks,
+                                        const int32_t* context_lens, int B, int Hq, int Hkv,
+                                        int dh, int bs, int max_context_len, kvq_fmt fmt,
+                                        float softmax_scale, void* workspace, size_t ws_bytes,
+                                        kvq_stream stream) {
+  kvq_status st = check_attn_common(out, out_dtype, q_bf16, k_cache, v_cache, num_blocks,
+                                    block_tables, max_blocks, context_lens, B, Hq, Hkv, dh, bs,
+                                    k_scale_cache, v_scale_cache, fmt, KVQ_SCALE_TENSOR);
+  if (st != KVQ_OK) return st;
+  if (Hq / Hkv > 4) return KVQ_ERR_UNSUPPORTED;
+  if (!aligned(k_scale_cache, 2) || !aligned(v_scale_cache, 2)) return KVQ_ERR_UNSUPPORTED;
+  const DecodePlan plan = decode_plan(B, Hq, dh, max_context_len, bs);
+  st = check_decode_ws(plan, max_context_len, max_blocks, bs, workspace, ws_bytes);
+  if (st != KVQ_OK) return st;
+  return map_err(launch_decode(out, out_dtype == KVQ_OUT_BF16, (const uint16_t*)q_bf16, k_cache,
+                               v_cache, num_blocks, block_tables, max_blocks, context_lens, B, Hq,
+                               Hkv, dh, max_context_len, nullptr, nullptr, fmt, 0, softmax_scale,
+                               plan, workspace, (hipStream_t)stream, k_scale_cache,
+                               v_scale_cache));
 }
 
 kvq_status kvq_prefill_attn(void* out, kvq_out out_dtype, const void* q_bf16,

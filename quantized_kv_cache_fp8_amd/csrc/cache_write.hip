@@ -197,6 +197,107 @@ __global__ __launch_bounds__(256) void cache_write_short_kernel(
   for (int c = 0; c < 16; ++c) vd[c * kBs] = (uint8_t)(vq[c >> 2] >> (8 * (c & 3)));
 }
 
+// Per-token-head scales (one fp16 scale per (token, head) for K and for V,
+// stored beside the codes in [num_blocks][Hkv][bs] scale caches): the lanes
+// that share a (token, head) row -- DH / 16 consecutive lanes, one 16-channel
+// chunk each -- reduce the row's amax over |x| bit patterns (an exact integer
+// max in which NaN patterns sort above +Inf), derive
+//   s = fl16(clamp(fl32(amax / fmax), 2^-24, 65504))   (1.0 for amax 0, Inf, NaN)
+// and quantize their chunk with it.
+// largest |x| bit pattern (sign cleared) among 8 bf16 values
+__device__ __forceinline__ uint32_t absmax_bits8(uint4 w) {
+  const uint32_t v[4] = {w.x & 0x7fff7fffu, w.y & 0x7fff7fffu, w.z & 0x7fff7fffu,
+                         w.w & 0x7fff7fffu};
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = v[i] & 0xffffu, hi = v[i] >> 16;
+    r = lo > r ? lo : r;
+    r = hi > r ? hi : r;
+  }
+  return r;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint16_t scale16_from_amax_bits(uint32_t abits) {
+  if (abits == 0 || abits >= 0x7f80u) return 0x3C00;  // 0, Inf or NaN -> 1.0
+  float s = __fdiv_rn(__uint_as_float(abits << 16), FmtTraits<FMT>::kMax);
+  s = __builtin_amdgcn_fmed3f(s, 0x1p-24f, 65504.0f);
+  return __builtin_bit_cast(uint16_t, (_Float16)s);  // round to nearest even
+}
+
+template <int FMT, int DH>
+__global__ __launch_bounds__(256) void cache_write_token_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint32_t units, int Hkv,
+    const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+    uint16_t* __restrict__ ksc, uint16_t* __restrict__ vsc, int64_t num_slots) {
+  constexpr int kNc = DH / 16;  // lanes per (token, head) row
+  const uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
+  const bool live = u < units;  // every lane takes part in the row reductions
+  const uint32_t uu = live ? u : units - 1;
+  const uint32_t q = uu % kNc, th = uu / kNc;
+  const uint32_t t = th / (uint32_t)Hkv;
+  const int h = (int)(th - t * (uint32_t)Hkv);
+  const size_t src = (size_t)th * DH + q * 16;
+  const uint4 k0 = *reinterpret_cast<const uint4*>(k + src);
+  const uint4 k1 = *reinterpret_cast<const uint4*>(k + src + 8);
+  const uint4 v0 = *reinterpret_cast<const uint4*>(v + src);
+  const uint4 v1 = *reinterpret_cast<const uint4*>(v + src + 8);
+  const int64_t s = slot_mapping[t];
+  uint32_t ak = absmax_bits8(k0), ak1 = absmax_bits8(k1);
+  uint32_t av = absmax_bits8(v0), av1 = absmax_bits8(v1);
+  ak = ak > ak1 ? ak : ak1;
+  av = av > av1 ? av : av1;
+#pragma unroll
+  for (int o = 1; o < kNc; o <<= 1) {  // rows are kNc aligned consecutive lanes
+    const uint32_t xk = __shfl_xor(ak, o), xv = __shfl_xor(av, o);
+    ak = ak > xk ? ak : xk;
+    av = av > xv ? av : xv;
+  }
+  if (!live || s < 0 || s >= num_slots) return;  // padding or out of the pool: skipped
+  const uint16_t sk16 = scale16_from_amax_bits<FMT>(ak), sv16 = scale16_from_amax_bits<FMT>(av);
+  const float sk = (float)__builtin_bit_cast(_Float16, sk16);
+  const float sv = (float)__builtin_bit_cast(_Float16, sv16);
+  const float rk = recip_rn(sk), rv = recip_rn(sv);
+  const uint4 kq = make_uint4(quant4<FMT>(make_uint2(k0.x, k0.y), sk, rk),
+                              quant4<FMT>(make_uint2(k0.z, k0.w), sk, rk),
+                              quant4<FMT>(make_uint2(k1.x, k1.y), sk, rk),
+                              quant4<FMT>(make_uint2(k1.z, k1.w), sk, rk));
+  const uint32_t vq[4] = {quant4<FMT>(make_uint2(v0.x, v0.y), sv, rv),
+                          quant4<FMT>(make_uint2(v0.z, v0.w), sv, rv),
+                          quant4<FMT>(make_uint2(v1.x, v1.y), sv, rv),
+                          quant4<FMT>(make_uint2(v1.z, v1.w), sv, rv)};
+  const size_t row = (size_t)((s >> 4) * Hkv + h);
+  const int off = (int)(s & (kBs - 1));
+  *reinterpret_cast<uint4*>(kc + row * kBs * DH + q * (kBs * 16) + off * 16) = kq;
+  uint8_t* vd = vc + row * kBs * DH + (size_t)q * 16 * kBs + off;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) vd[c * kBs] = (uint8_t)(vq[c >> 2] >> (8 * (c & 3)));
+  if (q == 0) {
+    ksc[row * kBs + off] = sk16;
+    vsc[row * kBs + off] = sv16;
+  }
+}
+
+hipError_t launch_cache_write_token(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv,
+                                    int dh, const int64_t* slot, uint8_t* kc, uint8_t* vc,
+                                    uint16_t* ksc, uint16_t* vsc, int64_t num_blocks, int fmt,
+                                    hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int64_t num_slots = num_blocks * kBs;
+  const uint32_t units = (uint32_t)(T * Hkv * (dh / 16));
+  dispatch_fmt(fmt, [&](auto f) {
+    constexpr int F = decltype(f)::value;
+    if (dh == 128)
+      cache_write_token_kernel<F, 128><<<(units + 255) / 256, 256, 0, s>>>(
+          k, v, units, Hkv, slot, kc, vc, ksc, vsc, num_slots);
+    else
+      cache_write_token_kernel<F, 64><<<(units + 255) / 256, 256, 0, s>>>(
+          k, v, units, Hkv, slot, kc, vc, ksc, vsc, num_slots);
+  });
+  return hipGetLastError();
+}
+
 // Writes of at most this many tokens take the one-pass kernel above.
 constexpr int64_t kShortWrite = 512;
 

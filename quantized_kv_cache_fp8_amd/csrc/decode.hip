@@ -434,7 +434,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 //   the channel's row in the channel-major tile),
 // and each lane loads its channel's 16 token bytes per block: one 64-lane load
 // is 1 KB of contiguous tile.
-template <int FMT, int DH, int NPW>
+template <int FMT, int DH, int NPW, bool TS>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(KVQ_DECODE_G4_WAVES_PER_EU, KVQ_DECODE_G4_WAVES_PER_EU))) void
 decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
@@ -443,7 +443,8 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
                        const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int NH,
                        int rph_shift, int max_ctx, const float* __restrict__ ks, int per_head,
                        float sm_scale, int nsplit, float* __restrict__ ws_ml,
-                       float* __restrict__ ws_acc) {
+                       float* __restrict__ ws_acc, const uint16_t* __restrict__ ksc,
+                       const uint16_t* __restrict__ vsc) {
   typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
   constexpr int PB = 8 * NPW;     // blocks per split: 4 waves x NPW pairs x 2
   constexpr int HALF = DH / 2;
@@ -487,6 +488,7 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
 
   i32x8 kr[2];
   uint4 vq[2][NC];  // [block of the pair][half]: 16 token codes of channel 64 half + lane
+  float tsk[2], tsv[2];  // per-token-head scales of token c16 of each block (TS)
   auto block_src = [&](int bi) {
     bi = bi < nblk ? bi : nblk - 1;
     return (size_t)clamp_block(btab[bi], num_blocks) * Hkv + h;
@@ -501,6 +503,11 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
         const uint4 a1 = load16(src + HALF * 16);
         kr[e] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                       (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      }
+      if constexpr (TS) {
+        const size_t si = block_src(2 * p + e) * kBlockSize + c16;
+        tsk[e] = (float)__builtin_bit_cast(_Float16, ksc[si]);
+        tsv[e] = (float)__builtin_bit_cast(_Float16, vsc[si]);
       }
     }
   };
@@ -527,7 +534,9 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
                                           (j >> 1) * HALF + 8 * (j & 1));
     qop[j] = __builtin_bit_cast(bf16x8, w);
   }
-  const float zc = sm_scale * ks[per_head ? h : 0] * kLog2e;
+  // with per-token-head scales sK multiplies each score and log2 sV is added
+  // to the exponent that forms P (the row sum l keeps the exponent without it)
+  const float zc = sm_scale * (TS ? 1.0f : ks[per_head ? h : 0]) * kLog2e;
 
   float m_run = kNegBig, l_part = 0.0f;  // this lane's head (S layout)
   f32x4 O[NC];                           // O[c][r]: head r, channel 64 c + lane
@@ -537,7 +546,7 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
 #pragma unroll 1
   for (; p < npair; p += 4) {
     // ---- S for both blocks (bf16 matrix cores, rows replicated per head)
-    float z[2];
+    float z[2], zp[2];  // log2-domain score; exponent of P (z + log2 sV with TS)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       f32x4 S = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -547,13 +556,19 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
             qop[j], codes_to_bf16x8<FMT>((uint32_t)kr[e][2 * j], (uint32_t)kr[e][2 * j + 1]), S,
             0, 0, 0);
       const bool valid = tok0 + (2 * p + e) * kBlockSize + c16 < ctx;
-      z[e] = valid ? S[0] * zc : -__builtin_inff();
+      if constexpr (TS) {
+        z[e] = valid ? S[0] * zc * tsk[e] : -__builtin_inff();
+        zp[e] = valid ? z[e] + __builtin_amdgcn_logf(tsv[e]) : -__builtin_inff();
+      } else {
+        z[e] = valid ? S[0] * zc : -__builtin_inff();
+        zp[e] = z[e];
+      }
     }
     if (p + 4 < npair) load_k(p + 4);  // K registers are free
     // ---- online softmax (lazy max, wave-uniform rare rescale)
-    const bool need = __builtin_fmaxf(z[0], z[1]) > m_run + kLazyTau;
+    const bool need = __builtin_fmaxf(zp[0], zp[1]) > m_run + kLazyTau;
     if (__builtin_amdgcn_ballot_w64(need)) {
-      const float mt = max16(__builtin_fmaxf(z[0], z[1]));
+      const float mt = max16(__builtin_fmaxf(zp[0], zp[1]));
       const bool up = mt > m_run + kLazyTau;
       const float f = up ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
       m_run = up ? mt : m_run;
@@ -569,9 +584,12 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
         }
       }
     }
-    const float p0 = __builtin_amdgcn_exp2f(z[0] - m_run);
-    const float p1 = __builtin_amdgcn_exp2f(z[1] - m_run);
-    l_part += p0 + p1;
+    const float p0 = __builtin_amdgcn_exp2f(zp[0] - m_run);
+    const float p1 = __builtin_amdgcn_exp2f(zp[1] - m_run);
+    if constexpr (TS)
+      l_part += __builtin_amdgcn_exp2f(z[0] - m_run) + __builtin_amdgcn_exp2f(z[1] - m_run);
+    else
+      l_part += p0 + p1;
     if (pub) {
       ptr[head_s * 32 + c16] = (_Float16)p0;
       ptr[head_s * 32 + 16 + c16] = (_Float16)p1;
@@ -700,7 +718,8 @@ __global__ __launch_bounds__(DH) void decode_combine_kernel(
     M = Mn;
   }
   const int h = hq / (Hq / Hkv);
-  const float r = L > 0.0f ? a / L * vs[per_head ? h : 0] : 0.0f;
+  const float sv = vs ? vs[per_head ? h : 0] : 1.0f;  // null: sV already folded into P
+  const float r = L > 0.0f ? a / L * sv : 0.0f;
   const size_t oi = ((size_t)b * Hq + hq) * DH + d;
   if constexpr (BF16)
     reinterpret_cast<uint16_t*>(out)[oi] = (uint16_t)f32_to_bf16_rne(r);
@@ -733,7 +752,9 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
                          const uint8_t* vc, int64_t num_blocks, const int32_t* bt,
                          int max_blocks, const int32_t* ctx, int B, int Hq, int Hkv, int dh,
                          int max_ctx, const float* ks, const float* vs, int fmt, int per_head,
-                         float softmax_scale, const DecodePlan& plan, void* ws, hipStream_t s) {
+                         float softmax_scale, const DecodePlan& plan, void* ws, hipStream_t s,
+                         const uint16_t* ksc, const uint16_t* vsc) {
+  const bool ts = ksc != nullptr;  // per-token-head fp16 scales (groups of <= 4 heads only)
   const int G = Hq / Hkv;
   const int NH = heads_per_group(G);
   float* ml = reinterpret_cast<float*>(ws);
@@ -750,13 +771,14 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
                                                           max_blocks, ctx, Hq, Hkv, NH,       \
                                                           rph_shift, max_ctx, ks, per_head,   \
                                                           sm, plan.nsplit, ml, acc)
-#define KVQ_SPLIT_G4(F, D, N)                                                              \
-  decode_split_g4_kernel<F, D, N><<<grid, 256, lds, s>>>(q, kc, vc, num_blocks, bt, max_blocks,   \
-                                                         ctx, Hq, Hkv, NH, rph_shift, max_ctx,  \
-                                                         ks, per_head, sm, plan.nsplit, ml, acc)
+#define KVQ_SPLIT_G4(F, D, N, T)                                                           \
+  decode_split_g4_kernel<F, D, N, T><<<grid, 256, lds, s>>>(                                 \
+      q, kc, vc, num_blocks, bt, max_blocks, ctx, Hq, Hkv, NH, rph_shift, max_ctx, ks,       \
+      per_head, sm, plan.nsplit, ml, acc, ksc, vsc)
 #define KVQ_SPLIT_HP(F, D, N)                                     \
   do {                                                            \
-    if (nhp_shift <= 2) KVQ_SPLIT_G4(F, D, N);                    \
+    if (ts) KVQ_SPLIT_G4(F, D, N, true);                          \
+    else if (nhp_shift <= 2) KVQ_SPLIT_G4(F, D, N, false);        \
     else if (nhp_shift == 3) KVQ_SPLIT(F, D, N, 2);               \
     else KVQ_SPLIT(F, D, N, 4);                                   \
   } while (0)
@@ -778,7 +800,8 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
   }
   const dim3 cgrid(Hq, B);
 #define KVQ_COMBINE(D, BF)                                                                     \
-  decode_combine_kernel<D, BF><<<cgrid, D, 0, s>>>(out, ml, acc, ctx, Hq, Hkv, max_ctx, vs,    \
+  decode_combine_kernel<D, BF><<<cgrid, D, 0, s>>>(out, ml, acc, ctx, Hq, Hkv, max_ctx,        \
+                                                   ts ? nullptr : vs,                          \
                                                    per_head, plan.part_blocks, plan.nsplit)
   if (dh == 128) {
     if (out_bf16) KVQ_COMBINE(128, true); else KVQ_COMBINE(128, false);

@@ -23,6 +23,13 @@ hipError_t launch_cache_write(const uint16_t* k, const uint16_t* v, int64_t T, i
                               const float* ks, const float* vs, int fmt, int per_head,
                               hipStream_t s);
 
+// Quantize-on-write with one fp16 scale per (token, KV head) for K and for V,
+// computed from the row's own amax; ksc/vsc are [num_blocks][Hkv][16] caches.
+hipError_t launch_cache_write_token(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv,
+                                    int dh, const int64_t* slot, uint8_t* kc, uint8_t* vc,
+                                    uint16_t* ksc, uint16_t* vsc, int64_t num_blocks, int fmt,
+                                    hipStream_t s);
+
 // Split-K decode geometry, shared by the workspace query and the launch.
 struct DecodePlan {
   int part_blocks;  // cache blocks per split
@@ -35,7 +42,8 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
                          const uint8_t* vc, int64_t num_blocks, const int32_t* bt,
                          int max_blocks, const int32_t* ctx, int B, int Hq, int Hkv, int dh,
                          int max_ctx, const float* ks, const float* vs, int fmt, int per_head,
-                         float softmax_scale, const DecodePlan& plan, void* ws, hipStream_t s);
+                         float softmax_scale, const DecodePlan& plan, void* ws, hipStream_t s,
+                         const uint16_t* ksc = nullptr, const uint16_t* vsc = nullptr);
 
 hipError_t launch_prefill(void* out, int out_bf16, const uint16_t* q, const int32_t* cu,
                           int max_q_len, const float* qs, int q_per_head, const uint8_t* kc,

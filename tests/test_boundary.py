@@ -119,3 +119,34 @@ def test_prefill_validation():
     assert st(qg=4) == -3 and st(dh=256) == -3
     assert st(fmt=2) == -3  # INT8 caches: the FP8-domain prefill does not take them
     assert st(maxq=0) == 0
+
+
+def test_token_scale_write_validation():
+    L = K.lib()
+    base = dict(k=FAKE, v=FAKE, T=4, Hkv=2, dh=128, slots=FAKE, kc=FAKE, vc=FAKE, ksc=FAKE,
+                vsc=FAKE, nb=8, bs=16, fmt=0, stream=None)
+    def st(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.kvq_cache_write_token_scales(*a.values())
+    assert st(ksc=None) == -1 and st(vsc=None) == -1 and st(slots=None) == -1
+    assert st(T=-1) == -2 and st(nb=0) == -2 and st(T=1 << 28, Hkv=8) == -2
+    assert st(dh=96) == -3 and st(bs=32) == -3 and st(fmt=3) == -3
+    assert st(ksc=FAKE + 1) == -3 and st(vc=FAKE + 8) == -3  # misaligned
+    assert st(T=0) == 0
+
+
+def test_token_scale_decode_validation():
+    L = K.lib()
+    base = dict(out=FAKE, odt=0, q=FAKE, kc=FAKE, vc=FAKE, ksc=FAKE, vsc=FAKE, nb=10, bt=FAKE,
+                mb=4, cl=FAKE, B=2, Hq=8, Hkv=2, dh=128, bs=16, maxctx=64, fmt=0, sm=0.0,
+                ws=FAKE, wsb=0, stream=None)
+    def st(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.kvq_decode_attn_token_scales(*a.values())
+    assert st(ksc=None) == -1 and st(vsc=None) == -1 and st(ws=None, wsb=1 << 20) == -1
+    assert st(Hq=6, Hkv=4) == -2 and st(maxctx=65) == -2
+    assert st(Hq=16, Hkv=2) == -3  # groups of more than 4 query heads
+    assert st(fmt=3) == -3 and st(dh=80) == -3 and st(vsc=FAKE + 1) == -3
+    assert st(wsb=16) == -4

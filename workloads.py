@@ -121,6 +121,15 @@ def make_kv(g: np.random.Generator, paging: Paging, Hkv: int, dh: int,
     return KVBatch(k, v, slots, offs)
 
 
+def scale_rows(g: np.random.Generator, x: np.ndarray, lo: float, hi: float) -> np.ndarray:
+    """bf16 [T, H, dh] with every (token, head) row multiplied by its own
+    log-uniform factor in [lo, hi] (rows of very different magnitudes, the case
+    per-token scales are for); re-rounded to bf16."""
+    T, H, _ = x.shape
+    f = log_uniform(g, T * H, lo, hi).reshape(T, H, 1)
+    return f32_to_bf16_bits(bf16_bits_to_f32(x) * f)
+
+
 @dataclass
 class DecodeWorkload:
     name: str
