@@ -39,6 +39,8 @@ namespace kvq {
 constexpr int kBs = 16;     // tokens per cache block
 constexpr int kChunk = 64;  // tokens per workgroup (one wave marks the runs)
 constexpr int kRowDw = kChunk / 4 + 1;  // LDS V-tile row: 16 dwords of codes + 1 pad
+// Writes of at most this many tokens take a one-pass kernel (no LDS, no barrier).
+constexpr int64_t kShortWrite = 512;
 
 template <int FMT>
 __device__ __forceinline__ uint32_t quant4(uint2 w, float s, float rs) {
@@ -46,11 +48,52 @@ __device__ __forceinline__ uint32_t quant4(uint2 w, float s, float rs) {
                    quotient(bf16lo(w.y), s, rs), quotient(bf16hi(w.y), s, rs));
 }
 
-template <int FMT, int DH>
+// Per-token-head scales (one fp16 scale per (token, head) for K and for V,
+// stored beside the codes in [num_blocks][Hkv][bs] scale caches).  The lanes
+// that share a (token, head) row -- aligned consecutive lanes, each holding a
+// few channels -- reduce the row's amax over |x| bit patterns (an exact
+// integer max in which NaN patterns sort above +Inf), derive
+//   s = fl16(clamp(fl32(amax / fmax), 2^-24, 65504))   (1.0 for amax 0, Inf, NaN)
+// and quantize their channels with it.  Long writes take the LDS-staged kernel
+// below with TS set (a row is DH / 4 lanes of 4 channels); short ones take
+// cache_write_token_kernel (a row is DH / 16 lanes of 16 channels).
+
+// largest |x| bit pattern (sign cleared) among 8 bf16 values
+__device__ __forceinline__ uint32_t absmax_bits8(uint4 w) {
+  const uint32_t v[4] = {w.x & 0x7fff7fffu, w.y & 0x7fff7fffu, w.z & 0x7fff7fffu,
+                         w.w & 0x7fff7fffu};
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = v[i] & 0xffffu, hi = v[i] >> 16;
+    r = lo > r ? lo : r;
+    r = hi > r ? hi : r;
+  }
+  return r;
+}
+
+// largest |x| bit pattern among 4 bf16 values
+__device__ __forceinline__ uint32_t absmax_bits4(uint2 w) {
+  const uint32_t a = w.x & 0x7fff7fffu, b = w.y & 0x7fff7fffu;
+  const uint32_t m0 = (a & 0xffffu) > (a >> 16) ? (a & 0xffffu) : (a >> 16);
+  const uint32_t m1 = (b & 0xffffu) > (b >> 16) ? (b & 0xffffu) : (b >> 16);
+  return m0 > m1 ? m0 : m1;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint16_t scale16_from_amax_bits(uint32_t abits) {
+  if (abits == 0 || abits >= 0x7f80u) return 0x3C00;  // 0, Inf or NaN -> 1.0
+  float s = __fdiv_rn(__uint_as_float(abits << 16), FmtTraits<FMT>::kMax);
+  s = __builtin_amdgcn_fmed3f(s, 0x1p-24f, 65504.0f);
+  return __builtin_bit_cast(uint16_t, (_Float16)s);  // round to nearest even
+}
+
+template <int FMT, int DH, bool TS>
 __global__ __launch_bounds__(256) void cache_write_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t T, int Hkv,
     const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
-    int64_t num_slots, const float* __restrict__ ks, const float* __restrict__ vs, int per_head) {
+    int64_t num_slots, const float* __restrict__ ks, const float* __restrict__ vs, int per_head,
+    uint16_t* __restrict__ ksc, uint16_t* __restrict__ vsc) {
   constexpr int kCq = DH / 4;  // channel quads per token row
   __shared__ int64_t s_slot[kChunk];
   __shared__ uint32_t s_run[kChunk];  // token index | run length << 8, compacted
@@ -58,6 +101,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   __shared__ uint32_t s_vt[DH * kRowDw];
   constexpr int kKRow = DH / 4 + 4;  // LDS K-tile row (dwords): DH codes + 16 B pad
   __shared__ __attribute__((aligned(16))) uint32_t s_kt[kChunk * kKRow];
+  __shared__ uint16_t s_sc[2][kChunk];  // per-token-head scales of the chunk (TS)
 
   const int h = (int)(blockIdx.x % (uint32_t)Hkv);
   const int64_t t0 = (int64_t)(blockIdx.x / (uint32_t)Hkv) * kChunk;
@@ -104,8 +148,12 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     if (tid == 0) s_nrun = __builtin_popcountll(mask);
   }
 
-  const float sk = ks[per_head ? h : 0], sv = vs[per_head ? h : 0];
-  const float rk = recip_rn(sk), rv = recip_rn(sv);
+  float sk = 1.0f, sv = 1.0f;
+  if constexpr (!TS) {
+    sk = ks[per_head ? h : 0];
+    sv = vs[per_head ? h : 0];
+  }
+  float rk = recip_rn(sk), rv = recip_rn(sv);
 #pragma unroll
   for (int jb = 0; jb < kJobs; ++jb) {
     const int job = tid + 256 * jb;
@@ -113,6 +161,26 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     uint32_t cv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      if constexpr (TS) {
+        // the kCq aligned consecutive lanes of token 4 tq + j hold its row
+        uint32_t ak = absmax_bits4(wk[jb][j]), av = absmax_bits4(wv[jb][j]);
+#pragma unroll
+        for (int o = 1; o < kCq; o <<= 1) {
+          const uint32_t xk = __shfl_xor(ak, o), xv = __shfl_xor(av, o);
+          ak = ak > xk ? ak : xk;
+          av = av > xv ? av : xv;
+        }
+        const uint16_t k16 = scale16_from_amax_bits<FMT>(ak);
+        const uint16_t v16 = scale16_from_amax_bits<FMT>(av);
+        if (cq == 0) {
+          s_sc[0][4 * tq + j] = k16;
+          s_sc[1][4 * tq + j] = v16;
+        }
+        sk = (float)__builtin_bit_cast(_Float16, k16);
+        sv = (float)__builtin_bit_cast(_Float16, v16);
+        rk = recip_rn(sk);
+        rv = recip_rn(sv);
+      }
       cv[j] = quant4<FMT>(wv[jb][j], sv, rv);
       s_kt[(4 * tq + j) * kKRow + cq] = quant4<FMT>(wk[jb][j], sk, rk);
     }
@@ -129,6 +197,14 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   }
   __syncthreads();
 
+  if constexpr (TS) {
+    if (tid < kChunk && s_slot[tid] >= 0) {
+      const int64_t sl = s_slot[tid];
+      const size_t i = (size_t)((sl >> 4) * Hkv + h) * kBs + (sl & (kBs - 1));
+      ksc[i] = s_sc[0][tid];
+      vsc[i] = s_sc[1][tid];
+    }
+  }
   // K: 16 code bytes per (token, chunk); tokens fastest across threads
   for (int job = tid; job < kChunk * (DH / 16); job += 256) {
     const int t = job % kChunk, q = job / kChunk;
@@ -197,35 +273,6 @@ __global__ __launch_bounds__(256) void cache_write_short_kernel(
   for (int c = 0; c < 16; ++c) vd[c * kBs] = (uint8_t)(vq[c >> 2] >> (8 * (c & 3)));
 }
 
-// Per-token-head scales (one fp16 scale per (token, head) for K and for V,
-// stored beside the codes in [num_blocks][Hkv][bs] scale caches): the lanes
-// that share a (token, head) row -- DH / 16 consecutive lanes, one 16-channel
-// chunk each -- reduce the row's amax over |x| bit patterns (an exact integer
-// max in which NaN patterns sort above +Inf), derive
-//   s = fl16(clamp(fl32(amax / fmax), 2^-24, 65504))   (1.0 for amax 0, Inf, NaN)
-// and quantize their chunk with it.
-// largest |x| bit pattern (sign cleared) among 8 bf16 values
-__device__ __forceinline__ uint32_t absmax_bits8(uint4 w) {
-  const uint32_t v[4] = {w.x & 0x7fff7fffu, w.y & 0x7fff7fffu, w.z & 0x7fff7fffu,
-                         w.w & 0x7fff7fffu};
-  uint32_t r = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = v[i] & 0xffffu, hi = v[i] >> 16;
-    r = lo > r ? lo : r;
-    r = hi > r ? hi : r;
-  }
-  return r;
-}
-
-template <int FMT>
-__device__ __forceinline__ uint16_t scale16_from_amax_bits(uint32_t abits) {
-  if (abits == 0 || abits >= 0x7f80u) return 0x3C00;  // 0, Inf or NaN -> 1.0
-  float s = __fdiv_rn(__uint_as_float(abits << 16), FmtTraits<FMT>::kMax);
-  s = __builtin_amdgcn_fmed3f(s, 0x1p-24f, 65504.0f);
-  return __builtin_bit_cast(uint16_t, (_Float16)s);  // round to nearest even
-}
-
 template <int FMT, int DH>
 __global__ __launch_bounds__(256) void cache_write_token_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint32_t units, int Hkv,
@@ -286,20 +333,27 @@ hipError_t launch_cache_write_token(const uint16_t* k, const uint16_t* v, int64_
   if (T == 0) return hipSuccess;
   const int64_t num_slots = num_blocks * kBs;
   const uint32_t units = (uint32_t)(T * Hkv * (dh / 16));
+  const uint32_t grid = (uint32_t)(((T + kChunk - 1) / kChunk) * Hkv);
   dispatch_fmt(fmt, [&](auto f) {
     constexpr int F = decltype(f)::value;
-    if (dh == 128)
+    if (T > kShortWrite) {  // the LDS-staged kernel, one scale per token row
+      if (dh == 128)
+        cache_write_kernel<F, 128, true><<<grid, 256, 0, s>>>(
+            k, v, T, Hkv, slot, kc, vc, num_slots, nullptr, nullptr, 0, ksc, vsc);
+      else
+        cache_write_kernel<F, 64, true><<<grid, 256, 0, s>>>(
+            k, v, T, Hkv, slot, kc, vc, num_slots, nullptr, nullptr, 0, ksc, vsc);
+    } else if (dh == 128) {
       cache_write_token_kernel<F, 128><<<(units + 255) / 256, 256, 0, s>>>(
           k, v, units, Hkv, slot, kc, vc, ksc, vsc, num_slots);
-    else
+    } else {
       cache_write_token_kernel<F, 64><<<(units + 255) / 256, 256, 0, s>>>(
           k, v, units, Hkv, slot, kc, vc, ksc, vsc, num_slots);
+    }
   });
   return hipGetLastError();
 }
 
-// Writes of at most this many tokens take the one-pass kernel above.
-constexpr int64_t kShortWrite = 512;
 
 template <int FMT, int DH>
 void launch_write(int64_t T, int Hkv, const uint16_t* k, const uint16_t* v, const int64_t* slot,
@@ -312,8 +366,8 @@ void launch_write(int64_t T, int Hkv, const uint16_t* k, const uint16_t* v, cons
     return;
   }
   const uint32_t grid = (uint32_t)(((T + kChunk - 1) / kChunk) * Hkv);
-  cache_write_kernel<FMT, DH><<<grid, 256, 0, s>>>(k, v, T, Hkv, slot, kc, vc, num_slots, ks, vs,
-                                                    per_head);
+  cache_write_kernel<FMT, DH, false><<<grid, 256, 0, s>>>(k, v, T, Hkv, slot, kc, vc, num_slots,
+                                                           ks, vs, per_head, nullptr, nullptr);
 }
 
 hipError_t launch_cache_write(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv, int dh,

@@ -61,6 +61,11 @@ namespace kvq {
 #ifndef KVQ_DECODE_G4_WAVES_PER_EU
 #define KVQ_DECODE_G4_WAVES_PER_EU 5
 #endif
+// ... and of its per-token-head-scale variant (4 more live registers: at 5
+// waves it spills)
+#ifndef KVQ_DECODE_TS_WAVES_PER_EU
+#define KVQ_DECODE_TS_WAVES_PER_EU 4
+#endif
 #ifndef KVQ_DECODE_WAVES_PER_EU
 #define KVQ_DECODE_WAVES_PER_EU 4
 #endif
@@ -436,7 +441,9 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 // is 1 KB of contiguous tile.
 template <int FMT, int DH, int NPW, bool TS>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(KVQ_DECODE_G4_WAVES_PER_EU, KVQ_DECODE_G4_WAVES_PER_EU))) void
+__attribute__((amdgpu_waves_per_eu(TS ? KVQ_DECODE_TS_WAVES_PER_EU : KVQ_DECODE_G4_WAVES_PER_EU,
+                                    TS ? KVQ_DECODE_TS_WAVES_PER_EU : KVQ_DECODE_G4_WAVES_PER_EU)))
+void
 decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
                        const uint8_t* __restrict__ vc, int64_t num_blocks,
                        const int32_t* __restrict__ bt, int max_blocks,
@@ -488,7 +495,7 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
 
   i32x8 kr[2];
   uint4 vq[2][NC];  // [block of the pair][half]: 16 token codes of channel 64 half + lane
-  float tsk[2], tsv[2];  // per-token-head scales of token c16 of each block (TS)
+  uint32_t tsc[2];  // fp16 scales of token c16 of each block, sK | sV << 16 (TS)
   auto block_src = [&](int bi) {
     bi = bi < nblk ? bi : nblk - 1;
     return (size_t)clamp_block(btab[bi], num_blocks) * Hkv + h;
@@ -506,8 +513,7 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
       }
       if constexpr (TS) {
         const size_t si = block_src(2 * p + e) * kBlockSize + c16;
-        tsk[e] = (float)__builtin_bit_cast(_Float16, ksc[si]);
-        tsv[e] = (float)__builtin_bit_cast(_Float16, vsc[si]);
+        tsc[e] = (uint32_t)ksc[si] | ((uint32_t)vsc[si] << 16);
       }
     }
   };
@@ -557,8 +563,9 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
             0, 0, 0);
       const bool valid = tok0 + (2 * p + e) * kBlockSize + c16 < ctx;
       if constexpr (TS) {
-        z[e] = valid ? S[0] * zc * tsk[e] : -__builtin_inff();
-        zp[e] = valid ? z[e] + __builtin_amdgcn_logf(tsv[e]) : -__builtin_inff();
+        const f16x2 sc = __builtin_bit_cast(f16x2, tsc[e]);
+        z[e] = valid ? S[0] * zc * (float)sc[0] : -__builtin_inff();
+        zp[e] = valid ? z[e] + __builtin_amdgcn_logf((float)sc[1]) : -__builtin_inff();
       } else {
         z[e] = valid ? S[0] * zc : -__builtin_inff();
         zp[e] = z[e];

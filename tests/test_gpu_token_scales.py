@@ -39,15 +39,20 @@ def u16(t):
     return to_np(t).view(np.uint16)
 
 
+# token counts that take the one-pass kernel (<= 512) and the LDS-staged one
+CONTEXTS = {"short": [301, 17, 1, 64], "long": [301, 17, 1, 64, 700, 33]}
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("dh", [64, 128])
-def test_write_matches_oracle(fmt, dh):
+@pytest.mark.parametrize("path", ["short", "long"])
+def test_write_matches_oracle(fmt, dh, path):
     """Rows whose magnitudes span 1e-9 .. 1e10 (scales clamped at both ends of
     fp16), all-zero rows, rows holding NaN / Inf, padding and out-of-pool
-    slots; the token count is not a multiple of the launch's lane groups."""
+    slots; token counts that are not multiples of the launch's tiles."""
     g = W.rng(500 + dh)
     Hkv, bs = 3, 16
-    paging = W.make_paging(g, [301, 17, 1, 64], bs)
+    paging = W.make_paging(g, CONTEXTS[path], bs)
     kv = W.make_kv(g, paging, Hkv, dh, k_outliers=(3, 20.0))
     k = W.scale_rows(g, kv.k, 1e-9, 1e10)
     v = W.scale_rows(g, kv.v, 1e-9, 1e10)
