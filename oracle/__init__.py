@@ -9,6 +9,7 @@ ctypes marshalling layer, written from the definitions on the pages:
   textbook chapter): M_KV formula and worked example (10.4.1), write / read /
   attention equations (10.4.2), granularity and metadata table (10.4.3), FP8
   cast path (10.4.5).
+  KIVI's per-channel K / per-token V 2-bit grouping and residual (10.4.4).
 * "vLLM FP8 量化 KV Cache 完整指南" (vLLM FP8 KV-cache guide): formats, scale
   shapes per granularity, default scale 1.0, Q quantized in the FP8-domain
   (FA3) attention path.
@@ -71,6 +72,13 @@ def lib() -> ctypes.CDLL:
         L.orc_cache_write_token.argtypes = [P, P, i64, i32, i32, P, P, P, P, P, i64, i32, i32]
         L.orc_decode_token_rows.argtypes = [P, P, i32, P, P, P, P, P, P, i32, P, i32, i32, i32,
                                             i32, i32, f32]
+        L.orc_kivi_group.argtypes = [P, i32, P, P, P]
+        L.orc_kivi_k_pos.argtypes = [i32, i32, P, P]
+        L.orc_kivi_v_pos.argtypes = [i32, i32, P, P]
+        L.orc_kivi_quantize.argtypes = [P, P, i64, i32, P, P, i64]
+        L.orc_kivi_dequant_tile.argtypes = [P, P, P]
+        L.orc_kivi_decode_rows.argtypes = [P, P, i32, P, P, P, i32, P, P, P, P, i32, i32, i32,
+                                           f32]
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = i32
         L.orc_fp8_max.argtypes = [i32]
@@ -357,4 +365,78 @@ def decode_token_rows(rows, q_bf16, k_cache, v_cache, k_scale_cache, v_scale_cac
     lib().orc_decode_token_rows(_p(out), _p(rows), rows.shape[0], _p(q), _p(k_cache),
                                 _p(v_cache), _p(k_scale_cache), _p(v_scale_cache), _p(bt),
                                 bt.shape[1], _p(cl), Hq, Hkv, dh, bs, fmt, softmax_scale)
+    return out
+
+
+# ------------------------------------------------------------------ KIVI 2-bit
+KIVI_G = 32        # tokens per K group and per cache block; channels per V group
+KIVI_DH = 128
+KIVI_TILE = 3072   # bytes per (block, head) tile
+
+
+def kivi_group(x) -> tuple[int, int, np.ndarray]:
+    """(s, z) fp16 bits and 2-bit codes of one set of values (fp32)."""
+    x = np.ascontiguousarray(x, np.float32)
+    s16, z16 = ctypes.c_uint16(), ctypes.c_uint16()
+    codes = np.zeros(x.size, np.uint8)
+    lib().orc_kivi_group(_p(x), x.size, ctypes.byref(s16), ctypes.byref(z16), _p(codes))
+    return s16.value, z16.value, codes
+
+
+def kivi_k_pos(t: int, c: int) -> tuple[int, int]:
+    b, i = ctypes.c_int(), ctypes.c_int()
+    lib().orc_kivi_k_pos(t, c, ctypes.byref(b), ctypes.byref(i))
+    return b.value, i.value
+
+
+def kivi_v_pos(t: int, c: int) -> tuple[int, int]:
+    b, i = ctypes.c_int(), ctypes.c_int()
+    lib().orc_kivi_v_pos(t, c, ctypes.byref(b), ctypes.byref(i))
+    return b.value, i.value
+
+
+def kivi_cache_shape(num_blocks: int, Hkv: int) -> tuple:
+    """uint8 [num_blocks][Hkv][3072]: one 32-token tile per (block, head)."""
+    return (num_blocks, Hkv, KIVI_TILE)
+
+
+def kivi_quantize(k_bf16, v_bf16, group_blocks, cache: np.ndarray) -> None:
+    """Quantize whole 32-token groups (k, v bf16 [n_groups * 32, Hkv, 128]) into
+    the blocks group_blocks[g] of the KIVI cache."""
+    k, v = _u16(k_bf16), _u16(v_bf16)
+    T, Hkv, dh = k.shape
+    assert dh == KIVI_DH and T % KIVI_G == 0 and v.shape == k.shape
+    assert cache.shape[1:] == (Hkv, KIVI_TILE) and cache.dtype == np.uint8
+    gb = np.ascontiguousarray(group_blocks, np.int32)
+    assert gb.size == T // KIVI_G
+    lib().orc_kivi_quantize(_p(k), _p(v), gb.size, Hkv, _p(gb), _p(cache), cache.shape[0])
+
+
+def kivi_dequant_tile(tile: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """k_hat, v_hat fp64 [32, 128] of one (block, head) tile."""
+    t = np.ascontiguousarray(tile, np.uint8)
+    assert t.size == KIVI_TILE
+    kh = np.zeros((KIVI_G, KIVI_DH))
+    vh = np.zeros((KIVI_G, KIVI_DH))
+    lib().orc_kivi_dequant_tile(_p(t), _p(kh), _p(vh))
+    return kh, vh
+
+
+def kivi_decode_rows(rows, q_bf16, cache, block_tables, quant_groups, res_k, res_v, res_lens,
+                     softmax_scale: float = 0.0) -> np.ndarray:
+    """Decode output (fp64 [n, 128]) of the listed (b, hq) rows over a KIVI cache
+    plus the bf16 residual (res_k / res_v [B, Hkv, R, 128])."""
+    q = _u16(q_bf16)
+    B, Hq, dh = q.shape
+    rk, rv = _u16(res_k), _u16(res_v)
+    _, Hkv, R, _ = rk.shape
+    rows = np.ascontiguousarray(rows, np.int32).reshape(-1, 2)
+    bt = np.ascontiguousarray(block_tables, np.int32)
+    qg = np.ascontiguousarray(quant_groups, np.int32)
+    rl = np.ascontiguousarray(res_lens, np.int32)
+    c = np.ascontiguousarray(cache, np.uint8)
+    out = np.zeros((rows.shape[0], dh), np.float64)
+    lib().orc_kivi_decode_rows(_p(out), _p(rows), rows.shape[0], _p(q), _p(c), _p(bt),
+                               bt.shape[1], _p(qg), _p(rk), _p(rv), _p(rl), R, Hq, Hkv,
+                               softmax_scale)
     return out

@@ -578,3 +578,197 @@ uint64_t orc_kv_cache_bytes(int L, int B, int Hkv, int64_t S, int dh, int bits_p
 uint64_t orc_token_head_bytes(int dh, int bits_per_elem, int scale_bytes) {
   return 2ull * (uint64_t)dh * (uint64_t)bits_per_elem / 8ull + 2ull * (uint64_t)scale_bytes;
 }
+
+/* ---- KIVI-style asymmetric 2-bit KV (textbook 10.4.4: K grouped per channel
+ * over G tokens, V per token over groups of channels; a high-precision residual
+ * keeps the newest tokens unquantized).  The pages give the axes only; the
+ * asymmetric codec is read as the plain min/max one:
+ *   s = fl16(min(fl32(fl32(max - min) / 3), 65504)), z = fl16(clamp(min, +-65504))
+ *   code = clip(round-half-even(fl32(fl32(x - z) / s)), 0, 3), or 0 when s == 0
+ *   x_hat = code * s + z
+ * over each set of 32 values (K: one channel of a 32-token group; V: one
+ * 32-channel group of one token).  A set holding an Inf or NaN gets s = z = 0
+ * (every code 0).  fp16 rounding is to nearest even.
+ * Layout (this library's design; dh = 128): the quantized part is paged in
+ * 32-token blocks, one K group per block, and each (block, head) tile is 3072
+ * bytes: K codes [0, 1024), K scales (fp16, per channel) [1024, 1280), K zeros
+ * [1280, 1536), V codes [1536, 2560), V (scale, zero) pairs per (token,
+ * 32-channel group) [2560, 3072).  Code positions are given by kivi_k_pos and
+ * kivi_v_pos below.  The residual holds the newest tokens in bf16, token-major
+ * [B][Hkv][R][dh] for K and for V, oldest first. ---- */
+
+#define KIVI_G 32
+#define KIVI_DH 128
+#define KIVI_TILE 3072
+
+static uint16_t f16_bits_signed(double x) { /* |x| <= 65504, round to nearest even */
+  if (x < 0) return (uint16_t)(0x8000u | f16_bits_rne(-x));
+  return f16_bits_rne(x);
+}
+
+/* (s, z) fp16 bits of a set of n finite-or-not values */
+static void kivi_params(const float* x, int n, uint16_t* s16, uint16_t* z16) {
+  float mn = INFINITY, mx = -INFINITY;
+  for (int i = 0; i < n; ++i) {
+    if (!isfinite(x[i])) { *s16 = 0; *z16 = 0; return; }
+    if (x[i] < mn) mn = x[i];
+    if (x[i] > mx) mx = x[i];
+  }
+  float range = (float)((double)mx - (double)mn);   /* fl32(max - min) */
+  float s = (float)((double)range / 3.0);           /* fl32(range / 3) */
+  double sd = s > 65504.0f ? 65504.0 : (double)s;
+  double zd = mn < -65504.0f ? -65504.0 : (mn > 65504.0f ? 65504.0 : (double)mn);
+  *s16 = f16_bits_rne(sd);
+  *z16 = f16_bits_signed(zd);
+}
+
+static uint8_t kivi_code(float x, uint16_t s16, uint16_t z16) {
+  double s = orc_f16_to_double(s16);
+  if (s == 0.0) return 0;
+  float d = (float)((double)x - orc_f16_to_double(z16));  /* fl32(x - z) */
+  float q = (float)((double)d / s);                       /* fl32(d / s) */
+  double r = rint((double)q);
+  if (r < 0.0) r = 0.0;
+  if (r > 3.0) r = 3.0;
+  return (uint8_t)r;
+}
+
+/* One set: its (s, z) and codes (for tests). */
+void orc_kivi_group(const float* x, int n, uint16_t* s16, uint16_t* z16, uint8_t* codes) {
+  kivi_params(x, n, s16, z16);
+  for (int i = 0; i < n; ++i) codes[i] = kivi_code(x[i], *s16, *z16);
+}
+
+/* byte and bit offset of the code of token t (0..31), channel c (0..127) in a tile */
+void orc_kivi_k_pos(int t, int c, int* byte, int* bit) {
+  int th = t / 16, c16 = t % 16, j = c / 32, g4 = (c % 32) / 8, i = c % 8;
+  int lane = 16 * g4 + c16;
+  *byte = 16 * lane + 8 * th + 4 * (j / 2) + i / 2;
+  *bit = 4 * (i % 2) + 2 * (j % 2);
+}
+
+void orc_kivi_v_pos(int t, int c, int* byte, int* bit) {
+  int lane = c % 64, hc = c / 64, w = t / 16, sl = (t % 16) / 4, u = t % 4;
+  *byte = 1536 + 16 * lane + 8 * hc + 4 * w + 2 * (sl % 2) + u / 2;
+  *bit = 4 * (u % 2) + 2 * (sl / 2);
+}
+
+static void put_code(uint8_t* tile, int byte, int bit, uint8_t code) {
+  tile[byte] = (uint8_t)((tile[byte] & ~(3u << bit)) | ((unsigned)code << bit));
+}
+
+static uint8_t get_code(const uint8_t* tile, int byte, int bit) {
+  return (uint8_t)((tile[byte] >> bit) & 3u);
+}
+
+static void put_u16(uint8_t* p, uint16_t v) {
+  p[0] = (uint8_t)(v & 0xff);
+  p[1] = (uint8_t)(v >> 8);
+}
+
+static uint16_t get_u16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* Quantize whole 32-token groups: k, v bf16 [n_groups * 32][Hkv][128]; group g
+ * goes to block group_blocks[g] (skipped when outside [0, num_blocks)). */
+void orc_kivi_quantize(const uint16_t* k, const uint16_t* v, int64_t n_groups, int Hkv,
+                       const int32_t* group_blocks, uint8_t* cache, int64_t num_blocks) {
+#pragma omp parallel for schedule(static)
+  for (int64_t g = 0; g < n_groups; ++g) {
+    int64_t blk = group_blocks[g];
+    if (blk < 0 || blk >= num_blocks) continue;
+    for (int h = 0; h < Hkv; ++h) {
+      uint8_t* tile = cache + (blk * Hkv + h) * KIVI_TILE;
+      float x[KIVI_G];
+      uint16_t s16, z16;
+      for (int c = 0; c < KIVI_DH; ++c) { /* K: one channel over the group's tokens */
+        for (int t = 0; t < KIVI_G; ++t)
+          x[t] = orc_bf16_to_f32(k[((g * KIVI_G + t) * Hkv + h) * KIVI_DH + c]);
+        kivi_params(x, KIVI_G, &s16, &z16);
+        put_u16(tile + 1024 + 2 * c, s16);
+        put_u16(tile + 1280 + 2 * c, z16);
+        for (int t = 0; t < KIVI_G; ++t) {
+          int byte, bit;
+          orc_kivi_k_pos(t, c, &byte, &bit);
+          put_code(tile, byte, bit, kivi_code(x[t], s16, z16));
+        }
+      }
+      for (int t = 0; t < KIVI_G; ++t) { /* V: one token over 32-channel groups */
+        for (int gc = 0; gc < KIVI_DH / 32; ++gc) {
+          for (int i = 0; i < 32; ++i)
+            x[i] = orc_bf16_to_f32(v[((g * KIVI_G + t) * Hkv + h) * KIVI_DH + 32 * gc + i]);
+          kivi_params(x, 32, &s16, &z16);
+          put_u16(tile + 2560 + 16 * t + 4 * gc, s16);
+          put_u16(tile + 2560 + 16 * t + 4 * gc + 2, z16);
+          for (int i = 0; i < 32; ++i) {
+            int byte, bit;
+            orc_kivi_v_pos(t, 32 * gc + i, &byte, &bit);
+            put_code(tile, byte, bit, kivi_code(x[i], s16, z16));
+          }
+        }
+      }
+    }
+  }
+}
+
+/* Dequantized tile of one (block, head): k_hat, v_hat fp64 [32][128]. */
+void orc_kivi_dequant_tile(const uint8_t* tile, double* kh, double* vh) {
+  for (int c = 0; c < KIVI_DH; ++c) {
+    double s = orc_f16_to_double(get_u16(tile + 1024 + 2 * c));
+    double z = orc_f16_to_double(get_u16(tile + 1280 + 2 * c));
+    for (int t = 0; t < KIVI_G; ++t) {
+      int byte, bit;
+      orc_kivi_k_pos(t, c, &byte, &bit);
+      kh[t * KIVI_DH + c] = (double)get_code(tile, byte, bit) * s + z;
+    }
+  }
+  for (int t = 0; t < KIVI_G; ++t) {
+    for (int c = 0; c < KIVI_DH; ++c) {
+      const uint8_t* m = tile + 2560 + 16 * t + 4 * (c / 32);
+      double s = orc_f16_to_double(get_u16(m)), z = orc_f16_to_double(get_u16(m + 2));
+      int byte, bit;
+      orc_kivi_v_pos(t, c, &byte, &bit);
+      vh[t * KIVI_DH + c] = (double)get_code(tile, byte, bit) * s + z;
+    }
+  }
+}
+
+/* Decode rows (b, hq) over a KIVI cache: the sequence's keys are its
+ * quant_groups[b] quantized groups (block_tables[b][0..]) followed by its
+ * res_lens[b] residual tokens, in position order; attention as textbook
+ * 10.4.2 on the dequantized values.  out: fp64 [n][128]. */
+void orc_kivi_decode_rows(double* out, const int32_t* rows, int n, const uint16_t* q,
+                          const uint8_t* cache, const int32_t* block_tables, int max_blocks,
+                          const int32_t* quant_groups, const uint16_t* res_k,
+                          const uint16_t* res_v, const int32_t* res_lens, int R, int Hq, int Hkv,
+                          float softmax_scale) {
+  int G = Hq / Hkv;
+  double sm = default_scale(softmax_scale, KIVI_DH);
+#pragma omp parallel for schedule(dynamic)
+  for (int i = 0; i < n; ++i) {
+    int b = rows[2 * i], hq = rows[2 * i + 1], h = hq / G;
+    int ng = quant_groups[b], nr = res_lens[b];
+    int nk = ng * KIVI_G + nr;
+    double* kk = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1) * KIVI_DH);
+    double* vv = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1) * KIVI_DH);
+    for (int g = 0; g < ng; ++g) {
+      int64_t blk = block_tables[(int64_t)b * max_blocks + g];
+      orc_kivi_dequant_tile(cache + (blk * Hkv + h) * KIVI_TILE, kk + (int64_t)g * KIVI_G * KIVI_DH,
+                            vv + (int64_t)g * KIVI_G * KIVI_DH);
+    }
+    for (int r = 0; r < nr; ++r)
+      for (int d = 0; d < KIVI_DH; ++d) {
+        int64_t src = (((int64_t)b * Hkv + h) * R + r) * KIVI_DH + d;
+        kk[((int64_t)ng * KIVI_G + r) * KIVI_DH + d] = orc_bf16_to_f32(res_k[src]);
+        vv[((int64_t)ng * KIVI_G + r) * KIVI_DH + d] = orc_bf16_to_f32(res_v[src]);
+      }
+    double qd[KIVI_DH];
+    for (int d = 0; d < KIVI_DH; ++d)
+      qd[d] = (double)orc_bf16_to_f32(q[((int64_t)b * Hq + hq) * KIVI_DH + d]);
+    if (nk > 0)
+      orc_dense_attn(out + (int64_t)i * KIVI_DH, qd, kk, vv, 1, nk, KIVI_DH, 0, sm);
+    else
+      for (int d = 0; d < KIVI_DH; ++d) out[(int64_t)i * KIVI_DH + d] = 0.0;
+    free(kk);
+    free(vv);
+  }
+}
