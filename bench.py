@@ -57,14 +57,20 @@ def parse():
 # source it was measured on.
 TRAFFIC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "decode_llama3_8b_layer_hbm_traffic.md")
-DECODE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantized_kv_cache_fp8_amd",
-                          "csrc", "decode.hip")
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantized_kv_cache_fp8_amd",
+                    "csrc")
+# the sources the headline decode kernels are compiled from
+DECODE_SRCS = ("decode.hip", "attn_common.hpp", "codec.hpp")
 
 
 def decode_source_digest() -> str:
+    """sha256 over the decode kernels' sources, in DECODE_SRCS order."""
     import hashlib
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in DECODE_SRCS:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():

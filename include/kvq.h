@@ -218,6 +218,61 @@ kvq_status kvq_decode_attn_token_scales(void* out, kvq_out out_dtype, const void
                                         float softmax_scale, void* workspace, size_t ws_bytes,
                                         kvq_stream stream);
 
+/* ---------------------------------------------------------------- KIVI 2-bit
+ * KIVI-style asymmetric 2-bit KV ([T] 10.4.4: K quantized per channel within
+ * groups of G tokens, V per token within groups of channels; the newest
+ * tokens stay unquantized in a high-precision residual and are compressed in
+ * batches).  Here G = 32 tokens, V groups are 32 channels, dh = 128.  For each
+ * set of 32 values (K: one channel of a 32-token group; V: one 32-channel
+ * group of one token):
+ *   s = fl16(min(fl32(fl32(max - min) / 3), 65504)), z = fl16(clamp(min, +-65504))
+ *   code = clip(round-half-even(fl32(fl32(x - z) / s)), 0, 3)   (0 if s == 0)
+ *   x_hat = code * s + z;  a set holding an Inf or NaN stores s = z = 0.
+ * (fp16 rounding is to nearest even.)
+ * kivi_cache: uint8 [num_blocks][Hkv][3072], one 32-token block (= one K group)
+ *   per tile.  Tile bytes: [0, 1024) K codes, [1024, 1280) K scales and
+ *   [1280, 1536) K zeros (fp16 per channel), [1536, 2560) V codes,
+ *   [2560, 3072) V (scale, zero) fp16 pairs [token][channel group].  The code
+ *   bit positions are this library's design (kivi.hip states them); the
+ *   cache is only meant to be read by kvq_kivi_decode_attn.
+ * Residual: res_k, res_v bf16 [B][Hkv][R][128], token-major; sequence b's
+ *   res_lens[b] newest tokens, oldest first, follow its quantized groups.
+ *
+ * Quantize whole groups: k, v bf16 [n_groups * 32][Hkv][128]; tokens
+ * 32 g .. 32 g + 31 form group g and go to block group_blocks[g] (int32
+ * [n_groups]; a block outside [0, num_blocks) skips the group).  Only the
+ * target tiles are written.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED (dh != 128, alignment). */
+kvq_status kvq_kivi_quantize(const void* k_bf16, const void* v_bf16, int64_t n_groups, int Hkv,
+                             int dh, const int32_t* group_blocks, uint8_t* kivi_cache,
+                             int64_t num_blocks, kvq_stream stream);
+
+/* Bytes of device workspace kvq_kivi_decode_attn needs (0 for invalid sizes). */
+size_t kvq_kivi_decode_workspace_size(int B, int Hq, int Hkv, int max_groups);
+
+/* Decode attention over a KIVI cache ([T] 10.4.2 attention on the values
+ * x_hat read back per 10.4.4's grouping): the query of sequence b attends its
+ * quant_groups[b] quantized groups (blocks block_tables[b][0 .. quant_groups[b]-1],
+ * positions 32 g .. 32 g + 31) and then its res_lens[b] residual tokens.
+ *   q: bf16 [B][Hq][128]; out: [B][Hq][128] fp32 or bf16; Hq / Hkv <= 4.
+ *   quant_groups, res_lens: int32 [B], read on the device, clamped to
+ *     [0, max_groups] and [0, R]; max_groups <= max_blocks; 1 <= R <= 256.
+ *   Block ids outside the pool are clamped into it.
+ *   softmax_scale <= 0 means 1/sqrt(128).  A sequence with no tokens gets an
+ *   all-zero row.
+ * Precision: the quantized part runs on f16 matrix cores (q s, z, q and the
+ * dequantized V in f16, P in f16, fp32 accumulation), so |q|, |K| and |V|
+ * must lie within the fp16 range; the residual is attended in fp32.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE. */
+kvq_status kvq_kivi_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
+                                const uint8_t* kivi_cache, int64_t num_blocks,
+                                const int32_t* block_tables, int max_blocks,
+                                const int32_t* quant_groups, int max_groups,
+                                const void* res_k_bf16, const void* res_v_bf16,
+                                const int32_t* res_lens, int R, int B, int Hq, int Hkv, int dh,
+                                float softmax_scale, void* workspace, size_t ws_bytes,
+                                kvq_stream stream);
+
 /* ---------------------------------------------------------------- prefill
  * Causal chunked prefill in the FP8 domain ([G] the FlashAttention-3 note:
  * attention computed on FP8 operands with Q quantized too; [T] 10.4.5 storage

@@ -30,7 +30,8 @@ GRAN_NAMES = {"tensor": KVQ_SCALE_TENSOR, "head": KVQ_SCALE_HEAD,
 EXPORTS = ["kvq_strerror", "kvq_kv_cache_bytes", "kvq_fp8_encode", "kvq_fp8_decode",
            "kvq_calibrate_scales", "kvq_cache_write", "kvq_decode_workspace_size",
            "kvq_decode_attn", "kvq_prefill_attn", "kvq_cache_write_token_scales",
-           "kvq_decode_attn_token_scales"]
+           "kvq_decode_attn_token_scales", "kvq_kivi_quantize", "kvq_kivi_decode_workspace_size",
+           "kvq_kivi_decode_attn"]
 
 
 class KvqError(RuntimeError):
@@ -68,6 +69,11 @@ def lib() -> ctypes.CDLL:
                                                    i32, P]
         L.kvq_decode_attn_token_scales.argtypes = [P, i32, P, P, P, P, P, i64, P, i32, P, i32, i32,
                                                    i32, i32, i32, i32, i32, f32, P, sz, P]
+        L.kvq_kivi_quantize.argtypes = [P, P, i64, i32, i32, P, P, i64, P]
+        L.kvq_kivi_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.kvq_kivi_decode_workspace_size.restype = sz
+        L.kvq_kivi_decode_attn.argtypes = [P, i32, P, P, i64, P, i32, P, i32, P, P, P, i32, i32,
+                                           i32, i32, i32, f32, P, sz, P]
         L.kvq_prefill_attn.argtypes = [P, i32, P, P, i32, P, i32, P, P, i64, P, i32, P, i32, i32,
                                        i32, i32, i32, P, P, i32, i32, f32, P]
         _lib = L
@@ -234,3 +240,43 @@ def kvq_prefill_attn(out, q, cu_seqlens_q, max_q_len, q_scale, q_gran, k_cache, 
                                   _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
                                   B, Hq, Hkv, dh, bs, _ptr(k_scale), _ptr(v_scale), _fmt(fmt),
                                   _gran(kv_gran), float(softmax_scale), _stream(stream)))
+
+
+KIVI_TILE = 3072  # bytes per (32-token block, head) tile of the 2-bit cache
+
+
+def kvq_kivi_quantize(k, v, group_blocks, kivi_cache, stream=None) -> None:
+    """k, v: bf16 [n_groups * 32, Hkv, 128]; group_blocks int32 [n_groups];
+    kivi_cache uint8 [num_blocks, Hkv, 3072]."""
+    T, Hkv, dh = k.shape
+    if T % 32 or kivi_cache.dim() != 3 or kivi_cache.shape[2] != KIVI_TILE:
+        raise ValueError("k must hold whole 32-token groups and kivi_cache be [nb, Hkv, 3072]")
+    _check("kvq_kivi_quantize",
+           lib().kvq_kivi_quantize(_ptr(k), _ptr(v), T // 32, Hkv, dh, _ptr(group_blocks),
+                                   _ptr(kivi_cache), kivi_cache.shape[0], _stream(stream)))
+
+
+def kvq_kivi_decode_workspace_size(B: int, Hq: int, Hkv: int, max_groups: int) -> int:
+    return int(lib().kvq_kivi_decode_workspace_size(B, Hq, Hkv, max_groups))
+
+
+def kvq_kivi_decode_attn(out, q, kivi_cache, block_tables, quant_groups, max_groups, res_k,
+                         res_v, res_lens, softmax_scale=0.0, workspace=None,
+                         stream=None) -> None:
+    """out: fp32 or bf16 [B, Hq, 128]; q bf16 [B, Hq, 128]; res_k / res_v bf16
+    [B, Hkv, R, 128]; quant_groups / res_lens int32 [B]."""
+    import torch
+    B, Hq, dh = q.shape
+    _, Hkv, R, _ = res_k.shape
+    ws_bytes = kvq_kivi_decode_workspace_size(B, Hq, Hkv, max_groups)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
+    _check("kvq_kivi_decode_attn",
+           lib().kvq_kivi_decode_attn(_ptr(out), out_dt, _ptr(q), _ptr(kivi_cache),
+                                      kivi_cache.shape[0], _ptr(block_tables),
+                                      block_tables.shape[1], _ptr(quant_groups), int(max_groups),
+                                      _ptr(res_k), _ptr(res_v), _ptr(res_lens), R, B, Hq, Hkv,
+                                      dh, float(softmax_scale), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))

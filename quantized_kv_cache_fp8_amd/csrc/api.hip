@@ -227,6 +227,58 @@ kvq_status kvq_decode_attn_token_scales(void* out, kvq_out out_dtype, const void
                                v_scale_cache));
 }
 
+kvq_status kvq_kivi_quantize(const void* k_bf16, const void* v_bf16, int64_t n_groups, int Hkv,
+                             int dh, const int32_t* group_blocks, uint8_t* kivi_cache,
+                             int64_t num_blocks, kvq_stream stream) {
+  if (n_groups < 0 || Hkv < 1 || num_blocks < 1) return KVQ_ERR_SHAPE;
+  if (dh != 128) return KVQ_ERR_UNSUPPORTED;
+  if ((uint64_t)n_groups * (uint64_t)Hkv >= (1ull << 31)) return KVQ_ERR_SHAPE;
+  if (!kivi_cache) return KVQ_ERR_NULL;
+  if (n_groups == 0) return KVQ_OK;
+  if (!k_bf16 || !v_bf16 || !group_blocks) return KVQ_ERR_NULL;
+  if (!aligned(k_bf16, 16) || !aligned(v_bf16, 16) || !aligned(kivi_cache, 16) ||
+      !aligned(group_blocks, 4))
+    return KVQ_ERR_UNSUPPORTED;
+  return map_err(launch_kivi_quantize((const uint16_t*)k_bf16, (const uint16_t*)v_bf16, n_groups,
+                                      Hkv, group_blocks, kivi_cache, num_blocks,
+                                      (hipStream_t)stream));
+}
+
+size_t kvq_kivi_decode_workspace_size(int B, int Hq, int Hkv, int max_groups) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_groups < 0) return 0;
+  return kivi_decode_plan(B, Hq, Hkv, max_groups).ws_bytes;
+}
+
+kvq_status kvq_kivi_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
+                                const uint8_t* kivi_cache, int64_t num_blocks,
+                                const int32_t* block_tables, int max_blocks,
+                                const int32_t* quant_groups, int max_groups,
+                                const void* res_k_bf16, const void* res_v_bf16,
+                                const int32_t* res_lens, int R, int B, int Hq, int Hkv, int dh,
+                                float softmax_scale, void* workspace, size_t ws_bytes,
+                                kvq_stream stream) {
+  if (!out_ok(out_dtype)) return KVQ_ERR_UNSUPPORTED;
+  if (B < 1 || Hq < 1 || Hkv < 1 || num_blocks < 1 || max_blocks < 1 || R < 1)
+    return KVQ_ERR_SHAPE;
+  if (Hq % Hkv || max_groups < 0 || max_groups > max_blocks) return KVQ_ERR_SHAPE;
+  if (dh != 128 || Hq / Hkv > 4 || R > 256 || B > 65535 || Hkv > 65535)
+    return KVQ_ERR_UNSUPPORTED;
+  if (!out || !q_bf16 || !kivi_cache || !block_tables || !quant_groups || !res_k_bf16 ||
+      !res_v_bf16 || !res_lens || !workspace)
+    return KVQ_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(q_bf16, 16) || !aligned(kivi_cache, 16) ||
+      !aligned(res_k_bf16, 16) || !aligned(res_v_bf16, 16) || !aligned(workspace, 16))
+    return KVQ_ERR_UNSUPPORTED;
+  const KiviPlan plan = kivi_decode_plan(B, Hq, Hkv, max_groups);
+  if (plan.nsplit > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (ws_bytes < plan.ws_bytes) return KVQ_ERR_WORKSPACE;
+  return map_err(launch_kivi_decode(out, out_dtype == KVQ_OUT_BF16, (const uint16_t*)q_bf16,
+                                    kivi_cache, num_blocks, block_tables, max_blocks,
+                                    quant_groups, max_groups, (const uint16_t*)res_k_bf16,
+                                    (const uint16_t*)res_v_bf16, res_lens, R, B, Hq, Hkv,
+                                    softmax_scale, plan, workspace, (hipStream_t)stream));
+}
+
 kvq_status kvq_prefill_attn(void* out, kvq_out out_dtype, const void* q_bf16,
                             const int32_t* cu_seqlens_q, int max_q_len, const float* q_scale,
                             kvq_gran q_gran, const uint8_t* k_cache, const uint8_t* v_cache,

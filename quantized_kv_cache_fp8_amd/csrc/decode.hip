@@ -35,7 +35,7 @@
 // internal accumulation keeps only about 16 bits relative to the largest
 // product, which at decode-sized logits (tens in log2 units) is visible in
 // the output, whereas bf16 products accumulate in full fp32.
-#include "codec.hpp"
+#include "attn_common.hpp"
 #include "launch.hpp"
 
 namespace kvq {
@@ -48,11 +48,6 @@ namespace kvq {
 // Waves per SIMD the split kernel is compiled for.  At 4 the whole state
 // (Q operand, one block pair of codes, the O tile) fits in 128 registers, so
 // a compute unit keeps 16 waves' loads in flight.
-// Whether cache loads are marked nontemporal: every cache byte is read once
-// per call, so the loads stream through L2 instead of allocating in it.
-#ifndef KVQ_DECODE_NT_LOADS
-#define KVQ_DECODE_NT_LOADS 1
-#endif
 // Whether each wave keeps two block pairs in flight (two register sets).
 #ifndef KVQ_DECODE_DOUBLE_BUFFER
 #define KVQ_DECODE_DOUBLE_BUFFER 0
@@ -72,69 +67,6 @@ namespace kvq {
 
 namespace {
 constexpr int kBlockSize = 16;  // tokens per cache block
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-
-// max over the 16 lanes of a row (lanes 16i .. 16i+15); every lane gets it
-__device__ __forceinline__ float max16(float x) {
-  x = __builtin_fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
-  x = __builtin_fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = __builtin_fmaxf(x, dpp<0x141>(x));  // row_half_mirror
-  x = __builtin_fmaxf(x, dpp<0x140>(x));  // row_mirror
-  return x;
-}
-
-// 8 codes (two dwords) -> 8 exact bf16 / f16 values, assembled as one 128-bit
-// value so the converts land directly in the MFMA operand registers
-template <int FMT>
-__device__ __forceinline__ bf16x8 codes_to_bf16x8(uint32_t a, uint32_t b) {
-  const uint4 u = make_uint4(__builtin_bit_cast(uint32_t, dec2_bf16<FMT, false>(a)),
-                             __builtin_bit_cast(uint32_t, dec2_bf16<FMT, true>(a)),
-                             __builtin_bit_cast(uint32_t, dec2_bf16<FMT, false>(b)),
-                             __builtin_bit_cast(uint32_t, dec2_bf16<FMT, true>(b)));
-  return __builtin_bit_cast(bf16x8, u);
-}
-template <int FMT>
-__device__ __forceinline__ f16x8 codes_to_f16x8(uint32_t a, uint32_t b) {
-  const uint4 u = make_uint4(__builtin_bit_cast(uint32_t, dec2_f16<FMT, false>(a)),
-                             __builtin_bit_cast(uint32_t, dec2_f16<FMT, true>(a)),
-                             __builtin_bit_cast(uint32_t, dec2_f16<FMT, false>(b)),
-                             __builtin_bit_cast(uint32_t, dec2_f16<FMT, true>(b)));
-  return __builtin_bit_cast(f16x8, u);
-}
-
-__device__ __forceinline__ uint4 load16(const uint8_t* p) {
-#if KVQ_DECODE_NT_LOADS
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-#else
-  return *reinterpret_cast<const uint4*>(p);
-#endif
-}
-__device__ __forceinline__ uint2 load8(const uint8_t* p) {
-#if KVQ_DECODE_NT_LOADS
-  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-  return make_uint2(v.x, v.y);
-#else
-  return *reinterpret_cast<const uint2*>(p);
-#endif
-}
-
-__device__ __forceinline__ int64_t clamp_block(int64_t blk, int64_t num_blocks) {
-  return blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
-}
 }  // namespace
 
 // dynamic LDS bytes for one workgroup: per-wave P transpose scratch
@@ -690,10 +622,13 @@ __global__ __launch_bounds__(DH) void decode_combine_kernel(
     const float* __restrict__ vs, int per_head, int part_blocks, int nsplit) {
   constexpr int kBatch = 16;
   const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  int ctx = ctx_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > max_ctx ? max_ctx : ctx);
-  const int span = part_blocks * kBlockSize;
-  const int nvalid = (ctx + span - 1) / span;
+  int nvalid = nsplit;  // part_blocks == 0: every split holds a partial (maybe empty)
+  if (part_blocks > 0) {
+    int ctx = ctx_lens[b];
+    ctx = ctx < 0 ? 0 : (ctx > max_ctx ? max_ctx : ctx);
+    const int span = part_blocks * kBlockSize;
+    nvalid = (ctx + span - 1) / span;
+  }
   const size_t row0 = ((size_t)b * Hq + hq) * nsplit;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml);
   float M = kNegBig, L = 0.0f, a = 0.0f;
@@ -805,18 +740,25 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
 #undef KVQ_SPLIT_G4
 #undef KVQ_SPLIT
   }
+  launch_decode_combine(out, out_bf16, ml, acc, ctx, B, Hq, Hkv, dh, max_ctx, ts ? nullptr : vs,
+                        per_head, plan.part_blocks, plan.nsplit, s);
+  return hipGetLastError();
+}
+
+void launch_decode_combine(void* out, int out_bf16, const float* ml, const float* acc,
+                           const int32_t* ctx, int B, int Hq, int Hkv, int dh, int max_ctx,
+                           const float* vs, int per_head, int part_blocks, int nsplit,
+                           hipStream_t s) {
   const dim3 cgrid(Hq, B);
 #define KVQ_COMBINE(D, BF)                                                                     \
-  decode_combine_kernel<D, BF><<<cgrid, D, 0, s>>>(out, ml, acc, ctx, Hq, Hkv, max_ctx,        \
-                                                   ts ? nullptr : vs,                          \
-                                                   per_head, plan.part_blocks, plan.nsplit)
+  decode_combine_kernel<D, BF><<<cgrid, D, 0, s>>>(out, ml, acc, ctx, Hq, Hkv, max_ctx, vs,    \
+                                                   per_head, part_blocks, nsplit)
   if (dh == 128) {
     if (out_bf16) KVQ_COMBINE(128, true); else KVQ_COMBINE(128, false);
   } else {
     if (out_bf16) KVQ_COMBINE(64, true); else KVQ_COMBINE(64, false);
   }
 #undef KVQ_COMBINE
-  return hipGetLastError();
 }
 
 }  // namespace kvq

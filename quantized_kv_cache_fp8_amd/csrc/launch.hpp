@@ -45,6 +45,31 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
                          float softmax_scale, const DecodePlan& plan, void* ws, hipStream_t s,
                          const uint16_t* ksc = nullptr, const uint16_t* vsc = nullptr);
 
+// Log-sum-exp merge of split partials ([B][Hq][nsplit] (m, l) pairs and dh
+// partial sums) into out, times vs (null: 1).  part_blocks > 0: sequence b's
+// first ceil(ctx / (16 part_blocks)) splits are merged; 0: all nsplit are.
+void launch_decode_combine(void* out, int out_bf16, const float* ml, const float* acc,
+                           const int32_t* ctx, int B, int Hq, int Hkv, int dh, int max_ctx,
+                           const float* vs, int per_head, int part_blocks, int nsplit,
+                           hipStream_t s);
+
+// KIVI-style 2-bit cache (dh = 128, 32-token blocks, 3072-byte tiles).
+hipError_t launch_kivi_quantize(const uint16_t* k, const uint16_t* v, int64_t n_groups, int Hkv,
+                                const int32_t* group_blocks, uint8_t* cache, int64_t num_blocks,
+                                hipStream_t s);
+struct KiviPlan {
+  int groups_per_split;  // 32-token groups per quantized split
+  int nsplit;            // splits per sequence: the residual's, then the quantized ones
+  size_t ws_bytes;       // workspace bytes
+};
+KiviPlan kivi_decode_plan(int B, int Hq, int Hkv, int max_groups);
+hipError_t launch_kivi_decode(void* out, int out_bf16, const uint16_t* q, const uint8_t* cache,
+                              int64_t num_blocks, const int32_t* bt, int max_blocks,
+                              const int32_t* quant_groups, int max_groups, const uint16_t* res_k,
+                              const uint16_t* res_v, const int32_t* res_lens, int R, int B,
+                              int Hq, int Hkv, float softmax_scale, const KiviPlan& plan,
+                              void* ws, hipStream_t s);
+
 hipError_t launch_prefill(void* out, int out_bf16, const uint16_t* q, const int32_t* cu,
                           int max_q_len, const float* qs, int q_per_head, const uint8_t* kc,
                           const uint8_t* vc, int64_t num_blocks, const int32_t* bt,

@@ -150,3 +150,34 @@ def test_token_scale_decode_validation():
     assert st(Hq=16, Hkv=2) == -3  # groups of more than 4 query heads
     assert st(fmt=3) == -3 and st(dh=80) == -3 and st(vsc=FAKE + 1) == -3
     assert st(wsb=16) == -4
+
+
+def test_kivi_quantize_validation():
+    L = K.lib()
+    base = dict(k=FAKE, v=FAKE, ng=4, Hkv=2, dh=128, gb=FAKE, cache=FAKE, nb=8, stream=None)
+    def st(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.kvq_kivi_quantize(*a.values())
+    assert st(gb=None) == -1 and st(cache=None) == -1 and st(k=None) == -1
+    assert st(ng=-1) == -2 and st(nb=0) == -2 and st(Hkv=0) == -2
+    assert st(dh=64) == -3 and st(k=FAKE + 4) == -3
+    assert st(ng=0) == 0
+
+
+def test_kivi_decode_validation():
+    L = K.lib()
+    base = dict(out=FAKE, odt=0, q=FAKE, cache=FAKE, nb=10, bt=FAKE, mb=8, qg=FAKE, mg=6,
+                rk=FAKE, rv=FAKE, rl=FAKE, R=128, B=2, Hq=8, Hkv=2, dh=128, sm=0.0, ws=FAKE,
+                wsb=0, stream=None)
+    def st(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.kvq_kivi_decode_attn(*a.values())
+    assert st(rk=None) == -1 and st(qg=None) == -1 and st(ws=None, wsb=1 << 24) == -1
+    assert st(mg=9) == -2 and st(R=0) == -2 and st(Hq=6, Hkv=4) == -2
+    assert st(Hq=16, Hkv=2) == -3 and st(dh=64) == -3 and st(R=300) == -3 and st(odt=5) == -3
+    assert st(rv=FAKE + 2) == -3
+    assert st(wsb=16) == -4
+    assert K.kvq_kivi_decode_workspace_size(2, 8, 2, 6) > 0
+    assert K.kvq_kivi_decode_workspace_size(2, 7, 2, 6) == 0

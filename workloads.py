@@ -223,3 +223,58 @@ def fp8_chunked_prefill(seed: int = BASE_SEED + 3, B: int = 8, prefix: int = 409
     Hq=32, Hkv=8, dh=128; N(0,1); per-head E4M3 scales for Q, K and V."""
     return prefill_workload(f"fp8-chunked-prefill-b{B}-prefix{prefix}-chunk{chunk}", seed,
                             [prefix] * B, [chunk] * B)
+
+
+# ------------------------------------------------------------------ KIVI 2-bit
+
+@dataclass
+class KiviWorkload:
+    """Sequences whose first quant_groups[b] 32-token groups are quantized into
+    a paged 2-bit cache (block = group) and whose next res_lens[b] tokens sit in
+    a bf16 residual [B, Hkv, R, dh]."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    R: int
+    paging: Paging  # bs = 32; context_lens = 32 * quant_groups
+    k: np.ndarray  # uint16 [sum(quant_groups) * 32, Hkv, dh]: quantized tokens, group order
+    v: np.ndarray
+    group_blocks: np.ndarray  # int32 [n_groups]: block of each group
+    quant_groups: np.ndarray  # int32 [B]
+    res_k: np.ndarray  # uint16 [B, Hkv, R, dh]
+    res_v: np.ndarray
+    res_lens: np.ndarray  # int32 [B]
+    q: np.ndarray  # uint16 [B, Hq, dh]
+
+
+def kivi_workload(name: str, seed: int, Hq: int, Hkv: int, quant_groups, res_lens, R: int = 128,
+                  dh: int = 128, k_outliers=(4, 10.0), head_range=(0.5, 4.0),
+                  max_blocks: int | None = None) -> KiviWorkload:
+    """K with a few fixed outlier channels (the per-channel structure KIVI's K
+    grouping is for), V plain; per-head magnitudes log-uniform; N(0,1) q."""
+    g = rng(seed)
+    qg = np.asarray(quant_groups, np.int32)
+    rl = np.asarray(res_lens, np.int32)
+    B = len(qg)
+    paging = make_paging(g, qg * 32, 32, max_blocks)
+    n = int(qg.sum())
+    gb = np.concatenate([paging.block_tables[b, :qg[b]] for b in range(B)]).astype(np.int32) \
+        if n else np.zeros(0, np.int32)
+    k_ch = g.choice(dh, size=k_outliers[0], replace=False) if k_outliers[0] else None
+    km = log_uniform(g, Hkv, *head_range)
+    vm = log_uniform(g, Hkv, *head_range)
+    k = normal_bf16(g, (n * 32, Hkv, dh), 1, km, k_ch, k_outliers[1])
+    v = normal_bf16(g, (n * 32, Hkv, dh), 1, vm)
+    rk = normal_bf16(g, (B, Hkv, R, dh), 1, km, k_ch, k_outliers[1])
+    rv = normal_bf16(g, (B, Hkv, R, dh), 1, vm)
+    q = normal_bf16(g, (B, Hq, dh))
+    return KiviWorkload(name, B, Hq, Hkv, R, paging, k, v, gb, qg, rk, rv, rl, q)
+
+
+def kivi_2bit_decode(seed: int = BASE_SEED + 5, B: int = 8, S: int = 16384,
+                     R: int = 128) -> KiviWorkload:
+    """B=8, Hq=32, Hkv=8, dh=128, S=16384 tokens per sequence: the first
+    S - 128 in 2-bit groups of 32, the newest 128 in the bf16 residual."""
+    return kivi_workload(f"kivi-2bit-decode-b{B}-s{S}-res{R}", seed, 32, 8,
+                         [(S - R) // 32] * B, [R] * B, R)
