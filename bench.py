@@ -307,8 +307,60 @@ def token_scale_rows(K, torch, dev, stream, k_all, v_all, slots_all, caches, wl,
     return rows
 
 
+def kivi_rows(K, W, torch, dev, stream, reps=50):
+    """KIVI-style 2-bit cache (textbook 10.4.4): quantize of every full group and
+    decode over it plus the bf16 residual, on B=8, Hq=32, Hkv=8, S=16384."""
+    kw = W.kivi_2bit_decode()
+
+    def dt(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    k, v, gb = dt(kw.k), dt(kw.v), dt(kw.group_blocks)
+    nb = kw.paging.num_blocks
+    # copies of the cache in rotation so no call reads another's data from L2 / MALL
+    caches = [torch.empty((nb, kw.Hkv, K.KIVI_TILE), dtype=torch.uint8, device=dev)
+              for _ in range(3)]
+    rows = {}
+
+    def quant():
+        K.kvq_kivi_quantize(k, v, gb, caches[0])
+    ms = time_call(torch, stream, quant, 10)
+    ng = len(kw.group_blocks)
+    nbytes = ng * 32 * kw.Hkv * 128 * 2 * 2 + ng * kw.Hkv * K.KIVI_TILE + ng * 4
+    rows["kivi_quantize"] = {"workload": kw.name + " all full groups", "ms": round(ms, 4),
+                             "GB/s": round(nbytes / ms / 1e6, 1)}
+    for c in caches[1:]:
+        K.kvq_kivi_quantize(k, v, gb, c)
+    q, bt, qg, rk, rv, rl = (dt(kw.q), dt(kw.paging.block_tables), dt(kw.quant_groups),
+                             dt(kw.res_k), dt(kw.res_v), dt(kw.res_lens))
+    mg = int(kw.quant_groups.max())
+    out = torch.empty((kw.B, kw.Hq, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(K.kvq_kivi_decode_workspace_size(kw.B, kw.Hq, kw.Hkv, mg), dtype=torch.uint8,
+                     device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i in range(reps + 5):
+        if i >= 5:
+            ev[i - 5][0].record(stream)
+        K.kvq_kivi_decode_attn(out, q, caches[i % 3], bt, qg, mg, rk, rv, rl, workspace=ws)
+        if i >= 5:
+            ev[i - 5][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # algorithmic bytes: every quantized tile once, the residual once
+    nbytes = (int(kw.quant_groups.sum()) * kw.Hkv * K.KIVI_TILE +
+              int(kw.res_lens.sum()) * kw.Hkv * 128 * 2 * 2)
+    gbs = nbytes / ms / 1e6
+    rows["kivi_decode"] = {"workload": kw.name, "ms": round(ms, 5), "bytes": nbytes,
+                           "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    return rows
+
+
 def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, vs, wl, dec):
     rows = {}
+    rows.update(kivi_rows(K, W, torch, dev, stream))
     rows.update(token_scale_rows(K, torch, dev, stream, k_all, v_all, slots_all, caches, wl,
                                  dec))
     # the same decode with a symmetric INT8 cache (textbook 10.4.2 write rule)
