@@ -306,6 +306,17 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
   ng = ng < 0 ? 0 : (ng > max_groups ? max_groups : ng);
   const int g0 = (split - 1) * PG;
   const int ngs = ng - g0 < PG ? ng - g0 : PG;  // groups of this split (may be <= 0)
+  if (ngs <= 0) {  // past the sequence's groups: an empty partial
+    for (int o = threadIdx.x; o < NH * kDH; o += 256) {
+      const size_t ridx = ((size_t)b * Hq + hq0 + o / kDH) * nsplit + split;
+      ws_acc[ridx * kDH + o % kDH] = 0.0f;
+      if (o % kDH == 0) {
+        ws_ml[ridx * 2 + 0] = kNegBig;
+        ws_ml[ridx * 2 + 1] = 0.0f;
+      }
+    }
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -313,10 +324,9 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
   const int c16 = lane & 15, g4 = lane >> 4;
   const int rph_mask = (1 << rph_shift) - 1;
   const int head_a = c16 >> rph_shift;  // A row of the S tile
-  const bool head_a_real = head_a < NH;
   const int head_s = (4 * g4) >> rph_shift;  // S rows of this lane
   const bool pub = ((4 * g4) & rph_mask) == 0 && head_s < NH;
-  const int head_p = lane & 3;  // A row of the P V tile
+  const int head_p = lane & 3;  // A row of the P V tile (rows >= NH read zeros)
 
   uint8_t* wl_base = smem + wave * kWaveLds;
   _Float16* ptr = reinterpret_cast<_Float16*>(wl_base);          // P [4][32]
@@ -336,7 +346,7 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     qh[j] = f16x8{};
-    if (head_a_real) {
+    if (head_a < NH) {
       const uint4 w = *reinterpret_cast<const uint4*>(
           q + ((size_t)b * Hq + hq0 + head_a) * kDH + 32 * j + 8 * g4);
       const uint32_t u[4] = {w.x, w.y, w.z, w.w};
@@ -375,17 +385,16 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
     x.vm = load8(tile + kVm + 8 * lane);
   };
 
+  // rows of heads >= NH in P, A' hi and A' lo stay zero (their products land in
+  // output rows nobody reads, so the operand loads need no masking)
+  for (int i = lane; i < (256 + 2048) / 16; i += 64)
+    reinterpret_cast<uint4*>(wl_base)[i] = make_uint4(0, 0, 0, 0);
+
   float m_run = kNegBig, l_part = 0.0f;
   f32x4 O[2];
   O[0] = O[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  int gi = wave;
-  Regs cur;
-  if (gi < ngs) load(cur, gi);
-#pragma unroll 1
-  for (; gi < ngs; gi += 4) {
-    Regs nxt;
-    if (gi + 4 < ngs) load(nxt, gi + 4);
+  auto step = [&](const Regs& cur) {
     // ---- stage A' = q s, the K zeros and the V (s, z) of this group in LDS
     {
       const f16x2 s2 = __builtin_bit_cast(f16x2, cur.ks);
@@ -417,8 +426,8 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ao = head_a * kDH + 32 * j + 8 * g4;
-      const f16x8 ahi = head_a_real ? *reinterpret_cast<const f16x8*>(aq + ao) : f16x8{};
-      const f16x8 alo = head_a_real ? *reinterpret_cast<const f16x8*>(al + ao) : f16x8{};
+      const f16x8 ahi = *reinterpret_cast<const f16x8*>(aq + ao);
+      const f16x8 alo = *reinterpret_cast<const f16x8*>(al + ao);
       // token half 0 in kc.x / kc.y, half 1 in kc.z / kc.w; dword j / 2, field j % 2
       const uint32_t w0 = j < 2 ? cur.kc.x : cur.kc.y, w1 = j < 2 ? cur.kc.z : cur.kc.w;
       const f16x8 b0 = codes8((j & 1) ? hi2(w0) : lo2(w0));
@@ -455,16 +464,13 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
       ptr[head_s * kG + 16 + c16] = (_Float16)p1;
     }
     // ---- O += P V_hat: 8 steps of 4 tokens x 2 halves of 64 channels
-    f16x8 pa[4] = {};
-    if (head_p < NH) {
+
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pa[i] = *reinterpret_cast<const f16x8*>(ptr + head_p * kG + 8 * i);
-    }
+    for (int t8 = 0; t8 < 4; ++t8) {  // 8 tokens: two MFMA steps per half
+      const f16x8 p8 = *reinterpret_cast<const f16x8*>(ptr + head_p * kG + 8 * t8);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int gc = 2 * c + (lane >> 5);  // channel group of channel 64 c + lane
-#pragma unroll
-      for (int t8 = 0; t8 < 4; ++t8) {  // 8 tokens: two MFMA steps
+      for (int c = 0; c < 2; ++c) {
+        const int gc = 2 * c + (lane >> 5);  // channel group of channel 64 c + lane
         const uint4 s8 = *reinterpret_cast<const uint4*>(vsS + gc * kG + 8 * t8);
         const uint4 z8 = *reinterpret_cast<const uint4*>(vsZ + gc * kG + 8 * t8);
         const uint32_t word = c ? (t8 < 2 ? cur.vc.z : cur.vc.w) : (t8 < 2 ? cur.vc.x : cur.vc.y);
@@ -480,15 +486,27 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
                                                       __builtin_bit_cast(f16x2, za));
           const f16x2 v23 = __builtin_elementwise_fma(c23, __builtin_bit_cast(f16x2, sb),
                                                       __builtin_bit_cast(f16x2, zb2));
-          const f16x8 p8 = pa[tq >> 1];
-          const f16x4 a = (tq & 1) ? f16x4{p8[4], p8[5], p8[6], p8[7]}
-                                   : f16x4{p8[0], p8[1], p8[2], p8[3]};
+          const f16x4 a = st ? f16x4{p8[4], p8[5], p8[6], p8[7]}
+                             : f16x4{p8[0], p8[1], p8[2], p8[3]};
           O[c] = __builtin_amdgcn_mfma_f32_4x4x4f16(a, f16x4{v01[0], v01[1], v23[0], v23[1]},
                                                    O[c], 0, 0, 0);
         }
       }
     }
-    cur = nxt;
+  };
+
+  // two register sets in turn: the next group's loads are in flight while
+  // the current one is processed
+  Regs ra, rb;
+  int gi = wave;
+  if (gi < ngs) load(ra, gi);
+#pragma unroll 1
+  for (; gi < ngs; gi += 8) {
+    if (gi + 4 < ngs) load(rb, gi + 4);
+    step(ra);
+    if (gi + 4 >= ngs) break;
+    if (gi + 8 < ngs) load(ra, gi + 8);
+    step(rb);
   }
 
   // ---- merge the 4 waves through LDS and write the split's partial
@@ -530,10 +548,16 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------- launchers
+// Workgroups the quantized splits should at least give (the split shrinks,
+// from 32 groups down to 4, until they do).
+#ifndef KVQ_KIVI_MIN_WGS
+#define KVQ_KIVI_MIN_WGS 2048
+#endif
+
 KiviPlan kivi_decode_plan(int B, int Hq, int Hkv, int max_groups) {
   KiviPlan p{};
   int PG = 32;
-  while (PG > 4 && (int64_t)B * Hkv * ((max_groups + PG - 1) / PG) < 2048) PG >>= 1;
+  while (PG > 4 && (int64_t)B * Hkv * ((max_groups + PG - 1) / PG) < KVQ_KIVI_MIN_WGS) PG >>= 1;
   p.groups_per_split = PG;
   p.nsplit = 1 + (max_groups + PG - 1) / PG;
   p.ws_bytes = (size_t)B * Hq * p.nsplit * (2 + kDH) * sizeof(float);
