@@ -178,6 +178,69 @@ kvq_status kvq_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
                            kvq_fmt fmt, kvq_gran gran, float softmax_scale, void* workspace,
                            size_t ws_bytes, kvq_stream stream);
 
+/* ---------------------------------------------------------------- skip-layers, padded pages
+ * Mixed quantized / unquantized layers ([G] kv_cache_dtype_skip_layers): the
+ * listed layers keep the model's native dtype ("auto"), every other layer
+ * uses the quantized cache; skipped layers still take part in the page
+ * (block) alignment, the smaller pages being padded so that the mixed cache
+ * lines up page by page.
+ *
+ * Reading of the skip rule: a layer is skipped when it is a sliding-window
+ * layer and the list holds "sliding_window", or when the list holds its layer
+ * index written in decimal ("0", "1", "23").  Returns 1 (skipped) or 0. */
+int kvq_layer_skipped(int layer_index, int is_sliding_window, const char* const* skip_list,
+                      int n_skip);
+
+/* The layer index inside a module prefix such as "model.layers.12.self_attn":
+ * the one dot-separated component made only of decimal digits; -1 when there
+ * is none or more than one. */
+int kvq_layer_index(const char* prefix);
+
+/* Bytes of one page (one block of bs tokens, K and V, all KV heads) of a
+ * layer whose cache stores bits_per_elem bits per element: 2 Hkv bs dh bits/8
+ * (0 for negative arguments). */
+uint64_t kvq_page_bytes(int Hkv, int dh, int bs, int bits_per_elem);
+
+/* Reading of the page padding: every layer's pages are padded to the largest
+ * natural page among the L layers (layer_bits[l] = 16 for a skipped bf16
+ * layer, 8 for an FP8 / INT8 one), rounded up to 16 bytes.  0 for invalid
+ * arguments. */
+uint64_t kvq_common_page_bytes(const int* layer_bits, int L, int Hkv, int dh, int bs);
+
+/* The quantized calls on a padded layout: block b of k_cache starts at byte
+ * b * block_stride (likewise v_cache), block_stride >= Hkv * bs * dh and a
+ * multiple of 16; inside a block the layout is the one above.  One page of a
+ * mixed pool holds a layer's K block then its V block (k_cache = page base,
+ * v_cache = page base + Hkv * bs * dh, block_stride = the common page size);
+ * padding bytes are never read or written.  Otherwise identical to
+ * kvq_cache_write / kvq_decode_attn / kvq_prefill_attn, which are these calls
+ * with block_stride = Hkv * bs * dh.
+ * Errors: as the unpadded calls; KVQ_ERR_SHAPE for a block_stride below
+ * Hkv * bs * dh, KVQ_ERR_UNSUPPORTED when it is not a multiple of 16. */
+kvq_status kvq_cache_write_paged(const void* k_bf16, const void* v_bf16, int64_t T, int Hkv,
+                                 int dh, const int64_t* slot_mapping, uint8_t* k_cache,
+                                 uint8_t* v_cache, int64_t num_blocks, int bs,
+                                 int64_t block_stride, const float* k_scale,
+                                 const float* v_scale, kvq_fmt fmt, kvq_gran gran,
+                                 kvq_stream stream);
+kvq_status kvq_decode_attn_paged(void* out, kvq_out out_dtype, const void* q_bf16,
+                                 const uint8_t* k_cache, const uint8_t* v_cache,
+                                 int64_t num_blocks, const int32_t* block_tables, int max_blocks,
+                                 const int32_t* context_lens, int B, int Hq, int Hkv, int dh,
+                                 int bs, int64_t block_stride, int max_context_len,
+                                 const float* k_scale, const float* v_scale, kvq_fmt fmt,
+                                 kvq_gran gran, float softmax_scale, void* workspace,
+                                 size_t ws_bytes, kvq_stream stream);
+kvq_status kvq_prefill_attn_paged(void* out, kvq_out out_dtype, const void* q_bf16,
+                                  const int32_t* cu_seqlens_q, int max_q_len,
+                                  const float* q_scale, kvq_gran q_gran, const uint8_t* k_cache,
+                                  const uint8_t* v_cache, int64_t num_blocks,
+                                  const int32_t* block_tables, int max_blocks,
+                                  const int32_t* context_lens, int B, int Hq, int Hkv, int dh,
+                                  int bs, int64_t block_stride, const float* k_scale,
+                                  const float* v_scale, kvq_fmt fmt, kvq_gran kv_gran,
+                                  float softmax_scale, kvq_stream stream);
+
 /* ---------------------------------------------------------------- per-token-head scales
  * Finer scale granularity ([T] 10.4.3: one scale per token row along dh; its
  * metadata example keeps one FP16 scale for K and one for V per token and

@@ -31,7 +31,9 @@ EXPORTS = ["kvq_strerror", "kvq_kv_cache_bytes", "kvq_fp8_encode", "kvq_fp8_deco
            "kvq_calibrate_scales", "kvq_cache_write", "kvq_decode_workspace_size",
            "kvq_decode_attn", "kvq_prefill_attn", "kvq_cache_write_token_scales",
            "kvq_decode_attn_token_scales", "kvq_kivi_quantize", "kvq_kivi_decode_workspace_size",
-           "kvq_kivi_decode_attn"]
+           "kvq_kivi_decode_attn", "kvq_cache_write_paged", "kvq_decode_attn_paged",
+           "kvq_prefill_attn_paged", "kvq_layer_skipped", "kvq_layer_index", "kvq_page_bytes",
+           "kvq_common_page_bytes"]
 
 
 class KvqError(RuntimeError):
@@ -74,6 +76,18 @@ def lib() -> ctypes.CDLL:
         L.kvq_kivi_decode_workspace_size.restype = sz
         L.kvq_kivi_decode_attn.argtypes = [P, i32, P, P, i64, P, i32, P, i32, P, P, P, i32, i32,
                                            i32, i32, i32, f32, P, sz, P]
+        L.kvq_cache_write_paged.argtypes = [P, P, i64, i32, i32, P, P, P, i64, i32, i64, P, P,
+                                            i32, i32, P]
+        L.kvq_decode_attn_paged.argtypes = [P, i32, P, P, P, i64, P, i32, P, i32, i32, i32, i32,
+                                            i32, i64, i32, P, P, i32, i32, f32, P, sz, P]
+        L.kvq_prefill_attn_paged.argtypes = [P, i32, P, P, i32, P, i32, P, P, i64, P, i32, P, i32,
+                                             i32, i32, i32, i32, i64, P, P, i32, i32, f32, P]
+        L.kvq_layer_skipped.argtypes = [i32, i32, P, i32]
+        L.kvq_layer_index.argtypes = [ctypes.c_char_p]
+        L.kvq_page_bytes.argtypes = [i32, i32, i32, i32]
+        L.kvq_page_bytes.restype = ctypes.c_uint64
+        L.kvq_common_page_bytes.argtypes = [P, i32, i32, i32, i32]
+        L.kvq_common_page_bytes.restype = ctypes.c_uint64
         L.kvq_prefill_attn.argtypes = [P, i32, P, P, i32, P, i32, P, P, i64, P, i32, P, i32, i32,
                                        i32, i32, i32, P, P, i32, i32, f32, P]
         _lib = L
@@ -280,3 +294,89 @@ def kvq_kivi_decode_attn(out, q, kivi_cache, block_tables, quant_groups, max_gro
                                       dh, float(softmax_scale), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(),
                                       _stream(stream)))
+
+
+# ------------------------------------------------------------------ skip-layers, padded pages
+
+def kvq_layer_skipped(layer_index: int, is_sliding_window: bool, skip_list) -> bool:
+    """The guide's skip rule: sliding-window layers when "sliding_window" is
+    listed, or the layer whose decimal index is listed."""
+    arr = (ctypes.c_char_p * max(1, len(skip_list)))(*[str(x).encode() for x in skip_list])
+    return bool(lib().kvq_layer_skipped(int(layer_index), int(bool(is_sliding_window)),
+                                        ctypes.cast(arr, ctypes.c_void_p), len(skip_list)))
+
+
+def kvq_layer_index(prefix: str) -> int:
+    return int(lib().kvq_layer_index(prefix.encode()))
+
+
+def kvq_page_bytes(Hkv: int, dh: int, bs: int, bits_per_elem: int) -> int:
+    return int(lib().kvq_page_bytes(Hkv, dh, bs, bits_per_elem))
+
+
+def kvq_common_page_bytes(layer_bits, Hkv: int, dh: int, bs: int) -> int:
+    arr = (ctypes.c_int * max(1, len(layer_bits)))(*[int(b) for b in layer_bits])
+    return int(lib().kvq_common_page_bytes(ctypes.cast(arr, ctypes.c_void_p), len(layer_bits),
+                                           Hkv, dh, bs))
+
+
+def _paged_dims(k_cache, v_cache):
+    """(num_blocks, Hkv, bs, dh, block_stride) of a K/V cache pair that may be
+    views into a pool of padded pages: inside a block the tensors must be
+    dense; the block stride (bytes) is stride(0), the same for K and V."""
+    nb, Hkv, bs, dh = _cache_dims(k_cache, v_cache)
+    if k_cache.stride()[1:] != (dh * bs, 16 * bs, 16, 1) or v_cache.stride()[1:] != (dh * bs, bs, 1):
+        raise ValueError("caches must be dense inside each block")
+    if k_cache.stride(0) != v_cache.stride(0):
+        raise ValueError("k_cache and v_cache must share one block stride")
+    return nb, Hkv, bs, dh, k_cache.stride(0)
+
+
+def kvq_cache_write_paged(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, fmt, gran,
+                          stream=None) -> None:
+    """kvq_cache_write on caches whose blocks sit block_stride = k_cache.stride(0)
+    bytes apart (views into a pool of padded pages)."""
+    T, Hkv, dh = k.shape
+    nb, _, bs, _, bst = _paged_dims(k_cache, v_cache)
+    _check("kvq_cache_write_paged",
+           lib().kvq_cache_write_paged(_ptr(k), _ptr(v), T, Hkv, dh, _ptr(slot_mapping),
+                                       _ptr(k_cache), _ptr(v_cache), nb, bs, bst, _ptr(k_scale),
+                                       _ptr(v_scale), _fmt(fmt), _gran(gran), _stream(stream)))
+
+
+def kvq_decode_attn_paged(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                          k_scale, v_scale, fmt, gran, softmax_scale=0.0, workspace=None,
+                          stream=None) -> None:
+    import torch
+    B, Hq, dh = q.shape
+    nb, Hkv, bs, _, bst = _paged_dims(k_cache, v_cache)
+    ws_bytes = kvq_decode_workspace_size(B, Hq, dh, max_context_len, bs)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
+    _check("kvq_decode_attn_paged",
+           lib().kvq_decode_attn_paged(_ptr(out), out_dt, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       nb, _ptr(block_tables), block_tables.shape[1],
+                                       _ptr(context_lens), B, Hq, Hkv, dh, bs, bst,
+                                       int(max_context_len), _ptr(k_scale), _ptr(v_scale),
+                                       _fmt(fmt), _gran(gran), float(softmax_scale),
+                                       _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream)))
+
+
+def kvq_prefill_attn_paged(out, q, cu_seqlens_q, max_q_len, q_scale, q_gran, k_cache, v_cache,
+                           block_tables, context_lens, k_scale, v_scale, fmt, kv_gran,
+                           softmax_scale=0.0, stream=None) -> None:
+    import torch
+    _, Hq, dh = q.shape
+    nb, Hkv, bs, _, bst = _paged_dims(k_cache, v_cache)
+    B = cu_seqlens_q.shape[0] - 1
+    out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
+    _check("kvq_prefill_attn_paged",
+           lib().kvq_prefill_attn_paged(_ptr(out), out_dt, _ptr(q), _ptr(cu_seqlens_q),
+                                        int(max_q_len), _ptr(q_scale), _gran(q_gran),
+                                        _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_tables),
+                                        block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, dh,
+                                        bs, bst, _ptr(k_scale), _ptr(v_scale), _fmt(fmt),
+                                        _gran(kv_gran), float(softmax_scale), _stream(stream)))

@@ -107,14 +107,34 @@ kvq_status kvq_calibrate_scales(const void* x_bf16, int64_t T, int H, int dh, kv
                                   (hipStream_t)stream));
 }
 
+// block_stride: validated against the natural Hkv * bs * dh after the sizes
+static kvq_status check_stride(int64_t block_stride, int Hkv, int bs, int dh) {
+  if (block_stride < (int64_t)Hkv * bs * dh) return KVQ_ERR_SHAPE;
+  if (block_stride % 16) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
 kvq_status kvq_cache_write(const void* k_bf16, const void* v_bf16, int64_t T, int Hkv, int dh,
                            const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
                            int64_t num_blocks, int bs, const float* k_scale,
                            const float* v_scale, kvq_fmt fmt, kvq_gran gran,
                            kvq_stream stream) {
+  return kvq_cache_write_paged(k_bf16, v_bf16, T, Hkv, dh, slot_mapping, k_cache, v_cache,
+                               num_blocks, bs, (int64_t)Hkv * bs * dh, k_scale, v_scale, fmt,
+                               gran, stream);
+}
+
+kvq_status kvq_cache_write_paged(const void* k_bf16, const void* v_bf16, int64_t T, int Hkv,
+                                 int dh, const int64_t* slot_mapping, uint8_t* k_cache,
+                                 uint8_t* v_cache, int64_t num_blocks, int bs,
+                                 int64_t block_stride, const float* k_scale,
+                                 const float* v_scale, kvq_fmt fmt, kvq_gran gran,
+                                 kvq_stream stream) {
   if (!fmt_ok(fmt) || !gran_ok(gran)) return KVQ_ERR_UNSUPPORTED;
   if (T < 0 || Hkv < 1 || num_blocks < 1) return KVQ_ERR_SHAPE;
   if (!dh_ok(dh) || bs != 16 || Hkv > 256) return KVQ_ERR_UNSUPPORTED;
+  const kvq_status sst = check_stride(block_stride, Hkv, bs, dh);
+  if (sst != KVQ_OK) return sst;
   if ((uint64_t)T * (uint64_t)Hkv * (uint64_t)(dh / 8) >= (1ull << 32)) return KVQ_ERR_SHAPE;
   if (!k_cache || !v_cache || !k_scale || !v_scale) return KVQ_ERR_NULL;
   if (T == 0) return KVQ_OK;
@@ -124,7 +144,8 @@ kvq_status kvq_cache_write(const void* k_bf16, const void* v_bf16, int64_t T, in
     return KVQ_ERR_UNSUPPORTED;
   return map_err(launch_cache_write((const uint16_t*)k_bf16, (const uint16_t*)v_bf16, T, Hkv, dh,
                                     slot_mapping, k_cache, v_cache, num_blocks, k_scale, v_scale,
-                                    fmt, gran == KVQ_SCALE_HEAD, (hipStream_t)stream));
+                                    fmt, gran == KVQ_SCALE_HEAD, (hipStream_t)stream,
+                                    block_stride));
 }
 
 size_t kvq_decode_workspace_size(int B, int Hq, int dh, int max_context_len, int bs) {
@@ -164,9 +185,25 @@ kvq_status kvq_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
                            int max_context_len, const float* k_scale, const float* v_scale,
                            kvq_fmt fmt, kvq_gran gran, float softmax_scale, void* workspace,
                            size_t ws_bytes, kvq_stream stream) {
+  return kvq_decode_attn_paged(out, out_dtype, q_bf16, k_cache, v_cache, num_blocks, block_tables,
+                               max_blocks, context_lens, B, Hq, Hkv, dh, bs,
+                               (int64_t)Hkv * bs * dh, max_context_len, k_scale, v_scale, fmt,
+                               gran, softmax_scale, workspace, ws_bytes, stream);
+}
+
+kvq_status kvq_decode_attn_paged(void* out, kvq_out out_dtype, const void* q_bf16,
+                                 const uint8_t* k_cache, const uint8_t* v_cache,
+                                 int64_t num_blocks, const int32_t* block_tables, int max_blocks,
+                                 const int32_t* context_lens, int B, int Hq, int Hkv, int dh,
+                                 int bs, int64_t block_stride, int max_context_len,
+                                 const float* k_scale, const float* v_scale, kvq_fmt fmt,
+                                 kvq_gran gran, float softmax_scale, void* workspace,
+                                 size_t ws_bytes, kvq_stream stream) {
   kvq_status st = check_attn_common(out, out_dtype, q_bf16, k_cache, v_cache, num_blocks,
                                     block_tables, max_blocks, context_lens, B, Hq, Hkv, dh, bs,
                                     k_scale, v_scale, fmt, gran);
+  if (st != KVQ_OK) return st;
+  st = check_stride(block_stride, Hkv, bs, dh);
   if (st != KVQ_OK) return st;
   const DecodePlan plan = decode_plan(B, Hq, dh, max_context_len, bs);
   st = check_decode_ws(plan, max_context_len, max_blocks, bs, workspace, ws_bytes);
@@ -175,7 +212,7 @@ kvq_status kvq_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
                                v_cache, num_blocks, block_tables, max_blocks, context_lens, B, Hq,
                                Hkv, dh, max_context_len, k_scale, v_scale, fmt,
                                gran == KVQ_SCALE_HEAD, softmax_scale, plan, workspace,
-                               (hipStream_t)stream));
+                               (hipStream_t)stream, nullptr, nullptr, block_stride));
 }
 
 kvq_status kvq_cache_write_token_scales(const void* k_bf16, const void* v_bf16, int64_t T,
@@ -286,9 +323,26 @@ kvq_status kvq_prefill_attn(void* out, kvq_out out_dtype, const void* q_bf16,
                             const int32_t* context_lens, int B, int Hq, int Hkv, int dh, int bs,
                             const float* k_scale, const float* v_scale, kvq_fmt fmt,
                             kvq_gran kv_gran, float softmax_scale, kvq_stream stream) {
+  return kvq_prefill_attn_paged(out, out_dtype, q_bf16, cu_seqlens_q, max_q_len, q_scale, q_gran,
+                                k_cache, v_cache, num_blocks, block_tables, max_blocks,
+                                context_lens, B, Hq, Hkv, dh, bs, (int64_t)Hkv * bs * dh, k_scale,
+                                v_scale, fmt, kv_gran, softmax_scale, stream);
+}
+
+kvq_status kvq_prefill_attn_paged(void* out, kvq_out out_dtype, const void* q_bf16,
+                                  const int32_t* cu_seqlens_q, int max_q_len,
+                                  const float* q_scale, kvq_gran q_gran, const uint8_t* k_cache,
+                                  const uint8_t* v_cache, int64_t num_blocks,
+                                  const int32_t* block_tables, int max_blocks,
+                                  const int32_t* context_lens, int B, int Hq, int Hkv, int dh,
+                                  int bs, int64_t block_stride, const float* k_scale,
+                                  const float* v_scale, kvq_fmt fmt, kvq_gran kv_gran,
+                                  float softmax_scale, kvq_stream stream) {
   kvq_status st = check_attn_common(out, out_dtype, q_bf16, k_cache, v_cache, num_blocks,
                                     block_tables, max_blocks, context_lens, B, Hq, Hkv, dh, bs,
                                     k_scale, v_scale, fmt, kv_gran);
+  if (st != KVQ_OK) return st;
+  st = check_stride(block_stride, Hkv, bs, dh);
   if (st != KVQ_OK) return st;
   if (fmt == KVQ_FMT_INT8) return KVQ_ERR_UNSUPPORTED;  // FP8-domain path: FP8 caches only
   if (!gran_ok(q_gran)) return KVQ_ERR_UNSUPPORTED;
@@ -299,7 +353,74 @@ kvq_status kvq_prefill_attn(void* out, kvq_out out_dtype, const void* q_bf16,
                                 cu_seqlens_q, max_q_len, q_scale, q_gran == KVQ_SCALE_HEAD,
                                 k_cache, v_cache, num_blocks, block_tables, max_blocks,
                                 context_lens, B, Hq, Hkv, dh, k_scale, v_scale, fmt,
-                                kv_gran == KVQ_SCALE_HEAD, softmax_scale, (hipStream_t)stream));
+                                kv_gran == KVQ_SCALE_HEAD, softmax_scale, (hipStream_t)stream,
+                                block_stride));
+}
+
+// ---------------------------------------------------------------- skip-layers
+int kvq_layer_index(const char* prefix) {
+  if (!prefix) return -1;
+  int found = -1, count = 0;
+  const char* p = prefix;
+  while (true) {
+    const char* e = p;
+    while (*e && *e != '.') ++e;
+    bool digits = e > p;
+    long v = 0;
+    for (const char* c = p; c < e; ++c) {
+      if (*c < '0' || *c > '9' || v > 100000000L) {
+        digits = false;
+        break;
+      }
+      v = v * 10 + (*c - '0');
+    }
+    if (digits) {
+      ++count;
+      found = (int)v;
+    }
+    if (!*e) break;
+    p = e + 1;
+  }
+  return count == 1 ? found : -1;
+}
+
+int kvq_layer_skipped(int layer_index, int is_sliding_window, const char* const* skip_list,
+                      int n_skip) {
+  if (!skip_list || n_skip <= 0) return 0;
+  char idx[16];
+  int n = 0;
+  if (layer_index >= 0) {  // decimal text of the index
+    char rev[16];
+    int v = layer_index;
+    do {
+      rev[n++] = (char)('0' + v % 10);
+      v /= 10;
+    } while (v && n < 15);
+    for (int i = 0; i < n; ++i) idx[i] = rev[n - 1 - i];
+  }
+  idx[n] = 0;
+  for (int i = 0; i < n_skip; ++i) {
+    const char* s = skip_list[i];
+    if (!s) continue;
+    if (is_sliding_window && strcmp(s, "sliding_window") == 0) return 1;
+    if (n > 0 && strcmp(s, idx) == 0) return 1;
+  }
+  return 0;
+}
+
+uint64_t kvq_page_bytes(int Hkv, int dh, int bs, int bits_per_elem) {
+  if (Hkv < 0 || dh < 0 || bs < 0 || bits_per_elem < 0) return 0;
+  return 2ull * (uint64_t)Hkv * (uint64_t)dh * (uint64_t)bs * (uint64_t)bits_per_elem / 8ull;
+}
+
+uint64_t kvq_common_page_bytes(const int* layer_bits, int L, int Hkv, int dh, int bs) {
+  if (!layer_bits || L < 1) return 0;
+  uint64_t p = 0;
+  for (int l = 0; l < L; ++l) {
+    const uint64_t b = kvq_page_bytes(Hkv, dh, bs, layer_bits[l]);
+    p = b > p ? b : p;
+  }
+  return (p + 15) / 16 * 16;
 }
 
 }  // extern "C"

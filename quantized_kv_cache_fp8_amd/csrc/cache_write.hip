@@ -92,8 +92,9 @@ template <int FMT, int DH, bool TS>
 __global__ __launch_bounds__(256) void cache_write_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t T, int Hkv,
     const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
-    int64_t num_slots, const float* __restrict__ ks, const float* __restrict__ vs, int per_head,
-    uint16_t* __restrict__ ksc, uint16_t* __restrict__ vsc) {
+    int64_t num_slots, int64_t bstride, const float* __restrict__ ks,
+    const float* __restrict__ vs, int per_head, uint16_t* __restrict__ ksc,
+    uint16_t* __restrict__ vsc) {
   constexpr int kCq = DH / 4;  // channel quads per token row
   __shared__ int64_t s_slot[kChunk];
   __shared__ uint32_t s_run[kChunk];  // token index | run length << 8, compacted
@@ -211,8 +212,8 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     const int64_t s = s_slot[t];
     if (s < 0) continue;
     const uint4 w = *reinterpret_cast<const uint4*>(s_kt + t * kKRow + 4 * q);
-    *reinterpret_cast<uint4*>(kc + (size_t)((s >> 4) * Hkv + h) * kBs * DH + q * (kBs * 16) +
-                              (s & (kBs - 1)) * 16) = w;
+    *reinterpret_cast<uint4*>(kc + (size_t)(s >> 4) * bstride + (size_t)h * kBs * DH +
+                              q * (kBs * 16) + (s & (kBs - 1)) * 16) = w;
   }
 
   const int nrun = s_nrun;
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     // codes of tokens i..i+3 of channel c (bytes past the run are ignored)
     const uint32_t* row = s_vt + c * kRowDw + (i >> 2);
     const uint32_t w = __builtin_amdgcn_alignbyte(row[1], row[0], (uint32_t)(i & 3));
-    uint8_t* dst = vc + ((size_t)((s >> 4) * Hkv + h) * DH + c) * kBs + (s & (kBs - 1));
+    uint8_t* dst = vc + (size_t)(s >> 4) * bstride + ((size_t)h * DH + c) * kBs + (s & (kBs - 1));
     if (n == 4) {
       *reinterpret_cast<uint32_t*>(dst) = w;  // a full quad starts 4-aligned
     } else {
@@ -241,7 +242,8 @@ template <int FMT, int DH>
 __global__ __launch_bounds__(256) void cache_write_short_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint32_t units, int Hkv,
     const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
-    int64_t num_slots, const float* __restrict__ ks, const float* __restrict__ vs, int per_head) {
+    int64_t num_slots, int64_t bstride, const float* __restrict__ ks,
+    const float* __restrict__ vs, int per_head) {
   constexpr int kNc = DH / 16;  // chunks per token row
   const uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
   if (u >= units) return;
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(256) void cache_write_short_kernel(
                           quant4<FMT>(make_uint2(v0.z, v0.w), sv, rv),
                           quant4<FMT>(make_uint2(v1.x, v1.y), sv, rv),
                           quant4<FMT>(make_uint2(v1.z, v1.w), sv, rv)};
-  const size_t tile = (size_t)((s >> 4) * Hkv + h) * kBs * DH;
+  const size_t tile = (size_t)(s >> 4) * bstride + (size_t)h * kBs * DH;
   const int off = (int)(s & (kBs - 1));
   *reinterpret_cast<uint4*>(kc + tile + q * (kBs * 16) + off * 16) = kq;
   uint8_t* vd = vc + tile + (size_t)q * 16 * kBs + off;  // channel 16 q, token off
@@ -277,7 +279,7 @@ template <int FMT, int DH>
 __global__ __launch_bounds__(256) void cache_write_token_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint32_t units, int Hkv,
     const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
-    uint16_t* __restrict__ ksc, uint16_t* __restrict__ vsc, int64_t num_slots) {
+    uint16_t* __restrict__ ksc, uint16_t* __restrict__ vsc, int64_t num_slots, int64_t bstride) {
   constexpr int kNc = DH / 16;  // lanes per (token, head) row
   const uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
   const bool live = u < units;  // every lane takes part in the row reductions
@@ -314,10 +316,11 @@ __global__ __launch_bounds__(256) void cache_write_token_kernel(
                           quant4<FMT>(make_uint2(v0.z, v0.w), sv, rv),
                           quant4<FMT>(make_uint2(v1.x, v1.y), sv, rv),
                           quant4<FMT>(make_uint2(v1.z, v1.w), sv, rv)};
-  const size_t row = (size_t)((s >> 4) * Hkv + h);
+  const size_t row = (size_t)((s >> 4) * Hkv + h);  // scale caches are not padded
+  const size_t tile = (size_t)(s >> 4) * bstride + (size_t)h * kBs * DH;
   const int off = (int)(s & (kBs - 1));
-  *reinterpret_cast<uint4*>(kc + row * kBs * DH + q * (kBs * 16) + off * 16) = kq;
-  uint8_t* vd = vc + row * kBs * DH + (size_t)q * 16 * kBs + off;
+  *reinterpret_cast<uint4*>(kc + tile + q * (kBs * 16) + off * 16) = kq;
+  uint8_t* vd = vc + tile + (size_t)q * 16 * kBs + off;
 #pragma unroll
   for (int c = 0; c < 16; ++c) vd[c * kBs] = (uint8_t)(vq[c >> 2] >> (8 * (c & 3)));
   if (q == 0) {
@@ -329,7 +332,8 @@ __global__ __launch_bounds__(256) void cache_write_token_kernel(
 hipError_t launch_cache_write_token(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv,
                                     int dh, const int64_t* slot, uint8_t* kc, uint8_t* vc,
                                     uint16_t* ksc, uint16_t* vsc, int64_t num_blocks, int fmt,
-                                    hipStream_t s) {
+                                    hipStream_t s, int64_t bstride) {
+  if (bstride <= 0) bstride = (int64_t)Hkv * kBs * dh;
   if (T == 0) return hipSuccess;
   const int64_t num_slots = num_blocks * kBs;
   const uint32_t units = (uint32_t)(T * Hkv * (dh / 16));
@@ -339,16 +343,16 @@ hipError_t launch_cache_write_token(const uint16_t* k, const uint16_t* v, int64_
     if (T > kShortWrite) {  // the LDS-staged kernel, one scale per token row
       if (dh == 128)
         cache_write_kernel<F, 128, true><<<grid, 256, 0, s>>>(
-            k, v, T, Hkv, slot, kc, vc, num_slots, nullptr, nullptr, 0, ksc, vsc);
+            k, v, T, Hkv, slot, kc, vc, num_slots, bstride, nullptr, nullptr, 0, ksc, vsc);
       else
         cache_write_kernel<F, 64, true><<<grid, 256, 0, s>>>(
-            k, v, T, Hkv, slot, kc, vc, num_slots, nullptr, nullptr, 0, ksc, vsc);
+            k, v, T, Hkv, slot, kc, vc, num_slots, bstride, nullptr, nullptr, 0, ksc, vsc);
     } else if (dh == 128) {
       cache_write_token_kernel<F, 128><<<(units + 255) / 256, 256, 0, s>>>(
-          k, v, units, Hkv, slot, kc, vc, ksc, vsc, num_slots);
+          k, v, units, Hkv, slot, kc, vc, ksc, vsc, num_slots, bstride);
     } else {
       cache_write_token_kernel<F, 64><<<(units + 255) / 256, 256, 0, s>>>(
-          k, v, units, Hkv, slot, kc, vc, ksc, vsc, num_slots);
+          k, v, units, Hkv, slot, kc, vc, ksc, vsc, num_slots, bstride);
     }
   });
   return hipGetLastError();
@@ -357,29 +361,32 @@ hipError_t launch_cache_write_token(const uint16_t* k, const uint16_t* v, int64_
 
 template <int FMT, int DH>
 void launch_write(int64_t T, int Hkv, const uint16_t* k, const uint16_t* v, const int64_t* slot,
-                  uint8_t* kc, uint8_t* vc, int64_t num_slots, const float* ks, const float* vs,
-                  int per_head, hipStream_t s) {
+                  uint8_t* kc, uint8_t* vc, int64_t num_slots, int64_t bstride, const float* ks,
+                  const float* vs, int per_head, hipStream_t s) {
   if (T <= kShortWrite) {
     const uint32_t units = (uint32_t)(T * Hkv * (DH / 16));
     cache_write_short_kernel<FMT, DH><<<(units + 255) / 256, 256, 0, s>>>(
-        k, v, units, Hkv, slot, kc, vc, num_slots, ks, vs, per_head);
+        k, v, units, Hkv, slot, kc, vc, num_slots, bstride, ks, vs, per_head);
     return;
   }
   const uint32_t grid = (uint32_t)(((T + kChunk - 1) / kChunk) * Hkv);
-  cache_write_kernel<FMT, DH, false><<<grid, 256, 0, s>>>(k, v, T, Hkv, slot, kc, vc, num_slots,
-                                                           ks, vs, per_head, nullptr, nullptr);
+  cache_write_kernel<FMT, DH, false><<<grid, 256, 0, s>>>(
+      k, v, T, Hkv, slot, kc, vc, num_slots, bstride, ks, vs, per_head, nullptr, nullptr);
 }
 
 hipError_t launch_cache_write(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv, int dh,
                               const int64_t* slot, uint8_t* kc, uint8_t* vc, int64_t num_blocks,
                               const float* ks, const float* vs, int fmt, int per_head,
-                              hipStream_t s) {
+                              hipStream_t s, int64_t bstride) {
   if (T == 0) return hipSuccess;
   const int64_t num_slots = num_blocks * kBs;
+  if (bstride <= 0) bstride = (int64_t)Hkv * kBs * dh;
   dispatch_fmt(fmt, [&](auto f) {
     constexpr int F = decltype(f)::value;
-    if (dh == 128) launch_write<F, 128>(T, Hkv, k, v, slot, kc, vc, num_slots, ks, vs, per_head, s);
-    else launch_write<F, 64>(T, Hkv, k, v, slot, kc, vc, num_slots, ks, vs, per_head, s);
+    if (dh == 128)
+      launch_write<F, 128>(T, Hkv, k, v, slot, kc, vc, num_slots, bstride, ks, vs, per_head, s);
+    else
+      launch_write<F, 64>(T, Hkv, k, v, slot, kc, vc, num_slots, bstride, ks, vs, per_head, s);
   });
   return hipGetLastError();
 }

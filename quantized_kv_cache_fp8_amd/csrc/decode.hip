@@ -101,7 +101,7 @@ template <int FMT, int DH, int NPW, int HPL>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(KVQ_DECODE_WAVES_PER_EU, KVQ_DECODE_WAVES_PER_EU))) void
 decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
-                    const uint8_t* __restrict__ vc, int64_t num_blocks,
+                    const uint8_t* __restrict__ vc, int64_t num_blocks, int64_t bstride,
                     const int32_t* __restrict__ bt, int max_blocks,
                     const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int NH, int rph_shift,
                     int max_ctx, const float* __restrict__ ks, int per_head, float sm_scale,
@@ -164,7 +164,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   uint2 vr[NV], vr2[NV];
   auto block_src = [&](int bi) {
     bi = bi < nblk ? bi : nblk - 1;
-    return (size_t)clamp_block(btab[bi], num_blocks) * Hkv + h;
+    return (size_t)clamp_block(btab[bi], num_blocks) * bstride + (size_t)h * tile;
   };
   auto load_k = [&](int p, i32x8 (&kr)[2]) {
 #pragma unroll
@@ -174,7 +174,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
         // chunks g4 and DH/32 + g4 (channels 16 g4 + [0,16) and DH/2 + 16 g4 + [0,16))
         // of token c16: each of the two loads covers 16 tokens x 4 chunks, i.e.
         // DH/32 KB of contiguous tile
-        const uint8_t* src = kc + block_src(2 * p + e) * tile + g4 * 256 + c16 * 16;
+        const uint8_t* src = kc + block_src(2 * p + e) + g4 * 256 + c16 * 16;
         const uint4 a0 = load16(src);
         const uint4 a1 = load16(src + HALF * 16);
         kr[e] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
@@ -183,7 +183,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     }
   };
   auto load_v = [&](int p, uint2 (&vr)[NV]) {
-    const uint8_t* src = vc + block_src(2 * p + eb) * tile + c16 * kBlockSize + tk;
+    const uint8_t* src = vc + block_src(2 * p + eb) + c16 * kBlockSize + tk;
 #pragma unroll
     for (int n = 0; n < NV; ++n) vr[n] = load8(src + 16 * n * kBlockSize);
   };
@@ -377,7 +377,7 @@ __attribute__((amdgpu_waves_per_eu(TS ? KVQ_DECODE_TS_WAVES_PER_EU : KVQ_DECODE_
                                     TS ? KVQ_DECODE_TS_WAVES_PER_EU : KVQ_DECODE_G4_WAVES_PER_EU)))
 void
 decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
-                       const uint8_t* __restrict__ vc, int64_t num_blocks,
+                       const uint8_t* __restrict__ vc, int64_t num_blocks, int64_t bstride,
                        const int32_t* __restrict__ bt, int max_blocks,
                        const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int NH,
                        int rph_shift, int max_ctx, const float* __restrict__ ks, int per_head,
@@ -428,23 +428,23 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   i32x8 kr[2];
   uint4 vq[2][NC];  // [block of the pair][half]: 16 token codes of channel 64 half + lane
   uint32_t tsc[2];  // fp16 scales of token c16 of each block, sK | sV << 16 (TS)
-  auto block_src = [&](int bi) {
+  auto block_id = [&](int bi) {
     bi = bi < nblk ? bi : nblk - 1;
-    return (size_t)clamp_block(btab[bi], num_blocks) * Hkv + h;
+    return (size_t)clamp_block(btab[bi], num_blocks);
   };
   auto load_k = [&](int p) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       kr[e] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
       if (chan_live) {
-        const uint8_t* src = kc + block_src(2 * p + e) * tile + g4 * 256 + c16 * 16;
+        const uint8_t* src = kc + block_id(2 * p + e) * bstride + h * tile + g4 * 256 + c16 * 16;
         const uint4 a0 = load16(src);
         const uint4 a1 = load16(src + HALF * 16);
         kr[e] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                       (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
       }
-      if constexpr (TS) {
-        const size_t si = block_src(2 * p + e) * kBlockSize + c16;
+      if constexpr (TS) {  // scale caches are [num_blocks][Hkv][16], never padded
+        const size_t si = (block_id(2 * p + e) * Hkv + h) * kBlockSize + c16;
         tsc[e] = (uint32_t)ksc[si] | ((uint32_t)vsc[si] << 16);
       }
     }
@@ -452,7 +452,7 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   auto load_v = [&](int p) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const uint8_t* src = vc + block_src(2 * p + e) * tile + lane * kBlockSize;
+      const uint8_t* src = vc + block_id(2 * p + e) * bstride + h * tile + lane * kBlockSize;
 #pragma unroll
       for (int c = 0; c < NC; ++c) vq[e][c] = load16(src + c * 64 * kBlockSize);
     }
@@ -695,8 +695,9 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
                          int max_blocks, const int32_t* ctx, int B, int Hq, int Hkv, int dh,
                          int max_ctx, const float* ks, const float* vs, int fmt, int per_head,
                          float softmax_scale, const DecodePlan& plan, void* ws, hipStream_t s,
-                         const uint16_t* ksc, const uint16_t* vsc) {
+                         const uint16_t* ksc, const uint16_t* vsc, int64_t bstride) {
   const bool ts = ksc != nullptr;  // per-token-head fp16 scales (groups of <= 4 heads only)
+  if (bstride <= 0) bstride = (int64_t)Hkv * kBlockSize * dh;
   const int G = Hq / Hkv;
   const int NH = heads_per_group(G);
   float* ml = reinterpret_cast<float*>(ws);
@@ -709,13 +710,13 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
   const int rph_shift = 4 - nhp_shift;         // RPH = 16 / NHp rows per head
   if (max_ctx > 0) {
 #define KVQ_SPLIT(F, D, N, HP)                                                               \
-  decode_split_kernel<F, D, N, HP><<<grid, 256, lds, s>>>(q, kc, vc, num_blocks, bt,          \
+  decode_split_kernel<F, D, N, HP><<<grid, 256, lds, s>>>(q, kc, vc, num_blocks, bstride, bt, \
                                                           max_blocks, ctx, Hq, Hkv, NH,       \
                                                           rph_shift, max_ctx, ks, per_head,   \
                                                           sm, plan.nsplit, ml, acc)
 #define KVQ_SPLIT_G4(F, D, N, T)                                                           \
   decode_split_g4_kernel<F, D, N, T><<<grid, 256, lds, s>>>(                                 \
-      q, kc, vc, num_blocks, bt, max_blocks, ctx, Hq, Hkv, NH, rph_shift, max_ctx, ks,       \
+      q, kc, vc, num_blocks, bstride, bt, max_blocks, ctx, Hq, Hkv, NH, rph_shift, max_ctx, ks, \
       per_head, sm, plan.nsplit, ml, acc, ksc, vsc)
 #define KVQ_SPLIT_HP(F, D, N)                                     \
   do {                                                            \

@@ -21,14 +21,17 @@ hipError_t launch_calibrate(const uint16_t* x, int64_t T, int H, int dh, int fmt
 hipError_t launch_cache_write(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv, int dh,
                               const int64_t* slot, uint8_t* kc, uint8_t* vc, int64_t num_blocks,
                               const float* ks, const float* vs, int fmt, int per_head,
-                              hipStream_t s);
+                              hipStream_t s, int64_t bstride = 0);
+
+// bstride: bytes from one cache block to the next in k_cache and in v_cache
+// (0 = the natural Hkv * 16 * dh; larger = pages padded to a common size).
 
 // Quantize-on-write with one fp16 scale per (token, KV head) for K and for V,
 // computed from the row's own amax; ksc/vsc are [num_blocks][Hkv][16] caches.
 hipError_t launch_cache_write_token(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv,
                                     int dh, const int64_t* slot, uint8_t* kc, uint8_t* vc,
                                     uint16_t* ksc, uint16_t* vsc, int64_t num_blocks, int fmt,
-                                    hipStream_t s);
+                                    hipStream_t s, int64_t bstride = 0);
 
 // Split-K decode geometry, shared by the workspace query and the launch.
 struct DecodePlan {
@@ -43,7 +46,8 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
                          int max_blocks, const int32_t* ctx, int B, int Hq, int Hkv, int dh,
                          int max_ctx, const float* ks, const float* vs, int fmt, int per_head,
                          float softmax_scale, const DecodePlan& plan, void* ws, hipStream_t s,
-                         const uint16_t* ksc = nullptr, const uint16_t* vsc = nullptr);
+                         const uint16_t* ksc = nullptr, const uint16_t* vsc = nullptr,
+                         int64_t bstride = 0);
 
 // Log-sum-exp merge of split partials ([B][Hq][nsplit] (m, l) pairs and dh
 // partial sums) into out, times vs (null: 1).  part_blocks > 0: sequence b's
@@ -75,6 +79,6 @@ hipError_t launch_prefill(void* out, int out_bf16, const uint16_t* q, const int3
                           const uint8_t* vc, int64_t num_blocks, const int32_t* bt,
                           int max_blocks, const int32_t* ctx, int B, int Hq, int Hkv, int dh,
                           const float* ks, const float* vs, int fmt, int kv_per_head,
-                          float softmax_scale, hipStream_t s);
+                          float softmax_scale, hipStream_t s, int64_t bstride = 0);
 
 }  // namespace kvq

@@ -69,7 +69,8 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
     void* __restrict__ out, int out_bf16, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ cu, int n_qtiles, const float* __restrict__ qs, int q_per_head,
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc, int64_t num_blocks,
-    const int32_t* __restrict__ bt, int max_blocks, const int32_t* __restrict__ ctx_lens, int Hq,
+    int64_t bstride, const int32_t* __restrict__ bt, int max_blocks,
+    const int32_t* __restrict__ ctx_lens, int Hq,
     int Hkv, const float* __restrict__ ks, const float* __restrict__ vs, int kv_per_head,
     float sm_scale) {
   constexpr int NT = 64 * GT;          // threads
@@ -161,7 +162,7 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
       live[j] = kt * 4 + j < nblk_ctx;
       int64_t blk = __builtin_amdgcn_readlane(idv, j);
       blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
-      base[j] = ((size_t)blk * Hkv + h) * tile_stride;
+      base[j] = (size_t)blk * bstride + (size_t)h * tile_stride;
     }
     auto pick = [&](int j, size_t& off, bool& ok) {
       off = j == 0 ? base[0] : j == 1 ? base[1] : j == 2 ? base[2] : base[3];
@@ -376,17 +377,18 @@ template <int FMT, int DH>
 static void launch_prefill_gt(int GT, dim3 grid, hipStream_t s, void* out, int out_bf16,
                               const uint16_t* q, const int32_t* cu, int nqt, const float* qs,
                               int qph, const uint8_t* kc, const uint8_t* vc, int64_t nb,
+                              int64_t bstride,
                               const int32_t* bt, int mb, const int32_t* ctx, int Hq, int Hkv,
                               const float* ks, const float* vs, int kvph, float sm) {
   if (GT == 4)
     prefill_kernel<FMT, DH, 4><<<grid, 256, 0, s>>>(out, out_bf16, q, cu, nqt, qs, qph, kc, vc, nb,
-                                                    bt, mb, ctx, Hq, Hkv, ks, vs, kvph, sm);
+                                                    bstride, bt, mb, ctx, Hq, Hkv, ks, vs, kvph, sm);
   else if (GT == 2)
     prefill_kernel<FMT, DH, 2><<<grid, 128, 0, s>>>(out, out_bf16, q, cu, nqt, qs, qph, kc, vc, nb,
-                                                    bt, mb, ctx, Hq, Hkv, ks, vs, kvph, sm);
+                                                    bstride, bt, mb, ctx, Hq, Hkv, ks, vs, kvph, sm);
   else
     prefill_kernel<FMT, DH, 1><<<grid, 64, 0, s>>>(out, out_bf16, q, cu, nqt, qs, qph, kc, vc, nb,
-                                                   bt, mb, ctx, Hq, Hkv, ks, vs, kvph, sm);
+                                                   bstride, bt, mb, ctx, Hq, Hkv, ks, vs, kvph, sm);
 }
 
 hipError_t launch_prefill(void* out, int out_bf16, const uint16_t* q, const int32_t* cu,
@@ -394,7 +396,8 @@ hipError_t launch_prefill(void* out, int out_bf16, const uint16_t* q, const int3
                           const uint8_t* vc, int64_t num_blocks, const int32_t* bt,
                           int max_blocks, const int32_t* ctx, int B, int Hq, int Hkv, int dh,
                           const float* ks, const float* vs, int fmt, int kv_per_head,
-                          float softmax_scale, hipStream_t s) {
+                          float softmax_scale, hipStream_t s, int64_t bstride) {
+  if (bstride <= 0) bstride = (int64_t)Hkv * 16 * dh;
   const int G = Hq / Hkv;
   const int GT = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
   const int nqt = (max_q_len + kQT - 1) / kQT;
@@ -403,17 +406,17 @@ hipError_t launch_prefill(void* out, int out_bf16, const uint16_t* q, const int3
   if (fmt == E4M3) {
     if (dh == 128)
       launch_prefill_gt<E4M3, 128>(GT, grid, s, out, out_bf16, q, cu, nqt, qs, q_per_head, kc, vc,
-                                   num_blocks, bt, max_blocks, ctx, Hq, Hkv, ks, vs, kv_per_head, sm);
+                                   num_blocks, bstride, bt, max_blocks, ctx, Hq, Hkv, ks, vs, kv_per_head, sm);
     else
       launch_prefill_gt<E4M3, 64>(GT, grid, s, out, out_bf16, q, cu, nqt, qs, q_per_head, kc, vc,
-                                  num_blocks, bt, max_blocks, ctx, Hq, Hkv, ks, vs, kv_per_head, sm);
+                                  num_blocks, bstride, bt, max_blocks, ctx, Hq, Hkv, ks, vs, kv_per_head, sm);
   } else {
     if (dh == 128)
       launch_prefill_gt<E5M2, 128>(GT, grid, s, out, out_bf16, q, cu, nqt, qs, q_per_head, kc, vc,
-                                   num_blocks, bt, max_blocks, ctx, Hq, Hkv, ks, vs, kv_per_head, sm);
+                                   num_blocks, bstride, bt, max_blocks, ctx, Hq, Hkv, ks, vs, kv_per_head, sm);
     else
       launch_prefill_gt<E5M2, 64>(GT, grid, s, out, out_bf16, q, cu, nqt, qs, q_per_head, kc, vc,
-                                  num_blocks, bt, max_blocks, ctx, Hq, Hkv, ks, vs, kv_per_head, sm);
+                                  num_blocks, bstride, bt, max_blocks, ctx, Hq, Hkv, ks, vs, kv_per_head, sm);
   }
   return hipGetLastError();
 }

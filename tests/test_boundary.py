@@ -181,3 +181,53 @@ def test_kivi_decode_validation():
     assert st(wsb=16) == -4
     assert K.kvq_kivi_decode_workspace_size(2, 8, 2, 6) > 0
     assert K.kvq_kivi_decode_workspace_size(2, 7, 2, 6) == 0
+
+
+def test_skip_rule_follows_the_guide_examples():
+    # vLLM FP8 KV-cache guide, skip-layers section: "sliding_window" skips every
+    # sliding-window layer; "0 1 23" skips exactly those layer indices
+    sw = ["sliding_window"]
+    assert K.kvq_layer_skipped(3, True, sw) and not K.kvq_layer_skipped(3, False, sw)
+    idx = ["0", "1", "23"]
+    assert [i for i in range(40) if K.kvq_layer_skipped(i, False, idx)] == [0, 1, 23]
+    assert not K.kvq_layer_skipped(5, True, idx)  # a sliding layer not named by index
+    assert K.kvq_layer_skipped(23, True, ["sliding_window", "23"])
+    assert not K.kvq_layer_skipped(2, False, []) and not K.kvq_layer_skipped(2, False, ["02"])
+    assert not K.kvq_layer_skipped(-1, False, ["-1"])
+
+
+def test_layer_index_from_module_prefix():
+    assert K.kvq_layer_index("model.layers.0.self_attn") == 0
+    assert K.kvq_layer_index("model.layers.23.self_attn.attn") == 23
+    assert K.kvq_layer_index("lm_head") == -1
+    assert K.kvq_layer_index("model.layers.1.mlp.experts.7") == -1  # ambiguous
+    assert K.kvq_layer_index("model.layers.x1.attn") == -1
+
+
+def test_page_bytes_and_common_page():
+    # bf16 pages are twice the FP8 ones; every layer pads to the largest
+    assert K.kvq_page_bytes(8, 128, 16, 8) == 2 * 8 * 128 * 16
+    assert K.kvq_page_bytes(8, 128, 16, 16) == 2 * K.kvq_page_bytes(8, 128, 16, 8)
+    assert K.kvq_common_page_bytes([8, 16, 8], 8, 128, 16) == K.kvq_page_bytes(8, 128, 16, 16)
+    assert K.kvq_common_page_bytes([8, 8], 8, 128, 16) == K.kvq_page_bytes(8, 128, 16, 8)
+    assert K.kvq_common_page_bytes([2], 1, 8, 1) == 16  # 4 bytes of 2-bit codes, rounded to 16
+    assert K.kvq_common_page_bytes([], 8, 128, 16) == 0
+
+
+def test_paged_stride_validation():
+    L = K.lib()
+    nat = 2 * 16 * 128
+    w = [FAKE, FAKE, 4, 2, 128, FAKE, FAKE, FAKE, 8, 16, nat, FAKE, FAKE, 0, 0, None]
+    assert L.kvq_cache_write_paged(*w) != -2
+    w[10] = nat - 16
+    assert L.kvq_cache_write_paged(*w) == -2
+    w[10] = nat + 8
+    assert L.kvq_cache_write_paged(*w) == -3
+    d = dict(out=FAKE, odt=0, q=FAKE, kc=FAKE, vc=FAKE, nb=10, bt=FAKE, mb=4, cl=FAKE, B=2, Hq=8,
+             Hkv=2, dh=128, bs=16, bst=nat - 16, maxctx=64, ks=FAKE, vs=FAKE, fmt=0, gran=0,
+             sm=0.0, ws=FAKE, wsb=0, stream=None)
+    assert L.kvq_decode_attn_paged(*d.values()) == -2
+    p = dict(out=FAKE, odt=0, q=FAKE, cu=FAKE, maxq=8, qs=FAKE, qg=0, kc=FAKE, vc=FAKE, nb=4,
+             bt=FAKE, mb=4, cl=FAKE, B=1, Hq=8, Hkv=2, dh=128, bs=16, bst=nat + 4, ks=FAKE,
+             vs=FAKE, fmt=0, kvg=0, sm=0.0, stream=None)
+    assert L.kvq_prefill_attn_paged(*p.values()) == -3
