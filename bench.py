@@ -138,42 +138,44 @@ def main():
         vc = torch.empty((wl.paging.num_blocks, Hkv, dh, bs), dtype=torch.uint8, device=dev)
         K.kvq_cache_write(k_all, v_all, slots_all, kc, vc, ks, vs, "fp8_e4m3", "tensor")
         caches.append((kc, vc))
-    # the step's new token of every sequence: its last position
+    # the step's new token of every sequence: its last position (already in the
+    # caches from the setup write; the step writes it again, as a decode step does)
     last = wl.kv.seq_offsets[1:] - 1
     k_new, v_new = k_all[torch.from_numpy(last).to(dev)], v_all[torch.from_numpy(last).to(dev)]
+    k_new, v_new = k_new.contiguous(), v_new.contiguous()
     slot_new = slots_all[torch.from_numpy(last).to(dev)]
     out = torch.empty((B, Hq, dh), dtype=torch.float32, device=dev)
     ws_bytes = K.kvq_decode_workspace_size(B, Hq, dh, max_ctx, bs)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
+    sh = stream.cuda_stream
+
     def step(i):
+        # one decode step: quantize-write the new token and attend, in one kernel
+        # launch (plus the split combine)
         kc, vc = caches[i % len(caches)]
-        K.kvq_cache_write(k_new, v_new, slot_new, kc, vc, ks, vs, "fp8_e4m3", "tensor")
-        K.kvq_decode_attn(out, q, kc, vc, bt, ctx, max_ctx, ks, vs, "fp8_e4m3", "tensor",
-                          workspace=ws)
+        K.kvq_decode_attn_append(out, q, k_new, v_new, kc, vc, bt, ctx, max_ctx, ks, vs,
+                                 "fp8_e4m3", "tensor", workspace=ws, stream=sh)
 
     kv_bytes = sum_ctx * Hkv * dh * 2  # FP8 K + V history read by one decode step
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # decode kernel time from HIP events on the launch stream, over the timed region
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # kernel time from HIP events on the launch stream around the timed region
+    # (the step is the one append call: split kernel + combine), averaged per step
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        kc, vc = caches[i % len(caches)]
-        K.kvq_cache_write(k_new, v_new, slot_new, kc, vc, ks, vs, "fp8_e4m3", "tensor")
-        ev[i][0].record(stream)
-        K.kvq_decode_attn(out, q, kc, vc, bt, ctx, max_ctx, ks, vs, "fp8_e4m3", "tensor",
-                          workspace=ws)
-        ev[i][1].record(stream)
+        step(i)
+    ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    dec_ms = ev0.elapsed_time(ev1) / args.steps
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (dec_ms * 1e-3) / 1e9
 
@@ -193,12 +195,13 @@ def main():
         "config": {"workload": wl.name, "B": B, "Hq": Hq, "Hkv": Hkv, "dh": dh,
                    "block_size": bs, "sum_context": sum_ctx, "max_context": max_ctx,
                    "kv_format": "e4m3", "scale": "per-tensor amax/448",
-                   "step": "cache_write(new token) + decode_attn", "cache_copies": args.copies,
+                   "step": "decode_attn_append (new token quantize-write + decode, one kernel)",
+                   "cache_copies": args.copies,
                    "kv_bytes_per_step": kv_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "kvq_decode_attn (split + combine)",
+                     "kernel": "kvq_decode_attn_append (split + combine)",
                      "avg_ms": round(dec_ms, 5)},
     }
 
@@ -206,6 +209,16 @@ def main():
     if not args.no_rows:
         result["rows"] = measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches,
                                       ks, vs, wl, (q, bt, ctx, max_ctx, ws, out))
+
+        def two_calls():
+            kc, vc = caches[0]
+            K.kvq_cache_write(k_new, v_new, slot_new, kc, vc, ks, vs, "fp8_e4m3", "tensor")
+            K.kvq_decode_attn(out, q, kc, vc, bt, ctx, max_ctx, ks, vs, "fp8_e4m3", "tensor",
+                              workspace=ws)
+        ms = time_call(torch, stream, two_calls, 50)
+        result["rows"]["step_write_then_decode"] = {
+            "workload": wl.name + " (kvq_cache_write of the new tokens, then kvq_decode_attn)",
+            "ms": round(ms, 5), "GB/s": round(kv_bytes / ms / 1e6, 1)}
 
     # ------------------------------------------------------------ copy probe (untimed)
     if args.copy_probe_mib > 0:

@@ -336,6 +336,28 @@ kvq_status kvq_kivi_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16
                                 float softmax_scale, void* workspace, size_t ws_bytes,
                                 kvq_stream stream);
 
+/* Decode with the step's new token appended: for every sequence b with
+ * context_lens[b] >= 1 (clamped to max_context_len) the new token's K and V
+ * (k_new, v_new: bf16 [B][Hkv][dh]) are quantized and written at position
+ * context_lens[b] - 1, i.e. block block_tables[b][pos / bs], offset pos % bs
+ * (skipped when that block id lies outside [0, num_blocks)), and the query
+ * then attends positions 0 .. context_lens[b] - 1 as in kvq_decode_attn.
+ * The result and the cache bytes equal kvq_cache_write of those tokens
+ * followed by kvq_decode_attn; here one kernel does both ([T] 10.4.2 write
+ * rule and attention of the same step), so no launch sits between them.
+ * Groups of at most 4 query heads per KV head (Hq / Hkv <= 4); larger groups
+ * return KVQ_ERR_UNSUPPORTED.  k_new / v_new must be 16-byte aligned.
+ * Errors: as kvq_decode_attn. */
+kvq_status kvq_decode_attn_append(void* out, kvq_out out_dtype, const void* q_bf16,
+                                  const void* k_new_bf16, const void* v_new_bf16,
+                                  uint8_t* k_cache, uint8_t* v_cache, int64_t num_blocks,
+                                  const int32_t* block_tables, int max_blocks,
+                                  const int32_t* context_lens, int B, int Hq, int Hkv, int dh,
+                                  int bs, int max_context_len, const float* k_scale,
+                                  const float* v_scale, kvq_fmt fmt, kvq_gran gran,
+                                  float softmax_scale, void* workspace, size_t ws_bytes,
+                                  kvq_stream stream);
+
 /* ---------------------------------------------------------------- prefill
  * Causal chunked prefill in the FP8 domain ([G] the FlashAttention-3 note:
  * attention computed on FP8 operands with Q quantized too; [T] 10.4.5 storage

@@ -33,7 +33,7 @@ EXPORTS = ["kvq_strerror", "kvq_kv_cache_bytes", "kvq_fp8_encode", "kvq_fp8_deco
            "kvq_decode_attn_token_scales", "kvq_kivi_quantize", "kvq_kivi_decode_workspace_size",
            "kvq_kivi_decode_attn", "kvq_cache_write_paged", "kvq_decode_attn_paged",
            "kvq_prefill_attn_paged", "kvq_layer_skipped", "kvq_layer_index", "kvq_page_bytes",
-           "kvq_common_page_bytes"]
+           "kvq_common_page_bytes", "kvq_decode_attn_append"]
 
 
 class KvqError(RuntimeError):
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_page_bytes.restype = ctypes.c_uint64
         L.kvq_common_page_bytes.argtypes = [P, i32, i32, i32, i32]
         L.kvq_common_page_bytes.restype = ctypes.c_uint64
+        L.kvq_decode_attn_append.argtypes = [P, i32, P, P, P, P, P, i64, P, i32, P, i32, i32,
+                                             i32, i32, i32, i32, P, P, i32, i32, f32, P, sz, P]
         L.kvq_prefill_attn.argtypes = [P, i32, P, P, i32, P, i32, P, P, i64, P, i32, P, i32, i32,
                                        i32, i32, i32, P, P, i32, i32, f32, P]
         _lib = L
@@ -380,3 +382,26 @@ def kvq_prefill_attn_paged(out, q, cu_seqlens_q, max_q_len, q_scale, q_gran, k_c
                                         block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, dh,
                                         bs, bst, _ptr(k_scale), _ptr(v_scale), _fmt(fmt),
                                         _gran(kv_gran), float(softmax_scale), _stream(stream)))
+
+
+def kvq_decode_attn_append(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                           max_context_len, k_scale, v_scale, fmt, gran, softmax_scale=0.0,
+                           workspace=None, stream=None) -> None:
+    """kvq_decode_attn with the new token (k_new / v_new bf16 [B, Hkv, dh]) quantized
+    into position context_lens[b] - 1 by the same kernel."""
+    import torch
+    B, Hq, dh = q.shape
+    nb, Hkv, bs, _ = _cache_dims(k_cache, v_cache)
+    if workspace is None:
+        ws_bytes = kvq_decode_workspace_size(B, Hq, dh, max_context_len, bs)
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
+    _check("kvq_decode_attn_append",
+           lib().kvq_decode_attn_append(_ptr(out), out_dt, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                        _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_tables),
+                                        block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, dh,
+                                        bs, int(max_context_len), _ptr(k_scale), _ptr(v_scale),
+                                        _fmt(fmt), _gran(gran), float(softmax_scale),
+                                        _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream)))

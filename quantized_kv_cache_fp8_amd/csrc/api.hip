@@ -215,6 +215,34 @@ kvq_status kvq_decode_attn_paged(void* out, kvq_out out_dtype, const void* q_bf1
                                (hipStream_t)stream, nullptr, nullptr, block_stride));
 }
 
+kvq_status kvq_decode_attn_append(void* out, kvq_out out_dtype, const void* q_bf16,
+                                  const void* k_new_bf16, const void* v_new_bf16,
+                                  uint8_t* k_cache, uint8_t* v_cache, int64_t num_blocks,
+                                  const int32_t* block_tables, int max_blocks,
+                                  const int32_t* context_lens, int B, int Hq, int Hkv, int dh,
+                                  int bs, int max_context_len, const float* k_scale,
+                                  const float* v_scale, kvq_fmt fmt, kvq_gran gran,
+                                  float softmax_scale, void* workspace, size_t ws_bytes,
+                                  kvq_stream stream) {
+  kvq_status st = check_attn_common(out, out_dtype, q_bf16, k_cache, v_cache, num_blocks,
+                                    block_tables, max_blocks, context_lens, B, Hq, Hkv, dh, bs,
+                                    k_scale, v_scale, fmt, gran);
+  if (st != KVQ_OK) return st;
+  if (Hq / Hkv > 4) return KVQ_ERR_UNSUPPORTED;
+  if (!k_new_bf16 || !v_new_bf16) return KVQ_ERR_NULL;
+  if (!aligned(k_new_bf16, 16) || !aligned(v_new_bf16, 16)) return KVQ_ERR_UNSUPPORTED;
+  const DecodePlan plan = decode_plan(B, Hq, dh, max_context_len, bs);
+  st = check_decode_ws(plan, max_context_len, max_blocks, bs, workspace, ws_bytes);
+  if (st != KVQ_OK) return st;
+  return map_err(launch_decode(out, out_dtype == KVQ_OUT_BF16, (const uint16_t*)q_bf16, k_cache,
+                               v_cache, num_blocks, block_tables, max_blocks, context_lens, B, Hq,
+                               Hkv, dh, max_context_len, k_scale, v_scale, fmt,
+                               gran == KVQ_SCALE_HEAD, softmax_scale, plan, workspace,
+                               (hipStream_t)stream, nullptr, nullptr, 0,
+                               (const uint16_t*)k_new_bf16, (const uint16_t*)v_new_bf16, k_cache,
+                               v_cache));
+}
+
 kvq_status kvq_cache_write_token_scales(const void* k_bf16, const void* v_bf16, int64_t T,
                                         int Hkv, int dh, const int64_t* slot_mapping,
                                         uint8_t* k_cache, uint8_t* v_cache,

@@ -73,7 +73,7 @@ constexpr int kBlockSize = 16;  // tokens per cache block
 // [4][16 rows][32 tokens] f16, then the wave-merge buffers.
 static size_t decode_lds_bytes(int NH, int dh) {
   return 4 * 16 * 32 * sizeof(_Float16) + 2 * 4 * 16 * sizeof(float) +
-         (size_t)4 * NH * dh * sizeof(float);
+         (size_t)4 * NH * dh * sizeof(float) + 2 * (size_t)dh;  // + appended token's codes
 }
 
 // Lazy running max: it only moves when a score exceeds it by more than 2^8,
@@ -371,10 +371,16 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 //   the channel's row in the channel-major tile),
 // and each lane loads its channel's 16 token bytes per block: one 64-lane load
 // is 1 KB of contiguous tile.
-template <int FMT, int DH, int NPW, bool TS>
+// MODE 0: scales per tensor or per head; 1: per-token-head fp16 scales (TS);
+// 2: append -- the workgroup whose split holds position ctx - 1 quantizes the
+// new token (k_new / v_new), writes its codes to the cache and patches them
+// into its own K / V registers, so no workgroup reads that slot from memory.
+template <int FMT, int DH, int NPW, int MODE>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(TS ? KVQ_DECODE_TS_WAVES_PER_EU : KVQ_DECODE_G4_WAVES_PER_EU,
-                                    TS ? KVQ_DECODE_TS_WAVES_PER_EU : KVQ_DECODE_G4_WAVES_PER_EU)))
+__attribute__((amdgpu_waves_per_eu(MODE == 1 ? KVQ_DECODE_TS_WAVES_PER_EU
+                                                : KVQ_DECODE_G4_WAVES_PER_EU,
+                                    MODE == 1 ? KVQ_DECODE_TS_WAVES_PER_EU
+                                                : KVQ_DECODE_G4_WAVES_PER_EU)))
 void
 decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
                        const uint8_t* __restrict__ vc, int64_t num_blocks, int64_t bstride,
@@ -383,7 +389,10 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
                        int rph_shift, int max_ctx, const float* __restrict__ ks, int per_head,
                        float sm_scale, int nsplit, float* __restrict__ ws_ml,
                        float* __restrict__ ws_acc, const uint16_t* __restrict__ ksc,
-                       const uint16_t* __restrict__ vsc) {
+                       const uint16_t* __restrict__ vsc, const uint16_t* __restrict__ k_new,
+                       const uint16_t* __restrict__ v_new, uint8_t* kc_w, uint8_t* vc_w,
+                       const float* __restrict__ vs) {
+  constexpr bool TS = MODE == 1, APPEND = MODE == 2;
   typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
   constexpr int PB = 8 * NPW;     // blocks per split: 4 waves x NPW pairs x 2
   constexpr int HALF = DH / 2;
@@ -472,6 +481,40 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
                                           (j >> 1) * HALF + 8 * (j & 1));
     qop[j] = __builtin_bit_cast(bf16x8, w);
   }
+  // ---- append: the new token (position ctx - 1) of this sequence, if this
+  //      split holds it: its codes go to LDS (K then V channels), the cache
+  //      and, at use, into the registers of the pair that holds them
+  int p_new = -1, e_new = 0, off_new = 0;
+  uint8_t* pw = reinterpret_cast<uint8_t*>(wo + 4 * NH * DH);  // [2][DH]: K codes, V codes
+  const uint8_t* patch = pw;
+  if constexpr (APPEND) {
+    const int bi = (ctx - 1 - tok0) / kBlockSize;  // tok0 < ctx, so bi >= 0
+    if (bi < nblk) {
+      p_new = bi >> 1;
+      e_new = bi & 1;
+      off_new = (ctx - 1) & (kBlockSize - 1);
+      if (tid < 2 * DH) {
+        const bool isv = tid >= DH;
+        const int d = isv ? tid - DH : tid;
+        const uint16_t x = (isv ? v_new : k_new)[((size_t)b * Hkv + h) * DH + d];
+        const float sc = (isv ? vs : ks)[per_head ? h : 0];
+        const float qv = quotient(__uint_as_float((uint32_t)x << 16), sc, recip_rn(sc));
+        pw[tid] = (uint8_t)(enc2<FMT>(qv, qv) & 0xffu);
+      }
+      __syncthreads();
+      const int64_t raw = btab[bi];
+      if (raw >= 0 && raw < num_blocks && grp == h * gpk) {  // one writer per KV head
+        uint8_t* kt = kc_w + (size_t)raw * bstride + (size_t)h * tile;
+        uint8_t* vt = vc_w + (size_t)raw * bstride + (size_t)h * tile;
+        if (tid < DH / 16)
+          *reinterpret_cast<uint4*>(kt + tid * 256 + off_new * 16) =
+              *reinterpret_cast<const uint4*>(patch + 16 * tid);
+        else if (tid >= 64 && tid < 64 + DH)
+          vt[(tid - 64) * kBlockSize + off_new] = patch[DH + tid - 64];
+      }
+    }
+  }
+
   // with per-token-head scales sK multiplies each score and log2 sV is added
   // to the exponent that forms P (the row sum l keeps the exponent without it)
   const float zc = sm_scale * (TS ? 1.0f : ks[per_head ? h : 0]) * kLog2e;
@@ -484,6 +527,15 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
 #pragma unroll 1
   for (; p < npair; p += 4) {
     // ---- S for both blocks (bf16 matrix cores, rows replicated per head)
+    if constexpr (APPEND) {
+      if (p == p_new && c16 == off_new && chan_live) {  // the appended token's K codes
+        const uint4 a0 = *reinterpret_cast<const uint4*>(patch + 16 * g4);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(patch + HALF + 16 * g4);
+        const i32x8 kn = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                               (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        if (e_new == 0) kr[0] = kn; else kr[1] = kn;
+      }
+    }
     float z[2], zp[2];  // log2-domain score; exponent of P (z + log2 sV with TS)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -547,6 +599,23 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
           for (int c = 0; c < NC; ++c) {
             uint32_t* d = reinterpret_cast<uint32_t*>(&vq[e][c]);
             d[w] &= keep;
+          }
+        }
+      }
+    }
+    if constexpr (APPEND) {
+      if (p == p_new) {  // the appended token's V codes: byte off_new of each channel's run
+        const int wi = off_new >> 2, sh = 8 * (off_new & 3);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const uint32_t code = patch[DH + 64 * c + lane];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            if (e != e_new) continue;
+            uint32_t* d = reinterpret_cast<uint32_t*>(&vq[e][c]);
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              if (w == wi) d[w] = (d[w] & ~(0xffu << sh)) | (code << sh);
           }
         }
       }
@@ -695,8 +764,11 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
                          int max_blocks, const int32_t* ctx, int B, int Hq, int Hkv, int dh,
                          int max_ctx, const float* ks, const float* vs, int fmt, int per_head,
                          float softmax_scale, const DecodePlan& plan, void* ws, hipStream_t s,
-                         const uint16_t* ksc, const uint16_t* vsc, int64_t bstride) {
+                         const uint16_t* ksc, const uint16_t* vsc, int64_t bstride,
+                         const uint16_t* k_new, const uint16_t* v_new, uint8_t* kc_w,
+                         uint8_t* vc_w) {
   const bool ts = ksc != nullptr;  // per-token-head fp16 scales (groups of <= 4 heads only)
+  const bool app = k_new != nullptr;  // fused append (groups of <= 4 heads only)
   if (bstride <= 0) bstride = (int64_t)Hkv * kBlockSize * dh;
   const int G = Hq / Hkv;
   const int NH = heads_per_group(G);
@@ -714,14 +786,15 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
                                                           max_blocks, ctx, Hq, Hkv, NH,       \
                                                           rph_shift, max_ctx, ks, per_head,   \
                                                           sm, plan.nsplit, ml, acc)
-#define KVQ_SPLIT_G4(F, D, N, T)                                                           \
-  decode_split_g4_kernel<F, D, N, T><<<grid, 256, lds, s>>>(                                 \
+#define KVQ_SPLIT_G4(F, D, N, M)                                                           \
+  decode_split_g4_kernel<F, D, N, M><<<grid, 256, lds, s>>>(                                 \
       q, kc, vc, num_blocks, bstride, bt, max_blocks, ctx, Hq, Hkv, NH, rph_shift, max_ctx, ks, \
-      per_head, sm, plan.nsplit, ml, acc, ksc, vsc)
+      per_head, sm, plan.nsplit, ml, acc, ksc, vsc, k_new, v_new, kc_w, vc_w, vs)
 #define KVQ_SPLIT_HP(F, D, N)                                     \
   do {                                                            \
-    if (ts) KVQ_SPLIT_G4(F, D, N, true);                          \
-    else if (nhp_shift <= 2) KVQ_SPLIT_G4(F, D, N, false);        \
+    if (ts) KVQ_SPLIT_G4(F, D, N, 1);                             \
+    else if (app) KVQ_SPLIT_G4(F, D, N, 2);                       \
+    else if (nhp_shift <= 2) KVQ_SPLIT_G4(F, D, N, 0);            \
     else if (nhp_shift == 3) KVQ_SPLIT(F, D, N, 2);               \
     else KVQ_SPLIT(F, D, N, 4);                                   \
   } while (0)

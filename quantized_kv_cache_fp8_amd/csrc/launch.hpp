@@ -47,7 +47,9 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
                          int max_ctx, const float* ks, const float* vs, int fmt, int per_head,
                          float softmax_scale, const DecodePlan& plan, void* ws, hipStream_t s,
                          const uint16_t* ksc = nullptr, const uint16_t* vsc = nullptr,
-                         int64_t bstride = 0);
+                         int64_t bstride = 0, const uint16_t* k_new = nullptr,
+                         const uint16_t* v_new = nullptr, uint8_t* kc_w = nullptr,
+                         uint8_t* vc_w = nullptr);
 
 // Log-sum-exp merge of split partials ([B][Hq][nsplit] (m, l) pairs and dh
 // partial sums) into out, times vs (null: 1).  part_blocks > 0: sequence b's
