@@ -7,9 +7,9 @@
 // Design: |x| of a bf16 value is its bit pattern with the sign cleared, and
 // for non-negative floats the integer order of the bit patterns is the
 // numeric order (NaN patterns sort above +Inf).  So the whole reduction is an
-// exact, order-free integer max: packed 16-bit max in registers, a wave max
-// through DPP, a workgroup max through LDS and one global atomicMax per
-// workgroup on the fp32 image (bf16 bits << 16).  Three launches on the
+// exact, order-free integer max: packed 16-bit max in registers, a workgroup
+// max per head through LDS atomics and one global atomicMax per (workgroup,
+// head) on the fp32 image (bf16 bits << 16).  Three launches on the
 // caller's stream: clear (unless accumulating), reduce, finalize.
 #include "codec.hpp"
 #include "launch.hpp"
@@ -25,6 +25,15 @@ __global__ void amax_clear_kernel(uint32_t* amax, int n) {
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
+static int64_t gcd64(int64_t a, int64_t b) {
+  while (b) {
+    const int64_t t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
 // Packed |x| max over one 16-byte chunk (8 bf16) -> a pair of u16 maxima.
 __device__ __forceinline__ u16x2 absmax8(uint4 w) {
   const uint32_t m = 0x7fff7fffu;
@@ -34,41 +43,43 @@ __device__ __forceinline__ u16x2 absmax8(uint4 w) {
                                    __builtin_elementwise_max(c, d));
 }
 
-// grid (gx, H); 256 threads.  Workgroup (x, h) scans rows t = x*rpi + r, ...
-// of head h.  A row (t, h) is dh contiguous bf16 = dh/8 16-byte chunks.
-__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, int64_t T,
-                                                   int H, int dh, int per_head,
-                                                   uint32_t* __restrict__ amax) {
-  __shared__ uint32_t red[4];
-  const int h = blockIdx.y;
-  const int cpr = dh >> 3;             // chunks per row
-  const int rpi = 256 / cpr;           // rows per workgroup step
-  const int r = threadIdx.x / cpr, c = threadIdx.x % cpr;
+// grid (gx), 256 threads: a flat grid-stride scan over the tensor's 16-byte
+// chunks (8 bf16), consecutive threads on consecutive chunks, so every wave
+// reads 1 KB of contiguous memory per load.  The stride is a multiple of the
+// chunks per token (H * dh / 8), so each thread always lands on the same head
+// h = (chunk / (dh / 8)) % H and keeps one running max; the heads are then
+// reduced in LDS, one atomicMax per (workgroup, slot).
+__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x,
+                                                   int64_t nchunks, int H, int dh, int per_head,
+                                                   int64_t stride, uint32_t* __restrict__ amax) {
+  __shared__ uint32_t red[256];  // per head (per_head) or one slot
+  const int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cpr = dh >> 3;  // chunks per (token, head) row
+  const int h = (int)((c0 / cpr) % H);
+  for (int i = threadIdx.x; i < 256; i += 256) red[i] = 0u;
+  const uint4* src = reinterpret_cast<const uint4*>(x);
   u16x2 acc = {0, 0};
-  if (r < rpi) {
-    const int64_t step = (int64_t)gridDim.x * rpi;
-    int64_t t = (int64_t)blockIdx.x * rpi + r;
-    // two rows in flight per thread
-    for (; t + step < T; t += 2 * step) {
-      uint4 w0 = *reinterpret_cast<const uint4*>(x + ((t * H + h) * dh + c * 8));
-      uint4 w1 = *reinterpret_cast<const uint4*>(x + (((t + step) * H + h) * dh + c * 8));
-      acc = __builtin_elementwise_max(acc, __builtin_elementwise_max(absmax8(w0), absmax8(w1)));
-    }
-    if (t < T) {
-      uint4 w0 = *reinterpret_cast<const uint4*>(x + ((t * H + h) * dh + c * 8));
-      acc = __builtin_elementwise_max(acc, absmax8(w0));
-    }
+  int64_t c = c0;
+  // four chunks in flight per thread
+  for (; c + 3 * stride < nchunks; c += 4 * stride) {
+    const uint4 w0 = src[c], w1 = src[c + stride], w2 = src[c + 2 * stride],
+                w3 = src[c + 3 * stride];
+    acc = __builtin_elementwise_max(
+        acc, __builtin_elementwise_max(__builtin_elementwise_max(absmax8(w0), absmax8(w1)),
+                                       __builtin_elementwise_max(absmax8(w2), absmax8(w3))));
   }
-  uint32_t m = umax(acc.x, acc.y);
-  // wave max (64 lanes)
-  for (int off = 32; off >= 1; off >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, off));
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  for (; c < nchunks; c += stride) acc = __builtin_elementwise_max(acc, absmax8(src[c]));
+  const uint32_t m = umax(acc.x, acc.y);
+  if (per_head && H > 256) {  // more heads than LDS slots: straight to memory
+    if (m) atomicMax(amax + h, m << 16);
+    return;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
-    if (m) atomicMax(amax + (per_head ? h : 0), m << 16);
-  }
+  if (m) atomicMax(&red[per_head ? h : 0], m);  // LDS atomic: workgroup-local
+  __syncthreads();
+  const int nslot = per_head ? H : 1;
+  for (int i = threadIdx.x; i < nslot; i += 256)
+    if (red[i]) atomicMax(amax + i, red[i] << 16);
 }
 
 template <int FMT>
@@ -88,12 +99,16 @@ hipError_t launch_calibrate(const uint16_t* x, int64_t T, int H, int dh, int fmt
   uint32_t* amax = reinterpret_cast<uint32_t*>(amax_io);
   if (!accumulate) amax_clear_kernel<<<(n + 255) / 256, 256, 0, s>>>(amax, n);
   if (T > 0) {
-    const int rpi = 256 / (dh >> 3);
-    int64_t rows_wg = (T + rpi - 1) / rpi;  // workgroups that would each take one step
-    int64_t target = (int64_t)device_cu_count() * 8 / H;
-    if (target < 1) target = 1;
-    int gx = (int)(rows_wg < target ? rows_wg : target);
-    amax_kernel<<<dim3(gx, H), 256, 0, s>>>(x, T, H, dh, per_head, amax);
+    const int64_t nchunks = T * H * (dh >> 3);
+    const int64_t cpt = (int64_t)H * (dh >> 3);  // chunks per token: the stride's unit
+    // about 8 workgroups per CU, the grid's thread count a multiple of cpt
+    int64_t threads = (int64_t)device_cu_count() * 8 * 256;
+    const int64_t unit = cpt % 256 == 0 ? cpt : cpt * 256 / gcd64(cpt, 256);  // lcm(cpt, 256)
+    threads = (threads + unit - 1) / unit * unit;
+    const int64_t need = (nchunks + 255) / 256 * 256;
+    if (threads > need) threads = (need + unit - 1) / unit * unit;
+    amax_kernel<<<(uint32_t)(threads / 256), 256, 0, s>>>(x, nchunks, H, dh, per_head, threads,
+                                                          amax);
   }
   dispatch_fmt(fmt, [&](auto f) {
     scale_finalize_kernel<decltype(f)::value><<<(n + 255) / 256, 256, 0, s>>>(amax, scale_out, n);

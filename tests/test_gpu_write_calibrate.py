@@ -141,7 +141,8 @@ def same_f32(a, b):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("gran", [oracle.GRAN_TENSOR, oracle.GRAN_HEAD])
-@pytest.mark.parametrize("shape", [(1, 1, 64), (333, 6, 64), (4099, 8, 128), (50, 32, 128)])
+@pytest.mark.parametrize("shape", [(1, 1, 64), (333, 6, 64), (4099, 8, 128), (50, 32, 128), (77, 5, 64),
+                                   (7, 300, 64)])
 def test_calibrate_matches_oracle(fmt, gran, shape):
     g = W.rng(sum(shape) + fmt)
     x = W.normal_bf16(g, shape, 1, W.log_uniform(g, shape[1], 0.5, 20.0), g.choice(shape[2], 2),
