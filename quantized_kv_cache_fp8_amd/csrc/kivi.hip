@@ -53,6 +53,10 @@
 #ifndef KVQ_KIVI_WAVES_PER_EU
 #define KVQ_KIVI_WAVES_PER_EU 4
 #endif
+// Groups whose loads a wave keeps in flight (register sets: 2 or 3).
+#ifndef KVQ_KIVI_PREFETCH
+#define KVQ_KIVI_PREFETCH 2
+#endif
 
 namespace kvq {
 
@@ -207,12 +211,14 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(
 // ---------------------------------------------------------------- decode
 namespace {
 // dynamic LDS: per wave [P 4 x 32 f16][A' hi 4 x 128 f16][A' lo 4 x 128 f16]
-// [z 128 f16][V s 4 x 32 f16][V z 4 x 32 f16], then the wave-merge buffers
-// (also the residual split's q rows and scores)
+// [z 128 f16][V s 4 x 32 f16][V z 4 x 32 f16], then the workgroup's q rows in
+// f16 [4][128] and the wave-merge buffers (the residual split reuses the space
+// for its q rows and scores)
 constexpr int kWaveLds = 256 + 1024 + 1024 + 256 + 256 + 256;
 constexpr int kMaxResidual = 256;
 size_t kivi_lds_bytes(int NH) {
-  const size_t a = 4 * kWaveLds + 2 * 4 * 16 * sizeof(float) + (size_t)4 * NH * kDH * sizeof(float);
+  const size_t a = 4 * kWaveLds + 1024 + 2 * 4 * 16 * sizeof(float) +
+                   (size_t)4 * NH * kDH * sizeof(float);
   const size_t r = (size_t)4 * kDH * sizeof(float) + (size_t)4 * kMaxResidual * sizeof(float);
   return a > r ? a : r;
 }
@@ -335,28 +341,20 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
   _Float16* zb = reinterpret_cast<_Float16*>(wl_base + 2304);    // K zeros [128]
   uint16_t* vsS = reinterpret_cast<uint16_t*>(wl_base + 2560);   // V scales [4][32]
   uint16_t* vsZ = reinterpret_cast<uint16_t*>(wl_base + 2816);   // V zeros [4][32]
-  float* wm = reinterpret_cast<float*>(smem + 4 * kWaveLds);
+  _Float16* qsh = reinterpret_cast<_Float16*>(smem + 4 * kWaveLds);  // q rows [4][128]
+  float* wm = reinterpret_cast<float*>(smem + 4 * kWaveLds + 1024);
   float* wlsum = wm + 4 * 16;
   float* wo = wlsum + 4 * 16;  // [4][NH][128]
 
-  // q operands: A of the bias product (f16, rows replicated per head) and the
-  // two channels 2 lane, 2 lane + 1 of every head (fp32) for A' = q s
-  f16x8 qh[4];
-  float qa[4][2];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    qh[j] = f16x8{};
-    if (head_a < NH) {
-      const uint4 w = *reinterpret_cast<const uint4*>(
-          q + ((size_t)b * Hq + hq0 + head_a) * kDH + 32 * j + 8 * g4);
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qh[j][2 * e] = (_Float16)__uint_as_float(u[e] << 16);
-        qh[j][2 * e + 1] = (_Float16)__uint_as_float(u[e] & 0xffff0000u);
-      }
-    }
+  // q operands: the workgroup's q rows in f16 in LDS (A of the bias product,
+  // rows of heads >= NH zero) and the two channels 2 lane, 2 lane + 1 of every
+  // head (fp32) for A' = q s
+  for (int i = tid; i < 4 * kDH; i += 256) {
+    const int hh = i / kDH;
+    qsh[i] = hh < NH ? (_Float16)bf16_to_f32(q[((size_t)b * Hq + hq0 + hh) * kDH + i % kDH])
+                     : (_Float16)0.0f;
   }
+  float qa[4][2];
 #pragma unroll
   for (int hh = 0; hh < 4; ++hh) {
     qa[hh][0] = qa[hh][1] = 0.0f;
@@ -389,6 +387,7 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
   // output rows nobody reads, so the operand loads need no masking)
   for (int i = lane; i < (256 + 2048) / 16; i += 64)
     reinterpret_cast<uint4*>(wl_base)[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();  // the q rows are read by every wave
 
   float m_run = kNegBig, l_part = 0.0f;
   f32x4 O[2];
@@ -420,7 +419,8 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const f16x8 zop = *reinterpret_cast<const f16x8*>(zb + 32 * j + 8 * g4);
-      Cb = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[j], zop, Cb, 0, 0, 0);
+      const f16x8 qop = *reinterpret_cast<const f16x8*>(qsh + head_a * kDH + 32 * j + 8 * g4);
+      Cb = __builtin_amdgcn_mfma_f32_16x16x32_f16(qop, zop, Cb, 0, 0, 0);
     }
     f32x4 S0 = Cb, S1 = Cb;
 #pragma unroll
@@ -495,6 +495,25 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
     }
   };
 
+#if KVQ_KIVI_PREFETCH >= 3
+  // three register sets in turn: the next two groups' loads are in flight
+  // while the current one is processed
+  Regs r0, r1, r2;
+  int gi = wave;
+  if (gi < ngs) load(r0, gi);
+  if (gi + 4 < ngs) load(r1, gi + 4);
+#pragma unroll 1
+  for (; gi < ngs; gi += 12) {
+    if (gi + 8 < ngs) load(r2, gi + 8);
+    step(r0);
+    if (gi + 4 >= ngs) break;
+    if (gi + 12 < ngs) load(r0, gi + 12);
+    step(r1);
+    if (gi + 8 >= ngs) break;
+    if (gi + 16 < ngs) load(r1, gi + 16);
+    step(r2);
+  }
+#else
   // two register sets in turn: the next group's loads are in flight while
   // the current one is processed
   Regs ra, rb;
@@ -508,6 +527,7 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
     if (gi + 8 < ngs) load(ra, gi + 8);
     step(rb);
   }
+#endif
 
   // ---- merge the 4 waves through LDS and write the split's partial
   float x = l_part;
