@@ -345,8 +345,7 @@ kvq_status kvq_kivi_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16
  * The result and the cache bytes equal kvq_cache_write of those tokens
  * followed by kvq_decode_attn; here one kernel does both ([T] 10.4.2 write
  * rule and attention of the same step), so no launch sits between them.
- * Groups of at most 4 query heads per KV head (Hq / Hkv <= 4); larger groups
- * return KVQ_ERR_UNSUPPORTED.  k_new / v_new must be 16-byte aligned.
+ * k_new / v_new must be 16-byte aligned.
  * Errors: as kvq_decode_attn. */
 kvq_status kvq_decode_attn_append(void* out, kvq_out out_dtype, const void* q_bf16,
                                   const void* k_new_bf16, const void* v_new_bf16,

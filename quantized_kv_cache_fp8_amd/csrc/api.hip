@@ -228,7 +228,6 @@ kvq_status kvq_decode_attn_append(void* out, kvq_out out_dtype, const void* q_bf
                                     block_tables, max_blocks, context_lens, B, Hq, Hkv, dh, bs,
                                     k_scale, v_scale, fmt, gran);
   if (st != KVQ_OK) return st;
-  if (Hq / Hkv > 4) return KVQ_ERR_UNSUPPORTED;
   if (!k_new_bf16 || !v_new_bf16) return KVQ_ERR_NULL;
   if (!aligned(k_new_bf16, 16) || !aligned(v_new_bf16, 16)) return KVQ_ERR_UNSUPPORTED;
   const DecodePlan plan = decode_plan(B, Hq, dh, max_context_len, bs);

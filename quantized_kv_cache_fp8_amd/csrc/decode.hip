@@ -97,7 +97,48 @@ struct LaneHeads {
   static constexpr int kStride = 4 / HPL;  // S register of distinct head i: r = i * kStride
 };
 
-template <int FMT, int DH, int NPW, int HPL>
+// Append (decode step with the new token fused in): if this workgroup's split
+// holds position ctx - 1, quantize that token's K and V for head h (the write
+// kernels' codec arithmetic) into pw [2][DH] in LDS, store them into the cache
+// when `writer` (one workgroup per KV head), and return the block pair,
+// block and offset at which the caller patches them into its registers.
+// Every thread of the workgroup calls it (it holds a barrier).
+template <int FMT, int DH>
+__device__ __forceinline__ void append_prologue(
+    int ctx, int tok0, int nblk, const int32_t* __restrict__ btab, int64_t num_blocks,
+    int64_t bstride, int h, int Hkv, int b, bool writer, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const float* __restrict__ ks,
+    const float* __restrict__ vs, int per_head, uint8_t* kc_w, uint8_t* vc_w, uint8_t* pw,
+    int& p_new, int& e_new, int& off_new) {
+  const int bi = (ctx - 1 - tok0) / kBlockSize;  // tok0 < ctx, so bi >= 0
+  if (bi >= nblk) return;                        // the same for the whole workgroup
+  const int tid = threadIdx.x;
+  const size_t tile = (size_t)kBlockSize * DH;
+  p_new = bi >> 1;
+  e_new = bi & 1;
+  off_new = (ctx - 1) & (kBlockSize - 1);
+  if (tid < 2 * DH) {
+    const bool isv = tid >= DH;
+    const int d = isv ? tid - DH : tid;
+    const uint16_t x = (isv ? v_new : k_new)[((size_t)b * Hkv + h) * DH + d];
+    const float sc = (isv ? vs : ks)[per_head ? h : 0];
+    const float qv = quotient(__uint_as_float((uint32_t)x << 16), sc, recip_rn(sc));
+    pw[tid] = (uint8_t)(enc2<FMT>(qv, qv) & 0xffu);
+  }
+  __syncthreads();
+  const int64_t raw = btab[bi];
+  if (writer && raw >= 0 && raw < num_blocks) {
+    uint8_t* kt = kc_w + (size_t)raw * bstride + (size_t)h * tile;
+    uint8_t* vt = vc_w + (size_t)raw * bstride + (size_t)h * tile;
+    if (tid < DH / 16)
+      *reinterpret_cast<uint4*>(kt + tid * 256 + off_new * 16) =
+          *reinterpret_cast<const uint4*>(pw + 16 * tid);
+    else if (tid >= 64 && tid < 64 + DH)
+      vt[(tid - 64) * kBlockSize + off_new] = pw[DH + tid - 64];
+  }
+}
+
+template <int FMT, int DH, int NPW, int HPL, bool APPEND>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(KVQ_DECODE_WAVES_PER_EU, KVQ_DECODE_WAVES_PER_EU))) void
 decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
@@ -105,7 +146,9 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
                     const int32_t* __restrict__ bt, int max_blocks,
                     const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int NH, int rph_shift,
                     int max_ctx, const float* __restrict__ ks, int per_head, float sm_scale,
-                    int nsplit, float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
+                    int nsplit, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
+                    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+                    uint8_t* kc_w, uint8_t* vc_w, const float* __restrict__ vs) {
   constexpr int NV = DH / 16;   // f16 MFMAs per block pair (16 channels each)
   constexpr int PB = 8 * NPW;   // blocks per split: 4 waves x NPW pairs x 2
   constexpr int HALF = DH / 2;
@@ -209,6 +252,14 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
                                           (j >> 1) * HALF + 8 * (j & 1));
     qop[j] = __builtin_bit_cast(bf16x8, w);
   }
+  // ---- append: the new token (position ctx - 1) of this sequence
+  int p_new = -1, e_new = 0, off_new = 0;
+  uint8_t* pw = reinterpret_cast<uint8_t*>(wo + 4 * NH * DH);  // [2][DH]: K codes, V codes
+  const uint8_t* patch = pw;
+  if constexpr (APPEND)
+    append_prologue<FMT, DH>(ctx, tok0, nblk, btab, num_blocks, bstride, h, Hkv, b,
+                             grp == h * gpk, k_new, v_new, ks, vs, per_head, kc_w, vc_w, pw,
+                             p_new, e_new, off_new);
   const float zc = sm_scale * ks[per_head ? h : 0] * kLog2e;
 
   // running state per distinct head (identical across the 16 lanes of a group)
@@ -226,6 +277,15 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   auto pair_step = [&](int p, i32x8 (&kr)[2], uint2 (&vr)[NV]) {
     // ---- S for both blocks on bf16 matrix cores (codes -> bf16 is exact):
     //      lane holds head head_l[i] for token c16 of block e
+    if constexpr (APPEND) {
+      if (p == p_new && c16 == off_new && chan_live) {  // the appended token's K codes
+        const uint4 a0 = *reinterpret_cast<const uint4*>(patch + 16 * g4);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(patch + HALF + 16 * g4);
+        const i32x8 kn = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                               (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        if (e_new == 0) kr[0] = kn; else kr[1] = kn;
+      }
+    }
     float z[2][HPL];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -279,6 +339,18 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     //      Value codes of tokens past the context (the tail of the last block,
     //      or a re-read block) may hold anything, NaN included: zero them,
     //      since their zero weights would not cancel a NaN.
+    if constexpr (APPEND) {
+      // the appended token's V codes: byte off_new - tk of this lane's 8-token run
+      if (p == p_new && eb == e_new && off_new >= tk && off_new < tk + 8) {
+        const int sh = 8 * ((off_new - tk) & 3);
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+          const uint32_t code = patch[DH + 16 * n + c16];
+          if (off_new - tk < 4) vr[n].x = (vr[n].x & ~(0xffu << sh)) | (code << sh);
+          else vr[n].y = (vr[n].y & ~(0xffu << sh)) | (code << sh);
+        }
+      }
+    }
     if (2 * p + 2 > nblk_left || tok0 + (2 * p + 2) * kBlockSize > ctx) {
       const int left = ctx - (tok0 + (2 * p + eb) * kBlockSize + tk);
       const uint64_t keep = left >= 8 ? ~0ull : (left <= 0 ? 0ull : (1ull << (8 * left)) - 1);
@@ -481,39 +553,14 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
                                           (j >> 1) * HALF + 8 * (j & 1));
     qop[j] = __builtin_bit_cast(bf16x8, w);
   }
-  // ---- append: the new token (position ctx - 1) of this sequence, if this
-  //      split holds it: its codes go to LDS (K then V channels), the cache
-  //      and, at use, into the registers of the pair that holds them
+  // ---- append: the new token (position ctx - 1) of this sequence
   int p_new = -1, e_new = 0, off_new = 0;
   uint8_t* pw = reinterpret_cast<uint8_t*>(wo + 4 * NH * DH);  // [2][DH]: K codes, V codes
   const uint8_t* patch = pw;
-  if constexpr (APPEND) {
-    const int bi = (ctx - 1 - tok0) / kBlockSize;  // tok0 < ctx, so bi >= 0
-    if (bi < nblk) {
-      p_new = bi >> 1;
-      e_new = bi & 1;
-      off_new = (ctx - 1) & (kBlockSize - 1);
-      if (tid < 2 * DH) {
-        const bool isv = tid >= DH;
-        const int d = isv ? tid - DH : tid;
-        const uint16_t x = (isv ? v_new : k_new)[((size_t)b * Hkv + h) * DH + d];
-        const float sc = (isv ? vs : ks)[per_head ? h : 0];
-        const float qv = quotient(__uint_as_float((uint32_t)x << 16), sc, recip_rn(sc));
-        pw[tid] = (uint8_t)(enc2<FMT>(qv, qv) & 0xffu);
-      }
-      __syncthreads();
-      const int64_t raw = btab[bi];
-      if (raw >= 0 && raw < num_blocks && grp == h * gpk) {  // one writer per KV head
-        uint8_t* kt = kc_w + (size_t)raw * bstride + (size_t)h * tile;
-        uint8_t* vt = vc_w + (size_t)raw * bstride + (size_t)h * tile;
-        if (tid < DH / 16)
-          *reinterpret_cast<uint4*>(kt + tid * 256 + off_new * 16) =
-              *reinterpret_cast<const uint4*>(patch + 16 * tid);
-        else if (tid >= 64 && tid < 64 + DH)
-          vt[(tid - 64) * kBlockSize + off_new] = patch[DH + tid - 64];
-      }
-    }
-  }
+  if constexpr (APPEND)
+    append_prologue<FMT, DH>(ctx, tok0, nblk, btab, num_blocks, bstride, h, Hkv, b,
+                             grp == h * gpk, k_new, v_new, ks, vs, per_head, kc_w, vc_w, pw,
+                             p_new, e_new, off_new);
 
   // with per-token-head scales sK multiplies each score and log2 sV is added
   // to the exponent that forms P (the row sum l keeps the exponent without it)
@@ -781,11 +828,17 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
   while ((1 << nhp_shift) < NH) ++nhp_shift;  // NHp = 2^nhp_shift >= NH
   const int rph_shift = 4 - nhp_shift;         // RPH = 16 / NHp rows per head
   if (max_ctx > 0) {
-#define KVQ_SPLIT(F, D, N, HP)                                                               \
-  decode_split_kernel<F, D, N, HP><<<grid, 256, lds, s>>>(q, kc, vc, num_blocks, bstride, bt, \
-                                                          max_blocks, ctx, Hq, Hkv, NH,       \
-                                                          rph_shift, max_ctx, ks, per_head,   \
-                                                          sm, plan.nsplit, ml, acc)
+#define KVQ_SPLIT(F, D, N, HP)                                                              \
+  do {                                                                                      \
+    if (app)                                                                                \
+      decode_split_kernel<F, D, N, HP, true><<<grid, 256, lds, s>>>(                         \
+          q, kc, vc, num_blocks, bstride, bt, max_blocks, ctx, Hq, Hkv, NH, rph_shift,       \
+          max_ctx, ks, per_head, sm, plan.nsplit, ml, acc, k_new, v_new, kc_w, vc_w, vs);    \
+    else                                                                                    \
+      decode_split_kernel<F, D, N, HP, false><<<grid, 256, lds, s>>>(                        \
+          q, kc, vc, num_blocks, bstride, bt, max_blocks, ctx, Hq, Hkv, NH, rph_shift,       \
+          max_ctx, ks, per_head, sm, plan.nsplit, ml, acc, k_new, v_new, kc_w, vc_w, vs);    \
+  } while (0)
 #define KVQ_SPLIT_G4(F, D, N, M)                                                           \
   decode_split_g4_kernel<F, D, N, M><<<grid, 256, lds, s>>>(                                 \
       q, kc, vc, num_blocks, bstride, bt, max_blocks, ctx, Hq, Hkv, NH, rph_shift, max_ctx, ks, \
@@ -793,7 +846,7 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
 #define KVQ_SPLIT_HP(F, D, N)                                     \
   do {                                                            \
     if (ts) KVQ_SPLIT_G4(F, D, N, 1);                             \
-    else if (app) KVQ_SPLIT_G4(F, D, N, 2);                       \
+    else if (nhp_shift <= 2 && app) KVQ_SPLIT_G4(F, D, N, 2);     \
     else if (nhp_shift <= 2) KVQ_SPLIT_G4(F, D, N, 0);            \
     else if (nhp_shift == 3) KVQ_SPLIT(F, D, N, 2);               \
     else KVQ_SPLIT(F, D, N, 4);                                   \

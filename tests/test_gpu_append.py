@@ -69,7 +69,8 @@ def both_paths(wl, out_dtype="f32"):
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "int8"])
 @pytest.mark.parametrize("gran", ["tensor", "head"])
-@pytest.mark.parametrize("Hq,Hkv,dh", [(32, 8, 128), (16, 8, 64), (8, 8, 128)])
+@pytest.mark.parametrize("Hq,Hkv,dh", [(32, 8, 128), (16, 8, 64), (8, 8, 128), (64, 8, 128),
+                                       (24, 4, 64), (32, 2, 128)])
 def test_append_equals_write_then_decode(fmt, gran, Hq, Hkv, dh):
     """Ragged contexts put the new token first, last and inside blocks, in the
     first split and in partial last splits."""
