@@ -153,3 +153,22 @@ def test_full_size_sampled_rows(which):
     got = out[rows[:, 0], rows[:, 1]]
     check(got, ref)
     assert np.all(np.isfinite(out))
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (64, 8)])
+def test_explicit_softmax_scale(Hq, Hkv):
+    """A caller-given softmax scale in place of 1/sqrt(dh), for both kernels."""
+    import torch
+    cl = [300, 17, 1029]
+    wl = W.decode_workload("decode-sm", 107, len(cl), Hq, Hkv, 128, cl, 16, "e4m3", "head",
+                           head_range=(0.5, 4.0))
+    run = DecodeRun(wl)
+    run.gpu_scales()
+    run.gpu_write()
+    run.K.kvq_decode_attn(run.out, run.q, run.kc, run.vc, run.bt, run.cl, run.max_ctx, run.ks,
+                          run.vs, run.fmt, run.gran, softmax_scale=0.2)
+    torch.cuda.synchronize()
+    kc, vc = run.oracle_caches()
+    ref = oracle.decode_attn(wl.q, kc, vc, wl.paging.block_tables, wl.paging.context_lens,
+                             run.ks_ref, run.vs_ref, run.fmt, run.gran, 0.2)
+    check(to_np(run.out), ref)

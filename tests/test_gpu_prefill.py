@@ -54,10 +54,11 @@ class PrefillRun:
         self.out = torch.empty((wl.q.shape[0], wl.Hq, wl.dh), dtype=odt, device=dev)
         self.max_q = int(np.diff(wl.cu_seqlens).max())
 
-    def gpu(self):
+    def gpu(self, softmax_scale=0.0):
         import torch
         self.K.kvq_prefill_attn(self.out, self.q, self.cu, self.max_q, self.qs, self.qg, self.kc,
-                                self.vc, self.bt, self.cl, self.ks, self.vs, self.fmt, self.kg)
+                                self.vc, self.bt, self.cl, self.ks, self.vs, self.fmt, self.kg,
+                                softmax_scale=softmax_scale)
         torch.cuda.synchronize()
         return to_np(self.out)
 
@@ -69,12 +70,12 @@ class PrefillRun:
                            self.fmt, self.kg)
         return kc, vc
 
-    def oracle_full(self):
+    def oracle_full(self, softmax_scale=0.0):
         kc, vc = self.oracle_caches()
         wl = self.wl
         return oracle.prefill_attn(wl.q, wl.cu_seqlens, self.qs_ref, self.qg, kc, vc,
                                    wl.paging.block_tables, wl.paging.context_lens, self.ks_ref,
-                                   self.vs_ref, self.fmt, self.kg)
+                                   self.vs_ref, self.fmt, self.kg, softmax_scale)
 
 
 def check(out, ref):
@@ -153,3 +154,10 @@ def test_full_size_sampled_rows():
     got = out[rows[:, 0], rows[:, 1]]
     check(got, ref)
     assert np.all(np.isfinite(out))
+
+
+def test_explicit_softmax_scale():
+    """A caller-given softmax scale in place of 1/sqrt(dh)."""
+    wl = W.prefill_workload("prefill-sm", 314, [50, 0], [70, 33], Hq=16, Hkv=4)
+    run = PrefillRun(wl)
+    check(run.gpu(0.05), run.oracle_full(0.05))
