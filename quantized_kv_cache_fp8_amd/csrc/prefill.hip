@@ -146,6 +146,7 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
   //      registers while the current tile is computed
   constexpr int KP = kKT * DH / 16 / NT;  // K pieces (16 B) per thread
   constexpr int VP = 4 * DH / NT;         // V (block, channel) rows (16 B) per thread
+  static_assert(DH % 64 == 0 && NT % 64 == 0, "a wave's pieces must share one block");
   uint4 kreg[KP], vreg[VP];
   // block ids of tile kt: lanes 0..3 of idv hold btab[4 kt + lane] (clamped
   // to the context's last block); loaded one tile ahead as a vector load, so
@@ -155,38 +156,35 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
     return btab[bi < nblk_ctx ? bi : nblk_ctx - 1];
   };
   auto load_tile = [&](int kt, int idv) {
-    size_t base[4];
-    bool live[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      live[j] = kt * 4 + j < nblk_ctx;
-      int64_t blk = __builtin_amdgcn_readlane(idv, j);
+    // every 16-byte piece of one wave lies in a single block of the tile (DH
+    // and NT are multiples of 64), so that block's id is read from lane beta
+    // of idv with a wave-uniform index
+    auto piece_base = [&](int u, size_t& off, bool& ok) {
+      const int beta = __builtin_amdgcn_readfirstlane(u / DH);
+      int64_t blk = __builtin_amdgcn_readlane(idv, beta);
       blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
-      base[j] = (size_t)blk * bstride + (size_t)h * tile_stride;
-    }
-    auto pick = [&](int j, size_t& off, bool& ok) {
-      off = j == 0 ? base[0] : j == 1 ? base[1] : j == 2 ? base[2] : base[3];
-      ok = j == 0 ? live[0] : j == 1 ? live[1] : j == 2 ? live[2] : live[3];
+      off = (size_t)blk * bstride + (size_t)h * tile_stride;
+      ok = kt * 4 + beta < nblk_ctx;
     };
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       // piece u = (block beta, 16-channel chunk, token): consecutive threads
       // read consecutive 16-byte runs of a K tile ([DH/16][16 tokens][16])
       const int u = threadIdx.x + i * NT;
-      const int beta = u / DH, piece = (u / 16) % (DH / 16), t = u % 16;
+      const int piece = (u / 16) % (DH / 16), t = u % 16;
       size_t off;
       bool ok;
-      pick(beta, off, ok);
+      piece_base(u, off, ok);
       kreg[i] = make_uint4(0, 0, 0, 0);
       if (ok) kreg[i] = *reinterpret_cast<const uint4*>(kc + off + piece * 256 + t * 16);
     }
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
       const int u = threadIdx.x + i * NT;
-      const int beta = u / DH, d = u - beta * DH;
+      const int d = u % DH;
       size_t off;
       bool ok;
-      pick(beta, off, ok);
+      piece_base(u, off, ok);
       vreg[i] = make_uint4(0, 0, 0, 0);
       if (ok) vreg[i] = *reinterpret_cast<const uint4*>(vc + off + d * 16);
     }
@@ -198,12 +196,16 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
       for (int i = 0; i < VP; ++i) {
         const int beta = (threadIdx.x + i * NT) / DH;
         const int left = ctx - (kt * 4 + beta) * 16;  // tokens of this block inside the context
-        uint32_t* wd = reinterpret_cast<uint32_t*>(&vreg[i]);
+        uint32_t keep[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int n = left - 4 * j;  // tokens of dword j inside the context
-          wd[j] &= n >= 4 ? 0xffffffffu : (n <= 0 ? 0u : (1u << (8 * n)) - 1);
+          keep[j] = n >= 4 ? 0xffffffffu : (n <= 0 ? 0u : (1u << (8 * n)) - 1);
         }
+        vreg[i].x &= keep[0];
+        vreg[i].y &= keep[1];
+        vreg[i].z &= keep[2];
+        vreg[i].w &= keep[3];
       }
     }
   };
