@@ -239,6 +239,22 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def time_rotating(torch, stream, fn, reps, warm=5):
+    """Mean time per call of fn(i), i = 0 .. reps - 1, between one pair of
+    events on the launch stream (per-call event pairs would also count any host
+    delay between an event and the launch that follows it)."""
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(reps):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def time_call(torch, stream, fn, reps):
     fn()
     torch.cuda.synchronize()
@@ -262,17 +278,10 @@ def decode_row(K, torch, dev, stream, k_all, v_all, slots_all, caches, wl, dec, 
     K.kvq_calibrate_scales(v_all, fmt, "tensor", amax, vs)
     for kc, vc in caches:
         K.kvq_cache_write(k_all, v_all, slots_all, kc, vc, ks, vs, fmt, "tensor")
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    for i in range(reps + 5):
+    def call(i):
         kc, vc = caches[i % len(caches)]
-        if i >= 5:
-            ev[i - 5][0].record(stream)
         K.kvq_decode_attn(out, q, kc, vc, bt, ctx, max_ctx, ks, vs, fmt, "tensor", workspace=ws)
-        if i >= 5:
-            ev[i - 5][1].record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms = time_rotating(torch, stream, call, reps)
     kv_bytes = int(wl.paging.context_lens.sum()) * wl.Hkv * wl.dh * 2
     gbs = kv_bytes / ms / 1e6
     return {"workload": wl.name + f" ({fmt} cache, per-tensor scale)", "ms": round(ms, 5),
@@ -300,18 +309,11 @@ def token_scale_rows(K, torch, dev, stream, k_all, v_all, slots_all, caches, wl,
                                         "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1)}
     for (kc, vc), (ksc, vsc) in zip(caches, scs):
         K.kvq_cache_write_token_scales(k_all, v_all, slots_all, kc, vc, ksc, vsc, "fp8_e4m3")
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    for i in range(reps + 5):
+    def call(i):
         (kc, vc), (ksc, vsc) = caches[i % len(caches)], scs[i % len(caches)]
-        if i >= 5:
-            ev[i - 5][0].record(stream)
         K.kvq_decode_attn_token_scales(out, q, kc, vc, ksc, vsc, bt, ctx, max_ctx, "fp8_e4m3",
                                        workspace=ws)
-        if i >= 5:
-            ev[i - 5][1].record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms = time_rotating(torch, stream, call, reps)
     kv_bytes = int(wl.paging.context_lens.sum()) * wl.Hkv * (wl.dh * 2 + 4)
     gbs = kv_bytes / ms / 1e6
     rows["decode_token_scales"] = {"workload": wl.name + " (e4m3 cache, fp16 per-token-head "
@@ -352,16 +354,9 @@ def kivi_rows(K, W, torch, dev, stream, reps=50):
     out = torch.empty((kw.B, kw.Hq, 128), dtype=torch.float32, device=dev)
     ws = torch.empty(K.kvq_kivi_decode_workspace_size(kw.B, kw.Hq, kw.Hkv, mg), dtype=torch.uint8,
                      device=dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    for i in range(reps + 5):
-        if i >= 5:
-            ev[i - 5][0].record(stream)
+    def call(i):
         K.kvq_kivi_decode_attn(out, q, caches[i % 3], bt, qg, mg, rk, rv, rl, workspace=ws)
-        if i >= 5:
-            ev[i - 5][1].record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms = time_rotating(torch, stream, call, reps)
     # algorithmic bytes: every quantized tile once, the residual once
     nbytes = (int(kw.quant_groups.sum()) * kw.Hkv * K.KIVI_TILE +
               int(kw.res_lens.sum()) * kw.Hkv * 128 * 2 * 2)

@@ -45,12 +45,11 @@ namespace kvq {
 #ifndef KVQ_DECODE_MAX_SPLIT_BLOCKS
 #define KVQ_DECODE_MAX_SPLIT_BLOCKS 32
 #endif
-// Waves per SIMD the split kernel is compiled for.  At 4 the whole state
-// (Q operand, one block pair of codes, the O tile) fits in 128 registers, so
-// a compute unit keeps 16 waves' loads in flight.
-// Whether each wave keeps two block pairs in flight (two register sets).
-#ifndef KVQ_DECODE_DOUBLE_BUFFER
-#define KVQ_DECODE_DOUBLE_BUFFER 0
+// Waves per SIMD the generic split kernel is compiled for.  At 4 the whole
+// state (Q operand, one block pair of codes, the O tile) fits in 128
+// registers, so a compute unit keeps 16 waves' loads in flight.
+#ifndef KVQ_DECODE_WAVES_PER_EU
+#define KVQ_DECODE_WAVES_PER_EU 4
 #endif
 // Waves per SIMD of the kernel for groups of at most 4 heads.
 #ifndef KVQ_DECODE_G4_WAVES_PER_EU
@@ -61,8 +60,15 @@ namespace kvq {
 #ifndef KVQ_DECODE_TS_WAVES_PER_EU
 #define KVQ_DECODE_TS_WAVES_PER_EU 4
 #endif
-#ifndef KVQ_DECODE_WAVES_PER_EU
-#define KVQ_DECODE_WAVES_PER_EU 4
+// Whether each wave of the generic kernel keeps two block pairs in flight
+// (two register sets).
+#ifndef KVQ_DECODE_DOUBLE_BUFFER
+#define KVQ_DECODE_DOUBLE_BUFFER 0
+#endif
+// Workgroup order: 1 puts the head groups of one split next to each other
+// (they read neighbouring tiles of the same blocks), 0 the splits of one group.
+#ifndef KVQ_DECODE_GRP_MAJOR
+#define KVQ_DECODE_GRP_MAJOR 1
 #endif
 
 namespace {
@@ -155,7 +161,8 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   constexpr int RS = LaneHeads<HPL>::kStride;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  const int split = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
+  const int split = KVQ_DECODE_GRP_MAJOR ? blockIdx.y : blockIdx.x;
+  const int grp = KVQ_DECODE_GRP_MAJOR ? blockIdx.x : blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int gpk = G / NH;
   const int h = grp / gpk;
@@ -471,7 +478,8 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   constexpr int NC = DH / 64;     // 64-channel halves of the output
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  const int split = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
+  const int split = KVQ_DECODE_GRP_MAJOR ? blockIdx.y : blockIdx.x;
+  const int grp = KVQ_DECODE_GRP_MAJOR ? blockIdx.x : blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int gpk = G / NH;
   const int h = grp / gpk;
@@ -822,7 +830,8 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
   float* ml = reinterpret_cast<float*>(ws);
   float* acc = ml + (size_t)B * Hq * plan.nsplit * 2;
   const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / __builtin_sqrtf((float)dh);
-  const dim3 grid(plan.nsplit, Hq / NH, B);
+  const dim3 grid(KVQ_DECODE_GRP_MAJOR ? Hq / NH : plan.nsplit,
+                  KVQ_DECODE_GRP_MAJOR ? plan.nsplit : Hq / NH, B);
   const size_t lds = decode_lds_bytes(NH, dh);
   int nhp_shift = 0;
   while ((1 << nhp_shift) < NH) ++nhp_shift;  // NHp = 2^nhp_shift >= NH
