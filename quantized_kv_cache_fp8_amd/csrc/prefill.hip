@@ -46,10 +46,18 @@ constexpr int kScaleLo = 123;    // E8M0 block scale 2^-4 (P_lo carries 16x its 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
 
-// position of key k (0..63) inside a transposed V row: keys are stored in the
-// order lane group g = (k>>2)&1 reads them, byte j = 16*(k>>5) + 4*((k>>3)&3) + (k&3)
+// Key order of the P V contraction.  Lane group g of the S tile holds keys
+// k = 32 t + 8 j + 4 g + r (t, j, r: key half, quad pair, byte); its P bytes
+// fill operand dword d = pv_slot(t, j), byte r.  A transposed V row stores
+// key k at the byte where lane group g reads that slot, vt_pos(k) =
+// 32 g + 4 pv_slot(t, j) + r.  The slot order puts the four key quads of one
+// cache block 16 bytes apart (never side by side), so each loaded dword is
+// stored from the register it arrived in.
+__device__ __forceinline__ constexpr int pv_slot(int t, int j) {
+  return 4 * (j & 1) + 2 * (j >> 1) + t;
+}
 __device__ __forceinline__ int vt_pos(int k) {
-  return 32 * ((k >> 2) & 1) + 16 * (k >> 5) + 4 * ((k >> 3) & 3) + (k & 3);
+  return 32 * ((k >> 2) & 1) + 4 * pv_slot(k >> 5, (k >> 3) & 3) + (k & 3);
 }
 
 // MFMA operand format code (cbsz / blgp): 0 = fp8 (E4M3), 1 = bf8 (E5M2)
@@ -147,7 +155,12 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
   constexpr int KP = kKT * DH / 16 / NT;  // K pieces (16 B) per thread
   constexpr int VP = 4 * DH / NT;         // V (block, channel) rows (16 B) per thread
   static_assert(DH % 64 == 0 && NT % 64 == 0, "a wave's pieces must share one block");
-  uint4 kreg[KP], vreg[VP];
+  // (held as vector values, not arrays: an array here can be moved to LDS or
+  // scratch memory by the compiler, which then waits for each load at issue)
+  using KRegs = uint32_t __attribute__((ext_vector_type(4 * KP)));
+  using VRegs = uint32_t __attribute__((ext_vector_type(4 * VP)));
+  KRegs kreg;
+  VRegs vreg;
   // block ids of tile kt: lanes 0..3 of idv hold btab[4 kt + lane] (clamped
   // to the context's last block); loaded one tile ahead as a vector load, so
   // neither a scalar-load chain nor a wait for it sits on the tile's path
@@ -155,16 +168,21 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
     const int bi = kt * 4 + (lane & 3);
     return btab[bi < nblk_ctx ? bi : nblk_ctx - 1];
   };
+  // every load is unconditional and in bounds: load_ids clamps the block index
+  // to the context's last block and the id to the pool, so no register is
+  // zeroed or branched over (a conditional load here made the compiler wait
+  // for it right after issue).  Keys past the context are masked out of S by
+  // the causal test, and their V codes are zeroed below.
+  const int nb_last = num_blocks - 1 < 0x7fffffff ? (int)(num_blocks - 1) : 0x7fffffff;
   auto load_tile = [&](int kt, int idv) {
     // every 16-byte piece of one wave lies in a single block of the tile (DH
     // and NT are multiples of 64), so that block's id is read from lane beta
     // of idv with a wave-uniform index
-    auto piece_base = [&](int u, size_t& off, bool& ok) {
+    auto piece_base = [&](int u) {
       const int beta = __builtin_amdgcn_readfirstlane(u / DH);
-      int64_t blk = __builtin_amdgcn_readlane(idv, beta);
-      blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
-      off = (size_t)blk * bstride + (size_t)h * tile_stride;
-      ok = kt * 4 + beta < nblk_ctx;
+      int blk = __builtin_amdgcn_readlane(idv, beta);
+      blk = blk < 0 ? 0 : (blk > nb_last ? nb_last : blk);
+      return (size_t)blk * bstride + (size_t)h * tile_stride;
     };
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
@@ -172,22 +190,23 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
       // read consecutive 16-byte runs of a K tile ([DH/16][16 tokens][16])
       const int u = threadIdx.x + i * NT;
       const int piece = (u / 16) % (DH / 16), t = u % 16;
-      size_t off;
-      bool ok;
-      piece_base(u, off, ok);
-      kreg[i] = make_uint4(0, 0, 0, 0);
-      if (ok) kreg[i] = *reinterpret_cast<const uint4*>(kc + off + piece * 256 + t * 16);
+      const uint4 w = *reinterpret_cast<const uint4*>(kc + piece_base(u) + piece * 256 + t * 16);
+      kreg[4 * i] = w.x;
+      kreg[4 * i + 1] = w.y;
+      kreg[4 * i + 2] = w.z;
+      kreg[4 * i + 3] = w.w;
     }
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
       const int u = threadIdx.x + i * NT;
-      const int d = u % DH;
-      size_t off;
-      bool ok;
-      piece_base(u, off, ok);
-      vreg[i] = make_uint4(0, 0, 0, 0);
-      if (ok) vreg[i] = *reinterpret_cast<const uint4*>(vc + off + d * 16);
+      const uint4 w = *reinterpret_cast<const uint4*>(vc + piece_base(u) + (u % DH) * 16);
+      vreg[4 * i] = w.x;
+      vreg[4 * i + 1] = w.y;
+      vreg[4 * i + 2] = w.z;
+      vreg[4 * i + 3] = w.w;
     }
+  };
+  auto store_tile = [&](int kt, uint8_t* k_lds, uint8_t* v_lds) {
     // slots past the context may hold any bytes, NaN codes included; their
     // zero weights would not cancel a NaN, so they are zeroed (only the tile
     // holding the context's last block has any)
@@ -196,34 +215,33 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
       for (int i = 0; i < VP; ++i) {
         const int beta = (threadIdx.x + i * NT) / DH;
         const int left = ctx - (kt * 4 + beta) * 16;  // tokens of this block inside the context
-        uint32_t keep[4];
+        // dword j keeps the tokens 4j .. 4j + 3 that lie inside the context
+        auto keep = [&](int j) {
+          const int n = left - 4 * j;
+          return n >= 4 ? 0xffffffffu : (n <= 0 ? 0u : (1u << (8 * n)) - 1);
+        };
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = left - 4 * j;  // tokens of dword j inside the context
-          keep[j] = n >= 4 ? 0xffffffffu : (n <= 0 ? 0u : (1u << (8 * n)) - 1);
-        }
-        vreg[i].x &= keep[0];
-        vreg[i].y &= keep[1];
-        vreg[i].z &= keep[2];
-        vreg[i].w &= keep[3];
+        for (int j = 0; j < 4; ++j) vreg[4 * i + j] &= keep(j);
       }
     }
-  };
-  auto store_tile = [&](uint8_t* k_lds, uint8_t* v_lds) {
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int u = threadIdx.x + i * NT;
       const int key = 16 * (u / DH) + u % 16, piece = (u / 16) % (DH / 16);
-      *reinterpret_cast<uint4*>(k_lds + key * KROW + piece * 16) = kreg[i];
+      *reinterpret_cast<uint4*>(k_lds + key * KROW + piece * 16) =
+          make_uint4(kreg[4 * i], kreg[4 * i + 1], kreg[4 * i + 2], kreg[4 * i + 3]);
     }
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
       const int u = threadIdx.x + i * NT;
       const int beta = u / DH, d = u - beta * DH;
-      // dword j holds keys 16 beta + 4j .. + 3; vt_pos puts j = 0, 2 and j = 1, 3 side by side
-      uint8_t* row = v_lds + d * VROW + vt_pos(16 * beta);
-      *reinterpret_cast<uint2*>(row) = make_uint2(vreg[i].x, vreg[i].z);
-      *reinterpret_cast<uint2*>(row + 32) = make_uint2(vreg[i].y, vreg[i].w);
+      // dword q holds keys 16 beta + 4 q .. + 3, at vt_pos of its first key:
+      // q = 0, 1, 2, 3 go to +0, +32, +16, +48 from q = 0's position
+      uint32_t* rw = reinterpret_cast<uint32_t*>(v_lds + d * VROW + vt_pos(16 * beta));
+      rw[0] = vreg[4 * i];
+      rw[8] = vreg[4 * i + 1];
+      rw[4] = vreg[4 * i + 2];
+      rw[12] = vreg[4 * i + 3];
     }
   };
 
@@ -231,7 +249,7 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
   int ids_next = 0;
   if (nkt > 0) {
     load_tile(0, load_ids(0));
-    store_tile(k_buf[0], v_buf[0]);
+    store_tile(0, k_buf[0], v_buf[0]);
     if (nkt > 1) load_tile(1, load_ids(1));
     __syncthreads();
   }
@@ -304,18 +322,23 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
         }
         // both halves of each dword are written, so the merge operand's old
         // contents do not matter
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[0], fp[1], ph[4 * t + v4], false);
+        const int d = pv_slot(t, v4);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[0], fp[1], ph[d], false);
         hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[2], fp[3], hi, true);
         const f32x2 h01 = dec2_f32<E4M3, false>((uint32_t)hi);
         const f32x2 h23 = dec2_f32<E4M3, true>((uint32_t)hi);
         // the scaled encode divides by its scale: e4m3((F p - P_hi) * 16)
-        s16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
-            __builtin_bit_cast(s16x2, pl[4 * t + v4]), fp[0] - h01.x, fp[1] - h01.y, 0.0625f,
-            false);
+        // the merge operand's other half is overwritten by the second encode,
+        // so it is any free register (an empty asm defines one, emitting no
+        // instruction), and no copy or zero is needed to feed it
+        s16x2 lo;
+        asm volatile("" : "=v"(lo));
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, fp[0] - h01.x, fp[1] - h01.y, 0.0625f,
+                                                      false);
         lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, fp[2] - h23.x, fp[3] - h23.y, 0.0625f,
                                                       true);
-        ph[4 * t + v4] = hi;
-        pl[4 * t + v4] = __builtin_bit_cast(int, lo);
+        ph[d] = hi;
+        pl[d] = __builtin_bit_cast(int, lo);
       }
 
     // ---- O^T += V^T P^T for channel tiles of 32: P_hi at scale 1, P_lo at
@@ -342,7 +365,7 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
     //      readers all passed the previous barrier; then start loading tile
     //      kt + 2; one barrier per tile
     if (kt + 1 < nkt) {
-      store_tile(k_buf[(kt + 1) & 1], v_buf[(kt + 1) & 1]);
+      store_tile(kt + 1, k_buf[(kt + 1) & 1], v_buf[(kt + 1) & 1]);
       if (kt + 2 < nkt) load_tile(kt + 2, ids_next);
     }
     __syncthreads();
