@@ -54,6 +54,15 @@ __device__ __forceinline__ f16x8 codes_to_f16x8(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(f16x8, u);
 }
 
+// word w of a uint4 held in registers (w folds to a constant once unrolled;
+// a pointer cast instead can keep the array in scratch memory)
+__device__ __forceinline__ uint32_t& u4word(uint4& v, int w) {
+  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+}
+__device__ __forceinline__ uint32_t u4word(const uint4& v, int w) {
+  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+}
+
 __device__ __forceinline__ uint4 load16(const uint8_t* p) {
 #if KVQ_DECODE_NT_LOADS
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));

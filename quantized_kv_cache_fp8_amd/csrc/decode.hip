@@ -547,6 +547,18 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
     }
   };
 
+  // Q first, then the first pair's K and V.  Q is waited for before the loop
+  // (the empty asm uses its registers) while K and V stay in flight: a load
+  // issued before the loop and first used inside it would otherwise make that
+  // use wait for every outstanding load, in every iteration.
+  uint4 qw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    qw[j] = make_uint4(0, 0, 0, 0);
+    if (head_a_real && chan_live)
+      qw[j] = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + hq0 + head_a) * DH +
+                                              16 * g4 + (j >> 1) * HALF + 8 * (j & 1));
+  }
   int p = wave;
   if (p < npair) {
     load_k(p);
@@ -555,11 +567,8 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   bf16x8 qop[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (head_a_real && chan_live)
-      w = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + hq0 + head_a) * DH + 16 * g4 +
-                                          (j >> 1) * HALF + 8 * (j & 1));
-    qop[j] = __builtin_bit_cast(bf16x8, w);
+    asm volatile("" ::"v"(qw[j].x), "v"(qw[j].y), "v"(qw[j].z), "v"(qw[j].w));
+    qop[j] = __builtin_bit_cast(bf16x8, qw[j]);
   }
   // ---- append: the new token (position ctx - 1) of this sequence
   int p_new = -1, e_new = 0, off_new = 0;
@@ -579,8 +588,11 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
 #pragma unroll
   for (int c = 0; c < NC; ++c) O[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-#pragma unroll 1
-  for (; p < npair; p += 4) {
+  // One block pair: S, online softmax, P V.  With `pre` the next pair of this
+  // wave is loaded as registers free up.  The last pair runs as a separate
+  // step without loads, so inside the loop both prefetches always happen and
+  // the wait for a pair's K codes never has to cover its V codes too.
+  auto pair_step = [&](int p, bool pre) __attribute__((always_inline)) {
     // ---- S for both blocks (bf16 matrix cores, rows replicated per head)
     if constexpr (APPEND) {
       if (p == p_new && c16 == off_new && chan_live) {  // the appended token's K codes
@@ -610,7 +622,7 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
         zp[e] = z[e];
       }
     }
-    if (p + 4 < npair) load_k(p + 4);  // K registers are free
+    if (pre) load_k(p + 4);  // K registers are free
     // ---- online softmax (lazy max, wave-uniform rare rescale)
     const bool need = __builtin_fmaxf(zp[0], zp[1]) > m_run + kLazyTau;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -651,10 +663,7 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
           const int n = left - 4 * w;
           const uint32_t keep = n >= 4 ? 0xffffffffu : (n <= 0 ? 0u : (1u << (8 * n)) - 1);
 #pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            uint32_t* d = reinterpret_cast<uint32_t*>(&vq[e][c]);
-            d[w] &= keep;
-          }
+          for (int c = 0; c < NC; ++c) u4word(vq[e][c], w) &= keep;
         }
       }
     }
@@ -667,10 +676,11 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             if (e != e_new) continue;
-            uint32_t* d = reinterpret_cast<uint32_t*>(&vq[e][c]);
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-              if (w == wi) d[w] = (d[w] & ~(0xffu << sh)) | (code << sh);
+            for (int w = 0; w < 4; ++w) {
+              uint32_t& d = u4word(vq[e][c], w);
+              if (w == wi) d = (d & ~(0xffu << sh)) | (code << sh);
+            }
           }
         }
       }
@@ -688,14 +698,17 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
                                : f16x4{p8[0], p8[1], p8[2], p8[3]};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint32_t codes = reinterpret_cast<const uint32_t*>(&vq[tq >> 2][c])[tq & 3];
+        const uint32_t codes = u4word(vq[tq >> 2][c], tq & 3);
         const f16x2 lo = dec2_f16<FMT, false>(codes), hi = dec2_f16<FMT, true>(codes);
         const f16x4 bv = {lo[0], lo[1], hi[0], hi[1]};
         O[c] = __builtin_amdgcn_mfma_f32_4x4x4f16(a, bv, O[c], 0, 0, 0);
       }
     }
-    if (p + 4 < npair) load_v(p + 4);  // V registers are free
-  }
+    if (pre) load_v(p + 4);  // V registers are free
+  };
+#pragma unroll 1
+  for (; p + 4 < npair; p += 4) pair_step(p, true);
+  if (p < npair) pair_step(p, false);
 
   // ---- merge the 4 waves through LDS and write the split's partial
   float x = l_part;
