@@ -53,10 +53,6 @@
 #ifndef KVQ_KIVI_WAVES_PER_EU
 #define KVQ_KIVI_WAVES_PER_EU 4
 #endif
-// Groups whose loads a wave keeps in flight (register sets: 2 or 3).
-#ifndef KVQ_KIVI_PREFETCH
-#define KVQ_KIVI_PREFETCH 2
-#endif
 
 namespace kvq {
 
@@ -371,10 +367,20 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
     uint32_t ks, kz;
     uint2 vm;
   };
+  // this wave's groups are wave + 4 k, k < NPW; their block ids come in one
+  // vector load (lane k holds group wave + 4 k's id, clamped to the split's
+  // last group), waited for here, before the loop
   const int32_t* btab = bt + (size_t)b * max_blocks + g0;
-  auto load = [&](Regs& x, int gi) {
-    int64_t blk = btab[gi];
-    blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
+  int idv = 0;
+  if (lane < NPW) {
+    const int gl = wave + 4 * lane;
+    idv = btab[gl < ngs ? gl : ngs - 1];
+  }
+  asm volatile("" ::"v"(idv));
+  const int nb_last = num_blocks - 1 < 0x7fffffff ? (int)(num_blocks - 1) : 0x7fffffff;
+  auto load = [&](Regs& x, int k) {
+    int blk = __builtin_amdgcn_readlane(idv, k);
+    blk = blk < 0 ? 0 : (blk > nb_last ? nb_last : blk);
     const uint8_t* tile = cache + ((size_t)blk * Hkv + h) * kTile;
     x.kc = load16(tile + 16 * lane);
     x.ks = *reinterpret_cast<const uint32_t*>(tile + kKs + 4 * lane);
@@ -387,26 +393,31 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
   // output rows nobody reads, so the operand loads need no masking)
   for (int i = lane; i < (256 + 2048) / 16; i += 64)
     reinterpret_cast<uint4*>(wl_base)[i] = make_uint4(0, 0, 0, 0);
+  // group 0's loads go out before the barrier (so they are issued ahead of
+  // group 1's, and in flight while the q rows are staged)
+  Regs r[2];
+  load(r[0], 0);
   __syncthreads();  // the q rows are read by every wave
 
   float m_run = kNegBig, l_part = 0.0f;
   f32x4 O[2];
   O[0] = O[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto step = [&](const Regs& cur) {
+  auto step = [&](const Regs& cur, bool live) {
     // ---- stage A' = q s, the K zeros and the V (s, z) of this group in LDS
     {
       const f16x2 s2 = __builtin_bit_cast(f16x2, cur.ks);
       const float s0 = (float)s2[0], s1 = (float)s2[1];
+      // (rows of heads >= NH have q = 0 and stay zero; writing them anyway
+      // keeps the scale load out of a branch, where it would be issued late)
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh)
-        if (hh < NH) {
-          const float x0 = qa[hh][0] * s0, x1 = qa[hh][1] * s1;
-          const f16x2 hi = f16x2{(_Float16)x0, (_Float16)x1};
-          reinterpret_cast<f16x2*>(aq + hh * kDH)[lane] = hi;
-          reinterpret_cast<f16x2*>(al + hh * kDH)[lane] =
-              f16x2{(_Float16)(x0 - (float)hi[0]), (_Float16)(x1 - (float)hi[1])};
-        }
+      for (int hh = 0; hh < 4; ++hh) {
+        const float x0 = qa[hh][0] * s0, x1 = qa[hh][1] * s1;
+        const f16x2 hi = f16x2{(_Float16)x0, (_Float16)x1};
+        reinterpret_cast<f16x2*>(aq + hh * kDH)[lane] = hi;
+        reinterpret_cast<f16x2*>(al + hh * kDH)[lane] =
+            f16x2{(_Float16)(x0 - (float)hi[0]), (_Float16)(x1 - (float)hi[1])};
+      }
       reinterpret_cast<uint32_t*>(zb)[lane] = cur.kz;
       const int t = lane >> 1, ga = 2 * (lane & 1);
       vsS[ga * kG + t] = (uint16_t)(cur.vm.x & 0xffffu);
@@ -437,7 +448,10 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
       S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, b0, S0, 0, 0, 0);
       S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, b1, S1, 0, 0, 0);
     }
-    const float zt[2] = {S0[0] * zc, S1[0] * zc};
+    // a group past the split's end (live false) has every score at -inf: it
+    // adds nothing (its tile is a real one, so its values are finite)
+    const float zt[2] = {live ? S0[0] * zc : -__builtin_inff(),
+                         live ? S1[0] * zc : -__builtin_inff()};
     // ---- online softmax (lazy max, wave-uniform rare rescale)
     const bool need = __builtin_fmaxf(zt[0], zt[1]) > m_run + kLazyTauK;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -495,39 +509,17 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
     }
   };
 
-#if KVQ_KIVI_PREFETCH >= 3
-  // three register sets in turn: the next two groups' loads are in flight
-  // while the current one is processed
-  Regs r0, r1, r2;
-  int gi = wave;
-  if (gi < ngs) load(r0, gi);
-  if (gi + 4 < ngs) load(r1, gi + 4);
-#pragma unroll 1
-  for (; gi < ngs; gi += 12) {
-    if (gi + 8 < ngs) load(r2, gi + 8);
-    step(r0);
-    if (gi + 4 >= ngs) break;
-    if (gi + 12 < ngs) load(r0, gi + 12);
-    step(r1);
-    if (gi + 8 >= ngs) break;
-    if (gi + 16 < ngs) load(r1, gi + 16);
-    step(r2);
+  // two register sets in turn, the loop fully unrolled: group k + 1's loads
+  // are in flight while group k is processed.  Loads and steps are
+  // unconditional (a group past the split's last one re-reads that group's
+  // tile and contributes nothing), so no load is moved into a branch and each
+  // wait for a group's registers leaves the next group's loads in flight.
+#pragma unroll
+  for (int k = 0; k < NPW; ++k) {
+    if (k + 1 < NPW) load(r[(k + 1) & 1], k + 1);
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out before the step
+    step(r[k & 1], wave + 4 * k < ngs);
   }
-#else
-  // two register sets in turn: the next group's loads are in flight while
-  // the current one is processed
-  Regs ra, rb;
-  int gi = wave;
-  if (gi < ngs) load(ra, gi);
-#pragma unroll 1
-  for (; gi < ngs; gi += 8) {
-    if (gi + 4 < ngs) load(rb, gi + 4);
-    step(ra);
-    if (gi + 4 >= ngs) break;
-    if (gi + 8 < ngs) load(ra, gi + 8);
-    step(rb);
-  }
-#endif
 
   // ---- merge the 4 waves through LDS and write the split's partial
   float x = l_part;
