@@ -50,8 +50,9 @@
 #include "attn_common.hpp"
 #include "launch.hpp"
 
+// Waves per SIMD of the decode split kernel (94 VGPRs at 5; 6 spills)
 #ifndef KVQ_KIVI_WAVES_PER_EU
-#define KVQ_KIVI_WAVES_PER_EU 4
+#define KVQ_KIVI_WAVES_PER_EU 5
 #endif
 
 namespace kvq {
