@@ -238,6 +238,19 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     for (int n = 0; n < NV; ++n) vr[n] = load8(src + 16 * n * kBlockSize);
   };
 
+  // A operand of S = Q K^T (bf16, exact): query head_a in the channel slots
+  // of the K operand: j = 2 i + c covers channels 16 g4 + i * DH/2 + 8 c + 0..7.
+  // Q is loaded first and waited for before the loop (the empty asm uses its
+  // registers) while the first pair's K and V stay in flight, so no load
+  // issued before the loop is still pending at its head.
+  uint4 qw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    qw[j] = make_uint4(0, 0, 0, 0);
+    if (head_a_real && chan_live)
+      qw[j] = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + hq0 + head_a) * DH +
+                                              16 * g4 + (j >> 1) * HALF + 8 * (j & 1));
+  }
   int p = wave;
   if (p < npair) {
     load_k(p, kr);
@@ -247,17 +260,11 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     load_k(p + 4, kr2);
     load_v(p + 4, vr2);
   }
-
-  // A operand of S = Q K^T (bf16, exact): query head_a in the channel slots
-  // of the K operand: j = 2 i + c covers channels 16 g4 + i * DH/2 + 8 c + 0..7
   bf16x8 qop[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (head_a_real && chan_live)
-      w = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + hq0 + head_a) * DH + 16 * g4 +
-                                          (j >> 1) * HALF + 8 * (j & 1));
-    qop[j] = __builtin_bit_cast(bf16x8, w);
+    asm volatile("" ::"v"(qw[j].x), "v"(qw[j].y), "v"(qw[j].z), "v"(qw[j].w));
+    qop[j] = __builtin_bit_cast(bf16x8, qw[j]);
   }
   // ---- append: the new token (position ctx - 1) of this sequence
   int p_new = -1, e_new = 0, off_new = 0;
@@ -281,7 +288,9 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   for (int n = 0; n < NV; ++n) O[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // one block pair: S, online softmax, P V (kr / vr hold the pair's codes)
-  auto pair_step = [&](int p, i32x8 (&kr)[2], uint2 (&vr)[NV]) {
+  // (with `pre` the wave's next pair is loaded as registers free up)
+  auto pair_step = [&](int p, i32x8 (&kr)[2], uint2 (&vr)[NV], bool pre)
+      __attribute__((always_inline)) {
     // ---- S for both blocks on bf16 matrix cores (codes -> bf16 is exact):
     //      lane holds head head_l[i] for token c16 of block e
     if constexpr (APPEND) {
@@ -308,7 +317,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     }
     // this pair's K registers are free: the next pair's keys load during the
     // softmax and P V below
-    if (!KVQ_DECODE_DOUBLE_BUFFER && p + 4 < npair) load_k(p + 4, kr);
+    if (!KVQ_DECODE_DOUBLE_BUFFER && pre) load_k(p + 4, kr);
     // ---- online softmax per head.  Each lane tests its own scores against
     //      the running max; only when one exceeds it by more than tau does the
     //      wave take the (rare, wave-uniform) branch that finds the exact
@@ -373,20 +382,20 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     for (int n = 0; n < NV; ++n)
       O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, codes_to_f16x8<FMT>(vr[n].x, vr[n].y),
                                                     O[n], 0, 0, 0);
-    if (!KVQ_DECODE_DOUBLE_BUFFER && p + 4 < npair) load_v(p + 4, vr);  // V registers are free now
+    if (!KVQ_DECODE_DOUBLE_BUFFER && pre) load_v(p + 4, vr);  // V registers are free now
     };
 
 #if KVQ_DECODE_DOUBLE_BUFFER
   // two register sets: while one pair is computed the pair after it lands
 #pragma unroll 1
   for (; p < npair; p += 8) {
-    pair_step(p, kr, vr);
+    pair_step(p, kr, vr, false);
     if (p + 8 < npair) {
       load_k(p + 8, kr);
       load_v(p + 8, vr);
     }
     if (p + 4 < npair) {
-      pair_step(p + 4, kr2, vr2);
+      pair_step(p + 4, kr2, vr2, false);
       if (p + 12 < npair) {
         load_k(p + 12, kr2);
         load_v(p + 12, vr2);
@@ -394,8 +403,11 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     }
   }
 #else
+  // the last pair runs without loads, so inside the loop both prefetches
+  // always happen and a pair's K wait never covers its V codes too
 #pragma unroll 1
-  for (; p < npair; p += 4) pair_step(p, kr, vr);
+  for (; p + 4 < npair; p += 4) pair_step(p, kr, vr, true);
+  if (p < npair) pair_step(p, kr, vr, false);
 #endif
 
   // ---- merge the 4 waves through LDS and write the split's partial

@@ -123,7 +123,9 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 __global__ __launch_bounds__(256) void kivi_quantize_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int Hkv,
     const int32_t* __restrict__ group_blocks, int64_t num_blocks, uint8_t* __restrict__ cache) {
-  __shared__ float xs[2][kG][kDH + 1];  // K, V values
+  // K, V values as their bf16 bits (exact; rows padded to 130 elements so
+  // the per-token V reductions fall in distinct banks)
+  __shared__ uint16_t xs[2][kG][kDH + 2];
   __shared__ uint8_t cs[2][kG][kDH];    // K, V codes
   const int g = (int)(blockIdx.x / (uint32_t)Hkv);
   const int h = (int)(blockIdx.x - (uint32_t)g * (uint32_t)Hkv);
@@ -141,10 +143,8 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(
       const uint4 b = *reinterpret_cast<const uint4*>(x + src + 8);
       const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        xs[m][t][16 * q + 2 * i] = __uint_as_float(w[i] << 16);
-        xs[m][t][16 * q + 2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-      }
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<uint32_t*>(&xs[m][t][16 * q + 2 * i]) = w[i];
     }
   }
   __syncthreads();
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(
     float mn = __builtin_inff(), mx = -__builtin_inff();
     bool fin = true;
     for (int i = 0; i < kG; ++i) {
-      const float x = isk ? xs[0][i][c] : xs[1][t][32 * gc + i];
+      const float x = __uint_as_float((uint32_t)(isk ? xs[0][i][c] : xs[1][t][32 * gc + i]) << 16);
       fin = fin && __builtin_isfinite(x);
       mn = __builtin_fminf(mn, x);
       mx = __builtin_fmaxf(mx, x);
@@ -165,11 +165,13 @@ __global__ __launch_bounds__(256) void kivi_quantize_kernel(
     if (isk) {
       reinterpret_cast<uint16_t*>(tile + kKs)[c] = (uint16_t)(sz & 0xffffu);
       reinterpret_cast<uint16_t*>(tile + kKz)[c] = (uint16_t)(sz >> 16);
-      for (int i = 0; i < kG; ++i) cs[0][i][c] = (uint8_t)kivi_code(xs[0][i][c], s, rs, z);
+      for (int i = 0; i < kG; ++i)
+        cs[0][i][c] = (uint8_t)kivi_code(__uint_as_float((uint32_t)xs[0][i][c] << 16), s, rs, z);
     } else {
       reinterpret_cast<uint32_t*>(tile + kVm)[tid - kDH] = sz;  // at 16 t + 4 gc
       for (int i = 0; i < kG; ++i)
-        cs[1][t][32 * gc + i] = (uint8_t)kivi_code(xs[1][t][32 * gc + i], s, rs, z);
+        cs[1][t][32 * gc + i] =
+            (uint8_t)kivi_code(__uint_as_float((uint32_t)xs[1][t][32 * gc + i] << 16), s, rs, z);
     }
   }
   __syncthreads();
