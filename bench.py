@@ -335,8 +335,9 @@ def kivi_rows(K, W, torch, dev, stream, reps=50):
     k, v, gb = dt(kw.k), dt(kw.v), dt(kw.group_blocks)
     nb = kw.paging.num_blocks
     # copies of the cache in rotation so no call reads another's data from L2 / MALL
+    # (6 x 104 MB: well past the 256 MB MALL, so every call reads from HBM)
     caches = [torch.empty((nb, kw.Hkv, K.KIVI_TILE), dtype=torch.uint8, device=dev)
-              for _ in range(3)]
+              for _ in range(6)]
     rows = {}
 
     def quant():
@@ -355,7 +356,8 @@ def kivi_rows(K, W, torch, dev, stream, reps=50):
     ws = torch.empty(K.kvq_kivi_decode_workspace_size(kw.B, kw.Hq, kw.Hkv, mg), dtype=torch.uint8,
                      device=dev)
     def call(i):
-        K.kvq_kivi_decode_attn(out, q, caches[i % 3], bt, qg, mg, rk, rv, rl, workspace=ws)
+        K.kvq_kivi_decode_attn(out, q, caches[i % len(caches)], bt, qg, mg, rk, rv, rl,
+                               workspace=ws)
     ms = time_rotating(torch, stream, call, reps)
     # algorithmic bytes: every quantized tile once, the residual once
     nbytes = (int(kw.quant_groups.sum()) * kw.Hkv * K.KIVI_TILE +
