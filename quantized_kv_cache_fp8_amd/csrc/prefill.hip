@@ -30,6 +30,12 @@
 #include "codec.hpp"
 #include "launch.hpp"
 
+// Terms P is carried in: 2 (P_hi + P_lo / 16, which meets the 2e-3 bar) or 1
+// (P_hi alone: an ablation build, measured but outside the bar)
+#ifndef KVQ_PREFILL_P_TERMS
+#define KVQ_PREFILL_P_TERMS 2
+#endif
+
 namespace kvq {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -325,20 +331,22 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
         const int d = pv_slot(t, v4);
         int hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[0], fp[1], ph[d], false);
         hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[2], fp[3], hi, true);
-        const f32x2 h01 = dec2_f32<E4M3, false>((uint32_t)hi);
-        const f32x2 h23 = dec2_f32<E4M3, true>((uint32_t)hi);
-        // the scaled encode divides by its scale: e4m3((F p - P_hi) * 16)
-        // the merge operand's other half is overwritten by the second encode,
-        // so it is any free register (an empty asm defines one, emitting no
-        // instruction), and no copy or zero is needed to feed it
-        s16x2 lo;
-        asm volatile("" : "=v"(lo));
-        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, fp[0] - h01.x, fp[1] - h01.y, 0.0625f,
-                                                      false);
-        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, fp[2] - h23.x, fp[3] - h23.y, 0.0625f,
-                                                      true);
+        if constexpr (KVQ_PREFILL_P_TERMS == 2) {
+          const f32x2 h01 = dec2_f32<E4M3, false>((uint32_t)hi);
+          const f32x2 h23 = dec2_f32<E4M3, true>((uint32_t)hi);
+          // the merge operand's other half is overwritten by the second encode,
+          // so it is any free register (an empty asm defines one, emitting no
+          // instruction), and no copy or zero is needed to feed it
+          s16x2 lo;
+          asm volatile("" : "=v"(lo));
+          // the scaled encode divides by its scale: e4m3((F p - P_hi) * 16)
+          lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, fp[0] - h01.x, fp[1] - h01.y, 0.0625f,
+                                                        false);
+          lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, fp[2] - h23.x, fp[3] - h23.y, 0.0625f,
+                                                        true);
+          pl[d] = __builtin_bit_cast(int, lo);
+        }
         ph[d] = hi;
-        pl[d] = __builtin_bit_cast(int, lo);
       }
 
     // ---- O^T += V^T P^T for channel tiles of 32: P_hi at scale 1, P_lo at
@@ -356,10 +364,12 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
     for (int dt = 0; dt < DH / 32; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
           va[dt], ph, acc[dt], MfmaFmt<FMT>::value, 0, 0, kScaleOne, 0, kScaleOne);
+    if constexpr (KVQ_PREFILL_P_TERMS == 2) {
 #pragma unroll
-    for (int dt = 0; dt < DH / 32; ++dt)
-      acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          va[dt], pl, acc[dt], MfmaFmt<FMT>::value, 0, 0, kScaleOne, 0, kScaleLo);
+      for (int dt = 0; dt < DH / 32; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            va[dt], pl, acc[dt], MfmaFmt<FMT>::value, 0, 0, kScaleOne, 0, kScaleLo);
+    }
 
     // ---- tile kt + 1 (loaded during this tile) into the other buffer, whose
     //      readers all passed the previous barrier; then start loading tile
