@@ -65,6 +65,11 @@ namespace kvq {
 #ifndef KVQ_DECODE_DOUBLE_BUFFER
 #define KVQ_DECODE_DOUBLE_BUFFER 0
 #endif
+// Waves per workgroup of the kernel for groups of at most 4 heads (4, 2 or 1):
+// fewer waves per workgroup give each wave more block pairs of the same split.
+#ifndef KVQ_DECODE_G4_NW
+#define KVQ_DECODE_G4_NW 4
+#endif
 // Workgroup order: 1 puts the head groups of one split next to each other
 // (they read neighbouring tiles of the same blocks), 0 the splits of one group.
 #ifndef KVQ_DECODE_GRP_MAJOR
@@ -80,6 +85,11 @@ constexpr int kBlockSize = 16;  // tokens per cache block
 static size_t decode_lds_bytes(int NH, int dh) {
   return 4 * 16 * 32 * sizeof(_Float16) + 2 * 4 * 16 * sizeof(float) +
          (size_t)4 * NH * dh * sizeof(float) + 2 * (size_t)dh;  // + appended token's codes
+}
+static size_t decode_g4_lds_bytes(int NH, int dh) {
+  constexpr int NW = KVQ_DECODE_G4_NW;
+  return NW * 16 * 32 * sizeof(_Float16) + 2 * NW * 16 * sizeof(float) +
+         (size_t)NW * NH * dh * sizeof(float) + 2 * (size_t)dh;  // + appended token's codes
 }
 
 // Lazy running max: it only moves when a score exceeds it by more than 2^8,
@@ -109,7 +119,7 @@ struct LaneHeads {
 // when `writer` (one workgroup per KV head), and return the block pair,
 // block and offset at which the caller patches them into its registers.
 // Every thread of the workgroup calls it (it holds a barrier).
-template <int FMT, int DH>
+template <int FMT, int DH, int NT = 256>
 __device__ __forceinline__ void append_prologue(
     int ctx, int tok0, int nblk, const int32_t* __restrict__ btab, int64_t num_blocks,
     int64_t bstride, int h, int Hkv, int b, bool writer, const uint16_t* __restrict__ k_new,
@@ -123,13 +133,13 @@ __device__ __forceinline__ void append_prologue(
   p_new = bi >> 1;
   e_new = bi & 1;
   off_new = (ctx - 1) & (kBlockSize - 1);
-  if (tid < 2 * DH) {
-    const bool isv = tid >= DH;
-    const int d = isv ? tid - DH : tid;
+  for (int i = tid; i < 2 * DH; i += NT) {
+    const bool isv = i >= DH;
+    const int d = isv ? i - DH : i;
     const uint16_t x = (isv ? v_new : k_new)[((size_t)b * Hkv + h) * DH + d];
     const float sc = (isv ? vs : ks)[per_head ? h : 0];
     const float qv = quotient(__uint_as_float((uint32_t)x << 16), sc, recip_rn(sc));
-    pw[tid] = (uint8_t)(enc2<FMT>(qv, qv) & 0xffu);
+    pw[i] = (uint8_t)(enc2<FMT>(qv, qv) & 0xffu);
   }
   __syncthreads();
   const int64_t raw = btab[bi];
@@ -139,8 +149,11 @@ __device__ __forceinline__ void append_prologue(
     if (tid < DH / 16)
       *reinterpret_cast<uint4*>(kt + tid * 256 + off_new * 16) =
           *reinterpret_cast<const uint4*>(pw + 16 * tid);
-    else if (tid >= 64 && tid < 64 + DH)
-      vt[(tid - 64) * kBlockSize + off_new] = pw[DH + tid - 64];
+    // V codes from the second wave on (the first stores K), or from every
+    // thread when the workgroup has one wave
+    const int v0 = NT > 64 ? 64 : 0;
+    for (int i = tid - v0; i >= 0 && i < DH; i += NT - v0)
+      vt[i * kBlockSize + off_new] = pw[DH + i];
   }
 }
 
@@ -467,7 +480,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 // new token (k_new / v_new), writes its codes to the cache and patches them
 // into its own K / V registers, so no workgroup reads that slot from memory.
 template <int FMT, int DH, int NPW, int MODE>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(64 * KVQ_DECODE_G4_NW)
 __attribute__((amdgpu_waves_per_eu(MODE == 1 ? KVQ_DECODE_TS_WAVES_PER_EU
                                                 : KVQ_DECODE_G4_WAVES_PER_EU,
                                     MODE == 1 ? KVQ_DECODE_TS_WAVES_PER_EU
@@ -485,7 +498,8 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
                        const float* __restrict__ vs) {
   constexpr bool TS = MODE == 1, APPEND = MODE == 2;
   typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-  constexpr int PB = 8 * NPW;     // blocks per split: 4 waves x NPW pairs x 2
+  constexpr int NW = KVQ_DECODE_G4_NW;  // waves per workgroup
+  constexpr int PB = 2 * NW * NPW;      // blocks per split: NW waves x NPW pairs x 2
   constexpr int HALF = DH / 2;
   constexpr int NC = DH / 64;     // 64-channel halves of the output
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -519,10 +533,12 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   // P V: A row of this lane (head lane % 4), and the lane that holds head r's
   // running state in the S layout (first lane of its first lane group)
   const int head_p = lane & 3;
+  // LDS (decode_g4_lds_bytes): per wave P scratch [16][32] f16, then the
+  // waves' m and l [NW][16] and O [NW][NH][DH], then the appended token's codes
   _Float16* ptr = reinterpret_cast<_Float16*>(smem) + wave * 16 * 32;  // this wave's P scratch
-  float* wm = reinterpret_cast<float*>(smem + 4 * 16 * 32 * sizeof(_Float16));
-  float* wl = wm + 4 * 16;
-  float* wo = wl + 4 * 16;  // [4][NH][DH]
+  float* wm = reinterpret_cast<float*>(smem + NW * 16 * 32 * sizeof(_Float16));
+  float* wl = wm + NW * 16;
+  float* wo = wl + NW * 16;  // [NW][NH][DH]
   const int32_t* btab = bt + (size_t)b * max_blocks + (size_t)split * PB;
   const size_t tile = (size_t)kBlockSize * DH;  // bytes per (block, head) tile
 
@@ -584,10 +600,10 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   }
   // ---- append: the new token (position ctx - 1) of this sequence
   int p_new = -1, e_new = 0, off_new = 0;
-  uint8_t* pw = reinterpret_cast<uint8_t*>(wo + 4 * NH * DH);  // [2][DH]: K codes, V codes
+  uint8_t* pw = reinterpret_cast<uint8_t*>(wo + NW * NH * DH);  // [2][DH]: K codes, V codes
   const uint8_t* patch = pw;
   if constexpr (APPEND)
-    append_prologue<FMT, DH>(ctx, tok0, nblk, btab, num_blocks, bstride, h, Hkv, b,
+    append_prologue<FMT, DH, 64 * NW>(ctx, tok0, nblk, btab, num_blocks, bstride, h, Hkv, b,
                              grp == h * gpk, k_new, v_new, ks, vs, per_head, kc_w, vc_w, pw,
                              p_new, e_new, off_new);
 
@@ -634,7 +650,7 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
         zp[e] = z[e];
       }
     }
-    if (pre) load_k(p + 4);  // K registers are free
+    if (pre) load_k(p + NW);  // K registers are free
     // ---- online softmax (lazy max, wave-uniform rare rescale)
     const bool need = __builtin_fmaxf(zp[0], zp[1]) > m_run + kLazyTau;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -716,13 +732,13 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
         O[c] = __builtin_amdgcn_mfma_f32_4x4x4f16(a, bv, O[c], 0, 0, 0);
       }
     }
-    if (pre) load_v(p + 4);  // V registers are free
+    if (pre) load_v(p + NW);  // V registers are free
   };
 #pragma unroll 1
-  for (; p + 4 < npair; p += 4) pair_step(p, true);
+  for (; p + NW < npair; p += NW) pair_step(p, true);
   if (p < npair) pair_step(p, false);
 
-  // ---- merge the 4 waves through LDS and write the split's partial
+  // ---- merge the NW waves through LDS and write the split's partial
   float x = l_part;
   x += dpp<0xB1>(x);
   x += dpp<0x4E>(x);
@@ -738,14 +754,14 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
 #pragma unroll
       for (int c = 0; c < NC; ++c) wo[(wave * NH + r) * DH + 64 * c + lane] = O[c][r];
   __syncthreads();
-  for (int o = tid; o < NH * DH; o += 256) {
+  for (int o = tid; o < NH * DH; o += 64 * NW) {
     const int row = o / DH, d = o - row * DH;
     float M = kNegBig;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = __builtin_fmaxf(M, wm[w * 16 + row]);
+    for (int w = 0; w < NW; ++w) M = __builtin_fmaxf(M, wm[w * 16 + row]);
     float a = 0.0f, L = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = __builtin_amdgcn_exp2f(wm[w * 16 + row] - M);
       a += f * wo[(w * NH + row) * DH + d];
       L += f * wl[w * 16 + row];
@@ -874,7 +890,8 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
           max_ctx, ks, per_head, sm, plan.nsplit, ml, acc, k_new, v_new, kc_w, vc_w, vs);    \
   } while (0)
 #define KVQ_SPLIT_G4(F, D, N, M)                                                           \
-  decode_split_g4_kernel<F, D, N, M><<<grid, 256, lds, s>>>(                                 \
+  decode_split_g4_kernel<F, D, N * 4 / KVQ_DECODE_G4_NW, M>                                   \
+      <<<grid, 64 * KVQ_DECODE_G4_NW, decode_g4_lds_bytes(NH, dh), s>>>(                    \
       q, kc, vc, num_blocks, bstride, bt, max_blocks, ctx, Hq, Hkv, NH, rph_shift, max_ctx, ks, \
       per_head, sm, plan.nsplit, ml, acc, ksc, vsc, k_new, v_new, kc_w, vc_w, vs)
 #define KVQ_SPLIT_HP(F, D, N)                                     \
