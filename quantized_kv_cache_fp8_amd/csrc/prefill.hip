@@ -35,12 +35,19 @@
 #ifndef KVQ_PREFILL_P_TERMS
 #define KVQ_PREFILL_P_TERMS 2
 #endif
+// 1: P in f16 and P V on f16 matrix cores, with the V codes converted to f16
+// (exactly) when a tile is staged -- a build option measured against the
+// FP8-domain P V above; Q K^T stays on FP8 matrix cores either way
+#ifndef KVQ_PREFILL_P_F16
+#define KVQ_PREFILL_P_F16 0
+#endif
 
 namespace kvq {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 namespace {
 constexpr int kQT = 32;          // query rows per wave
@@ -89,7 +96,8 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
     float sm_scale) {
   constexpr int NT = 64 * GT;          // threads
   constexpr int KROW = DH + 16;        // padded K row in LDS (bytes)
-  constexpr int VROW = kKT + 16;       // padded transposed-V row in LDS (bytes)
+  // padded transposed-V row in LDS (bytes): 64 codes, or 64 f16 values
+  constexpr int VROW = (KVQ_PREFILL_P_F16 ? 2 * kKT : kKT) + 16;
   // two K/V tile buffers: tile kt is read from buffer kt & 1 while tile kt + 1
   // is written into the other one
   __shared__ __attribute__((aligned(16))) uint8_t k_buf[2][kKT * KROW];
@@ -241,6 +249,19 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
     for (int i = 0; i < VP; ++i) {
       const int u = threadIdx.x + i * NT;
       const int beta = u / DH, d = u - beta * DH;
+#if KVQ_PREFILL_P_F16
+      // block beta is one 16-key step of the f16 contraction: its 32 bytes
+      // hold keys 0-3, 8-11 (read by lane group 0) then 4-7, 12-15 (group 1)
+      auto f16q = [&](uint32_t w) {  // 4 codes -> 4 exact f16 values (2 dwords)
+        const f16x2 lo = dec2_f16<FMT, false>(w), hi = dec2_f16<FMT, true>(w);
+        return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+      };
+      const uint2 q0 = f16q(vreg[4 * i]), q1 = f16q(vreg[4 * i + 1]);
+      const uint2 q2 = f16q(vreg[4 * i + 2]), q3 = f16q(vreg[4 * i + 3]);
+      uint4* rw = reinterpret_cast<uint4*>(v_lds + d * VROW + 32 * beta);
+      rw[0] = make_uint4(q0.x, q0.y, q2.x, q2.y);
+      rw[1] = make_uint4(q1.x, q1.y, q3.x, q3.y);
+#else
       // dword q holds keys 16 beta + 4 q .. + 3, at vt_pos of its first key:
       // q = 0, 1, 2, 3 go to +0, +32, +16, +48 from q = 0's position
       uint32_t* rw = reinterpret_cast<uint32_t*>(v_lds + d * VROW + vt_pos(16 * beta));
@@ -248,10 +269,15 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
       rw[8] = vreg[4 * i + 1];
       rw[4] = vreg[4 * i + 2];
       rw[12] = vreg[4 * i + 3];
+#endif
     }
   };
 
+#if KVQ_PREFILL_P_F16
+  f16x8 pb[4];  // P of 16-key step beta (cache block beta of the tile)
+#else
   i32x8 ph = {}, pl = {};  // probability operands (every byte rewritten per tile)
+#endif
   int ids_next = 0;
   if (nkt > 0) {
     load_tile(0, load_ids(0));
@@ -326,6 +352,16 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
           fp[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][4 * v4 + r], zc, -bias));
           l_run += fp[r];
         }
+#if KVQ_PREFILL_P_F16
+        // keys 32 t + 8 v4 + 4 g + r: step beta = 2 t + v4 / 2, slot 4 (v4 & 1) + r
+        {
+          const int beta = 2 * t + (v4 >> 1), o = 4 * (v4 & 1);
+          pb[beta][o] = (_Float16)fp[0];
+          pb[beta][o + 1] = (_Float16)fp[1];
+          pb[beta][o + 2] = (_Float16)fp[2];
+          pb[beta][o + 3] = (_Float16)fp[3];
+        }
+#else
         // both halves of each dword are written, so the merge operand's old
         // contents do not matter
         const int d = pv_slot(t, v4);
@@ -347,8 +383,20 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
           pl[d] = __builtin_bit_cast(int, lo);
         }
         ph[d] = hi;
+#endif
       }
 
+#if KVQ_PREFILL_P_F16
+    // ---- O^T += V^T P^T on f16 matrix cores: 4 channel tiles x 4 key steps
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+      for (int beta = 0; beta < 4; ++beta) {
+        const f16x8 va16 =
+            *reinterpret_cast<const f16x8*>(v_lds + (32 * dt + c) * VROW + 32 * beta + 16 * g);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va16, pb[beta], acc[dt], 0, 0, 0);
+      }
+#else
     // ---- O^T += V^T P^T for channel tiles of 32: P_hi at scale 1, P_lo at
     //      scale 2^-4 (E8M0 block scales 127 and 123) into one accumulator
     i32x8 va[DH / 32];
@@ -370,6 +418,7 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
         acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             va[dt], pl, acc[dt], MfmaFmt<FMT>::value, 0, 0, kScaleOne, 0, kScaleLo);
     }
+#endif
 
     // ---- tile kt + 1 (loaded during this tile) into the other buffer, whose
     //      readers all passed the previous barrier; then start loading tile
