@@ -41,6 +41,10 @@
 #ifndef KVQ_PREFILL_P_F16
 #define KVQ_PREFILL_P_F16 0
 #endif
+// waves per SIMD the kernel is compiled for (groups of 2 or 4 heads)
+#ifndef KVQ_PREFILL_WAVES
+#define KVQ_PREFILL_WAVES 2
+#endif
 
 namespace kvq {
 
@@ -86,7 +90,7 @@ struct MfmaFmt {
 
 template <int FMT, int DH, int GT>
 __global__ __launch_bounds__(64 * GT)
-__attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void prefill_kernel(
+__attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 : KVQ_PREFILL_WAVES))) void prefill_kernel(
     void* __restrict__ out, int out_bf16, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ cu, int n_qtiles, const float* __restrict__ qs, int q_per_head,
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc, int64_t num_blocks,
@@ -96,8 +100,10 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
     float sm_scale) {
   constexpr int NT = 64 * GT;          // threads
   constexpr int KROW = DH + 16;        // padded K row in LDS (bytes)
-  // padded transposed-V row in LDS (bytes): 64 codes, or 64 f16 values
-  constexpr int VROW = (KVQ_PREFILL_P_F16 ? 2 * kKT : kKT) + 16;
+  // transposed-V row in LDS (bytes): 64 codes + 16 pad, or 64 f16 values
+  // unpadded, their 16-byte chunks swizzled by the row (chunk x of row r at
+  // x ^ (r & 7)) so the 8 lanes of an LDS read cycle hit distinct banks
+  constexpr int VROW = KVQ_PREFILL_P_F16 ? 2 * kKT : kKT + 16;
   // two K/V tile buffers: tile kt is read from buffer kt & 1 while tile kt + 1
   // is written into the other one
   __shared__ __attribute__((aligned(16))) uint8_t k_buf[2][kKT * KROW];
@@ -258,9 +264,9 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
       };
       const uint2 q0 = f16q(vreg[4 * i]), q1 = f16q(vreg[4 * i + 1]);
       const uint2 q2 = f16q(vreg[4 * i + 2]), q3 = f16q(vreg[4 * i + 3]);
-      uint4* rw = reinterpret_cast<uint4*>(v_lds + d * VROW + 32 * beta);
-      rw[0] = make_uint4(q0.x, q0.y, q2.x, q2.y);
-      rw[1] = make_uint4(q1.x, q1.y, q3.x, q3.y);
+      uint4* rw = reinterpret_cast<uint4*>(v_lds + d * VROW);
+      rw[(2 * beta) ^ (d & 7)] = make_uint4(q0.x, q0.y, q2.x, q2.y);
+      rw[(2 * beta + 1) ^ (d & 7)] = make_uint4(q1.x, q1.y, q3.x, q3.y);
 #else
       // dword q holds keys 16 beta + 4 q .. + 3, at vt_pos of its first key:
       // q = 0, 1, 2, 3 go to +0, +32, +16, +48 from q = 0's position
@@ -392,8 +398,9 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : 2, GT == 1 ? 1 : 2))) void pref
     for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
       for (int beta = 0; beta < 4; ++beta) {
-        const f16x8 va16 =
-            *reinterpret_cast<const f16x8*>(v_lds + (32 * dt + c) * VROW + 32 * beta + 16 * g);
+        const int row = 32 * dt + c;
+        const f16x8 va16 = *reinterpret_cast<const f16x8*>(
+            v_lds + row * VROW + 16 * ((2 * beta + g) ^ (row & 7)));
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va16, pb[beta], acc[dt], 0, 0, 0);
       }
 #else
