@@ -363,10 +363,16 @@ kvq_status kvq_decode_attn_append(void* out, kvq_out out_dtype, const void* q_bf
  * vs compute type; [T] 10.4.2 attention with a mask):
  *   q: bf16 [total_q][Hq][dh], variable length: sequence b owns rows
  *     cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (int32 [B+1], cu_seqlens_q[0] = 0),
- *     read on the device only; max_q_len bounds every chunk length on the host.
+ *     read on the device only; max_q_len bounds every chunk length on the host
+ *     (rows of a longer chunk past that bound are left unspecified).  An empty
+ *     chunk (cu_seqlens_q[b+1] == cu_seqlens_q[b]) is allowed.
  *   Row i of sequence b is the token at absolute position
  *     context_lens[b] - qlen_b + i and attends keys 0..position (causal).  The
  *     chunk's own K/V must already be in the cache (kvq_cache_write).
+ *     context_lens: int32 [B], read on the device, clamped to
+ *     [0, max_blocks * bs]; a row whose position is negative (a context
+ *     shorter than its chunk) sees no key and gets an all-zero row.
+ *   Block ids outside [0, num_blocks) are clamped into the pool, as in decode.
  *   Q is quantized in-kernel to E4M3 with q_scale (q_gran: [1] or [Hq]):
  *     q_hat = s_q * fp8(fl32(q / s_q)); Q K^T runs on FP8 matrix cores with
  *     fp32 accumulation; P is fed to the P V product as two E4M3 terms,

@@ -81,6 +81,13 @@ __device__ __forceinline__ int vt_pos(int k) {
 __device__ __forceinline__ float fmax3(float a, float b, float c) {
   return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
+// x of this lane and of lane ^ 32, from one v_permlane32_swap (a VALU op:
+// no LDS round trip)
+__device__ __forceinline__ f32x2 halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return f32x2{__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+}
 
 template <int FMT>
 struct MfmaFmt {
@@ -194,42 +201,44 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
   // for it right after issue).  Keys past the context are masked out of S by
   // the causal test, and their V codes are zeroed below.
   const int nb_last = num_blocks - 1 < 0x7fffffff ? (int)(num_blocks - 1) : 0x7fffffff;
-  auto load_tile = [&](int kt, int idv) {
-    // every 16-byte piece of one wave lies in a single block of the tile (DH
-    // and NT are multiples of 64), so that block's id is read from lane beta
-    // of idv with a wave-uniform index
-    auto piece_base = [&](int u) {
-      const int beta = __builtin_amdgcn_readfirstlane(u / DH);
-      int blk = __builtin_amdgcn_readlane(idv, beta);
-      blk = blk < 0 ? 0 : (blk > nb_last ? nb_last : blk);
-      return (size_t)blk * bstride + (size_t)h * tile_stride;
-    };
+  // every 16-byte piece of one wave lies in a single block of the tile (DH
+  // and NT are multiples of 64), so that block's id is read from lane beta
+  // of idv with a wave-uniform index
+  auto piece_base = [&](int u, int idv) {
+    const int beta = __builtin_amdgcn_readfirstlane(u / DH);
+    int blk = __builtin_amdgcn_readlane(idv, beta);
+    blk = blk < 0 ? 0 : (blk > nb_last ? nb_last : blk);
+    return (size_t)blk * bstride + (size_t)h * tile_stride;
+  };
+  auto load_k = [&](int idv) {
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       // piece u = (block beta, 16-channel chunk, token): consecutive threads
       // read consecutive 16-byte runs of a K tile ([DH/16][16 tokens][16])
       const int u = threadIdx.x + i * NT;
       const int piece = (u / 16) % (DH / 16), t = u % 16;
-      const uint4 w = *reinterpret_cast<const uint4*>(kc + piece_base(u) + piece * 256 + t * 16);
+      const uint4 w = *reinterpret_cast<const uint4*>(kc + piece_base(u, idv) + piece * 256 + t * 16);
       kreg[4 * i] = w.x;
       kreg[4 * i + 1] = w.y;
       kreg[4 * i + 2] = w.z;
       kreg[4 * i + 3] = w.w;
     }
+  };
+  auto load_v = [&](int idv) {
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
       const int u = threadIdx.x + i * NT;
-      const uint4 w = *reinterpret_cast<const uint4*>(vc + piece_base(u) + (u % DH) * 16);
+      const uint4 w = *reinterpret_cast<const uint4*>(vc + piece_base(u, idv) + (u % DH) * 16);
       vreg[4 * i] = w.x;
       vreg[4 * i + 1] = w.y;
       vreg[4 * i + 2] = w.z;
       vreg[4 * i + 3] = w.w;
     }
   };
-  auto store_tile = [&](int kt, uint8_t* k_lds, uint8_t* v_lds) {
-    // slots past the context may hold any bytes, NaN codes included; their
-    // zero weights would not cancel a NaN, so they are zeroed (only the tile
-    // holding the context's last block has any)
+  // slots past the context may hold any bytes, NaN codes included; their
+  // zero weights would not cancel a NaN, so the V codes of tile kt are zeroed
+  // there (only the tile holding the context's last block has any)
+  auto mask_v = [&](int kt) {
     if (kt * kKT + kKT > ctx) {
 #pragma unroll
       for (int i = 0; i < VP; ++i) {
@@ -244,6 +253,8 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
         for (int j = 0; j < 4; ++j) vreg[4 * i + j] &= keep(j);
       }
     }
+  };
+  auto store_k = [&](uint8_t* k_lds) {
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int u = threadIdx.x + i * NT;
@@ -251,6 +262,8 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
       *reinterpret_cast<uint4*>(k_lds + key * KROW + piece * 16) =
           make_uint4(kreg[4 * i], kreg[4 * i + 1], kreg[4 * i + 2], kreg[4 * i + 3]);
     }
+  };
+  auto store_v = [&](uint8_t* v_lds) {
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
       const int u = threadIdx.x + i * NT;
@@ -284,40 +297,28 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
 #else
   i32x8 ph = {}, pl = {};  // probability operands (every byte rewritten per tile)
 #endif
-  int ids_next = 0;
-  if (nkt > 0) {
-    load_tile(0, load_ids(0));
-    store_tile(0, k_buf[0], v_buf[0]);
-    if (nkt > 1) load_tile(1, load_ids(1));
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nkt; ++kt) {
-    const uint8_t* k_lds = k_buf[kt & 1];
-    const uint8_t* v_lds = v_buf[kt & 1];
-    if (kt + 2 < nkt) ids_next = load_ids(kt + 2);  // lands during this tile
 
-    // ---- S^T = K Q^T for keys [64kt, 64kt + 64): raw FP8 dot products
-    f32x16 s[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[t][v] = 0.0f;
-#pragma unroll
-    for (int m = 0; m < DH / 64; ++m)  // the two key halves' chains interleave
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint8_t* ap = k_lds + (32 * t + c) * KROW + 64 * m + 32 * g;
-        const uint4 a0 = *reinterpret_cast<const uint4*>(ap);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16);
-        i32x8 A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                   (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        s[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, qb[m], s[t], MfmaFmt<FMT>::value,
-                                                               0, 0, 0, 0, 0);
-      }
+  // ---- S^T = K Q^T for keys [64kt, 64kt + 64): raw FP8 dot products.  MFMA
+  //      i covers channels [64 (i / 2), +64) of key half i % 2; consecutive
+  //      MFMAs feed different accumulators
+  constexpr int NS = 2 * DH / 64;
+  auto qk_read = [&](const uint8_t* k_lds, int i) {
+    const uint8_t* ap = k_lds + (32 * (i & 1) + c) * KROW + 64 * (i >> 1) + 32 * g;
+    const uint4 a0 = *reinterpret_cast<const uint4*>(ap);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16);
+    return i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                 (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  };
+  auto qk_mfma = [&](f32x16* s, int i, const i32x8& A) {
+    s[i & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, qb[i >> 1], s[i & 1],
+                                                               MfmaFmt<FMT>::value, 0, 0, 0, 0, 0);
+  };
 
-    // ---- online softmax for this lane's query (column c); lane holds keys
-    //      64kt + 32t + 8(v/4) + 4g + (v%4).  Causally masked scores (and
-    //      every key past the context) become -inf.
+  // ---- online softmax for this lane's query (column c); lane holds keys
+  //      64kt + 32t + 8(v/4) + 4g + (v%4).  Causally masked scores (and
+  //      every key past the context) become -inf.  Returns the exponent
+  //      bias of F p for the tile.
+  auto softmax_max = [&](f32x16* s, int kt) {
     if (kt * kKT + kKT - 1 > pos_min) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -332,7 +333,8 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int v = 0; v < 16; v += 2) tmax = fmax3(tmax, s[t][v], s[t][v + 1]);
-    tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+    const f32x2 th = halves(tmax);
+    tmax = __builtin_fmaxf(th.x, th.y);
     // the running max only moves when a score exceeds it by more than 2^tau
     // (in log2 units), so F p stays <= F 2^tau = 256 and rescales are rare
     if (__builtin_amdgcn_ballot_w64((tmax - m_raw) * zc > kTau)) {
@@ -345,55 +347,54 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
         for (int v = 0; v < 16; ++v) acc[dt][v] *= f;
       m_raw = mnew;
     }
-    // F p = exp2(raw * zc - (m * zc - log2 F)); P_hi = e4m3(F p),
-    // P_lo = e4m3(16 (F p - P_hi)); both exact-range, no saturation needed
-    const float bias = m_raw * zc - kLog2F;
+    // F p = exp2(raw * zc - (m * zc - log2 F))
+    return m_raw * zc - kLog2F;
+  };
+  // probabilities of keys 32 t + 8 v4 + 4 g + (0..3): P_hi = e4m3(F p),
+  // P_lo = e4m3(16 (F p - P_hi)); both exact-range, no saturation needed
+  auto p_chunk = [&](const f32x16* s, int t, int v4, float bias) {
+    float fp[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        float fp[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          fp[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][4 * v4 + r], zc, -bias));
-          l_run += fp[r];
-        }
+    for (int r = 0; r < 4; ++r) {
+      fp[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][4 * v4 + r], zc, -bias));
+      l_run += fp[r];
+    }
 #if KVQ_PREFILL_P_F16
-        // keys 32 t + 8 v4 + 4 g + r: step beta = 2 t + v4 / 2, slot 4 (v4 & 1) + r
-        {
-          const int beta = 2 * t + (v4 >> 1), o = 4 * (v4 & 1);
-          pb[beta][o] = (_Float16)fp[0];
-          pb[beta][o + 1] = (_Float16)fp[1];
-          pb[beta][o + 2] = (_Float16)fp[2];
-          pb[beta][o + 3] = (_Float16)fp[3];
-        }
+    // keys 32 t + 8 v4 + 4 g + r: step beta = 2 t + v4 / 2, slot 4 (v4 & 1) + r
+    const int beta = 2 * t + (v4 >> 1), o = 4 * (v4 & 1);
+    pb[beta][o] = (_Float16)fp[0];
+    pb[beta][o + 1] = (_Float16)fp[1];
+    pb[beta][o + 2] = (_Float16)fp[2];
+    pb[beta][o + 3] = (_Float16)fp[3];
 #else
-        // both halves of each dword are written, so the merge operand's old
-        // contents do not matter
-        const int d = pv_slot(t, v4);
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[0], fp[1], ph[d], false);
-        hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[2], fp[3], hi, true);
-        if constexpr (KVQ_PREFILL_P_TERMS == 2) {
-          const f32x2 h01 = dec2_f32<E4M3, false>((uint32_t)hi);
-          const f32x2 h23 = dec2_f32<E4M3, true>((uint32_t)hi);
-          // the merge operand's other half is overwritten by the second encode,
-          // so it is any free register (an empty asm defines one, emitting no
-          // instruction), and no copy or zero is needed to feed it
-          s16x2 lo;
-          asm volatile("" : "=v"(lo));
-          // the scaled encode divides by its scale: e4m3((F p - P_hi) * 16)
-          lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, fp[0] - h01.x, fp[1] - h01.y, 0.0625f,
-                                                        false);
-          lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, fp[2] - h23.x, fp[3] - h23.y, 0.0625f,
-                                                        true);
-          pl[d] = __builtin_bit_cast(int, lo);
-        }
-        ph[d] = hi;
+    // both halves of each dword are written, so the merge operand's old
+    // contents do not matter
+    const int d = pv_slot(t, v4);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[0], fp[1], ph[d], false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[2], fp[3], hi, true);
+    if constexpr (KVQ_PREFILL_P_TERMS == 2) {
+      const f32x2 h01 = dec2_f32<E4M3, false>((uint32_t)hi);
+      const f32x2 h23 = dec2_f32<E4M3, true>((uint32_t)hi);
+      // the merge operand's other half is overwritten by the second encode,
+      // so it is any free register (an empty asm defines one, emitting no
+      // instruction), and no copy or zero is needed to feed it
+      s16x2 lo;
+      asm volatile("" : "=v"(lo));
+      // the scaled encode divides by its scale: e4m3((F p - P_hi) * 16)
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, fp[0] - h01.x, fp[1] - h01.y, 0.0625f,
+                                                    false);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, fp[2] - h23.x, fp[3] - h23.y, 0.0625f,
+                                                    true);
+      pl[d] = __builtin_bit_cast(int, lo);
+    }
+    ph[d] = hi;
 #endif
-      }
+  };
 
+  // ---- O^T += V^T P^T
+  auto pv = [&](const uint8_t* v_lds) {
 #if KVQ_PREFILL_P_F16
-    // ---- O^T += V^T P^T on f16 matrix cores: 4 channel tiles x 4 key steps
+    // f16 matrix cores: 4 channel tiles x 4 key steps
 #pragma unroll
     for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
@@ -404,8 +405,8 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va16, pb[beta], acc[dt], 0, 0, 0);
       }
 #else
-    // ---- O^T += V^T P^T for channel tiles of 32: P_hi at scale 1, P_lo at
-    //      scale 2^-4 (E8M0 block scales 127 and 123) into one accumulator
+    // channel tiles of 32: P_hi at scale 1, P_lo at scale 2^-4 (E8M0 block
+    // scales 127 and 123) into one accumulator
     i32x8 va[DH / 32];
 #pragma unroll
     for (int dt = 0; dt < DH / 32; ++dt) {
@@ -426,20 +427,62 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
             va[dt], pl, acc[dt], MfmaFmt<FMT>::value, 0, 0, kScaleOne, 0, kScaleLo);
     }
 #endif
+  };
+
+  int ids_next = 0;
+  if (nkt > 0) {
+    const int id0 = load_ids(0);
+    load_k(id0);
+    load_v(id0);
+    mask_v(0);
+    store_k(k_buf[0]);
+    store_v(v_buf[0]);
+    if (nkt > 1) {
+      const int id1 = load_ids(1);
+      load_k(id1);
+      load_v(id1);
+    }
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nkt; ++kt) {
+    const uint8_t* k_lds = k_buf[kt & 1];
+    const uint8_t* v_lds = v_buf[kt & 1];
+    if (kt + 2 < nkt) ids_next = load_ids(kt + 2);  // lands during this tile
+
+    f32x16 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[t][v] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i)  // the two key halves' chains interleave
+      qk_mfma(s, i, qk_read(k_lds, i));
+    const float bias = softmax_max(s, kt);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) p_chunk(s, t, v4, bias);
+    pv(v_lds);
 
     // ---- tile kt + 1 (loaded during this tile) into the other buffer, whose
     //      readers all passed the previous barrier; then start loading tile
     //      kt + 2; one barrier per tile
     if (kt + 1 < nkt) {
-      store_tile(kt + 1, k_buf[(kt + 1) & 1], v_buf[(kt + 1) & 1]);
-      if (kt + 2 < nkt) load_tile(kt + 2, ids_next);
+      mask_v(kt + 1);
+      store_k(k_buf[(kt + 1) & 1]);
+      store_v(v_buf[(kt + 1) & 1]);
+      if (kt + 2 < nkt) {
+        load_k(ids_next);
+        load_v(ids_next);
+      }
     }
     __syncthreads();
   }
 
   // ---- epilogue: O = acc / (sum of F p) * sV; lane holds channels
   //      32dt + 8i + 4g + r of query c
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const f32x2 lh = halves(l_run);
+  const float l_tot = lh.x + lh.y;
   if (!qvalid) return;
   const float sv = vs[kv_per_head ? h : 0];
   const float scale = l_tot > 0.0f ? sv / l_tot : 0.0f;

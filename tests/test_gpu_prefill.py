@@ -93,6 +93,21 @@ def test_small_ragged_chunks(fmt, dh):
     check(run.gpu(), run.oracle_full())
 
 
+def test_empty_chunk_and_chunk_longer_than_context():
+    """A sequence with no new rows between two others, and one whose context
+    is shorter than its chunk: its first rows sit at negative positions, see
+    no key and come out as zeros (the oracle's empty softmax)."""
+    wl = W.prefill_workload("empty", 207, [30, 10, 0], [17, 0, 40], 8, 2, 128, 16, "e4m3")
+    wl.paging.context_lens[2] = 25
+    run = PrefillRun(wl)
+    out = run.gpu()
+    ref = run.oracle_full()
+    cu = wl.cu_seqlens
+    assert np.all(ref[cu[2]:cu[2] + 15] == 0)
+    assert np.all(out[cu[2]:cu[2] + 15] == 0)
+    check(out, ref)
+
+
 @pytest.mark.parametrize("fmt,fill", [("e4m3", 0xFF), ("e5m2", 0xFF), ("e5m2", 0x7C)])
 def test_stale_nan_bytes_past_the_context(fmt, fill):
     """Slots past each sequence's context hold NaN (or Inf) codes, as a reused
