@@ -104,8 +104,38 @@ def _gran(g) -> int:
     return GRAN_NAMES[g] if isinstance(g, str) else int(g)
 
 
-def _ptr(t) -> int | None:
-    return None if t is None else t.data_ptr()
+# dtypes each kind of tensor argument may have (names of torch dtypes)
+_KINDS = {"bf16": ("bfloat16",), "u8": ("uint8",), "f32": ("float32",), "i32": ("int32",),
+          "i64": ("int64",), "s16": ("int16", "uint16", "float16"),
+          "out": ("float32", "bfloat16")}
+
+
+def _ptr(t, kind: str | None = None, dense: bool = True) -> int | None:
+    """Device address of tensor t (None passes NULL, which the library
+    rejects where a pointer is required).  t must live on the GPU, be
+    contiguous unless dense is False (padded-page cache views, whose layout
+    the caller checks), and have a dtype of the given kind."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("kvq: tensor arguments must be on the GPU")
+    if dense and not t.is_contiguous():
+        raise ValueError("kvq: tensor arguments must be contiguous")
+    if kind is not None and t.dtype not in _kind_dtypes(kind):
+        raise TypeError(f"kvq: dtype {t.dtype} where {'/'.join(_KINDS[kind])} is expected")
+    return t.data_ptr()
+
+
+_KIND_DTYPES: dict = {}
+
+
+def _kind_dtypes(kind: str) -> frozenset:
+    """The torch dtypes of a kind, built once (the per-call check allocates nothing)."""
+    s = _KIND_DTYPES.get(kind)
+    if s is None:
+        import torch
+        s = _KIND_DTYPES[kind] = frozenset(getattr(torch, n) for n in _KINDS[kind])
+    return s
 
 
 def _cache_dims(k_cache, v_cache):
@@ -145,22 +175,23 @@ def kvq_kv_cache_bytes(L: int, B: int, Hkv: int, S: int, dh: int, bits_per_elem:
 
 def kvq_fp8_encode(x, fmt, out, stream=None) -> None:
     """out (uint8, same numel) <- saturating RNE codes of fp32 x."""
-    _check("kvq_fp8_encode", lib().kvq_fp8_encode(_fmt(fmt), _ptr(x), x.numel(), _ptr(out),
-                                                  _stream(stream)))
+    _check("kvq_fp8_encode", lib().kvq_fp8_encode(_fmt(fmt), _ptr(x, "f32"), x.numel(),
+                                                  _ptr(out, "u8"), _stream(stream)))
 
 
 def kvq_fp8_decode(codes, fmt, out, stream=None) -> None:
     """out (fp32, same numel) <- exact values of uint8 codes."""
-    _check("kvq_fp8_decode", lib().kvq_fp8_decode(_fmt(fmt), _ptr(codes), codes.numel(),
-                                                  _ptr(out), _stream(stream)))
+    _check("kvq_fp8_decode", lib().kvq_fp8_decode(_fmt(fmt), _ptr(codes, "u8"), codes.numel(),
+                                                  _ptr(out, "f32"), _stream(stream)))
 
 
 def kvq_calibrate_scales(x, fmt, gran, amax_io, scale_out, accumulate=False, stream=None) -> None:
     """x: bf16 [T, H, dh]; amax_io / scale_out: fp32 [1] or [H]."""
     T, H, dh = x.shape
     _check("kvq_calibrate_scales",
-           lib().kvq_calibrate_scales(_ptr(x), T, H, dh, _fmt(fmt), _gran(gran), _ptr(amax_io),
-                                      _ptr(scale_out), int(bool(accumulate)), _stream(stream)))
+           lib().kvq_calibrate_scales(_ptr(x, "bf16"), T, H, dh, _fmt(fmt), _gran(gran),
+                                      _ptr(amax_io, "f32"), _ptr(scale_out, "f32"),
+                                      int(bool(accumulate)), _stream(stream)))
 
 
 def kvq_cache_write(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, fmt, gran,
@@ -170,9 +201,10 @@ def kvq_cache_write(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, fmt,
     T, Hkv, dh = k.shape
     nb, _, bs, _ = _cache_dims(k_cache, v_cache)
     _check("kvq_cache_write",
-           lib().kvq_cache_write(_ptr(k), _ptr(v), T, Hkv, dh, _ptr(slot_mapping), _ptr(k_cache),
-                                 _ptr(v_cache), nb, bs, _ptr(k_scale), _ptr(v_scale), _fmt(fmt),
-                                 _gran(gran), _stream(stream)))
+           lib().kvq_cache_write(_ptr(k, "bf16"), _ptr(v, "bf16"), T, Hkv, dh,
+                                 _ptr(slot_mapping, "i64"), _ptr(k_cache, "u8"),
+                                 _ptr(v_cache, "u8"), nb, bs, _ptr(k_scale, "f32"),
+                                 _ptr(v_scale, "f32"), _fmt(fmt), _gran(gran), _stream(stream)))
 
 
 def kvq_decode_workspace_size(B: int, Hq: int, dh: int, max_context_len: int, bs: int) -> int:
@@ -191,12 +223,13 @@ def kvq_decode_attn(out, q, k_cache, v_cache, block_tables, context_lens, max_co
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
     _check("kvq_decode_attn",
-           lib().kvq_decode_attn(_ptr(out), out_dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), nb,
-                                 _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B,
-                                 Hq, Hkv, dh, bs, int(max_context_len), _ptr(k_scale),
-                                 _ptr(v_scale), _fmt(fmt), _gran(gran), float(softmax_scale),
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                 _stream(stream)))
+           lib().kvq_decode_attn(_ptr(out, "out"), out_dt, _ptr(q, "bf16"), _ptr(k_cache, "u8"),
+                                 _ptr(v_cache, "u8"), nb, _ptr(block_tables, "i32"),
+                                 block_tables.shape[1], _ptr(context_lens, "i32"), B, Hq, Hkv, dh,
+                                 bs, int(max_context_len), _ptr(k_scale, "f32"),
+                                 _ptr(v_scale, "f32"), _fmt(fmt), _gran(gran),
+                                 float(softmax_scale), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def _scale_cache_dims(k_scale_cache, v_scale_cache, nb, Hkv, bs):
@@ -214,9 +247,10 @@ def kvq_cache_write_token_scales(k, v, slot_mapping, k_cache, v_cache, k_scale_c
     nb, _, bs, _ = _cache_dims(k_cache, v_cache)
     _scale_cache_dims(k_scale_cache, v_scale_cache, nb, Hkv, bs)
     _check("kvq_cache_write_token_scales",
-           lib().kvq_cache_write_token_scales(_ptr(k), _ptr(v), T, Hkv, dh, _ptr(slot_mapping),
-                                              _ptr(k_cache), _ptr(v_cache), _ptr(k_scale_cache),
-                                              _ptr(v_scale_cache), nb, bs, _fmt(fmt),
+           lib().kvq_cache_write_token_scales(_ptr(k, "bf16"), _ptr(v, "bf16"), T, Hkv, dh,
+                                              _ptr(slot_mapping, "i64"), _ptr(k_cache, "u8"),
+                                              _ptr(v_cache, "u8"), _ptr(k_scale_cache, "s16"),
+                                              _ptr(v_scale_cache, "s16"), nb, bs, _fmt(fmt),
                                               _stream(stream)))
 
 
@@ -233,12 +267,16 @@ def kvq_decode_attn_token_scales(out, q, k_cache, v_cache, k_scale_cache, v_scal
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
     _check("kvq_decode_attn_token_scales",
-           lib().kvq_decode_attn_token_scales(
-               _ptr(out), out_dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale_cache),
-               _ptr(v_scale_cache), nb, _ptr(block_tables), block_tables.shape[1],
-               _ptr(context_lens), B, Hq, Hkv, dh, bs, int(max_context_len), _fmt(fmt),
-               float(softmax_scale), _ptr(workspace),
-               workspace.numel() * workspace.element_size(), _stream(stream)))
+           lib().kvq_decode_attn_token_scales(_ptr(out, "out"), out_dt, _ptr(q, "bf16"),
+                                              _ptr(k_cache, "u8"), _ptr(v_cache, "u8"),
+                                              _ptr(k_scale_cache, "s16"),
+                                              _ptr(v_scale_cache, "s16"), nb,
+                                              _ptr(block_tables, "i32"), block_tables.shape[1],
+                                              _ptr(context_lens, "i32"), B, Hq, Hkv, dh, bs,
+                                              int(max_context_len), _fmt(fmt),
+                                              float(softmax_scale), _ptr(workspace),
+                                              workspace.numel() * workspace.element_size(),
+                                              _stream(stream)))
 
 
 def kvq_prefill_attn(out, q, cu_seqlens_q, max_q_len, q_scale, q_gran, k_cache, v_cache,
@@ -251,10 +289,12 @@ def kvq_prefill_attn(out, q, cu_seqlens_q, max_q_len, q_scale, q_gran, k_cache, 
     B = cu_seqlens_q.shape[0] - 1
     out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
     _check("kvq_prefill_attn",
-           lib().kvq_prefill_attn(_ptr(out), out_dt, _ptr(q), _ptr(cu_seqlens_q), int(max_q_len),
-                                  _ptr(q_scale), _gran(q_gran), _ptr(k_cache), _ptr(v_cache), nb,
-                                  _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
-                                  B, Hq, Hkv, dh, bs, _ptr(k_scale), _ptr(v_scale), _fmt(fmt),
+           lib().kvq_prefill_attn(_ptr(out, "out"), out_dt, _ptr(q, "bf16"),
+                                  _ptr(cu_seqlens_q, "i32"), int(max_q_len), _ptr(q_scale, "f32"),
+                                  _gran(q_gran), _ptr(k_cache, "u8"), _ptr(v_cache, "u8"), nb,
+                                  _ptr(block_tables, "i32"), block_tables.shape[1],
+                                  _ptr(context_lens, "i32"), B, Hq, Hkv, dh, bs,
+                                  _ptr(k_scale, "f32"), _ptr(v_scale, "f32"), _fmt(fmt),
                                   _gran(kv_gran), float(softmax_scale), _stream(stream)))
 
 
@@ -268,8 +308,9 @@ def kvq_kivi_quantize(k, v, group_blocks, kivi_cache, stream=None) -> None:
     if T % 32 or kivi_cache.dim() != 3 or kivi_cache.shape[2] != KIVI_TILE:
         raise ValueError("k must hold whole 32-token groups and kivi_cache be [nb, Hkv, 3072]")
     _check("kvq_kivi_quantize",
-           lib().kvq_kivi_quantize(_ptr(k), _ptr(v), T // 32, Hkv, dh, _ptr(group_blocks),
-                                   _ptr(kivi_cache), kivi_cache.shape[0], _stream(stream)))
+           lib().kvq_kivi_quantize(_ptr(k, "bf16"), _ptr(v, "bf16"), T // 32, Hkv, dh,
+                                   _ptr(group_blocks, "i32"), _ptr(kivi_cache, "u8"),
+                                   kivi_cache.shape[0], _stream(stream)))
 
 
 def kvq_kivi_decode_workspace_size(B: int, Hq: int, Hkv: int, max_groups: int) -> int:
@@ -289,11 +330,13 @@ def kvq_kivi_decode_attn(out, q, kivi_cache, block_tables, quant_groups, max_gro
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
     _check("kvq_kivi_decode_attn",
-           lib().kvq_kivi_decode_attn(_ptr(out), out_dt, _ptr(q), _ptr(kivi_cache),
-                                      kivi_cache.shape[0], _ptr(block_tables),
-                                      block_tables.shape[1], _ptr(quant_groups), int(max_groups),
-                                      _ptr(res_k), _ptr(res_v), _ptr(res_lens), R, B, Hq, Hkv,
-                                      dh, float(softmax_scale), _ptr(workspace),
+           lib().kvq_kivi_decode_attn(_ptr(out, "out"), out_dt, _ptr(q, "bf16"),
+                                      _ptr(kivi_cache, "u8"), kivi_cache.shape[0],
+                                      _ptr(block_tables, "i32"), block_tables.shape[1],
+                                      _ptr(quant_groups, "i32"), int(max_groups),
+                                      _ptr(res_k, "bf16"), _ptr(res_v, "bf16"),
+                                      _ptr(res_lens, "i32"), R, B, Hq, Hkv, dh,
+                                      float(softmax_scale), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(),
                                       _stream(stream)))
 
@@ -318,8 +361,8 @@ def kvq_page_bytes(Hkv: int, dh: int, bs: int, bits_per_elem: int) -> int:
 
 def kvq_common_page_bytes(layer_bits, Hkv: int, dh: int, bs: int) -> int:
     arr = (ctypes.c_int * max(1, len(layer_bits)))(*[int(b) for b in layer_bits])
-    return int(lib().kvq_common_page_bytes(ctypes.cast(arr, ctypes.c_void_p), len(layer_bits),
-                                           Hkv, dh, bs))
+    return int(lib().kvq_common_page_bytes(ctypes.cast(arr, ctypes.c_void_p), len(layer_bits), Hkv,
+                                           dh, bs))
 
 
 def _paged_dims(k_cache, v_cache):
@@ -327,7 +370,8 @@ def _paged_dims(k_cache, v_cache):
     views into a pool of padded pages: inside a block the tensors must be
     dense; the block stride (bytes) is stride(0), the same for K and V."""
     nb, Hkv, bs, dh = _cache_dims(k_cache, v_cache)
-    if k_cache.stride()[1:] != (dh * bs, 16 * bs, 16, 1) or v_cache.stride()[1:] != (dh * bs, bs, 1):
+    if (k_cache.stride()[1:] != (dh * bs, 16 * bs, 16, 1)
+            or v_cache.stride()[1:] != (dh * bs, bs, 1)):
         raise ValueError("caches must be dense inside each block")
     if k_cache.stride(0) != v_cache.stride(0):
         raise ValueError("k_cache and v_cache must share one block stride")
@@ -341,9 +385,11 @@ def kvq_cache_write_paged(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale
     T, Hkv, dh = k.shape
     nb, _, bs, _, bst = _paged_dims(k_cache, v_cache)
     _check("kvq_cache_write_paged",
-           lib().kvq_cache_write_paged(_ptr(k), _ptr(v), T, Hkv, dh, _ptr(slot_mapping),
-                                       _ptr(k_cache), _ptr(v_cache), nb, bs, bst, _ptr(k_scale),
-                                       _ptr(v_scale), _fmt(fmt), _gran(gran), _stream(stream)))
+           lib().kvq_cache_write_paged(_ptr(k, "bf16"), _ptr(v, "bf16"), T, Hkv, dh,
+                                       _ptr(slot_mapping, "i64"), _ptr(k_cache, "u8", False),
+                                       _ptr(v_cache, "u8", False), nb, bs, bst,
+                                       _ptr(k_scale, "f32"), _ptr(v_scale, "f32"), _fmt(fmt),
+                                       _gran(gran), _stream(stream)))
 
 
 def kvq_decode_attn_paged(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
@@ -357,12 +403,13 @@ def kvq_decode_attn_paged(out, q, k_cache, v_cache, block_tables, context_lens, 
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
     _check("kvq_decode_attn_paged",
-           lib().kvq_decode_attn_paged(_ptr(out), out_dt, _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                       nb, _ptr(block_tables), block_tables.shape[1],
-                                       _ptr(context_lens), B, Hq, Hkv, dh, bs, bst,
-                                       int(max_context_len), _ptr(k_scale), _ptr(v_scale),
-                                       _fmt(fmt), _gran(gran), float(softmax_scale),
-                                       _ptr(workspace),
+           lib().kvq_decode_attn_paged(_ptr(out, "out"), out_dt, _ptr(q, "bf16"),
+                                       _ptr(k_cache, "u8", False), _ptr(v_cache, "u8", False), nb,
+                                       _ptr(block_tables, "i32"), block_tables.shape[1],
+                                       _ptr(context_lens, "i32"), B, Hq, Hkv, dh, bs, bst,
+                                       int(max_context_len), _ptr(k_scale, "f32"),
+                                       _ptr(v_scale, "f32"), _fmt(fmt), _gran(gran),
+                                       float(softmax_scale), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(),
                                        _stream(stream)))
 
@@ -376,11 +423,13 @@ def kvq_prefill_attn_paged(out, q, cu_seqlens_q, max_q_len, q_scale, q_gran, k_c
     B = cu_seqlens_q.shape[0] - 1
     out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
     _check("kvq_prefill_attn_paged",
-           lib().kvq_prefill_attn_paged(_ptr(out), out_dt, _ptr(q), _ptr(cu_seqlens_q),
-                                        int(max_q_len), _ptr(q_scale), _gran(q_gran),
-                                        _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_tables),
-                                        block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, dh,
-                                        bs, bst, _ptr(k_scale), _ptr(v_scale), _fmt(fmt),
+           lib().kvq_prefill_attn_paged(_ptr(out, "out"), out_dt, _ptr(q, "bf16"),
+                                        _ptr(cu_seqlens_q, "i32"), int(max_q_len),
+                                        _ptr(q_scale, "f32"), _gran(q_gran),
+                                        _ptr(k_cache, "u8", False), _ptr(v_cache, "u8", False), nb,
+                                        _ptr(block_tables, "i32"), block_tables.shape[1],
+                                        _ptr(context_lens, "i32"), B, Hq, Hkv, dh, bs, bst,
+                                        _ptr(k_scale, "f32"), _ptr(v_scale, "f32"), _fmt(fmt),
                                         _gran(kv_gran), float(softmax_scale), _stream(stream)))
 
 
@@ -397,11 +446,13 @@ def kvq_decode_attn_append(out, q, k_new, v_new, k_cache, v_cache, block_tables,
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
     _check("kvq_decode_attn_append",
-           lib().kvq_decode_attn_append(_ptr(out), out_dt, _ptr(q), _ptr(k_new), _ptr(v_new),
-                                        _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_tables),
-                                        block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, dh,
-                                        bs, int(max_context_len), _ptr(k_scale), _ptr(v_scale),
-                                        _fmt(fmt), _gran(gran), float(softmax_scale),
-                                        _ptr(workspace),
+           lib().kvq_decode_attn_append(_ptr(out, "out"), out_dt, _ptr(q, "bf16"),
+                                        _ptr(k_new, "bf16"), _ptr(v_new, "bf16"),
+                                        _ptr(k_cache, "u8"), _ptr(v_cache, "u8"), nb,
+                                        _ptr(block_tables, "i32"), block_tables.shape[1],
+                                        _ptr(context_lens, "i32"), B, Hq, Hkv, dh, bs,
+                                        int(max_context_len), _ptr(k_scale, "f32"),
+                                        _ptr(v_scale, "f32"), _fmt(fmt), _gran(gran),
+                                        float(softmax_scale), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(),
                                         _stream(stream)))

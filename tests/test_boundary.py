@@ -231,3 +231,13 @@ def test_paged_stride_validation():
              bt=FAKE, mb=4, cl=FAKE, B=1, Hq=8, Hkv=2, dh=128, bs=16, bst=nat + 4, ks=FAKE,
              vs=FAKE, fmt=0, kvg=0, sm=0.0, stream=None)
     assert L.kvq_prefill_attn_paged(*p.values()) == -3
+
+
+def test_binding_rejects_host_tensors():
+    """The Python binding passes device addresses only: a host tensor is
+    refused before the library is called."""
+    import torch
+    x = torch.zeros(8, dtype=torch.float32)
+    out = torch.zeros(8, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU"):
+        K.kvq_fp8_encode(x, "e4m3", out)

@@ -62,3 +62,22 @@ def test_encode_ragged_lengths(n):
     got = to_np(out)
     assert np.array_equal(got[:n], oracle.fp8_encode(oracle.FMT_E4M3, x))
     assert np.all(got[n:] == 0xA5)  # nothing written past the end
+
+
+def test_binding_rejects_strided_and_mistyped_tensors():
+    """A non-contiguous view or a tensor of the wrong dtype is refused by the
+    binding before any launch."""
+    import torch
+    import quantized_kv_cache_fp8_amd as K
+    dev = torch.device("cuda:0")
+    x = torch.zeros(16, dtype=torch.float32, device=dev)
+    out = torch.zeros(16, dtype=torch.uint8, device=dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        K.kvq_fp8_encode(x[::2], "e4m3", out[:8])
+    with pytest.raises(TypeError, match="float32"):
+        K.kvq_fp8_encode(x.to(torch.bfloat16), "e4m3", out)
+    with pytest.raises(TypeError, match="uint8"):
+        K.kvq_fp8_encode(x, "e4m3", out.to(torch.int8))
+    K.kvq_fp8_encode(x, "e4m3", out)
+    torch.cuda.synchronize()
+    assert int(out.sum()) == 0
