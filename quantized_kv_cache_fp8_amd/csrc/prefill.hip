@@ -19,9 +19,11 @@
 // Work decomposition: grid (query tiles of 32 rows, Hq / GT, sequences); a
 // workgroup has GT waves, one per query head of a GQA group, so every K/V tile
 // staged in LDS serves all GT heads.  Query tiles are issued longest-first
-// (the causal triangle makes late tiles the most expensive).  Per 64-key tile:
-// the workgroup copies K (4 cache blocks) into LDS row-major and V, whose cache
-// tiles are already channel-major, with its keys permuted into the order the B
+// (the causal triangle makes late tiles the most expensive), and workgroups
+// are renumbered so that each XCD takes consecutive tiles of the same
+// (sequence, head group) and keeps their K/V tiles in its own L2.  Per 64-key
+// tile: the workgroup copies K (4 cache blocks) into LDS row-major and V, whose
+// cache tiles are already channel-major, with its keys permuted into the order the B
 // operand holds P in (so each lane's A operand is one 32-byte run); the next
 // tile's bytes are loaded into registers while the current one is computed.
 // Each wave then runs 2*DH/64 MFMAs for S^T, the online softmax in registers
@@ -40,6 +42,12 @@
 // FP8-domain P V above; Q K^T stays on FP8 matrix cores either way
 #ifndef KVQ_PREFILL_P_F16
 #define KVQ_PREFILL_P_F16 0
+#endif
+// 1: workgroups are renumbered so that the ones dispatched to one XCD take
+// consecutive query tiles of the same (sequence, head group), whose K/V tiles
+// then stay in that XCD's L2; 0: grid order
+#ifndef KVQ_PREFILL_XCD_MAP
+#define KVQ_PREFILL_XCD_MAP 1
 #endif
 // waves per SIMD the kernel is compiled for (groups of 2 or 4 heads)
 #ifndef KVQ_PREFILL_WAVES
@@ -116,8 +124,20 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
   __shared__ __attribute__((aligned(16))) uint8_t k_buf[2][kKT * KROW];
   __shared__ __attribute__((aligned(16))) uint8_t v_buf[2][DH * VROW];
 
+#if KVQ_PREFILL_XCD_MAP
+  // workgroup w goes to XCD w % 8 (round-robin dispatch); over the largest
+  // multiple of 8 workgroups, logical tile (w % 8) * (N8 / 8) + w / 8 gives
+  // each XCD one contiguous run of the grid order, the rest keep their index
+  const uint32_t nx = gridDim.x, ny = gridDim.y;
+  const uint32_t w = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const uint32_t n8 = (nx * ny * gridDim.z) & ~7u;
+  const uint32_t lg = w < n8 ? (w & 7u) * (n8 >> 3) + (w >> 3) : w;
+  const int qt = n_qtiles - 1 - (int)(lg % nx);  // longest tiles first
+  const int grp = (int)((lg / nx) % ny), b = (int)(lg / (nx * ny));
+#else
   const int qt = n_qtiles - 1 - (int)blockIdx.x;  // longest tiles first
   const int grp = blockIdx.y, b = blockIdx.z;
+#endif
   const int G = Hq / Hkv;
   const int gpk = G / GT;
   const int h = grp / gpk;
