@@ -127,13 +127,15 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
 #if KVQ_PREFILL_XCD_MAP
   // workgroup w goes to XCD w % 8 (round-robin dispatch); over the largest
   // multiple of 8 workgroups, logical tile (w % 8) * (N8 / 8) + w / 8 gives
-  // each XCD one contiguous run of the grid order, the rest keep their index
-  const uint32_t nx = gridDim.x, ny = gridDim.y;
-  const uint32_t w = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
-  const uint32_t n8 = (nx * ny * gridDim.z) & ~7u;
+  // each XCD one contiguous run of the logical order, the rest keep their
+  // index.  The logical order runs query tiles fastest, then sequences, then
+  // head groups, so each XCD's run mixes sequences of different lengths.
+  const uint32_t nx = gridDim.x, nz = gridDim.z;
+  const uint32_t w = blockIdx.x + nx * (blockIdx.y + gridDim.y * blockIdx.z);
+  const uint32_t n8 = (nx * gridDim.y * nz) & ~7u;
   const uint32_t lg = w < n8 ? (w & 7u) * (n8 >> 3) + (w >> 3) : w;
   const int qt = n_qtiles - 1 - (int)(lg % nx);  // longest tiles first
-  const int grp = (int)((lg / nx) % ny), b = (int)(lg / (nx * ny));
+  const int b = (int)((lg / nx) % nz), grp = (int)(lg / (nx * nz));
 #else
   const int qt = n_qtiles - 1 - (int)blockIdx.x;  // longest tiles first
   const int grp = blockIdx.y, b = blockIdx.z;
