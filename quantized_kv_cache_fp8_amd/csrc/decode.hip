@@ -42,6 +42,10 @@ namespace kvq {
 
 // Largest split (cache blocks per workgroup): 8, 16, 32 or 64.  Larger splits mean
 // fewer partial results to merge, smaller ones more workgroups in flight.
+// query heads per combine workgroup (when it divides Hq)
+#ifndef KVQ_COMBINE_HPW
+#define KVQ_COMBINE_HPW 4
+#endif
 #ifndef KVQ_DECODE_MAX_SPLIT_BLOCKS
 #define KVQ_DECODE_MAX_SPLIT_BLOCKS 32
 #endif
@@ -775,18 +779,19 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   }
 }
 
-// grid (Hq, B), DH threads: merge the valid splits of one (b, hq) row.
+// grid (Hq / HPW, B), DH x HPW threads: merge the valid splits of HPW
+// (b, hq) rows, one per thread row.
 // Splits are taken 16 at a time, every load of a batch issued together (the
 // (m, l) pairs are the same for all threads of the row: broadcast loads), and
 // merged by log-sum-exp with a running maximum, so a typical row costs one
 // round trip to memory and needs no LDS or barrier.
-template <int DH, bool BF16>
-__global__ __launch_bounds__(DH) void decode_combine_kernel(
+template <int DH, bool BF16, int HPW>
+__global__ __launch_bounds__(DH * HPW) void decode_combine_kernel(
     void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
     const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int max_ctx,
     const float* __restrict__ vs, int per_head, int part_blocks, int nsplit) {
   constexpr int kBatch = 16;
-  const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int hq = blockIdx.x * HPW + threadIdx.y, b = blockIdx.y, d = threadIdx.x;
   int nvalid = nsplit;  // part_blocks == 0: every split holds a partial (maybe empty)
   if (part_blocks > 0) {
     int ctx = ctx_lens[b];
@@ -927,10 +932,17 @@ void launch_decode_combine(void* out, int out_bf16, const float* ml, const float
                            const int32_t* ctx, int B, int Hq, int Hkv, int dh, int max_ctx,
                            const float* vs, int per_head, int part_blocks, int nsplit,
                            hipStream_t s) {
-  const dim3 cgrid(Hq, B);
+  constexpr int kHpw = KVQ_COMBINE_HPW;
+  const bool wide = kHpw > 1 && Hq % kHpw == 0;
 #define KVQ_COMBINE(D, BF)                                                                     \
-  decode_combine_kernel<D, BF><<<cgrid, D, 0, s>>>(out, ml, acc, ctx, Hq, Hkv, max_ctx, vs,    \
-                                                   per_head, part_blocks, nsplit)
+  do {                                                                                         \
+    if (wide)                                                                                  \
+      decode_combine_kernel<D, BF, kHpw><<<dim3(Hq / kHpw, B), dim3(D, kHpw), 0, s>>>(         \
+          out, ml, acc, ctx, Hq, Hkv, max_ctx, vs, per_head, part_blocks, nsplit);             \
+    else                                                                                       \
+      decode_combine_kernel<D, BF, 1><<<dim3(Hq, B), D, 0, s>>>(                               \
+          out, ml, acc, ctx, Hq, Hkv, max_ctx, vs, per_head, part_blocks, nsplit);             \
+  } while (0)
   if (dh == 128) {
     if (out_bf16) KVQ_COMBINE(128, true); else KVQ_COMBINE(128, false);
   } else {
