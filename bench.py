@@ -402,43 +402,49 @@ def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, 
     rows["cache_write"] = {"workload": wl.name + " full context", "ms": round(ms, 4),
                            "GB/s": round(nbytes / ms / 1e6, 1)}
     del kc, vc
-    # FP8-domain causal chunked prefill: 8 x (4096 cached + 4096 new), per-head scales
-    pw = W.fp8_chunked_prefill()
-
+    # FP8-domain causal chunked prefill: 8 x (4096 cached + 4096 new), per-head
+    # scales; and a ragged batch of the same head shape (chunk = prefix, 256 to
+    # 4096 tokens), where work per sequence differs 16-fold
     def dt(a):
         if a.dtype == np.uint16:
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
                 torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    q = dt(pw.q)
-    pk, pv = dt(pw.kv.k), dt(pw.kv.v)
-    qs = torch.empty(pw.Hq, device=dev)
-    pks = torch.empty(pw.Hkv, device=dev)
-    pvs = torch.empty(pw.Hkv, device=dev)
-    am = torch.empty(pw.Hq, device=dev)
-    K.kvq_calibrate_scales(q, "fp8_e4m3", "head", am, qs)
-    K.kvq_calibrate_scales(pk, "fp8_e4m3", "head", am[:pw.Hkv], pks)
-    K.kvq_calibrate_scales(pv, "fp8_e4m3", "head", am[:pw.Hkv], pvs)
-    pkc = torch.empty((pw.paging.num_blocks, pw.Hkv, pw.dh // 16, pw.bs, 16), dtype=torch.uint8,
-                      device=dev)
-    pvc = torch.empty((pw.paging.num_blocks, pw.Hkv, pw.dh, pw.bs), dtype=torch.uint8, device=dev)
-    K.kvq_cache_write(pk, pv, dt(pw.kv.slot_mapping), pkc, pvc, pks, pvs, "fp8_e4m3", "head")
-    out = torch.empty((q.shape[0], pw.Hq, pw.dh), dtype=torch.float32, device=dev)
-    cu, bt, cl = dt(pw.cu_seqlens), dt(pw.paging.block_tables), dt(pw.paging.context_lens)
-    max_q = int(np.diff(pw.cu_seqlens).max())
 
-    def prefill():
-        K.kvq_prefill_attn(out, q, cu, max_q, qs, "head", pkc, pvc, bt, cl, pks, pvs,
-                           "fp8_e4m3", "head")
-    ms = time_call(torch, stream, prefill, 5)
-    flops = 0
-    for b in range(len(pw.prefix_lens)):
-        P, C = int(pw.prefix_lens[b]), int(pw.cu_seqlens[b + 1] - pw.cu_seqlens[b])
-        flops += 4 * pw.dh * pw.Hq * (C * P + C * (C + 1) // 2)
-    tf = flops / (ms * 1e-3) / 1e12
-    rows["prefill"] = {"workload": pw.name, "ms": round(ms, 4),
-                       "algorithmic_TFLOP": round(flops / 1e12, 4), "TFLOP/s": round(tf, 1),
-                       "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
+    def prefill_case(pw):
+        q = dt(pw.q)
+        pk, pv = dt(pw.kv.k), dt(pw.kv.v)
+        qs = torch.empty(pw.Hq, device=dev)
+        pks = torch.empty(pw.Hkv, device=dev)
+        pvs = torch.empty(pw.Hkv, device=dev)
+        am = torch.empty(pw.Hq, device=dev)
+        K.kvq_calibrate_scales(q, "fp8_e4m3", "head", am, qs)
+        K.kvq_calibrate_scales(pk, "fp8_e4m3", "head", am[:pw.Hkv], pks)
+        K.kvq_calibrate_scales(pv, "fp8_e4m3", "head", am[:pw.Hkv], pvs)
+        pkc = torch.empty((pw.paging.num_blocks, pw.Hkv, pw.dh // 16, pw.bs, 16),
+                          dtype=torch.uint8, device=dev)
+        pvc = torch.empty((pw.paging.num_blocks, pw.Hkv, pw.dh, pw.bs), dtype=torch.uint8,
+                          device=dev)
+        K.kvq_cache_write(pk, pv, dt(pw.kv.slot_mapping), pkc, pvc, pks, pvs, "fp8_e4m3", "head")
+        out = torch.empty((q.shape[0], pw.Hq, pw.dh), dtype=torch.float32, device=dev)
+        cu, bt, cl = dt(pw.cu_seqlens), dt(pw.paging.block_tables), dt(pw.paging.context_lens)
+        max_q = int(np.diff(pw.cu_seqlens).max())
+
+        def prefill():
+            K.kvq_prefill_attn(out, q, cu, max_q, qs, "head", pkc, pvc, bt, cl, pks, pvs,
+                               "fp8_e4m3", "head")
+        ms = time_call(torch, stream, prefill, 5)
+        flops = 0
+        for b in range(len(pw.prefix_lens)):
+            P, C = int(pw.prefix_lens[b]), int(pw.cu_seqlens[b + 1] - pw.cu_seqlens[b])
+            flops += 4 * pw.dh * pw.Hq * (C * P + C * (C + 1) // 2)
+        tf = flops / (ms * 1e-3) / 1e12
+        return {"workload": pw.name, "ms": round(ms, 4),
+                "algorithmic_TFLOP": round(flops / 1e12, 4), "TFLOP/s": round(tf, 1),
+                "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
+
+    rows["prefill"] = prefill_case(W.fp8_chunked_prefill())
+    rows["prefill_ragged"] = prefill_case(W.ragged_chunked_prefill())
     return rows
 
 

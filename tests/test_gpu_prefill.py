@@ -171,6 +171,25 @@ def test_full_size_sampled_rows():
     assert np.all(np.isfinite(out))
 
 
+def test_ragged_full_size_sampled_rows():
+    """The ragged batch of the bench (chunk = prefix, 256 to 4096 tokens, full
+    head shape): every sequence's first and last row and a seeded sample."""
+    wl = W.ragged_chunked_prefill()
+    run = PrefillRun(wl)
+    out = run.gpu()
+    kc, vc = run.oracle_caches()
+    g = W.rng(67)
+    cu = wl.cu_seqlens
+    rows = [(int(cu[b]), 3) for b in range(8)] + [(int(cu[b + 1]) - 1, 28) for b in range(8)]
+    rows += [(int(g.integers(cu[-1])), int(g.integers(32))) for _ in range(32)]
+    rows = np.array(rows, np.int64)
+    ref = oracle.prefill_rows(rows, wl.q, wl.cu_seqlens, run.qs_ref, run.qg, kc, vc,
+                              wl.paging.block_tables, wl.paging.context_lens, run.ks_ref,
+                              run.vs_ref, run.fmt, run.kg)
+    check(out[rows[:, 0], rows[:, 1]], ref)
+    assert np.all(np.isfinite(out))
+
+
 def test_explicit_softmax_scale():
     """A caller-given softmax scale in place of 1/sqrt(dh)."""
     wl = W.prefill_workload("prefill-sm", 314, [50, 0], [70, 33], Hq=16, Hkv=4)

@@ -217,6 +217,13 @@ def prefill_workload(name: str, seed: int, prefix_lens, chunk_lens, Hq: int = 32
     return PrefillWorkload(name, Hq, Hkv, dh, bs, fmt, paging, kv, q, cu, pl)
 
 
+def ragged_chunked_prefill(seed: int = BASE_SEED + 7) -> PrefillWorkload:
+    """8 sequences whose chunk and cached prefix are equal and range from 256 to
+    4096 tokens (work per sequence differs 16-fold); Hq=32, Hkv=8, dh=128."""
+    lens = [4096, 512, 2048, 1024, 4096, 256, 3072, 1536]
+    return prefill_workload("fp8-chunked-prefill-ragged-b8-256-4096", seed, lens, lens)
+
+
 def fp8_chunked_prefill(seed: int = BASE_SEED + 3, B: int = 8, prefix: int = 4096,
                         chunk: int = 4096) -> PrefillWorkload:
     """8 sequences, a 4096-token chunk each on top of 4096 cached tokens;
