@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--copies", type=int, default=4, help="cache copies rotated per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-rows", action="store_true", help="skip the extra per-row measurements")
+    p.add_argument("--no-ragged", action="store_true",
+                   help="skip the ragged prefill row (so a profile's prefill dispatches are "
+                        "the equal-chunk batch only)")
     p.add_argument("--cpu-sample-rows", type=int, default=0,
                    help="(b, hq) rows in the CPU oracle sample (0 = all rows)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -214,7 +217,8 @@ def main():
     # ------------------------------------------------------------ other rows (untimed loop)
     if not args.no_rows:
         result["rows"] = measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches,
-                                      ks, vs, wl, (q, bt, ctx, max_ctx, ws, out))
+                                      ks, vs, wl, (q, bt, ctx, max_ctx, ws, out),
+                                      ragged=not args.no_ragged)
 
         def two_calls():
             kc, vc = caches[0]
@@ -374,7 +378,8 @@ def kivi_rows(K, W, torch, dev, stream, reps=50):
     return rows
 
 
-def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, vs, wl, dec):
+def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, vs, wl, dec,
+                 ragged=True):
     rows = {}
     rows.update(kivi_rows(K, W, torch, dev, stream))
     rows.update(token_scale_rows(K, torch, dev, stream, k_all, v_all, slots_all, caches, wl,
@@ -444,7 +449,8 @@ def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, 
                 "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
 
     rows["prefill"] = prefill_case(W.fp8_chunked_prefill())
-    rows["prefill_ragged"] = prefill_case(W.ragged_chunked_prefill())
+    if ragged:
+        rows["prefill_ragged"] = prefill_case(W.ragged_chunked_prefill())
     return rows
 
 
