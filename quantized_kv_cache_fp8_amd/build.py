@@ -24,8 +24,6 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics",
 ]
-# extra compiler flags for tuning builds (e.g. -DKVQ_DECODE_MAX_SPLIT_BLOCKS=16)
-FLAGS += os.environ.get("KVQ_EXTRA_FLAGS", "").split()
 
 
 def _compile(src: str) -> str:

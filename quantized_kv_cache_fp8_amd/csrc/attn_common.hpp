@@ -5,12 +5,6 @@
 
 #include "codec.hpp"
 
-// Whether cache loads are marked nontemporal: every cache byte is read once
-// per call, so the loads stream through L2 instead of allocating in it.
-#ifndef KVQ_DECODE_NT_LOADS
-#define KVQ_DECODE_NT_LOADS 1
-#endif
-
 namespace kvq {
 namespace {
 constexpr float kLog2e = 1.4426950408889634f;
@@ -63,23 +57,17 @@ __device__ __forceinline__ uint32_t u4word(const uint4& v, int w) {
   return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
 }
 
+// Cache loads are nontemporal: every cache byte is read once per call, so
+// the loads stream through L2 instead of allocating in it.
 __device__ __forceinline__ uint4 load16(const uint8_t* p) {
-#if KVQ_DECODE_NT_LOADS
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
-#else
-  return *reinterpret_cast<const uint4*>(p);
-#endif
 }
 __device__ __forceinline__ uint2 load8(const uint8_t* p) {
-#if KVQ_DECODE_NT_LOADS
   typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
   const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
   return make_uint2(v.x, v.y);
-#else
-  return *reinterpret_cast<const uint2*>(p);
-#endif
 }
 
 __device__ __forceinline__ int64_t clamp_block(int64_t blk, int64_t num_blocks) {

@@ -40,45 +40,22 @@
 
 namespace kvq {
 
-// Largest split (cache blocks per workgroup): 8, 16, 32 or 64.  Larger splits mean
-// fewer partial results to merge, smaller ones more workgroups in flight.
+// Tuning constants (each measured against its alternatives on the
+// Llama-3-8B-shaped layer):
 // query heads per combine workgroup (when it divides Hq)
-#ifndef KVQ_COMBINE_HPW
-#define KVQ_COMBINE_HPW 4
-#endif
-#ifndef KVQ_DECODE_MAX_SPLIT_BLOCKS
-#define KVQ_DECODE_MAX_SPLIT_BLOCKS 32
-#endif
-// Waves per SIMD the generic split kernel is compiled for.  At 4 the whole
-// state (Q operand, one block pair of codes, the O tile) fits in 128
-// registers, so a compute unit keeps 16 waves' loads in flight.
-#ifndef KVQ_DECODE_WAVES_PER_EU
-#define KVQ_DECODE_WAVES_PER_EU 4
-#endif
-// Waves per SIMD of the kernel for groups of at most 4 heads.
-#ifndef KVQ_DECODE_G4_WAVES_PER_EU
-#define KVQ_DECODE_G4_WAVES_PER_EU 5
-#endif
-// ... and of its per-token-head-scale variant (4 more live registers: at 5
-// waves it spills)
-#ifndef KVQ_DECODE_TS_WAVES_PER_EU
-#define KVQ_DECODE_TS_WAVES_PER_EU 4
-#endif
-// Whether each wave of the generic kernel keeps two block pairs in flight
-// (two register sets).
-#ifndef KVQ_DECODE_DOUBLE_BUFFER
-#define KVQ_DECODE_DOUBLE_BUFFER 0
-#endif
-// Waves per workgroup of the kernel for groups of at most 4 heads (4, 2 or 1):
-// fewer waves per workgroup give each wave more block pairs of the same split.
-#ifndef KVQ_DECODE_G4_NW
-#define KVQ_DECODE_G4_NW 4
-#endif
-// Workgroup order: 1 puts the head groups of one split next to each other
-// (they read neighbouring tiles of the same blocks), 0 the splits of one group.
-#ifndef KVQ_DECODE_GRP_MAJOR
-#define KVQ_DECODE_GRP_MAJOR 1
-#endif
+constexpr int kCombineHeadsPerWg = 4;
+// largest split (cache blocks per workgroup); smaller splits are taken only
+// when the grid would otherwise have too few workgroups
+constexpr int kMaxSplitBlocks = 32;
+// waves per SIMD of the generic split kernel: its whole state (Q operand, one
+// block pair of codes, the O tile) fits in 128 registers
+constexpr int kWavesPerSimd = 4;
+// ... of the kernel for groups of at most 4 heads, and of its
+// per-token-head-scale variant (4 more live registers: at 5 waves it spills)
+constexpr int kG4WavesPerSimd = 5;
+constexpr int kTsWavesPerSimd = 4;
+// waves per workgroup of the kernel for groups of at most 4 heads
+constexpr int kG4Waves = 4;
 
 namespace {
 constexpr int kBlockSize = 16;  // tokens per cache block
@@ -91,7 +68,7 @@ static size_t decode_lds_bytes(int NH, int dh) {
          (size_t)4 * NH * dh * sizeof(float) + 2 * (size_t)dh;  // + appended token's codes
 }
 static size_t decode_g4_lds_bytes(int NH, int dh) {
-  constexpr int NW = KVQ_DECODE_G4_NW;
+  constexpr int NW = kG4Waves;
   return NW * 16 * 32 * sizeof(_Float16) + 2 * NW * 16 * sizeof(float) +
          (size_t)NW * NH * dh * sizeof(float) + 2 * (size_t)dh;  // + appended token's codes
 }
@@ -163,7 +140,7 @@ __device__ __forceinline__ void append_prologue(
 
 template <int FMT, int DH, int NPW, int HPL, bool APPEND>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(KVQ_DECODE_WAVES_PER_EU, KVQ_DECODE_WAVES_PER_EU))) void
+__attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void
 decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
                     const uint8_t* __restrict__ vc, int64_t num_blocks, int64_t bstride,
                     const int32_t* __restrict__ bt, int max_blocks,
@@ -178,8 +155,8 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   constexpr int RS = LaneHeads<HPL>::kStride;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  const int split = KVQ_DECODE_GRP_MAJOR ? blockIdx.y : blockIdx.x;
-  const int grp = KVQ_DECODE_GRP_MAJOR ? blockIdx.x : blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.y;
+  const int grp = blockIdx.x, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int gpk = G / NH;
   const int h = grp / gpk;
@@ -227,8 +204,8 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   // V: lane holds tokens tk .. tk + 7 of block eb for channel 16 n + c16.
   // Blocks past the split's end re-read its last block; their scores are
   // masked and their values zeroed, so nothing outside the table is read.
-  i32x8 kr[2], kr2[2];
-  uint2 vr[NV], vr2[NV];
+  i32x8 kr[2];
+  uint2 vr[NV];
   auto block_src = [&](int bi) {
     bi = bi < nblk ? bi : nblk - 1;
     return (size_t)clamp_block(btab[bi], num_blocks) * bstride + (size_t)h * tile;
@@ -272,10 +249,6 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   if (p < npair) {
     load_k(p, kr);
     load_v(p, vr);
-  }
-  if (KVQ_DECODE_DOUBLE_BUFFER && p + 4 < npair) {
-    load_k(p + 4, kr2);
-    load_v(p + 4, vr2);
   }
   bf16x8 qop[4];
 #pragma unroll
@@ -334,7 +307,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     }
     // this pair's K registers are free: the next pair's keys load during the
     // softmax and P V below
-    if (!KVQ_DECODE_DOUBLE_BUFFER && pre) load_k(p + 4, kr);
+    if (pre) load_k(p + 4, kr);
     // ---- online softmax per head.  Each lane tests its own scores against
     //      the running max; only when one exceeds it by more than tau does the
     //      wave take the (rare, wave-uniform) branch that finds the exact
@@ -399,33 +372,14 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     for (int n = 0; n < NV; ++n)
       O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, codes_to_f16x8<FMT>(vr[n].x, vr[n].y),
                                                     O[n], 0, 0, 0);
-    if (!KVQ_DECODE_DOUBLE_BUFFER && pre) load_v(p + 4, vr);  // V registers are free now
+    if (pre) load_v(p + 4, vr);  // V registers are free now
     };
 
-#if KVQ_DECODE_DOUBLE_BUFFER
-  // two register sets: while one pair is computed the pair after it lands
-#pragma unroll 1
-  for (; p < npair; p += 8) {
-    pair_step(p, kr, vr, false);
-    if (p + 8 < npair) {
-      load_k(p + 8, kr);
-      load_v(p + 8, vr);
-    }
-    if (p + 4 < npair) {
-      pair_step(p + 4, kr2, vr2, false);
-      if (p + 12 < npair) {
-        load_k(p + 12, kr2);
-        load_v(p + 12, vr2);
-      }
-    }
-  }
-#else
   // the last pair runs without loads, so inside the loop both prefetches
   // always happen and a pair's K wait never covers its V codes too
 #pragma unroll 1
   for (; p + 4 < npair; p += 4) pair_step(p, kr, vr, true);
   if (p < npair) pair_step(p, kr, vr, false);
-#endif
 
   // ---- merge the 4 waves through LDS and write the split's partial
 #pragma unroll
@@ -484,11 +438,11 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 // new token (k_new / v_new), writes its codes to the cache and patches them
 // into its own K / V registers, so no workgroup reads that slot from memory.
 template <int FMT, int DH, int NPW, int MODE>
-__global__ __launch_bounds__(64 * KVQ_DECODE_G4_NW)
-__attribute__((amdgpu_waves_per_eu(MODE == 1 ? KVQ_DECODE_TS_WAVES_PER_EU
-                                                : KVQ_DECODE_G4_WAVES_PER_EU,
-                                    MODE == 1 ? KVQ_DECODE_TS_WAVES_PER_EU
-                                                : KVQ_DECODE_G4_WAVES_PER_EU)))
+__global__ __launch_bounds__(64 * kG4Waves)
+__attribute__((amdgpu_waves_per_eu(MODE == 1 ? kTsWavesPerSimd
+                                                : kG4WavesPerSimd,
+                                    MODE == 1 ? kTsWavesPerSimd
+                                                : kG4WavesPerSimd)))
 void
 decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc,
                        const uint8_t* __restrict__ vc, int64_t num_blocks, int64_t bstride,
@@ -502,14 +456,14 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
                        const float* __restrict__ vs) {
   constexpr bool TS = MODE == 1, APPEND = MODE == 2;
   typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-  constexpr int NW = KVQ_DECODE_G4_NW;  // waves per workgroup
+  constexpr int NW = kG4Waves;  // waves per workgroup
   constexpr int PB = 2 * NW * NPW;      // blocks per split: NW waves x NPW pairs x 2
   constexpr int HALF = DH / 2;
   constexpr int NC = DH / 64;     // 64-channel halves of the output
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  const int split = KVQ_DECODE_GRP_MAJOR ? blockIdx.y : blockIdx.x;
-  const int grp = KVQ_DECODE_GRP_MAJOR ? blockIdx.x : blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.y;
+  const int grp = blockIdx.x, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int gpk = G / NH;
   const int h = grp / gpk;
@@ -851,7 +805,7 @@ DecodePlan decode_plan(int B, int Hq, int dh, int max_context_len, int bs) {
   if (B < 1 || Hq < 1 || dh < 1 || bs < 1 || max_context_len < 0) return p;
   const int64_t nb = ((int64_t)max_context_len + bs - 1) / bs;
   const int64_t groups = (int64_t)B * (Hq >= 4 ? Hq / 4 : 1);
-  int P = KVQ_DECODE_MAX_SPLIT_BLOCKS;
+  int P = kMaxSplitBlocks;
   // shrink the split until the grid has enough workgroups to fill the chip
   while (P > 8 && groups * ((nb + P - 1) / P) < 2048) P >>= 1;
   p.part_blocks = P;
@@ -876,8 +830,7 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
   float* ml = reinterpret_cast<float*>(ws);
   float* acc = ml + (size_t)B * Hq * plan.nsplit * 2;
   const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / __builtin_sqrtf((float)dh);
-  const dim3 grid(KVQ_DECODE_GRP_MAJOR ? Hq / NH : plan.nsplit,
-                  KVQ_DECODE_GRP_MAJOR ? plan.nsplit : Hq / NH, B);
+  const dim3 grid(Hq / NH, plan.nsplit, B);  // head groups of one split dispatch together
   const size_t lds = decode_lds_bytes(NH, dh);
   int nhp_shift = 0;
   while ((1 << nhp_shift) < NH) ++nhp_shift;  // NHp = 2^nhp_shift >= NH
@@ -895,8 +848,8 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
           max_ctx, ks, per_head, sm, plan.nsplit, ml, acc, k_new, v_new, kc_w, vc_w, vs);    \
   } while (0)
 #define KVQ_SPLIT_G4(F, D, N, M)                                                           \
-  decode_split_g4_kernel<F, D, N * 4 / KVQ_DECODE_G4_NW, M>                                   \
-      <<<grid, 64 * KVQ_DECODE_G4_NW, decode_g4_lds_bytes(NH, dh), s>>>(                    \
+  decode_split_g4_kernel<F, D, N * 4 / kG4Waves, M>                                   \
+      <<<grid, 64 * kG4Waves, decode_g4_lds_bytes(NH, dh), s>>>(                    \
       q, kc, vc, num_blocks, bstride, bt, max_blocks, ctx, Hq, Hkv, NH, rph_shift, max_ctx, ks, \
       per_head, sm, plan.nsplit, ml, acc, ksc, vsc, k_new, v_new, kc_w, vc_w, vs)
 #define KVQ_SPLIT_HP(F, D, N)                                     \
@@ -932,7 +885,7 @@ void launch_decode_combine(void* out, int out_bf16, const float* ml, const float
                            const int32_t* ctx, int B, int Hq, int Hkv, int dh, int max_ctx,
                            const float* vs, int per_head, int part_blocks, int nsplit,
                            hipStream_t s) {
-  constexpr int kHpw = KVQ_COMBINE_HPW;
+  constexpr int kHpw = kCombineHeadsPerWg;
   const bool wide = kHpw > 1 && Hq % kHpw == 0;
 #define KVQ_COMBINE(D, BF)                                                                     \
   do {                                                                                         \

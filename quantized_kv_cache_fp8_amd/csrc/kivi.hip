@@ -50,12 +50,10 @@
 #include "attn_common.hpp"
 #include "launch.hpp"
 
-// Waves per SIMD of the decode split kernel (94 VGPRs at 5; 6 spills)
-#ifndef KVQ_KIVI_WAVES_PER_EU
-#define KVQ_KIVI_WAVES_PER_EU 5
-#endif
-
 namespace kvq {
+
+// Waves per SIMD of the decode split kernel (94 VGPRs at 5; 6 spills)
+constexpr int kKiviWavesPerSimd = 5;
 
 namespace {
 constexpr int kG = 32;       // tokens per K group and per cache block; channels per V group
@@ -283,7 +281,7 @@ __device__ void kivi_residual_split(const uint16_t* __restrict__ q, const uint16
 
 template <int NPW>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(KVQ_KIVI_WAVES_PER_EU, KVQ_KIVI_WAVES_PER_EU))) void
+__attribute__((amdgpu_waves_per_eu(kKiviWavesPerSimd, kKiviWavesPerSimd))) void
 kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache,
                          int64_t num_blocks, const int32_t* __restrict__ bt, int max_blocks,
                          const int32_t* __restrict__ quant_groups, int max_groups,
@@ -565,14 +563,12 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
 // ---------------------------------------------------------------- launchers
 // Workgroups the quantized splits should at least give (the split shrinks,
 // from 32 groups down to 4, until they do).
-#ifndef KVQ_KIVI_MIN_WGS
-#define KVQ_KIVI_MIN_WGS 2048
-#endif
+constexpr int kKiviMinWgs = 2048;
 
 KiviPlan kivi_decode_plan(int B, int Hq, int Hkv, int max_groups) {
   KiviPlan p{};
   int PG = 32;
-  while (PG > 4 && (int64_t)B * Hkv * ((max_groups + PG - 1) / PG) < KVQ_KIVI_MIN_WGS) PG >>= 1;
+  while (PG > 4 && (int64_t)B * Hkv * ((max_groups + PG - 1) / PG) < kKiviMinWgs) PG >>= 1;
   p.groups_per_split = PG;
   p.nsplit = 1 + (max_groups + PG - 1) / PG;
   p.ws_bytes = (size_t)B * Hq * p.nsplit * (2 + kDH) * sizeof(float);

@@ -32,34 +32,11 @@
 #include "codec.hpp"
 #include "launch.hpp"
 
-// Terms P is carried in: 2 (P_hi + P_lo / 16, which meets the 2e-3 bar) or 1
-// (P_hi alone: an ablation build, measured but outside the bar)
-#ifndef KVQ_PREFILL_P_TERMS
-#define KVQ_PREFILL_P_TERMS 2
-#endif
-// 1: P in f16 and P V on f16 matrix cores, with the V codes converted to f16
-// (exactly) when a tile is staged -- a build option measured against the
-// FP8-domain P V above; Q K^T stays on FP8 matrix cores either way
-#ifndef KVQ_PREFILL_P_F16
-#define KVQ_PREFILL_P_F16 0
-#endif
-// 1: workgroups are renumbered so that the ones dispatched to one XCD take
-// consecutive query tiles of the same (sequence, head group), whose K/V tiles
-// then stay in that XCD's L2; 0: grid order
-#ifndef KVQ_PREFILL_XCD_MAP
-#define KVQ_PREFILL_XCD_MAP 1
-#endif
-// waves per SIMD the kernel is compiled for (groups of 2 or 4 heads)
-#ifndef KVQ_PREFILL_WAVES
-#define KVQ_PREFILL_WAVES 2
-#endif
-
 namespace kvq {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 namespace {
 constexpr int kQT = 32;          // query rows per wave
@@ -70,6 +47,9 @@ constexpr int kScaleOne = 127;   // E8M0 block scale 2^0
 constexpr int kScaleLo = 123;    // E8M0 block scale 2^-4 (P_lo carries 16x its value)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
+// waves per SIMD the kernel is compiled for (groups of 2 or 4 heads): its
+// state takes 208 registers, so two fit
+constexpr int kWavesPerSimd = 2;
 
 // Key order of the P V contraction.  Lane group g of the S tile holds keys
 // k = 32 t + 8 j + 4 g + r (t, j, r: key half, quad pair, byte); its P bytes
@@ -105,7 +85,7 @@ struct MfmaFmt {
 
 template <int FMT, int DH, int GT>
 __global__ __launch_bounds__(64 * GT)
-__attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 : KVQ_PREFILL_WAVES))) void prefill_kernel(
+__attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : kWavesPerSimd, GT == 1 ? 1 : kWavesPerSimd))) void prefill_kernel(
     void* __restrict__ out, int out_bf16, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ cu, int n_qtiles, const float* __restrict__ qs, int q_per_head,
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc, int64_t num_blocks,
@@ -115,16 +95,12 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
     float sm_scale) {
   constexpr int NT = 64 * GT;          // threads
   constexpr int KROW = DH + 16;        // padded K row in LDS (bytes)
-  // transposed-V row in LDS (bytes): 64 codes + 16 pad, or 64 f16 values
-  // unpadded, their 16-byte chunks swizzled by the row (chunk x of row r at
-  // x ^ (r & 7)) so the 8 lanes of an LDS read cycle hit distinct banks
-  constexpr int VROW = KVQ_PREFILL_P_F16 ? 2 * kKT : kKT + 16;
+  constexpr int VROW = kKT + 16;       // transposed-V row in LDS (bytes): 64 codes + pad
   // two K/V tile buffers: tile kt is read from buffer kt & 1 while tile kt + 1
   // is written into the other one
   __shared__ __attribute__((aligned(16))) uint8_t k_buf[2][kKT * KROW];
   __shared__ __attribute__((aligned(16))) uint8_t v_buf[2][DH * VROW];
 
-#if KVQ_PREFILL_XCD_MAP
   // workgroup w goes to XCD w % 8 (round-robin dispatch); over the largest
   // multiple of 8 workgroups, logical tile (w % 8) * (N8 / 8) + w / 8 gives
   // each XCD one contiguous run of the logical order, the rest keep their
@@ -136,10 +112,6 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
   const uint32_t lg = w < n8 ? (w & 7u) * (n8 >> 3) + (w >> 3) : w;
   const int qt = n_qtiles - 1 - (int)(lg % nx);  // longest tiles first
   const int b = (int)((lg / nx) % nz), grp = (int)(lg / (nx * nz));
-#else
-  const int qt = n_qtiles - 1 - (int)blockIdx.x;  // longest tiles first
-  const int grp = blockIdx.y, b = blockIdx.z;
-#endif
   const int G = Hq / Hkv;
   const int gpk = G / GT;
   const int h = grp / gpk;
@@ -290,19 +262,6 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
     for (int i = 0; i < VP; ++i) {
       const int u = threadIdx.x + i * NT;
       const int beta = u / DH, d = u - beta * DH;
-#if KVQ_PREFILL_P_F16
-      // block beta is one 16-key step of the f16 contraction: its 32 bytes
-      // hold keys 0-3, 8-11 (read by lane group 0) then 4-7, 12-15 (group 1)
-      auto f16q = [&](uint32_t w) {  // 4 codes -> 4 exact f16 values (2 dwords)
-        const f16x2 lo = dec2_f16<FMT, false>(w), hi = dec2_f16<FMT, true>(w);
-        return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-      };
-      const uint2 q0 = f16q(vreg[4 * i]), q1 = f16q(vreg[4 * i + 1]);
-      const uint2 q2 = f16q(vreg[4 * i + 2]), q3 = f16q(vreg[4 * i + 3]);
-      uint4* rw = reinterpret_cast<uint4*>(v_lds + d * VROW);
-      rw[(2 * beta) ^ (d & 7)] = make_uint4(q0.x, q0.y, q2.x, q2.y);
-      rw[(2 * beta + 1) ^ (d & 7)] = make_uint4(q1.x, q1.y, q3.x, q3.y);
-#else
       // dword q holds keys 16 beta + 4 q .. + 3, at vt_pos of its first key:
       // q = 0, 1, 2, 3 go to +0, +32, +16, +48 from q = 0's position
       uint32_t* rw = reinterpret_cast<uint32_t*>(v_lds + d * VROW + vt_pos(16 * beta));
@@ -310,15 +269,10 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
       rw[8] = vreg[4 * i + 1];
       rw[4] = vreg[4 * i + 2];
       rw[12] = vreg[4 * i + 3];
-#endif
     }
   };
 
-#if KVQ_PREFILL_P_F16
-  f16x8 pb[4];  // P of 16-key step beta (cache block beta of the tile)
-#else
   i32x8 ph = {}, pl = {};  // probability operands (every byte rewritten per tile)
-#endif
 
   // ---- S^T = K Q^T for keys [64kt, 64kt + 64): raw FP8 dot products.  MFMA
   //      i covers channels [64 (i / 2), +64) of key half i % 2; consecutive
@@ -381,20 +335,12 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
       fp[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][4 * v4 + r], zc, -bias));
       l_run += fp[r];
     }
-#if KVQ_PREFILL_P_F16
-    // keys 32 t + 8 v4 + 4 g + r: step beta = 2 t + v4 / 2, slot 4 (v4 & 1) + r
-    const int beta = 2 * t + (v4 >> 1), o = 4 * (v4 & 1);
-    pb[beta][o] = (_Float16)fp[0];
-    pb[beta][o + 1] = (_Float16)fp[1];
-    pb[beta][o + 2] = (_Float16)fp[2];
-    pb[beta][o + 3] = (_Float16)fp[3];
-#else
     // both halves of each dword are written, so the merge operand's old
     // contents do not matter
     const int d = pv_slot(t, v4);
     int hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[0], fp[1], ph[d], false);
     hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp[2], fp[3], hi, true);
-    if constexpr (KVQ_PREFILL_P_TERMS == 2) {
+    {
       const f32x2 h01 = dec2_f32<E4M3, false>((uint32_t)hi);
       const f32x2 h23 = dec2_f32<E4M3, true>((uint32_t)hi);
       // the merge operand's other half is overwritten by the second encode,
@@ -410,23 +356,10 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
       pl[d] = __builtin_bit_cast(int, lo);
     }
     ph[d] = hi;
-#endif
   };
 
   // ---- O^T += V^T P^T
   auto pv = [&](const uint8_t* v_lds) {
-#if KVQ_PREFILL_P_F16
-    // f16 matrix cores: 4 channel tiles x 4 key steps
-#pragma unroll
-    for (int dt = 0; dt < DH / 32; ++dt)
-#pragma unroll
-      for (int beta = 0; beta < 4; ++beta) {
-        const int row = 32 * dt + c;
-        const f16x8 va16 = *reinterpret_cast<const f16x8*>(
-            v_lds + row * VROW + 16 * ((2 * beta + g) ^ (row & 7)));
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va16, pb[beta], acc[dt], 0, 0, 0);
-      }
-#else
     // channel tiles of 32: P_hi at scale 1, P_lo at scale 2^-4 (E8M0 block
     // scales 127 and 123) into one accumulator
     i32x8 va[DH / 32];
@@ -442,13 +375,12 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : KVQ_PREFILL_WAVES, GT == 1 ? 1 
     for (int dt = 0; dt < DH / 32; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
           va[dt], ph, acc[dt], MfmaFmt<FMT>::value, 0, 0, kScaleOne, 0, kScaleOne);
-    if constexpr (KVQ_PREFILL_P_TERMS == 2) {
+    {
 #pragma unroll
       for (int dt = 0; dt < DH / 32; ++dt)
         acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             va[dt], pl, acc[dt], MfmaFmt<FMT>::value, 0, 0, kScaleOne, 0, kScaleLo);
     }
-#endif
   };
 
   int ids_next = 0;
