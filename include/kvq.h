@@ -137,10 +137,9 @@ kvq_status kvq_calibrate_scales(const void* x_bf16, int64_t T, int H, int dh, kv
  *   quotient correctly rounded to fp32 and fp8() the encoder above.  Tokens
  *   whose slot is negative (padding) or out of range are skipped; no other
  *   cache byte is touched; if two tokens name the same slot, which one lands
- *   is unspecified.  Scales must lie in [2^-126, 2^126) (positive
- *   fp32 values whose reciprocal is a normal number, as every calibrated
- *   scale of a tensor with amax >= 2^-117 is); other values give unspecified
- *   codes.
+ *   is unspecified.  Scales must be positive finite fp32 values below
+ *   2^126 (subnormal ones included); every scale kvq_calibrate_scales returns
+ *   is one.  Other values give unspecified codes.
  *   k, v: bf16 [T][Hkv][dh]; slot_mapping: int64 [T].
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED. */
 kvq_status kvq_cache_write(const void* k_bf16, const void* v_bf16, int64_t T, int Hkv, int dh,
@@ -337,7 +336,7 @@ kvq_status kvq_kivi_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16
                                 kvq_stream stream);
 
 /* Decode with the step's new token appended: for every sequence b with
- * context_lens[b] >= 1 (clamped to max_context_len) the new token's K and V
+ * 1 <= context_lens[b] <= max_context_len the new token's K and V
  * (k_new, v_new: bf16 [B][Hkv][dh]) are quantized and written at position
  * context_lens[b] - 1, i.e. block block_tables[b][pos / bs], offset pos % bs
  * (skipped when that block id lies outside [0, num_blocks)), and the query
@@ -345,7 +344,10 @@ kvq_status kvq_kivi_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16
  * The result and the cache bytes equal kvq_cache_write of those tokens
  * followed by kvq_decode_attn; here one kernel does both ([T] 10.4.2 write
  * rule and attention of the same step), so no launch sits between them.
- * k_new / v_new must be 16-byte aligned.
+ * A sequence whose context_lens[b] exceeds max_context_len (a bound taken
+ * before the lengths grew) attends its first max_context_len positions, as
+ * kvq_decode_attn does, and its new token is neither written nor attended: no
+ * cache byte of it changes.  k_new / v_new must be 16-byte aligned.
  * Errors: as kvq_decode_attn. */
 kvq_status kvq_decode_attn_append(void* out, kvq_out out_dtype, const void* q_bf16,
                                   const void* k_new_bf16, const void* v_new_bf16,

@@ -151,6 +151,68 @@ def _cache_dims(k_cache, v_cache):
     return nb, Hkv, bs, dh
 
 
+def _shape(name: str, t, want) -> None:
+    """Raise ValueError unless tensor t has exactly the shape want."""
+    if tuple(t.shape) != tuple(want):
+        raise ValueError(f"kvq: {name} has shape {tuple(t.shape)}, expected {tuple(want)}")
+
+
+def _rows(name: str, t, dim: int, n: int) -> None:
+    """Raise ValueError unless t has `dim` dimensions and at least n rows."""
+    if t.dim() != dim or t.shape[0] < n:
+        raise ValueError(f"kvq: {name} must have {dim} dimension(s) and at least {n} rows, "
+                         f"got shape {tuple(t.shape)}")
+
+
+def _scales(name: str, t, gran, H: int) -> None:
+    """A scale tensor holds one value (per tensor) or H values (per head)."""
+    n = H if _gran(gran) == KVQ_SCALE_HEAD else 1
+    if t is not None and t.numel() != n:
+        raise ValueError(f"kvq: {name} must hold {n} value(s) for this granularity, "
+                         f"got {t.numel()}")
+
+
+def _attn_shapes(out, q, Hkv, dh, block_tables, context_lens, B):
+    """Shape checks shared by the decode calls: q [B, Hq, dh] with dh the
+    cache's and Hq a multiple of Hkv, out like q, at least B block-table rows
+    and context lengths."""
+    if q.dim() != 3 or q.shape[2] != dh or q.shape[1] % Hkv:
+        raise ValueError(f"kvq: q has shape {tuple(q.shape)}; expected [B, Hq, {dh}] with Hq a "
+                         f"multiple of Hkv = {Hkv}")
+    _shape("out", out, q.shape)
+    _rows("block_tables", block_tables, 2, B)
+    _rows("context_lens", context_lens, 1, B)
+
+
+def _write_shapes(k, v, slot_mapping, Hkv, dh) -> int:
+    """k and v [T, Hkv, dh] with the cache's Hkv and dh, slot_mapping [T]; returns T."""
+    if k.dim() != 3:
+        raise ValueError(f"kvq: k must be [T, Hkv, dh], got shape {tuple(k.shape)}")
+    T = k.shape[0]
+    _shape("k", k, (T, Hkv, dh))
+    _shape("v", v, (T, Hkv, dh))
+    _shape("slot_mapping", slot_mapping, (T,))
+    return T
+
+
+def _prefill_shapes(out, q, cu_seqlens_q, q_scale, q_gran, Hkv, dh, block_tables, context_lens,
+                    k_scale, v_scale, kv_gran) -> int:
+    """Shape checks of the prefill calls; returns B (cu_seqlens_q holds B + 1 offsets)."""
+    if q.dim() != 3 or q.shape[2] != dh or q.shape[1] % Hkv:
+        raise ValueError(f"kvq: q has shape {tuple(q.shape)}; expected [total_q, Hq, {dh}] with "
+                         f"Hq a multiple of Hkv = {Hkv}")
+    _shape("out", out, q.shape)
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape[0] < 2:
+        raise ValueError("kvq: cu_seqlens_q must be [B + 1] with B >= 1")
+    B = cu_seqlens_q.shape[0] - 1
+    _rows("block_tables", block_tables, 2, B)
+    _rows("context_lens", context_lens, 1, B)
+    _scales("q_scale", q_scale, q_gran, q.shape[1])
+    _scales("k_scale", k_scale, kv_gran, Hkv)
+    _scales("v_scale", v_scale, kv_gran, Hkv)
+    return B
+
+
 def _stream(stream) -> int | None:
     if stream is not None:
         return int(stream)
@@ -175,19 +237,27 @@ def kvq_kv_cache_bytes(L: int, B: int, Hkv: int, S: int, dh: int, bits_per_elem:
 
 def kvq_fp8_encode(x, fmt, out, stream=None) -> None:
     """out (uint8, same numel) <- saturating RNE codes of fp32 x."""
+    if out.numel() != x.numel():
+        raise ValueError("kvq: out must have as many elements as x")
     _check("kvq_fp8_encode", lib().kvq_fp8_encode(_fmt(fmt), _ptr(x, "f32"), x.numel(),
                                                   _ptr(out, "u8"), _stream(stream)))
 
 
 def kvq_fp8_decode(codes, fmt, out, stream=None) -> None:
     """out (fp32, same numel) <- exact values of uint8 codes."""
+    if out.numel() != codes.numel():
+        raise ValueError("kvq: out must have as many elements as codes")
     _check("kvq_fp8_decode", lib().kvq_fp8_decode(_fmt(fmt), _ptr(codes, "u8"), codes.numel(),
                                                   _ptr(out, "f32"), _stream(stream)))
 
 
 def kvq_calibrate_scales(x, fmt, gran, amax_io, scale_out, accumulate=False, stream=None) -> None:
     """x: bf16 [T, H, dh]; amax_io / scale_out: fp32 [1] or [H]."""
+    if x.dim() != 3:
+        raise ValueError(f"kvq: x must be [T, H, dh], got shape {tuple(x.shape)}")
     T, H, dh = x.shape
+    _scales("amax_io", amax_io, gran, H)
+    _scales("scale_out", scale_out, gran, H)
     _check("kvq_calibrate_scales",
            lib().kvq_calibrate_scales(_ptr(x, "bf16"), T, H, dh, _fmt(fmt), _gran(gran),
                                       _ptr(amax_io, "f32"), _ptr(scale_out, "f32"),
@@ -198,8 +268,10 @@ def kvq_cache_write(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, fmt,
                     stream=None) -> None:
     """k, v: bf16 [T, Hkv, dh]; slot_mapping int64 [T]; caches: K uint8
     [nb, Hkv, dh/16, bs, 16], V uint8 [nb, Hkv, dh, bs]."""
-    T, Hkv, dh = k.shape
-    nb, _, bs, _ = _cache_dims(k_cache, v_cache)
+    nb, Hkv, bs, dh = _cache_dims(k_cache, v_cache)
+    T = _write_shapes(k, v, slot_mapping, Hkv, dh)
+    _scales("k_scale", k_scale, gran, Hkv)
+    _scales("v_scale", v_scale, gran, Hkv)
     _check("kvq_cache_write",
            lib().kvq_cache_write(_ptr(k, "bf16"), _ptr(v, "bf16"), T, Hkv, dh,
                                  _ptr(slot_mapping, "i64"), _ptr(k_cache, "u8"),
@@ -216,8 +288,11 @@ def kvq_decode_attn(out, q, k_cache, v_cache, block_tables, context_lens, max_co
                     stream=None) -> None:
     """out: fp32 or bf16 [B, Hq, dh]; q bf16 [B, Hq, dh]; block_tables int32 [B, max_blocks]."""
     import torch
-    B, Hq, dh = q.shape
-    nb, Hkv, bs, _ = _cache_dims(k_cache, v_cache)
+    nb, Hkv, bs, dh = _cache_dims(k_cache, v_cache)
+    _attn_shapes(out, q, Hkv, dh, block_tables, context_lens, q.shape[0])
+    B, Hq, _ = q.shape
+    _scales("k_scale", k_scale, gran, Hkv)
+    _scales("v_scale", v_scale, gran, Hkv)
     ws_bytes = kvq_decode_workspace_size(B, Hq, dh, max_context_len, bs)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
@@ -243,8 +318,8 @@ def kvq_cache_write_token_scales(k, v, slot_mapping, k_cache, v_cache, k_scale_c
                                  v_scale_cache, fmt, stream=None) -> None:
     """As kvq_cache_write with one fp16 scale per (token, KV head), computed from
     the row and stored in k_scale_cache / v_scale_cache (16-bit [nb, Hkv, bs])."""
-    T, Hkv, dh = k.shape
-    nb, _, bs, _ = _cache_dims(k_cache, v_cache)
+    nb, Hkv, bs, dh = _cache_dims(k_cache, v_cache)
+    T = _write_shapes(k, v, slot_mapping, Hkv, dh)
     _scale_cache_dims(k_scale_cache, v_scale_cache, nb, Hkv, bs)
     _check("kvq_cache_write_token_scales",
            lib().kvq_cache_write_token_scales(_ptr(k, "bf16"), _ptr(v, "bf16"), T, Hkv, dh,
@@ -259,8 +334,9 @@ def kvq_decode_attn_token_scales(out, q, k_cache, v_cache, k_scale_cache, v_scal
                                  softmax_scale=0.0, workspace=None, stream=None) -> None:
     """kvq_decode_attn over a cache with per-token-head fp16 scales (Hq / Hkv <= 4)."""
     import torch
-    B, Hq, dh = q.shape
-    nb, Hkv, bs, _ = _cache_dims(k_cache, v_cache)
+    nb, Hkv, bs, dh = _cache_dims(k_cache, v_cache)
+    _attn_shapes(out, q, Hkv, dh, block_tables, context_lens, q.shape[0])
+    B, Hq, _ = q.shape
     _scale_cache_dims(k_scale_cache, v_scale_cache, nb, Hkv, bs)
     ws_bytes = kvq_decode_workspace_size(B, Hq, dh, max_context_len, bs)
     if workspace is None:
@@ -284,9 +360,10 @@ def kvq_prefill_attn(out, q, cu_seqlens_q, max_q_len, q_scale, q_gran, k_cache, 
                      softmax_scale=0.0, stream=None) -> None:
     """out: fp32 or bf16 [total_q, Hq, dh]; q bf16 [total_q, Hq, dh]; cu_seqlens_q int32 [B+1]."""
     import torch
-    _, Hq, dh = q.shape
-    nb, Hkv, bs, _ = _cache_dims(k_cache, v_cache)
-    B = cu_seqlens_q.shape[0] - 1
+    nb, Hkv, bs, dh = _cache_dims(k_cache, v_cache)
+    B = _prefill_shapes(out, q, cu_seqlens_q, q_scale, q_gran, Hkv, dh, block_tables,
+                        context_lens, k_scale, v_scale, kv_gran)
+    Hq = q.shape[1]
     out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
     _check("kvq_prefill_attn",
            lib().kvq_prefill_attn(_ptr(out, "out"), out_dt, _ptr(q, "bf16"),
@@ -304,9 +381,15 @@ KIVI_TILE = 3072  # bytes per (32-token block, head) tile of the 2-bit cache
 def kvq_kivi_quantize(k, v, group_blocks, kivi_cache, stream=None) -> None:
     """k, v: bf16 [n_groups * 32, Hkv, 128]; group_blocks int32 [n_groups];
     kivi_cache uint8 [num_blocks, Hkv, 3072]."""
+    if k.dim() != 3 or kivi_cache.dim() != 3 or kivi_cache.shape[2] != KIVI_TILE:
+        raise ValueError("kvq: k must be [T, Hkv, 128] and kivi_cache [nb, Hkv, 3072]")
     T, Hkv, dh = k.shape
-    if T % 32 or kivi_cache.dim() != 3 or kivi_cache.shape[2] != KIVI_TILE:
-        raise ValueError("k must hold whole 32-token groups and kivi_cache be [nb, Hkv, 3072]")
+    if T % 32:
+        raise ValueError("kvq: k must hold whole 32-token groups")
+    _shape("v", v, k.shape)
+    _shape("group_blocks", group_blocks, (T // 32,))
+    if kivi_cache.shape[1] != Hkv:
+        raise ValueError(f"kvq: kivi_cache has {kivi_cache.shape[1]} KV heads, k has {Hkv}")
     _check("kvq_kivi_quantize",
            lib().kvq_kivi_quantize(_ptr(k, "bf16"), _ptr(v, "bf16"), T // 32, Hkv, dh,
                                    _ptr(group_blocks, "i32"), _ptr(kivi_cache, "u8"),
@@ -323,8 +406,20 @@ def kvq_kivi_decode_attn(out, q, kivi_cache, block_tables, quant_groups, max_gro
     """out: fp32 or bf16 [B, Hq, 128]; q bf16 [B, Hq, 128]; res_k / res_v bf16
     [B, Hkv, R, 128]; quant_groups / res_lens int32 [B]."""
     import torch
+    if q.dim() != 3 or res_k.dim() != 4 or kivi_cache.dim() != 3:
+        raise ValueError("kvq: q must be [B, Hq, 128], res_k [B, Hkv, R, 128] and kivi_cache "
+                         "[nb, Hkv, 3072]")
     B, Hq, dh = q.shape
     _, Hkv, R, _ = res_k.shape
+    _shape("res_k", res_k, (B, Hkv, R, dh))
+    _shape("res_v", res_v, res_k.shape)
+    _shape("out", out, q.shape)
+    _shape("kivi_cache", kivi_cache, (kivi_cache.shape[0], Hkv, KIVI_TILE))
+    if Hq % Hkv:
+        raise ValueError(f"kvq: Hq = {Hq} is not a multiple of Hkv = {Hkv}")
+    _rows("block_tables", block_tables, 2, B)
+    _rows("quant_groups", quant_groups, 1, B)
+    _rows("res_lens", res_lens, 1, B)
     ws_bytes = kvq_kivi_decode_workspace_size(B, Hq, Hkv, max_groups)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
@@ -382,8 +477,10 @@ def kvq_cache_write_paged(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale
                           stream=None) -> None:
     """kvq_cache_write on caches whose blocks sit block_stride = k_cache.stride(0)
     bytes apart (views into a pool of padded pages)."""
-    T, Hkv, dh = k.shape
-    nb, _, bs, _, bst = _paged_dims(k_cache, v_cache)
+    nb, Hkv, bs, dh, bst = _paged_dims(k_cache, v_cache)
+    T = _write_shapes(k, v, slot_mapping, Hkv, dh)
+    _scales("k_scale", k_scale, gran, Hkv)
+    _scales("v_scale", v_scale, gran, Hkv)
     _check("kvq_cache_write_paged",
            lib().kvq_cache_write_paged(_ptr(k, "bf16"), _ptr(v, "bf16"), T, Hkv, dh,
                                        _ptr(slot_mapping, "i64"), _ptr(k_cache, "u8", False),
@@ -396,8 +493,11 @@ def kvq_decode_attn_paged(out, q, k_cache, v_cache, block_tables, context_lens, 
                           k_scale, v_scale, fmt, gran, softmax_scale=0.0, workspace=None,
                           stream=None) -> None:
     import torch
-    B, Hq, dh = q.shape
-    nb, Hkv, bs, _, bst = _paged_dims(k_cache, v_cache)
+    nb, Hkv, bs, dh, bst = _paged_dims(k_cache, v_cache)
+    _attn_shapes(out, q, Hkv, dh, block_tables, context_lens, q.shape[0])
+    B, Hq, _ = q.shape
+    _scales("k_scale", k_scale, gran, Hkv)
+    _scales("v_scale", v_scale, gran, Hkv)
     ws_bytes = kvq_decode_workspace_size(B, Hq, dh, max_context_len, bs)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
@@ -418,9 +518,10 @@ def kvq_prefill_attn_paged(out, q, cu_seqlens_q, max_q_len, q_scale, q_gran, k_c
                            block_tables, context_lens, k_scale, v_scale, fmt, kv_gran,
                            softmax_scale=0.0, stream=None) -> None:
     import torch
-    _, Hq, dh = q.shape
-    nb, Hkv, bs, _, bst = _paged_dims(k_cache, v_cache)
-    B = cu_seqlens_q.shape[0] - 1
+    nb, Hkv, bs, dh, bst = _paged_dims(k_cache, v_cache)
+    B = _prefill_shapes(out, q, cu_seqlens_q, q_scale, q_gran, Hkv, dh, block_tables,
+                        context_lens, k_scale, v_scale, kv_gran)
+    Hq = q.shape[1]
     out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
     _check("kvq_prefill_attn_paged",
            lib().kvq_prefill_attn_paged(_ptr(out, "out"), out_dt, _ptr(q, "bf16"),
@@ -439,8 +540,13 @@ def kvq_decode_attn_append(out, q, k_new, v_new, k_cache, v_cache, block_tables,
     """kvq_decode_attn with the new token (k_new / v_new bf16 [B, Hkv, dh]) quantized
     into position context_lens[b] - 1 by the same kernel."""
     import torch
-    B, Hq, dh = q.shape
-    nb, Hkv, bs, _ = _cache_dims(k_cache, v_cache)
+    nb, Hkv, bs, dh = _cache_dims(k_cache, v_cache)
+    _attn_shapes(out, q, Hkv, dh, block_tables, context_lens, q.shape[0])
+    B, Hq, _ = q.shape
+    _shape("k_new", k_new, (B, Hkv, dh))
+    _shape("v_new", v_new, (B, Hkv, dh))
+    _scales("k_scale", k_scale, gran, Hkv)
+    _scales("v_scale", v_scale, gran, Hkv)
     if workspace is None:
         ws_bytes = kvq_decode_workspace_size(B, Hq, dh, max_context_len, bs)
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)

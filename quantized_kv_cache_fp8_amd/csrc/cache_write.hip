@@ -43,9 +43,9 @@ constexpr int kRowDw = kChunk / 4 + 1;  // LDS V-tile row: 16 dwords of codes + 
 constexpr int64_t kShortWrite = 512;
 
 template <int FMT>
-__device__ __forceinline__ uint32_t quant4(uint2 w, float s, float rs) {
-  return enc4<FMT>(quotient(bf16lo(w.x), s, rs), quotient(bf16hi(w.x), s, rs),
-                   quotient(bf16lo(w.y), s, rs), quotient(bf16hi(w.y), s, rs));
+__device__ __forceinline__ uint32_t quant4(uint2 w, const Divisor& d) {
+  return enc4<FMT>(quotient(bf16lo(w.x), d), quotient(bf16hi(w.x), d),
+                   quotient(bf16lo(w.y), d), quotient(bf16hi(w.y), d));
 }
 
 // Per-token-head scales (one fp16 scale per (token, head) for K and for V,
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     sk = ks[per_head ? h : 0];
     sv = vs[per_head ? h : 0];
   }
-  float rk = recip_rn(sk), rv = recip_rn(sv);
+  Divisor dk = make_divisor(sk), dv = make_divisor(sv);
 #pragma unroll
   for (int jb = 0; jb < kJobs; ++jb) {
     const int job = tid + 256 * jb;
@@ -177,13 +177,11 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
           s_sc[0][4 * tq + j] = k16;
           s_sc[1][4 * tq + j] = v16;
         }
-        sk = (float)__builtin_bit_cast(_Float16, k16);
-        sv = (float)__builtin_bit_cast(_Float16, v16);
-        rk = recip_rn(sk);
-        rv = recip_rn(sv);
+        dk = make_divisor((float)__builtin_bit_cast(_Float16, k16));
+        dv = make_divisor((float)__builtin_bit_cast(_Float16, v16));
       }
-      cv[j] = quant4<FMT>(wv[jb][j], sv, rv);
-      s_kt[(4 * tq + j) * kKRow + cq] = quant4<FMT>(wk[jb][j], sk, rk);
+      cv[j] = quant4<FMT>(wv[jb][j], dv);
+      s_kt[(4 * tq + j) * kKRow + cq] = quant4<FMT>(wk[jb][j], dk);
     }
     // rows cv[j] = token j, bytes = channels 4cq..4cq+3 -> one dword per channel
     const uint32_t t0l = __builtin_amdgcn_perm(cv[1], cv[0], 0x05010400u);  // a0 b0 a1 b1
@@ -257,16 +255,15 @@ __global__ __launch_bounds__(256) void cache_write_short_kernel(
   const uint4 v1 = *reinterpret_cast<const uint4*>(v + src + 8);
   const int64_t s = slot_mapping[t];
   if (s < 0 || s >= num_slots) return;  // padding or out of the pool: skipped
-  const float sk = ks[per_head ? h : 0], sv = vs[per_head ? h : 0];
-  const float rk = recip_rn(sk), rv = recip_rn(sv);
-  const uint4 kq = make_uint4(quant4<FMT>(make_uint2(k0.x, k0.y), sk, rk),
-                              quant4<FMT>(make_uint2(k0.z, k0.w), sk, rk),
-                              quant4<FMT>(make_uint2(k1.x, k1.y), sk, rk),
-                              quant4<FMT>(make_uint2(k1.z, k1.w), sk, rk));
-  const uint32_t vq[4] = {quant4<FMT>(make_uint2(v0.x, v0.y), sv, rv),
-                          quant4<FMT>(make_uint2(v0.z, v0.w), sv, rv),
-                          quant4<FMT>(make_uint2(v1.x, v1.y), sv, rv),
-                          quant4<FMT>(make_uint2(v1.z, v1.w), sv, rv)};
+  const Divisor dk = make_divisor(ks[per_head ? h : 0]), dv = make_divisor(vs[per_head ? h : 0]);
+  const uint4 kq = make_uint4(quant4<FMT>(make_uint2(k0.x, k0.y), dk),
+                              quant4<FMT>(make_uint2(k0.z, k0.w), dk),
+                              quant4<FMT>(make_uint2(k1.x, k1.y), dk),
+                              quant4<FMT>(make_uint2(k1.z, k1.w), dk));
+  const uint32_t vq[4] = {quant4<FMT>(make_uint2(v0.x, v0.y), dv),
+                          quant4<FMT>(make_uint2(v0.z, v0.w), dv),
+                          quant4<FMT>(make_uint2(v1.x, v1.y), dv),
+                          quant4<FMT>(make_uint2(v1.z, v1.w), dv)};
   const size_t tile = (size_t)(s >> 4) * bstride + (size_t)h * kBs * DH;
   const int off = (int)(s & (kBs - 1));
   *reinterpret_cast<uint4*>(kc + tile + q * (kBs * 16) + off * 16) = kq;
@@ -305,17 +302,16 @@ __global__ __launch_bounds__(256) void cache_write_token_kernel(
   }
   if (!live || s < 0 || s >= num_slots) return;  // padding or out of the pool: skipped
   const uint16_t sk16 = scale16_from_amax_bits<FMT>(ak), sv16 = scale16_from_amax_bits<FMT>(av);
-  const float sk = (float)__builtin_bit_cast(_Float16, sk16);
-  const float sv = (float)__builtin_bit_cast(_Float16, sv16);
-  const float rk = recip_rn(sk), rv = recip_rn(sv);
-  const uint4 kq = make_uint4(quant4<FMT>(make_uint2(k0.x, k0.y), sk, rk),
-                              quant4<FMT>(make_uint2(k0.z, k0.w), sk, rk),
-                              quant4<FMT>(make_uint2(k1.x, k1.y), sk, rk),
-                              quant4<FMT>(make_uint2(k1.z, k1.w), sk, rk));
-  const uint32_t vq[4] = {quant4<FMT>(make_uint2(v0.x, v0.y), sv, rv),
-                          quant4<FMT>(make_uint2(v0.z, v0.w), sv, rv),
-                          quant4<FMT>(make_uint2(v1.x, v1.y), sv, rv),
-                          quant4<FMT>(make_uint2(v1.z, v1.w), sv, rv)};
+  const Divisor dk = make_divisor((float)__builtin_bit_cast(_Float16, sk16));
+  const Divisor dv = make_divisor((float)__builtin_bit_cast(_Float16, sv16));
+  const uint4 kq = make_uint4(quant4<FMT>(make_uint2(k0.x, k0.y), dk),
+                              quant4<FMT>(make_uint2(k0.z, k0.w), dk),
+                              quant4<FMT>(make_uint2(k1.x, k1.y), dk),
+                              quant4<FMT>(make_uint2(k1.z, k1.w), dk));
+  const uint32_t vq[4] = {quant4<FMT>(make_uint2(v0.x, v0.y), dv),
+                          quant4<FMT>(make_uint2(v0.z, v0.w), dv),
+                          quant4<FMT>(make_uint2(v1.x, v1.y), dv),
+                          quant4<FMT>(make_uint2(v1.z, v1.w), dv)};
   const size_t row = (size_t)((s >> 4) * Hkv + h);  // scale caches are not padded
   const size_t tile = (size_t)(s >> 4) * bstride + (size_t)h * kBs * DH;
   const int off = (int)(s & (kBs - 1));

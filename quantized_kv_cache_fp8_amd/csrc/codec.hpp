@@ -152,7 +152,8 @@ __device__ __forceinline__ f16x2 dec2_f16(uint32_t w) {
 }
 
 // ---------------------------------------------------------------- quotient
-// fl32(x / s) for a positive, finite, normal scale s, given rs = fl32(1 / s).
+// fl32(x / s) for a positive, finite, normal scale s whose reciprocal is
+// normal too, given rs = fl32(1 / s).
 //
 // q0 = fl32(x * rs) is within an ulp of x / s; its remainder
 // e = x - s * q0 is exact in one FMA, and q0 + e * rs rounded once is the
@@ -174,6 +175,27 @@ __device__ __forceinline__ float quotient(float x, float s, float rs) {
 
 // Correctly rounded reciprocal of the scale (computed once per thread).
 __device__ __forceinline__ float recip_rn(float s) { return __fdiv_rn(1.0f, s); }
+
+// A quantization scale prepared for the quotient above, for any positive
+// finite s below 2^126 (every calibrated scale; subnormal ones included).  A
+// scale below 2^-100 (calibration gives one only for a tensor whose amax is
+// below about 2^-91) has a reciprocal at or beyond the fp32 range, so it is
+// taken as s' = s 2^64 and the dividend as x' = x 2^64: both products are
+// exact powers-of-two scalings, x' / s' = x / s, and x' overflows only where
+// x / s saturates the format anyway.
+struct Divisor {
+  float s, rs, pre;
+};
+__device__ __forceinline__ Divisor make_divisor(float s) {
+  Divisor d;
+  d.pre = s < 0x1p-100f ? 0x1p64f : 1.0f;
+  d.s = s * d.pre;
+  d.rs = recip_rn(d.s);
+  return d;
+}
+__device__ __forceinline__ float quotient(float x, const Divisor& d) {
+  return quotient(x * d.pre, d.s, d.rs);
+}
 
 // bf16 bit patterns packed two per dword -> fp32 (exact).
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -118,8 +118,8 @@ __device__ __forceinline__ void append_prologue(
     const bool isv = i >= DH;
     const int d = isv ? i - DH : i;
     const uint16_t x = (isv ? v_new : k_new)[((size_t)b * Hkv + h) * DH + d];
-    const float sc = (isv ? vs : ks)[per_head ? h : 0];
-    const float qv = quotient(__uint_as_float((uint32_t)x << 16), sc, recip_rn(sc));
+    const float qv = quotient(__uint_as_float((uint32_t)x << 16),
+                              make_divisor((isv ? vs : ks)[per_head ? h : 0]));
     pw[i] = (uint8_t)(enc2<FMT>(qv, qv) & 0xffu);
   }
   __syncthreads();
@@ -162,8 +162,11 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   const int h = grp / gpk;
   const int hq0 = h * G + (grp - h * gpk) * NH;
 
-  int ctx = ctx_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > max_ctx ? max_ctx : ctx);
+  // a context beyond the host bound is attended up to the bound; the append
+  // then neither writes nor attends the new token (its true slot lies past
+  // what this launch covers)
+  const int ctx_raw = ctx_lens[b];
+  const int ctx = ctx_raw < 0 ? 0 : (ctx_raw > max_ctx ? max_ctx : ctx_raw);
   const int tok0 = split * PB * kBlockSize;
   if (tok0 >= ctx) return;  // nothing of this sequence lies in this split
   const int nblk_left = (ctx - tok0 + kBlockSize - 1) / kBlockSize;
@@ -261,7 +264,8 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   uint8_t* pw = reinterpret_cast<uint8_t*>(wo + 4 * NH * DH);  // [2][DH]: K codes, V codes
   const uint8_t* patch = pw;
   if constexpr (APPEND)
-    append_prologue<FMT, DH>(ctx, tok0, nblk, btab, num_blocks, bstride, h, Hkv, b,
+    if (ctx_raw <= max_ctx)
+      append_prologue<FMT, DH>(ctx, tok0, nblk, btab, num_blocks, bstride, h, Hkv, b,
                              grp == h * gpk, k_new, v_new, ks, vs, per_head, kc_w, vc_w, pw,
                              p_new, e_new, off_new);
   const float zc = sm_scale * ks[per_head ? h : 0] * kLog2e;
@@ -469,8 +473,11 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   const int h = grp / gpk;
   const int hq0 = h * G + (grp - h * gpk) * NH;
 
-  int ctx = ctx_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > max_ctx ? max_ctx : ctx);
+  // a context beyond the host bound is attended up to the bound; the append
+  // then neither writes nor attends the new token (its true slot lies past
+  // what this launch covers)
+  const int ctx_raw = ctx_lens[b];
+  const int ctx = ctx_raw < 0 ? 0 : (ctx_raw > max_ctx ? max_ctx : ctx_raw);
   const int tok0 = split * PB * kBlockSize;
   if (tok0 >= ctx) return;  // nothing of this sequence lies in this split
   const int nblk_left = (ctx - tok0 + kBlockSize - 1) / kBlockSize;
@@ -561,7 +568,8 @@ decode_split_g4_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   uint8_t* pw = reinterpret_cast<uint8_t*>(wo + NW * NH * DH);  // [2][DH]: K codes, V codes
   const uint8_t* patch = pw;
   if constexpr (APPEND)
-    append_prologue<FMT, DH, 64 * NW>(ctx, tok0, nblk, btab, num_blocks, bstride, h, Hkv, b,
+    if (ctx_raw <= max_ctx)
+      append_prologue<FMT, DH, 64 * NW>(ctx, tok0, nblk, btab, num_blocks, bstride, h, Hkv, b,
                              grp == h * gpk, k_new, v_new, ks, vs, per_head, kc_w, vc_w, pw,
                              p_new, e_new, off_new);
 

@@ -137,7 +137,7 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : kWavesPerSimd, GT == 1 ? 1 : kW
 
   // ---- quantize this wave's query rows to E4M3 (B operand of S^T)
   const float sq = qs[q_per_head ? hq : 0];
-  const float rsq = recip_rn(sq);
+  const Divisor dq = make_divisor(sq);
   i32x8 qb[DH / 64];
   {
     const uint16_t* qp = q + ((size_t)(q0 + qi) * Hq + hq) * DH;
@@ -147,10 +147,10 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : kWavesPerSimd, GT == 1 ? 1 : kW
       for (int j = 0; j < 4; ++j) {  // 4 x 8 channels = bytes [64m + 32g, +32)
         uint4 w = qvalid ? *reinterpret_cast<const uint4*>(qp + 64 * m + 32 * g + 8 * j)
                          : make_uint4(0, 0, 0, 0);
-        qb[m][2 * j] = (int)enc4<E4M3>(quotient(bf16lo(w.x), sq, rsq), quotient(bf16hi(w.x), sq, rsq),
-                                       quotient(bf16lo(w.y), sq, rsq), quotient(bf16hi(w.y), sq, rsq));
-        qb[m][2 * j + 1] = (int)enc4<E4M3>(quotient(bf16lo(w.z), sq, rsq), quotient(bf16hi(w.z), sq, rsq),
-                                           quotient(bf16lo(w.w), sq, rsq), quotient(bf16hi(w.w), sq, rsq));
+        qb[m][2 * j] = (int)enc4<E4M3>(quotient(bf16lo(w.x), dq), quotient(bf16hi(w.x), dq),
+                                       quotient(bf16lo(w.y), dq), quotient(bf16hi(w.y), dq));
+        qb[m][2 * j + 1] = (int)enc4<E4M3>(quotient(bf16lo(w.z), dq), quotient(bf16hi(w.z), dq),
+                                           quotient(bf16lo(w.w), dq), quotient(bf16hi(w.w), dq));
       }
     }
   }

@@ -114,7 +114,8 @@ class DecodeRun:
         self.kamax = torch.empty(nh, dtype=torch.float32, device=dev)
         self.vamax = torch.empty(nh, dtype=torch.float32, device=dev)
         odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
-        self.out = torch.empty((wl.B, wl.Hq, wl.dh), dtype=odt, device=dev)
+        # NaN until written: a row the kernels never write cannot pass as finite
+        self.out = torch.full((wl.B, wl.Hq, wl.dh), float("nan"), dtype=odt, device=dev)
         self.max_ctx = int(wl.paging.context_lens.max()) if wl.B else 0
 
     def gpu_scales(self):

@@ -241,3 +241,105 @@ def test_binding_rejects_host_tensors():
     out = torch.zeros(8, dtype=torch.uint8)
     with pytest.raises(ValueError, match="GPU"):
         K.kvq_fp8_encode(x, "e4m3", out)
+
+
+def _host_case():
+    """Host tensors of a consistent decode / write / prefill case (2 sequences,
+    Hq = 8, Hkv = 2, dh = 128, a pool of 10 blocks); the shape checks run
+    before any pointer is taken, so host tensors reach them."""
+    import torch
+    bf, u8, i32 = torch.bfloat16, torch.uint8, torch.int32
+    c = dict(kc=torch.zeros(10, 2, 8, 16, 16, dtype=u8), vc=torch.zeros(10, 2, 128, 16, dtype=u8),
+             q=torch.zeros(2, 8, 128, dtype=bf), out=torch.zeros(2, 8, 128),
+             bt=torch.zeros(2, 4, dtype=i32), cl=torch.zeros(2, dtype=i32),
+             k=torch.zeros(5, 2, 128, dtype=bf), v=torch.zeros(5, 2, 128, dtype=bf),
+             slots=torch.zeros(5, dtype=torch.int64), s1=torch.ones(1), s2=torch.ones(2),
+             kn=torch.zeros(2, 2, 128, dtype=bf), vn=torch.zeros(2, 2, 128, dtype=bf))
+    return c
+
+
+def _bad(c, **over):
+    d = dict(c)
+    d.update(over)
+    return d
+
+
+@pytest.mark.parametrize("over,match", [
+    (dict(k="k3"), "k has shape"),          # more KV heads than the cache
+    (dict(v="vshort"), "v has shape"),
+    (dict(slots="slots4"), "slot_mapping"),
+    (dict(s1="s2"), "k_scale"),              # per-tensor call with two scales
+])
+def test_binding_checks_write_shapes(over, match):
+    import torch
+    c = _host_case()
+    alt = dict(k3=torch.zeros(5, 3, 128, dtype=torch.bfloat16),
+               vshort=torch.zeros(4, 2, 128, dtype=torch.bfloat16),
+               slots4=torch.zeros(4, dtype=torch.int64), s2=c["s2"])
+    d = _bad(c, **{k: alt[v] for k, v in over.items()})
+    with pytest.raises(ValueError, match=match):
+        K.kvq_cache_write(d["k"], d["v"], d["slots"], d["kc"], d["vc"], d["s1"], c["s1"],
+                          "e4m3", "tensor")
+
+
+@pytest.mark.parametrize("over,match", [
+    (dict(out="out_small"), "out has shape"),
+    (dict(q="q_dh64"), "q has shape"),      # head dim other than the cache's
+    (dict(q="q_hq6"), "q has shape"),       # Hq not a multiple of Hkv
+    (dict(bt="bt1"), "block_tables"),       # fewer rows than sequences
+    (dict(cl="cl1"), "context_lens"),
+    (dict(s2="s1"), "k_scale"),             # per-head call with one scale
+])
+def test_binding_checks_decode_shapes(over, match):
+    import torch
+    c = _host_case()
+    alt = dict(out_small=torch.zeros(1, 8, 128), q_dh64=torch.zeros(2, 8, 64, dtype=torch.bfloat16),
+               q_hq6=torch.zeros(2, 7, 128, dtype=torch.bfloat16),
+               bt1=torch.zeros(1, 4, dtype=torch.int32), cl1=torch.zeros(1, dtype=torch.int32),
+               s1=c["s1"])
+    d = _bad(c, **{k: alt[v] for k, v in over.items()})
+    if over.get("out") or over.get("q"):
+        d["out"] = d["out"] if over.get("out") else torch.zeros(d["q"].shape)
+    with pytest.raises(ValueError, match=match):
+        K.kvq_decode_attn(d["out"], d["q"], d["kc"], d["vc"], d["bt"], d["cl"], 64, d["s2"],
+                          c["s2"], "e4m3", "head")
+
+
+def test_binding_checks_append_and_prefill_shapes():
+    import torch
+    c = _host_case()
+    with pytest.raises(ValueError, match="k_new"):
+        K.kvq_decode_attn_append(c["out"], c["q"], c["k"], c["vn"], c["kc"], c["vc"], c["bt"],
+                                 c["cl"], 64, c["s1"], c["s1"], "e4m3", "tensor")
+    cu = torch.tensor([0, 3, 5], dtype=torch.int32)
+    q = torch.zeros(5, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out has shape"):
+        K.kvq_prefill_attn(torch.zeros(4, 8, 128), q, cu, 3, c["s1"], "tensor", c["kc"], c["vc"],
+                           c["bt"], c["cl"], c["s1"], c["s1"], "e4m3", "tensor")
+    with pytest.raises(ValueError, match="q_scale"):
+        K.kvq_prefill_attn(torch.zeros(5, 8, 128), q, cu, 3, c["s2"], "head", c["kc"], c["vc"],
+                           c["bt"], c["cl"], c["s1"], c["s1"], "e4m3", "tensor")
+    with pytest.raises(ValueError, match="block_tables"):
+        K.kvq_prefill_attn(torch.zeros(5, 8, 128), q, torch.tensor([0, 1, 2, 5], dtype=torch.int32),
+                           3, c["s1"], "tensor", c["kc"], c["vc"], c["bt"], c["cl"], c["s1"],
+                           c["s1"], "e4m3", "tensor")
+
+
+def test_binding_checks_calibrate_and_kivi_shapes():
+    import torch
+    x = torch.zeros(4, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="scale_out"):
+        K.kvq_calibrate_scales(x, "e4m3", "head", torch.zeros(2), torch.zeros(1))
+    k = torch.zeros(64, 2, 128, dtype=torch.bfloat16)
+    cache = torch.zeros(4, 2, K.KIVI_TILE, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="group_blocks"):
+        K.kvq_kivi_quantize(k, k, torch.zeros(3, dtype=torch.int32), cache)
+    with pytest.raises(ValueError, match="KV heads"):
+        K.kvq_kivi_quantize(k, k, torch.zeros(2, dtype=torch.int32),
+                            torch.zeros(4, 3, K.KIVI_TILE, dtype=torch.uint8))
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    rk = torch.zeros(2, 2, 16, 128, dtype=torch.bfloat16)
+    i32 = torch.int32
+    with pytest.raises(ValueError, match="res_v"):
+        K.kvq_kivi_decode_attn(torch.zeros(2, 8, 128), q, cache, torch.zeros(2, 4, dtype=i32),
+                               torch.zeros(2, dtype=i32), 4, rk, rk[:, :, :8], torch.zeros(2, dtype=i32))

@@ -57,8 +57,8 @@ def both_paths(wl, out_dtype="f32"):
     q, bt, cl = to_dev(wl.q), to_dev(wl.paging.block_tables), to_dev(wl.paging.context_lens)
     mc = int(wl.paging.context_lens.max())
     odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
-    o1 = torch.empty((wl.B, wl.Hq, wl.dh), dtype=odt, device="cuda:0")
-    o2 = torch.empty_like(o1)
+    o1 = torch.full((wl.B, wl.Hq, wl.dh), float("nan"), dtype=odt, device="cuda:0")
+    o2 = torch.full_like(o1, float("nan"))
     K.kvq_cache_write(kn, vn, ns, kc, vc, ks, vs, fmt, gran)
     K.kvq_decode_attn(o1, q, kc, vc, bt, cl, mc, ks, vs, fmt, gran)
     K.kvq_decode_attn_append(o2, q, kn, vn, kc2, vc2, bt, cl, mc, ks, vs, fmt, gran)
@@ -99,3 +99,39 @@ def test_append_full_size_llama_layer():
     wl = W.llama_layer_decode()
     o1, o2, *_ = both_paths(wl)
     assert np.array_equal(o1, o2)
+
+
+def test_append_context_beyond_the_host_bound_writes_nothing():
+    """A sequence whose context length exceeds max_context_len attends its
+    first max_context_len positions, like kvq_decode_attn, and its new token is
+    neither written nor attended: no cache byte changes, in particular not the
+    slot at position max_context_len - 1."""
+    import torch
+    import quantized_kv_cache_fp8_amd as K
+    cl = [40, 100, 70]
+    wl = W.decode_workload("append-bound", 945, len(cl), 32, 8, 128, cl, 16, "e4m3", "tensor")
+    kc, vc, ks, vs, kn, vn, ns, fmt, gran = prepare(wl)
+    mc = 99  # below sequence 1's length 100
+    kc2, vc2 = kc.clone(), vc.clone()
+    kb, vb = to_np(kc), to_np(vc)  # before any call
+    q, bt, cl_d = to_dev(wl.q), to_dev(wl.paging.block_tables), to_dev(wl.paging.context_lens)
+    o1 = torch.full((wl.B, wl.Hq, wl.dh), float("nan"), device="cuda:0")
+    o2 = torch.full_like(o1, float("nan"))
+    ns_ref = ns.clone()
+    ns_ref[1] = -1  # the two-call path without sequence 1's write
+    K.kvq_cache_write(kn, vn, ns_ref, kc, vc, ks, vs, fmt, gran)
+    K.kvq_decode_attn(o1, q, kc, vc, bt, cl_d, mc, ks, vs, fmt, gran)
+    K.kvq_decode_attn_append(o2, q, kn, vn, kc2, vc2, bt, cl_d, mc, ks, vs, fmt, gran)
+    torch.cuda.synchronize()
+    ka, va = to_np(kc2), to_np(vc2)
+    assert np.array_equal(ka, to_np(kc)) and np.array_equal(va, to_np(vc))
+    assert np.array_equal(to_np(o1), to_np(o2))
+    # sequence 1: position 98 (= max_context_len - 1) keeps its token's codes,
+    # position 99 (its new token's true slot) keeps the fill
+    blk = wl.paging.block_tables[1]
+    for pos in (98, 99):
+        b, off = blk[pos // 16], pos % 16
+        assert np.array_equal(ka[b, :, :, off, :], kb[b, :, :, off, :])
+        assert np.array_equal(va[b, :, :, off], vb[b, :, :, off])
+    b, off = blk[99 // 16], 99 % 16
+    assert np.all(ka[b, :, :, off, :] == 0xFF) and np.all(va[b, :, :, off] == 0xFF)

@@ -34,7 +34,7 @@ def test_append_decode_replays_match_eager():
     mc = int(max(cl))
     ws = torch.empty(K.kvq_decode_workspace_size(wl.B, wl.Hq, 128, mc, 16), dtype=torch.uint8,
                      device="cuda:0")
-    out = torch.empty((wl.B, wl.Hq, 128), device="cuda:0")
+    out = torch.full((wl.B, wl.Hq, 128), float("nan"), device="cuda:0")
 
     def step():
         K.kvq_decode_attn_append(out, q, kn, vn, kc, vc, bt, ctx, mc, ks, vs, "e4m3", "tensor",

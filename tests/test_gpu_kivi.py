@@ -71,7 +71,7 @@ def run_decode(wl, out_dtype="f32", max_groups=None, fill=FILL):
     cache = gpu_cache(wl, fill)
     mg = int(wl.quant_groups.max()) if max_groups is None else max_groups
     odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
-    out = torch.empty((wl.B, wl.Hq, 128), dtype=odt, device="cuda:0")
+    out = torch.full((wl.B, wl.Hq, 128), float("nan"), dtype=odt, device="cuda:0")
     K.kvq_kivi_decode_attn(out, to_dev(wl.q), cache, to_dev(wl.paging.block_tables),
                            to_dev(wl.quant_groups), mg, to_dev(wl.res_k), to_dev(wl.res_v),
                            to_dev(wl.res_lens))
@@ -126,13 +126,11 @@ def test_empty_sequence_gives_zero_row():
     check(out[1:], oracle_decode(wl)[8:].reshape(out[1:].shape))
 
 
-def test_full_size_sampled_rows():
+def test_full_size_every_row():
     """B=8, Hq=32, Hkv=8, 16384 tokens per sequence (508 groups + 128
-    residual): 48 sampled (sequence, head) rows against the oracle."""
+    residual): every (sequence, head) row is written (the output starts as
+    NaN) and all 256 rows match the oracle."""
     wl = W.kivi_2bit_decode()
     out = run_decode(wl).reshape(-1, 128)
-    g = W.rng(850)
-    idx = g.choice(wl.B * wl.Hq, 48, replace=False)
-    rows = np.array([(i // wl.Hq, i % wl.Hq) for i in idx], np.int32)
-    ref = oracle_decode(wl, rows)
-    check(out[idx], ref)
+    assert np.all(np.isfinite(out))
+    check(out, oracle_decode(wl).reshape(out.shape))

@@ -6,15 +6,16 @@ by page).
 A pool holds, per block, one page of each of three layers: FP8 (E4M3), a
 skipped bf16 layer, FP8 (E5M2); pages are the bf16 layer's size.  Bar: the FP8
 layers' codes bit-exact against the oracle's dense caches, the skipped layer's
-bytes and every padding byte untouched, and decode / prefill outputs identical
-to the same calls on dense caches.
+bytes and every padding byte untouched; decode / prefill outputs on the
+padded layout identical to the same calls on dense caches and within 2e-3 of
+the oracle's attention over its own dense caches.
 """
 import numpy as np
 import pytest
 
 import oracle
 import workloads as W
-from helpers import FMT_ID, same_codes, to_dev, to_np
+from helpers import ATTN_TOL, FMT_ID, rel_err, row_rel_err, same_codes, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -81,7 +82,7 @@ def test_write_into_padded_pages(T_kind):
     assert np.all(p[:, 0, 2 * nat:] == FILL) and np.all(p[:, 2, 2 * nat:] == FILL)  # padding
 
 
-def test_decode_and_prefill_on_padded_pages_match_dense_caches():
+def test_decode_and_prefill_on_padded_pages_match_dense_caches_and_the_oracle():
     import torch
     import quantized_kv_cache_fp8_amd as K
     # prefill workload: 3 sequences, cached prefix + chunk; its caches serve decode too
@@ -89,17 +90,32 @@ def test_decode_and_prefill_on_padded_pages_match_dense_caches():
     pool, page, _ = make_pool(pw)
     kc, vc, ks, vs = write_layer(pw, pool, 2, page, "e4m3")
     dk, dv = kc.contiguous(), vc.contiguous()  # the same bytes, unpadded
+    # the oracle's own scales and dense caches of the same layer
+    fmt, gh = oracle.FMT_E4M3, oracle.GRAN_HEAD
+    rks = oracle.calibrate(pw.kv.k, fmt, gh)[1]
+    rvs = oracle.calibrate(pw.kv.v, fmt, gh)[1]
+    assert np.array_equal(to_np(ks), rks) and np.array_equal(to_np(vs), rvs)
+    nb = pw.paging.num_blocks
+    rk = np.full(oracle.k_cache_shape(nb, pw.Hkv, 16, pw.dh), FILL, np.uint8)
+    rv = np.full(oracle.v_cache_shape(nb, pw.Hkv, 16, pw.dh), FILL, np.uint8)
+    oracle.cache_write(pw.kv.k, pw.kv.v, pw.kv.slot_mapping, rk, rv, rks, rvs, fmt, gh)
     bt, cl = to_dev(pw.paging.block_tables), to_dev(pw.paging.context_lens)
     g = W.rng(921)
-    q = to_dev(W.normal_bf16(g, (len(pw.prefix_lens), pw.Hq, pw.dh)))
+    q_np = W.normal_bf16(g, (len(pw.prefix_lens), pw.Hq, pw.dh))
+    q = to_dev(q_np)
     mc = int(pw.paging.context_lens.max())
     outs = []
     for kk, vv, fn in ((kc, vc, K.kvq_decode_attn_paged), (dk, dv, K.kvq_decode_attn)):
-        out = torch.empty(q.shape, dtype=torch.float32, device="cuda:0")
+        out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda:0")
         fn(out, q, kk, vv, bt, cl, mc, ks, vs, "e4m3", "head")
         torch.cuda.synchronize()
         outs.append(to_np(out))
     assert np.array_equal(outs[0], outs[1])
+    ref = oracle.decode_attn(q_np, rk, rv, pw.paging.block_tables, pw.paging.context_lens, rks,
+                             rvs, fmt, gh)
+    e, er = rel_err(outs[0], ref), row_rel_err(outs[0], ref)
+    print(f"padded decode: global rel err {e:.3e}  worst row {er:.3e}", flush=True)
+    assert e <= ATTN_TOL and er <= ATTN_TOL
     qp = to_dev(pw.q)
     qs = torch.empty(pw.Hq, device="cuda:0")
     am = torch.empty(pw.Hq, device="cuda:0")
@@ -108,8 +124,16 @@ def test_decode_and_prefill_on_padded_pages_match_dense_caches():
     mq = int(np.diff(pw.cu_seqlens).max())
     outs = []
     for kk, vv, fn in ((kc, vc, K.kvq_prefill_attn_paged), (dk, dv, K.kvq_prefill_attn)):
-        out = torch.empty(qp.shape, dtype=torch.float32, device="cuda:0")
+        out = torch.full(qp.shape, float("nan"), dtype=torch.float32, device="cuda:0")
         fn(out, qp, cu, mq, qs, "head", kk, vv, bt, cl, ks, vs, "e4m3", "head")
         torch.cuda.synchronize()
         outs.append(to_np(out))
     assert np.array_equal(outs[0], outs[1])
+    rqs = oracle.calibrate(pw.q, fmt, gh)[1]
+    assert np.array_equal(to_np(qs), rqs)
+    ref = oracle.prefill_attn(pw.q, pw.cu_seqlens, rqs, gh, rk, rv, pw.paging.block_tables,
+                              pw.paging.context_lens, rks, rvs, fmt, gh)
+    e = rel_err(outs[0], ref)
+    print(f"padded prefill: global rel err {e:.3e}  worst row {row_rel_err(outs[0], ref):.3e}",
+          flush=True)
+    assert e <= ATTN_TOL

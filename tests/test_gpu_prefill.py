@@ -51,7 +51,9 @@ class PrefillRun:
         self.cl = to_dev(wl.paging.context_lens)
         self.cu = to_dev(wl.cu_seqlens)
         odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
-        self.out = torch.empty((wl.q.shape[0], wl.Hq, wl.dh), dtype=odt, device=dev)
+        # NaN until written: a tile the kernel never writes cannot pass as finite
+        self.out = torch.full((wl.q.shape[0], wl.Hq, wl.dh), float("nan"), dtype=odt,
+                              device=dev)
         self.max_q = int(np.diff(wl.cu_seqlens).max())
 
     def gpu(self, softmax_scale=0.0):
@@ -151,43 +153,51 @@ def test_reduced_chunked_prefill():
     check(run.gpu(), run.oracle_full())
 
 
-def test_full_size_sampled_rows():
-    """8 x (4096 cached + 4096 new) tokens, Hq=32, Hkv=8, dh=128; a seeded
-    sample of (row, head) pairs including every sequence's first and last row."""
-    wl = W.fp8_chunked_prefill()
-    run = PrefillRun(wl)
-    out = run.gpu()
-    kc, vc = run.oracle_caches()
-    g = W.rng(66)
+def workgroup_sample(wl, seed, GT=4, QT=32):
+    """One (row, head) pair per workgroup of the prefill grid -- every (sequence,
+    32-row query tile, group of GT heads) -- at a seeded row of the tile and a
+    seeded head of the group, plus every sequence's first and last row.  The
+    kernel's XCD renumbering maps each of these workgroups somewhere, so the
+    sample meets every stretch of it."""
+    g = W.rng(seed)
     cu = wl.cu_seqlens
-    rows = [(int(cu[b]), 0) for b in range(8)] + [(int(cu[b + 1]) - 1, 31) for b in range(8)]
-    rows += [(int(g.integers(cu[-1])), int(g.integers(32))) for _ in range(48)]
-    rows = np.array(rows, np.int64)
-    ref = oracle.prefill_rows(rows, wl.q, wl.cu_seqlens, run.qs_ref, run.qg, kc, vc,
-                              wl.paging.block_tables, wl.paging.context_lens, run.ks_ref,
-                              run.vs_ref, run.fmt, run.kg)
-    got = out[rows[:, 0], rows[:, 1]]
-    check(got, ref)
-    assert np.all(np.isfinite(out))
+    rows = []
+    for b in range(len(cu) - 1):
+        qlen = int(cu[b + 1] - cu[b])
+        if qlen == 0:
+            continue
+        rows += [(int(cu[b]), 0), (int(cu[b + 1]) - 1, wl.Hq - 1)]
+        for qt in range((qlen + QT - 1) // QT):
+            r = int(cu[b]) + qt * QT + int(g.integers(min(QT, qlen - qt * QT)))
+            for grp in range(wl.Hq // GT):
+                rows.append((r, grp * GT + int(g.integers(GT))))
+    return np.array(rows, np.int64)
 
 
-def test_ragged_full_size_sampled_rows():
-    """The ragged batch of the bench (chunk = prefix, 256 to 4096 tokens, full
-    head shape): every sequence's first and last row and a seeded sample."""
-    wl = W.ragged_chunked_prefill()
+def full_size_check(wl, seed):
     run = PrefillRun(wl)
     out = run.gpu()
+    assert np.all(np.isfinite(out)), "some output rows were never written"
     kc, vc = run.oracle_caches()
-    g = W.rng(67)
-    cu = wl.cu_seqlens
-    rows = [(int(cu[b]), 3) for b in range(8)] + [(int(cu[b + 1]) - 1, 28) for b in range(8)]
-    rows += [(int(g.integers(cu[-1])), int(g.integers(32))) for _ in range(32)]
-    rows = np.array(rows, np.int64)
+    rows = workgroup_sample(wl, seed)
+    print(f"{len(rows)} sampled (row, head) pairs", flush=True)
     ref = oracle.prefill_rows(rows, wl.q, wl.cu_seqlens, run.qs_ref, run.qg, kc, vc,
                               wl.paging.block_tables, wl.paging.context_lens, run.ks_ref,
                               run.vs_ref, run.fmt, run.kg)
     check(out[rows[:, 0], rows[:, 1]], ref)
-    assert np.all(np.isfinite(out))
+
+
+def test_full_size_sampled_rows():
+    """8 x (4096 cached + 4096 new) tokens, Hq=32, Hkv=8, dh=128: every output
+    row is written (the output starts as NaN), and one (row, head) pair per
+    workgroup of the grid -- 8192 pairs -- matches the oracle."""
+    full_size_check(W.fp8_chunked_prefill(), 66)
+
+
+def test_ragged_full_size_sampled_rows():
+    """The ragged batch of the bench (chunk = prefix, 256 to 4096 tokens, full
+    head shape): every row written, one sampled pair per workgroup."""
+    full_size_check(W.ragged_chunked_prefill(), 67)
 
 
 def test_explicit_softmax_scale():

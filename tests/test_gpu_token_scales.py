@@ -95,7 +95,7 @@ def decode_case(seed, fmt, Hq, Hkv, dh, cl, lo=1e-3, hi=1e3, fill=SENTINEL, sfil
     max_ctx = int(max(cl))
     outs = []
     for odt in ([torch.float32, torch.bfloat16] if also_bf16 else [torch.float32]):
-        out = torch.empty((len(cl), Hq, dh), dtype=odt, device="cuda:0")
+        out = torch.full((len(cl), Hq, dh), float("nan"), dtype=odt, device="cuda:0")
         K.kvq_decode_attn_token_scales(out, to_dev(q), gk, gv, gks, gvs,
                                        to_dev(paging.block_tables),
                                        to_dev(paging.context_lens), max_ctx, FMT_ID[fmt])

@@ -10,10 +10,13 @@ pytestmark = pytest.mark.gpu
 FMTS = [oracle.FMT_E4M3, oracle.FMT_E5M2, oracle.FMT_INT8]
 ALL_BF16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
 
-# scales in the supported range [2^-126, 2^126): powers of two, amax/fmax-like values,
-# the extremes (quotients overflow / underflow) and a seeded log-uniform spread
+# scales in the supported range (positive, below 2^126): powers of two, amax/fmax-like
+# values, the extremes (quotients overflow / underflow), scales below 2^-100 whose
+# reciprocal leaves the fp32 range (subnormal ones down to 2^-149 included: an E5M2
+# calibration of a tensor with amax below 2^-110 gives one) and a seeded
+# log-uniform spread
 SCALES = ([1.0, 0.5, 2.0 ** -9, 1.0 / 448, 10.0 / 448, 3.0, 0.0123, 123.456, 1e-30, 3.3e20,
-           1.1754944e-38, 6.0e37]
+           1.1754944e-38, 6.0e37, 2.0 ** -101, 3.1e-33, 2.0 ** -130, 1.0e-40, 2.0 ** -149]
           + list(np.exp(W.rng(77).uniform(np.log(1e-6), np.log(1e6), 48)).astype(np.float32)))
 
 
@@ -175,6 +178,32 @@ def test_calibrate_degenerate_sets():
     assert np.isinf(ga[0]) and gs[0] == 1.0
     ga, gs = gpu_calibrate(np.zeros((0, 3, 64), np.uint16), 1, oracle.GRAN_HEAD)
     assert np.all(ga == 0) and np.all(gs == 1.0)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_tiny_amax_gives_a_usable_subnormal_scale(fmt):
+    """A tensor whose amax is tiny (bf16 values near 2^-120, zeros among
+    them) calibrates to a scale below 2^-126 for E5M2 (amax / 57344) and near
+    it for the other formats; the scale and every code written with it, zeros
+    included, equal the oracle's (zeros stay code 0, not NaN)."""
+    g = W.rng(31 + fmt)
+    Hkv, dh = 2, 128
+    mant = g.integers(0, 128, (64, Hkv, dh)).astype(np.uint16)
+    expo = g.integers(1, 12, (64, Hkv, dh)).astype(np.uint16)  # 2^-126 .. 2^-116
+    k = (expo << 7) | mant | (g.integers(0, 2, (64, Hkv, dh)).astype(np.uint16) << 15)
+    k[:, :, :9] = 0  # zeros among them
+    k[3, 1, 20:30] = g.integers(1, 128, 10)  # bf16 subnormals
+    ga, gs = gpu_calibrate(k, fmt, oracle.GRAN_TENSOR)
+    ra, rs = oracle.calibrate(k, fmt, oracle.GRAN_TENSOR)
+    assert same_f32(ga, ra) and same_f32(gs, rs)
+    if fmt == oracle.FMT_E5M2:
+        assert 0 < rs[0] < 2.0 ** -126
+    slots = np.arange(64, dtype=np.int64)
+    for path in ("short", "long"):
+        gk, gv = gpu_write(k, k, slots, 4, Hkv, dh, rs, rs, fmt, oracle.GRAN_TENSOR, path)
+        rk, rv = oracle_write(k, k, slots, 4, Hkv, dh, rs, rs, fmt, oracle.GRAN_TENSOR)
+        assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
+        assert np.all(gk.reshape(4, Hkv, dh // 16, 16, 16)[0, :, 0, :, :9] == 0)
 
 
 # ------------------------------------------------------------------ full-size workloads

@@ -65,6 +65,76 @@ def test_scale_and_zero_are_numpy_fp16_roundings():
         assert z16 == f16_bits(np.clip(x.min(), -65504.0, 65504.0))
 
 
+def _numpy_kivi_codec(x: np.ndarray):
+    """The 2-bit codec of every row of x (float32 [n, 32]) in numpy's own fp32
+    and fp16 arithmetic: s = fl16(min(fl32(fl32(max - min) / 3), 65504)),
+    z = fl16(clamp(min, +-65504)), code = clip(rint(fl32(fl32(x - z) / s)), 0, 3)
+    (0 where s is 0); rows holding an Inf or NaN store s = z = 0 and codes 0."""
+    x = x.astype(np.float32)
+    bad = ~np.all(np.isfinite(x), axis=1)
+    xs = np.where(bad[:, None], np.float32(0), x)
+    mn, mx = xs.min(axis=1), xs.max(axis=1)
+    with np.errstate(over="ignore"):
+        s32 = (mx - mn) / np.float32(3.0)          # fp32 subtract, then fp32 divide
+    s16 = np.minimum(s32, np.float32(65504.0)).astype(np.float16)
+    z16 = np.clip(mn, np.float32(-65504.0), np.float32(65504.0)).astype(np.float16)
+    s16[bad], z16[bad] = 0, 0
+    sf, zf = s16.astype(np.float32), z16.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        q = (xs - zf[:, None]) / sf[:, None]      # fp32 subtract, then fp32 divide
+    codes = np.clip(np.rint(np.nan_to_num(q, nan=0.0, posinf=3.0, neginf=0.0)), 0, 3)
+    codes[(sf == 0) | bad] = 0
+    return s16.view(np.uint16), z16.view(np.uint16), codes.astype(np.uint8)
+
+
+def test_codec_matches_a_numpy_fp32_recompute():
+    """100,000 seeded sets of 32 bf16 values: normal sets over 24 decades of
+    magnitude, sets with outliers, sets whose values sit on the midpoints of
+    their own code grid (ties), near-constant sets, sets whose range or minimum
+    leaves the fp16 range, and sets holding an Inf or NaN.  The oracle's
+    (s, z, codes) equal a recompute in numpy's fp32 / fp16 arithmetic, which
+    shares nothing with the oracle's fp64-then-round code."""
+    g = W.rng(730)
+    n = 100_000
+    mag = np.exp(g.uniform(np.log(1e-12), np.log(1e12), n)).astype(np.float32)
+    x = (g.standard_normal((n, 32)) * mag[:, None]).astype(np.float32)
+    kind = g.integers(0, 8, n)
+    # outliers: one value 50x the rest
+    o = kind == 1
+    x[o, 0] *= 50
+    # ties: z + (k + 1/2) s for dyadic z, s, with both ends of the grid present
+    t = np.nonzero(kind == 2)[0]
+    e = g.integers(-10, 8, t.size)
+    sg = (g.choice([1, 3, 5], t.size) * 2.0 ** e).astype(np.float64)
+    zg = (g.integers(-40, 40, t.size) * 2.0 ** e).astype(np.float64)
+    kk = g.integers(0, 3, (t.size, 32)) + 0.5
+    kk[:, 0], kk[:, 1] = -0.5, 3.5  # extend the range so s stays sg and z stays zg - s/2
+    x[t] = (zg[:, None] + kk * sg[:, None]).astype(np.float32)
+    # near-constant sets
+    c = kind == 3
+    x[c] = (x[c, :1] * (1 + 1e-3 * g.standard_normal((c.sum(), 32)))).astype(np.float32)
+    # range or minimum beyond fp16
+    w = kind == 4
+    x[w] = (g.standard_normal((w.sum(), 32)) * 1e5).astype(np.float32)
+    m = kind == 5
+    x[m] = (-1e5 + g.standard_normal((m.sum(), 32))).astype(np.float32)
+    # non-finite members
+    f = np.nonzero(kind == 6)[0]
+    x[f, g.integers(0, 32, f.size)] = g.choice([np.inf, -np.inf, np.nan], f.size)
+    x = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x)).reshape(n, 32)
+    ws, wz, wc = _numpy_kivi_codec(x)
+    s16 = np.empty(n, np.uint16)
+    z16 = np.empty(n, np.uint16)
+    codes = np.empty((n, 32), np.uint8)
+    for i in range(n):
+        s16[i], z16[i], codes[i] = oracle.kivi_group(x[i])
+    assert np.array_equal(s16, ws)
+    assert np.array_equal(z16, wz)
+    assert np.array_equal(codes, wc)
+    # the tie sets really do hit midpoints, so round-half-even decides codes
+    assert np.any((wc[t] == 2) & (kk == 1.5))
+
+
 @pytest.mark.parametrize("scale", [1e-3, 1.0, 30.0, 3000.0])
 def test_rounding_error_bound_and_monotone_codes(scale):
     """Every code is in 0..3, codes do not decrease with x, and
