@@ -62,7 +62,8 @@ typedef enum {
   KVQ_ERR_UNSUPPORTED = -3, /* a valid but unimplemented value (dh, bs, group size, enum) */
   KVQ_ERR_WORKSPACE = -4,   /* the decode workspace is smaller than kvq_decode_workspace_size */
   KVQ_ERR_LAUNCH = -5,      /* the HIP runtime refused a launch (hipGetLastError) */
-  KVQ_ERR_DEVICE = -6       /* no usable HIP device, or it is not gfx950 */
+  KVQ_ERR_DEVICE = -6,      /* no usable HIP device, or it is not gfx950 */
+  KVQ_ERR_SCRATCH = -7      /* beyond the static scratch of kvq_decode_attn_append_noalloc */
 } kvq_status;
 
 /* Storage format of the cache codes ([G] kv_cache_dtype table: fp8 == fp8_e4m3,
@@ -358,6 +359,38 @@ kvq_status kvq_decode_attn_append(void* out, kvq_out out_dtype, const void* q_bf
                                   const float* v_scale, kvq_fmt fmt, kvq_gran gran,
                                   float softmax_scale, void* workspace, size_t ws_bytes,
                                   kvq_stream stream);
+
+/* Bytes of the device scratch array kvq_decode_attn_append_noalloc keeps its
+ * split partials in (16 MiB; one array per GPU). */
+#define KVQ_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* kvq_decode_attn_append for callers that cannot allocate device memory --
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation: the same kernels and the same results, bit for bit, but the
+ * split partials live in a file-scope device array of
+ * KVQ_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends, so no workspace is passed and nothing is allocated
+ * (no hipMalloc, no hipFree, no allocating library call).  The caller still
+ * passes every input and output.  The array's address on a device is looked
+ * up on the first call made with that device current.
+ * Limit: calls whose kvq_decode_workspace_size(B, Hq, dh, max_context_len, bs)
+ * exceeds KVQ_STATIC_SCRATCH_BYTES return KVQ_ERR_SCRATCH before any device
+ * work (B = 32, Hq = 32, dh = 128, bs = 16 fits up to max_context_len = 15872).
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents (no call reads what another left there): calls that overlap in
+ * time on one GPU -- on different streams, or from different threads -- race
+ * and must be ordered by the caller.
+ * Errors: as kvq_decode_attn_append without KVQ_ERR_WORKSPACE, plus
+ * KVQ_ERR_SCRATCH; KVQ_ERR_DEVICE if the array's address cannot be found. */
+kvq_status kvq_decode_attn_append_noalloc(void* out, kvq_out out_dtype, const void* q_bf16,
+                                          const void* k_new_bf16, const void* v_new_bf16,
+                                          uint8_t* k_cache, uint8_t* v_cache, int64_t num_blocks,
+                                          const int32_t* block_tables, int max_blocks,
+                                          const int32_t* context_lens, int B, int Hq, int Hkv,
+                                          int dh, int bs, int max_context_len,
+                                          const float* k_scale, const float* v_scale,
+                                          kvq_fmt fmt, kvq_gran gran, float softmax_scale,
+                                          kvq_stream stream);
 
 /* ---------------------------------------------------------------- prefill
  * Causal chunked prefill in the FP8 domain ([G] the FlashAttention-3 note:

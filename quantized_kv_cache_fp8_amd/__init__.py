@@ -33,7 +33,10 @@ EXPORTS = ["kvq_strerror", "kvq_kv_cache_bytes", "kvq_fp8_encode", "kvq_fp8_deco
            "kvq_decode_attn_token_scales", "kvq_kivi_quantize", "kvq_kivi_decode_workspace_size",
            "kvq_kivi_decode_attn", "kvq_cache_write_paged", "kvq_decode_attn_paged",
            "kvq_prefill_attn_paged", "kvq_layer_skipped", "kvq_layer_index", "kvq_page_bytes",
-           "kvq_common_page_bytes", "kvq_decode_attn_append"]
+           "kvq_common_page_bytes", "kvq_decode_attn_append", "kvq_decode_attn_append_noalloc"]
+
+# bytes of the device scratch array of kvq_decode_attn_append_noalloc (KVQ_STATIC_SCRATCH_BYTES)
+STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class KvqError(RuntimeError):
@@ -90,6 +93,9 @@ def lib() -> ctypes.CDLL:
         L.kvq_common_page_bytes.restype = ctypes.c_uint64
         L.kvq_decode_attn_append.argtypes = [P, i32, P, P, P, P, P, i64, P, i32, P, i32, i32,
                                              i32, i32, i32, i32, P, P, i32, i32, f32, P, sz, P]
+        L.kvq_decode_attn_append_noalloc.argtypes = [P, i32, P, P, P, P, P, i64, P, i32, P, i32,
+                                                     i32, i32, i32, i32, i32, P, P, i32, i32, f32,
+                                                     P]
         L.kvq_prefill_attn.argtypes = [P, i32, P, P, i32, P, i32, P, P, i64, P, i32, P, i32, i32,
                                        i32, i32, i32, P, P, i32, i32, f32, P]
         _lib = L
@@ -562,3 +568,28 @@ def kvq_decode_attn_append(out, q, k_new, v_new, k_cache, v_cache, block_tables,
                                         float(softmax_scale), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(),
                                         _stream(stream)))
+
+
+def kvq_decode_attn_append_noalloc(out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                                   context_lens, max_context_len, k_scale, v_scale, fmt, gran,
+                                   softmax_scale=0.0, stream=None) -> None:
+    """kvq_decode_attn_append with its split partials in the library's static
+    device scratch: no workspace argument, nothing allocated (for code under
+    graph capture or loops that may not allocate).  Calls that overlap on one
+    GPU share that scratch and must be ordered by the caller."""
+    import torch
+    nb, Hkv, bs, dh = _cache_dims(k_cache, v_cache)
+    _attn_shapes(out, q, Hkv, dh, block_tables, context_lens, q.shape[0])
+    B, Hq, _ = q.shape
+    _shape("k_new", k_new, (B, Hkv, dh))
+    _shape("v_new", v_new, (B, Hkv, dh))
+    _scales("k_scale", k_scale, gran, Hkv)
+    _scales("v_scale", v_scale, gran, Hkv)
+    out_dt = KVQ_OUT_BF16 if out.dtype == torch.bfloat16 else KVQ_OUT_F32
+    _check("kvq_decode_attn_append_noalloc",
+           lib().kvq_decode_attn_append_noalloc(
+               _ptr(out, "out"), out_dt, _ptr(q, "bf16"), _ptr(k_new, "bf16"),
+               _ptr(v_new, "bf16"), _ptr(k_cache, "u8"), _ptr(v_cache, "u8"), nb,
+               _ptr(block_tables, "i32"), block_tables.shape[1], _ptr(context_lens, "i32"), B, Hq,
+               Hkv, dh, bs, int(max_context_len), _ptr(k_scale, "f32"), _ptr(v_scale, "f32"),
+               _fmt(fmt), _gran(gran), float(softmax_scale), _stream(stream)))

@@ -65,6 +65,8 @@ const char* kvq_strerror(kvq_status st) {
     case KVQ_ERR_WORKSPACE: return "decode workspace too small";
     case KVQ_ERR_LAUNCH: return "HIP kernel launch failed";
     case KVQ_ERR_DEVICE: return "no usable gfx950 HIP device";
+    case KVQ_ERR_SCRATCH: return "the call needs more split-partial bytes than the library's "
+                                 "static scratch array holds (KVQ_STATIC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -215,6 +217,55 @@ kvq_status kvq_decode_attn_paged(void* out, kvq_out out_dtype, const void* q_bf1
                                (hipStream_t)stream, nullptr, nullptr, block_stride));
 }
 
+// Validation of the append calls up to the workspace (sizes, pointers, the
+// split plan's bounds); fills plan.
+static kvq_status check_append(const void* out, int out_dtype, const void* q, const void* k_new,
+                               const void* v_new, const uint8_t* kc, const uint8_t* vc,
+                               int64_t num_blocks, const int32_t* bt, int max_blocks,
+                               const int32_t* ctx, int B, int Hq, int Hkv, int dh, int bs,
+                               int max_context_len, const float* ks, const float* vs, int fmt,
+                               int gran, DecodePlan* plan) {
+  kvq_status st = check_attn_common(out, out_dtype, q, kc, vc, num_blocks, bt, max_blocks, ctx,
+                                    B, Hq, Hkv, dh, bs, ks, vs, fmt, gran);
+  if (st != KVQ_OK) return st;
+  if (!k_new || !v_new) return KVQ_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return KVQ_ERR_UNSUPPORTED;
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks * bs)
+    return KVQ_ERR_SHAPE;
+  *plan = decode_plan(B, Hq, dh, max_context_len, bs);
+  if (plan->nsplit > 65535) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+static_assert(KVQ_STATIC_SCRATCH_BYTES == kStaticScratchBytes,
+              "the header's scratch size must be the array's");
+
+kvq_status kvq_decode_attn_append_noalloc(void* out, kvq_out out_dtype, const void* q_bf16,
+                                          const void* k_new_bf16, const void* v_new_bf16,
+                                          uint8_t* k_cache, uint8_t* v_cache, int64_t num_blocks,
+                                          const int32_t* block_tables, int max_blocks,
+                                          const int32_t* context_lens, int B, int Hq, int Hkv,
+                                          int dh, int bs, int max_context_len,
+                                          const float* k_scale, const float* v_scale,
+                                          kvq_fmt fmt, kvq_gran gran, float softmax_scale,
+                                          kvq_stream stream) {
+  DecodePlan plan;
+  kvq_status st = check_append(out, out_dtype, q_bf16, k_new_bf16, v_new_bf16, k_cache, v_cache,
+                               num_blocks, block_tables, max_blocks, context_lens, B, Hq, Hkv,
+                               dh, bs, max_context_len, k_scale, v_scale, fmt, gran, &plan);
+  if (st != KVQ_OK) return st;
+  if (plan.ws_bytes > kStaticScratchBytes) return KVQ_ERR_SCRATCH;
+  void* ws = decode_static_scratch();  // the array's address on this device
+  if (!ws) return KVQ_ERR_DEVICE;
+  return map_err(launch_decode(out, out_dtype == KVQ_OUT_BF16, (const uint16_t*)q_bf16, k_cache,
+                               v_cache, num_blocks, block_tables, max_blocks, context_lens, B, Hq,
+                               Hkv, dh, max_context_len, k_scale, v_scale, fmt,
+                               gran == KVQ_SCALE_HEAD, softmax_scale, plan, ws,
+                               (hipStream_t)stream, nullptr, nullptr, 0,
+                               (const uint16_t*)k_new_bf16, (const uint16_t*)v_new_bf16, k_cache,
+                               v_cache));
+}
+
 kvq_status kvq_decode_attn_append(void* out, kvq_out out_dtype, const void* q_bf16,
                                   const void* k_new_bf16, const void* v_new_bf16,
                                   uint8_t* k_cache, uint8_t* v_cache, int64_t num_blocks,
@@ -224,13 +275,11 @@ kvq_status kvq_decode_attn_append(void* out, kvq_out out_dtype, const void* q_bf
                                   const float* v_scale, kvq_fmt fmt, kvq_gran gran,
                                   float softmax_scale, void* workspace, size_t ws_bytes,
                                   kvq_stream stream) {
-  kvq_status st = check_attn_common(out, out_dtype, q_bf16, k_cache, v_cache, num_blocks,
-                                    block_tables, max_blocks, context_lens, B, Hq, Hkv, dh, bs,
-                                    k_scale, v_scale, fmt, gran);
+  DecodePlan plan;
+  kvq_status st = check_append(out, out_dtype, q_bf16, k_new_bf16, v_new_bf16, k_cache, v_cache,
+                               num_blocks, block_tables, max_blocks, context_lens, B, Hq, Hkv,
+                               dh, bs, max_context_len, k_scale, v_scale, fmt, gran, &plan);
   if (st != KVQ_OK) return st;
-  if (!k_new_bf16 || !v_new_bf16) return KVQ_ERR_NULL;
-  if (!aligned(k_new_bf16, 16) || !aligned(v_new_bf16, 16)) return KVQ_ERR_UNSUPPORTED;
-  const DecodePlan plan = decode_plan(B, Hq, dh, max_context_len, bs);
   st = check_decode_ws(plan, max_context_len, max_blocks, bs, workspace, ws_bytes);
   if (st != KVQ_OK) return st;
   return map_err(launch_decode(out, out_dtype == KVQ_OUT_BF16, (const uint16_t*)q_bf16, k_cache,

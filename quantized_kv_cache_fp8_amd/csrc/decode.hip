@@ -35,6 +35,8 @@
 // internal accumulation keeps only about 16 bits relative to the largest
 // product, which at decode-sized logits (tens in log2 units) is visible in
 // the output, whereas bf16 products accumulate in full fp32.
+#include <mutex>
+
 #include "attn_common.hpp"
 #include "launch.hpp"
 
@@ -799,6 +801,32 @@ __global__ __launch_bounds__(DH * HPW) void decode_combine_kernel(
     reinterpret_cast<uint16_t*>(out)[oi] = (uint16_t)f32_to_bf16_rne(r);
   else
     reinterpret_cast<float*>(out)[oi] = r;
+}
+
+// ---------------------------------------------------------------- static scratch
+// Split partials of kvq_decode_attn_append_noalloc, for callers that cannot
+// allocate: a file-scope device array (each GPU the library runs on holds its
+// own copy until the process ends).  Host code never passes the array's name
+// to a kernel -- on the host it only stands in for the device symbol -- but
+// the address hipGetSymbolAddress returns for the current device.  Its
+// contents need no initialisation: every partial the combine reads is written
+// by the split kernel of the same call.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+void* g_scratch_ptr[kMaxScratchDevices];
+std::once_flag g_scratch_once[kMaxScratchDevices];
+}  // namespace
+
+void* decode_static_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_ptr[dev] = ptr;
+  });
+  return g_scratch_ptr[dev];
 }
 
 static int heads_per_group(int G) {

@@ -51,6 +51,13 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
                          const uint16_t* v_new = nullptr, uint8_t* kc_w = nullptr,
                          uint8_t* vc_w = nullptr);
 
+// Bytes of the device-resident scratch array the allocation-free decode
+// entry point keeps its split partials in (one array per GPU).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+// That array's device address on the current device, looked up once per
+// device (null if the lookup fails).
+void* decode_static_scratch();
+
 // Log-sum-exp merge of split partials ([B][Hq][nsplit] (m, l) pairs and dh
 // partial sums) into out, times vs (null: 1).  part_blocks > 0: sequence b's
 // first ceil(ctx / (16 part_blocks)) splits are merged; 0: all nsplit are.

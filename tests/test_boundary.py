@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_covers_every_status():
-    for st in range(-6, 1):
+    for st in range(-7, 1):
         assert K.kvq_strerror(st) and K.kvq_strerror(st) != "unknown status"
     assert K.kvq_strerror(-99) == "unknown status"
 
