@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--copies", type=int, default=4, help="cache copies rotated per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-cpu-rows", action="store_true",
+                   help="time only the headline decode sample on the CPU")
     p.add_argument("--no-rows", action="store_true", help="skip the extra per-row measurements")
     p.add_argument("--no-ragged", action="store_true",
                    help="skip the ragged prefill row (so a profile's prefill dispatches are "
@@ -244,7 +246,8 @@ def main():
 
     # ------------------------------------------------------------ CPU oracle baseline
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, args.cpu_seconds,
+                                              W=None if args.no_cpu_rows else W)
 
     print(json.dumps(result), flush=True)
 
@@ -378,9 +381,94 @@ def kivi_rows(K, W, torch, dev, stream, reps=50):
     return rows
 
 
+def long_context_rows(K, W, torch, dev, stream, steps=200, copies=4):
+    """Long-context decode with per-head scales: B=4, S=32768, Hq=32, Hkv=8,
+    dh=128, k/v scales [8] from per-head amax; the append step (new token's
+    quantize-write + attention) as for the headline layer, once with an E4M3
+    and once with an E5M2 cache.  Bytes per step: the FP8 K+V history,
+    4 x 32768 x 8 x 128 x 2 = 268,435,456."""
+    import dataclasses
+    base = W.long_context_decode("e4m3")
+
+    def dt(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    k_all, v_all, slots = dt(base.kv.k), dt(base.kv.v), dt(base.kv.slot_mapping)
+    q, bt, ctx = dt(base.q), dt(base.paging.block_tables), dt(base.paging.context_lens)
+    B, Hq, Hkv, dh, bs = base.B, base.Hq, base.Hkv, base.dh, base.bs
+    max_ctx = int(base.paging.context_lens.max())
+    last = torch.from_numpy(base.kv.seq_offsets[1:] - 1).to(dev)
+    k_new, v_new = k_all[last].contiguous(), v_all[last].contiguous()
+    nb = base.paging.num_blocks
+    kcs = [torch.empty((nb, Hkv, dh // 16, bs, 16), dtype=torch.uint8, device=dev)
+           for _ in range(copies)]
+    vcs = [torch.empty((nb, Hkv, dh, bs), dtype=torch.uint8, device=dev) for _ in range(copies)]
+    out = torch.empty((B, Hq, dh), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(K.kvq_decode_workspace_size(B, Hq, dh, max_ctx, bs), 16),
+                     dtype=torch.uint8, device=dev)
+    kv_bytes = int(base.paging.context_lens.sum()) * Hkv * dh * 2
+    rows = {}
+    for fmt in ("e4m3", "e5m2"):
+        wl = dataclasses.replace(base, name=f"long-context-decode-b{B}-s{max_ctx}-{fmt}", fmt=fmt)
+        ks = torch.empty(Hkv, device=dev)
+        vs = torch.empty(Hkv, device=dev)
+        am = torch.empty(Hkv, device=dev)
+        K.kvq_calibrate_scales(k_all, fmt, "head", am, ks)
+        K.kvq_calibrate_scales(v_all, fmt, "head", am, vs)
+        for kc, vc in zip(kcs, vcs):
+            K.kvq_cache_write(k_all, v_all, slots, kc, vc, ks, vs, fmt, "head")
+
+        def call(i):
+            K.kvq_decode_attn_append(out, q, k_new, v_new, kcs[i % copies], vcs[i % copies], bt,
+                                     ctx, max_ctx, ks, vs, fmt, "head", workspace=ws)
+        ms = time_rotating(torch, stream, call, steps, warm=10)
+        gbs = kv_bytes / ms / 1e6
+        rows[f"decode_long_{fmt}"] = {
+            "workload": wl.name + " (per-head k/v scales [8], append step)",
+            "ms": round(ms, 5), "bytes": kv_bytes, "GB/s": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del kcs, vcs
+    return rows
+
+
+def tiny_row(K, W, torch, dev, stream, reps=200):
+    """The tiny decode configuration (B=1, Hq=4, Hkv=2, dh=64, context 256 in 16
+    shuffled blocks, scale 1.0, E4M3): quantize-write of the 256 tokens then one
+    decode step, per call; latency-bound (64 KiB of cache)."""
+    wl = W.tiny_decode()
+
+    def dt(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    k, v, slots = dt(wl.kv.k), dt(wl.kv.v), dt(wl.kv.slot_mapping)
+    q, bt, ctx = dt(wl.q), dt(wl.paging.block_tables), dt(wl.paging.context_lens)
+    nb = wl.paging.num_blocks
+    kc = torch.empty((nb, wl.Hkv, wl.dh // 16, wl.bs, 16), dtype=torch.uint8, device=dev)
+    vc = torch.empty((nb, wl.Hkv, wl.dh, wl.bs), dtype=torch.uint8, device=dev)
+    one = torch.ones(1, device=dev)
+    out = torch.empty((wl.B, wl.Hq, wl.dh), device=dev)
+    mc = int(wl.paging.context_lens.max())
+    ws = torch.empty(max(K.kvq_decode_workspace_size(wl.B, wl.Hq, wl.dh, mc, wl.bs), 16),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        K.kvq_cache_write(k, v, slots, kc, vc, one, one, "fp8_e4m3", "tensor")
+        K.kvq_decode_attn(out, q, kc, vc, bt, ctx, mc, one, one, "fp8_e4m3", "tensor",
+                          workspace=ws)
+    ms = time_call(torch, stream, call, reps)
+    return {"workload": wl.name + " (kvq_cache_write of 256 tokens, then kvq_decode_attn)",
+            "us": round(ms * 1e3, 2)}
+
+
 def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, vs, wl, dec,
                  ragged=True):
     rows = {}
+    rows["tiny_write_then_decode"] = tiny_row(K, W, torch, dev, stream)
+    rows.update(long_context_rows(K, W, torch, dev, stream))
     rows.update(kivi_rows(K, W, torch, dev, stream))
     rows.update(token_scale_rows(K, torch, dev, stream, k_all, v_all, slots_all, caches, wl,
                                  dec))
@@ -454,12 +542,47 @@ def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, 
     return rows
 
 
-def cpu_baseline(wl, sample_rows, min_seconds):
-    """The fp64 oracle on the host: decode attention of the layer over a bounded
-    sample of (sequence, head) rows, repeated until at least min_seconds of
-    work have been timed."""
+def host_info():
+    """Threads the oracle runs with, the host's logical CPUs and its CPU model."""
+    import oracle
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return oracle.num_threads(), nproc, model
+
+
+def timed(fn, min_seconds=0.0):
+    """(seconds per call, calls): fn repeated until min_seconds have passed (once at least)."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        t = time.perf_counter() - t0
+        if t >= min_seconds:
+            return t / n, n
+
+
+def cpu_baseline(wl, sample_rows, min_seconds, W=None):
+    """The fp64 oracle on the host.  The headline figure: decode attention of
+    the Llama-shaped layer over a bounded sample of (sequence, head) rows,
+    repeated until at least min_seconds of work have been timed.  `rows`: the
+    oracle's calibrate, write and decode of the tiny and long-context
+    workloads and of the same layer, and FP8 prefill on a seeded subset of
+    (sequence, head) pairs scaled by pair count, each with the algorithmic
+    bytes or flops of the GPU rows."""
     import oracle
     fmt, gran = oracle.FMT_E4M3, oracle.GRAN_TENSOR
+    threads, nproc, model = host_info()
     ks = oracle.calibrate(wl.kv.k, fmt, gran)[1]
     vs = oracle.calibrate(wl.kv.v, fmt, gran)[1]
     kc = np.zeros(oracle.k_cache_shape(wl.paging.num_blocks, wl.Hkv, wl.bs, wl.dh), np.uint8)
@@ -469,24 +592,103 @@ def cpu_baseline(wl, sample_rows, min_seconds):
     if sample_rows:
         rows = rows[np.random.Generator(np.random.PCG64(5)).permutation(len(rows))[:sample_rows]]
     cl = wl.paging.context_lens
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.decode_rows(rows, wl.q, kc, vc, wl.paging.block_tables, cl, ks, vs, fmt, gran)
-        reps += 1
-        t = time.perf_counter() - t0
-        if t >= min_seconds:
-            break
+    t, reps = timed(lambda: oracle.decode_rows(rows, wl.q, kc, vc, wl.paging.block_tables, cl,
+                                               ks, vs, fmt, gran), min_seconds)
     # bytes of the FP8 history the sampled rows read (each row reads its sequence's K and V)
     G = wl.Hq // wl.Hkv
-    kv_bytes = float(sum(int(cl[b]) for b, _ in rows)) * wl.dh * 2 / G * reps
-    threads = oracle.num_threads()
-    return {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "seconds": round(t, 3), "repeats": reps,
-            "sample": f"decode attention of {len(rows)} of {wl.B * wl.Hq} (sequence, head) rows "
-                      f"of the same layer, repeated {reps} times; fp64, OpenMP over rows; bytes "
-                      f"counted as the FP8 K+V history those rows read (shared by the {G} heads "
-                      f"of a group)"}
+    kv_bytes = float(sum(int(cl[b]) for b, _ in rows)) * wl.dh * 2 / G
+    res = {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
+           "kind": "oracle", "nproc": nproc, "cpu_model": model,
+           "seconds": round(t * reps, 3), "repeats": reps,
+           "sample": f"decode attention of {len(rows)} of {wl.B * wl.Hq} (sequence, head) rows "
+                     f"of the same layer, repeated {reps} times; fp64, OpenMP over rows with "
+                     f"{threads} threads; bytes counted as the FP8 K+V history those rows read "
+                     f"(shared by the {G} heads of a group)"}
+    if W is not None:
+        res["rows"] = cpu_rows(oracle, W, wl, kc, vc, ks, vs)
+    return res
+
+
+def cpu_rows(oracle, W, wl, kc, vc, ks, vs):
+    """Oracle timings of calibrate, write and decode per workload (one pass
+    each, at the GPU rows' algorithmic bytes) and of prefill on a subset."""
+    out = {}
+
+    def rec(name, secs, nbytes=None, flops=None, note=None):
+        r = {"seconds": round(secs, 4)}
+        if nbytes is not None:
+            r["GB/s"] = round(nbytes / secs / 1e9, 4)
+        if flops is not None:
+            r["TFLOP/s"] = round(flops / secs / 1e12, 6)
+        if note:
+            r["sample"] = note
+        out[name] = r
+
+    # the tiny decode (scale 1.0): write of 256 tokens, one decode step
+    tw = W.tiny_decode()
+    s1 = np.ones(1, np.float32)
+    tkc = np.zeros(oracle.k_cache_shape(tw.paging.num_blocks, tw.Hkv, tw.bs, tw.dh), np.uint8)
+    tvc = np.zeros((tw.paging.num_blocks, tw.Hkv, tw.dh, tw.bs), np.uint8)
+    t, n = timed(lambda: (oracle.cache_write(tw.kv.k, tw.kv.v, tw.kv.slot_mapping, tkc, tvc, s1,
+                                             s1, 0, 0),
+                          oracle.decode_attn(tw.q, tkc, tvc, tw.paging.block_tables,
+                                             tw.paging.context_lens, s1, s1, 0, 0)), 1.0)
+    out["tiny_write_then_decode"] = {"us": round(t * 1e6, 2), "repeats": n}
+    # the Llama-shaped layer: calibrate K+V, full-context write, one decode step (every row)
+    T = wl.kv.k.shape[0]
+    fmt, gran = oracle.FMT_E4M3, oracle.GRAN_TENSOR
+    t, _ = timed(lambda: (oracle.calibrate(wl.kv.k, fmt, gran), oracle.calibrate(wl.kv.v, fmt, gran)))
+    rec("calibrate", t, 2 * T * wl.Hkv * wl.dh * 2)
+    t, _ = timed(lambda: oracle.cache_write(wl.kv.k, wl.kv.v, wl.kv.slot_mapping, kc, vc, ks, vs,
+                                            fmt, gran))
+    rec("cache_write", t, T * (wl.Hkv * wl.dh * 2 * 2 + wl.Hkv * wl.dh * 2 + 8))
+    t, _ = timed(lambda: oracle.decode_attn(wl.q, kc, vc, wl.paging.block_tables,
+                                            wl.paging.context_lens, ks, vs, fmt, gran))
+    rec("decode", t, T * wl.Hkv * wl.dh * 2)
+    # long context, per-head scales, E4M3: calibrate, write, decode
+    lw = W.long_context_decode("e4m3")
+    gh = oracle.GRAN_HEAD
+    LT = lw.kv.k.shape[0]
+    t, _ = timed(lambda: (oracle.calibrate(lw.kv.k, fmt, gh), oracle.calibrate(lw.kv.v, fmt, gh)))
+    rec("calibrate_long_e4m3", t, 2 * LT * lw.Hkv * lw.dh * 2)
+    lks = oracle.calibrate(lw.kv.k, fmt, gh)[1]
+    lvs = oracle.calibrate(lw.kv.v, fmt, gh)[1]
+    lkc = np.zeros(oracle.k_cache_shape(lw.paging.num_blocks, lw.Hkv, lw.bs, lw.dh), np.uint8)
+    lvc = np.zeros((lw.paging.num_blocks, lw.Hkv, lw.dh, lw.bs), np.uint8)
+    t, _ = timed(lambda: oracle.cache_write(lw.kv.k, lw.kv.v, lw.kv.slot_mapping, lkc, lvc, lks,
+                                            lvs, fmt, gh))
+    rec("cache_write_long_e4m3", t, LT * (lw.Hkv * lw.dh * 2 * 2 + lw.Hkv * lw.dh * 2 + 8))
+    t, _ = timed(lambda: oracle.decode_attn(lw.q, lkc, lvc, lw.paging.block_tables,
+                                            lw.paging.context_lens, lks, lvs, fmt, gh))
+    rec("decode_long_e4m3", t, LT * lw.Hkv * lw.dh * 2)
+    del lw, lkc, lvc
+    # FP8 prefill: every query row of one seeded (sequence, head) pair of the
+    # 8 x (4096 + 4096) workload, scaled to all 256 pairs by pair count (every pair
+    # does the same causal work)
+    pw = W.fp8_chunked_prefill()
+    qs = oracle.calibrate(pw.q, fmt, gh)[1]
+    pks = oracle.calibrate(pw.kv.k, fmt, gh)[1]
+    pvs = oracle.calibrate(pw.kv.v, fmt, gh)[1]
+    pkc = np.zeros(oracle.k_cache_shape(pw.paging.num_blocks, pw.Hkv, pw.bs, pw.dh), np.uint8)
+    pvc = np.zeros((pw.paging.num_blocks, pw.Hkv, pw.dh, pw.bs), np.uint8)
+    oracle.cache_write(pw.kv.k, pw.kv.v, pw.kv.slot_mapping, pkc, pvc, pks, pvs, fmt, gh)
+    g = np.random.Generator(np.random.PCG64(11))
+    nseq, npairs = len(pw.prefix_lens), 1
+    pairs = [(int(g.integers(nseq)), int(g.integers(pw.Hq))) for _ in range(npairs)]
+    cu = pw.cu_seqlens
+    rws = np.array([(r, h) for b, h in pairs for r in range(cu[b], cu[b + 1])], np.int64)
+    t, _ = timed(lambda: oracle.prefill_rows(rws, pw.q, pw.cu_seqlens, qs, gh, pkc, pvc,
+                                             pw.paging.block_tables, pw.paging.context_lens,
+                                             pks, pvs, fmt, gh))
+    total_pairs = nseq * pw.Hq
+    flops = 0
+    for b in range(nseq):
+        P, C = int(pw.prefix_lens[b]), int(cu[b + 1] - cu[b])
+        flops += 4 * pw.dh * pw.Hq * (C * P + C * (C + 1) // 2)
+    rec("prefill", t * total_pairs / npairs, flops=flops,
+        note=f"all {len(rws)} query rows of {npairs} seeded (sequence, head) pairs, timed "
+             f"{t:.2f} s, scaled by {total_pairs}/{npairs} pairs")
+    return out
 
 
 if __name__ == "__main__":

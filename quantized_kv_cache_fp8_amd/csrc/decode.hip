@@ -829,6 +829,83 @@ void* decode_static_scratch() {
   return g_scratch_ptr[dev];
 }
 
+// Rows with more than 16 splits (long contexts): grid (Hq, B), DH x kSL
+// threads per (b, hq) row.  Split lane j of the block merges splits j, j + kSL,
+// ... -- at most 16 of them in one batch for up to 16 kSL splits -- with every
+// load of a batch issued together, and the kSL lanes' (M, L, a) are merged
+// through LDS, so a row of up to 64 splits costs one round trip to memory
+// instead of four.
+constexpr int kSL = 4;
+template <int DH, bool BF16>
+__global__ __launch_bounds__(DH * kSL) void decode_combine_lanes_kernel(
+    void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
+    const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int max_ctx,
+    const float* __restrict__ vs, int per_head, int part_blocks, int nsplit) {
+  constexpr int kBatch = 16;
+  __shared__ float s_m[kSL], s_l[kSL][DH], s_a[kSL][DH];
+  const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x, j = threadIdx.y;
+  int nvalid = nsplit;
+  if (part_blocks > 0) {
+    int ctx = ctx_lens[b];
+    ctx = ctx < 0 ? 0 : (ctx > max_ctx ? max_ctx : ctx);
+    const int span = part_blocks * kBlockSize;
+    nvalid = (ctx + span - 1) / span;
+  }
+  const size_t row0 = ((size_t)b * Hq + hq) * nsplit;
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml);
+  float M = kNegBig, L = 0.0f, a = 0.0f;
+  for (int s0 = j; s0 < nvalid; s0 += kSL * kBatch) {
+    float2 p[kBatch];
+    float o[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int sp = s0 + i * kSL;
+      p[i] = make_float2(kNegBig, 0.0f);
+      o[i] = 0.0f;
+      if (sp < nvalid) {
+        p[i] = ml[row0 + sp];
+        o[i] = ws_acc[(row0 + sp) * DH + d];
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) Mn = __builtin_fmaxf(Mn, p[i].x);
+    const float f = __builtin_amdgcn_exp2f(M - Mn);
+    L *= f;
+    a *= f;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const float w = __builtin_amdgcn_exp2f(p[i].x - Mn);  // 0 for the padding entries
+      L += w * p[i].y;
+      a += w * o[i];
+    }
+    M = Mn;
+  }
+  if (d == 0) s_m[j] = M;
+  s_l[j][d] = L;
+  s_a[j][d] = a;
+  __syncthreads();
+  if (j != 0) return;
+  float Mt = kNegBig;
+#pragma unroll
+  for (int i = 0; i < kSL; ++i) Mt = __builtin_fmaxf(Mt, s_m[i]);
+  float Lt = 0.0f, at = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kSL; ++i) {
+    const float w = __builtin_amdgcn_exp2f(s_m[i] - Mt);
+    Lt += w * s_l[i][d];
+    at += w * s_a[i][d];
+  }
+  const int h = hq / (Hq / Hkv);
+  const float sv = vs ? vs[per_head ? h : 0] : 1.0f;  // null: sV already folded into P
+  const float r = Lt > 0.0f ? at / Lt * sv : 0.0f;
+  const size_t oi = ((size_t)b * Hq + hq) * DH + d;
+  if constexpr (BF16)
+    reinterpret_cast<uint16_t*>(out)[oi] = (uint16_t)f32_to_bf16_rne(r);
+  else
+    reinterpret_cast<float*>(out)[oi] = r;
+}
+
 static int heads_per_group(int G) {
   // largest divisor of G that fits the 16 rows of one MFMA tile
   for (int n = G < 16 ? G : 16; n >= 1; --n)
@@ -923,9 +1000,13 @@ void launch_decode_combine(void* out, int out_bf16, const float* ml, const float
                            hipStream_t s) {
   constexpr int kHpw = kCombineHeadsPerWg;
   const bool wide = kHpw > 1 && Hq % kHpw == 0;
+  const bool lanes = nsplit > 16;  // rows of more than one batch of splits
 #define KVQ_COMBINE(D, BF)                                                                     \
   do {                                                                                         \
-    if (wide)                                                                                  \
+    if (lanes)                                                                                 \
+      decode_combine_lanes_kernel<D, BF><<<dim3(Hq, B), dim3(D, kSL), 0, s>>>(                  \
+          out, ml, acc, ctx, Hq, Hkv, max_ctx, vs, per_head, part_blocks, nsplit);             \
+    else if (wide)                                                                             \
       decode_combine_kernel<D, BF, kHpw><<<dim3(Hq / kHpw, B), dim3(D, kHpw), 0, s>>>(         \
           out, ml, acc, ctx, Hq, Hkv, max_ctx, vs, per_head, part_blocks, nsplit);             \
     else                                                                                       \

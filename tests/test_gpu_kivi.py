@@ -104,11 +104,13 @@ def test_decode_matches_oracle(Hq, Hkv):
 
 def test_decode_bf16_output_and_loose_bound():
     """bf16 output = RNE of the fp32 output; a max_groups above every sequence's
-    group count changes nothing."""
+    group count changes the split plan (and with more than 16 splits the order
+    in which the combine merges them) but not the result beyond that rounding."""
     wl = W.kivi_workload("bf16", 820, 16, 4, [3, 50, 12], [128, 5, 0], max_blocks=70)
     f = run_decode(wl)
     assert np.array_equal(run_decode(wl, "bf16"), W.f32_to_bf16_bits(f))
-    assert np.array_equal(run_decode(wl, max_groups=70), f)
+    np.testing.assert_allclose(run_decode(wl, max_groups=70), f, rtol=0,
+                               atol=1e-5 * np.abs(f).max())
     check(f, oracle_decode(wl).reshape(f.shape))
 
 
