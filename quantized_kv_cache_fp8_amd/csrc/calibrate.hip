@@ -82,6 +82,65 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
     if (red[i]) atomicMax(amax + i, red[i] << 16);
 }
 
+// The same reduction with each workgroup on one contiguous range of the
+// tensor (a plain streaming read, like a copy's): the tensor is cut into units
+// of 256 J chunks, J = lcm(chunks per token, 256) / 256 in {1, 2, 4}, and
+// workgroup w scans units [w U / G, (w + 1) U / G).  Thread t reads chunks
+// t + 256 j of each unit, whose head ((t + 256 j) / cpr) % H is the same in
+// every unit since a unit holds whole tokens; it keeps one running max per j.
+// Four units are read per step (4 J loads in flight per thread), with
+// nontemporal loads: every byte is read once.
+template <int J>
+__global__ __launch_bounds__(256) void amax_contig_kernel(const uint16_t* __restrict__ x,
+                                                          int64_t nchunks, int64_t nunits,
+                                                          int H, int dh, int per_head,
+                                                          uint32_t* __restrict__ amax) {
+  __shared__ uint32_t red[256];
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const int t = threadIdx.x;
+  red[t] = 0u;
+  const int cpr = dh >> 3;
+  const int64_t u0 = nunits * blockIdx.x / gridDim.x, u1 = nunits * (blockIdx.x + 1) / gridDim.x;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x);
+  u16x2 acc[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) acc[j] = u16x2{0, 0};
+  auto chunk = [&](int64_t u, int j) { return u * (256 * J) + 256 * j + t; };
+  auto absmax8v = [&](u32x4 v) { return absmax8(make_uint4(v.x, v.y, v.z, v.w)); };
+  int64_t u = u0;
+  // whole units strictly inside the tensor, four at a time
+  const int64_t full = nchunks / (256 * J);  // units lying entirely inside the tensor
+  const int64_t uf = u1 < full ? u1 : full;
+  for (; u + 3 < uf; u += 4) {
+    u32x4 w[4][J];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int j = 0; j < J; ++j) w[k][j] = __builtin_nontemporal_load(src + chunk(u + k, j));
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int j = 0; j < J; ++j) acc[j] = __builtin_elementwise_max(acc[j], absmax8v(w[k][j]));
+  }
+  for (; u < u1; ++u)
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int64_t c = chunk(u, j);
+      if (c < nchunks) acc[j] = __builtin_elementwise_max(acc[j], absmax8v(src[c]));
+    }
+  __syncthreads();  // red[] cleared
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t m = umax(acc[j].x, acc[j].y);
+    const int h = per_head ? ((t + 256 * j) / cpr) % H : 0;
+    if (m) atomicMax(&red[h], m);  // LDS atomic: workgroup-local
+  }
+  __syncthreads();
+  const int nslot = per_head ? H : 1;
+  for (int i = t; i < nslot; i += 256)
+    if (red[i]) atomicMax(amax + i, red[i] << 16);
+}
+
 template <int FMT>
 __global__ void scale_finalize_kernel(const uint32_t* __restrict__ amax, float* __restrict__ scale,
                                       int n) {
@@ -101,6 +160,24 @@ hipError_t launch_calibrate(const uint16_t* x, int64_t T, int H, int dh, int fmt
   if (T > 0) {
     const int64_t nchunks = T * H * (dh >> 3);
     const int64_t cpt = (int64_t)H * (dh >> 3);  // chunks per token: the stride's unit
+    const int64_t lcm = cpt % 256 == 0 ? cpt : cpt * 256 / gcd64(cpt, 256);
+    const int J = (int)(lcm / 256);
+    if ((J == 1 || J == 2 || J == 4) && (!per_head || H <= 256)) {
+      // contiguous ranges: about 8 workgroups per CU, at least 4 units each
+      const int64_t nunits = (nchunks + 256 * J - 1) / (256 * J);
+      int64_t g = (int64_t)device_cu_count() * 8;
+      if (g > (nunits + 3) / 4) g = (nunits + 3) / 4;
+      if (g < 1) g = 1;
+      if (J == 1)
+        amax_contig_kernel<1><<<(uint32_t)g, 256, 0, s>>>(x, nchunks, nunits, H, dh, per_head,
+                                                          amax);
+      else if (J == 2)
+        amax_contig_kernel<2><<<(uint32_t)g, 256, 0, s>>>(x, nchunks, nunits, H, dh, per_head,
+                                                          amax);
+      else
+        amax_contig_kernel<4><<<(uint32_t)g, 256, 0, s>>>(x, nchunks, nunits, H, dh, per_head,
+                                                          amax);
+    } else {
     // about 8 workgroups per CU, the grid's thread count a multiple of cpt
     int64_t threads = (int64_t)device_cu_count() * 8 * 256;
     const int64_t unit = cpt % 256 == 0 ? cpt : cpt * 256 / gcd64(cpt, 256);  // lcm(cpt, 256)
@@ -109,6 +186,7 @@ hipError_t launch_calibrate(const uint16_t* x, int64_t T, int H, int dh, int fmt
     if (threads > need) threads = (need + unit - 1) / unit * unit;
     amax_kernel<<<(uint32_t)(threads / 256), 256, 0, s>>>(x, nchunks, H, dh, per_head, threads,
                                                           amax);
+    }
   }
   dispatch_fmt(fmt, [&](auto f) {
     scale_finalize_kernel<decltype(f)::value><<<(n + 255) / 256, 256, 0, s>>>(amax, scale_out, n);
