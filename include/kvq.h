@@ -83,10 +83,14 @@ typedef enum { KVQ_SCALE_TENSOR = 0, KVQ_SCALE_HEAD = 1 } kvq_gran;
 /* Element type of attention outputs. */
 typedef enum { KVQ_OUT_F32 = 0, KVQ_OUT_BF16 = 1 } kvq_out;
 
+/* Entry points take these three as plain int parameters, so a value outside
+ * the enumeration is a defined input that returns KVQ_ERR_UNSUPPORTED. */
+
 typedef void* kvq_stream; /* hipStream_t */
 
-/* Human-readable text for a status code (static storage, never NULL). */
-const char* kvq_strerror(kvq_status status);
+/* Human-readable text for a status code (static storage, never NULL).  Takes
+ * any int: a value that is no kvq_status gives "unknown status". */
+const char* kvq_strerror(int status);
 
 /* Bytes of a KV cache payload, [T] 10.4.1:
  *   M_KV = 2 * L * B * Hkv * S * dh * bits_per_elem / 8
@@ -104,9 +108,9 @@ uint64_t kvq_kv_cache_bytes(int L, int B, int Hkv, int64_t S, int dh, int bits_p
  *     E5M2 Inf codes give +-Inf).  codes: uint8 [n], out: fp32 [n].
  * n == 0 is a no-op.  Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE (n < 0),
  * KVQ_ERR_UNSUPPORTED (fmt). */
-kvq_status kvq_fp8_encode(kvq_fmt fmt, const float* x, int64_t n, uint8_t* out,
+kvq_status kvq_fp8_encode(int fmt, const float* x, int64_t n, uint8_t* out,
                           kvq_stream stream);
-kvq_status kvq_fp8_decode(kvq_fmt fmt, const uint8_t* codes, int64_t n, float* out,
+kvq_status kvq_fp8_decode(int fmt, const uint8_t* codes, int64_t n, float* out,
                           kvq_stream stream);
 
 /* ---------------------------------------------------------------- calibration
@@ -123,8 +127,8 @@ kvq_status kvq_fp8_decode(kvq_fmt fmt, const uint8_t* codes, int64_t n, float* o
  * T == 0 is allowed (amax of an empty set is 0).  amax_io and scale_out are
  * fp32 device arrays.  Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE (T < 0, H < 1,
  * dh < 1 or dh % 8), KVQ_ERR_UNSUPPORTED (fmt, gran). */
-kvq_status kvq_calibrate_scales(const void* x_bf16, int64_t T, int H, int dh, kvq_fmt fmt,
-                                kvq_gran gran, float* amax_io, float* scale_out, int accumulate,
+kvq_status kvq_calibrate_scales(const void* x_bf16, int64_t T, int H, int dh, int fmt,
+                                int gran, float* amax_io, float* scale_out, int accumulate,
                                 kvq_stream stream);
 
 /* ---------------------------------------------------------------- quantize-write
@@ -146,7 +150,7 @@ kvq_status kvq_calibrate_scales(const void* x_bf16, int64_t T, int H, int dh, kv
 kvq_status kvq_cache_write(const void* k_bf16, const void* v_bf16, int64_t T, int Hkv, int dh,
                            const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
                            int64_t num_blocks, int bs, const float* k_scale,
-                           const float* v_scale, kvq_fmt fmt, kvq_gran gran, kvq_stream stream);
+                           const float* v_scale, int fmt, int gran, kvq_stream stream);
 
 /* ---------------------------------------------------------------- decode
  * Bytes of device workspace kvq_decode_attn needs for these sizes (split-K
@@ -170,12 +174,12 @@ size_t kvq_decode_workspace_size(int B, int Hq, int dh, int max_context_len, int
  *   workspace: device buffer of >= kvq_decode_workspace_size(...) bytes; its
  *     contents need no initialisation and are overwritten.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE. */
-kvq_status kvq_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_decode_attn(void* out, int out_dtype, const void* q_bf16,
                            const uint8_t* k_cache, const uint8_t* v_cache, int64_t num_blocks,
                            const int32_t* block_tables, int max_blocks,
                            const int32_t* context_lens, int B, int Hq, int Hkv, int dh, int bs,
                            int max_context_len, const float* k_scale, const float* v_scale,
-                           kvq_fmt fmt, kvq_gran gran, float softmax_scale, void* workspace,
+                           int fmt, int gran, float softmax_scale, void* workspace,
                            size_t ws_bytes, kvq_stream stream);
 
 /* ---------------------------------------------------------------- skip-layers, padded pages
@@ -221,24 +225,24 @@ kvq_status kvq_cache_write_paged(const void* k_bf16, const void* v_bf16, int64_t
                                  int dh, const int64_t* slot_mapping, uint8_t* k_cache,
                                  uint8_t* v_cache, int64_t num_blocks, int bs,
                                  int64_t block_stride, const float* k_scale,
-                                 const float* v_scale, kvq_fmt fmt, kvq_gran gran,
+                                 const float* v_scale, int fmt, int gran,
                                  kvq_stream stream);
-kvq_status kvq_decode_attn_paged(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_decode_attn_paged(void* out, int out_dtype, const void* q_bf16,
                                  const uint8_t* k_cache, const uint8_t* v_cache,
                                  int64_t num_blocks, const int32_t* block_tables, int max_blocks,
                                  const int32_t* context_lens, int B, int Hq, int Hkv, int dh,
                                  int bs, int64_t block_stride, int max_context_len,
-                                 const float* k_scale, const float* v_scale, kvq_fmt fmt,
-                                 kvq_gran gran, float softmax_scale, void* workspace,
+                                 const float* k_scale, const float* v_scale, int fmt,
+                                 int gran, float softmax_scale, void* workspace,
                                  size_t ws_bytes, kvq_stream stream);
-kvq_status kvq_prefill_attn_paged(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_prefill_attn_paged(void* out, int out_dtype, const void* q_bf16,
                                   const int32_t* cu_seqlens_q, int max_q_len,
-                                  const float* q_scale, kvq_gran q_gran, const uint8_t* k_cache,
+                                  const float* q_scale, int q_gran, const uint8_t* k_cache,
                                   const uint8_t* v_cache, int64_t num_blocks,
                                   const int32_t* block_tables, int max_blocks,
                                   const int32_t* context_lens, int B, int Hq, int Hkv, int dh,
                                   int bs, int64_t block_stride, const float* k_scale,
-                                  const float* v_scale, kvq_fmt fmt, kvq_gran kv_gran,
+                                  const float* v_scale, int fmt, int kv_gran,
                                   float softmax_scale, kvq_stream stream);
 
 /* ---------------------------------------------------------------- per-token-head scales
@@ -261,7 +265,7 @@ kvq_status kvq_cache_write_token_scales(const void* k_bf16, const void* v_bf16, 
                                         int Hkv, int dh, const int64_t* slot_mapping,
                                         uint8_t* k_cache, uint8_t* v_cache,
                                         uint16_t* k_scale_cache, uint16_t* v_scale_cache,
-                                        int64_t num_blocks, int bs, kvq_fmt fmt,
+                                        int64_t num_blocks, int bs, int fmt,
                                         kvq_stream stream);
 
 /* Paged decode over a cache written by kvq_cache_write_token_scales: as
@@ -271,13 +275,13 @@ kvq_status kvq_cache_write_token_scales(const void* k_bf16, const void* v_bf16, 
  * (Hq / Hkv <= 4) are supported; larger groups return KVQ_ERR_UNSUPPORTED.
  * The workspace is sized by kvq_decode_workspace_size as for kvq_decode_attn.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE. */
-kvq_status kvq_decode_attn_token_scales(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_decode_attn_token_scales(void* out, int out_dtype, const void* q_bf16,
                                         const uint8_t* k_cache, const uint8_t* v_cache,
                                         const uint16_t* k_scale_cache,
                                         const uint16_t* v_scale_cache, int64_t num_blocks,
                                         const int32_t* block_tables, int max_blocks,
                                         const int32_t* context_lens, int B, int Hq, int Hkv,
-                                        int dh, int bs, int max_context_len, kvq_fmt fmt,
+                                        int dh, int bs, int max_context_len, int fmt,
                                         float softmax_scale, void* workspace, size_t ws_bytes,
                                         kvq_stream stream);
 
@@ -327,7 +331,7 @@ size_t kvq_kivi_decode_workspace_size(int B, int Hq, int Hkv, int max_groups);
  * dequantized V in f16, P in f16, fp32 accumulation), so |q|, |K| and |V|
  * must lie within the fp16 range; the residual is attended in fp32.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE. */
-kvq_status kvq_kivi_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_kivi_decode_attn(void* out, int out_dtype, const void* q_bf16,
                                 const uint8_t* kivi_cache, int64_t num_blocks,
                                 const int32_t* block_tables, int max_blocks,
                                 const int32_t* quant_groups, int max_groups,
@@ -350,13 +354,13 @@ kvq_status kvq_kivi_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16
  * kvq_decode_attn does, and its new token is neither written nor attended: no
  * cache byte of it changes.  k_new / v_new must be 16-byte aligned.
  * Errors: as kvq_decode_attn. */
-kvq_status kvq_decode_attn_append(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_decode_attn_append(void* out, int out_dtype, const void* q_bf16,
                                   const void* k_new_bf16, const void* v_new_bf16,
                                   uint8_t* k_cache, uint8_t* v_cache, int64_t num_blocks,
                                   const int32_t* block_tables, int max_blocks,
                                   const int32_t* context_lens, int B, int Hq, int Hkv, int dh,
                                   int bs, int max_context_len, const float* k_scale,
-                                  const float* v_scale, kvq_fmt fmt, kvq_gran gran,
+                                  const float* v_scale, int fmt, int gran,
                                   float softmax_scale, void* workspace, size_t ws_bytes,
                                   kvq_stream stream);
 
@@ -382,14 +386,14 @@ kvq_status kvq_decode_attn_append(void* out, kvq_out out_dtype, const void* q_bf
  * and must be ordered by the caller.
  * Errors: as kvq_decode_attn_append without KVQ_ERR_WORKSPACE, plus
  * KVQ_ERR_SCRATCH; KVQ_ERR_DEVICE if the array's address cannot be found. */
-kvq_status kvq_decode_attn_append_noalloc(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_decode_attn_append_noalloc(void* out, int out_dtype, const void* q_bf16,
                                           const void* k_new_bf16, const void* v_new_bf16,
                                           uint8_t* k_cache, uint8_t* v_cache, int64_t num_blocks,
                                           const int32_t* block_tables, int max_blocks,
                                           const int32_t* context_lens, int B, int Hq, int Hkv,
                                           int dh, int bs, int max_context_len,
                                           const float* k_scale, const float* v_scale,
-                                          kvq_fmt fmt, kvq_gran gran, float softmax_scale,
+                                          int fmt, int gran, float softmax_scale,
                                           kvq_stream stream);
 
 /* ---------------------------------------------------------------- prefill
@@ -417,13 +421,13 @@ kvq_status kvq_decode_attn_append_noalloc(void* out, kvq_out out_dtype, const vo
  *     bits of P.
  *   out: [total_q][Hq][dh] fp32 or bf16.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED. */
-kvq_status kvq_prefill_attn(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_prefill_attn(void* out, int out_dtype, const void* q_bf16,
                             const int32_t* cu_seqlens_q, int max_q_len, const float* q_scale,
-                            kvq_gran q_gran, const uint8_t* k_cache, const uint8_t* v_cache,
+                            int q_gran, const uint8_t* k_cache, const uint8_t* v_cache,
                             int64_t num_blocks, const int32_t* block_tables, int max_blocks,
                             const int32_t* context_lens, int B, int Hq, int Hkv, int dh, int bs,
-                            const float* k_scale, const float* v_scale, kvq_fmt fmt,
-                            kvq_gran kv_gran, float softmax_scale, kvq_stream stream);
+                            const float* k_scale, const float* v_scale, int fmt,
+                            int kv_gran, float softmax_scale, kvq_stream stream);
 
 #ifdef __cplusplus
 }

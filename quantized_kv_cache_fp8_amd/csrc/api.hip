@@ -55,7 +55,7 @@ using namespace kvq;
 
 extern "C" {
 
-const char* kvq_strerror(kvq_status st) {
+const char* kvq_strerror(int st) {
   switch (st) {
     case KVQ_OK: return "ok";
     case KVQ_ERR_NULL: return "a required pointer is NULL";
@@ -77,7 +77,7 @@ uint64_t kvq_kv_cache_bytes(int L, int B, int Hkv, int64_t S, int dh, int bits_p
          (uint64_t)bits_per_elem / 8ull;
 }
 
-kvq_status kvq_fp8_encode(kvq_fmt fmt, const float* x, int64_t n, uint8_t* out,
+kvq_status kvq_fp8_encode(int fmt, const float* x, int64_t n, uint8_t* out,
                           kvq_stream stream) {
   if (!fmt_ok(fmt)) return KVQ_ERR_UNSUPPORTED;
   if (n < 0) return KVQ_ERR_SHAPE;
@@ -87,7 +87,7 @@ kvq_status kvq_fp8_encode(kvq_fmt fmt, const float* x, int64_t n, uint8_t* out,
   return map_err(launch_fp8_encode(fmt, x, n, out, (hipStream_t)stream));
 }
 
-kvq_status kvq_fp8_decode(kvq_fmt fmt, const uint8_t* codes, int64_t n, float* out,
+kvq_status kvq_fp8_decode(int fmt, const uint8_t* codes, int64_t n, float* out,
                           kvq_stream stream) {
   if (!fmt_ok(fmt)) return KVQ_ERR_UNSUPPORTED;
   if (n < 0) return KVQ_ERR_SHAPE;
@@ -97,8 +97,8 @@ kvq_status kvq_fp8_decode(kvq_fmt fmt, const uint8_t* codes, int64_t n, float* o
   return map_err(launch_fp8_decode(fmt, codes, n, out, (hipStream_t)stream));
 }
 
-kvq_status kvq_calibrate_scales(const void* x_bf16, int64_t T, int H, int dh, kvq_fmt fmt,
-                                kvq_gran gran, float* amax_io, float* scale_out, int accumulate,
+kvq_status kvq_calibrate_scales(const void* x_bf16, int64_t T, int H, int dh, int fmt,
+                                int gran, float* amax_io, float* scale_out, int accumulate,
                                 kvq_stream stream) {
   if (!fmt_ok(fmt) || !gran_ok(gran)) return KVQ_ERR_UNSUPPORTED;
   if (T < 0 || H < 1 || H > 65535 || dh < 8 || dh % 8 || dh > 2048) return KVQ_ERR_SHAPE;
@@ -119,7 +119,7 @@ static kvq_status check_stride(int64_t block_stride, int Hkv, int bs, int dh) {
 kvq_status kvq_cache_write(const void* k_bf16, const void* v_bf16, int64_t T, int Hkv, int dh,
                            const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
                            int64_t num_blocks, int bs, const float* k_scale,
-                           const float* v_scale, kvq_fmt fmt, kvq_gran gran,
+                           const float* v_scale, int fmt, int gran,
                            kvq_stream stream) {
   return kvq_cache_write_paged(k_bf16, v_bf16, T, Hkv, dh, slot_mapping, k_cache, v_cache,
                                num_blocks, bs, (int64_t)Hkv * bs * dh, k_scale, v_scale, fmt,
@@ -130,7 +130,7 @@ kvq_status kvq_cache_write_paged(const void* k_bf16, const void* v_bf16, int64_t
                                  int dh, const int64_t* slot_mapping, uint8_t* k_cache,
                                  uint8_t* v_cache, int64_t num_blocks, int bs,
                                  int64_t block_stride, const float* k_scale,
-                                 const float* v_scale, kvq_fmt fmt, kvq_gran gran,
+                                 const float* v_scale, int fmt, int gran,
                                  kvq_stream stream) {
   if (!fmt_ok(fmt) || !gran_ok(gran)) return KVQ_ERR_UNSUPPORTED;
   if (T < 0 || Hkv < 1 || num_blocks < 1) return KVQ_ERR_SHAPE;
@@ -180,12 +180,12 @@ static kvq_status check_decode_ws(const DecodePlan& plan, int max_context_len, i
   return KVQ_OK;
 }
 
-kvq_status kvq_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_decode_attn(void* out, int out_dtype, const void* q_bf16,
                            const uint8_t* k_cache, const uint8_t* v_cache, int64_t num_blocks,
                            const int32_t* block_tables, int max_blocks,
                            const int32_t* context_lens, int B, int Hq, int Hkv, int dh, int bs,
                            int max_context_len, const float* k_scale, const float* v_scale,
-                           kvq_fmt fmt, kvq_gran gran, float softmax_scale, void* workspace,
+                           int fmt, int gran, float softmax_scale, void* workspace,
                            size_t ws_bytes, kvq_stream stream) {
   return kvq_decode_attn_paged(out, out_dtype, q_bf16, k_cache, v_cache, num_blocks, block_tables,
                                max_blocks, context_lens, B, Hq, Hkv, dh, bs,
@@ -193,13 +193,13 @@ kvq_status kvq_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
                                gran, softmax_scale, workspace, ws_bytes, stream);
 }
 
-kvq_status kvq_decode_attn_paged(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_decode_attn_paged(void* out, int out_dtype, const void* q_bf16,
                                  const uint8_t* k_cache, const uint8_t* v_cache,
                                  int64_t num_blocks, const int32_t* block_tables, int max_blocks,
                                  const int32_t* context_lens, int B, int Hq, int Hkv, int dh,
                                  int bs, int64_t block_stride, int max_context_len,
-                                 const float* k_scale, const float* v_scale, kvq_fmt fmt,
-                                 kvq_gran gran, float softmax_scale, void* workspace,
+                                 const float* k_scale, const float* v_scale, int fmt,
+                                 int gran, float softmax_scale, void* workspace,
                                  size_t ws_bytes, kvq_stream stream) {
   kvq_status st = check_attn_common(out, out_dtype, q_bf16, k_cache, v_cache, num_blocks,
                                     block_tables, max_blocks, context_lens, B, Hq, Hkv, dh, bs,
@@ -240,14 +240,14 @@ static kvq_status check_append(const void* out, int out_dtype, const void* q, co
 static_assert(KVQ_STATIC_SCRATCH_BYTES == kStaticScratchBytes,
               "the header's scratch size must be the array's");
 
-kvq_status kvq_decode_attn_append_noalloc(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_decode_attn_append_noalloc(void* out, int out_dtype, const void* q_bf16,
                                           const void* k_new_bf16, const void* v_new_bf16,
                                           uint8_t* k_cache, uint8_t* v_cache, int64_t num_blocks,
                                           const int32_t* block_tables, int max_blocks,
                                           const int32_t* context_lens, int B, int Hq, int Hkv,
                                           int dh, int bs, int max_context_len,
                                           const float* k_scale, const float* v_scale,
-                                          kvq_fmt fmt, kvq_gran gran, float softmax_scale,
+                                          int fmt, int gran, float softmax_scale,
                                           kvq_stream stream) {
   DecodePlan plan;
   kvq_status st = check_append(out, out_dtype, q_bf16, k_new_bf16, v_new_bf16, k_cache, v_cache,
@@ -266,13 +266,13 @@ kvq_status kvq_decode_attn_append_noalloc(void* out, kvq_out out_dtype, const vo
                                v_cache));
 }
 
-kvq_status kvq_decode_attn_append(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_decode_attn_append(void* out, int out_dtype, const void* q_bf16,
                                   const void* k_new_bf16, const void* v_new_bf16,
                                   uint8_t* k_cache, uint8_t* v_cache, int64_t num_blocks,
                                   const int32_t* block_tables, int max_blocks,
                                   const int32_t* context_lens, int B, int Hq, int Hkv, int dh,
                                   int bs, int max_context_len, const float* k_scale,
-                                  const float* v_scale, kvq_fmt fmt, kvq_gran gran,
+                                  const float* v_scale, int fmt, int gran,
                                   float softmax_scale, void* workspace, size_t ws_bytes,
                                   kvq_stream stream) {
   DecodePlan plan;
@@ -295,7 +295,7 @@ kvq_status kvq_cache_write_token_scales(const void* k_bf16, const void* v_bf16, 
                                         int Hkv, int dh, const int64_t* slot_mapping,
                                         uint8_t* k_cache, uint8_t* v_cache,
                                         uint16_t* k_scale_cache, uint16_t* v_scale_cache,
-                                        int64_t num_blocks, int bs, kvq_fmt fmt,
+                                        int64_t num_blocks, int bs, int fmt,
                                         kvq_stream stream) {
   if (!fmt_ok(fmt)) return KVQ_ERR_UNSUPPORTED;
   if (T < 0 || Hkv < 1 || num_blocks < 1) return KVQ_ERR_SHAPE;
@@ -315,13 +315,13 @@ kvq_status kvq_cache_write_token_scales(const void* k_bf16, const void* v_bf16, 
                                           (hipStream_t)stream));
 }
 
-kvq_status kvq_decode_attn_token_scales(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_decode_attn_token_scales(void* out, int out_dtype, const void* q_bf16,
                                         const uint8_t* k_cache, const uint8_t* v_cache,
                                         const uint16_t* k_scale_cache,
                                         const uint16_t* v_scale_cache, int64_t num_blocks,
                                         const int32_t* block_tables, int max_blocks,
                                         const int32_t* context_lens, int B, int Hq, int Hkv,
-                                        int dh, int bs, int max_context_len, kvq_fmt fmt,
+                                        int dh, int bs, int max_context_len, int fmt,
                                         float softmax_scale, void* workspace, size_t ws_bytes,
                                         kvq_stream stream) {
   kvq_status st = check_attn_common(out, out_dtype, q_bf16, k_cache, v_cache, num_blocks,
@@ -362,7 +362,7 @@ size_t kvq_kivi_decode_workspace_size(int B, int Hq, int Hkv, int max_groups) {
   return kivi_decode_plan(B, Hq, Hkv, max_groups).ws_bytes;
 }
 
-kvq_status kvq_kivi_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_kivi_decode_attn(void* out, int out_dtype, const void* q_bf16,
                                 const uint8_t* kivi_cache, int64_t num_blocks,
                                 const int32_t* block_tables, int max_blocks,
                                 const int32_t* quant_groups, int max_groups,
@@ -392,27 +392,27 @@ kvq_status kvq_kivi_decode_attn(void* out, kvq_out out_dtype, const void* q_bf16
                                     softmax_scale, plan, workspace, (hipStream_t)stream));
 }
 
-kvq_status kvq_prefill_attn(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_prefill_attn(void* out, int out_dtype, const void* q_bf16,
                             const int32_t* cu_seqlens_q, int max_q_len, const float* q_scale,
-                            kvq_gran q_gran, const uint8_t* k_cache, const uint8_t* v_cache,
+                            int q_gran, const uint8_t* k_cache, const uint8_t* v_cache,
                             int64_t num_blocks, const int32_t* block_tables, int max_blocks,
                             const int32_t* context_lens, int B, int Hq, int Hkv, int dh, int bs,
-                            const float* k_scale, const float* v_scale, kvq_fmt fmt,
-                            kvq_gran kv_gran, float softmax_scale, kvq_stream stream) {
+                            const float* k_scale, const float* v_scale, int fmt,
+                            int kv_gran, float softmax_scale, kvq_stream stream) {
   return kvq_prefill_attn_paged(out, out_dtype, q_bf16, cu_seqlens_q, max_q_len, q_scale, q_gran,
                                 k_cache, v_cache, num_blocks, block_tables, max_blocks,
                                 context_lens, B, Hq, Hkv, dh, bs, (int64_t)Hkv * bs * dh, k_scale,
                                 v_scale, fmt, kv_gran, softmax_scale, stream);
 }
 
-kvq_status kvq_prefill_attn_paged(void* out, kvq_out out_dtype, const void* q_bf16,
+kvq_status kvq_prefill_attn_paged(void* out, int out_dtype, const void* q_bf16,
                                   const int32_t* cu_seqlens_q, int max_q_len,
-                                  const float* q_scale, kvq_gran q_gran, const uint8_t* k_cache,
+                                  const float* q_scale, int q_gran, const uint8_t* k_cache,
                                   const uint8_t* v_cache, int64_t num_blocks,
                                   const int32_t* block_tables, int max_blocks,
                                   const int32_t* context_lens, int B, int Hq, int Hkv, int dh,
                                   int bs, int64_t block_stride, const float* k_scale,
-                                  const float* v_scale, kvq_fmt fmt, kvq_gran kv_gran,
+                                  const float* v_scale, int fmt, int kv_gran,
                                   float softmax_scale, kvq_stream stream) {
   kvq_status st = check_attn_common(out, out_dtype, q_bf16, k_cache, v_cache, num_blocks,
                                     block_tables, max_blocks, context_lens, B, Hq, Hkv, dh, bs,
