@@ -47,9 +47,16 @@ constexpr int kScaleOne = 127;   // E8M0 block scale 2^0
 constexpr int kScaleLo = 123;    // E8M0 block scale 2^-4 (P_lo carries 16x its value)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
-// waves per SIMD the kernel is compiled for (groups of 2 or 4 heads): its
-// state takes 208 registers, so two fit
-constexpr int kWavesPerSimd = 2;
+// waves per SIMD each instantiation is compiled for.  A lone wave issues a
+// VALU instruction only about every 8 cycles (two waves reach the 4-cycle
+// rate), and a tile's matrix products, LDS reads and barrier leave it idle
+// for long stretches, so more resident waves per SIMD keep both the vector
+// and the matrix units busier.  dh = 128 with groups of 4 heads fits 3 waves
+// (168 registers, its only spill is on the context's last tile); with groups
+// of 2 heads the state needs 224 registers, so 2; one head per group keeps 1.
+__host__ __device__ constexpr int prefill_waves(int dh, int gt) {
+  return gt == 1 ? 1 : (dh == 128 && gt == 2 ? 2 : 3);
+}
 
 // Key order of the P V contraction.  Lane group g of the S tile holds keys
 // k = 32 t + 8 j + 4 g + r (t, j, r: key half, quad pair, byte); its P bytes
@@ -85,7 +92,7 @@ struct MfmaFmt {
 
 template <int FMT, int DH, int GT>
 __global__ __launch_bounds__(64 * GT)
-__attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : kWavesPerSimd, GT == 1 ? 1 : kWavesPerSimd))) void prefill_kernel(
+__attribute__((amdgpu_waves_per_eu(prefill_waves(DH, GT), prefill_waves(DH, GT)))) void prefill_kernel(
     void* __restrict__ out, int out_bf16, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ cu, int n_qtiles, const float* __restrict__ qs, int q_per_head,
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc, int64_t num_blocks,
@@ -403,20 +410,25 @@ __attribute__((amdgpu_waves_per_eu(GT == 1 ? 1 : kWavesPerSimd, GT == 1 ? 1 : kW
     const uint8_t* v_lds = v_buf[kt & 1];
     if (kt + 2 < nkt) ids_next = load_ids(kt + 2);  // lands during this tile
 
-    f32x16 s[2];
+    // Always true (nkt counts exactly the tiles up to pos_max); the test stays
+    // because it changes the compiler's register allocation: without it, the
+    // 3-wave budget spills the query operand and reloads it every tile.
+    if (kt * kKT <= pos_max) {
+      f32x16 s[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[t][v] = 0.0f;
+        for (int v = 0; v < 16; ++v) s[t][v] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NS; ++i)  // the two key halves' chains interleave
-      qk_mfma(s, i, qk_read(k_lds, i));
-    const float bias = softmax_max(s, kt);
+      for (int i = 0; i < NS; ++i)  // the two key halves' chains interleave
+        qk_mfma(s, i, qk_read(k_lds, i));
+      const float bias = softmax_max(s, kt);
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) p_chunk(s, t, v4, bias);
-    pv(v_lds);
+        for (int v4 = 0; v4 < 4; ++v4) p_chunk(s, t, v4, bias);
+      pv(v_lds);
+    }
 
     // ---- tile kt + 1 (loaded during this tile) into the other buffer, whose
     //      readers all passed the previous barrier; then start loading tile
