@@ -23,16 +23,19 @@
 //      with v_perm_b32 and parked in an LDS tile [dh][64 tokens].
 //   3. K: for each valid token and 16-channel chunk one thread stores the 16
 //      code bytes (consecutive threads take consecutive tokens, so a block's
-//      chunk row of 16 tokens goes out as 256 contiguous bytes).  V: for each
-//      run and channel one thread stores the run's codes: one dword when the
-//      run fills its quad (the normal case for tokens of a sequence written
-//      in order, whatever its starting offset), single bytes otherwise (a
-//      decode step's one new token per sequence, the ends of a chunk or of a
-//      sequence).
+//      chunk row of 16 tokens goes out as 256 contiguous bytes).  V: a block
+//      whose 16 tokens all lie in the chunk with consecutive slots (the
+//      normal case for tokens of a sequence written in order) goes out as one
+//      16-byte store per channel row; for each remaining run and channel one
+//      thread stores the run's codes: one dword when the run fills its quad,
+//      single bytes otherwise (a decode step's one new token per sequence,
+//      the ends of a chunk or of a sequence).
 // Tokens with a negative slot, or a slot outside the pool, are skipped.
 // Writes of at most 512 tokens (a decode step) take a one-pass kernel instead.
 #include "codec.hpp"
 #include "launch.hpp"
+
+#include <type_traits>
 
 namespace kvq {
 
@@ -42,10 +45,17 @@ constexpr int kRowDw = kChunk / 4 + 1;  // LDS V-tile row: 16 dwords of codes + 
 // Writes of at most this many tokens take a one-pass kernel (no LDS, no barrier).
 constexpr int64_t kShortWrite = 512;
 
-template <int FMT>
+// four bf16 values -> four codes; PRE as in fp8_arg (INT8 takes the general
+// quotient and its own clip)
+template <int FMT, bool PRE = true>
 __device__ __forceinline__ uint32_t quant4(uint2 w, const Divisor& d) {
-  return enc4<FMT>(quotient(bf16lo(w.x), d), quotient(bf16hi(w.x), d),
-                   quotient(bf16lo(w.y), d), quotient(bf16hi(w.y), d));
+  if constexpr (FMT == INT8) {
+    return enc4<FMT>(quotient(bf16lo(w.x), d), quotient(bf16hi(w.x), d),
+                     quotient(bf16lo(w.y), d), quotient(bf16hi(w.y), d));
+  } else {
+    return cvt4<FMT>(fp8_arg<FMT, PRE>(bf16lo(w.x), d), fp8_arg<FMT, PRE>(bf16hi(w.x), d),
+                     fp8_arg<FMT, PRE>(bf16lo(w.y), d), fp8_arg<FMT, PRE>(bf16hi(w.y), d));
+  }
 }
 
 // Per-token-head scales (one fp16 scale per (token, head) for K and for V,
@@ -99,6 +109,8 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   __shared__ int64_t s_slot[kChunk];
   __shared__ uint32_t s_run[kChunk];  // token index | run length << 8, compacted
   __shared__ int s_nrun;
+  __shared__ uint8_t s_fblk[kChunk / kBs];  // chunk index of each whole block's first token
+  __shared__ int s_nfb;
   __shared__ uint32_t s_vt[DH * kRowDw];
   constexpr int kKRow = DH / 4 + 4;  // LDS K-tile row (dwords): DH codes + 16 B pad
   __shared__ __attribute__((aligned(16))) uint32_t s_kt[kChunk * kKRow];
@@ -134,11 +146,21 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   }
   __syncthreads();
 
-  if (tid < kChunk) {  // wave 0: runs of consecutive slots inside one quad
+  if (tid < kChunk) {  // wave 0: whole blocks, then runs inside one quad
     const int64_t s = s_slot[tid];
+    // a whole block: 16 tokens of this chunk with consecutive slots from a
+    // block's first slot
+    bool fb = s >= 0 && (s & (kBs - 1)) == 0 && tid + kBs <= kChunk;
+    for (int j = 1; fb && j < kBs; ++j) fb = s_slot[tid + j] == s + j;
+    const uint64_t fbm = __builtin_amdgcn_ballot_w64(fb);
+    const int off = (int)(s & (kBs - 1));
+    const bool in_full = s >= 0 && tid >= off && ((fbm >> (tid - off)) & 1) &&
+                         s_slot[tid - off] == s - off;
+    if (fb) s_fblk[__builtin_popcountll(fbm & ((1ull << tid) - 1))] = (uint8_t)tid;
+    if (tid == 0) s_nfb = __builtin_popcountll(fbm);
     const int q = (int)(s & 3);
     const bool cont = tid > 0 && q != 0 && s >= 0 && s_slot[tid - 1] == s - 1;
-    const bool start = s >= 0 && !cont;
+    const bool start = s >= 0 && !cont && !in_full;
     int n = 1;
     while (start && n < 4 - q && tid + n < kChunk && s_slot[tid + n] == s + n) ++n;
     const uint64_t mask = __builtin_amdgcn_ballot_w64(start);
@@ -154,46 +176,56 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     sk = ks[per_head ? h : 0];
     sv = vs[per_head ? h : 0];
   }
-  Divisor dk = make_divisor(sk), dv = make_divisor(sv);
+  const Divisor dk0 = make_divisor(sk), dv0 = make_divisor(sv);
+  // the tiny-scale prescale is decided per workgroup (per-token scales may
+  // need it anywhere)
+  auto quantize = [&](auto pre_tag) {
+    constexpr bool PRE = decltype(pre_tag)::value;
+    Divisor dk = dk0, dv = dv0;
 #pragma unroll
-  for (int jb = 0; jb < kJobs; ++jb) {
-    const int job = tid + 256 * jb;
-    const int cq = job % kCq, tq = job / kCq;
-    uint32_t cv[4];
+    for (int jb = 0; jb < kJobs; ++jb) {
+      const int job = tid + 256 * jb;
+      const int cq = job % kCq, tq = job / kCq;
+      uint32_t cv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (TS) {
-        // the kCq aligned consecutive lanes of token 4 tq + j hold its row
-        uint32_t ak = absmax_bits4(wk[jb][j]), av = absmax_bits4(wv[jb][j]);
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (TS) {
+          // the kCq aligned consecutive lanes of token 4 tq + j hold its row
+          uint32_t ak = absmax_bits4(wk[jb][j]), av = absmax_bits4(wv[jb][j]);
 #pragma unroll
-        for (int o = 1; o < kCq; o <<= 1) {
-          const uint32_t xk = __shfl_xor(ak, o), xv = __shfl_xor(av, o);
-          ak = ak > xk ? ak : xk;
-          av = av > xv ? av : xv;
+          for (int o = 1; o < kCq; o <<= 1) {
+            const uint32_t xk = __shfl_xor(ak, o), xv = __shfl_xor(av, o);
+            ak = ak > xk ? ak : xk;
+            av = av > xv ? av : xv;
+          }
+          const uint16_t k16 = scale16_from_amax_bits<FMT>(ak);
+          const uint16_t v16 = scale16_from_amax_bits<FMT>(av);
+          if (cq == 0) {
+            s_sc[0][4 * tq + j] = k16;
+            s_sc[1][4 * tq + j] = v16;
+          }
+          dk = make_divisor((float)__builtin_bit_cast(_Float16, k16));
+          dv = make_divisor((float)__builtin_bit_cast(_Float16, v16));
         }
-        const uint16_t k16 = scale16_from_amax_bits<FMT>(ak);
-        const uint16_t v16 = scale16_from_amax_bits<FMT>(av);
-        if (cq == 0) {
-          s_sc[0][4 * tq + j] = k16;
-          s_sc[1][4 * tq + j] = v16;
-        }
-        dk = make_divisor((float)__builtin_bit_cast(_Float16, k16));
-        dv = make_divisor((float)__builtin_bit_cast(_Float16, v16));
+        cv[j] = quant4<FMT, PRE>(wv[jb][j], dv);
+        s_kt[(4 * tq + j) * kKRow + cq] = quant4<FMT, PRE>(wk[jb][j], dk);
       }
-      cv[j] = quant4<FMT>(wv[jb][j], dv);
-      s_kt[(4 * tq + j) * kKRow + cq] = quant4<FMT>(wk[jb][j], dk);
+      // rows cv[j] = token j, bytes = channels 4cq..4cq+3 -> one dword per channel
+      const uint32_t t0l = __builtin_amdgcn_perm(cv[1], cv[0], 0x05010400u);  // a0 b0 a1 b1
+      const uint32_t t1l = __builtin_amdgcn_perm(cv[1], cv[0], 0x07030602u);  // a2 b2 a3 b3
+      const uint32_t t2l = __builtin_amdgcn_perm(cv[3], cv[2], 0x05010400u);  // c0 d0 c1 d1
+      const uint32_t t3l = __builtin_amdgcn_perm(cv[3], cv[2], 0x07030602u);  // c2 d2 c3 d3
+      uint32_t* row = s_vt + (4 * cq) * kRowDw + tq;
+      row[0] = __builtin_amdgcn_perm(t2l, t0l, 0x05040100u);
+      row[kRowDw] = __builtin_amdgcn_perm(t2l, t0l, 0x07060302u);
+      row[2 * kRowDw] = __builtin_amdgcn_perm(t3l, t1l, 0x05040100u);
+      row[3 * kRowDw] = __builtin_amdgcn_perm(t3l, t1l, 0x07060302u);
     }
-    // rows cv[j] = token j, bytes = channels 4cq..4cq+3 -> one dword per channel
-    const uint32_t t0l = __builtin_amdgcn_perm(cv[1], cv[0], 0x05010400u);  // a0 b0 a1 b1
-    const uint32_t t1l = __builtin_amdgcn_perm(cv[1], cv[0], 0x07030602u);  // a2 b2 a3 b3
-    const uint32_t t2l = __builtin_amdgcn_perm(cv[3], cv[2], 0x05010400u);  // c0 d0 c1 d1
-    const uint32_t t3l = __builtin_amdgcn_perm(cv[3], cv[2], 0x07030602u);  // c2 d2 c3 d3
-    uint32_t* row = s_vt + (4 * cq) * kRowDw + tq;
-    row[0] = __builtin_amdgcn_perm(t2l, t0l, 0x05040100u);
-    row[kRowDw] = __builtin_amdgcn_perm(t2l, t0l, 0x07060302u);
-    row[2 * kRowDw] = __builtin_amdgcn_perm(t3l, t1l, 0x05040100u);
-    row[3 * kRowDw] = __builtin_amdgcn_perm(t3l, t1l, 0x07060302u);
-  }
+  };
+  if (TS || dk0.pre != 1.0f || dv0.pre != 1.0f)
+    quantize(std::integral_constant<bool, true>{});
+  else
+    quantize(std::integral_constant<bool, false>{});
   __syncthreads();
 
   if constexpr (TS) {
@@ -214,6 +246,20 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
                               q * (kBs * 16) + (s & (kBs - 1)) * 16) = w;
   }
 
+  // V of whole blocks: one 16-byte store per channel row
+  const int nfb = s_nfb;
+  for (int job = tid; job < nfb * DH; job += 256) {
+    const int c = job % DH;
+    const int i = s_fblk[job / DH];
+    const int64_t s = s_slot[i];
+    const uint32_t* row = s_vt + c * kRowDw + (i >> 2);
+    const uint32_t sh = (uint32_t)(i & 3);
+    const uint4 w = make_uint4(__builtin_amdgcn_alignbyte(row[1], row[0], sh),
+                               __builtin_amdgcn_alignbyte(row[2], row[1], sh),
+                               __builtin_amdgcn_alignbyte(row[3], row[2], sh),
+                               __builtin_amdgcn_alignbyte(row[4], row[3], sh));
+    *reinterpret_cast<uint4*>(vc + (size_t)(s >> 4) * bstride + ((size_t)h * DH + c) * kBs) = w;
+  }
   const int nrun = s_nrun;
   for (int job = tid; job < nrun * DH; job += 256) {
     const int c = job % DH;

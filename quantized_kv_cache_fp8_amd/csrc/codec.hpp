@@ -197,6 +197,41 @@ __device__ __forceinline__ float quotient(float x, const Divisor& d) {
   return quotient(x * d.pre, d.s, d.rs);
 }
 
+// The FP8 encoders' argument: fl32(x / s) clamped to +-max with NaN kept, the
+// same value as clamp_keep_nan(quotient(x, d), max) in fewer operations (8).
+// Where |x / s| >= 2^16 every later step saturates, so the first estimate is
+// clamped to +-2^16 before the correction step instead of being selected
+// after it: an infinite x then stays infinite (not NaN) through the
+// correction and clamps to +-max; below 2^16 the estimate is untouched and the
+// arithmetic is the quotient's.  NaN is restored from x at the end (the clamps
+// drop it).  PRE: the divisor carries the 2^64 prescale of tiny scales (a
+// caller whose scales are all at or above 2^-100 passes false and saves one
+// multiply per value).
+template <int FMT, bool PRE>
+__device__ __forceinline__ float fp8_arg(float x, const Divisor& d) {
+  const float xs = PRE ? x * d.pre : x;
+  const float q0 = __builtin_amdgcn_fmed3f(xs * d.rs, -65536.0f, 65536.0f);
+  const float e = __builtin_fmaf(-q0, d.s, xs);
+  const float q1 = __builtin_copysignf(__builtin_fmaf(e, d.rs, q0), xs);
+  constexpr float m = FmtTraits<FMT>::kMax;
+  const float c = __builtin_amdgcn_fmed3f(q1, -m, m);
+  return xs != xs ? xs : c;
+}
+
+// Four already clamped (or NaN) values -> four FP8 codes, little-endian.
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+  int w;
+  if constexpr (FMT == E4M3) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+  }
+  return (uint32_t)w;
+}
+
 // bf16 bit patterns packed two per dword -> fp32 (exact).
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
