@@ -131,6 +131,18 @@ kvq_status kvq_calibrate_scales(const void* x_bf16, int64_t T, int H, int dh, in
                                 int gran, float* amax_io, float* scale_out, int accumulate,
                                 kvq_stream stream);
 
+/* K and V calibrated together ([G] scale sources: k_scale and v_scale are
+ * fitted from the K and V activations of the same layer): exactly
+ *   kvq_calibrate_scales(k_bf16, ..., k_amax_io, k_scale_out, ...) and
+ *   kvq_calibrate_scales(v_bf16, ..., v_amax_io, v_scale_out, ...)
+ * (bit-identical results), with K and V of one shape [T][H][dh] sharing each
+ * of the three launches (clear, reduce, finalize) instead of taking three each.
+ * The four output arrays must not overlap.  Errors as kvq_calibrate_scales. */
+kvq_status kvq_calibrate_scales_kv(const void* k_bf16, const void* v_bf16, int64_t T, int H,
+                                   int dh, int fmt, int gran, float* k_amax_io, float* v_amax_io,
+                                   float* k_scale_out, float* v_scale_out, int accumulate,
+                                   kvq_stream stream);
+
 /* ---------------------------------------------------------------- quantize-write
  * Quantize-on-write into the paged cache ([T] 10.4.2 write rule, 10.4.5
  * cast_fp8(K / sK)):

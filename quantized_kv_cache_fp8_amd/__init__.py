@@ -33,7 +33,8 @@ EXPORTS = ["kvq_strerror", "kvq_kv_cache_bytes", "kvq_fp8_encode", "kvq_fp8_deco
            "kvq_decode_attn_token_scales", "kvq_kivi_quantize", "kvq_kivi_decode_workspace_size",
            "kvq_kivi_decode_attn", "kvq_cache_write_paged", "kvq_decode_attn_paged",
            "kvq_prefill_attn_paged", "kvq_layer_skipped", "kvq_layer_index", "kvq_page_bytes",
-           "kvq_common_page_bytes", "kvq_decode_attn_append", "kvq_decode_attn_append_noalloc"]
+           "kvq_common_page_bytes", "kvq_decode_attn_append", "kvq_decode_attn_append_noalloc",
+           "kvq_calibrate_scales_kv"]
 
 # bytes of the device scratch array of kvq_decode_attn_append_noalloc (KVQ_STATIC_SCRATCH_BYTES)
 STATIC_SCRATCH_BYTES = 16 << 20
@@ -65,6 +66,7 @@ def lib() -> ctypes.CDLL:
         L.kvq_fp8_encode.argtypes = [i32, P, i64, P, P]
         L.kvq_fp8_decode.argtypes = [i32, P, i64, P, P]
         L.kvq_calibrate_scales.argtypes = [P, i64, i32, i32, i32, i32, P, P, i32, P]
+        L.kvq_calibrate_scales_kv.argtypes = [P, P, i64, i32, i32, i32, i32, P, P, P, P, i32, P]
         L.kvq_cache_write.argtypes = [P, P, i64, i32, i32, P, P, P, i64, i32, P, P, i32, i32, P]
         L.kvq_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
         L.kvq_decode_workspace_size.restype = sz
@@ -268,6 +270,24 @@ def kvq_calibrate_scales(x, fmt, gran, amax_io, scale_out, accumulate=False, str
            lib().kvq_calibrate_scales(_ptr(x, "bf16"), T, H, dh, _fmt(fmt), _gran(gran),
                                       _ptr(amax_io, "f32"), _ptr(scale_out, "f32"),
                                       int(bool(accumulate)), _stream(stream)))
+
+
+def kvq_calibrate_scales_kv(k, v, fmt, gran, k_amax_io, v_amax_io, k_scale_out, v_scale_out,
+                            accumulate=False, stream=None) -> None:
+    """k, v: bf16 [T, H, dh] of one shape; the four arrays fp32 [1] or [H]."""
+    if k.dim() != 3 or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"kvq: k and v must be [T, H, dh] of one shape, got {tuple(k.shape)} "
+                         f"and {tuple(v.shape)}")
+    T, H, dh = k.shape
+    for name, a in (("k_amax_io", k_amax_io), ("v_amax_io", v_amax_io),
+                    ("k_scale_out", k_scale_out), ("v_scale_out", v_scale_out)):
+        _scales(name, a, gran, H)
+    _check("kvq_calibrate_scales_kv",
+           lib().kvq_calibrate_scales_kv(_ptr(k, "bf16"), _ptr(v, "bf16"), T, H, dh, _fmt(fmt),
+                                         _gran(gran), _ptr(k_amax_io, "f32"),
+                                         _ptr(v_amax_io, "f32"), _ptr(k_scale_out, "f32"),
+                                         _ptr(v_scale_out, "f32"), int(bool(accumulate)),
+                                         _stream(stream)))
 
 
 def kvq_cache_write(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, fmt, gran,

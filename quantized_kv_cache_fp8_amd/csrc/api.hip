@@ -109,6 +109,22 @@ kvq_status kvq_calibrate_scales(const void* x_bf16, int64_t T, int H, int dh, in
                                   (hipStream_t)stream));
 }
 
+kvq_status kvq_calibrate_scales_kv(const void* k_bf16, const void* v_bf16, int64_t T, int H,
+                                   int dh, int fmt, int gran, float* k_amax_io, float* v_amax_io,
+                                   float* k_scale_out, float* v_scale_out, int accumulate,
+                                   kvq_stream stream) {
+  if (!fmt_ok(fmt) || !gran_ok(gran)) return KVQ_ERR_UNSUPPORTED;
+  if (T < 0 || H < 1 || H > 65535 || dh < 8 || dh % 8 || dh > 2048) return KVQ_ERR_SHAPE;
+  if (!k_amax_io || !v_amax_io || !k_scale_out || !v_scale_out) return KVQ_ERR_NULL;
+  if (T > 0 && (!k_bf16 || !v_bf16)) return KVQ_ERR_NULL;
+  if (T > 0 && (!aligned(k_bf16, 16) || !aligned(v_bf16, 16))) return KVQ_ERR_UNSUPPORTED;
+  const uint16_t* x[2] = {(const uint16_t*)k_bf16, (const uint16_t*)v_bf16};
+  float* amax[2] = {k_amax_io, v_amax_io};
+  float* scale[2] = {k_scale_out, v_scale_out};
+  return map_err(launch_calibrate_n(x, 2, T, H, dh, fmt, gran == KVQ_SCALE_HEAD, amax, scale,
+                                    accumulate, (hipStream_t)stream));
+}
+
 // block_stride: validated against the natural Hkv * bs * dh after the sizes
 static kvq_status check_stride(int64_t block_stride, int Hkv, int bs, int dh) {
   if (block_stride < (int64_t)Hkv * bs * dh) return KVQ_ERR_SHAPE;

@@ -18,9 +18,16 @@ namespace kvq {
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-__global__ void amax_clear_kernel(uint32_t* amax, int n) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) amax[i] = 0u;
+// up to two tensors per launch (K and V calibrated together share every
+// launch); tensor j's arrays are amax[j] / scale[j]
+struct CalibArrays {
+  uint32_t* amax[2];
+  float* scale[2];
+};
+
+__global__ void amax_clear_kernel(CalibArrays a, int n, int ntensors) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n * ntensors) a.amax[i / n][i % n] = 0u;
 }
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
@@ -91,16 +98,21 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
 // Four units are read per step (4 J loads in flight per thread), with
 // nontemporal loads: every byte is read once.
 template <int J>
-__global__ __launch_bounds__(256) void amax_contig_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256) void amax_contig_kernel(const uint16_t* __restrict__ x0,
+                                                          const uint16_t* __restrict__ x1,
                                                           int64_t nchunks, int64_t nunits,
                                                           int H, int dh, int per_head,
-                                                          uint32_t* __restrict__ amax) {
+                                                          CalibArrays arr, uint32_t gpt) {
   __shared__ uint32_t red[256];
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  // gpt workgroups per tensor: the first gpt scan x0, the next gpt x1
+  const uint32_t tj = blockIdx.x / gpt, wb = blockIdx.x - tj * gpt;
+  const uint16_t* __restrict__ x = tj ? x1 : x0;
+  uint32_t* __restrict__ amax = arr.amax[tj];
   const int t = threadIdx.x;
   red[t] = 0u;
   const int cpr = dh >> 3;
-  const int64_t u0 = nunits * blockIdx.x / gridDim.x, u1 = nunits * (blockIdx.x + 1) / gridDim.x;
+  const int64_t u0 = nunits * wb / gpt, u1 = nunits * (wb + 1) / gpt;
   const u32x4* src = reinterpret_cast<const u32x4*>(x);
   u16x2 acc[J];
 #pragma unroll
@@ -142,56 +154,76 @@ __global__ __launch_bounds__(256) void amax_contig_kernel(const uint16_t* __rest
 }
 
 template <int FMT>
-__global__ void scale_finalize_kernel(const uint32_t* __restrict__ amax, float* __restrict__ scale,
-                                      int n) {
+__global__ void scale_finalize_kernel(CalibArrays arr, int n, int ntensors) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+  if (i >= n * ntensors) return;
+  float* __restrict__ scale = arr.scale[i / n];
+  const uint32_t* __restrict__ amax = arr.amax[i / n];
+  i %= n;
   float a = __uint_as_float(amax[i]);
   // finite and > 0 -> correctly rounded amax / fmax; otherwise 1.0
   bool ok = a > 0.0f && a <= 3.4028234663852886e38f;
   scale[i] = ok ? __fdiv_rn(a, FmtTraits<FMT>::kMax) : 1.0f;
 }
 
-hipError_t launch_calibrate(const uint16_t* x, int64_t T, int H, int dh, int fmt, int per_head,
-                            float* amax_io, float* scale_out, int accumulate, hipStream_t s) {
+// x[j], amax_io[j], scale_out[j] for j < ntensors (1 or 2): every tensor has
+// the shape [T][H][dh]; three launches in all (clear unless accumulating,
+// reduce, finalize)
+hipError_t launch_calibrate_n(const uint16_t* const* x, int ntensors, int64_t T, int H, int dh,
+                              int fmt, int per_head, float* const* amax_io,
+                              float* const* scale_out, int accumulate, hipStream_t s) {
   const int n = per_head ? H : 1;
-  uint32_t* amax = reinterpret_cast<uint32_t*>(amax_io);
-  if (!accumulate) amax_clear_kernel<<<(n + 255) / 256, 256, 0, s>>>(amax, n);
+  CalibArrays arr;
+  for (int j = 0; j < 2; ++j) {
+    const int jj = j < ntensors ? j : 0;
+    arr.amax[j] = reinterpret_cast<uint32_t*>(amax_io[jj]);
+    arr.scale[j] = scale_out[jj];
+  }
+  if (!accumulate)
+    amax_clear_kernel<<<(n * ntensors + 255) / 256, 256, 0, s>>>(arr, n, ntensors);
   if (T > 0) {
     const int64_t nchunks = T * H * (dh >> 3);
     const int64_t cpt = (int64_t)H * (dh >> 3);  // chunks per token: the stride's unit
     const int64_t lcm = cpt % 256 == 0 ? cpt : cpt * 256 / gcd64(cpt, 256);
     const int J = (int)(lcm / 256);
     if ((J == 1 || J == 2 || J == 4) && (!per_head || H <= 256)) {
-      // contiguous ranges: about 8 workgroups per CU, at least 4 units each
+      // contiguous ranges: about 8 workgroups per CU in all, at least 4 units each
       const int64_t nunits = (nchunks + 256 * J - 1) / (256 * J);
-      int64_t g = (int64_t)device_cu_count() * 8;
+      int64_t g = (int64_t)device_cu_count() * 8 / ntensors;
       if (g > (nunits + 3) / 4) g = (nunits + 3) / 4;
       if (g < 1) g = 1;
+      const uint16_t* x1 = ntensors > 1 ? x[1] : x[0];
+      const uint32_t grid = (uint32_t)(g * ntensors);
       if (J == 1)
-        amax_contig_kernel<1><<<(uint32_t)g, 256, 0, s>>>(x, nchunks, nunits, H, dh, per_head,
-                                                          amax);
+        amax_contig_kernel<1><<<grid, 256, 0, s>>>(x[0], x1, nchunks, nunits, H, dh, per_head,
+                                                   arr, (uint32_t)g);
       else if (J == 2)
-        amax_contig_kernel<2><<<(uint32_t)g, 256, 0, s>>>(x, nchunks, nunits, H, dh, per_head,
-                                                          amax);
+        amax_contig_kernel<2><<<grid, 256, 0, s>>>(x[0], x1, nchunks, nunits, H, dh, per_head,
+                                                   arr, (uint32_t)g);
       else
-        amax_contig_kernel<4><<<(uint32_t)g, 256, 0, s>>>(x, nchunks, nunits, H, dh, per_head,
-                                                          amax);
+        amax_contig_kernel<4><<<grid, 256, 0, s>>>(x[0], x1, nchunks, nunits, H, dh, per_head,
+                                                   arr, (uint32_t)g);
     } else {
-    // about 8 workgroups per CU, the grid's thread count a multiple of cpt
-    int64_t threads = (int64_t)device_cu_count() * 8 * 256;
-    const int64_t unit = cpt % 256 == 0 ? cpt : cpt * 256 / gcd64(cpt, 256);  // lcm(cpt, 256)
-    threads = (threads + unit - 1) / unit * unit;
-    const int64_t need = (nchunks + 255) / 256 * 256;
-    if (threads > need) threads = (need + unit - 1) / unit * unit;
-    amax_kernel<<<(uint32_t)(threads / 256), 256, 0, s>>>(x, nchunks, H, dh, per_head, threads,
-                                                          amax);
+      // about 8 workgroups per CU, the grid's thread count a multiple of cpt
+      int64_t threads = (int64_t)device_cu_count() * 8 * 256;
+      threads = (threads + lcm - 1) / lcm * lcm;
+      const int64_t need = (nchunks + 255) / 256 * 256;
+      if (threads > need) threads = (need + lcm - 1) / lcm * lcm;
+      for (int j = 0; j < ntensors; ++j)
+        amax_kernel<<<(uint32_t)(threads / 256), 256, 0, s>>>(x[j], nchunks, H, dh, per_head,
+                                                              threads, arr.amax[j]);
     }
   }
   dispatch_fmt(fmt, [&](auto f) {
-    scale_finalize_kernel<decltype(f)::value><<<(n + 255) / 256, 256, 0, s>>>(amax, scale_out, n);
+    scale_finalize_kernel<decltype(f)::value>
+        <<<(n * ntensors + 255) / 256, 256, 0, s>>>(arr, n, ntensors);
   });
   return hipGetLastError();
+}
+
+hipError_t launch_calibrate(const uint16_t* x, int64_t T, int H, int dh, int fmt, int per_head,
+                            float* amax_io, float* scale_out, int accumulate, hipStream_t s) {
+  return launch_calibrate_n(&x, 1, T, H, dh, fmt, per_head, &amax_io, &scale_out, accumulate, s);
 }
 
 }  // namespace kvq

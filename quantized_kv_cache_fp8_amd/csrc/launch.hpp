@@ -17,6 +17,10 @@ hipError_t launch_fp8_decode(int fmt, const uint8_t* c, int64_t n, float* out, h
 
 hipError_t launch_calibrate(const uint16_t* x, int64_t T, int H, int dh, int fmt, int per_head,
                             float* amax_io, float* scale_out, int accumulate, hipStream_t s);
+// the same for ntensors (1 or 2) tensors of one shape, sharing every launch
+hipError_t launch_calibrate_n(const uint16_t* const* x, int ntensors, int64_t T, int H, int dh,
+                              int fmt, int per_head, float* const* amax_io,
+                              float* const* scale_out, int accumulate, hipStream_t s);
 
 hipError_t launch_cache_write(const uint16_t* k, const uint16_t* v, int64_t T, int Hkv, int dh,
                               const int64_t* slot, uint8_t* kc, uint8_t* vc, int64_t num_blocks,

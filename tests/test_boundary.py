@@ -99,6 +99,12 @@ def test_calibrate_and_codec_validation():
     assert L.kvq_calibrate_scales(FAKE, -4, 2, 128, 0, 0, FAKE, FAKE, 0, None) == -2
     assert L.kvq_calibrate_scales(FAKE, 4, 2, 12, 0, 0, FAKE, FAKE, 0, None) == -2
     assert L.kvq_calibrate_scales(FAKE, 4, 2, 128, 3, 0, FAKE, FAKE, 0, None) == -3
+    kv = L.kvq_calibrate_scales_kv
+    assert kv(FAKE, FAKE, 4, 2, 128, 0, 0, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert kv(FAKE, None, 4, 2, 128, 0, 0, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
+    assert kv(FAKE, FAKE, -1, 2, 128, 0, 0, FAKE, FAKE, FAKE, FAKE, 0, None) == -2
+    assert kv(FAKE, FAKE, 4, 0, 128, 0, 0, FAKE, FAKE, FAKE, FAKE, 0, None) == -2
+    assert kv(FAKE, FAKE, 4, 2, 128, 0, 7, FAKE, FAKE, FAKE, FAKE, 0, None) == -3
     assert L.kvq_fp8_encode(0, None, 8, FAKE, None) == -1
     assert L.kvq_fp8_encode(0, FAKE, -8, FAKE, None) == -2
     assert L.kvq_fp8_encode(0, FAKE, 0, FAKE, None) == 0
@@ -330,6 +336,10 @@ def test_binding_checks_calibrate_and_kivi_shapes():
     x = torch.zeros(4, 2, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="scale_out"):
         K.kvq_calibrate_scales(x, "e4m3", "head", torch.zeros(2), torch.zeros(1))
+    with pytest.raises(ValueError, match="one shape"):
+        K.kvq_calibrate_scales_kv(x, x[:2], "e4m3", "tensor", *[torch.zeros(1)] * 4)
+    with pytest.raises(ValueError, match="v_scale_out"):
+        K.kvq_calibrate_scales_kv(x, x, "e4m3", "head", *[torch.zeros(2)] * 3, torch.zeros(1))
     k = torch.zeros(64, 2, 128, dtype=torch.bfloat16)
     cache = torch.zeros(4, 2, K.KIVI_TILE, dtype=torch.uint8)
     with pytest.raises(ValueError, match="group_blocks"):

@@ -155,6 +155,40 @@ def test_calibrate_matches_oracle(fmt, gran, shape):
     assert same_f32(ga, ra) and same_f32(gs, rs)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("gran", [oracle.GRAN_TENSOR, oracle.GRAN_HEAD])
+@pytest.mark.parametrize("shape", [(1, 1, 64), (333, 6, 64), (4099, 8, 128), (7, 300, 64),
+                                   (0, 3, 64)])
+def test_calibrate_kv_equals_two_calls(fmt, gran, shape):
+    """K and V in one call: both results match the oracle per tensor and are
+    bit-identical to two single calls; accumulation continues both."""
+    import torch
+    import quantized_kv_cache_fp8_amd as K
+    g = W.rng(900 + sum(shape) + fmt)
+    k = W.normal_bf16(g, shape, 1, W.log_uniform(g, shape[1], 0.5, 20.0), g.choice(shape[2], 2), 10.0)
+    v = W.normal_bf16(g, shape, 1, W.log_uniform(g, shape[1], 1e-3, 5.0))
+    if shape[0] > 5:
+        v[5, 0, 3] = 0x7FC0  # a NaN in V only
+    n = shape[1] if gran == oracle.GRAN_HEAD else 1
+    arrs = [torch.full((n,), 12345.0, device="cuda:0") for _ in range(4)]
+    K.kvq_calibrate_scales_kv(to_dev(k), to_dev(v), fmt, gran, *arrs)
+    torch.cuda.synchronize()
+    ka, va, ks, vs = (to_np(a) for a in arrs)
+    for x, a, sc in ((k, ka, ks), (v, va, vs)):
+        ra, rs = oracle.calibrate(x, fmt, gran)
+        assert same_f32(a, ra) and same_f32(sc, rs)
+        ga, gs = gpu_calibrate(x, fmt, gran)
+        assert same_f32(a, ga) and same_f32(sc, gs)
+    # a second batch accumulates into both
+    k2 = W.normal_bf16(g, (9,) + shape[1:], 1, np.full(shape[1], 30.0))
+    v2 = W.normal_bf16(g, (9,) + shape[1:], 1, np.full(shape[1], 0.01))
+    K.kvq_calibrate_scales_kv(to_dev(k2), to_dev(v2), fmt, gran, *arrs, accumulate=True)
+    torch.cuda.synchronize()
+    for x, x2, a, sc in ((k, k2, arrs[0], arrs[2]), (v, v2, arrs[1], arrs[3])):
+        ra, rs = oracle.calibrate(np.concatenate([x, x2]), fmt, gran)
+        assert same_f32(to_np(a), ra) and same_f32(to_np(sc), rs)
+
+
 def test_calibrate_accumulates_across_batches():
     g = W.rng(8)
     a = W.normal_bf16(g, (100, 4, 64), 1, np.array([1, 2, 3, 4.0]))
