@@ -16,9 +16,10 @@
 //   1. The chunk's slots go to LDS; wave 0 marks the start of every run of
 //      tokens whose slots are consecutive inside one aligned group of four
 //      slots ("quad"), with the run's length (1..4).
-//   2. Every thread quantizes 4 tokens x 4 channels of K and V (bf16 loads of
-//      consecutive threads are one row; they are issued before step 1's
-//      barrier, since they do not depend on the slots).  K codes are parked
+//   2. Every thread quantizes 4 tokens x 4 channels (dh 64) or 4 tokens x 8
+//      channels (dh 128, one 16-byte bf16 load per token row) of K and V;
+//      the lanes of a token row are consecutive, and the loads are issued
+//      before step 1's barrier, since they do not depend on the slots.  K codes are parked
 //      in an LDS tile [64 tokens][dh]; the 4x4 V code block is transposed
 //      with v_perm_b32 and parked in an LDS tile [dh][64 tokens].
 //   3. K: for each valid token and 16-channel chunk one thread stores the 16
@@ -122,22 +123,33 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   // the bf16 loads do not depend on the slots: issue them first so both
   // latencies overlap (tokens past T read nothing)
   constexpr int kJobs = (kChunk / 4) * kCq / 256;  // 4x4 jobs per thread
+  // with two jobs a thread takes channel quads 2 c and 2 c + 1 of token quad
+  // tq (one 16-byte load per token row); with one, quad c of token quad tq
+  constexpr int kRowLanes = kCq / kJobs;  // lanes holding one token row
+  const int co = tid % kRowLanes, tqs = tid / kRowLanes;
+  auto job_cq = [&](int jb) { return kJobs * co + jb; };
   uint2 wk[kJobs][4], wv[kJobs][4];
 #pragma unroll
-  for (int jb = 0; jb < kJobs; ++jb) {
-    const int job = tid + 256 * jb;
-    const int cq = job % kCq, tq = job / kCq;
+  for (int j = 0; j < 4; ++j) {
+    const int64_t t = t0 + 4 * tqs + j;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t t = t0 + 4 * tq + j;
-      wk[jb][j] = wv[jb][j] = make_uint2(0, 0);
-      if (t < T) {
-        const size_t src = ((size_t)t * Hkv + h) * DH + cq * 4;
-        wk[jb][j] = *reinterpret_cast<const uint2*>(k + src);
-        wv[jb][j] = *reinterpret_cast<const uint2*>(v + src);
+    for (int jb = 0; jb < kJobs; ++jb) wk[jb][j] = wv[jb][j] = make_uint2(0, 0);
+    if (t < T) {
+      const size_t src = ((size_t)t * Hkv + h) * DH + co * 4 * kJobs;
+      if constexpr (kJobs == 2) {
+        const uint4 a = *reinterpret_cast<const uint4*>(k + src);
+        const uint4 b = *reinterpret_cast<const uint4*>(v + src);
+        wk[0][j] = make_uint2(a.x, a.y);
+        wk[1][j] = make_uint2(a.z, a.w);
+        wv[0][j] = make_uint2(b.x, b.y);
+        wv[1][j] = make_uint2(b.z, b.w);
+      } else {
+        wk[0][j] = *reinterpret_cast<const uint2*>(k + src);
+        wv[0][j] = *reinterpret_cast<const uint2*>(v + src);
       }
     }
   }
+  static_assert(kJobs == 1 || kJobs == 2, "one or two jobs per thread");
   if (tid < kChunk) {
     const int64_t t = t0 + tid;
     int64_t s = t < T ? slot_mapping[t] : -1;
@@ -182,30 +194,44 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   auto quantize = [&](auto pre_tag) {
     constexpr bool PRE = decltype(pre_tag)::value;
     Divisor dk = dk0, dv = dv0;
+    // per-token-head scales: the kRowLanes aligned consecutive lanes of token
+    // 4 tq + j hold its row (all of the thread's jobs)
+    Divisor tdk[4], tdv[4];
+    if constexpr (TS) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t ak = 0, av = 0;
+#pragma unroll
+        for (int jb = 0; jb < kJobs; ++jb) {
+          const uint32_t xk = absmax_bits4(wk[jb][j]), xv = absmax_bits4(wv[jb][j]);
+          ak = ak > xk ? ak : xk;
+          av = av > xv ? av : xv;
+        }
+#pragma unroll
+        for (int o = 1; o < kRowLanes; o <<= 1) {
+          const uint32_t xk = __shfl_xor(ak, o), xv = __shfl_xor(av, o);
+          ak = ak > xk ? ak : xk;
+          av = av > xv ? av : xv;
+        }
+        const uint16_t k16 = scale16_from_amax_bits<FMT>(ak);
+        const uint16_t v16 = scale16_from_amax_bits<FMT>(av);
+        if (co == 0) {
+          s_sc[0][4 * tqs + j] = k16;
+          s_sc[1][4 * tqs + j] = v16;
+        }
+        tdk[j] = make_divisor((float)__builtin_bit_cast(_Float16, k16));
+        tdv[j] = make_divisor((float)__builtin_bit_cast(_Float16, v16));
+      }
+    }
 #pragma unroll
     for (int jb = 0; jb < kJobs; ++jb) {
-      const int job = tid + 256 * jb;
-      const int cq = job % kCq, tq = job / kCq;
+      const int cq = job_cq(jb), tq = tqs;
       uint32_t cv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if constexpr (TS) {
-          // the kCq aligned consecutive lanes of token 4 tq + j hold its row
-          uint32_t ak = absmax_bits4(wk[jb][j]), av = absmax_bits4(wv[jb][j]);
-#pragma unroll
-          for (int o = 1; o < kCq; o <<= 1) {
-            const uint32_t xk = __shfl_xor(ak, o), xv = __shfl_xor(av, o);
-            ak = ak > xk ? ak : xk;
-            av = av > xv ? av : xv;
-          }
-          const uint16_t k16 = scale16_from_amax_bits<FMT>(ak);
-          const uint16_t v16 = scale16_from_amax_bits<FMT>(av);
-          if (cq == 0) {
-            s_sc[0][4 * tq + j] = k16;
-            s_sc[1][4 * tq + j] = v16;
-          }
-          dk = make_divisor((float)__builtin_bit_cast(_Float16, k16));
-          dv = make_divisor((float)__builtin_bit_cast(_Float16, v16));
+          dk = tdk[j];
+          dv = tdv[j];
         }
         cv[j] = quant4<FMT, PRE>(wv[jb][j], dv);
         s_kt[(4 * tq + j) * kKRow + cq] = quant4<FMT, PRE>(wk[jb][j], dk);
