@@ -116,6 +116,9 @@ __device__ __forceinline__ void append_prologue(
   p_new = bi >> 1;
   e_new = bi & 1;
   off_new = (ctx - 1) & (kBlockSize - 1);
+  // the block id goes out with the token's values (it does not depend on
+  // them), so the store below waits for one memory round trip, not two
+  const int64_t raw = btab[bi];
   for (int i = tid; i < 2 * DH; i += NT) {
     const bool isv = i >= DH;
     const int d = isv ? i - DH : i;
@@ -125,7 +128,6 @@ __device__ __forceinline__ void append_prologue(
     pw[i] = (uint8_t)(enc2<FMT>(qv, qv) & 0xffu);
   }
   __syncthreads();
-  const int64_t raw = btab[bi];
   if (writer && raw >= 0 && raw < num_blocks) {
     uint8_t* kt = kc_w + (size_t)raw * bstride + (size_t)h * tile;
     uint8_t* vt = vc_w + (size_t)raw * bstride + (size_t)h * tile;
