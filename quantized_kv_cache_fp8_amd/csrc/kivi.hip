@@ -562,8 +562,12 @@ kivi_decode_split_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
 
 // ---------------------------------------------------------------- launchers
 // Workgroups the quantized splits should at least give (the split shrinks,
-// from 32 groups down to 4, until they do).
-constexpr int kKiviMinWgs = 2048;
+// from 32 groups down to 4, until they do).  About one round of resident
+// workgroups (5 per CU): fewer, longer workgroups amortize each one's start
+// (q staging, the block ids, the first group's latency).  On 8 x 16384 tokens
+// 32-group splits (1088 workgroups) measured 34.1-37.0 us against 35.5-40.5
+// for 16-group ones (2112), in five alternating rounds on one box.
+constexpr int kKiviMinWgs = 1024;
 
 KiviPlan kivi_decode_plan(int B, int Hq, int Hkv, int max_groups) {
   KiviPlan p{};
