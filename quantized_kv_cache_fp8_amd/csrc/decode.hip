@@ -49,6 +49,12 @@ constexpr int kCombineHeadsPerWg = 4;
 // largest split (cache blocks per workgroup); smaller splits are taken only
 // when the grid would otherwise have too few workgroups
 constexpr int kMaxSplitBlocks = 32;
+// a split kernel instance covers 8 N blocks (4 waves, N block pairs each),
+// N in {1, 2, 4, 8}; the plan halves the split from the maximum, so the
+// maximum must be one of those sizes
+static_assert(kMaxSplitBlocks == 8 || kMaxSplitBlocks == 16 || kMaxSplitBlocks == 32 ||
+                  kMaxSplitBlocks == 64,
+              "split sizes are 8, 16, 32 or 64 blocks");
 // waves per SIMD of the generic split kernel: its whole state (Q operand, one
 // block pair of codes, the O tile) fits in 128 registers
 constexpr int kWavesPerSimd = 4;
@@ -982,6 +988,10 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
     else if (plan.part_blocks == 16) KVQ_SPLIT_HP(F, D, 2);   \
     else KVQ_SPLIT_HP(F, D, 1);                               \
   } while (0)
+    // any other split size would cover only part of each split
+    if (plan.part_blocks != 8 && plan.part_blocks != 16 && plan.part_blocks != 32 &&
+        plan.part_blocks != 64)
+      return hipErrorInvalidValue;
     dispatch_fmt(fmt, [&](auto f) {
       constexpr int F = decltype(f)::value;
       if (dh == 128) KVQ_SPLIT_NP(F, 128); else KVQ_SPLIT_NP(F, 64);
