@@ -372,7 +372,7 @@ def kivi_rows(K, W, torch, dev, stream, reps=50):
     def call(i):
         K.kvq_kivi_decode_attn(out, q, caches[i % len(caches)], bt, qg, mg, rk, rv, rl,
                                workspace=ws)
-    ms = time_rotating(torch, stream, call, reps)
+    ms = time_rotating(torch, stream, call, 2 * reps, warm=20)
     # algorithmic bytes: every quantized tile once, the residual once
     nbytes = (int(kw.quant_groups.sum()) * kw.Hkv * K.KIVI_TILE +
               int(kw.res_lens.sum()) * kw.Hkv * 128 * 2 * 2)
