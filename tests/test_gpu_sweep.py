@@ -89,3 +89,34 @@ def test_prefill_sweep(case):
     e, er = rel_err(out, ref), row_rel_err(out, ref)
     print(f"global rel err {e:.3e}  worst row {er:.3e}", flush=True)
     assert e <= ATTN_TOL
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_kivi_sweep(case):
+    """KIVI 2-bit path: tiles bit-exact, decode within 2e-3 globally and per row,
+    over random group counts (none, one, split boundaries), residual lengths
+    and capacities, and head layouts."""
+    from test_gpu_kivi import gpu_cache, oracle_cache, oracle_decode, run_decode
+    g = np.random.default_rng(SWEEP_SEED + 90 + case)
+    Hkv = int(g.choice([1, 2, 4, 8]))
+    G = int(g.choice([1, 2, 3, 4]))
+    B = int(g.integers(1, 6))
+    R = int(g.choice([1, 32, 128, 256]))
+    qg = g.integers(0, 80, size=B)
+    qg[g.random(B) < 0.25] = 0
+    qg[g.random(B) < 0.2] = 32  # a split boundary
+    rl = g.integers(0, R + 1, size=B)
+    if (qg + rl).max() == 0:
+        qg[0] = 3
+    print(f"case {case}: B={B} Hq={G * Hkv} Hkv={Hkv} R={R} groups={qg.tolist()} "
+          f"residual={rl.tolist()}", flush=True)
+    wl = W.kivi_workload(f"ksweep{case}", SWEEP_SEED + 190 + case, G * Hkv, Hkv, qg, rl, R=R)
+    assert np.array_equal(to_np(gpu_cache(wl)), oracle_cache(wl))
+    out = run_decode(wl)
+    ref = oracle_decode(wl).reshape(out.shape)
+    empty = (qg + rl) == 0
+    assert not out[empty].any(), "an empty sequence must give zero rows"
+    o, r = out[~empty], ref[~empty]
+    e, er = rel_err(o, r), row_rel_err(o, r)
+    print(f"global rel err {e:.3e}  worst row {er:.3e}", flush=True)
+    assert e <= ATTN_TOL and er <= ATTN_TOL
