@@ -166,7 +166,9 @@ kvq_status kvq_cache_write(const void* k_bf16, const void* v_bf16, int64_t T, in
 
 /* ---------------------------------------------------------------- decode
  * Bytes of device workspace kvq_decode_attn needs for these sizes (split-K
- * partial results).  Returns 0 for invalid sizes. */
+ * partial results).  Returns 0 for invalid sizes.  The size never decreases as
+ * max_context_len grows (B, Hq, dh and bs fixed), so a workspace sized for the
+ * longest context serves every shorter call. */
 size_t kvq_decode_workspace_size(int B, int Hq, int dh, int max_context_len, int bs);
 
 /* Paged decode attention over the FP8 cache with the dequantization fused in
@@ -391,7 +393,7 @@ kvq_status kvq_decode_attn_append(void* out, int out_dtype, const void* q_bf16,
  * up on the first call made with that device current.
  * Limit: calls whose kvq_decode_workspace_size(B, Hq, dh, max_context_len, bs)
  * exceeds KVQ_STATIC_SCRATCH_BYTES return KVQ_ERR_SCRATCH before any device
- * work (B = 32, Hq = 32, dh = 128, bs = 16 fits up to max_context_len = 15872).
+ * work (B = 32, Hq = 32, dh = 128, bs = 16 fits up to max_context_len = 19840).
  * Every call on a GPU shares that GPU's array, which keeps the last call's
  * contents (no call reads what another left there): calls that overlap in
  * time on one GPU -- on different streams, or from different threads -- race

@@ -10,10 +10,11 @@
 // into registers, are converted there (exactly: every E4M3/E5M2 value is a
 // bf16 and an f16 value) and feed the matrix cores.
 //
-// Work decomposition (flash-decoding): grid = (nsplit, Hq / NH, B).  A
-// workgroup of 4 waves owns one split (part_blocks cache blocks of 16 tokens)
-// of one sequence and the NH <= 16 query heads that share one KV head, so
-// every K/V byte is read from HBM once and serves all NH heads.  Wave w takes
+// Work decomposition (flash-decoding): grid = (Hq / NH, nsplit, B), head
+// groups fastest.  A workgroup of 4 waves owns one split (part_blocks cache
+// blocks of 16 tokens) of one sequence and the NH <= 16 query heads that share
+// one KV head, so every K/V byte is read from HBM once and serves all NH
+// heads.  Wave w takes
 // block pairs w, w + 4, ... of the split, one pair (32 tokens) per step:
 //
 //   S = Q K^T on v_mfma_f32_16x16x32_bf16: A = the NH query rows (bf16, rows
@@ -46,15 +47,14 @@ namespace kvq {
 // Llama-3-8B-shaped layer):
 // query heads per combine workgroup (when it divides Hq)
 constexpr int kCombineHeadsPerWg = 4;
-// largest split (cache blocks per workgroup); smaller splits are taken only
-// when the grid would otherwise have too few workgroups
-constexpr int kMaxSplitBlocks = 32;
-// a split kernel instance covers 8 N blocks (4 waves, N block pairs each),
-// N in {1, 2, 4, 8}; the plan halves the split from the maximum, so the
-// maximum must be one of those sizes
-static_assert(kMaxSplitBlocks == 8 || kMaxSplitBlocks == 16 || kMaxSplitBlocks == 32 ||
-                  kMaxSplitBlocks == 64,
-              "split sizes are 8, 16, 32 or 64 blocks");
+// split sizes (cache blocks per workgroup), largest first: the plan takes the
+// first that still gives the grid enough workgroups to fill the chip, so
+// smaller splits are taken only for short contexts or small batches.  A split
+// kernel instance covers 8 N blocks (4 waves, N block pairs each), and one is
+// built for each of these sizes.
+constexpr int kSplitBlocks[] = {40, 32, 16, 8};
+// workgroups a plan aims for (about 1.6 rounds of resident workgroups)
+constexpr int64_t kFillWgs = 2048;
 // waves per SIMD of the generic split kernel: its whole state (Q operand, one
 // block pair of codes, the O tile) fits in 128 registers
 constexpr int kWavesPerSimd = 4;
@@ -926,12 +926,32 @@ DecodePlan decode_plan(int B, int Hq, int dh, int max_context_len, int bs) {
   if (B < 1 || Hq < 1 || dh < 1 || bs < 1 || max_context_len < 0) return p;
   const int64_t nb = ((int64_t)max_context_len + bs - 1) / bs;
   const int64_t groups = (int64_t)B * (Hq >= 4 ? Hq / 4 : 1);
-  int P = kMaxSplitBlocks;
-  // shrink the split until the grid has enough workgroups to fill the chip
-  while (P > 8 && groups * ((nb + P - 1) / P) < 2048) P >>= 1;
+  // splits per sequence that give the grid kFillWgs workgroups
+  const int64_t fill = (kFillWgs + groups - 1) / groups;
+  // the largest split that still fills the chip (8 blocks if none does).
+  // 40-block splits first: 49.9 against 50.4 us per step for 32 on the
+  // Llama-shaped layer (ragged contexts up to 8192), 93.2 against 94.5 us on
+  // 32 x 8192 tokens (best of seven alternating rounds); 48 and 56 blocks gain
+  // less on the ragged layer, 24 loses everywhere.
+  int P = 8;
+  for (int c : kSplitBlocks)
+    if ((nb + c - 1) / c >= fill) {
+      P = c;
+      break;
+    }
   p.part_blocks = P;
   p.nsplit = (int)(nb > 0 ? (nb + P - 1) / P : 1);
-  p.ws_bytes = (size_t)B * Hq * p.nsplit * (2 + dh) * sizeof(float);
+  // The workspace holds the most splits any max_context_len up to this one
+  // plans, so a workspace sized for the longest context serves every shorter
+  // call: a shorter context can take a smaller split and so more splits.
+  // Below the 16-block threshold, 16 (fill - 1) blocks, the plan takes 8-block
+  // splits, ceil(nb / 8) of them; above it no plan exceeds 2 (fill - 1) splits
+  // save its own (a 16-block plan stops at 32 (fill - 1) blocks, a 32-block
+  // plan at 40 (fill - 1)).
+  int64_t ws_splits = p.nsplit;
+  const int64_t short_splits = (nb + 7) / 8 < 2 * (fill - 1) ? (nb + 7) / 8 : 2 * (fill - 1);
+  if (short_splits > ws_splits) ws_splits = short_splits;
+  p.ws_bytes = (size_t)B * Hq * (size_t)ws_splits * (2 + dh) * sizeof(float);
   return p;
 }
 
@@ -983,14 +1003,14 @@ hipError_t launch_decode(void* out, int out_bf16, const uint16_t* q, const uint8
   } while (0)
 #define KVQ_SPLIT_NP(F, D)                                    \
   do {                                                        \
-    if (plan.part_blocks == 64) KVQ_SPLIT_HP(F, D, 8);        \
+    if (plan.part_blocks == 40) KVQ_SPLIT_HP(F, D, 5);        \
     else if (plan.part_blocks == 32) KVQ_SPLIT_HP(F, D, 4);   \
     else if (plan.part_blocks == 16) KVQ_SPLIT_HP(F, D, 2);   \
     else KVQ_SPLIT_HP(F, D, 1);                               \
   } while (0)
     // any other split size would cover only part of each split
     if (plan.part_blocks != 8 && plan.part_blocks != 16 && plan.part_blocks != 32 &&
-        plan.part_blocks != 64)
+        plan.part_blocks != 40)
       return hipErrorInvalidValue;
     dispatch_fmt(fmt, [&](auto f) {
       constexpr int F = decltype(f)::value;

@@ -57,6 +57,22 @@ def test_workspace_size_is_positive_and_monotone():
     assert a % (32 * 32 * (128 + 2) * 4) == 0
 
 
+@pytest.mark.parametrize("B,Hq,dh", [(32, 32, 128), (4, 32, 128), (1, 4, 64), (8, 64, 128),
+                                     (3, 6, 64), (128, 32, 128)])
+def test_workspace_size_never_shrinks_as_the_context_grows(B, Hq, dh):
+    """A workspace sized for the longest context serves every shorter call:
+    across every split-size threshold of the plan, the size is non-decreasing
+    in max_context_len, a whole number of (b, hq, split) partials, and at least
+    one 40-block split per 640 tokens."""
+    unit = B * Hq * (dh + 2) * 4
+    prev = 0
+    for ctx in range(0, 40001, 7):
+        ws = K.kvq_decode_workspace_size(B, Hq, dh, ctx, 16)
+        assert ws >= prev, f"max_context_len {ctx}: {ws} < {prev}"
+        assert ws % unit == 0 and ws // unit >= max(1, -(-ctx // 640))
+        prev = ws
+
+
 def status_of_decode(**over):
     L = K.lib()
     args = dict(out=FAKE, odt=0, q=FAKE, kc=FAKE, vc=FAKE, nb=10, bt=FAKE, mb=4, cl=FAKE, B=2,

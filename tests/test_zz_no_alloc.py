@@ -62,10 +62,13 @@ def test_noalloc_equals_the_workspace_call_twice_in_a_row():
 def test_sizes_beyond_the_static_scratch_are_refused():
     import quantized_kv_cache_fp8_amd as K
     B, Hq, dh = 32, 32, 128
-    assert K.kvq_decode_workspace_size(B, Hq, dh, 15872, 16) <= K.STATIC_SCRATCH_BYTES
-    assert K.kvq_decode_workspace_size(B, Hq, dh, 16384, 16) > K.STATIC_SCRATCH_BYTES
+    assert K.kvq_decode_workspace_size(B, Hq, dh, 19840, 16) <= K.STATIC_SCRATCH_BYTES
+    assert K.kvq_decode_workspace_size(B, Hq, dh, 19841, 16) > K.STATIC_SCRATCH_BYTES
+    # the workspace size never shrinks as the context grows, so every longer
+    # context is refused too
+    assert K.kvq_decode_workspace_size(B, Hq, dh, 20480, 16) > K.STATIC_SCRATCH_BYTES
     L = K.lib()
     FAKE = 0x10000
-    args = [FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, 1024, FAKE, B, Hq, 8, dh, 16, 16384,
+    args = [FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, 1280, FAKE, B, Hq, 8, dh, 16, 20480,
             FAKE, FAKE, 0, 0, 0.0, None]
     assert L.kvq_decode_attn_append_noalloc(*args) == -7  # KVQ_ERR_SCRATCH, no device work
