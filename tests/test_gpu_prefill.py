@@ -200,6 +200,17 @@ def test_ragged_full_size_sampled_rows():
     full_size_check(W.ragged_chunked_prefill(), 67)
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_long_prefix_sampled_rows(fmt):
+    """Chunks on top of long cached prefixes, at the full head shape: 32768 and
+    20000 cached tokens (hundreds of key tiles per query tile, the running
+    maximum raised over a long row) and an empty prefix.  Every row is written,
+    and one sampled pair per workgroup matches the oracle."""
+    wl = W.prefill_workload(f"long-prefix-{fmt}", 320, [32768, 20000, 0], [512, 1000, 300],
+                            Hq=32, Hkv=8, dh=128, fmt=fmt)
+    full_size_check(wl, 321)
+
+
 def test_explicit_softmax_scale():
     """A caller-given softmax scale in place of 1/sqrt(dh)."""
     wl = W.prefill_workload("prefill-sm", 314, [50, 0], [70, 33], Hq=16, Hkv=4)
