@@ -461,8 +461,23 @@ def tiny_row(K, W, torch, dev, stream, reps=200):
         K.kvq_decode_attn(out, q, kc, vc, bt, ctx, mc, one, one, "fp8_e4m3", "tensor",
                           workspace=ws)
     ms = time_call(torch, stream, call, reps)
+    # the same two calls captured once in a HIP graph and replayed: the
+    # kernels' own latency, without the binding's per-call host work
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    out.fill_(float("nan"))
+    ms_graph = time_call(torch, stream, g.replay, reps)
     return {"workload": wl.name + " (kvq_cache_write of 256 tokens, then kvq_decode_attn)",
-            "us": round(ms * 1e3, 2)}
+            "us": round(ms * 1e3, 2), "us_graph_replay": round(ms_graph * 1e3, 2),
+            "graph_replay_matches_eager": bool(torch.equal(out, eager))}
 
 
 def measure_rows(K, W, torch, dev, stream, k_all, v_all, slots_all, caches, ks, vs, wl, dec,
