@@ -20,8 +20,10 @@
 // workgroup has GT waves, one per query head of a GQA group, so every K/V tile
 // staged in LDS serves all GT heads.  Query tiles are issued longest-first
 // (the causal triangle makes late tiles the most expensive), and workgroups
-// are renumbered so that each XCD takes consecutive tiles of the same
-// (sequence, head group) and keeps their K/V tiles in its own L2.  Per 64-key
+// are renumbered so that each XCD runs one contiguous stretch of a logical
+// order -- query tiles fastest, then sequences, then head groups -- whose
+// resident workgroups share the K/V tiles of a few (sequence, head group)
+// pairs in that XCD's own L2.  Per 64-key
 // tile: the workgroup copies K (4 cache blocks) into LDS row-major and V, whose
 // cache tiles are already channel-major, with its keys permuted into the order the B
 // operand holds P in (so each lane's A operand is one 32-byte run); the next
