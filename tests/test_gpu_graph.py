@@ -1,12 +1,14 @@
 """The decode step captured in a HIP graph (torch.cuda.CUDAGraph) and replayed:
 the library allocates nothing and issues no memsets, so every replay must give
 the eager result bit for bit.  Replays alternate with eager work on the same
-stream, and each replay is checked."""
+stream, and each replay is checked; the eager result itself (and the cache the
+step leaves) is checked against the oracle."""
 import numpy as np
 import pytest
 
+import oracle
 import workloads as W
-from helpers import to_dev, to_np
+from helpers import ATTN_TOL, rel_err, row_rel_err, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -47,6 +49,18 @@ def test_append_decode_replays_match_eager():
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     eager = to_np(out).copy()
+    # the eager step itself against the oracle over every token (the append
+    # wrote each sequence's newest one)
+    f, gr = oracle.FMT_E4M3, oracle.GRAN_TENSOR
+    ks_ref, vs_ref = oracle.calibrate(wl.kv.k, f, gr)[1], oracle.calibrate(wl.kv.v, f, gr)[1]
+    assert np.array_equal(to_np(ks), ks_ref) and np.array_equal(to_np(vs), vs_ref)
+    kc_ref = np.full(tuple(kc.shape), 0xFF, np.uint8)
+    vc_ref = np.full(tuple(vc.shape), 0xFF, np.uint8)
+    oracle.cache_write(wl.kv.k, wl.kv.v, wl.kv.slot_mapping, kc_ref, vc_ref, ks_ref, vs_ref, f, gr)
+    assert np.array_equal(to_np(kc), kc_ref) and np.array_equal(to_np(vc), vc_ref)
+    ref = oracle.decode_attn(wl.q, kc_ref, vc_ref, wl.paging.block_tables,
+                             wl.paging.context_lens, ks_ref, vs_ref, f, gr)
+    assert rel_err(eager, ref) <= ATTN_TOL and row_rel_err(eager, ref) <= ATTN_TOL
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
