@@ -34,6 +34,25 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) == set(K.EXPORTS)
 
 
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/kvq.h compiles as strict C99 (no C++, no HIP headers needed) and
+    every function it declares resolves against libkvq.so at link time."""
+    import subprocess
+    names = declared_functions()
+    src = tmp_path / "uses_every_symbol.c"
+    src.write_text("#include \"kvq.h\"\n"
+                   "typedef void (*fn)(void);\n"
+                   "fn table[] = {\n" + "".join(f"  (fn){n},\n" for n in names) + "};\n"
+                   "int main(void) { return table[0] == 0; }\n")
+    exe = tmp_path / "uses_every_symbol"
+    r = subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                        "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                        str(exe), "-L", os.path.dirname(K.LIB_PATH), "-lkvq",
+                        "-Wl,--no-as-needed", "-Wl,--unresolved-symbols=report-all"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_strerror_covers_every_status():
     for st in range(-7, 1):
         assert K.kvq_strerror(st) and K.kvq_strerror(st) != "unknown status"
