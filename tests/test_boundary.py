@@ -36,7 +36,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_header_is_plain_c_and_links(tmp_path):
     """include/kvq.h compiles as strict C99 (no C++, no HIP headers needed) and
-    every function it declares resolves against libkvq.so at link time."""
+    every function it declares resolves at link time against the library the
+    binding loads."""
     import subprocess
     names = declared_functions()
     src = tmp_path / "uses_every_symbol.c"
@@ -47,8 +48,7 @@ def test_header_is_plain_c_and_links(tmp_path):
     exe = tmp_path / "uses_every_symbol"
     r = subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
                         "-I", os.path.join(ROOT, "include"), str(src), "-o",
-                        str(exe), "-L", os.path.dirname(K.LIB_PATH), "-lkvq",
-                        "-Wl,--no-as-needed", "-Wl,--unresolved-symbols=report-all"],
+                        str(exe), K.LIB_PATH, "-Wl,--unresolved-symbols=ignore-in-shared-libs"],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
 
