@@ -34,21 +34,23 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) == set(K.EXPORTS)
 
 
-def test_header_is_plain_c_and_links(tmp_path):
+def test_header_is_plain_c_and_links():
     """include/kvq.h compiles as strict C99 (no C++, no HIP headers needed) and
     every function it declares resolves at link time against the library the
     binding loads."""
     import subprocess
     names = declared_functions()
-    src = tmp_path / "uses_every_symbol.c"
-    src.write_text("#include \"kvq.h\"\n"
-                   "typedef void (*fn)(void);\n"
-                   "fn table[] = {\n" + "".join(f"  (fn){n},\n" for n in names) + "};\n"
-                   "int main(void) { return table[0] == 0; }\n")
-    exe = tmp_path / "uses_every_symbol"
+    work = os.path.join(ROOT, "tests", "c_client", "_build")  # git-ignored
+    os.makedirs(work, exist_ok=True)
+    src = os.path.join(work, "uses_every_symbol.c")
+    with open(src, "w") as fh:
+        fh.write("#include \"kvq.h\"\n"
+                 "typedef void (*fn)(void);\n"
+                 "fn table[] = {\n" + "".join(f"  (fn){n},\n" for n in names) + "};\n"
+                 "int main(void) { return table[0] == 0; }\n")
+    exe = os.path.join(work, "uses_every_symbol")
     r = subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
-                        "-I", os.path.join(ROOT, "include"), str(src), "-o",
-                        str(exe), K.LIB_PATH, "-Wl,--unresolved-symbols=ignore-in-shared-libs"],
+                        "-I", os.path.join(ROOT, "include"), src, "-o", exe, K.LIB_PATH, "-Wl,--unresolved-symbols=ignore-in-shared-libs"],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
 
