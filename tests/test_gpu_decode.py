@@ -169,3 +169,28 @@ def test_explicit_softmax_scale(Hq, Hkv):
     ref = oracle.decode_attn(wl.q, kc, vc, wl.paging.block_tables, wl.paging.context_lens,
                              run.ks_ref, run.vs_ref, run.fmt, run.gran, 0.2)
     check(to_np(run.out), ref)
+
+@pytest.mark.parametrize("B,Hq,Hkv,cl", [
+    (3, 8, 2, [700, 1, 300]),      # up to 16 splits, 4 | Hq: 4 channels per thread, 4 rows
+    (1, 3, 1, [1000]),             # up to 16 splits, 4 does not divide Hq: one row per workgroup
+    (2, 3, 1, [2176, 100]),        # 17 splits, B * Hq * nsplit even: lanes, 4 channels per thread
+    (1, 3, 1, [2176]),             # 17 splits, B * Hq * nsplit odd: lanes, one channel per thread
+])
+def test_every_split_merge_form(B, Hq, Hkv, cl):
+    """Each form of the split merge, chosen by the split count and the parity of
+    B x Hq x nsplit (16-byte aligned partials), against the oracle; the bf16
+    output is the fp32 one rounded to nearest even."""
+    wl = W.decode_workload("merge-forms", 1800 + B * 10 + Hq, B, Hq, Hkv, 128, cl, 16, "e4m3",
+                           "head", k_outliers=(2, 8.0), head_range=(0.5, 20.0))
+    run = DecodeRun(wl)
+    run.gpu_scales()
+    run.gpu_write()
+    kc, vc = run.oracle_caches()
+    out = run.gpu_decode()
+    ref = oracle.decode_attn(wl.q, kc, vc, wl.paging.block_tables, wl.paging.context_lens,
+                             run.ks_ref, run.vs_ref, run.fmt, run.gran)
+    check(out, ref)
+    run16 = DecodeRun(wl, out_dtype="bf16")
+    run16.gpu_scales()
+    run16.gpu_write()
+    assert np.array_equal(run16.gpu_decode(), W.f32_to_bf16_bits(out))
