@@ -59,7 +59,9 @@ constexpr int64_t kFillWgs = 2048;
 // block pair of codes, the O tile) fits in 128 registers
 constexpr int kWavesPerSimd = 4;
 // ... of the kernel for groups of at most 4 heads, and of its
-// per-token-head-scale variant (4 more live registers: at 5 waves it spills)
+// per-token-head-scale variant (114 registers at 4 waves; held to 94 for 5
+// waves it spills nothing but times the same, 52.1 against 52.2 us on the
+// Llama-shaped layer, so the allocator keeps its room)
 constexpr int kG4WavesPerSimd = 5;
 constexpr int kTsWavesPerSimd = 4;
 // waves per workgroup of the kernel for groups of at most 4 heads
