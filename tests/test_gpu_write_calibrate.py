@@ -116,6 +116,39 @@ def test_write_partial_and_misaligned_runs(start, path):
     assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
 
 
+@pytest.mark.parametrize("path", ["short", "long"])
+def test_duplicate_slots_land_one_of_the_writers(path):
+    """Tokens that name the same slot (the header leaves which one lands
+    unspecified): every 16-byte K piece of such a slot, one thread's store, is
+    the piece of one of its writers, every V byte is one of their bytes, and
+    every other slot is bit-exact.  The candidates are the oracle's cache with
+    the first writers alone and with the second writers written over them."""
+    g = W.rng(31)
+    Hkv, dh, T = 2, 128, 120
+    k = W.normal_bf16(g, (T, Hkv, dh))
+    v = W.normal_bf16(g, (T, Hkv, dh))
+    slots = g.permutation(8 * 16)[:T].astype(np.int64)
+    slots[90:] = slots[10:40]  # tokens 90..119 land on the slots of tokens 10..39
+    ks, vs = [0.02, 0.05], [0.03, 0.01]
+    gk, gv = gpu_write(k, v, slots, 8, Hkv, dh, ks, vs, 0, oracle.GRAN_HEAD, path)
+    first = slots.copy()
+    first[90:] = -1
+    ak, av = oracle_write(k, v, first, 8, Hkv, dh, ks, vs, 0, oracle.GRAN_HEAD)
+    bk, bv = ak.copy(), av.copy()
+    second = np.full(T, -1, np.int64)
+    second[90:] = slots[90:]
+    oracle.cache_write(k, v, second, bk, bv, np.asarray(ks, np.float32),
+                       np.asarray(vs, np.float32), 0, oracle.GRAN_HEAD)
+    # K: [blk][h][chunk][off][16] -- compare whole 16-byte pieces
+    pk = lambda c: c.reshape(-1, 16)
+    ok_k = np.all(pk(gk) == pk(ak), axis=1) | np.all(pk(gk) == pk(bk), axis=1)
+    assert ok_k.all(), f"{(~ok_k).sum()} K pieces match neither writer"
+    assert np.all((gv == av) | (gv == bv)), "a V byte matches neither writer"
+    # slots with one writer (or none) are exact: there the two candidates agree
+    assert np.array_equal(gk[ak == bk], ak[ak == bk]) and np.array_equal(gv[av == bv], av[av == bv])
+    assert (ak != bk).any()  # the duplicates really differ
+
+
 def test_write_empty_batch_is_a_no_op():
     gk, gv = gpu_write(np.zeros((0, 2, 64), np.uint16), np.zeros((0, 2, 64), np.uint16),
                        np.zeros(0, np.int64), 2, 2, 64, [1.0], [1.0], 0, 0)
