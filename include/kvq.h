@@ -322,7 +322,8 @@ kvq_status kvq_decode_attn_token_scales(void* out, int out_dtype, const void* q_
  * Quantize whole groups: k, v bf16 [n_groups * 32][Hkv][128]; tokens
  * 32 g .. 32 g + 31 form group g and go to block group_blocks[g] (int32
  * [n_groups]; a block outside [0, num_blocks) skips the group).  Only the
- * target tiles are written.
+ * target tiles are written; two groups that name the same block leave that
+ * tile's contents unspecified (each writes its tile piece by piece).
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED (dh != 128, alignment). */
 kvq_status kvq_kivi_quantize(const void* k_bf16, const void* v_bf16, int64_t n_groups, int Hkv,
                              int dh, const int32_t* group_blocks, uint8_t* kivi_cache,
