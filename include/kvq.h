@@ -329,7 +329,9 @@ kvq_status kvq_kivi_quantize(const void* k_bf16, const void* v_bf16, int64_t n_g
                              int dh, const int32_t* group_blocks, uint8_t* kivi_cache,
                              int64_t num_blocks, kvq_stream stream);
 
-/* Bytes of device workspace kvq_kivi_decode_attn needs (0 for invalid sizes). */
+/* Bytes of device workspace kvq_kivi_decode_attn needs (0 for invalid sizes).
+ * Never decreases as max_groups grows (B, Hq and Hkv fixed), so a workspace
+ * sized for the largest max_groups serves every smaller call. */
 size_t kvq_kivi_decode_workspace_size(int B, int Hq, int Hkv, int max_groups);
 
 /* Decode attention over a KIVI cache ([T] 10.4.2 attention on the values

@@ -575,7 +575,17 @@ KiviPlan kivi_decode_plan(int B, int Hq, int Hkv, int max_groups) {
   while (PG > 4 && (int64_t)B * Hkv * ((max_groups + PG - 1) / PG) < kKiviMinWgs) PG >>= 1;
   p.groups_per_split = PG;
   p.nsplit = 1 + (max_groups + PG - 1) / PG;
-  p.ws_bytes = (size_t)B * Hq * p.nsplit * (2 + kDH) * sizeof(float);
+  // The workspace holds the most splits any max_groups up to this one plans
+  // (a smaller max_groups can take a smaller split and so more of them), so a
+  // workspace sized for the largest serves every call.  With fill quantized
+  // splits per sequence filling the chip, 4-group splits run up to 8 (fill - 1)
+  // groups, ceil(max_groups / 4) of them; no larger split size ever plans more
+  // than 2 (fill - 1).
+  const int64_t fill = (kKiviMinWgs + (int64_t)B * Hkv - 1) / ((int64_t)B * Hkv);
+  int64_t ws_q = (max_groups + PG - 1) / PG;
+  const int64_t short_q = (max_groups + 3) / 4 < 2 * (fill - 1) ? (max_groups + 3) / 4 : 2 * (fill - 1);
+  if (short_q > ws_q) ws_q = short_q;
+  p.ws_bytes = (size_t)B * Hq * (size_t)(1 + ws_q) * (2 + kDH) * sizeof(float);
   return p;
 }
 

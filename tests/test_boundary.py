@@ -55,6 +55,20 @@ def test_header_is_plain_c_and_links():
     assert r.returncode == 0, r.stderr
 
 
+@pytest.mark.parametrize("B,Hq,Hkv", [(8, 32, 8), (1, 4, 1), (3, 6, 2), (64, 32, 8)])
+def test_kivi_workspace_size_never_shrinks_as_groups_grow(B, Hq, Hkv):
+    """The same promise for the 2-bit decode: non-decreasing in max_groups, a
+    whole number of (b, hq, split) partials, at least the residual split plus
+    one 32-group split per 32 groups."""
+    unit = B * Hq * (128 + 2) * 4
+    prev = 0
+    for mg in range(0, 3001, 3):
+        ws = K.kvq_kivi_decode_workspace_size(B, Hq, Hkv, mg)
+        assert ws >= prev, f"max_groups {mg}: {ws} < {prev}"
+        assert ws % unit == 0 and ws // unit >= 1 + -(-mg // 32)
+        prev = ws
+
+
 def test_strerror_covers_every_status():
     for st in range(-7, 1):
         assert K.kvq_strerror(st) and K.kvq_strerror(st) != "unknown status"
